@@ -1,0 +1,97 @@
+"""Multi-depth draft attention with the diagonal extension (oracle).
+
+Sources:
+
+- NeMo Automodel PR 2376, description: P-EAGLE reuses the EAGLE-3
+  ``cache_hidden`` diagonal-extension attention, which matches vLLM's
+  single-base-position decode; its parity section states that the K-step
+  ``cache_hidden`` forward equals a flat parallel forward over
+  [context, mask_1, ..., mask_{K-1}].
+- snxtyle/P_Eagle README: packed conversations are isolated by ``cu_seqlens``
+  (no attention across conversations).
+- speculators P-EAGLE guide, "Architecture": all depths in one pass, depth d at
+  position anchor + d.
+
+Predicate (reading of the pages): the query of draft row (d, p, head h) may see
+key row (e, p') iff
+
+    (e == 0 and p' is in the same packed sequence as p and p' <= p)     causal context
+ or (e >= 1 and p' == p and e <= d)                                     own anchor's depths 1..d
+
+so row (d, p) sees (p - a_s + 1) + d keys. Scores are <q', k'> / sqrt(D) on the
+RoPE-rotated q', k' (positions p - a_s + d, module ``rope``); q head h reads kv
+head floor(h / G), G = Hq / Hkv. Softmax over the allowed keys; out = P v; lse is
+the natural log of the softmax denominator of the scaled scores.
+
+The oracle builds the explicit dense boolean mask over all T key rows for each
+block of query rows and computes the softmax in float64. It never derives the
+mask from a tiling.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .bf16 import to_f64
+from .cod import row_depths
+from .rope import rotate, row_positions
+
+
+def row_meta(idx, depth_off, cu_seqlens) -> dict:
+    """depth, anchor, sequence id and position value of every draft row."""
+    idx = np.asarray(idx, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return dict(depth=row_depths(depth_off), anchor=idx,
+                seq=np.searchsorted(cu, idx, side="right") - 1,
+                pos=row_positions(idx, depth_off, cu_seqlens))
+
+
+def allowed_mask(meta: dict, qrows) -> np.ndarray:
+    """Dense boolean mask [len(qrows), T]: may query row i see key row c."""
+    qd = meta["depth"][qrows][:, None]
+    qa = meta["anchor"][qrows][:, None]
+    qs = meta["seq"][qrows][:, None]
+    kd = meta["depth"][None, :]
+    ka = meta["anchor"][None, :]
+    ks = meta["seq"][None, :]
+    context = (kd == 0) & (ks == qs) & (ka <= qa)
+    diagonal = (kd >= 1) & (ka == qa) & (kd <= qd)
+    return context | diagonal
+
+
+def draft_attention(q, k, v, idx, depth_off, cu_seqlens, theta: float,
+                    scale: float | None = None, rows=None, block: int = 256) -> dict:
+    """out [R, Hq, D] and lse [Hq, R] (float64) for the draft rows ``rows``.
+
+    q: bf16 bits [T, Hq, D]; k, v: bf16 bits [T, Hkv, D], all pre-RoPE.
+    """
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    meta = row_meta(idx, depth_off, cu_seqlens)
+    rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    kr = rotate(to_f64(k), meta["pos"], theta)             # [T, Hkv, D]
+    vf = to_f64(v)
+    out = np.empty((len(rows), Hq, D), dtype=np.float64)
+    lse = np.empty((Hq, len(rows)), dtype=np.float64)
+    for b0 in range(0, len(rows), block):
+        br = rows[b0:b0 + block]
+        mask = allowed_mask(meta, br)                      # [B, T]
+        qr = rotate(to_f64(q[br]), meta["pos"][br], theta)  # [B, Hq, D]
+        for h in range(Hq):
+            g = h // G
+            s = (qr[:, h, :] @ kr[:, g, :].T) * scale       # [B, T]
+            s = np.where(mask, s, -np.inf)
+            mx = s.max(axis=1, keepdims=True)
+            p = np.exp(s - mx)
+            den = p.sum(axis=1, keepdims=True)
+            out[b0:b0 + len(br), h, :] = (p @ vf[:, g, :]) / den
+            lse[h, b0:b0 + len(br)] = mx[:, 0] + np.log(den[:, 0])
+    return dict(out=out, lse=lse)
+
+
+def useful_pairs(idx, depth_off, cu_seqlens) -> int:
+    """Number of allowed (query row, key row) pairs per head: sum of (p - a_s + 1) + d."""
+    meta = row_meta(idx, depth_off, cu_seqlens)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return int(np.sum(meta["anchor"] - cu[meta["seq"]] + 1 + meta["depth"]))

@@ -1,0 +1,99 @@
+"""Pins for the fused-input and verification oracles: brute-force sums and
+argmax loops, special cases, and the planted-acceptance structure."""
+import numpy as np
+
+from oracle import cod, fuse, verify
+from oracle.bf16 import to_f64
+from token_drafting_amd import synth
+
+
+def _fuse_case(n=7, K=3, A=10, H=4, vocab=20, seed=3):
+    sel = cod.cod_select(n, K, 0.7, 0.2, seed, [0, n])
+    aux = synth.normal_bf16(seed, 50, (n, A))
+    W = synth.normal_bf16(seed, 51, (H, A), std=0.02)
+    mh = synth.normal_bf16(seed, 52, (A,))
+    E = synth.normal_bf16(seed, 53, (vocab, H))
+    tokens = np.random.default_rng(seed).integers(0, vocab - 1, size=n).astype(np.int32)
+    return sel, aux, W, mh, E, tokens, vocab - 1
+
+
+def test_fuse_brute_force():
+    sel, aux, W, mh, E, tokens, ptd = _fuse_case()
+    out = fuse.fuse_inputs(aux, W, mh, tokens, E, ptd, sel["idx"], sel["depth_off"])
+    a, w, m = to_f64(aux), to_f64(W), to_f64(mh)
+    H, A = w.shape
+    depth = cod.row_depths(sel["depth_off"])
+    for r, p in enumerate(sel["idx"]):
+        for h in range(H):
+            src = a[p] if depth[r] == 0 else m
+            want = 0.0
+            for t in range(A):
+                want += src[t] * w[h, t]
+            assert abs(out["hidden"][r, h] - want) < 1e-12
+        tok = tokens[p] if depth[r] == 0 else ptd
+        assert np.array_equal(out["embed_rows"][r], E[tok])
+
+
+def test_fuse_special_cases():
+    sel, aux, W, mh, E, tokens, ptd = _fuse_case(n=9, K=4)
+    n, A = aux.shape
+    # unit aux rows pick out columns of W: fc(e_t) = W[:, t]
+    unit = np.zeros((n, A), dtype=np.uint16)
+    unit[np.arange(n), np.arange(n) % A] = 0x3F80
+    zero_mask = np.zeros_like(mh)
+    out = fuse.fuse_inputs(unit, W, zero_mask, tokens, E, ptd, sel["idx"], sel["depth_off"])
+    d0 = sel["depth_off"][1]
+    for r in range(d0):
+        p = sel["idx"][r]
+        assert np.array_equal(out["hidden"][r], to_f64(W)[:, p % A])
+    assert (out["hidden"][d0:] == 0).all()                 # zero mask_hidden -> zero rows
+    out2 = fuse.fuse_inputs(aux, W, mh, tokens, E, ptd, sel["idx"], sel["depth_off"])
+    deep = out2["hidden"][d0:]
+    assert (deep == deep[0]).all()                          # every depth >= 1 row is the same
+    assert (out2["embed_rows"][d0:] == E[ptd]).all()
+    rows = np.array([0, d0, len(sel["idx"]) - 1])
+    sub = fuse.fuse_inputs(aux, W, mh, tokens, E, ptd, sel["idx"], sel["depth_off"], rows=rows)
+    assert np.array_equal(sub["hidden"], out2["hidden"][rows])
+
+
+def _f32_to_bits(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_argmax_brute_force_and_ties():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((6, 3, 50)).astype(np.float32)
+    x[0, 0, [3, 17, 40]] = 9.0                  # tie: lowest index wins
+    x[1, 2, :] = -1.0                           # all equal -> index 0
+    x[2, 1, [49]] = 5.0
+    x[3, 0, [0, 49]] = 7.0
+    bits = _f32_to_bits(x)
+    got = verify.argmax_rows(bits)
+    vals = to_f64(bits)
+    for i in range(6):
+        for d in range(3):
+            best, arg = -np.inf, -1
+            for t in range(50):
+                if vals[i, d, t] > best:
+                    best, arg = vals[i, d, t], t
+            assert got[i, d] == arg
+    assert got[0, 0] == 3 and got[1, 2] == 0 and got[2, 1] == 49 and got[3, 0] == 0
+
+
+def test_accept_lengths_examples():
+    a = np.array([[1, 2, 3, 4], [1, 2, 3, 4], [9, 2, 3, 4], [1, 2, 0, 4]])
+    b = np.array([[1, 2, 3, 4], [1, 2, 3, 5], [1, 2, 3, 4], [1, 2, 3, 4]])
+    # a later match after a mismatch does not count
+    assert verify.accept_lengths(a, b).tolist() == [4, 3, 0, 2]
+
+
+def test_planted_acceptance_structure():
+    K, V, N = 8, 1000, 3000
+    lg = synth.verify_logits(seed=5, drafts=N, K=K, V=V, p_plant=0.7)
+    res = verify.verify(lg["draft_logits"], lg["target_logits"])
+    L, planted = res["accept_len"], lg["planted"]
+    assert (L >= planted).all()
+    # beyond the planted prefix only a chance match (probability ~1/V per step) extends L
+    assert (L > planted).sum() <= 12
+    # mean planted prefix of a geometric stop: sum_{k=1..K} 0.7^k = 2.1993...
+    assert abs(planted.mean() - sum(0.7 ** k for k in range(1, K + 1))) < 0.12

@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs for the P-EAGLE draft forward.
+
+This module only draws random numbers and packs them into the buffers the draft
+forward consumes. It holds none of the method's arithmetic: how many rows survive
+COD sampling, which rows they are, the projection, RoPE, attention and the
+acceptance rule all live elsewhere. Callers pass the row count ``T`` in.
+
+Every tensor has its own generator, ``numpy.random.default_rng([seed, tag])``,
+so any tensor can be drawn without drawing the others first. Floating tensors
+are drawn as float32 normals and rounded to bfloat16 with round-to-nearest-even;
+they are returned as raw bf16 bit patterns (``uint16``), exactly the bytes that
+cross the C boundary.
+
+The workload shapes follow the pages: an EAGLE-3 drafter fed the concatenation
+of three target hidden states (speculators P-EAGLE guide, "Architecture"), a
+learnable ``mask_hidden`` of width 3 x target hidden (NeMo Automodel PR 2376,
+description), packed conversations delimited by ``cu_seqlens`` (snxtyle/P_Eagle
+README, data-preparation list), and K parallel depths with COD ratios 0.7 / 0.2
+(speculators guide, "Key Parameters").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Tensor tags: each input draws from default_rng([seed, TAG]).
+TAG_LENGTHS, TAG_AUX, TAG_W, TAG_MASK, TAG_EMBED, TAG_TOKENS = 1, 2, 3, 4, 5, 6
+TAG_Q, TAG_K, TAG_V, TAG_LOGITS = 7, 8, 9, 10
+
+VOCAB_IN = 32000          # input-embedding vocabulary of the synthetic drafter
+PLANT_VALUE_BITS = 0x4180  # bf16 bit pattern of 16.0 (exact), the planted maximum
+
+# The five synthetic workloads. Shapes only; no derived quantity lives here.
+CONFIGS = {
+    1: dict(workload="tiny-256", n=256, K=4, r=0.7, r_min=0.2, H=256, aux_dim=3 * 512,
+            Hq=4, Hkv=1, D=64, theta=1.0e4, num_seqs=1),
+    2: dict(workload="gemma270m-draft-4k", n=4096, K=4, r=0.7, r_min=0.2, H=640,
+            aux_dim=3 * 2560, Hq=4, Hkv=1, D=256, theta=1.0e4, num_seqs=1),
+    3: dict(workload="packed8-llama8b-draft-4k", n=4096, K=4, r=0.7, r_min=0.2, H=4096,
+            aux_dim=3 * 4096, Hq=32, Hkv=8, D=128, theta=5.0e5, num_seqs=8,
+            len_lo=256, len_hi=1024),
+    4: dict(workload="gemma270m-draft-32k-K4", n=32768, K=4, r=0.7, r_min=0.2, H=640,
+            aux_dim=3 * 2560, Hq=4, Hkv=1, D=256, theta=1.0e4, num_seqs=1),
+    5: dict(workload="llama8b-draft-16k-K8", n=16384, K=8, r=0.7, r_min=0.2, H=4096,
+            aux_dim=3 * 4096, Hq=32, Hkv=8, D=128, theta=5.0e5, num_seqs=1,
+            verify=dict(drafts=4096, K=8, V=32000, p_plant=0.7)),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); return the uint16 bits.
+
+    Inputs are finite normals, so the NaN/overflow corner of the rounding is not
+    reached.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def _rng(seed: int, tag: int) -> np.random.Generator:
+    return np.random.default_rng([int(seed), int(tag)])
+
+
+def normal_bf16(seed: int, tag: int, shape, std: float = 1.0,
+                chunk_rows: int = 1 << 20) -> np.ndarray:
+    """bf16 bits of N(0, std^2) samples of the given shape, drawn in row chunks."""
+    shape = tuple(int(s) for s in shape)
+    rng = _rng(seed, tag)
+    total = int(np.prod(shape)) if shape else 1
+    out = np.empty(total, dtype=np.uint16)
+    step = max(1, chunk_rows * (shape[-1] if shape else 1))
+    for lo in range(0, total, step):
+        hi = min(total, lo + step)
+        x = rng.standard_normal(hi - lo, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        out[lo:hi] = f32_to_bf16_bits(x)
+    return out.reshape(shape)
+
+
+def packed_lengths(seed: int, n: int, num_seqs: int, lo: int, hi: int) -> np.ndarray:
+    """Lengths of ``num_seqs`` conversations packed with no padding into n tokens.
+
+    Draw num_seqs-1 integers uniform in [lo, hi]; the last length is what is left
+    of n. Redraw from the same stream until the last one also lies in [lo, hi].
+    This is uniform over the packings with every length in range.
+    """
+    rng = _rng(seed, TAG_LENGTHS)
+    for _ in range(100000):
+        first = rng.integers(lo, hi + 1, size=num_seqs - 1)
+        last = n - int(first.sum())
+        if lo <= last <= hi:
+            return np.concatenate([first, [last]]).astype(np.int64)
+    raise RuntimeError("no valid packing found")
+
+
+def cu_seqlens_for(cfg: dict, seed: int) -> np.ndarray:
+    """int32 [S+1] sequence starts of the packed buffer (0 ... n)."""
+    n, S = cfg["n"], cfg.get("num_seqs", 1)
+    if S == 1:
+        return np.array([0, n], dtype=np.int32)
+    lens = packed_lengths(seed, n, S, cfg["len_lo"], cfg["len_hi"])
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def base_inputs(cfg: dict, seed: int) -> dict:
+    """Everything the fused input stage needs: cu_seqlens, aux, fc weight,
+    mask_hidden, embedding table, tokens and the reserved ptd token id."""
+    n, H, A = cfg["n"], cfg["H"], cfg["aux_dim"]
+    vocab = cfg.get("vocab_in", VOCAB_IN)
+    out = dict(
+        cu_seqlens=cu_seqlens_for(cfg, seed),
+        aux=normal_bf16(seed, TAG_AUX, (n, A)),
+        fc_weight=normal_bf16(seed, TAG_W, (H, A), std=0.02),
+        mask_hidden=normal_bf16(seed, TAG_MASK, (A,)),
+        embed=normal_bf16(seed, TAG_EMBED, (vocab, H)),
+        # tokens never take the last id, which is reserved as the ptd token
+        tokens=_rng(seed, TAG_TOKENS).integers(0, vocab - 1, size=n).astype(np.int32),
+        ptd_token_id=vocab - 1,
+        vocab=vocab,
+    )
+    return out
+
+
+def qkv_inputs(seed: int, T: int, Hq: int, Hkv: int, D: int) -> dict:
+    """Pre-RoPE q [T,Hq,D], k and v [T,Hkv,D], bf16 bits of N(0,1)."""
+    return dict(q=normal_bf16(seed, TAG_Q, (T, Hq, D)),
+                k=normal_bf16(seed, TAG_K, (T, Hkv, D)),
+                v=normal_bf16(seed, TAG_V, (T, Hkv, D)))
+
+
+def verify_logits(seed: int, drafts: int, K: int, V: int, p_plant: float,
+                  chunk: int = 256) -> dict:
+    """Draft and target logits [drafts, K, V] as bf16 bits of N(0,1) noise, with
+    planted shared maxima.
+
+    For each draft, depth d gets a plant with probability p_plant, but only while
+    every earlier depth was planted too. A plant writes 16.0 (exact in bf16, far
+    above any N(0,1) sample of this size) at one uniform position t* in both the
+    draft and the target row. ``planted`` holds how many leading depths were
+    planted per draft.
+    """
+    rng = _rng(seed, TAG_LOGITS)
+    plant_rng = _rng(seed, TAG_LOGITS + 100)
+    draft = np.empty((drafts, K, V), dtype=np.uint16)
+    target = np.empty((drafts, K, V), dtype=np.uint16)
+    for lo in range(0, drafts, chunk):
+        hi = min(drafts, lo + chunk)
+        m = (hi - lo) * K * V
+        draft[lo:hi] = f32_to_bf16_bits(rng.standard_normal(m, dtype=np.float32)).reshape(hi - lo, K, V)
+        target[lo:hi] = f32_to_bf16_bits(rng.standard_normal(m, dtype=np.float32)).reshape(hi - lo, K, V)
+    coins = plant_rng.random((drafts, K)) < p_plant
+    where = plant_rng.integers(0, V, size=(drafts, K))
+    planted = np.zeros(drafts, dtype=np.int32)
+    for i in range(drafts):
+        for d in range(K):
+            if not coins[i, d]:
+                break
+            draft[i, d, where[i, d]] = PLANT_VALUE_BITS
+            target[i, d, where[i, d]] = PLANT_VALUE_BITS
+            planted[i] += 1
+    return dict(draft_logits=draft, target_logits=target, planted=planted)
