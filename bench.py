@@ -1,0 +1,218 @@
+"""Benchmark of the P-EAGLE draft forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic inputs resident in
+HBM: COD index build, fused input stage (fc GEMM + mask/ptd substitution), RoPE table,
+RoPE gather + draft attention, and greedy verification. The default workload is the
+32K-context, K=4 Gemma-270M-shaped drafter (n = 32768, 4 q heads / 1 kv head, head dim
+256); its verification stage scores 4096 drafts of K=4 tokens over a 32000 vocabulary.
+
+Prints one JSON line. `value` is useful draft-attention TFLOP/s over the whole step
+(4 * D * Hq * allowed query-key pairs, divided by the step time); the attention call
+alone, drafted tokens/s and the per-kernel split are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768, help="oracle sample size (rows)")
+    return ap.parse_args()
+
+
+def useful_pairs(idx, depth_off, cu):
+    """Allowed (query row, key row) pairs per head: sum over rows of (p - a_s + 1) + d."""
+    idx = idx.astype(np.int64)
+    depth = np.repeat(np.arange(len(depth_off) - 1), np.diff(depth_off))
+    seq = np.searchsorted(cu, idx, side="right") - 1
+    return int(np.sum(idx - cu[seq] + 1 + depth)), idx - cu[seq] + 1 + depth
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.CONFIGS[args.config]
+    seed = args.config
+    n, K, Hq, Hkv, D = cfg["n"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---------------- inputs (host, seeded) -> HBM
+    t0 = time.time()
+    m, T = peagle.cod_counts(n, K, cfg["r"], cfg["r_min"])
+    base = synth.base_inputs(cfg, seed)
+    qkv = synth.qkv_inputs(seed, T, Hq, Hkv, D)
+    vcfg = cfg.get("verify") or dict(drafts=4096, K=K, V=32000, p_plant=0.7)
+    logits = synth.verify_logits(seed, vcfg["drafts"], vcfg["K"], vcfg["V"], vcfg["p_plant"])
+    cu_h = base["cu_seqlens"]
+    d = {k: to_dev(v) for k, v in base.items() if isinstance(v, np.ndarray)}
+    q, k, v = (to_dev(qkv[t]) for t in ("q", "k", "v"))
+    dl, tl = to_dev(logits["draft_logits"]), to_dev(logits["target_logits"])
+    gen_s = time.time() - t0
+
+    S = cu_h.size - 1
+    H = cfg["H"]
+    max_pos = peagle.rope_max_pos(n, K)
+    sel = dict(m=m, T=T, idx=torch.empty(T, dtype=torch.int32, device=dev),
+               depth_off=torch.empty(K + 1, dtype=torch.int32, device=dev),
+               cu_seqlens_d=torch.empty((K, S + 1), dtype=torch.int32, device=dev),
+               row_of=torch.empty((K, n), dtype=torch.int32, device=dev))
+    hidden = torch.empty((T, H), dtype=torch.float32, device=dev)
+    emb = torch.empty((T, H), dtype=torch.int16, device=dev)
+    cos = torch.empty((max_pos + 1, D // 2), dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(peagle.attn_workspace_bytes(n, T, Hq, Hkv, D), dtype=torch.uint8, device=dev)
+    Nd, Kv = vcfg["drafts"], vcfg["K"]
+    dtok = torch.empty((Nd, Kv), dtype=torch.int32, device=dev)
+    ttok = torch.empty((Nd, Kv), dtype=torch.int32, device=dev)
+    alen = torch.empty(Nd, dtype=torch.int32, device=dev)
+    lib = peagle.lib()
+
+    stages = ["cod_select", "fuse_inputs", "rope_table", "attn_prepare", "attn_core", "accept_prefix"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        peagle.cod_select_into(n, K, cfg["r"], cfg["r_min"], seed, d["cu_seqlens"], sel)
+        mark(1)
+        peagle.fuse_inputs(n, K, T, sel["idx"], d["aux"], d["fc_weight"], d["mask_hidden"],
+                           d["tokens"], d["embed"], base["ptd_token_id"], hidden, emb)
+        mark(2)
+        peagle._check("peagle_rope_table", lib.peagle_rope_table(
+            D, cfg["theta"], max_pos, peagle._ptr(cos), peagle._ptr(sin), peagle._stream()))
+        mark(3)
+        peagle.draft_attn(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse, ws, phase="prepare")
+        mark(4)
+        peagle.draft_attn(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse, ws, phase="core")
+        mark(5)
+        peagle.accept_prefix(dl, tl, dtok, ttok, alen)
+        mark(6)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(6)] for i in range(args.steps)])
+    stage_ms = dict(zip(stages, per.mean(axis=0).tolist()))
+    ms_step = wall * 1e3 / args.steps
+
+    # ---------------- accounting
+    idx_h = sel["idx"].cpu().numpy()
+    off_h = sel["depth_off"].cpu().numpy()
+    P, _ = useful_pairs(idx_h, off_h, cu_h)
+    attn_flop = 4.0 * D * Hq * P
+    core_ms = stage_ms["attn_core"]
+    attn_call_ms = stage_ms["attn_prepare"] + core_ms
+    core_tflops = attn_flop / (core_ms * 1e-3) / 1e12
+    value = attn_flop / (ms_step * 1e-3) / 1e12
+    # algorithmic bytes of the HBM-bound stages
+    rope_bytes = T * (Hq + Hkv) * D * 2 * 2 + T * D * 4
+    verify_bytes = 2 * Nd * Kv * vcfg["V"] * 2 + 8 * Nd * Kv + 4 * Nd
+    cod_bytes = 4 * T + 4 * K * n + 4 * K * (S + 1) + 4 * (K + 1)
+    fc_flop = 2.0 * (n + 1) * cfg["aux_dim"] * H
+
+    result = {
+        "metric": "draft-attn fwd TFLOP/s + drafted tokens/s, 32K ctx K=4; % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "n": n, "K": K, "r": cfg["r"], "r_min": cfg["r_min"],
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "draft_rows": T,
+                   "useful_pairs_per_head": P, "verify": f"{Nd}x{Kv}x{vcfg['V']}"},
+        "attn_core_tflops": round(core_tflops, 2),
+        "attn_core_frac_bf16_peak": round(core_tflops / PEAK_BF16_TFLOPS, 4),
+        "drafted_tokens_per_s": round(T / (attn_call_ms * 1e-3), 1),
+        "pipeline_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "stage_ms": {k2: round(v2, 4) for k2, v2 in stage_ms.items()},
+        "stage_rate": {
+            "cod_select_GBps": round(cod_bytes / (stage_ms["cod_select"] * 1e-3) / 1e9, 2),
+            "fuse_fc_TFLOPs": round(fc_flop / (stage_ms["fuse_inputs"] * 1e-3) / 1e12, 2),
+            "attn_prepare_rope_GBps": round(rope_bytes / (stage_ms["attn_prepare"] * 1e-3) / 1e9, 1),
+            "accept_prefix_GBps": round(verify_bytes / (stage_ms["accept_prefix"] * 1e-3) / 1e9, 1),
+        },
+        "roofline": {"kernel": "attn_core_kernel (both launches of peagle_draft_attn_core)",
+                     "bound": "mfma", "achieved": round(core_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(core_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "input_gen_s": round(gen_s, 1),
+        "wall_s_timed": round(wall, 4),
+    }
+
+    # ---------------- oracle on the host cores (bounded sample)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, seed, qkv, cu_h, idx_h, off_h, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, seed, qkv, cu, idx, depth_off, rows_wanted):
+    """The float64 oracle's draft attention on a seeded sample of query rows of the same
+    workload (dense mask over all key rows, as the oracle always computes it)."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as oattn
+
+    T = int(depth_off[-1])
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(T, size=min(rows_wanted, T), replace=False))
+    _, keys = useful_pairs(idx, depth_off, cu)
+    flop = 4.0 * cfg["D"] * cfg["Hq"] * float(keys[rows].sum())
+    t0 = time.perf_counter()
+    oattn.draft_attention(qkv["q"], qkv["k"], qkv["v"], idx, depth_off, cu, cfg["theta"], rows=rows)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"oracle draft attention (float64, dense mask) on {len(rows)} seeded random "
+                      f"query rows of {T}, all heads; {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

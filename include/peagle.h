@@ -1,0 +1,195 @@
+/*
+ * peagle.h -- C ABI of libpeagle, the MI355X (gfx950) draft forward of P-EAGLE
+ * parallel drafting: all K prediction depths of an EAGLE-3 style drafter in one pass.
+ *
+ * Sources (the pages that describe the method):
+ *   [G]  speculators documentation, user guide "P-EAGLE": sections "Architecture",
+ *        "COD Sampling", "Inference Process", "Key Parameters".
+ *   [N]  NeMo Automodel pull request 2376, "feat(speculative): add P-EAGLE
+ *        parallel-drafting training for EAGLE-3 drafts": the PR description
+ *        (implementation, checkpoint contract, parity section) and the commit message
+ *        of the RoPE fix.
+ *   [R]  snxtyle/P_Eagle README: packed conversations isolated by cu_seqlens.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns all memory;
+ *     the library never allocates, frees or synchronises. Work is enqueued
+ *     asynchronously on `stream` (a hipStream_t passed as void*, NULL = null stream).
+ *   - Tensors are dense, row-major, and bf16 tensors are raw bit patterns (uint16_t).
+ *     Device pointers must be 16-byte aligned.
+ *   - Arguments are checked on the host before anything is enqueued. A bad argument
+ *     returns PEAGLE_ERR_ARG (or PEAGLE_ERR_UNSUPPORTED for a valid but unimplemented
+ *     shape) and enqueues nothing. A launch failure returns PEAGLE_ERR_HIP. Faults inside
+ *     a kernel surface at the caller's next synchronisation.
+ *   - Integer arrays that are device data (cu_seqlens, idx, row_of, tokens) are trusted:
+ *     the kernels clamp indices derived from them so a malformed array cannot make them
+ *     read or write out of bounds, but the results are then meaningless.
+ *   - Notation: n tokens in the packed buffer, S packed sequences, K depths, T draft
+ *     rows. Draft rows are depth-major; inside a depth they ascend by anchor. Depth 0
+ *     keeps every position, so draft row p of depth 0 is anchor p.
+ *   - The library keeps no state and is safe to call from several threads.
+ */
+#ifndef PEAGLE_H_
+#define PEAGLE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t peagle_bf16; /* raw bfloat16 bits */
+
+enum {
+  PEAGLE_OK = 0,
+  PEAGLE_ERR_ARG = -1,         /* invalid argument; nothing enqueued */
+  PEAGLE_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head_dim 96) */
+  PEAGLE_ERR_HIP = -3,         /* the HIP runtime rejected a launch */
+  PEAGLE_ERR_WORKSPACE = -4    /* workspace smaller than the *_workspace_bytes result */
+};
+
+#define PEAGLE_MAX_DEPTHS 64
+
+/* Human-readable name of a status code (static string). */
+const char *peagle_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int peagle_version(void);
+
+/*
+ * peagle_cod_counts -- host arithmetic of COD sampling [G, "COD Sampling"]: depth 0
+ * keeps all n positions, depth d keeps about n*r^d, never fewer than about n*r_min.
+ *   m[d] = min(n, max(floor(n*r^d + 1/2), floor(n*r_min + 1/2)))  for d in [0, K)
+ *   *T   = sum of m[d]
+ * n >= 1, 1 <= K <= PEAGLE_MAX_DEPTHS, 0 < r <= 1, 0 <= r_min <= 1.
+ * m: (host) int64[K]; T: (host) int64. Either may be NULL when not wanted.
+ */
+int peagle_cod_counts(int64_t n, int32_t K, double r, double r_min, int64_t *m, int64_t *T);
+
+/*
+ * peagle_cod_select -- COD index builder [G, "COD Sampling"]. Depth d keeps the m[d]
+ * buffer indices p with the smallest SplitMix64(seed XOR p) (first output of the
+ * SplitMix64 generator from state seed^p, compared as unsigned 64-bit words), p being
+ * the index in the whole packed buffer. The sets are nested: R_d within R_{d-1}.
+ *   cu_seqlens    int32[S+1]       packed-sequence starts, 0 = cu[0] <= ... <= cu[S] = n
+ *   idx           int32[T]   out   anchors, depth-major, ascending within a depth
+ *   depth_off     int32[K+1] out   first draft row of each depth (prefix sum of m)
+ *   cu_seqlens_d  int32[K*(S+1)] out  [d][s] = kept anchors of depth d below cu[s]
+ *   row_of        int32[K*n] out   [d][p] = draft row of (d, p), or -1 if not kept
+ * Requires n < 2^31 and T as given by peagle_cod_counts.
+ */
+int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
+                      const int32_t *cu_seqlens, int32_t num_seqs, int32_t *idx,
+                      int32_t *depth_off, int32_t *cu_seqlens_d, int32_t *row_of, void *stream);
+
+/*
+ * peagle_fuse_inputs -- fused input stage [N, description; G, "Architecture"]. Depth 0
+ * rows take fc(aux[p]) and the embedding of tokens[p]; depth >= 1 rows take
+ * fc(mask_hidden) and the embedding of ptd_token_id. fc is a bias-free linear layer
+ * run as a bf16 MFMA GEMM with fp32 accumulation; no fc_norm.
+ *   idx           int32[T]            from peagle_cod_select
+ *   aux           bf16[n, aux_dim]    concatenated target aux hidden states (3 x H_target)
+ *   fc_weight     bf16[H, aux_dim]    linear-layer layout (output-major)
+ *   mask_hidden   bf16[aux_dim]       the learnable placeholder
+ *   tokens        int32[n]            token of each position
+ *   embed         bf16[vocab, H]      input embedding table
+ *   hidden_out    fp32[T, H]   out
+ *   embed_out     bf16[T, H]   out
+ * aux_dim and H must be multiples of 8. ptd_token_id must lie in [0, vocab)
+ * (required and range-checked, as in [N]'s recipe arguments).
+ */
+int peagle_fuse_inputs(int64_t n, int32_t K, int64_t T, const int32_t *idx,
+                       const peagle_bf16 *aux, int32_t aux_dim, const peagle_bf16 *fc_weight,
+                       const peagle_bf16 *mask_hidden, const int32_t *tokens,
+                       const peagle_bf16 *embed, int32_t vocab, int32_t ptd_token_id, int32_t H,
+                       float *hidden_out, peagle_bf16 *embed_out, void *stream);
+
+/*
+ * peagle_rope_table -- cos/sin cache indexed by position value [N, RoPE-fix commit]:
+ *   cos_out[pos][j] = cos(pos * theta^(-2j/D)), sin_out likewise, j < D/2,
+ * angles and cos/sin evaluated in float64, stored fp32, for pos in [0, max_pos].
+ *   cos_out, sin_out  fp32[max_pos+1, head_dim/2]  out
+ * head_dim even, theta > 0, max_pos >= 0.
+ */
+int peagle_rope_table(int32_t head_dim, double theta, int32_t max_pos, float *cos_out,
+                      float *sin_out, void *stream);
+
+/* Bytes of workspace peagle_draft_attn_* need for these sizes (0 on bad arguments). */
+size_t peagle_draft_attn_workspace_bytes(int64_t n, int64_t T, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * peagle_draft_attn_fwd -- multi-depth draft attention forward [N, description and
+ * parity section; R; G, "Architecture"]. The query of draft row (d, p), head h, sees
+ *   - depth-0 keys p' of the same packed sequence with p' <= p, and
+ *   - its own anchor's depth-e rows for 1 <= e <= d (the diagonal extension),
+ * on RoPE-rotated q and k at positions p - a_s + d (a_s = start of p's sequence; cos/sin
+ * gathered by position value, [N, RoPE-fix commit]); q head h reads kv head
+ * floor(h / (Hq/Hkv)). Softmax in fp32, QK^T and PV on bf16 MFMA.
+ *   idx, depth_off, row_of   from peagle_cod_select
+ *   cu_seqlens       int32[S+1]
+ *   q                bf16[T, Hq, D]   pre-RoPE
+ *   k, v             bf16[T, Hkv, D]  pre-RoPE
+ *   softmax_scale    usually 1/sqrt(D)
+ *   rope_cos/sin     fp32[rope_max_pos+1, D/2] from peagle_rope_table;
+ *                    rope_max_pos >= n + K - 2 (the largest position any row can take)
+ *   out              fp32[T, Hq, D]   out
+ *   lse              fp32[Hq, T]      out, natural-log softmax denominators; may be NULL
+ *   workspace        >= peagle_draft_attn_workspace_bytes(n, T, Hq, Hkv, D) bytes,
+ *                    device memory, 256-byte aligned; its contents are scratch
+ * head_dim in {64, 128, 256}; Hq % Hkv == 0 and 256 % (Hq/Hkv) == 0.
+ * Equal to peagle_draft_attn_prepare followed by peagle_draft_attn_core.
+ */
+int peagle_draft_attn_fwd(int64_t n, int32_t K, int64_t T, const int32_t *idx,
+                          const int32_t *depth_off, const int32_t *row_of,
+                          const int32_t *cu_seqlens, int32_t num_seqs, const peagle_bf16 *q,
+                          const peagle_bf16 *k, const peagle_bf16 *v, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                          const float *rope_cos, const float *rope_sin, int32_t rope_max_pos,
+                          float *out, float *lse, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * The two halves of peagle_draft_attn_fwd, same arguments, for callers that time them
+ * apart: _prepare rotates q and k by position value into the workspace (RoPE), lays
+ * the depth-0 v out in attention tiles and builds the anchor-major row list; _core runs
+ * the attention itself from that workspace, which must hold what a _prepare call with
+ * the same arguments wrote (stream order suffices).
+ */
+int peagle_draft_attn_prepare(int64_t n, int32_t K, int64_t T, const int32_t *idx,
+                              const int32_t *depth_off, const int32_t *row_of,
+                              const int32_t *cu_seqlens, int32_t num_seqs,
+                              const peagle_bf16 *q, const peagle_bf16 *k, const peagle_bf16 *v,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              float softmax_scale, const float *rope_cos, const float *rope_sin,
+                              int32_t rope_max_pos, float *out, float *lse, void *workspace,
+                              size_t workspace_bytes, void *stream);
+int peagle_draft_attn_core(int64_t n, int32_t K, int64_t T, const int32_t *idx,
+                           const int32_t *depth_off, const int32_t *row_of,
+                           const int32_t *cu_seqlens, int32_t num_seqs, const peagle_bf16 *q,
+                           const peagle_bf16 *k, const peagle_bf16 *v, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                           const float *rope_cos, const float *rope_sin, int32_t rope_max_pos,
+                           float *out, float *lse, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * peagle_accept_prefix -- greedy verification [G, "Inference Process"]: the target
+ * checks every draft token in one pass and the longest correct prefix is accepted.
+ *   draft_logits, target_logits  bf16[N, K, V]; row [i, d] of target_logits scores the
+ *                                token that draft depth d proposes; shared vocabulary
+ *   draft_tok, target_tok        int32[N, K] out  argmax per row (lowest index on ties)
+ *   accept_len                   int32[N]    out  leading d with draft_tok == target_tok
+ * 1 <= K <= PEAGLE_MAX_DEPTHS, V >= 1. NaN logits give unspecified tokens.
+ */
+int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,
+                         const peagle_bf16 *draft_logits, const peagle_bf16 *target_logits,
+                         int32_t *draft_tok, int32_t *target_tok, int32_t *accept_len,
+                         void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PEAGLE_H_ */

@@ -1,0 +1,133 @@
+"""The C boundary without a GPU: the library loads, exports every declared symbol,
+its host arithmetic matches the oracle, and bad arguments are refused before any
+device work (all calls here pass NULL device pointers)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import cod as ocod
+from token_drafting_amd import build, peagle
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "peagle.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(peagle.lib_path()):
+        build.build()
+    return peagle.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(peagle_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in peagle.SIGNATURES, name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.peagle_version() >= 100
+    for code in (0, -1, -2, -3, -4):
+        assert lib.peagle_status_string(code).decode() != "unknown status"
+
+
+@pytest.mark.parametrize("n,K,r,r_min", [(256, 4, 0.7, 0.2), (4096, 4, 0.7, 0.2), (32768, 4, 0.7, 0.2),
+                                         (16384, 8, 0.7, 0.2), (10, 3, 0.5, 0.0), (4, 3, 0.1, 0.0),
+                                         (1, 8, 0.7, 0.2), (100, 64, 0.95, 0.01), (7, 5, 1.0, 1.0)])
+def test_cod_counts_match_oracle(lib, n, K, r, r_min):
+    m, T = peagle.cod_counts(n, K, r, r_min)
+    want = ocod.retained_counts(n, K, r, r_min)
+    assert m == want and T == sum(want)
+
+
+def test_cod_counts_random_against_oracle(lib):
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        n = int(rng.integers(1, 200000))
+        K = int(rng.integers(1, 12))
+        r = float(rng.uniform(0.05, 1.0))
+        r_min = float(rng.uniform(0.0, 1.0))
+        m, _ = peagle.cod_counts(n, K, r, r_min)
+        assert m == ocod.retained_counts(n, K, r, r_min), (n, K, r, r_min)
+
+
+def _code(fn, *args):
+    return getattr(peagle.lib(), fn)(*args)
+
+
+def test_cod_argument_errors(lib):
+    T = C.c_int64()
+    for bad in [(0, 4, 0.7, 0.2), (10, 0, 0.7, 0.2), (10, 65, 0.7, 0.2), (10, 4, 0.0, 0.2),
+                (10, 4, 1.5, 0.2), (10, 4, 0.7, -0.1), (10, 4, 0.7, 1.1), (10, 4, float("nan"), 0.2)]:
+        assert _code("peagle_cod_counts", *bad, None, C.byref(T)) == peagle.ERR_ARG
+    # valid counts, NULL device pointers -> refused
+    assert _code("peagle_cod_select", 10, 4, 0.7, 0.2, 1, None, 1, None, None, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_cod_select", 10, 4, 0.7, 0.2, 1, None, 0, None, None, None, None, None) == peagle.ERR_ARG
+
+
+def test_fuse_argument_errors(lib):
+    args = dict(n=8, K=2, T=12, aux_dim=16, vocab=10, ptd=9, H=8)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return _code("peagle_fuse_inputs", a["n"], a["K"], a["T"], None, None, a["aux_dim"], None,
+                     None, None, None, a["vocab"], a["ptd"], a["H"], None, None, None)
+    assert call() == peagle.ERR_ARG                 # valid shapes, NULL pointers
+    assert call(ptd=10) == peagle.ERR_ARG           # ptd_token_id out of range
+    assert call(ptd=-1) == peagle.ERR_ARG
+    assert call(T=7) == peagle.ERR_ARG              # T < n
+    assert call(T=17) == peagle.ERR_ARG             # T > K n
+    assert call(aux_dim=12) == peagle.ERR_ARG       # not a multiple of 8
+    assert call(H=12) == peagle.ERR_ARG
+
+
+def test_attention_argument_errors(lib):
+    base = dict(n=64, K=4, T=150, S=1, Hq=4, Hkv=1, D=64, scale=0.125, max_pos=66, ws=1 << 30)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return _code("peagle_draft_attn_fwd", a["n"], a["K"], a["T"], None, None, None, None, a["S"],
+                     None, None, None, a["Hq"], a["Hkv"], a["D"], a["scale"], None, None,
+                     a["max_pos"], None, None, None, a["ws"], None)
+    assert call() == peagle.ERR_ARG                    # NULL pointers
+    assert call(D=96) == peagle.ERR_UNSUPPORTED
+    assert call(D=32) == peagle.ERR_UNSUPPORTED
+    assert call(Hq=6, Hkv=2) == peagle.ERR_UNSUPPORTED   # group of 3 does not divide 256
+    assert call(Hq=5, Hkv=2) == peagle.ERR_ARG
+    assert call(max_pos=65) == peagle.ERR_ARG          # below n + K - 2
+    assert call(ws=1024) == peagle.ERR_WORKSPACE
+    assert call(scale=0.0) == peagle.ERR_ARG
+    assert call(T=63) == peagle.ERR_ARG
+    assert call(S=0) == peagle.ERR_ARG
+    for fn in ("peagle_draft_attn_prepare", "peagle_draft_attn_core"):
+        assert _code(fn, 64, 4, 150, None, None, None, None, 1, None, None, None, 4, 1, 96, 0.125,
+                     None, None, 66, None, None, None, 1 << 30, None) == peagle.ERR_UNSUPPORTED
+
+
+def test_rope_and_accept_argument_errors(lib):
+    assert _code("peagle_rope_table", 63, 1e4, 10, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_rope_table", 64, -1.0, 10, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_rope_table", 64, 1e4, -1, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_rope_table", 64, 1e4, 10, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_accept_prefix", 4, 0, 100, None, None, None, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_accept_prefix", 4, 65, 100, None, None, None, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_accept_prefix", 4, 8, 0, None, None, None, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_accept_prefix", 4, 8, 100, None, None, None, None, None, None) == peagle.ERR_ARG
+
+
+def test_workspace_bytes(lib):
+    a = peagle.attn_workspace_bytes(4096, 10375, 4, 1, 256)
+    b = peagle.attn_workspace_bytes(4096, 12000, 4, 1, 256)
+    assert 0 < a < b
+    assert a % 256 == 0
+    assert peagle.attn_workspace_bytes(0, 10, 4, 1, 64) == 0

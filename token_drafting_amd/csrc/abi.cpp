@@ -1,0 +1,219 @@
+// C entry points of libpeagle: host-side validation, then the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/peagle.h"
+#include "kernels.h"
+
+using namespace peagle;
+
+namespace {
+
+constexpr int64_t kMaxI32 = 0x7FFFFFFF;
+
+int status_of(hipError_t e) { return e == hipSuccess ? PEAGLE_OK : PEAGLE_ERR_HIP; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// COD counts [speculators P-EAGLE guide, "COD Sampling"]: depth d keeps
+// max(round(n r^d), round(n r_min)) positions, rounding half up, capped at n.
+int counts(int64_t n, int32_t K, double r, double r_min, int64_t* m, int64_t* T) {
+  if (n < 1 || n > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return PEAGLE_ERR_ARG;
+  if (!std::isfinite(r) || !(r > 0.0) || r > 1.0) return PEAGLE_ERR_ARG;
+  if (!std::isfinite(r_min) || r_min < 0.0 || r_min > 1.0) return PEAGLE_ERR_ARG;
+  const double nd = (double)n;
+  const int64_t floor_count = (int64_t)std::floor(nd * r_min + 0.5);
+  int64_t total = 0;
+  for (int d = 0; d < K; ++d) {
+    int64_t md = (int64_t)std::floor(nd * std::pow(r, (double)d) + 0.5);
+    if (md < floor_count) md = floor_count;
+    if (md > n) md = n;
+    if (m) m[d] = md;
+    total += md;
+  }
+  if (T) *T = total;
+  return PEAGLE_OK;
+}
+
+struct AttnCall {
+  AttnArgs a;
+  const int32_t *idx, *depth_off, *row_of, *cu;
+  const uint16_t *q, *k, *v;
+  const float *cs, *sn;
+  float *out, *lse;
+  char* ws;
+  hipStream_t stream;
+};
+
+int attn_check(int64_t n, int32_t K, int64_t T, const int32_t* idx, const int32_t* depth_off,
+               const int32_t* row_of, const int32_t* cu, int32_t S, const peagle_bf16* q,
+               const peagle_bf16* k, const peagle_bf16* v, int32_t Hq, int32_t Hkv, int32_t D,
+               float scale, const float* cs, const float* sn, int32_t max_pos, float* out,
+               float* lse, void* ws, size_t ws_bytes, void* stream, AttnCall* call) {
+  if (n < 1 || n > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return PEAGLE_ERR_ARG;
+  if (T < n || T > (int64_t)K * n || T > kMaxI32) return PEAGLE_ERR_ARG;
+  if (S < 1 || S > n) return PEAGLE_ERR_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PEAGLE_ERR_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return PEAGLE_ERR_ARG;
+  if ((int64_t)max_pos < n + K - 2) return PEAGLE_ERR_ARG;
+  if (D != 64 && D != 128 && D != 256) return PEAGLE_ERR_UNSUPPORTED;
+  if (256 % (Hq / Hkv) != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if (ws_bytes < attn_layout(n, T, Hq, Hkv, D).total) return PEAGLE_ERR_WORKSPACE;
+  if (!idx || !depth_off || !row_of || !cu || !q || !k || !v || !cs || !sn || !out || !ws)
+    return PEAGLE_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(cs) ||
+      !aligned16(sn) || (reinterpret_cast<uintptr_t>(ws) & 255) != 0)
+    return PEAGLE_ERR_ARG;
+  call->a = AttnArgs{(int32_t)n, K, (int32_t)T, S, Hq, Hkv, D, max_pos, scale};
+  call->idx = idx;
+  call->depth_off = depth_off;
+  call->row_of = row_of;
+  call->cu = cu;
+  call->q = q;
+  call->k = k;
+  call->v = v;
+  call->cs = cs;
+  call->sn = sn;
+  call->out = out;
+  call->lse = lse;
+  call->ws = static_cast<char*>(ws);
+  call->stream = static_cast<hipStream_t>(stream);
+  return PEAGLE_OK;
+}
+
+int run_prepare(const AttnCall& c) {
+  return status_of(launch_attn_prepare(c.a, c.idx, c.depth_off, c.row_of, c.cu, c.q, c.k, c.v,
+                                       c.cs, c.sn, c.ws, c.stream));
+}
+
+int run_core(const AttnCall& c) {
+  return status_of(launch_attn_core(c.a, c.q, c.k, c.v, c.cs, c.sn, c.out, c.lse, c.ws, c.stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* peagle_status_string(int status) {
+  switch (status) {
+    case PEAGLE_OK: return "ok";
+    case PEAGLE_ERR_ARG: return "invalid argument";
+    case PEAGLE_ERR_UNSUPPORTED: return "unsupported shape";
+    case PEAGLE_ERR_HIP: return "HIP launch failure";
+    case PEAGLE_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int peagle_version(void) { return 100; }
+
+int peagle_cod_counts(int64_t n, int32_t K, double r, double r_min, int64_t* m, int64_t* T) {
+  return counts(n, K, r, r_min, m, T);
+}
+
+int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t* idx,
+                      int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of, void* stream) {
+  int64_t m[PEAGLE_MAX_DEPTHS], T = 0;
+  const int st = counts(n, K, r, r_min, m, &T);
+  if (st != PEAGLE_OK) return st;
+  if (T > kMaxI32 || (int64_t)K * n > ((int64_t)1 << 40)) return PEAGLE_ERR_ARG;
+  if (num_seqs < 1 || num_seqs > n) return PEAGLE_ERR_ARG;
+  if (!cu_seqlens || !idx || !depth_off || !cu_seqlens_d || !row_of) return PEAGLE_ERR_ARG;
+  CodArgs a{};
+  a.n = (int32_t)n;
+  a.K = K;
+  a.S = num_seqs;
+  a.seed = seed;
+  a.off[0] = 0;
+  for (int d = 0; d < K; ++d) {
+    a.m[d] = (int32_t)m[d];
+    a.off[d + 1] = a.off[d] + (int32_t)m[d];
+  }
+  return status_of(launch_cod_select(a, cu_seqlens, idx, depth_off, cu_seqlens_d, row_of,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int peagle_fuse_inputs(int64_t n, int32_t K, int64_t T, const int32_t* idx,
+                       const peagle_bf16* aux, int32_t aux_dim, const peagle_bf16* fc_weight,
+                       const peagle_bf16* mask_hidden, const int32_t* tokens,
+                       const peagle_bf16* embed, int32_t vocab, int32_t ptd_token_id, int32_t H,
+                       float* hidden_out, peagle_bf16* embed_out, void* stream) {
+  if (n < 1 || n > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return PEAGLE_ERR_ARG;
+  if (T < n || T > (int64_t)K * n || T > kMaxI32) return PEAGLE_ERR_ARG;
+  if (aux_dim < 8 || aux_dim % 8 != 0 || H < 8 || H % 8 != 0 || vocab < 1) return PEAGLE_ERR_ARG;
+  if (ptd_token_id < 0 || ptd_token_id >= vocab) return PEAGLE_ERR_ARG;
+  if (!idx || !aux || !fc_weight || !mask_hidden || !tokens || !embed || !hidden_out || !embed_out)
+    return PEAGLE_ERR_ARG;
+  if (!aligned16(aux) || !aligned16(fc_weight) || !aligned16(mask_hidden) || !aligned16(embed) ||
+      !aligned16(hidden_out) || !aligned16(embed_out))
+    return PEAGLE_ERR_ARG;
+  FuseArgs a{(int32_t)n, (int32_t)T, aux_dim, H, vocab, ptd_token_id};
+  return status_of(launch_fuse(a, idx, aux, fc_weight, mask_hidden, tokens, embed, hidden_out,
+                               embed_out, static_cast<hipStream_t>(stream)));
+}
+
+int peagle_rope_table(int32_t head_dim, double theta, int32_t max_pos, float* cos_out,
+                      float* sin_out, void* stream) {
+  if (head_dim < 2 || head_dim % 2 != 0 || max_pos < 0) return PEAGLE_ERR_ARG;
+  if (!std::isfinite(theta) || !(theta > 0.0)) return PEAGLE_ERR_ARG;
+  if ((int64_t)(max_pos + 1) * (head_dim / 2) > kMaxI32) return PEAGLE_ERR_ARG;
+  if (!cos_out || !sin_out) return PEAGLE_ERR_ARG;
+  return status_of(
+      launch_rope_table(head_dim, theta, max_pos, cos_out, sin_out, static_cast<hipStream_t>(stream)));
+}
+
+size_t peagle_draft_attn_workspace_bytes(int64_t n, int64_t T, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim) {
+  if (n < 1 || T < n || T > kMaxI32 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
+    return 0;
+  return attn_layout(n, T, num_q_heads, num_kv_heads, head_dim).total;
+}
+
+#define PEAGLE_ATTN_ARGS                                                                       \
+  int64_t n, int32_t K, int64_t T, const int32_t *idx, const int32_t *depth_off,              \
+      const int32_t *row_of, const int32_t *cu_seqlens, int32_t num_seqs, const peagle_bf16 *q, \
+      const peagle_bf16 *k, const peagle_bf16 *v, int32_t num_q_heads, int32_t num_kv_heads,    \
+      int32_t head_dim, float softmax_scale, const float *rope_cos, const float *rope_sin,     \
+      int32_t rope_max_pos, float *out, float *lse, void *workspace, size_t workspace_bytes,   \
+      void *stream
+#define PEAGLE_ATTN_FWD                                                                         \
+  n, K, T, idx, depth_off, row_of, cu_seqlens, num_seqs, q, k, v, num_q_heads, num_kv_heads,   \
+      head_dim, softmax_scale, rope_cos, rope_sin, rope_max_pos, out, lse, workspace,          \
+      workspace_bytes, stream
+
+int peagle_draft_attn_prepare(PEAGLE_ATTN_ARGS) {
+  AttnCall c;
+  const int st = attn_check(PEAGLE_ATTN_FWD, &c);
+  return st != PEAGLE_OK ? st : run_prepare(c);
+}
+
+int peagle_draft_attn_core(PEAGLE_ATTN_ARGS) {
+  AttnCall c;
+  const int st = attn_check(PEAGLE_ATTN_FWD, &c);
+  return st != PEAGLE_OK ? st : run_core(c);
+}
+
+int peagle_draft_attn_fwd(PEAGLE_ATTN_ARGS) {
+  AttnCall c;
+  int st = attn_check(PEAGLE_ATTN_FWD, &c);
+  if (st != PEAGLE_OK) return st;
+  st = run_prepare(c);
+  return st != PEAGLE_OK ? st : run_core(c);
+}
+
+int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,
+                         const peagle_bf16* draft_logits, const peagle_bf16* target_logits,
+                         int32_t* draft_tok, int32_t* target_tok, int32_t* accept_len,
+                         void* stream) {
+  if (num_drafts < 0 || K < 1 || K > PEAGLE_MAX_DEPTHS || vocab < 1) return PEAGLE_ERR_ARG;
+  if (!draft_logits || !target_logits || !draft_tok || !target_tok || !accept_len)
+    return PEAGLE_ERR_ARG;
+  if (num_drafts == 0) return PEAGLE_OK;
+  return status_of(launch_accept(num_drafts, K, vocab, draft_logits, target_logits, draft_tok,
+                                 target_tok, accept_len, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// COD (Conditional Drop-token) index builder.
+//
+// Follows the speculators P-EAGLE guide, section "COD Sampling": depth 0 keeps every
+// position, depth d keeps about n*r^d (floor n*r_min). Depth d keeps the m_d buffer
+// indices p with the smallest SplitMix64(seed XOR p), compared as unsigned 64-bit words
+// (SplitMix64 as published by Steele, Lea and Flood, OOPSLA 2014: add the golden gamma,
+// then the variant-13 mixer). Taking the m_d smallest of one ranking nests the sets.
+// The hash is a bijection, so the m_d-th smallest hash is a unique threshold and depth d
+// keeps exactly the p with hash <= threshold.
+//
+// One workgroup of 1024 threads does the whole job; the outputs are < 1 MB even at
+// n = 32K, so this kernel is latency-bound:
+//   1. per depth, an MSB-first radix select (8 passes of 8 bits) finds the threshold;
+//   2. one pass over p in chunks of 1024 computes each hash once, takes a wave ballot
+//      per depth and writes idx / row_of in ascending p (ordered compaction);
+//   3. cu_seqlens_d by binary search of each sequence start in the depth's idx run.
+#include "common.h"
+#include "kernels.h"
+
+namespace peagle {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
+
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  uint64_t z = x + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ __launch_bounds__(kThreads) void cod_select_kernel(
+    CodArgs a, const int32_t* __restrict__ cu, int32_t* __restrict__ idx,
+    int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t thr[kMaxDepths];
+  __shared__ int32_t wcount[2][kMaxDepths][kWaves];
+  __shared__ int32_t carry[2][kMaxDepths];
+  __shared__ uint64_t s_prefix;
+  __shared__ int32_t s_rank;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = a.n, K = a.K;
+
+  // 1. thresholds: keep p at depth d iff hash(p) <= thr[d] (m_d == 0 keeps nothing).
+  for (int d = 0; d < K; ++d) {
+    const int m = a.m[d];
+    if (m >= n || m == 0) {
+      if (tid == 0) thr[d] = ~0ull;
+      continue;
+    }
+    if (d > 0 && a.m[d - 1] == m) {  // same count, same threshold
+      if (tid == 0) thr[d] = thr[d - 1];
+      __syncthreads();
+      continue;
+    }
+    uint64_t prefix = 0, pmask = 0;
+    int rank = m;  // we want the rank-th smallest hash (1-based) among those matching prefix
+    for (int shift = 56; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int p = tid; p < n; p += kThreads) {
+        const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
+        if ((h & pmask) == prefix) atomicAdd(&hist[(h >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int before = 0, b = 0;
+        for (; b < 255; ++b) {
+          if (before + (int)hist[b] >= rank) break;
+          before += hist[b];
+        }
+        s_rank = rank - before;
+        s_prefix = prefix | ((uint64_t)b << shift);
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      rank = s_rank;
+      pmask |= 0xFFull << shift;
+    }
+    if (tid == 0) thr[d] = prefix;
+    __syncthreads();
+  }
+  if (tid <= K) depth_off[tid] = a.off[tid];
+  __syncthreads();
+
+  // 2. ordered compaction, all depths in one pass over p. Per chunk of 1024 positions a
+  // wave ballot gives each lane its rank inside the wave; per-wave counts go through LDS.
+  // The running count before the chunk (carry) is block-uniform and lives in LDS too;
+  // both are double-buffered by chunk parity so one barrier per chunk suffices.
+  if (tid < K) carry[0][tid] = 0;
+  __syncthreads();
+  int parity = 0;
+  for (int base = 0; base < n; base += kThreads, parity ^= 1) {
+    const int p = base + tid;
+    const bool inside = p < n;
+    const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
+    for (int d = 0; d < K; ++d) {
+      const bool keep = inside && a.m[d] > 0 && h <= thr[d];
+      const uint64_t ball = __ballot(keep);
+      if (lane == 0) wcount[parity][d][wave] = __popcll(ball);
+    }
+    __syncthreads();
+    for (int d = 0; d < K; ++d) {
+      const bool keep = inside && a.m[d] > 0 && h <= thr[d];
+      const uint64_t ball = __ballot(keep);
+      int before = carry[parity][d], total = 0;
+      for (int w = 0; w < kWaves; ++w) {
+        const int c = wcount[parity][d][w];
+        if (w < wave) before += c;
+        total += c;
+      }
+      const int r = a.off[d] + before + __popcll(ball & ((1ull << lane) - 1ull));
+      if (inside) {
+        row_of[(size_t)d * n + p] = keep ? r : -1;
+        if (keep && r < a.off[d + 1]) idx[r] = p;
+      }
+      if (tid == 0) carry[parity ^ 1][d] = carry[parity][d] + total;
+    }
+    // wcount[parity] and carry[parity] are rewritten two chunks later, after a barrier
+    // that every thread reaches only once it has finished with them.
+  }
+  __threadfence();
+  __syncthreads();
+
+  // 3. kept anchors of depth d before each sequence start.
+  for (int t = tid; t < K * (a.S + 1); t += kThreads) {
+    const int d = t / (a.S + 1), s = t % (a.S + 1);
+    cu_d[t] = lower_count(idx + a.off[d], a.m[d], cu[s]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_t* idx,
+                             int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(cod_select_kernel, dim3(1), dim3(kThreads), 0, stream, a, cu_seqlens, idx,
+                     depth_off, cu_seqlens_d, row_of);
+  return hipGetLastError();
+}
+
+}  // namespace peagle

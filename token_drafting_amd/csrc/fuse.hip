@@ -1,0 +1,175 @@
+// Fused input stage of the draft forward.
+//
+// NeMo Automodel PR 2376 (description): depth 0 takes the real token embedding and the
+// fc projection of the concatenated target aux hidden states; depths >= 1 take the
+// embedding of the reserved ptd_token_id and the fc projection of the learnable
+// mask_hidden [1, 3*H_target]. The speculators P-EAGLE guide ("Architecture") says the
+// selected target hidden states are concatenated and projected.
+//
+// Draft rows are depth-major and depth 0 keeps every position, so draft row p of depth
+// 0 is anchor p: the projection of aux row p lands directly in hidden_out[p]. The
+// projected mask_hidden is one extra GEMM row (row n) and lands in hidden_out[n], the
+// first depth-1 row; the fill kernel copies it to the remaining depth >= 1 rows and
+// gathers the embedding rows.
+//
+// fc_gemm: C[M,N] = A[M,K] * B[N,K]^T, bf16 in, fp32 accumulate and out, on
+// v_mfma_f32_32x32x16_bf16. Workgroup tile 256x128x64, 4 waves in 2x2, wave tile
+// 128x64 (4x2 MFMA tiles). Both operands are K-contiguous, so each MFMA operand is one
+// 16-byte LDS read; LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by
+// (row & 7) so the 32 rows a half-wave reads spread over all banks.
+#include "common.h"
+#include "kernels.h"
+
+namespace peagle {
+
+namespace {
+
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kAChunks = BM * BK / 8 / kThreads;  // 16-byte chunks per thread
+constexpr int kBChunks = BN * BK / 8 / kThreads;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK * 2 + ((chunk ^ (row & 7)) << 4); }
+
+__global__ __launch_bounds__(kThreads) void fc_gemm_kernel(
+    const uint16_t* __restrict__ aux, const uint16_t* __restrict__ mask_hidden,
+    const uint16_t* __restrict__ W, float* __restrict__ C, int n, int M, int N, int K) {
+  __shared__ __attribute__((aligned(16))) char As[BM * BK * 2];
+  __shared__ __attribute__((aligned(16))) char Bs[BN * BK * 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+
+  u32x4 ra[kAChunks], rb[kBChunks];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+      const int q = tid + i * kThreads, row = q >> 3, c = q & 7;
+      const int m = m0 + row, k = k0 + c * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m < M && k < K) {
+        const uint16_t* src = (m < n) ? aux + (size_t)m * K : mask_hidden;
+        v = *reinterpret_cast<const u32x4*>(src + k);
+      }
+      ra[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i) {
+      const int q = tid + i * kThreads, row = q >> 3, c = q & 7;
+      const int col = n0 + row, k = k0 + c * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (col < N && k < K) v = *reinterpret_cast<const u32x4*>(W + (size_t)col * K + k);
+      rb[i] = v;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+      const int q = tid + i * kThreads;
+      *reinterpret_cast<u32x4*>(As + swz(q >> 3, q & 7)) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i) {
+      const int q = tid + i * kThreads;
+      *reinterpret_cast<u32x4*>(Bs + swz(q >> 3, q & 7)) = rb[i];
+    }
+  };
+
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int r32 = lane & 31, half = lane >> 5;
+  load_tile(0);
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (k0 + BK < K) load_tile(k0 + BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + r32;
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(As + swz(row, ks * 2 + half)));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wn * 64 + j * 32 + r32;
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(Bs + swz(row, ks * 2 + half)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn * 64 + j * 32 + r32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row < M) C[(size_t)row * N + col] = acc[i][j][r];
+      }
+    }
+}
+
+// Depth >= 1 rows: hidden = projected mask_hidden (row n), embedding of ptd_token_id.
+// Depth 0 rows (r < n, anchor r): embedding of tokens[r]. One thread per 16 bytes.
+__global__ __launch_bounds__(256) void fuse_fill_kernel(
+    const int32_t* __restrict__ tokens, const uint16_t* __restrict__ embed,
+    float* __restrict__ hidden, uint16_t* __restrict__ embed_out, int n, int T, int H, int vocab,
+    int ptd) {
+  const int ech = H / 8, hch = H / 4;  // 16-byte chunks per embed / hidden row
+  const size_t total_e = (size_t)T * ech;
+  const size_t total_h = (T > n + 1) ? (size_t)(T - n - 1) * hch : 0;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total_e + total_h; t += stride) {
+    if (t < total_e) {
+      const int r = (int)(t / ech), c = (int)(t % ech);
+      int tok = (r < n) ? tokens[r] : ptd;
+      tok = min(max(tok, 0), vocab - 1);
+      *reinterpret_cast<u32x4*>(embed_out + (size_t)r * H + c * 8) =
+          *reinterpret_cast<const u32x4*>(embed + (size_t)tok * H + c * 8);
+    } else {
+      const size_t u = t - total_e;
+      const int r = n + 1 + (int)(u / hch), c = (int)(u % hch);
+      *reinterpret_cast<floatx4*>(hidden + (size_t)r * H + c * 4) =
+          *reinterpret_cast<const floatx4*>(hidden + (size_t)n * H + c * 4);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* aux,
+                       const uint16_t* fc_weight, const uint16_t* mask_hidden,
+                       const int32_t* tokens, const uint16_t* embed, float* hidden_out,
+                       uint16_t* embed_out, hipStream_t stream) {
+  (void)idx;  // depth-0 row r is anchor r; depth >= 1 rows need no anchor
+  const int M = (a.T > a.n) ? a.n + 1 : a.n;
+  dim3 grid((a.H + BN - 1) / BN, (M + BM - 1) / BM);
+  hipLaunchKernelGGL(fc_gemm_kernel, grid, dim3(kThreads), 0, stream, aux, mask_hidden, fc_weight,
+                     hidden_out, a.n, M, a.H, a.aux_dim);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t work = (size_t)a.T * (a.H / 8) + (size_t)(a.T > a.n + 1 ? a.T - a.n - 1 : 0) * (a.H / 4);
+  const int blocks = (int)((work + 255) / 256 < 65536 ? (work + 255) / 256 : 65536);
+  if (blocks > 0)
+    hipLaunchKernelGGL(fuse_fill_kernel, dim3(blocks), dim3(256), 0, stream, tokens, embed,
+                       hidden_out, embed_out, a.n, a.T, a.H, a.vocab, a.ptd);
+  return hipGetLastError();
+}
+
+}  // namespace peagle

@@ -1,0 +1,63 @@
+// Host-side launchers of the P-EAGLE draft-forward kernels. Internal to libpeagle:
+// arguments are validated by the C entry points before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace peagle {
+
+constexpr int kMaxDepths = 64;
+
+struct CodArgs {
+  int32_t n, K, S;
+  uint64_t seed;
+  int32_t m[kMaxDepths];
+  int32_t off[kMaxDepths + 1];
+};
+
+hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_t* idx,
+                             int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
+                             hipStream_t stream);
+
+struct FuseArgs {
+  int32_t n, T, aux_dim, H, vocab, ptd;
+};
+
+hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* aux,
+                       const uint16_t* fc_weight, const uint16_t* mask_hidden,
+                       const int32_t* tokens, const uint16_t* embed, float* hidden_out,
+                       uint16_t* embed_out, hipStream_t stream);
+
+hipError_t launch_rope_table(int32_t head_dim, double theta, int32_t max_pos, float* cos_out,
+                             float* sin_out, hipStream_t stream);
+
+// Workspace of the draft attention, carved from one caller-provided buffer.
+struct AttnLayout {
+  size_t qinfo, qstart, qrot, krot, vt, chunks, nchunks, total;
+  int max_chunks;
+};
+AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D);
+int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv);
+
+struct AttnArgs {
+  int32_t n, K, T, S, Hq, Hkv, D, max_pos;
+  float scale;
+};
+
+hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int32_t* depth_off,
+                               const int32_t* row_of, const int32_t* cu_seqlens,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const float* rope_cos, const float* rope_sin, char* ws,
+                               hipStream_t stream);
+
+hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const float* rope_cos, const float* rope_sin,
+                            float* out, float* lse, const char* ws, hipStream_t stream);
+
+hipError_t launch_accept(int32_t N, int32_t K, int32_t V, const uint16_t* draft,
+                         const uint16_t* target, int32_t* draft_tok, int32_t* target_tok,
+                         int32_t* accept_len, hipStream_t stream);
+
+}  // namespace peagle

@@ -1,0 +1,296 @@
+// RoPE gathered by position value, plus the layout preparation of the draft attention.
+//
+// NeMo Automodel PR 2376, commit message of the RoPE fix: cos/sin are gathered by the
+// actual position values (not sliced by sequence length), from a cache sized to the
+// highest requested position, which exceeds the sequence length for the per-depth
+// offsets. Draft row (d, p) sits at position p - a_s + d, a_s being the start of p's
+// packed sequence (the speculators guide, "Architecture": depth d at anchor + d; the
+// snxtyle/P_Eagle README: packed sequences separated by cu_seqlens). Llama rotate-half
+// convention, frequencies theta^(-2j/D); applied to q and k, not v.
+//
+// Kernels:
+//   rope_table_kernel    cos/sin [max_pos+1, D/2] fp32, angles and cos/sin in fp64.
+//   qlist_kernel         anchor-major list of draft rows (all depths of anchor 0, then
+//                        of anchor 1, ...) with per-row (row, anchor, depth, seq start),
+//                        and qstart[p] = first entry of anchor p. One workgroup.
+//   rope_rotate_kernel   q' and k' of every draft row, bf16, draft-row order.
+//   v_transpose_kernel   depth-0 v as 32-key tiles laid out [d][32 keys], keys permuted
+//                        inside each 16-key group as (0-3, 8-11, 4-7, 12-15) so that a
+//                        16-byte read is the PV operand of one MFMA half-wave.
+#include <algorithm>
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace peagle {
+
+namespace {
+
+__global__ __launch_bounds__(256) void rope_table_kernel(float* __restrict__ cos_out,
+                                                         float* __restrict__ sin_out, int half,
+                                                         int D, double theta, int max_pos) {
+  const size_t total = (size_t)(max_pos + 1) * half;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
+       t += (size_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(t / half), j = (int)(t % half);
+    const double inv = pow(theta, -2.0 * (double)j / (double)D);
+    const double ang = (double)pos * inv;
+    cos_out[t] = (float)cos(ang);
+    sin_out[t] = (float)sin(ang);
+  }
+}
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive scan of one value per thread over the 1024-thread block; returns the
+// exclusive prefix and writes the block total to *total.
+__device__ int block_exclusive_scan(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    const int c = sh[w];
+    if (w < wave) before += c;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void qlist_kernel(
+    const int32_t* __restrict__ row_of, const int32_t* __restrict__ cu, int n, int K, int S,
+    int T, int QR, int max_chunks, int4* __restrict__ qinfo, int32_t* __restrict__ qstart,
+    int2* __restrict__ chunks, int32_t* __restrict__ nchunks) {
+  __shared__ int sh[kScanThreads / 64];
+  constexpr int kItems = 8;  // contiguous anchors per thread per chunk
+  int carry = 0;
+  for (int base = 0; base < n; base += kScanThreads * kItems) {
+    const int p0 = base + threadIdx.x * kItems;
+    int cnt[kItems];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int p = p0 + i;
+      int c = 0;
+      if (p < n)
+        while (c < K && row_of[(size_t)c * n + p] >= 0) ++c;  // nested: depths 0..c-1
+      cnt[i] = c;
+      mine += c;
+    }
+    int total;
+    int start = carry + block_exclusive_scan(mine, sh, &total);
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) {
+      const int p = p0 + i;
+      if (p >= n) break;
+      qstart[p] = start;
+      const int s = min(max(upper_index(cu, S + 1, p), 0), S);
+      const int lo = cu[s];
+      for (int d = 0; d < cnt[i]; ++d)
+        if (start + d < T) qinfo[start + d] = make_int4(row_of[(size_t)d * n + p], p, d, lo);
+      start += cnt[i];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) qstart[n] = min(carry, T);
+  __threadfence();
+  __syncthreads();
+
+  // Chunks of at most QR consecutive list entries that never cross a sequence: chunk
+  // table entries (first entry, entry count), sequence after sequence.
+  int ccarry = 0;
+  for (int base = 0; base < S; base += kScanThreads) {
+    const int s = base + threadIdx.x;
+    int first = 0, rows = 0, cnt = 0;
+    if (s < S) {
+      const int a = min(max(cu[s], 0), n), b = min(max(cu[s + 1], 0), n);
+      first = qstart[a];
+      rows = max(qstart[b] - first, 0);
+      cnt = (rows + QR - 1) / QR;
+    }
+    int total;
+    const int at = ccarry + block_exclusive_scan(cnt, sh, &total);
+    for (int i = 0; i < cnt; ++i)
+      if (at + i < max_chunks) chunks[at + i] = make_int2(first + i * QR, min(QR, rows - i * QR));
+    ccarry += total;
+  }
+  if (threadIdx.x == 0) *nchunks = min(ccarry, max_chunks);
+}
+
+// One thread per (row, head, 8-wide chunk of the first half of the head dimension).
+__global__ __launch_bounds__(256) void rope_rotate_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ depth_off,
+    const int32_t* __restrict__ cu, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const float* __restrict__ cosT, const float* __restrict__ sinT, uint16_t* __restrict__ qr,
+    uint16_t* __restrict__ kr, int n, int K, int S, int T, int Hq, int Hkv, int D, int max_pos) {
+  const int half = D / 2, cpr = half / 8;  // chunks per head
+  const int heads = Hq + Hkv;
+  const size_t total = (size_t)T * heads * cpr;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
+       t += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(t % cpr);
+    const int h = (int)((t / cpr) % heads);
+    const int r = (int)(t / ((size_t)cpr * heads));
+    const int d = min(max(upper_index(depth_off, K + 1, r), 0), K - 1);
+    const int p = min(max(idx[r], 0), n - 1);
+    const int s = min(max(upper_index(cu, S + 1, p), 0), S);
+    const int pos = min(max(p - cu[s] + d, 0), max_pos);
+    const uint16_t* src = (h < Hq) ? q + ((size_t)r * Hq + h) * D : k + ((size_t)r * Hkv + (h - Hq)) * D;
+    uint16_t* dst = (h < Hq) ? qr + ((size_t)r * Hq + h) * D : kr + ((size_t)r * Hkv + (h - Hq)) * D;
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + c * 8);
+    const u32x4 x2 = *reinterpret_cast<const u32x4*>(src + half + c * 8);
+    const floatx4* cp = reinterpret_cast<const floatx4*>(cosT + (size_t)pos * half + c * 8);
+    const floatx4* sp = reinterpret_cast<const floatx4*>(sinT + (size_t)pos * half + c * 8);
+    const floatx4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+    u32x4 y1, y2;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t o1 = 0, o2 = 0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int j = w * 2 + e;
+        const float a = bf16_bits_to_f32((x1[w] >> (16 * e)) & 0xFFFFu);
+        const float b = bf16_bits_to_f32((x2[w] >> (16 * e)) & 0xFFFFu);
+        const float cs = (j < 4) ? c0[j] : c1[j - 4];
+        const float sn = (j < 4) ? s0[j] : s1[j - 4];
+        o1 |= (uint32_t)f32_to_bf16_bits(a * cs - b * sn) << (16 * e);
+        o2 |= (uint32_t)f32_to_bf16_bits(b * cs + a * sn) << (16 * e);
+      }
+      y1[w] = o1;
+      y2[w] = o2;
+    }
+    *reinterpret_cast<u32x4*>(dst + c * 8) = y1;
+    *reinterpret_cast<u32x4*>(dst + half + c * 8) = y2;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
+                                                          uint16_t* __restrict__ vt, int n, int Hkv,
+                                                          int ntiles) {
+  __shared__ uint16_t tile[32][D + 8];
+  const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  constexpr int cpr = D / 8;
+  for (int q = tid; q < 32 * cpr; q += 256) {
+    const int key = q / cpr, c = q % cpr, pos = t * 32 + key;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (pos < n) val = *reinterpret_cast<const u32x4*>(v + ((size_t)pos * Hkv + g) * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      tile[key][c * 8 + 2 * w] = (uint16_t)(val[w] & 0xFFFFu);
+      tile[key][c * 8 + 2 * w + 1] = (uint16_t)(val[w] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* out = vt + ((size_t)g * ntiles + t) * D * 32;
+  for (int q = tid; q < D * 4; q += 256) {
+    const int d = q >> 2, chunk = q & 3;
+    uint16_t vals[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // element e of chunk (2*g16 + h) holds key 16*g16 + 8*(e/4) + 4*h + e%4
+      const int g16 = chunk >> 1, h = chunk & 1;
+      const int key = 16 * g16 + 8 * (e >> 2) + 4 * h + (e & 3);
+      vals[e] = tile[key][d];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) o[w] = (uint32_t)vals[2 * w] | ((uint32_t)vals[2 * w + 1] << 16);
+    *reinterpret_cast<u32x4*>(out + (size_t)d * 32 + chunk * 8) = o;
+  }
+}
+
+template <typename F>
+hipError_t launch_for_d(int D, F&& f) {
+  switch (D) {
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    case 256: return f(std::integral_constant<int, 256>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(int32_t head_dim, double theta, int32_t max_pos, float* cos_out,
+                             float* sin_out, hipStream_t stream) {
+  const int half = head_dim / 2;
+  const size_t total = (size_t)(max_pos + 1) * half;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, stream, cos_out, sin_out, half,
+                     head_dim, theta, max_pos);
+  return hipGetLastError();
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Upper bound on the chunk count: every sequence adds at most one partial chunk, and a
+// sequence holds at least one anchor, so S <= n.
+int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv) {
+  const int QR = 256 / std::max(1, Hq / std::max(1, Hkv));
+  return (int)((T + QR - 1) / QR + n);
+}
+
+AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D) {
+  AttnLayout L;
+  const size_t ntiles = (size_t)((n + 31) / 32);
+  size_t off = 0;
+  L.qinfo = off;  off += align256((size_t)T * sizeof(int4));
+  L.qstart = off; off += align256((size_t)(n + 1) * sizeof(int32_t));
+  L.qrot = off;   off += align256((size_t)T * Hq * D * 2);
+  L.krot = off;   off += align256((size_t)T * Hkv * D * 2);
+  L.vt = off;     off += align256(ntiles * 32 * Hkv * D * 2);
+  L.max_chunks = attn_max_chunks(n, T, Hq, Hkv);
+  L.chunks = off; off += align256((size_t)L.max_chunks * sizeof(int2));
+  L.nchunks = off; off += 256;
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int32_t* depth_off,
+                               const int32_t* row_of, const int32_t* cu_seqlens,
+                               const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const float* rope_cos, const float* rope_sin, char* ws,
+                               hipStream_t stream) {
+  const AttnLayout L = attn_layout(a.n, a.T, a.Hq, a.Hkv, a.D);
+  int4* qinfo = reinterpret_cast<int4*>(ws + L.qinfo);
+  int32_t* qstart = reinterpret_cast<int32_t*>(ws + L.qstart);
+  uint16_t* qr = reinterpret_cast<uint16_t*>(ws + L.qrot);
+  uint16_t* kr = reinterpret_cast<uint16_t*>(ws + L.krot);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
+
+  int2* chunks = reinterpret_cast<int2*>(ws + L.chunks);
+  int32_t* nchunks = reinterpret_cast<int32_t*>(ws + L.nchunks);
+  hipLaunchKernelGGL(qlist_kernel, dim3(1), dim3(kScanThreads), 0, stream, row_of, cu_seqlens, a.n,
+                     a.K, a.S, a.T, 256 / (a.Hq / a.Hkv), L.max_chunks, qinfo, qstart, chunks,
+                     nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const size_t work = (size_t)a.T * (a.Hq + a.Hkv) * (a.D / 16);
+  const int blocks = (int)std::min<size_t>((work + 255) / 256, 1 << 20);
+  hipLaunchKernelGGL(rope_rotate_kernel, dim3(blocks), dim3(256), 0, stream, idx, depth_off,
+                     cu_seqlens, q, k, rope_cos, rope_sin, qr, kr, a.n, a.K, a.S, a.T, a.Hq, a.Hkv,
+                     a.D, a.max_pos);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int ntiles = (a.n + 31) / 32;
+  return launch_for_d(a.D, [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    hipLaunchKernelGGL(v_transpose_kernel<D>, dim3(ntiles, a.Hkv), dim3(256), 0, stream, v, vt,
+                       a.n, a.Hkv, ntiles);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace peagle

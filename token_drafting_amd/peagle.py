@@ -1,0 +1,203 @@
+"""ctypes binding of libpeagle (include/peagle.h).
+
+Argument marshalling only: every step of the draft forward runs in the library's HIP
+kernels. torch provides device memory and the stream; tensors are passed by
+``data_ptr()`` and work is enqueued on ``torch.cuda.current_stream()``.
+
+bf16 tensors may be ``torch.bfloat16`` or ``torch.uint16``/``int16`` holding raw bits.
+The library must be built (``python -m token_drafting_amd.build``); loading fails loudly
+otherwise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpeagle.so")
+_lib = None
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4
+MAX_DEPTHS = 64
+
+_i32, _i64, _u64, _f32, _f64, _p, _sz = (C.c_int32, C.c_int64, C.c_uint64, C.c_float,
+                                         C.c_double, C.c_void_p, C.c_size_t)
+_ATTN = [_i64, _i32, _i64, _p, _p, _p, _p, _i32, _p, _p, _p, _i32, _i32, _i32, _f32, _p, _p,
+         _i32, _p, _p, _p, _sz, _p]
+SIGNATURES = {
+    "peagle_status_string": ([_i32], C.c_char_p),
+    "peagle_version": ([], _i32),
+    "peagle_cod_counts": ([_i64, _i32, _f64, _f64, _p, _p], _i32),
+    "peagle_cod_select": ([_i64, _i32, _f64, _f64, _u64, _p, _i32, _p, _p, _p, _p, _p], _i32),
+    "peagle_fuse_inputs": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32, _i32,
+                            _p, _p, _p], _i32),
+    "peagle_rope_table": ([_i32, _f64, _i32, _p, _p, _p], _i32),
+    "peagle_draft_attn_workspace_bytes": ([_i64, _i64, _i32, _i32, _i32], _sz),
+    "peagle_draft_attn_fwd": (_ATTN, _i32),
+    "peagle_draft_attn_prepare": (_ATTN, _i32),
+    "peagle_draft_attn_core": (_ATTN, _i32),
+    "peagle_accept_prefix": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _p], _i32),
+}
+
+
+class PeagleError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({lib().peagle_status_string(status).decode()})")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> C.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m token_drafting_amd.build`")
+        h = C.CDLL(_LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.argtypes, f.restype = args, res
+        _lib = h
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise PeagleError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    return t
+
+
+# ---------------------------------------------------------------- COD
+def cod_counts(n: int, K: int, r: float, r_min: float) -> tuple[list, int]:
+    m = (C.c_int64 * K)()
+    T = C.c_int64()
+    _check("peagle_cod_counts", lib().peagle_cod_counts(n, K, r, r_min, m, C.byref(T)))
+    return list(m), T.value
+
+
+def cod_select(n: int, K: int, r: float, r_min: float, seed: int, cu_seqlens: torch.Tensor):
+    """Returns dict(m, T, idx, depth_off, cu_seqlens_d [K,S+1], row_of [K,n])."""
+    _dev(cu_seqlens, "cu_seqlens")
+    m, T = cod_counts(n, K, r, r_min)
+    S = cu_seqlens.numel() - 1
+    dev = cu_seqlens.device
+    out = dict(m=m, T=T,
+               idx=torch.empty(T, dtype=torch.int32, device=dev),
+               depth_off=torch.empty(K + 1, dtype=torch.int32, device=dev),
+               cu_seqlens_d=torch.empty((K, S + 1), dtype=torch.int32, device=dev),
+               row_of=torch.empty((K, n), dtype=torch.int32, device=dev))
+    cod_select_into(n, K, r, r_min, seed, cu_seqlens, out)
+    return out
+
+
+def cod_select_into(n, K, r, r_min, seed, cu_seqlens, out):
+    S = cu_seqlens.numel() - 1
+    _check("peagle_cod_select", lib().peagle_cod_select(
+        n, K, r, r_min, seed & ((1 << 64) - 1), _ptr(cu_seqlens), S, _ptr(out["idx"]),
+        _ptr(out["depth_off"]), _ptr(out["cu_seqlens_d"]), _ptr(out["row_of"]), _stream()))
+
+
+# ---------------------------------------------------------------- fuse
+def fuse_inputs(n, K, T, idx, aux, fc_weight, mask_hidden, tokens, embed, ptd_token_id,
+                hidden_out=None, embed_out=None):
+    H, A = fc_weight.shape
+    vocab = embed.shape[0]
+    for t, name in ((idx, "idx"), (aux, "aux"), (fc_weight, "fc_weight"),
+                    (mask_hidden, "mask_hidden"), (tokens, "tokens"), (embed, "embed")):
+        _dev(t, name)
+    dev = aux.device
+    if hidden_out is None:
+        hidden_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if embed_out is None:
+        embed_out = torch.empty((T, H), dtype=embed.dtype, device=dev)
+    _check("peagle_fuse_inputs", lib().peagle_fuse_inputs(
+        n, K, T, _ptr(idx), _ptr(aux), A, _ptr(fc_weight), _ptr(mask_hidden), _ptr(tokens),
+        _ptr(embed), vocab, ptd_token_id, H, _ptr(hidden_out), _ptr(embed_out), _stream()))
+    return hidden_out, embed_out
+
+
+# ---------------------------------------------------------------- RoPE
+def rope_table(head_dim: int, theta: float, max_pos: int, device="cuda"):
+    cos = torch.empty((max_pos + 1, head_dim // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check("peagle_rope_table", lib().peagle_rope_table(head_dim, theta, max_pos, _ptr(cos),
+                                                        _ptr(sin), _stream()))
+    return cos, sin
+
+
+def rope_max_pos(n: int, K: int) -> int:
+    """Largest position any draft row can take: (n - 1) + (K - 1)."""
+    return n + K - 2
+
+
+# ---------------------------------------------------------------- attention
+def attn_workspace_bytes(n, T, Hq, Hkv, D) -> int:
+    return int(lib().peagle_draft_attn_workspace_bytes(n, T, Hq, Hkv, D))
+
+
+def _attn_args(n, K, sel, cu_seqlens, q, k, v, cos, sin, out, lse, ws, scale):
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    S = cu_seqlens.numel() - 1
+    return (n, K, T, _ptr(sel["idx"]), _ptr(sel["depth_off"]), _ptr(sel["row_of"]),
+            _ptr(cu_seqlens), S, _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, D,
+            float(scale if scale is not None else 1.0 / math.sqrt(D)), _ptr(cos), _ptr(sin),
+            cos.shape[0] - 1, _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream())
+
+
+def draft_attn(n, K, sel, cu_seqlens, q, k, v, cos, sin, out=None, lse=None, workspace=None,
+               scale=None, phase="fwd"):
+    """phase: "fwd" (prepare + core), "prepare" or "core"."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (cos, "rope_cos"), (sin, "rope_sin")):
+        _dev(t, name)
+    T, Hq, D = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(attn_workspace_bytes(n, T, Hq, k.shape[1], D), dtype=torch.uint8,
+                                device=dev)
+    fn = {"fwd": "peagle_draft_attn_fwd", "prepare": "peagle_draft_attn_prepare",
+          "core": "peagle_draft_attn_core"}[phase]
+    _check(fn, getattr(lib(), fn)(*_attn_args(n, K, sel, cu_seqlens, q, k, v, cos, sin, out,
+                                               lse, workspace, scale)))
+    return out, lse, workspace
+
+
+# ---------------------------------------------------------------- verify
+def accept_prefix(draft_logits, target_logits, draft_tok=None, target_tok=None, accept_len=None):
+    _dev(draft_logits, "draft_logits")
+    _dev(target_logits, "target_logits")
+    N, K, V = draft_logits.shape
+    dev = draft_logits.device
+    if draft_tok is None:
+        draft_tok = torch.empty((N, K), dtype=torch.int32, device=dev)
+    if target_tok is None:
+        target_tok = torch.empty((N, K), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(N, dtype=torch.int32, device=dev)
+    _check("peagle_accept_prefix", lib().peagle_accept_prefix(
+        N, K, V, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tok), _ptr(target_tok),
+        _ptr(accept_len), _stream()))
+    return draft_tok, target_tok, accept_len
