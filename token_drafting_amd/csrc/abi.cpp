@@ -89,7 +89,7 @@ int run_prepare(const AttnCall& c) {
 }
 
 int run_core(const AttnCall& c) {
-  return status_of(launch_attn_core(c.a, c.q, c.k, c.v, c.cs, c.sn, c.out, c.lse, c.ws, c.stream));
+  return status_of(launch_attn_core(c.a, c.v, c.out, c.lse, c.ws, c.stream));
 }
 
 }  // namespace

@@ -10,13 +10,18 @@
 // Work decomposition. Rows are visited in anchor-major order (all depths of anchor 0,
 // then of anchor 1, ...; built by qlist_kernel). A workgroup owns a chunk of up to
 // QR = 256/G consecutive rows of that list, never crossing a packed sequence, for all G
-// q heads of one kv head: 256 query slots, roughly 25 anchors and all their depths at
-// K=4, G=4. Every row of the chunk reads a
-// prefix of the same depth-0 K/V, so each K/V tile is loaded to LDS once and used by
-// all 256 slots (all depths, all heads of the group). Tiles wholly inside every row's
-// range run unmasked; the few at the chunk's edge are masked per element; tiles past
-// the last anchor are never visited. The diagonal keys of the chunk's anchors are a
-// short contiguous run of the anchor-major list, processed as extra masked tiles.
+// q heads of one kv head: 256 query slots (4 waves of 64 in the main kernel), roughly
+// 25 anchors and all their depths at K=4, G=4. Every row of the chunk reads a prefix of the same depth-0
+// K/V, so each K/V tile is loaded to LDS once and used by all 256 slots (all depths, all
+// heads of the group). Tiles wholly inside every row's range run unmasked; the one or
+// two at the chunk's edge are masked per element; tiles past the last anchor are never
+// visited. The diagonal keys of the chunk's anchors are a short contiguous run of the
+// anchor-major list, processed as extra masked tiles.
+//
+// Staging. K and V^T tiles go global -> LDS with global_load_lds_dwordx4 (no register
+// round trip) into two LDS buffers: tile t+1 streams in while tile t is computed, one
+// barrier per tile. The loop is unrolled by two so each buffer is a distinct static
+// array and the compiler does not make LDS reads wait on the other buffer's loads.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16). Scores are computed transposed,
 // S^T = K * Q^T, so a lane holds one query column and 16 of the 32 keys of a tile: the
@@ -26,17 +31,28 @@
 // group are taken in the order (0-3, 8-11 | 4-7, 12-15); V^T tiles are stored in that
 // order (v_transpose_kernel), so each PV operand is one 16-byte LDS read.
 //
-// Softmax: base-2 exponent with the 1/sqrt(D)*log2(e) factor folded into one FMA; the
-// running max is only raised (and O, l rescaled) when a tile's max exceeds it by more
-// than 8, so P <= 2^8 and the rescale of the large O accumulator is rare.
+// Softmax: base-2 exponent with the 1/sqrt(D)*log2(e) factor folded into one FMA. The
+// main kernel fixes each row's reference max m at its first tile (which holds the first
+// key of the row's sequence, so it is finite) and never rescales: P = 2^(s - m) may grow
+// above 1 but stays far from fp32/bf16 overflow as long as the row's softmax sum stays
+// below 2^64, and floating point keeps the same relative precision at any scale. The O
+// accumulators are then touched only by MFMAs inside the loop and stay in AGPRs. A row
+// whose sum exceeds 2^64 (a later score more than ~40 above the first tile's maximum,
+// in base-2 units) flags its chunk, and the second kernel recomputes the chunk with a
+// rescaling online softmax.
 //
 // Precision. Rounding q', k' and P to bf16 perturbs each score by ~1e-3 and each weight
 // by up to 2^-9; for a row whose output mixes only a handful of keys that moves it by
 // up to ~1e-2 (outputs there reach |v| ~ 5). Chunks whose context span is short
-// (<= kShortSpan keys, the first anchors of each sequence) therefore run an exact-split
-// variant: q' = q_hi + q_lo and k' = k_hi + k_lo in bf16 (three MFMAs per step for
-// S^T), P = P_hi + P_lo (two MFMAs for PV), with q', k' rotated in fp32 from the
-// pre-RoPE inputs. Rows with many keys average the rounding out and take the plain path.
+// (<= kShortSpan keys: the first anchors of each sequence) run in the second kernel,
+// which also carries k' = k_hi + k_lo (k_lo from the RoPE kernel, two MFMAs per step of
+// S^T) and P = P_hi + P_lo (two MFMAs per step of PV); q' stays bf16. Rows with many
+// keys average the rounding out and take the plain path.
+//
+// LDS layouts. K tiles: one 16-byte-padded row per key (stride 2D + 16 bytes), so the
+// 32 keys a half-wave reads at one head-dim offset fall in distinct bank groups and a
+// lane's 16 k-step reads share one base address. V^T tiles: rows of 32 keys (64 bytes),
+// 16-byte chunk index XOR ((d >> 1) & 3).
 #include <algorithm>
 #include <type_traits>
 
@@ -47,117 +63,136 @@ namespace peagle {
 
 namespace {
 
-constexpr int KT = 32;             // keys per tile
+constexpr int KT = 32;  // keys per tile
+constexpr int kMainNT = 1;   // query columns of 32 per wave in the main kernel
+constexpr int kExactNT = 1;  // and in the exact / redo kernel
 constexpr float kRescaleLog2 = 8.f;
-constexpr int kShortSpan = 96;     // context span (keys) up to which a chunk runs exact-split
+constexpr float kSumLimit = 18446744073709551616.f;  // 2^64: above it a row is redone
 
 template <int D, int NT>
 struct Cfg {
-  static constexpr int kThreads = 512 / NT;          // 256 query slots per workgroup
-  static constexpr int KROW = D * 2;                 // bytes of one K row in LDS
-  static constexpr int KBYTES = KT * KROW;
-  static constexpr int VBYTES = D * KT * 2;          // V^T tile: D rows x 32 keys
-  static constexpr int KCH = KT * (D / 8);           // 16-byte chunks of a K tile
-  static constexpr int VCH = D * (KT / 8);           // 16-byte chunks of a V^T tile
-  static constexpr int NKC = (KCH + kThreads - 1) / kThreads;  // per thread (last may idle)
-  static constexpr int NVC = (VCH + kThreads - 1) / kThreads;
-  static constexpr int DK = D / 16;                  // k-steps of S^T
-  static constexpr int MT = D / 32;                  // 32-row M tiles of O^T
+  static constexpr int TH = 512 / NT;             // 256 query slots per workgroup
+  static constexpr int WAVES = TH / 64;
+  static constexpr int KROW = D * 2 + 16;         // padded K row
+  static constexpr int KBUF = (KT * KROW + 1023) / 1024 * 1024;  // whole DMA blocks
+  static constexpr int VBYTES = D * KT * 2;       // V^T tile: D rows x 32 keys
+  static constexpr int KCH = KT * (D / 8);        // 16-byte chunks of a K tile
+  static constexpr int DK = D / 16;               // k-steps of S^T
+  static constexpr int MT = D / 32;               // 32-row M tiles of O^T
 };
 
-__device__ __forceinline__ int k_off(int key, int chunk, int krow) {
-  return key * krow + ((chunk ^ (key & 7)) << 4);
-}
 __device__ __forceinline__ int v_off(int d, int chunk) {
   return d * (KT * 2) + ((chunk ^ ((d >> 1) & 3)) << 4);
 }
 
-__device__ __forceinline__ float bf16_elem(const u32x4& w, int e) {
-  return bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+// s_waitcnt vmcnt(0): this wave's LDS-DMA writes have landed (expcnt/lgkmcnt not waited).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-// fp32 RoPE of the 8 head-dim elements [d0, d0+8) of one pre-RoPE bf16 head row at
-// position pos (rotate-half: element j pairs with j + D/2).
-template <int D>
-__device__ __forceinline__ void rope8(const uint16_t* __restrict__ row, const float* __restrict__ cosT,
-                                      const float* __restrict__ sinT, int pos, int d0, float out[8]) {
-  constexpr int H2 = D / 2;
-  const bool first = d0 < H2;
-  const int j0 = first ? d0 : d0 - H2;
-  const u32x4 x = *reinterpret_cast<const u32x4*>(row + d0);
-  const u32x4 y = *reinterpret_cast<const u32x4*>(row + (first ? d0 + H2 : d0 - H2));
-  const floatx4* cp = reinterpret_cast<const floatx4*>(cosT + (size_t)pos * H2 + j0);
-  const floatx4* sp = reinterpret_cast<const floatx4*>(sinT + (size_t)pos * H2 + j0);
-  const floatx4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float a = bf16_elem(x, e), b = bf16_elem(y, e);
-    const float cs = e < 4 ? c0[e] : c1[e - 4], sn = e < 4 ? s0[e] : s1[e - 4];
-    out[e] = first ? a * cs - b * sn : a * cs + b * sn;
-  }
-}
+struct AttnParams {
+  const int4* qinfo;
+  const int32_t* qstart;
+  const int2* chunks;
+  const int32_t* nchunks;
+  const int32_t* seq_chunk;
+  int32_t* flags;  // [chunk * Hkv + g]: the main kernel asks for a redo
+  const uint16_t* qr;
+  const uint16_t* kr;
+  const uint16_t* kr_lo;
+  const uint16_t* vt;
+  const uint16_t* v;
+  float* out;
+  float* lse;
+  int n, T, S, Hq, Hkv, G, QR, ntiles, exact_per_seq, max_chunks;
+  float c_log2;
+};
 
-// EXACT = false runs the chunks with a long context span, EXACT = true the short ones;
-// each returns at once for the other kind, so the two launches together cover all.
-template <int D, int NT, bool EXACT>
-__global__ __launch_bounds__(512 / NT) void attn_core_kernel(
-    const int4* __restrict__ qinfo, const int32_t* __restrict__ qstart,
-    const int2* __restrict__ chunks, const int32_t* __restrict__ nchunks_dev,
-    const uint16_t* __restrict__ qr, const uint16_t* __restrict__ kr,
-    const uint16_t* __restrict__ vt, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ q_in, const uint16_t* __restrict__ k_in,
-    const float* __restrict__ cosT, const float* __restrict__ sinT, float* __restrict__ out,
-    float* __restrict__ lse, int n, int T, int Hq, int Hkv, int G, int QR, int ntiles,
-    int max_pos, float c_log2) {
+// EXACT = false: the main kernel, every chunk with a long context span. EXACT = true:
+// chunks with a short span, and chunks the main kernel flagged for a redo.
+template <int D, bool EXACT>
+__global__ __launch_bounds__(512 / (EXACT ? kExactNT : kMainNT)) void attn_core_kernel(
+    const AttnParams p) {
+  constexpr int NT = EXACT ? kExactNT : kMainNT;
   using C = Cfg<D, NT>;
-  constexpr int TH = C::kThreads;
-  __shared__ __attribute__((aligned(16))) char Ks[C::KBYTES];
-  __shared__ __attribute__((aligned(16))) char Kl[EXACT ? C::KBYTES : 16];  // k_lo (exact split)
-  __shared__ __attribute__((aligned(16))) char Vs[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char Ks0[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char Ks1[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char Vs0[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char Vs1[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char Kl0[EXACT ? C::KBUF : 16];
+  __shared__ __attribute__((aligned(1024))) char Kl1[EXACT ? C::KBUF : 16];
   __shared__ int s_range[6];
   __shared__ int s_kp[KT], s_kd[KT];
+  __shared__ int s_redo;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, half = lane >> 5;
   const int bid = blockIdx.x;
-  // Chunks are listed sequence by sequence, anchors ascending: the last ones have the
-  // longest prefixes, so they are dispatched first. The grid is sized for the largest
-  // possible chunk count; blocks past the actual count exit.
-  const int chunk = *nchunks_dev - 1 - bid / Hkv;
-  if (chunk < 0) return;
-  const int g = bid % Hkv;
-  const int2 ch = chunks[chunk];
+  const int g = bid % p.Hkv;
+  int chunk;
+  bool redo = false;
+  if constexpr (EXACT) {
+    const int r = bid / p.Hkv;
+    const int n_short = p.S * p.exact_per_seq;
+    if (r < n_short) {  // one of the first chunks of a sequence
+      const int s = r / p.exact_per_seq, j = r % p.exact_per_seq;
+      chunk = p.seq_chunk[s] + j;
+      if (chunk >= p.seq_chunk[s + 1]) return;
+    } else {            // a chunk the main kernel flagged
+      chunk = r - n_short;
+      if (chunk >= *p.nchunks || p.flags[chunk * p.Hkv + g] == 0) return;
+      redo = true;
+    }
+  } else {
+    // Chunks are listed sequence by sequence, anchors ascending: the last ones have the
+    // longest prefixes, so they are dispatched first. The grid is sized for the largest
+    // possible chunk count; blocks past the actual count exit.
+    chunk = *p.nchunks - 1 - bid / p.Hkv;
+    if (chunk < 0) return;
+  }
+  const int n = p.n, T = p.T, Hkv = p.Hkv;
+  const int2 ch = p.chunks[chunk];
   const int j0 = min(max(ch.x, 0), T - 1);
   const int jn = min(max(ch.y, 1), T - j0);
 
   if (tid == 0) {
-    const int4 first = qinfo[j0], last = qinfo[j0 + jn - 1];
+    const int4 first = p.qinfo[j0], last = p.qinfo[j0 + jn - 1];
     const int p_first = min(max(first.y, 0), n - 1), p_last = min(max(last.y, 0), n - 1);
     const int lo_first = min(max(first.w, 0), p_first), lo_last = min(max(last.w, 0), p_last);
-    s_range[0] = lo_first;                // first key of any row
-    s_range[1] = p_last;                  // last key of any row
-    s_range[2] = lo_last;                 // keys in [lo_last, p_first] are seen by every row
+    s_range[0] = lo_first;  // first key of any row
+    s_range[1] = p_last;    // last key of any row
+    s_range[2] = lo_last;   // keys in [lo_last, p_first] are seen by every row
     s_range[3] = p_first;
-    s_range[4] = min(max(qstart[p_first], 0), T);      // diagonal keys: entries of the
-    s_range[5] = min(max(qstart[p_last + 1], 0), T);   // chunk's anchors in the list
+    s_range[4] = min(max(p.qstart[p_first], 0), T);     // diagonal keys: entries of the
+    s_range[5] = min(max(p.qstart[p_last + 1], 0), T);  // chunk's anchors in the list
+    s_redo = 0;
   }
+  __syncthreads();
+  const int k_lo = s_range[0], k_hi = s_range[1], full_lo = s_range[2], full_hi = s_range[3];
+  const int dg_lo = s_range[4], dg_hi = s_range[5];
+  const bool is_short = (k_hi - k_lo + 1) <= kShortSpan;  // uniform over the workgroup
+  if (EXACT ? (!is_short && !redo) : is_short) return;
 
-  // Query slots of this lane: NT columns of 32.
+  // Query slots of this lane: NT columns of 32 (lanes l and l+32 share a column, each
+  // holding 16 of the 32 keys of a tile).
   int q_row[NT], q_head[NT], q_p[NT], q_d[NT], q_lo[NT];
   bool q_on[NT];
   bf16x8 qf[NT][C::DK];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int slot = wave * 32 * NT + nt * 32 + r32;
-    const int rl = slot % QR, hl = slot / QR;
+    const int rl = slot % p.QR, hl = slot / p.QR;
     q_on[nt] = rl < jn;
-    const int4 qi = qinfo[j0 + min(rl, jn - 1)];
+    const int4 qi = p.qinfo[j0 + min(rl, jn - 1)];
     q_row[nt] = min(max(qi.x, 0), T - 1);
     q_p[nt] = min(max(qi.y, 0), n - 1);
     q_d[nt] = qi.z;
     q_lo[nt] = min(max(qi.w, 0), q_p[nt]);
-    q_head[nt] = g * G + hl;
-    const uint16_t* qrow = qr + ((size_t)q_row[nt] * Hq + q_head[nt]) * D + half * 8;
+    q_head[nt] = g * p.G + hl;
+    const uint16_t* qrow = p.qr + ((size_t)q_row[nt] * p.Hq + q_head[nt]) * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < C::DK; ++kk)
       qf[nt][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kk * 16));
@@ -174,45 +209,27 @@ __global__ __launch_bounds__(512 / NT) void attn_core_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[nt][mt][r] = 0.f;
   }
-  __syncthreads();
-  const int k_lo = s_range[0], k_hi = s_range[1], full_lo = s_range[2], full_hi = s_range[3];
-  const int dg_lo = s_range[4], dg_hi = s_range[5];
-  const bool precise = (k_hi - k_lo + 1) <= kShortSpan;   // uniform over the workgroup
-  if (precise != EXACT) return;
 
-  // One tile of scores -> online softmax -> PV. mode 0: no mask, 1: context range,
-  // 2: diagonal keys (meta in s_kp / s_kd). `exact`: hi/lo split products.
-  auto compute = [&](int mode, int key0) {
-    constexpr bool exact = EXACT;
+  // One tile: S^T = K Q^T -> mask -> softmax weights -> O^T += V^T P^T.
+  // mode 0: no mask, 1: context range, 2: diagonal keys (meta in s_kp / s_kd).
+  // SET_MAX: the main kernel's first tile fixes the reference max.
+  auto compute = [&](const char* Ks, const char* Kl, const char* Vs, int mode, int key0,
+                     bool set_max) {
     floatx16 s[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
-    if constexpr (!exact) {
+    const char* kbase = Ks + r32 * C::KROW + half * 16;
 #pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + k_off(r32, kk * 2 + half, C::KROW)));
+    for (int kk = 0; kk < C::DK; ++kk) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + kk * 32));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(a, qf[nt][kk], s[nt]);
-      }
-    } else {
-      for (int kk = 0; kk < C::DK; ++kk) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + k_off(r32, kk * 2 + half, C::KROW)));
-        const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(Kl + k_off(r32, kk * 2 + half, C::KROW)));
+      for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(a, qf[nt][kk], s[nt]);
+      if constexpr (EXACT) {
+        const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(Kl + (kbase - Ks) + kk * 32));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          float qv[8];
-          const int qpos = min(q_p[nt] - q_lo[nt] + q_d[nt], max_pos);
-          rope8<D>(q_in + ((size_t)q_row[nt] * Hq + q_head[nt]) * D, cosT, sinT, qpos,
-                   kk * 16 + half * 8, qv);
-          bf16x8 ql;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ql[e] = (__bf16)(qv[e] - (float)qf[nt][kk][e]);
-          s[nt] = mfma32(a, qf[nt][kk], s[nt]);
-          s[nt] = mfma32(al, qf[nt][kk], s[nt]);
-          s[nt] = mfma32(a, ql, s[nt]);
-        }
+        for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(al, qf[nt][kk], s[nt]);
       }
     }
     if (mode == 1) {
@@ -233,158 +250,110 @@ __global__ __launch_bounds__(512 / NT) void attn_core_kernel(
           if (kp != q_p[nt] || kd < 1 || kd > q_d[nt]) s[nt][r] = -INFINITY;
       }
     }
-    float m_new[NT];
-    bool need = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float mx = s[nt][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      m_new[nt] = fmaxf(m_run[nt], mx * c_log2);
-      need |= m_new[nt] > m_run[nt] + kRescaleLog2;
-    }
-    if (__any(need)) {
+    if (EXACT || set_max) {
+      float m_new[NT];
+      bool need = false;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const float alpha = (m_new[nt] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new[nt]);
-        l_run[nt] *= alpha;
+        float mx = fmaxf(s[nt][0], s[nt][1]);
 #pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt)
+        for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[nt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        m_new[nt] = fmaxf(m_run[nt], mx * p.c_log2);
+        need |= m_new[nt] > m_run[nt] + kRescaleLog2;
+      }
+      if constexpr (EXACT) {
+        if (__any(need)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[nt][mt][r] *= alpha;
-        m_run[nt] = m_new[nt];
+          for (int nt = 0; nt < NT; ++nt) {
+            const float alpha = (m_new[nt] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new[nt]);
+            l_run[nt] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[nt][mt][r] *= alpha;
+            m_run[nt] = m_new[nt];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) m_run[nt] = m_new[nt];  // O is still zero
       }
     }
     bf16x8 pb[NT][2];
-    float pf[NT][16];
+    [[maybe_unused]] bf16x8 pl[NT][2];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float mu = (m_run[nt] == -INFINITY) ? 0.f : m_run[nt];
       float ls = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(fmaf(s[nt][r], c_log2, -mu));
+        const float pr = __builtin_amdgcn_exp2f(fmaf(s[nt][r], p.c_log2, -mu));
         ls += pr;
-        pf[nt][r] = pr;
         pb[nt][r >> 3][r & 7] = (__bf16)pr;
+        if constexpr (EXACT) pl[nt][r >> 3][r & 7] = (__bf16)(pr - (float)pb[nt][r >> 3][r & 7]);
       }
       l_run[nt] += ls;
     }
-    if constexpr (!exact) {
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+    for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + v_off(mt * 32 + r32, ks * 2 + half)));
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + v_off(mt * 32 + r32, ks * 2 + half)));
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) o[nt][mt] = mfma32(a, pb[nt][ks], o[nt][mt]);
-        }
-    } else {
-      bf16x8 pl[NT][2];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pl[nt][r >> 3][r & 7] = (__bf16)(pf[nt][r] - (float)pb[nt][r >> 3][r & 7]);
-      for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + v_off(mt * 32 + r32, ks * 2 + half)));
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            o[nt][mt] = mfma32(a, pb[nt][ks], o[nt][mt]);
-            o[nt][mt] = mfma32(a, pl[nt][ks], o[nt][mt]);
-          }
-        }
-    }
-  };
-
-  // ---- causal context: depth-0 key tiles ----
-  u32x4 rk[C::NKC], rv[C::NVC];
-  auto load_ctx = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < C::NKC; ++i) {
-      const int q = tid + i * TH, key = q / (D / 8), c = q % (D / 8), pos = t * KT + key;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (q < C::KCH && pos < n) val = *reinterpret_cast<const u32x4*>(kr + ((size_t)pos * Hkv + g) * D + c * 8);
-      rk[i] = val;
-    }
-    const uint16_t* vsrc = vt + ((size_t)g * ntiles + t) * (size_t)(D * KT);
-#pragma unroll
-    for (int i = 0; i < C::NVC; ++i) {
-      const int q = tid + i * TH;
-      if (q < C::VCH) rv[i] = *reinterpret_cast<const u32x4*>(vsrc + q * 8);
-    }
-  };
-  auto store_ctx = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::NKC; ++i) {
-      const int q = tid + i * TH;
-      if (q < C::KCH) *reinterpret_cast<u32x4*>(Ks + k_off(q / (D / 8), q % (D / 8), C::KROW)) = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::NVC; ++i) {
-      const int q = tid + i * TH;
-      if (q < C::VCH) *reinterpret_cast<u32x4*>(Vs + v_off(q >> 2, q & 3)) = rv[i];
-    }
-  };
-  // Exact-split staging: k' rotated in fp32 from the pre-RoPE k at the key's own
-  // position, stored as bf16 hi (Ks) and lo (Kl). `row_pos` gives (row, position) of key
-  // slot `key` or row -1 for an empty slot.
-  auto stage_k_split = [&](auto row_pos) {
-    for (int q = tid; q < C::KCH; q += TH) {
-      const int key = q / (D / 8), c = q % (D / 8);
-      const int2 rp = row_pos(key);
-      u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-      if (rp.x >= 0) {
-        float kv[8];
-        rope8<D>(k_in + ((size_t)rp.x * Hkv + g) * D, cosT, sinT, rp.y, c * 8, kv);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t h2 = 0, l2 = 0;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const float x = kv[2 * w + e];
-            const uint16_t hb = f32_to_bf16_bits(x);
-            h2 |= (uint32_t)hb << (16 * e);
-            l2 |= (uint32_t)f32_to_bf16_bits(x - bf16_bits_to_f32(hb)) << (16 * e);
-          }
-          hi[w] = h2;
-          lo[w] = l2;
+        for (int nt = 0; nt < NT; ++nt) {
+          o[nt][mt] = mfma32(a, pb[nt][ks], o[nt][mt]);
+          if constexpr (EXACT) o[nt][mt] = mfma32(a, pl[nt][ks], o[nt][mt]);
         }
       }
-      *reinterpret_cast<u32x4*>(Ks + k_off(key, c, C::KROW)) = hi;
-      *reinterpret_cast<u32x4*>(Kl + k_off(key, c, C::KROW)) = lo;
+  };
+
+  // ---- causal context: depth-0 key tiles, streamed by LDS DMA ----
+  // A wave moves 1 KB per instruction: lane i fills bytes [16 i, 16 i + 16) of that KB.
+  auto dma_k = [&](const uint16_t* src, int t, char* dst) {
+#pragma unroll
+    for (int i = wave; i < C::KBUF / 1024; i += C::WAVES) {
+      const int P = i * 1024 + lane * 16;
+      const int key = P / C::KROW, off = P - key * C::KROW;
+      const bool real = key < KT && off < D * 2;  // else padding: any valid source
+      const int pos = min(t * KT + (real ? key : 0), n - 1);  // rows past n are masked
+      dma16(src + ((size_t)pos * Hkv + g) * D + (real ? off >> 1 : 0), dst + i * 1024);
     }
+  };
+  auto dma_v = [&](int t, char* dst) {
+    const uint16_t* vsrc = p.vt + ((size_t)g * p.ntiles + t) * (size_t)(D * KT);
+#pragma unroll
+    for (int i = wave; i < C::VBYTES / 1024; i += C::WAVES) {
+      const int P = i * 1024 + lane * 16;
+      const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 1) & 3);
+      dma16(vsrc + d * KT + c * 8, dst + i * 1024);
+    }
+  };
+  auto issue = [&](int t, char* Kd, char* Kld, char* Vd) {
+    dma_k(p.kr, t, Kd);
+    if constexpr (EXACT) dma_k(p.kr_lo, t, Kld);
+    dma_v(t, Vd);
   };
 
   const int t_first = k_lo / KT, t_last = k_hi / KT;
-  if constexpr (!EXACT) {
-    load_ctx(t_first);
-    for (int t = t_first; t <= t_last; ++t) {
-      __syncthreads();
-      store_ctx();
-      __syncthreads();
-      if (t < t_last) load_ctx(t + 1);
+  issue(t_first, Ks0, Kl0, Vs0);
+  for (int t = t_first; t <= t_last; t += 2) {
+    wait_dma();
+    __syncthreads();  // tile t landed in buffer 0; buffer 1 is free
+    if (t + 1 <= t_last) issue(t + 1, Ks1, Kl1, Vs1);
+    {
       const int key0 = t * KT;
       const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
-      compute(full ? 0 : 1, key0);
+      compute(Ks0, Kl0, Vs0, full ? 0 : 1, key0, t == t_first);
     }
-  } else {
-    const int p_first = full_hi, lo_first = k_lo;
-    for (int t = t_first; t <= t_last; ++t) {
-      __syncthreads();
-      load_ctx(t);
-      store_ctx();  // V^T tile (and plain K, overwritten below)
-      __syncthreads();
-      stage_k_split([&](int key) {
-        const int pos = t * KT + key;
-        if (pos < k_lo || pos > k_hi) return make_int2(-1, 0);
-        const int start = pos < p_first ? lo_first : min(max(qinfo[min(max(qstart[pos], 0), T - 1)].w, 0), pos);
-        return make_int2(pos, min(pos - start, max_pos));
-      });
-      __syncthreads();
-      compute(1, t * KT);
+    if (t + 1 > t_last) break;
+    wait_dma();
+    __syncthreads();  // tile t+1 landed in buffer 1; buffer 0 is free
+    if (t + 2 <= t_last) issue(t + 2, Ks0, Kl0, Vs0);
+    {
+      const int key0 = (t + 1) * KT;
+      const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
+      compute(Ks1, Kl1, Vs1, full ? 0 : 1, key0, false);
     }
   }
 
@@ -395,54 +364,47 @@ __global__ __launch_bounds__(512 / NT) void attn_core_kernel(
       const int jk = jb + tid;
       int kp = -1, kd = 0;
       if (jk < dg_hi) {
-        const int4 qi = qinfo[jk];
-        kp = qi.y;
-        kd = qi.z;
+        const int4 e = p.qinfo[jk];
+        kp = e.y;
+        kd = e.z;
       }
       s_kp[tid] = kp;
       s_kd[tid] = kd;
     }
-    for (int q = tid; q < C::KCH; q += TH) {
+    for (int q = tid; q < C::KCH; q += C::TH) {
       const int key = q / (D / 8), c = q % (D / 8), jk = jb + key;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u}, kl = {0u, 0u, 0u, 0u};
       if (jk < dg_hi) {
-        const int row = min(max(qinfo[jk].x, 0), T - 1);
-        kv = *reinterpret_cast<const u32x4*>(kr + ((size_t)row * Hkv + g) * D + c * 8);
-        vv = *reinterpret_cast<const u32x4*>(v + ((size_t)row * Hkv + g) * D + c * 8);
+        const int row = min(max(p.qinfo[jk].x, 0), T - 1);
+        kv = *reinterpret_cast<const u32x4*>(p.kr + ((size_t)row * Hkv + g) * D + c * 8);
+        vv = *reinterpret_cast<const u32x4*>(p.v + ((size_t)row * Hkv + g) * D + c * 8);
+        if constexpr (EXACT) kl = *reinterpret_cast<const u32x4*>(p.kr_lo + ((size_t)row * Hkv + g) * D + c * 8);
       }
-      *reinterpret_cast<u32x4*>(Ks + k_off(key, c, C::KROW)) = kv;
+      *reinterpret_cast<u32x4*>(Ks0 + key * C::KROW + c * 16) = kv;
+      if constexpr (EXACT) *reinterpret_cast<u32x4*>(Kl0 + key * C::KROW + c * 16) = kl;
       // scatter the 8 d-values of this key into the V^T tile (key order as in v_transpose)
       const int vchunk = 2 * (key >> 4) + ((key & 7) >> 2);
       const int elem = 4 * ((key & 15) >> 3) + (key & 3);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = c * 8 + e;
-        const uint16_t val = (uint16_t)((vv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        *reinterpret_cast<uint16_t*>(Vs + v_off(d, vchunk) + elem * 2) = val;
+        *reinterpret_cast<uint16_t*>(Vs0 + v_off(d, vchunk) + elem * 2) =
+            (uint16_t)((vv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
       }
     }
-    if constexpr (EXACT) {
-      __syncthreads();
-      stage_k_split([&](int key) {
-        const int jk = jb + key;
-        if (jk >= dg_hi) return make_int2(-1, 0);
-        const int4 qi = qinfo[jk];
-        const int p = min(max(qi.y, 0), n - 1);
-        const int pos = min(max(p - min(max(qi.w, 0), p) + qi.z, 0), max_pos);
-        return make_int2(min(max(qi.x, 0), T - 1), pos);
-      });
-    }
     __syncthreads();
-    compute(2, 0);
+    compute(Ks0, Kl0, Vs0, 2, 0, false);
   }
 
-  // ---- epilogue: O / l, lse ----
+  // ---- epilogue: O / l, lse; the main kernel flags rows whose sum left the safe range ----
+  bool bad = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lt = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
+    if constexpr (!EXACT) bad |= q_on[nt] && !(lt <= kSumLimit);
     const float inv = 1.f / lt;
     if (q_on[nt]) {
-      float* dst = out + ((size_t)q_row[nt] * Hq + q_head[nt]) * D;
+      float* dst = p.out + ((size_t)q_row[nt] * p.Hq + q_head[nt]) * D;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
@@ -452,43 +414,63 @@ __global__ __launch_bounds__(512 / NT) void attn_core_kernel(
           for (int j = 0; j < 4; ++j) w[j] = o[nt][mt][4 * i + j] * inv;
           *reinterpret_cast<floatx4*>(dst + mt * 32 + 8 * i + 4 * half) = w;
         }
-      if (lse != nullptr && half == 0)
-        lse[(size_t)q_head[nt] * T + q_row[nt]] = (m_run[nt] + __log2f(lt)) * 0.69314718055994531f;
+      if (p.lse != nullptr && half == 0)
+        p.lse[(size_t)q_head[nt] * T + q_row[nt]] = (m_run[nt] + __log2f(lt)) * 0.69314718055994531f;
     }
+  }
+  if constexpr (!EXACT) {
+    if (__any(bad) && lane == 0) s_redo = 1;
+    __syncthreads();
+    if (tid == 0 && s_redo) p.flags[chunk * Hkv + g] = 1;
+  } else {
+    if (redo && tid == 0) p.flags[chunk * Hkv + g] = 0;
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* q, const uint16_t* k,
-                            const uint16_t* v, const float* rope_cos, const float* rope_sin,
-                            float* out, float* lse, const char* ws, hipStream_t stream) {
+hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, float* lse,
+                            const char* ws, hipStream_t stream) {
   const AttnLayout L = attn_layout(a.n, a.T, a.Hq, a.Hkv, a.D);
-  const int4* qinfo = reinterpret_cast<const int4*>(ws + L.qinfo);
-  const int32_t* qstart = reinterpret_cast<const int32_t*>(ws + L.qstart);
-  const uint16_t* qr = reinterpret_cast<const uint16_t*>(ws + L.qrot);
-  const uint16_t* kr = reinterpret_cast<const uint16_t*>(ws + L.krot);
-  const uint16_t* vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
-  const int2* chunks = reinterpret_cast<const int2*>(ws + L.chunks);
-  const int32_t* nchunks = reinterpret_cast<const int32_t*>(ws + L.nchunks);
-  const int G = a.Hq / a.Hkv;
-  const int QR = 256 / G;
-  const int ntiles = (a.n + 31) / 32;
-  const float c_log2 = a.scale * 1.4426950408889634f;
-  const dim3 grid(L.max_chunks * a.Hkv);
-#define PEAGLE_CORE(DD, NN)                                                                    \
-  do {                                                                                         \
-    hipLaunchKernelGGL((attn_core_kernel<DD, NN, true>), grid, dim3(Cfg<DD, NN>::kThreads), 0, \
-                       stream, qinfo, qstart, chunks, nchunks, qr, kr, vt, v, q, k, rope_cos,      \
-                       rope_sin, out, lse, a.n, a.T, a.Hq, a.Hkv, G, QR, ntiles, a.max_pos, c_log2);      \
-    hipLaunchKernelGGL((attn_core_kernel<DD, NN, false>), grid, dim3(Cfg<DD, NN>::kThreads), 0, \
-                       stream, qinfo, qstart, chunks, nchunks, qr, kr, vt, v, q, k, rope_cos,      \
-                       rope_sin, out, lse, a.n, a.T, a.Hq, a.Hkv, G, QR, ntiles, a.max_pos, c_log2);      \
+  AttnParams p;
+  p.qinfo = reinterpret_cast<const int4*>(ws + L.qinfo);
+  p.qstart = reinterpret_cast<const int32_t*>(ws + L.qstart);
+  p.chunks = reinterpret_cast<const int2*>(ws + L.chunks);
+  p.nchunks = reinterpret_cast<const int32_t*>(ws + L.nchunks);
+  p.seq_chunk = reinterpret_cast<const int32_t*>(ws + L.seq_chunk);
+  p.flags = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + L.flags);
+  p.qr = reinterpret_cast<const uint16_t*>(ws + L.qrot);
+  p.kr = reinterpret_cast<const uint16_t*>(ws + L.krot);
+  p.kr_lo = reinterpret_cast<const uint16_t*>(ws + L.krot_lo);
+  p.vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.n = a.n;
+  p.T = a.T;
+  p.S = a.S;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.G = a.Hq / a.Hkv;
+  p.QR = 256 / p.G;
+  p.ntiles = (a.n + 31) / 32;
+  p.exact_per_seq = attn_exact_chunks_per_seq(a.K, p.QR);
+  p.max_chunks = L.max_chunks;
+  p.c_log2 = a.scale * 1.4426950408889634f;
+  // main kernel first (it may flag chunks), then short and flagged chunks
+  const dim3 main_grid(L.max_chunks * a.Hkv);
+  const dim3 exact_grid((a.S * p.exact_per_seq + L.max_chunks) * a.Hkv);
+#define PEAGLE_CORE(DD)                                                                       \
+  do {                                                                                        \
+    hipLaunchKernelGGL((attn_core_kernel<DD, false>), main_grid, dim3(Cfg<DD, kMainNT>::TH), \
+                       0, stream, p);                                                         \
+    hipLaunchKernelGGL((attn_core_kernel<DD, true>), exact_grid, dim3(Cfg<DD, kExactNT>::TH), \
+                       0, stream, p);                                                         \
   } while (0)
   switch (a.D) {
-    case 64: PEAGLE_CORE(64, 1); break;
-    case 128: PEAGLE_CORE(128, 1); break;
-    case 256: PEAGLE_CORE(256, 1); break;
+    case 64: PEAGLE_CORE(64); break;
+    case 128: PEAGLE_CORE(128); break;
+    case 256: PEAGLE_CORE(256); break;
     default: return hipErrorInvalidValue;
   }
 #undef PEAGLE_CORE

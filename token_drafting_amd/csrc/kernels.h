@@ -35,11 +35,19 @@ hipError_t launch_rope_table(int32_t head_dim, double theta, int32_t max_pos, fl
 
 // Workspace of the draft attention, carved from one caller-provided buffer.
 struct AttnLayout {
-  size_t qinfo, qstart, qrot, krot, vt, chunks, nchunks, total;
+  size_t qinfo, qstart, qrot, krot, krot_lo, vt, chunks, nchunks, seq_chunk, flags, total;
   int max_chunks;
 };
 AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D);
 int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv);
+
+// Attention chunks whose context span is at most this many keys (the first anchors of
+// each sequence) run the exact-split variant; the RoPE kernel stores k_lo for the rows
+// of those anchors.
+constexpr int kShortSpan = 96;
+// Chunks per sequence that can be short: their rows belong to the first kShortSpan
+// anchors, which own at most kShortSpan * K list entries.
+inline int attn_exact_chunks_per_seq(int K, int QR) { return (kShortSpan * K + QR - 1) / QR; }
 
 struct AttnArgs {
   int32_t n, K, T, S, Hq, Hkv, D, max_pos;
@@ -52,9 +60,8 @@ hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int3
                                const float* rope_cos, const float* rope_sin, char* ws,
                                hipStream_t stream);
 
-hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* q, const uint16_t* k,
-                            const uint16_t* v, const float* rope_cos, const float* rope_sin,
-                            float* out, float* lse, const char* ws, hipStream_t stream);
+hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, float* lse,
+                            const char* ws, hipStream_t stream);
 
 hipError_t launch_accept(int32_t N, int32_t K, int32_t V, const uint16_t* draft,
                          const uint16_t* target, int32_t* draft_tok, int32_t* target_tok,

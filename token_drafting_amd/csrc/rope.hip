@@ -69,7 +69,9 @@ __device__ int block_exclusive_scan(int v, int* sh, int* total) {
 __global__ __launch_bounds__(kScanThreads) void qlist_kernel(
     const int32_t* __restrict__ row_of, const int32_t* __restrict__ cu, int n, int K, int S,
     int T, int QR, int max_chunks, int4* __restrict__ qinfo, int32_t* __restrict__ qstart,
-    int2* __restrict__ chunks, int32_t* __restrict__ nchunks) {
+    int2* __restrict__ chunks, int32_t* __restrict__ nchunks, int32_t* __restrict__ seq_chunk,
+    int32_t* __restrict__ flags, int nflags) {
+  for (int i = threadIdx.x; i < nflags; i += kScanThreads) flags[i] = 0;  // redo requests
   __shared__ int sh[kScanThreads / 64];
   constexpr int kItems = 8;  // contiguous anchors per thread per chunk
   int carry = 0;
@@ -119,11 +121,15 @@ __global__ __launch_bounds__(kScanThreads) void qlist_kernel(
     }
     int total;
     const int at = ccarry + block_exclusive_scan(cnt, sh, &total);
+    if (s < S) seq_chunk[s] = min(at, max_chunks);
     for (int i = 0; i < cnt; ++i)
       if (at + i < max_chunks) chunks[at + i] = make_int2(first + i * QR, min(QR, rows - i * QR));
     ccarry += total;
   }
-  if (threadIdx.x == 0) *nchunks = min(ccarry, max_chunks);
+  if (threadIdx.x == 0) {
+    *nchunks = min(ccarry, max_chunks);
+    seq_chunk[S] = min(ccarry, max_chunks);
+  }
 }
 
 // One thread per (row, head, 8-wide chunk of the first half of the head dimension).
@@ -131,7 +137,8 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ depth_off,
     const int32_t* __restrict__ cu, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float* __restrict__ cosT, const float* __restrict__ sinT, uint16_t* __restrict__ qr,
-    uint16_t* __restrict__ kr, int n, int K, int S, int T, int Hq, int Hkv, int D, int max_pos) {
+    uint16_t* __restrict__ kr, uint16_t* __restrict__ kr_lo, int n, int K, int S, int T, int Hq,
+    int Hkv, int D, int max_pos) {
   const int half = D / 2, cpr = half / 8;  // chunks per head
   const int heads = Hq + Hkv;
   const size_t total = (size_t)T * heads * cpr;
@@ -143,7 +150,8 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(
     const int d = min(max(upper_index(depth_off, K + 1, r), 0), K - 1);
     const int p = min(max(idx[r], 0), n - 1);
     const int s = min(max(upper_index(cu, S + 1, p), 0), S);
-    const int pos = min(max(p - cu[s] + d, 0), max_pos);
+    const int offset = p - cu[s];  // anchor's offset in its sequence
+    const int pos = min(max(offset + d, 0), max_pos);
     const uint16_t* src = (h < Hq) ? q + ((size_t)r * Hq + h) * D : k + ((size_t)r * Hkv + (h - Hq)) * D;
     uint16_t* dst = (h < Hq) ? qr + ((size_t)r * Hq + h) * D : kr + ((size_t)r * Hkv + (h - Hq)) * D;
     const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + c * 8);
@@ -151,10 +159,10 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(
     const floatx4* cp = reinterpret_cast<const floatx4*>(cosT + (size_t)pos * half + c * 8);
     const floatx4* sp = reinterpret_cast<const floatx4*>(sinT + (size_t)pos * half + c * 8);
     const floatx4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-    u32x4 y1, y2;
+    u32x4 y1, y2, z1, z2;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      uint32_t o1 = 0, o2 = 0;
+      uint32_t o1 = 0, o2 = 0, l1 = 0, l2 = 0;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int j = w * 2 + e;
@@ -162,14 +170,27 @@ __global__ __launch_bounds__(256) void rope_rotate_kernel(
         const float b = bf16_bits_to_f32((x2[w] >> (16 * e)) & 0xFFFFu);
         const float cs = (j < 4) ? c0[j] : c1[j - 4];
         const float sn = (j < 4) ? s0[j] : s1[j - 4];
-        o1 |= (uint32_t)f32_to_bf16_bits(a * cs - b * sn) << (16 * e);
-        o2 |= (uint32_t)f32_to_bf16_bits(b * cs + a * sn) << (16 * e);
+        const float r1 = a * cs - b * sn, r2 = b * cs + a * sn;
+        const uint16_t h1 = f32_to_bf16_bits(r1), h2 = f32_to_bf16_bits(r2);
+        o1 |= (uint32_t)h1 << (16 * e);
+        o2 |= (uint32_t)h2 << (16 * e);
+        l1 |= (uint32_t)f32_to_bf16_bits(r1 - bf16_bits_to_f32(h1)) << (16 * e);
+        l2 |= (uint32_t)f32_to_bf16_bits(r2 - bf16_bits_to_f32(h2)) << (16 * e);
       }
       y1[w] = o1;
       y2[w] = o2;
+      z1[w] = l1;
+      z2[w] = l2;
     }
     *reinterpret_cast<u32x4*>(dst + c * 8) = y1;
     *reinterpret_cast<u32x4*>(dst + half + c * 8) = y2;
+    // k rows of a sequence's first anchors also keep the rounding residual (k_lo) for the
+    // attention's exact-split chunks
+    if (h >= Hq && offset < kShortSpan) {
+      uint16_t* lo = kr_lo + ((size_t)r * Hkv + (h - Hq)) * D;
+      *reinterpret_cast<u32x4*>(lo + c * 8) = z1;
+      *reinterpret_cast<u32x4*>(lo + half + c * 8) = z2;
+    }
   }
 }
 
@@ -248,10 +269,13 @@ AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D)
   L.qstart = off; off += align256((size_t)(n + 1) * sizeof(int32_t));
   L.qrot = off;   off += align256((size_t)T * Hq * D * 2);
   L.krot = off;   off += align256((size_t)T * Hkv * D * 2);
+  L.krot_lo = off; off += align256((size_t)T * Hkv * D * 2);
   L.vt = off;     off += align256(ntiles * 32 * Hkv * D * 2);
   L.max_chunks = attn_max_chunks(n, T, Hq, Hkv);
   L.chunks = off; off += align256((size_t)L.max_chunks * sizeof(int2));
   L.nchunks = off; off += 256;
+  L.seq_chunk = off; off += align256((size_t)(n + 1) * sizeof(int32_t));
+  L.flags = off;  off += align256((size_t)L.max_chunks * Hkv * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -266,21 +290,24 @@ hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int3
   int32_t* qstart = reinterpret_cast<int32_t*>(ws + L.qstart);
   uint16_t* qr = reinterpret_cast<uint16_t*>(ws + L.qrot);
   uint16_t* kr = reinterpret_cast<uint16_t*>(ws + L.krot);
+  uint16_t* kr_lo = reinterpret_cast<uint16_t*>(ws + L.krot_lo);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
 
   int2* chunks = reinterpret_cast<int2*>(ws + L.chunks);
   int32_t* nchunks = reinterpret_cast<int32_t*>(ws + L.nchunks);
+  int32_t* seq_chunk = reinterpret_cast<int32_t*>(ws + L.seq_chunk);
   hipLaunchKernelGGL(qlist_kernel, dim3(1), dim3(kScanThreads), 0, stream, row_of, cu_seqlens, a.n,
                      a.K, a.S, a.T, 256 / (a.Hq / a.Hkv), L.max_chunks, qinfo, qstart, chunks,
-                     nchunks);
+                     nchunks, seq_chunk, reinterpret_cast<int32_t*>(ws + L.flags),
+                     L.max_chunks * a.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const size_t work = (size_t)a.T * (a.Hq + a.Hkv) * (a.D / 16);
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 1 << 20);
   hipLaunchKernelGGL(rope_rotate_kernel, dim3(blocks), dim3(256), 0, stream, idx, depth_off,
-                     cu_seqlens, q, k, rope_cos, rope_sin, qr, kr, a.n, a.K, a.S, a.T, a.Hq, a.Hkv,
-                     a.D, a.max_pos);
+                     cu_seqlens, q, k, rope_cos, rope_sin, qr, kr, kr_lo, a.n, a.K, a.S, a.T, a.Hq,
+                     a.Hkv, a.D, a.max_pos);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
