@@ -34,7 +34,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768, help="oracle sample size (rows)")
+    ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle sample size (rows)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the timed steps, "
+                         "so a counter run can scale its byte counters against known traffic")
     return ap.parse_args()
 
 
@@ -49,8 +52,8 @@ def useful_pairs(idx, depth_off, cu):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the draft forward has no multi-GPU path; "
+              "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -121,6 +124,15 @@ def main():
         mark(5)
         peagle.accept_prefix(dl, tl, dtok, ttok, alen)
         mark(6)
+
+    if args.calibration_copy_mib:
+        nbytes = args.calibration_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

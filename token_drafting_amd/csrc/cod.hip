@@ -10,7 +10,9 @@
 //
 // One workgroup of 1024 threads does the whole job; the outputs are < 1 MB even at
 // n = 32K, so this kernel is latency-bound:
-//   1. per depth, an MSB-first radix select (8 passes of 8 bits) finds the threshold;
+//   1. a 12-bit histogram of the hashes locates, for every depth, the bin that holds the
+//      m_d-th smallest hash; the handful of hashes in that bin are ranked directly (an
+//      8-bit radix select is the fallback for a bin with more than 1024 hashes);
 //   2. one pass over p in chunks of 1024 computes each hash once, takes a wave ballot
 //      per depth and writes idx / row_of in ascending p (ordered compaction);
 //   3. cu_seqlens_d by binary search of each sequence start in the depth's idx run.
@@ -31,15 +33,74 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
   return z ^ (z >> 31);
 }
 
+// Exclusive scan of one value per thread over the 1024-thread block (wave shuffles, then
+// the 16 wave totals through LDS). Returns the prefix; *total receives the block sum.
+__device__ int block_scan_excl(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = sh[w];
+    if (w < wave) before += c;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+// The rank-th smallest (1-based) hash, by MSB-first radix select with 8-bit digits.
+// Slow path, taken only when a 12-bit bin of the fast path holds too many hashes.
+__device__ uint64_t radix_select(const CodArgs& a, int rank, uint32_t* hist, uint64_t* s_prefix,
+                                 int* s_rank) {
+  const int tid = threadIdx.x, n = a.n;
+  uint64_t prefix = 0, pmask = 0;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < n; p += kThreads) {
+      const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
+      if ((h & pmask) == prefix) atomicAdd(&hist[(h >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int before = 0, b = 0;
+      for (; b < 255; ++b) {
+        if (before + (int)hist[b] >= rank) break;
+        before += hist[b];
+      }
+      *s_rank = rank - before;
+      *s_prefix = prefix | ((uint64_t)b << shift);
+    }
+    __syncthreads();
+    prefix = *s_prefix;
+    rank = *s_rank;
+    pmask |= 0xFFull << shift;
+  }
+  return prefix;
+}
+
 __global__ __launch_bounds__(kThreads) void cod_select_kernel(
     CodArgs a, const int32_t* __restrict__ cu, int32_t* __restrict__ idx,
     int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
-  __shared__ uint32_t hist[256];
+  constexpr int kBinBits = 12, kBins = 1 << kBinBits, kPerThread = kBins / kThreads;
+  constexpr int kCand = 1024;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint64_t cand[kCand];
   __shared__ uint64_t thr[kMaxDepths];
+  __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths];
   __shared__ int32_t wcount[2][kMaxDepths][kWaves];
   __shared__ int32_t carry[2][kMaxDepths];
+  __shared__ int32_t sh[kWaves];
   __shared__ uint64_t s_prefix;
-  __shared__ int32_t s_rank;
+  __shared__ int32_t s_rank, s_count;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -47,6 +108,38 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
   const int n = a.n, K = a.K;
 
   // 1. thresholds: keep p at depth d iff hash(p) <= thr[d] (m_d == 0 keeps nothing).
+  //    One histogram of the top 12 hash bits serves every depth: its prefix sums give the
+  //    bin holding the m_d-th smallest hash and the rank inside that bin; the bin's few
+  //    hashes (n / 4096 on average) are then ranked directly.
+  for (int b = tid; b < kBins; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  for (int p = tid; p < n; p += kThreads)
+    atomicAdd(&hist[splitmix64(a.seed ^ (uint64_t)p) >> (64 - kBinBits)], 1u);
+  __syncthreads();
+  {
+    uint32_t mine[kPerThread];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      mine[i] = hist[tid * kPerThread + i];
+      sum += mine[i];
+    }
+    int total;
+    int before = block_scan_excl(sum, sh, &total);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int b = tid * kPerThread + i;
+      for (int d = 0; d < K; ++d) {
+        const int m = a.m[d];
+        if (m > before && m <= before + (int)mine[i]) {
+          bin_of[d] = b;
+          rank_in_bin[d] = m - before;
+        }
+      }
+      before += mine[i];
+    }
+  }
+  __syncthreads();
   for (int d = 0; d < K; ++d) {
     const int m = a.m[d];
     if (m >= n || m == 0) {
@@ -55,34 +148,35 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
     }
     if (d > 0 && a.m[d - 1] == m) {  // same count, same threshold
       if (tid == 0) thr[d] = thr[d - 1];
+      continue;
+    }
+    const uint32_t b = (uint32_t)bin_of[d];
+    if (hist[b] > (uint32_t)kCand) {  // pathological bin: full radix select
+      const uint64_t t = radix_select(a, m, hist + 0, &s_prefix, &s_rank);
+      if (tid == 0) thr[d] = t;
+      __syncthreads();
+      // the histogram was overwritten: rebuild it for the depths still to come
+      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+      __syncthreads();
+      for (int p = tid; p < n; p += kThreads)
+        atomicAdd(&hist[splitmix64(a.seed ^ (uint64_t)p) >> (64 - kBinBits)], 1u);
       __syncthreads();
       continue;
     }
-    uint64_t prefix = 0, pmask = 0;
-    int rank = m;  // we want the rank-th smallest hash (1-based) among those matching prefix
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
-      for (int p = tid; p < n; p += kThreads) {
-        const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
-        if ((h & pmask) == prefix) atomicAdd(&hist[(h >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int before = 0, b = 0;
-        for (; b < 255; ++b) {
-          if (before + (int)hist[b] >= rank) break;
-          before += hist[b];
-        }
-        s_rank = rank - before;
-        s_prefix = prefix | ((uint64_t)b << shift);
-      }
-      __syncthreads();
-      prefix = s_prefix;
-      rank = s_rank;
-      pmask |= 0xFFull << shift;
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+    for (int p = tid; p < n; p += kThreads) {
+      const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
+      if ((h >> (64 - kBinBits)) == b) cand[atomicAdd(&s_count, 1)] = h;
     }
-    if (tid == 0) thr[d] = prefix;
+    __syncthreads();
+    const int c = s_count, want = rank_in_bin[d] - 1;
+    for (int i = tid; i < c; i += kThreads) {
+      const uint64_t h = cand[i];
+      int smaller = 0;
+      for (int j = 0; j < c; ++j) smaller += cand[j] < h;
+      if (smaller == want) thr[d] = h;  // hashes are distinct: exactly one writer
+    }
     __syncthreads();
   }
   if (tid <= K) depth_off[tid] = a.off[tid];

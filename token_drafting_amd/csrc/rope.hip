@@ -73,33 +73,38 @@ __global__ __launch_bounds__(kScanThreads) void qlist_kernel(
     int32_t* __restrict__ flags, int nflags) {
   for (int i = threadIdx.x; i < nflags; i += kScanThreads) flags[i] = 0;  // redo requests
   __shared__ int sh[kScanThreads / 64];
-  constexpr int kItems = 8;  // contiguous anchors per thread per chunk
+  constexpr int kItems = 32;  // contiguous anchors per thread per chunk
   int carry = 0;
   for (int base = 0; base < n; base += kScanThreads * kItems) {
     const int p0 = base + threadIdx.x * kItems;
+    // kept depths per anchor: every row_of load is independent of the others
     int cnt[kItems];
+#pragma unroll
+    for (int i = 0; i < kItems; ++i) cnt[i] = 0;
+    for (int d = 0; d < K; ++d) {
+      const int32_t* ro = row_of + (size_t)d * n;
+#pragma unroll
+      for (int i = 0; i < kItems; ++i)
+        if (p0 + i < n) cnt[i] += ro[p0 + i] >= 0;
+    }
     int mine = 0;
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int p = p0 + i;
-      int c = 0;
-      if (p < n)
-        while (c < K && row_of[(size_t)c * n + p] >= 0) ++c;  // nested: depths 0..c-1
-      cnt[i] = c;
-      mine += c;
-    }
+    for (int i = 0; i < kItems; ++i) mine += cnt[i];
     int total;
     int start = carry + block_exclusive_scan(mine, sh, &total);
+    if (p0 < n) {
+      int s = min(max(upper_index(cu, S + 1, p0), 0), S);
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int p = p0 + i;
-      if (p >= n) break;
-      qstart[p] = start;
-      const int s = min(max(upper_index(cu, S + 1, p), 0), S);
-      const int lo = cu[s];
-      for (int d = 0; d < cnt[i]; ++d)
-        if (start + d < T) qinfo[start + d] = make_int4(row_of[(size_t)d * n + p], p, d, lo);
-      start += cnt[i];
+      for (int i = 0; i < kItems; ++i) {
+        const int p = p0 + i;
+        if (p >= n) break;
+        while (s < S && cu[s + 1] <= p) ++s;  // anchors ascend: the sequence only advances
+        const int lo = cu[min(s, S)];
+        qstart[p] = start;
+        for (int d = 0; d < cnt[i]; ++d)  // nested sets: the kept depths are 0 .. cnt-1
+          if (start + d < T) qinfo[start + d] = make_int4(row_of[(size_t)d * n + p], p, d, lo);
+        start += cnt[i];
+      }
     }
     carry += total;
   }
