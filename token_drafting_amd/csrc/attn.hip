@@ -52,7 +52,7 @@
 // LDS layouts. K tiles: one 16-byte-padded row per key (stride 2D + 16 bytes), so the
 // 32 keys a half-wave reads at one head-dim offset fall in distinct bank groups and a
 // lane's 16 k-step reads share one base address. V^T tiles: rows of 32 keys (64 bytes),
-// 16-byte chunk index XOR ((d >> 1) & 3).
+// 16-byte chunk index XOR ((d >> 2) & 3).
 #include <algorithm>
 #include <type_traits>
 
@@ -81,8 +81,10 @@ struct Cfg {
   static constexpr int MT = D / 32;               // 32-row M tiles of O^T
 };
 
+// V^T row d is 64 bytes (4 chunks of 8 keys); the chunk index is XOR-ed with bits 2-3 of
+// d so the 16 rows read in one LDS cycle cover all 16 sixteen-byte slots of the 64 banks.
 __device__ __forceinline__ int v_off(int d, int chunk) {
-  return d * (KT * 2) + ((chunk ^ ((d >> 1) & 3)) << 4);
+  return d * (KT * 2) + ((chunk ^ ((d >> 2) & 3)) << 4);
 }
 
 // s_waitcnt vmcnt(0): this wave's LDS-DMA writes have landed (expcnt/lgkmcnt not waited).
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(512 / (EXACT ? kExactNT : kMainNT)) void attn_core_
 #pragma unroll
     for (int i = wave; i < C::VBYTES / 1024; i += C::WAVES) {
       const int P = i * 1024 + lane * 16;
-      const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 1) & 3);
+      const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 2) & 3);
       dma16(vsrc + d * KT + c * 8, dst + i * 1024);
     }
   };
@@ -458,8 +460,10 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p.max_chunks = L.max_chunks;
   p.c_log2 = a.scale * 1.4426950408889634f;
   // main kernel first (it may flag chunks), then short and flagged chunks
-  const dim3 main_grid(L.max_chunks * a.Hkv);
-  const dim3 exact_grid((a.S * p.exact_per_seq + L.max_chunks) * a.Hkv);
+  // chunk count <= ceil(T / QR) + S (each sequence adds at most one partial chunk)
+  const int chunk_bound = std::min(L.max_chunks, (a.T + p.QR - 1) / p.QR + a.S);
+  const dim3 main_grid(chunk_bound * a.Hkv);
+  const dim3 exact_grid((a.S * p.exact_per_seq + chunk_bound) * a.Hkv);
 #define PEAGLE_CORE(DD)                                                                       \
   do {                                                                                        \
     hipLaunchKernelGGL((attn_core_kernel<DD, false>), main_grid, dim3(Cfg<DD, kMainNT>::TH), \

@@ -8,14 +8,15 @@
 // The hash is a bijection, so the m_d-th smallest hash is a unique threshold and depth d
 // keeps exactly the p with hash <= threshold.
 //
-// One workgroup of 1024 threads does the whole job; the outputs are < 1 MB even at
-// n = 32K, so this kernel is latency-bound:
+// One workgroup of 1024 threads per block of 1024 positions. The thresholds are cheap
+// (a few passes of hashing over n), so every workgroup derives them itself and no
+// workgroup waits on another:
 //   1. a 12-bit histogram of the hashes locates, for every depth, the bin that holds the
 //      m_d-th smallest hash; the handful of hashes in that bin are ranked directly (an
 //      8-bit radix select is the fallback for a bin with more than 1024 hashes);
-//   2. one pass over p in chunks of 1024 computes each hash once, takes a wave ballot
-//      per depth and writes idx / row_of in ascending p (ordered compaction);
-//   3. cu_seqlens_d by binary search of each sequence start in the depth's idx run.
+//   2. the workgroup counts the kept positions of every depth before its block;
+//   3. ordered compaction of its own block with wave ballots (coalesced idx / row_of);
+//   4. cu_seqlens_d for the sequence starts inside its block.
 #include "common.h"
 #include "kernels.h"
 
@@ -96,8 +97,9 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
   __shared__ uint64_t cand[kCand];
   __shared__ uint64_t thr[kMaxDepths];
   __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths];
-  __shared__ int32_t wcount[2][kMaxDepths][kWaves];
-  __shared__ int32_t carry[2][kMaxDepths];
+  __shared__ uint64_t wmask[kMaxDepths][kWaves];
+  __shared__ int32_t wsum[8][kWaves];
+  __shared__ int32_t before_blk[kMaxDepths];
   __shared__ int32_t sh[kWaves];
   __shared__ uint64_t s_prefix;
   __shared__ int32_t s_rank, s_count;
@@ -179,53 +181,79 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
     }
     __syncthreads();
   }
-  if (tid <= K) depth_off[tid] = a.off[tid];
   __syncthreads();
 
-  // 2. ordered compaction, all depths in one pass over p. Per chunk of 1024 positions a
-  // wave ballot gives each lane its rank inside the wave; per-wave counts go through LDS.
-  // The running count before the chunk (carry) is block-uniform and lives in LDS too;
-  // both are double-buffered by chunk parity so one barrier per chunk suffices.
-  if (tid < K) carry[0][tid] = 0;
-  __syncthreads();
-  int parity = 0;
-  for (int base = 0; base < n; base += kThreads, parity ^= 1) {
-    const int p = base + tid;
-    const bool inside = p < n;
-    const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
-    for (int d = 0; d < K; ++d) {
-      const bool keep = inside && a.m[d] > 0 && h <= thr[d];
-      const uint64_t ball = __ballot(keep);
-      if (lane == 0) wcount[parity][d][wave] = __popcll(ball);
+  // 2. kept positions of every depth before this workgroup's block: one pass over
+  //    [0, base), eight depths per pass, reduced over the workgroup.
+  const int base = blockIdx.x * kThreads;
+  for (int d0 = 0; d0 < K; d0 += 8) {
+    int c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = 0;
+    for (int p = tid; p < base; p += kThreads) {
+      const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (d0 + j < K) c[j] += (a.m[d0 + j] > 0 && h <= thr[d0 + j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int v = c[j];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0) wsum[j][wave] = v;
     }
     __syncthreads();
-    for (int d = 0; d < K; ++d) {
-      const bool keep = inside && a.m[d] > 0 && h <= thr[d];
-      const uint64_t ball = __ballot(keep);
-      int before = carry[parity][d], total = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = wcount[parity][d][w];
-        if (w < wave) before += c;
-        total += c;
-      }
-      const int r = a.off[d] + before + __popcll(ball & ((1ull << lane) - 1ull));
-      if (inside) {
-        row_of[(size_t)d * n + p] = keep ? r : -1;
-        if (keep && r < a.off[d + 1]) idx[r] = p;
-      }
-      if (tid == 0) carry[parity ^ 1][d] = carry[parity][d] + total;
+    if (tid < 8 && d0 + tid < K) {
+      int v = 0;
+      for (int w = 0; w < kWaves; ++w) v += wsum[tid][w];
+      before_blk[d0 + tid] = v;
     }
-    // wcount[parity] and carry[parity] are rewritten two chunks later, after a barrier
-    // that every thread reaches only once it has finished with them.
+    __syncthreads();
   }
-  __threadfence();
-  __syncthreads();
 
-  // 3. kept anchors of depth d before each sequence start.
+  // 3. ordered compaction of the block [base, base + 1024): a wave ballot per depth gives
+  //    each lane its rank inside the wave, the wave masks in LDS give the rank inside
+  //    the block.
+  const int p = base + tid;
+  const bool inside = p < n;
+  const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
+  for (int d = 0; d < K; ++d) {
+    const bool keep = inside && a.m[d] > 0 && h <= thr[d];
+    const uint64_t ball = __ballot(keep);
+    if (lane == 0) wmask[d][wave] = ball;
+  }
+  __syncthreads();
+  for (int d = 0; d < K; ++d) {
+    const uint64_t ball = wmask[d][wave];
+    const bool keep = (ball >> lane) & 1ull;
+    int r = a.off[d] + before_blk[d] + __popcll(ball & ((1ull << lane) - 1ull));
+    for (int w = 0; w < wave; ++w) r += __popcll(wmask[d][w]);
+    if (inside) {
+      row_of[(size_t)d * n + p] = keep ? r : -1;
+      if (keep && r < a.off[d + 1]) idx[r] = p;
+    }
+  }
+
+  // 4. kept anchors of depth d before each sequence start that falls in this block (the
+  //    last block also owns cu = n).
   for (int t = tid; t < K * (a.S + 1); t += kThreads) {
     const int d = t / (a.S + 1), s = t % (a.S + 1);
-    cu_d[t] = lower_count(idx + a.off[d], a.m[d], cu[s]);
+    const int x = cu[s];
+    const bool mine = (x >= base && x < base + kThreads && x < n) ||
+                      (x >= n && blockIdx.x == gridDim.x - 1);
+    if (!mine) continue;
+    int v;
+    if (x >= n) {
+      v = a.m[d];
+    } else {
+      const int off = x - base, w = off >> 6, l = off & 63;
+      v = before_blk[d] + __popcll(wmask[d][w] & ((1ull << l) - 1ull));
+      for (int j = 0; j < w; ++j) v += __popcll(wmask[d][j]);
+    }
+    cu_d[t] = v;
   }
+  if (blockIdx.x == 0 && tid <= K) depth_off[tid] = a.off[tid];
 }
 
 }  // namespace
@@ -233,8 +261,8 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
 hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_t* idx,
                              int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
                              hipStream_t stream) {
-  hipLaunchKernelGGL(cod_select_kernel, dim3(1), dim3(kThreads), 0, stream, a, cu_seqlens, idx,
-                     depth_off, cu_seqlens_d, row_of);
+  hipLaunchKernelGGL(cod_select_kernel, dim3((a.n + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, a, cu_seqlens, idx, depth_off, cu_seqlens_d, row_of);
   return hipGetLastError();
 }
 

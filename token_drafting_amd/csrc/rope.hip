@@ -10,9 +10,10 @@
 //
 // Kernels:
 //   rope_table_kernel    cos/sin [max_pos+1, D/2] fp32, angles and cos/sin in fp64.
-//   qlist_kernel         anchor-major list of draft rows (all depths of anchor 0, then
+//   qcount/qlist_kernel  anchor-major list of draft rows (all depths of anchor 0, then
 //                        of anchor 1, ...) with per-row (row, anchor, depth, seq start),
-//                        and qstart[p] = first entry of anchor p. One workgroup.
+//                        and qstart[p] = first entry of anchor p.
+//   chunk_kernel         the attention's chunk table (chunks never cross a sequence).
 //   rope_rotate_kernel   q' and k' of every draft row, bf16, draft-row order.
 //   v_transpose_kernel   depth-0 v as 32-key tiles laid out [d][32 keys], keys permuted
 //                        inside each 16-key group as (0-3, 8-11, 4-7, 12-15) so that a
@@ -66,62 +67,72 @@ __device__ int block_exclusive_scan(int v, int* sh, int* total) {
   return before + x - v;
 }
 
-__global__ __launch_bounds__(kScanThreads) void qlist_kernel(
-    const int32_t* __restrict__ row_of, const int32_t* __restrict__ cu, int n, int K, int S,
-    int T, int QR, int max_chunks, int4* __restrict__ qinfo, int32_t* __restrict__ qstart,
-    int2* __restrict__ chunks, int32_t* __restrict__ nchunks, int32_t* __restrict__ seq_chunk,
-    int32_t* __restrict__ flags, int nflags) {
-  for (int i = threadIdx.x; i < nflags; i += kScanThreads) flags[i] = 0;  // redo requests
-  __shared__ int sh[kScanThreads / 64];
-  constexpr int kItems = 32;  // contiguous anchors per thread per chunk
-  int carry = 0;
-  for (int base = 0; base < n; base += kScanThreads * kItems) {
-    const int p0 = base + threadIdx.x * kItems;
-    // kept depths per anchor: every row_of load is independent of the others
-    int cnt[kItems];
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) cnt[i] = 0;
-    for (int d = 0; d < K; ++d) {
-      const int32_t* ro = row_of + (size_t)d * n;
-#pragma unroll
-      for (int i = 0; i < kItems; ++i)
-        if (p0 + i < n) cnt[i] += ro[p0 + i] >= 0;
-    }
-    int mine = 0;
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) mine += cnt[i];
-    int total;
-    int start = carry + block_exclusive_scan(mine, sh, &total);
-    if (p0 < n) {
-      int s = min(max(upper_index(cu, S + 1, p0), 0), S);
-#pragma unroll
-      for (int i = 0; i < kItems; ++i) {
-        const int p = p0 + i;
-        if (p >= n) break;
-        while (s < S && cu[s + 1] <= p) ++s;  // anchors ascend: the sequence only advances
-        const int lo = cu[min(s, S)];
-        qstart[p] = start;
-        for (int d = 0; d < cnt[i]; ++d)  // nested sets: the kept depths are 0 .. cnt-1
-          if (start + d < T) qinfo[start + d] = make_int4(row_of[(size_t)d * n + p], p, d, lo);
-        start += cnt[i];
-      }
-    }
-    carry += total;
-  }
-  if (threadIdx.x == 0) qstart[n] = min(carry, T);
-  __threadfence();
-  __syncthreads();
+// Kept depths of every anchor (depth sets are nested, so anchor p owns list entries for
+// depths 0 .. c(p)-1); per block of 1024 anchors, the block total.
+__device__ __forceinline__ int kept_depths(const int32_t* __restrict__ row_of, int n, int K, int p) {
+  int c = 0;
+  if (p < n)
+    for (int d = 0; d < K; ++d) c += row_of[(size_t)d * n + p] >= 0;
+  return c;
+}
 
-  // Chunks of at most QR consecutive list entries that never cross a sequence: chunk
-  // table entries (first entry, entry count), sequence after sequence.
+__global__ __launch_bounds__(kScanThreads) void qcount_kernel(const int32_t* __restrict__ row_of,
+                                                              int n, int K,
+                                                              int32_t* __restrict__ blocksum) {
+  __shared__ int sh[kScanThreads / 64];
+  int total;
+  block_exclusive_scan(kept_depths(row_of, n, K, blockIdx.x * kScanThreads + threadIdx.x), sh, &total);
+  if (threadIdx.x == 0) blocksum[blockIdx.x] = total;
+}
+
+// Anchor-major list: entry qstart[p] + d is draft row (d, p), stored with its anchor, its
+// depth and the start of its sequence. Each block adds up the totals of the blocks before
+// it, then scans its own anchors.
+__global__ __launch_bounds__(kScanThreads) void qlist_kernel(
+    const int32_t* __restrict__ row_of, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ blocksum, int n, int K, int S, int T, int4* __restrict__ qinfo,
+    int32_t* __restrict__ qstart) {
+  __shared__ int sh[kScanThreads / 64];
+  __shared__ int s_off;
+  const int b = blockIdx.x, p = b * kScanThreads + threadIdx.x;
+  if (threadIdx.x < 64) {
+    int v = 0;
+    for (int j = threadIdx.x; j < b; j += 64) v += blocksum[j];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (threadIdx.x == 0) s_off = v;
+  }
+  const int c = kept_depths(row_of, n, K, p);
+  int total;
+  const int excl = block_exclusive_scan(c, sh, &total);  // its barriers also publish s_off
+  const int start = s_off + excl;
+  if (p < n) {
+    qstart[p] = start;
+    const int s = min(max(upper_index(cu, S + 1, p), 0), S);
+    const int lo = cu[s];
+    for (int d = 0; d < c; ++d)
+      if (start + d < T) qinfo[start + d] = make_int4(row_of[(size_t)d * n + p], p, d, lo);
+  }
+  if (b == gridDim.x - 1 && threadIdx.x == 0) qstart[n] = min(s_off + total, T);
+}
+
+// Chunks of at most QR consecutive list entries that never cross a sequence: chunk table
+// entries (first entry, entry count), sequence after sequence; seq_chunk[s] = first chunk
+// of sequence s. Also clears the per-(chunk, kv head) redo flags. One workgroup.
+__global__ __launch_bounds__(kScanThreads) void chunk_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ qstart, int n, int S, int QR,
+    int max_chunks, int2* __restrict__ chunks, int32_t* __restrict__ nchunks,
+    int32_t* __restrict__ seq_chunk, int32_t* __restrict__ flags, int nflags) {
+  __shared__ int sh[kScanThreads / 64];
+  for (int i = threadIdx.x; i < nflags; i += kScanThreads) flags[i] = 0;
   int ccarry = 0;
   for (int base = 0; base < S; base += kScanThreads) {
     const int s = base + threadIdx.x;
     int first = 0, rows = 0, cnt = 0;
     if (s < S) {
-      const int a = min(max(cu[s], 0), n), b = min(max(cu[s + 1], 0), n);
+      const int a = min(max(cu[s], 0), n), e = min(max(cu[s + 1], 0), n);
       first = qstart[a];
-      rows = max(qstart[b] - first, 0);
+      rows = max(qstart[e] - first, 0);
       cnt = (rows + QR - 1) / QR;
     }
     int total;
@@ -281,6 +292,7 @@ AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D)
   L.nchunks = off; off += 256;
   L.seq_chunk = off; off += align256((size_t)(n + 1) * sizeof(int32_t));
   L.flags = off;  off += align256((size_t)L.max_chunks * Hkv * sizeof(int32_t));
+  L.blocksum = off; off += align256((size_t)((n + 1023) / 1024) * sizeof(int32_t));
   L.total = off;
   return L;
 }
@@ -301,10 +313,15 @@ hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int3
   int2* chunks = reinterpret_cast<int2*>(ws + L.chunks);
   int32_t* nchunks = reinterpret_cast<int32_t*>(ws + L.nchunks);
   int32_t* seq_chunk = reinterpret_cast<int32_t*>(ws + L.seq_chunk);
-  hipLaunchKernelGGL(qlist_kernel, dim3(1), dim3(kScanThreads), 0, stream, row_of, cu_seqlens, a.n,
-                     a.K, a.S, a.T, 256 / (a.Hq / a.Hkv), L.max_chunks, qinfo, qstart, chunks,
-                     nchunks, seq_chunk, reinterpret_cast<int32_t*>(ws + L.flags),
-                     L.max_chunks * a.Hkv);
+  int32_t* blocksum = reinterpret_cast<int32_t*>(ws + L.blocksum);
+  const int nblk = (a.n + kScanThreads - 1) / kScanThreads;
+  hipLaunchKernelGGL(qcount_kernel, dim3(nblk), dim3(kScanThreads), 0, stream, row_of, a.n, a.K,
+                     blocksum);
+  hipLaunchKernelGGL(qlist_kernel, dim3(nblk), dim3(kScanThreads), 0, stream, row_of, cu_seqlens,
+                     blocksum, a.n, a.K, a.S, a.T, qinfo, qstart);
+  hipLaunchKernelGGL(chunk_kernel, dim3(1), dim3(kScanThreads), 0, stream, cu_seqlens, qstart, a.n,
+                     a.S, 256 / (a.Hq / a.Hkv), L.max_chunks, chunks, nchunks, seq_chunk,
+                     reinterpret_cast<int32_t*>(ws + L.flags), L.max_chunks * a.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
