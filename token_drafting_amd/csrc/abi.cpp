@@ -4,7 +4,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/peagle.h"
+#include "peagle.h"
 #include "kernels.h"
 
 using namespace peagle;
@@ -59,7 +59,7 @@ int attn_check(int64_t n, int32_t K, int64_t T, const int32_t* idx, const int32_
   if (!(scale > 0.f) || !std::isfinite(scale)) return PEAGLE_ERR_ARG;
   if ((int64_t)max_pos < n + K - 2) return PEAGLE_ERR_ARG;
   if (D != 64 && D != 128 && D != 256) return PEAGLE_ERR_UNSUPPORTED;
-  if (256 % (Hq / Hkv) != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if (kAttnSlots % (Hq / Hkv) != 0) return PEAGLE_ERR_UNSUPPORTED;
   if (ws_bytes < attn_layout(n, T, Hq, Hkv, D).total) return PEAGLE_ERR_WORKSPACE;
   if (!idx || !depth_off || !row_of || !cu || !q || !k || !v || !cs || !sn || !out || !ws)
     return PEAGLE_ERR_ARG;

@@ -10,10 +10,10 @@
 // Work decomposition. Rows are visited in anchor-major order (all depths of anchor 0,
 // then of anchor 1, ...; built by qlist_kernel). A workgroup owns a chunk of up to
 // QR = 256/G consecutive rows of that list, never crossing a packed sequence, for all G
-// q heads of one kv head: 256 query slots (4 waves of 64 in the main kernel), roughly
-// 25 anchors and all their depths at K=4, G=4. Every row of the chunk reads a prefix of the same depth-0
+// q heads of one kv head: 256 query slots in 8 waves of 32, roughly 25 anchors and all
+// their depths at K=4, G=4. Every row of the chunk reads a prefix of the same depth-0
 // K/V, so each K/V tile is loaded to LDS once and used by all 256 slots (all depths, all
-// heads of the group). Tiles wholly inside every row's range run unmasked; the one or
+// heads of the group); halving the workgroup to 128 slots was measured 1.5x slower. Tiles wholly inside every row's range run unmasked; the one or
 // two at the chunk's edge are masked per element; tiles past the last anchor are never
 // visited. The diagonal keys of the chunk's anchors are a short contiguous run of the
 // anchor-major list, processed as extra masked tiles.
@@ -71,8 +71,8 @@ constexpr float kSumLimit = 18446744073709551616.f;  // 2^64: above it a row is 
 
 template <int D, int NT>
 struct Cfg {
-  static constexpr int TH = 512 / NT;             // 256 query slots per workgroup
-  static constexpr int WAVES = TH / 64;
+  static constexpr int WAVES = kAttnSlots / (32 * NT);
+  static constexpr int TH = 64 * WAVES;
   static constexpr int KROW = D * 2 + 16;         // padded K row
   static constexpr int KBUF = (KT * KROW + 1023) / 1024 * 1024;  // whole DMA blocks
   static constexpr int VBYTES = D * KT * 2;       // V^T tile: D rows x 32 keys
@@ -116,7 +116,7 @@ struct AttnParams {
 // EXACT = false: the main kernel, every chunk with a long context span. EXACT = true:
 // chunks with a short span, and chunks the main kernel flagged for a redo.
 template <int D, bool EXACT>
-__global__ __launch_bounds__(512 / (EXACT ? kExactNT : kMainNT)) void attn_core_kernel(
+__global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void attn_core_kernel(
     const AttnParams p) {
   constexpr int NT = EXACT ? kExactNT : kMainNT;
   using C = Cfg<D, NT>;
@@ -454,7 +454,7 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.G = a.Hq / a.Hkv;
-  p.QR = 256 / p.G;
+  p.QR = kAttnSlots / p.G;
   p.ntiles = (a.n + 31) / 32;
   p.exact_per_seq = attn_exact_chunks_per_seq(a.K, p.QR);
   p.max_chunks = L.max_chunks;

@@ -41,6 +41,10 @@ struct AttnLayout {
 AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D);
 int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv);
 
+// Query slots (rows x q heads of one kv head) per attention workgroup: a chunk holds
+// kAttnSlots / G consecutive rows of the anchor-major list.
+constexpr int kAttnSlots = 256;
+
 // Attention chunks whose context span is at most this many keys (the first anchors of
 // each sequence) run the exact-split variant; the RoPE kernel stores k_lo for the rows
 // of those anchors.

@@ -273,7 +273,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Upper bound on the chunk count: every sequence adds at most one partial chunk, and a
 // sequence holds at least one anchor, so S <= n.
 int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv) {
-  const int QR = 256 / std::max(1, Hq / std::max(1, Hkv));
+  const int QR = kAttnSlots / std::max(1, Hq / std::max(1, Hkv));
   return (int)((T + QR - 1) / QR + n);
 }
 
@@ -320,7 +320,7 @@ hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int3
   hipLaunchKernelGGL(qlist_kernel, dim3(nblk), dim3(kScanThreads), 0, stream, row_of, cu_seqlens,
                      blocksum, a.n, a.K, a.S, a.T, qinfo, qstart);
   hipLaunchKernelGGL(chunk_kernel, dim3(1), dim3(kScanThreads), 0, stream, cu_seqlens, qstart, a.n,
-                     a.S, 256 / (a.Hq / a.Hkv), L.max_chunks, chunks, nchunks, seq_chunk,
+                     a.S, kAttnSlots / (a.Hq / a.Hkv), L.max_chunks, chunks, nchunks, seq_chunk,
                      reinterpret_cast<int32_t*>(ws + L.flags), L.max_chunks * a.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
