@@ -31,14 +31,19 @@ namespace {
 __global__ __launch_bounds__(256) void rope_table_kernel(float* __restrict__ cos_out,
                                                          float* __restrict__ sin_out, int half,
                                                          int D, double theta, int max_pos) {
+  __shared__ double inv[512];  // theta^(-2j/D) for j < D/2 (D <= 1024)
+  for (int j = threadIdx.x; j < half && j < 512; j += blockDim.x)
+    inv[j] = pow(theta, -2.0 * (double)j / (double)D);
+  __syncthreads();
   const size_t total = (size_t)(max_pos + 1) * half;
   for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
        t += (size_t)gridDim.x * blockDim.x) {
     const int pos = (int)(t / half), j = (int)(t % half);
-    const double inv = pow(theta, -2.0 * (double)j / (double)D);
-    const double ang = (double)pos * inv;
-    cos_out[t] = (float)cos(ang);
-    sin_out[t] = (float)sin(ang);
+    const double ang = (double)pos * (j < 512 ? inv[j] : pow(theta, -2.0 * (double)j / (double)D));
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    cos_out[t] = (float)cs;
+    sin_out[t] = (float)sn;
   }
 }
 
