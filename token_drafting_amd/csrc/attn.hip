@@ -87,8 +87,40 @@ __device__ __forceinline__ int v_off(int d, int chunk) {
   return d * (KT * 2) + ((chunk ^ ((d >> 2) & 3)) << 4);
 }
 
+// Scheduling pattern for a run of N LDS reads each feeding M MFMAs: the first PF reads
+// go first, then one MFMA group and one read alternate, then the last PF MFMA groups.
+// Read-ahead depths (D = 256, 2 waves per SIMD): 2 K fragments and 3 V fragments are what
+// fits in the 256-register budget beside O (128), Q (64) and S (16); one more spills a Q
+// fragment to scratch inside the loop, whose reload then waits on the tile DMA.
+constexpr int kPrefetchK = 2, kPrefetchV = 3;
+constexpr int kSchedDsRead = 0x100, kSchedMfma = 0x008;
+template <int N, int PF, int M>
+__device__ __forceinline__ void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+#pragma unroll
+  for (int i = 0; i < N - PF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, PF * M, 0);
+}
+
 // s_waitcnt vmcnt(0): this wave's LDS-DMA writes have landed (expcnt/lgkmcnt not waited).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// A wave-uniform pointer the optimiser cannot follow across loop iterations: it stays one
+// scalar register pair (the DMA uses the scalar-base + 32-bit lane offset form) instead of
+// being strength-reduced into a 64-bit pointer per lane and per source.
+__device__ __forceinline__ const char* uniform_opaque(const char* p) {
+  asm("" : "+s"(p));
+  return p;
+}
+
+// A 32-bit lane offset kept 32-bit at its use (not hoisted as a 64-bit extension).
+__device__ __forceinline__ uint32_t lane_opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 __device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
@@ -223,15 +255,28 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
     const char* kbase = Ks + r32 * C::KROW + half * 16;
+    if constexpr (!EXACT) {
+      // K fragments are read kPrefetchK steps ahead of the MFMA that uses them, so LDS
+      // latency overlaps the MFMA chain instead of stalling each step.
+      bf16x8 kf[C::DK];
 #pragma unroll
-    for (int kk = 0; kk < C::DK; ++kk) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + kk * 32));
+      for (int kk = 0; kk < C::DK; ++kk)
+        kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + kk * 32));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(a, qf[nt][kk], s[nt]);
-      if constexpr (EXACT) {
+      for (int kk = 0; kk < C::DK; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(kf[kk], qf[nt][kk], s[nt]);
+      sched_reads_ahead<C::DK, kPrefetchK, NT>();
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < C::DK; ++kk) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + kk * 32));
         const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(Kl + (kbase - Ks) + kk * 32));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(al, qf[nt][kk], s[nt]);
+        for (int nt = 0; nt < NT; ++nt) {
+          s[nt] = mfma32(a, qf[nt][kk], s[nt]);
+          s[nt] = mfma32(al, qf[nt][kk], s[nt]);
+        }
       }
     }
     if (mode == 1) {
@@ -297,38 +342,71 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
       }
       l_run[nt] += ls;
     }
+    if constexpr (!EXACT) {
+      bf16x8 vf[C::MT][2];
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
+      for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + v_off(mt * 32 + r32, ks * 2 + half)));
+        for (int ks = 0; ks < 2; ++ks)
+          vf[mt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + v_off(mt * 32 + r32, ks * 2 + half)));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          o[nt][mt] = mfma32(a, pb[nt][ks], o[nt][mt]);
-          if constexpr (EXACT) o[nt][mt] = mfma32(a, pl[nt][ks], o[nt][mt]);
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) o[nt][mt] = mfma32(vf[mt][ks], pb[nt][ks], o[nt][mt]);
+      sched_reads_ahead<2 * C::MT, kPrefetchV, NT>();
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + v_off(mt * 32 + r32, ks * 2 + half)));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            o[nt][mt] = mfma32(a, pb[nt][ks], o[nt][mt]);
+            o[nt][mt] = mfma32(a, pl[nt][ks], o[nt][mt]);
+          }
         }
-      }
+    }
   };
 
   // ---- causal context: depth-0 key tiles, streamed by LDS DMA ----
   // A wave moves 1 KB per instruction: lane i fills bytes [16 i, 16 i + 16) of that KB.
-  auto dma_k = [&](const uint16_t* src, int t, char* dst) {
+  // Each lane's source offset inside a tile does not depend on the tile, so it is computed
+  // once; the tile base is uniform (scalar registers). The last tile may reach up to 31
+  // rows past key n - 1: the K regions carry that many rows of padding, and such keys are
+  // always masked.
+  constexpr int KI = (C::KBUF / 1024 + C::WAVES - 1) / C::WAVES;  // K blocks per wave
+  constexpr int VI = (C::VBYTES / 1024 + C::WAVES - 1) / C::WAVES;
+  uint32_t koff[KI], voff[VI];
 #pragma unroll
-    for (int i = wave; i < C::KBUF / 1024; i += C::WAVES) {
-      const int P = i * 1024 + lane * 16;
-      const int key = P / C::KROW, off = P - key * C::KROW;
-      const bool real = key < KT && off < D * 2;  // else padding: any valid source
-      const int pos = min(t * KT + (real ? key : 0), n - 1);  // rows past n are masked
-      dma16(src + ((size_t)pos * Hkv + g) * D + (real ? off >> 1 : 0), dst + i * 1024);
+  for (int j = 0; j < KI; ++j) {
+    const int P = (wave + j * C::WAVES) * 1024 + lane * 16;
+    const int key = P / C::KROW, off = P - key * C::KROW;
+    const bool real = key < KT && off < D * 2;  // else padding: any valid source
+    koff[j] = real ? (uint32_t)(key * Hkv * D * 2 + off) : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < VI; ++j) {
+    const int P = (wave + j * C::WAVES) * 1024 + lane * 16;
+    const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 2) & 3);
+    voff[j] = (uint32_t)((d * KT + c * 8) * 2);
+  }
+  auto dma_k = [&](const uint16_t* src, int t, char* dst) {
+    const char* base = uniform_opaque(reinterpret_cast<const char*>(src + ((size_t)t * KT * Hkv + g) * D));
+#pragma unroll
+    for (int j = 0; j < KI; ++j) {
+      const int i = wave + j * C::WAVES;
+      if (i < C::KBUF / 1024) dma16(base + lane_opaque(koff[j]), dst + i * 1024);
     }
   };
   auto dma_v = [&](int t, char* dst) {
-    const uint16_t* vsrc = p.vt + ((size_t)g * p.ntiles + t) * (size_t)(D * KT);
+    const char* base = uniform_opaque(reinterpret_cast<const char*>(p.vt + ((size_t)g * p.ntiles + t) * (size_t)(D * KT)));
 #pragma unroll
-    for (int i = wave; i < C::VBYTES / 1024; i += C::WAVES) {
-      const int P = i * 1024 + lane * 16;
-      const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 2) & 3);
-      dma16(vsrc + d * KT + c * 8, dst + i * 1024);
+    for (int j = 0; j < VI; ++j) {
+      const int i = wave + j * C::WAVES;
+      if (i < C::VBYTES / 1024) dma16(base + lane_opaque(voff[j]), dst + i * 1024);
     }
   };
   auto issue = [&](int t, char* Kd, char* Kld, char* Vd) {

@@ -289,8 +289,9 @@ AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D)
   L.qinfo = off;  off += align256((size_t)T * sizeof(int4));
   L.qstart = off; off += align256((size_t)(n + 1) * sizeof(int32_t));
   L.qrot = off;   off += align256((size_t)T * Hq * D * 2);
-  L.krot = off;   off += align256((size_t)T * Hkv * D * 2);
-  L.krot_lo = off; off += align256((size_t)T * Hkv * D * 2);
+  // K regions: 32 rows of padding so the last 32-key tile of depth-0 keys stays inside
+  L.krot = off;   off += align256((size_t)(T + 32) * Hkv * D * 2);
+  L.krot_lo = off; off += align256((size_t)(T + 32) * Hkv * D * 2);
   L.vt = off;     off += align256(ntiles * 32 * Hkv * D * 2);
   L.max_chunks = attn_max_chunks(n, T, Hq, Hkv);
   L.chunks = off; off += align256((size_t)L.max_chunks * sizeof(int2));
