@@ -41,6 +41,21 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_RECORDS = {4: "profiles/attn_core_gemma270m_32k_K4_traffic.md"}
+
+
+def traffic_bytes(config):
+    """HBM bytes per attention-core call from the stored counter record (calibrated
+    FETCH_SIZE + WRITE_SIZE), or None when there is none for this workload or it was taken
+    on different kernel sources."""
+    from token_drafting_amd import profiling
+    path = TRAFFIC_RECORDS.get(config)
+    if path is None:
+        return None
+    rec = profiling.recorded_traffic(os.path.join(os.path.dirname(os.path.abspath(__file__)), path))
+    return None if rec is None else int(round(rec["core_call_bytes"]))
+
+
 def useful_pairs(idx, depth_off, cu):
     """Allowed (query row, key row) pairs per head: sum over rows of (p - a_s + 1) + d."""
     idx = idx.astype(np.int64)
@@ -194,7 +209,7 @@ def main():
         "roofline": {"kernel": "attn_core_kernel (both launches of peagle_draft_attn_core)",
                      "bound": "mfma", "achieved": round(core_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(core_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic_bytes(args.config)},
         "input_gen_s": round(gen_s, 1),
         "wall_s_timed": round(wall, 4),
     }

@@ -5,13 +5,13 @@
 // draft token is correct iff it equals the target's argmax at the same depth; draft and
 // target share one vocabulary here. Ties go to the lowest index.
 //
-// One workgroup (4 waves) per draft. Each wave scans whole [V] rows: every lane folds its
-// 16-byte chunks into one integer key that orders like (value, -index), so the argmax
-// with the lowest-index tie rule is a plain unsigned max; a butterfly across the wave
-// finishes it. The bf16 value is mapped to an order-preserving 16-bit code (sign-
-// magnitude to offset binary, -0 folded onto +0 so that equal values tie). Then wave 0
-// takes one ballot over the K match bits; the accepted length is the number of trailing
-// ones of that mask.
+// One workgroup (4 waves) per draft. Each wave scans whole [V] rows with streaming loads,
+// four in flight per lane. Every lane folds its 16-byte chunks into one integer key that
+// orders like (value, -index), so the argmax with the lowest-index tie rule is a plain
+// unsigned max; a butterfly across the wave finishes it. The bf16 value is mapped to an
+// order-preserving 16-bit code (sign-magnitude to offset binary, -0 folded onto +0 so
+// that equal values tie). Then wave 0 takes one ballot over the K match bits; the
+// accepted length is the number of trailing ones of that mask.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,15 +53,25 @@ __device__ uint32_t row_argmax(const uint16_t* __restrict__ row, int V, bool vec
   if (vec) {
     const int nch = V / 8;
     const u32x4* src = reinterpret_cast<const u32x4*>(row);
-    for (int c = lane; c < nch; c += 64) {
-      const u32x4 w = src[c];
+    auto fold = [&](const u32x4& w, int c) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t bits = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
         const Key k = ArgKey<Key>::make(bits, (uint32_t)(c * 8 + e));
         best = k > best ? k : best;
       }
+    };
+    // kUnroll independent 16-byte loads in flight per lane before any is folded
+    constexpr int kUnroll = 4;
+    int c = lane;
+    for (; c + 64 * (kUnroll - 1) < nch; c += 64 * kUnroll) {
+      u32x4 w[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(src + c + 64 * u);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) fold(w[u], c + 64 * u);
     }
+    for (; c < nch; c += 64) fold(__builtin_nontemporal_load(src + c), c);
     done = nch * 8;
   }
   for (int i = done + lane; i < V; i += 64) {

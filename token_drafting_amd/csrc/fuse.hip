@@ -31,6 +31,16 @@ constexpr int kBChunks = BN * BK / 8 / kThreads;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK * 2 + ((chunk ^ (row & 7)) << 4); }
 
+// Workgroups are handed to the 8 XCDs round-robin by linear id, and each XCD has its own
+// L2. The linear id b is remapped so that XCD b % 8 runs a contiguous range of tile ids,
+// and tile ids enumerate the N tiles of one M block together: the N tiles that share an
+// A block run at the same time on one XCD and fetch that A block from HBM once.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int b, int tiles) {
+  const int q = tiles / kXcds, r = tiles % kXcds, x = b % kXcds;
+  return x * q + min(x, r) + b / kXcds;
+}
+
 __global__ __launch_bounds__(kThreads) void fc_gemm_kernel(
     const uint16_t* __restrict__ aux, const uint16_t* __restrict__ mask_hidden,
     const uint16_t* __restrict__ W, float* __restrict__ C, int n, int M, int N, int K) {
@@ -39,7 +49,9 @@ __global__ __launch_bounds__(kThreads) void fc_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int ntn = (N + BN - 1) / BN;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
 
   u32x4 ra[kAChunks], rb[kBChunks];
   auto load_tile = [&](int k0) {
@@ -159,7 +171,7 @@ hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* au
                        uint16_t* embed_out, hipStream_t stream) {
   (void)idx;  // depth-0 row r is anchor r; depth >= 1 rows need no anchor
   const int M = (a.T > a.n) ? a.n + 1 : a.n;
-  dim3 grid((a.H + BN - 1) / BN, (M + BM - 1) / BM);
+  const dim3 grid(((a.H + BN - 1) / BN) * ((M + BM - 1) / BM));
   hipLaunchKernelGGL(fc_gemm_kernel, grid, dim3(kThreads), 0, stream, aux, mask_hidden, fc_weight,
                      hidden_out, a.n, M, a.H, a.aux_dim);
   hipError_t e = hipGetLastError();
