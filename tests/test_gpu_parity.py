@@ -247,7 +247,7 @@ def test_accept_prefix_ties_and_signs(pe):
     bits = synth.f32_to_bf16_bits(x)
     bits[3, 2, 10] = 0x8000
     tgt = bits.copy()
-    tgt[1, 3, 9] = synth.f32_to_bf16_bits(np.float32(5.0))
+    tgt[1, 3, 9] = synth.f32_to_bf16_bits(np.array([5.0], np.float32))[0]
     dt, tt, L = pe.accept_prefix(to_dev(bits), to_dev(tgt))
     want = over.verify(bits, tgt)
     assert np.array_equal(to_host(dt), want["draft_tok"])

@@ -13,7 +13,7 @@
 //   qcount/qlist_kernel  anchor-major list of draft rows (all depths of anchor 0, then
 //                        of anchor 1, ...) with per-row (row, anchor, depth, seq start),
 //                        and qstart[p] = first entry of anchor p.
-//   chunk_kernel         the attention's chunk table (chunks never cross a sequence).
+//   chunk_count/fill     the attention's chunk table (chunks never cross a sequence).
 //   rope_rotate_kernel   q' and k' of every draft row, bf16, draft-row order.
 //   v_transpose_kernel   depth-0 v as 32-key tiles laid out [d][32 keys], keys permuted
 //                        inside each 16-key group as (0-3, 8-11, 4-7, 12-15) so that a
@@ -121,30 +121,25 @@ __global__ __launch_bounds__(kScanThreads) void qlist_kernel(
   if (b == gridDim.x - 1 && threadIdx.x == 0) qstart[n] = min(s_off + total, T);
 }
 
-// Chunks of at most QR consecutive list entries that never cross a sequence: chunk table
-// entries (first entry, entry count), sequence after sequence; seq_chunk[s] = first chunk
-// of sequence s. Also clears the per-(chunk, kv head) redo flags. One workgroup.
-__global__ __launch_bounds__(kScanThreads) void chunk_kernel(
+// Chunks of at most QR consecutive list entries that never cross a sequence, numbered
+// sequence after sequence: seq_chunk[s] = first chunk of sequence s (a scan of the
+// per-sequence chunk counts), seq_chunk[S] = *nchunks. One workgroup.
+__global__ __launch_bounds__(kScanThreads) void chunk_count_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ qstart, int n, int S, int QR,
-    int max_chunks, int2* __restrict__ chunks, int32_t* __restrict__ nchunks,
-    int32_t* __restrict__ seq_chunk, int32_t* __restrict__ flags, int nflags) {
+    int max_chunks, int32_t* __restrict__ nchunks, int32_t* __restrict__ seq_chunk) {
   __shared__ int sh[kScanThreads / 64];
-  for (int i = threadIdx.x; i < nflags; i += kScanThreads) flags[i] = 0;
   int ccarry = 0;
   for (int base = 0; base < S; base += kScanThreads) {
     const int s = base + threadIdx.x;
-    int first = 0, rows = 0, cnt = 0;
+    int cnt = 0;
     if (s < S) {
       const int a = min(max(cu[s], 0), n), e = min(max(cu[s + 1], 0), n);
-      first = qstart[a];
-      rows = max(qstart[e] - first, 0);
+      const int rows = max(qstart[e] - qstart[a], 0);
       cnt = (rows + QR - 1) / QR;
     }
     int total;
     const int at = ccarry + block_exclusive_scan(cnt, sh, &total);
     if (s < S) seq_chunk[s] = min(at, max_chunks);
-    for (int i = 0; i < cnt; ++i)
-      if (at + i < max_chunks) chunks[at + i] = make_int2(first + i * QR, min(QR, rows - i * QR));
     ccarry += total;
   }
   if (threadIdx.x == 0) {
@@ -153,26 +148,47 @@ __global__ __launch_bounds__(kScanThreads) void chunk_kernel(
   }
 }
 
-// One thread per (row, head, 8-wide chunk of the first half of the head dimension).
+// Chunk table entries (first list entry, entry count), one thread per chunk: the chunk's
+// sequence is the last s with seq_chunk[s] <= c (empty sequences share their successor's
+// start, so the last one is the non-empty sequence). Also clears the per-(chunk, kv head)
+// redo flags.
+__global__ __launch_bounds__(256) void chunk_fill_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ qstart,
+    const int32_t* __restrict__ seq_chunk, const int32_t* __restrict__ nchunks, int n, int S,
+    int QR, int max_chunks, int2* __restrict__ chunks, int32_t* __restrict__ flags, int nflags) {
+  const int nc = min(max(*nchunks, 0), max_chunks);
+  const int stride = gridDim.x * blockDim.x;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nflags; i += stride) flags[i] = 0;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < nc; c += stride) {
+    const int s = min(max(upper_index(seq_chunk, S + 1, c), 0), S - 1);
+    const int j = c - seq_chunk[s];
+    const int a = min(max(cu[s], 0), n), e = min(max(cu[s + 1], 0), n);
+    const int first = qstart[a], rows = max(qstart[e] - first, 0);
+    chunks[c] = make_int2(first + j * QR, min(QR, rows - j * QR));
+  }
+}
+
+// One thread per (list entry, head, 8-wide chunk of the first half of the head
+// dimension). The anchor-major list entry gives the draft row, its anchor, depth and
+// sequence start, so the position value is one load away. Idx is 32-bit unless the
+// work count needs 64 bits.
+template <typename Idx>
 __global__ __launch_bounds__(256) void rope_rotate_kernel(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ depth_off,
-    const int32_t* __restrict__ cu, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const int4* __restrict__ qinfo, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const float* __restrict__ cosT, const float* __restrict__ sinT, uint16_t* __restrict__ qr,
-    uint16_t* __restrict__ kr, uint16_t* __restrict__ kr_lo, int n, int K, int S, int T, int Hq,
-    int Hkv, int D, int max_pos) {
+    uint16_t* __restrict__ kr, uint16_t* __restrict__ kr_lo, int n, int T, int Hq, int Hkv, int D,
+    int max_pos) {
   const int half = D / 2, cpr = half / 8;  // chunks per head
-  const int heads = Hq + Hkv;
-  const size_t total = (size_t)T * heads * cpr;
-  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
-       t += (size_t)gridDim.x * blockDim.x) {
-    const int c = (int)(t % cpr);
-    const int h = (int)((t / cpr) % heads);
-    const int r = (int)(t / ((size_t)cpr * heads));
-    const int d = min(max(upper_index(depth_off, K + 1, r), 0), K - 1);
-    const int p = min(max(idx[r], 0), n - 1);
-    const int s = min(max(upper_index(cu, S + 1, p), 0), S);
-    const int offset = p - cu[s];  // anchor's offset in its sequence
-    const int pos = min(max(offset + d, 0), max_pos);
+  const Idx heads = (Idx)(Hq + Hkv), per_entry = heads * (Idx)cpr;
+  const Idx total = (Idx)T * per_entry;
+  for (Idx t = (Idx)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (Idx)gridDim.x * blockDim.x) {
+    const Idx j = t / per_entry, rem = t - j * per_entry;
+    const int h = (int)(rem / (Idx)cpr), c = (int)(rem - (Idx)h * cpr);
+    const int4 e = qinfo[j];
+    const int r = min(max(e.x, 0), T - 1);
+    const int p = min(max(e.y, 0), n - 1);
+    const int offset = p - min(max(e.w, 0), p);  // anchor's offset in its sequence
+    const int pos = min(max(offset + e.z, 0), max_pos);
     const uint16_t* src = (h < Hq) ? q + ((size_t)r * Hq + h) * D : k + ((size_t)r * Hkv + (h - Hq)) * D;
     uint16_t* dst = (h < Hq) ? qr + ((size_t)r * Hq + h) * D : kr + ((size_t)r * Hkv + (h - Hq)) * D;
     const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + c * 8);
@@ -325,17 +341,29 @@ hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int3
                      blocksum);
   hipLaunchKernelGGL(qlist_kernel, dim3(nblk), dim3(kScanThreads), 0, stream, row_of, cu_seqlens,
                      blocksum, a.n, a.K, a.S, a.T, qinfo, qstart);
-  hipLaunchKernelGGL(chunk_kernel, dim3(1), dim3(kScanThreads), 0, stream, cu_seqlens, qstart, a.n,
-                     a.S, kAttnSlots / (a.Hq / a.Hkv), L.max_chunks, chunks, nchunks, seq_chunk,
-                     reinterpret_cast<int32_t*>(ws + L.flags), L.max_chunks * a.Hkv);
+  const int QR = kAttnSlots / (a.Hq / a.Hkv);
+  hipLaunchKernelGGL(chunk_count_kernel, dim3(1), dim3(kScanThreads), 0, stream, cu_seqlens, qstart,
+                     a.n, a.S, QR, L.max_chunks, nchunks, seq_chunk);
+  {
+    // chunk count <= ceil(T / QR) + S; the flags cover max_chunks * Hkv entries
+    const int64_t work = std::max<int64_t>((int64_t)(a.T + QR - 1) / QR + a.S,
+                                           (int64_t)L.max_chunks * a.Hkv);
+    const int blocks = (int)std::min<int64_t>((work + 255) / 256, 2048);
+    hipLaunchKernelGGL(chunk_fill_kernel, dim3(blocks), dim3(256), 0, stream, cu_seqlens, qstart,
+                       seq_chunk, nchunks, a.n, a.S, QR, L.max_chunks, chunks,
+                       reinterpret_cast<int32_t*>(ws + L.flags), L.max_chunks * a.Hkv);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const size_t work = (size_t)a.T * (a.Hq + a.Hkv) * (a.D / 16);
   const int blocks = (int)std::min<size_t>((work + 255) / 256, 1 << 20);
-  hipLaunchKernelGGL(rope_rotate_kernel, dim3(blocks), dim3(256), 0, stream, idx, depth_off,
-                     cu_seqlens, q, k, rope_cos, rope_sin, qr, kr, kr_lo, a.n, a.K, a.S, a.T, a.Hq,
-                     a.Hkv, a.D, a.max_pos);
+  if (work < (size_t)UINT32_MAX)
+    hipLaunchKernelGGL(rope_rotate_kernel<uint32_t>, dim3(blocks), dim3(256), 0, stream, qinfo, q, k,
+                       rope_cos, rope_sin, qr, kr, kr_lo, a.n, a.T, a.Hq, a.Hkv, a.D, a.max_pos);
+  else
+    hipLaunchKernelGGL(rope_rotate_kernel<size_t>, dim3(blocks), dim3(256), 0, stream, qinfo, q, k,
+                       rope_cos, rope_sin, qr, kr, kr_lo, a.n, a.T, a.Hq, a.Hkv, a.D, a.max_pos);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
