@@ -56,6 +56,23 @@ def _read(folder: str, counter: str):
     return sorted(out)
 
 
+def _read_all(folder: str):
+    """{dispatch id: {"name", "dur_ns", counter: value}} of one counter run."""
+    out = {}
+    for root, _, files in os.walk(folder):
+        for fn in files:
+            if fn.endswith("counter_collection.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    for r in csv.DictReader(f):
+                        d = out.setdefault(int(r["Dispatch_Id"]), {
+                            "name": _short(r["Kernel_Name"]),
+                            "dur_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    if not out:
+        raise SystemExit(f"no counter rows under {folder}")
+    return out
+
+
 def _calibration(rows, copy_bytes: int, counter: str) -> float:
     """bytes per counter KiB, from the largest plain-copy dispatch of the run."""
     copies = [r for r in rows if "copyBuffer" in r[1]]
@@ -123,6 +140,69 @@ def write_summary(path: str, summary: dict, command: str) -> None:
         f.write("\n".join(lines))
 
 
+SIMDS = 256 * 4  # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8
+MFMA_BF16_FLOP_PER_MOP = 512  # SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512-FLOP units
+
+
+def kernel_table(mfma_dir: str, fetch_dir: str, write_dir: str, copy_mib: int) -> list:
+    """Per kernel: duration, bf16 MFMA FLOP/s, MFMA-busy share of the SIMD cycles, shader
+    clock seen by the dispatch, and calibrated HBM bytes and GB/s."""
+    copy_bytes = copy_mib << 20
+    fetch, write = _read_all(fetch_dir), _read_all(write_dir)
+    f_fac = _calibration([(k, v["name"], 0, v["FETCH_SIZE"]) for k, v in fetch.items()],
+                         copy_bytes, "FETCH_SIZE")
+    w_fac = _calibration([(k, v["name"], 0, v["WRITE_SIZE"]) for k, v in write.items()],
+                         copy_bytes, "WRITE_SIZE")
+    acc = defaultdict(lambda: defaultdict(list))
+    for v in _read_all(mfma_dir).values():
+        a = acc[v["name"]]
+        a["dur"].append(v["dur_ns"])
+        a["mops"].append(v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))
+        a["busy"].append(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0))
+        a["gui"].append(v.get("GRBM_GUI_ACTIVE", 0.0))
+    for run, key, fac, ctr in ((fetch, "rd", f_fac, "FETCH_SIZE"), (write, "wr", w_fac, "WRITE_SIZE")):
+        for v in run.values():
+            acc[v["name"]][key].append(v[ctr] * fac)
+            acc[v["name"]][key + "_dur"].append(v["dur_ns"])
+    rows = []
+    for name, a in acc.items():
+        if "copyBuffer" in name or name.startswith("at::") or not a["dur"]:
+            continue
+        mean = lambda x: sum(x) / len(x) if x else 0.0
+        dur = mean(a["dur"]) * 1e-9
+        gui = mean(a["gui"]) / XCDS
+        rd, wr = mean(a["rd"]), mean(a["wr"])
+        io_dur = mean(a["rd_dur"] + a["wr_dur"]) * 1e-9
+        rows.append({
+            "kernel": name, "calls": len(a["dur"]), "us": dur * 1e6,
+            "bf16_tflops": mean(a["mops"]) * MFMA_BF16_FLOP_PER_MOP / dur / 1e12 if dur else 0.0,
+            "mfma_busy": mean(a["busy"]) / (SIMDS * gui) if gui else 0.0,
+            "clock_ghz": gui / dur / 1e9 if dur else 0.0,
+            "read_mb": rd / 1e6, "write_mb": wr / 1e6,
+            "hbm_gbps": (rd + wr) / io_dur / 1e9 if io_dur else 0.0,
+        })
+    return sorted(rows, key=lambda r: -r["us"])
+
+
+def write_kernel_table(path: str, rows: list, title: str, command: str) -> None:
+    lines = [f"# {title}", "", "Counter runs (each its own process):", "", "```", command, "```", "",
+             "Columns: dispatch duration in the MFMA-counter run; bf16 TFLOP/s = "
+             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / duration; MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs); clock = "
+             "GRBM_GUI_ACTIVE / 8 / duration; HBM bytes = FETCH_SIZE and WRITE_SIZE scaled by "
+             "the plain copy of known size in the same runs; GB/s = those bytes over the "
+             "byte runs' own dispatch durations.", "",
+             "| kernel | calls | us | bf16 TFLOP/s | MFMA busy | clock GHz | read MB | written MB | HBM GB/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{r['kernel']}` | {r['calls']} | {r['us']:.1f} | {r['bf16_tflops']:.1f} | "
+                     f"{100 * r['mfma_busy']:.1f}% | {r['clock_ghz']:.2f} | {r['read_mb']:.2f} | "
+                     f"{r['write_mb']:.2f} | {r['hbm_gbps']:.0f} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def recorded_traffic(path: str):
     """The stored record if it was taken on the current kernel sources, else None."""
     try:
@@ -142,10 +222,18 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--fetch", required=True, help="rocprofv3 output folder of the FETCH_SIZE run")
     ap.add_argument("--write", required=True, help="rocprofv3 output folder of the WRITE_SIZE run")
+    ap.add_argument("--mfma", help="rocprofv3 output folder of the MFMA counter run; with it, "
+                    "write the per-kernel table instead of the traffic record")
     ap.add_argument("--copy-mib", type=int, required=True, help="calibration copy size of the runs")
     ap.add_argument("--out", required=True)
+    ap.add_argument("--title", default="Per-kernel counters")
     ap.add_argument("--command", required=True, help="the counter commands, for the record")
     a = ap.parse_args()
+    if a.mfma:
+        rows = kernel_table(a.mfma, a.fetch, a.write, a.copy_mib)
+        write_kernel_table(a.out, rows, a.title, a.command)
+        print(json.dumps(rows[:3]))
+        return
     s = summarize(a.fetch, a.write, a.copy_mib)
     write_summary(a.out, s, a.command)
     print(json.dumps(s["record"]))
