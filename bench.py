@@ -34,7 +34,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle sample size (rows)")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle sample size in query rows (0: sized for about 10-20 s of "
+                         "host time from the oracle's cost per row, Hq * T * D)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps, "
                          "so a counter run can scale its byte counters against known traffic")
@@ -227,6 +229,11 @@ def cpu_baseline(cfg, seed, qkv, cu, idx, depth_off, rows_wanted):
     from oracle import attention as oattn
 
     T = int(depth_off[-1])
+    if rows_wanted <= 0:
+        # the dense oracle costs ~Hq * T * D per query row; 6144 rows of the 32K, K=4,
+        # D=256 workload (4 * 83001 * 256 per row) take about 11 s on 16 host threads
+        rows_wanted = int(round(6144 * (4 * 83001 * 256) / (cfg["Hq"] * T * cfg["D"])))
+        rows_wanted = max(64, rows_wanted)
     rng = np.random.default_rng(1234)
     rows = np.sort(rng.choice(T, size=min(rows_wanted, T), replace=False))
     _, keys = useful_pairs(idx, depth_off, cu)
