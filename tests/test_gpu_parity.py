@@ -99,8 +99,11 @@ def _fuse_case(pe, n, K, H, A, seed, rows=None, vocab=32000):
     return h, e, want
 
 
+# aux widths that are multiples of 192 take the DMA-fed GEMM (ragged row and column tiles
+# included); the others take the register-staged one
 @pytest.mark.parametrize("n,K,H,A", [(256, 4, 256, 1536), (300, 4, 136, 520), (97, 1, 64, 64),
-                                     (513, 8, 200, 776)])
+                                     (513, 8, 200, 776), (300, 4, 136, 384), (97, 1, 64, 192),
+                                     (513, 8, 200, 960)])
 def test_fuse_small_full(pe, n, K, H, A):
     print(f"fuse n={n} K={K} H={H} A={A}", flush=True)
     h, e, want = _fuse_case(pe, n, K, H, A, seed=11)

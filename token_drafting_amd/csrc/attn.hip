@@ -87,45 +87,10 @@ __device__ __forceinline__ int v_off(int d, int chunk) {
   return d * (KT * 2) + ((chunk ^ ((d >> 2) & 3)) << 4);
 }
 
-// Scheduling pattern for a run of N LDS reads each feeding M MFMAs: the first PF reads
-// go first, then one MFMA group and one read alternate, then the last PF MFMA groups.
 // Read-ahead depths (D = 256, 2 waves per SIMD): 2 K fragments and 3 V fragments are what
 // fits in the 256-register budget beside O (128), Q (64) and S (16); one more spills a Q
 // fragment to scratch inside the loop, whose reload then waits on the tile DMA.
 constexpr int kPrefetchK = 2, kPrefetchV = 3;
-constexpr int kSchedDsRead = 0x100, kSchedMfma = 0x008;
-template <int N, int PF, int M>
-__device__ __forceinline__ void sched_reads_ahead() {
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
-#pragma unroll
-  for (int i = 0; i < N - PF; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, PF * M, 0);
-}
-
-// s_waitcnt vmcnt(0): this wave's LDS-DMA writes have landed (expcnt/lgkmcnt not waited).
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// A wave-uniform pointer the optimiser cannot follow across loop iterations: it stays one
-// scalar register pair (the DMA uses the scalar-base + 32-bit lane offset form) instead of
-// being strength-reduced into a 64-bit pointer per lane and per source.
-__device__ __forceinline__ const char* uniform_opaque(const char* p) {
-  asm("" : "+s"(p));
-  return p;
-}
-
-// A 32-bit lane offset kept 32-bit at its use (not hoisted as a 64-bit extension).
-__device__ __forceinline__ uint32_t lane_opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
 
 struct AttnParams {
   const int4* qinfo;

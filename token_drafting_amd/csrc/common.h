@@ -50,4 +50,48 @@ __device__ __forceinline__ int lower_count(const int32_t* a, int len, int32_t x)
   return lo;
 }
 
+// ---- LDS DMA (global_load_lds_dwordx4) and scheduling helpers ----
+
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maxima (N < 16): at most N of
+// this wave's vector-memory operations (here: LDS-DMA tile loads) are still outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ void wait_dma() { wait_vm<0>(); }
+
+// A wave-uniform pointer the optimiser cannot follow across loop iterations: it stays one
+// scalar register pair (the DMA uses the scalar-base + 32-bit lane offset form) instead of
+// being strength-reduced into a 64-bit pointer per lane and per source.
+__device__ __forceinline__ const char* uniform_opaque(const char* p) {
+  asm("" : "+s"(p));
+  return p;
+}
+
+// A 32-bit lane offset kept 32-bit at its use (not hoisted as a 64-bit extension).
+__device__ __forceinline__ uint32_t lane_opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Scheduling pattern for a run of N LDS reads each feeding M MFMAs: the first PF reads
+// go first, then one MFMA group and one read alternate, then the last PF MFMA groups.
+constexpr int kSchedDsRead = 0x100, kSchedMfma = 0x008;
+template <int N, int PF, int M>
+__device__ __forceinline__ void sched_reads_ahead() {
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+#pragma unroll
+  for (int i = 0; i < N - PF; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, PF * M, 0);
+}
+
 }  // namespace peagle
