@@ -203,6 +203,45 @@ def write_kernel_table(path: str, rows: list, title: str, command: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+def write_trace_summary(path: str, trace_dir: str, bench_log: str, title: str, command: str,
+                        timed: int) -> None:
+    """Kernel-trace summary: per-kernel durations from rocprofv3's kernel trace, and the
+    agreement of the attention launches' last `timed` calls with bench.py's live timing."""
+    rows = []
+    for root, _, files in os.walk(trace_dir):
+        for fn in files:
+            if fn.endswith("kernel_trace.csv"):
+                with open(os.path.join(root, fn)) as f:
+                    rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    per = defaultdict(list)
+    for r in rows:
+        per[_short(r["Kernel_Name"])].append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    total = sum(d for v in per.values() for _, d in v)
+    lines = [f"# {title}", "", "Command (from the repository root):", "", "    " + command, "",
+             "Durations in microseconds from the kernel trace (all calls, warm-up included).", "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+        d = [x for _, x in v]
+        lines.append(f"| `{name}` | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {min(d) / 1e3:.1f} | "
+                     f"{max(d) / 1e3:.1f} | {100 * sum(d) / total:.2f} |")
+    core = [k for k in per if any(c in k for c in CORE_KERNELS)]
+    last = sum(sum(d for _, d in sorted(per[k])[-timed:]) / timed for k in core) / 1e3
+    live = None
+    with open(bench_log) as f:
+        for line in f:
+            if line.startswith("{"):
+                live = json.loads(line)["stage_ms"]["attn_core"] * 1e3
+    lines += ["", f"Agreement with the live timing: over the last {timed} calls the attention core "
+              f"launches ({', '.join('`' + k + '`' for k in sorted(core))}) average {last:.1f} us "
+              f"per call in the trace; bench.py's HIP events on the launch stream measured "
+              f"{live:.1f} us per call in the same run." if live is not None else "", ""]
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+
+
 def recorded_traffic(path: str):
     """The stored record if it was taken on the current kernel sources, else None."""
     try:
@@ -220,15 +259,24 @@ def recorded_traffic(path: str):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--fetch", required=True, help="rocprofv3 output folder of the FETCH_SIZE run")
-    ap.add_argument("--write", required=True, help="rocprofv3 output folder of the WRITE_SIZE run")
+    ap.add_argument("--fetch", help="rocprofv3 output folder of the FETCH_SIZE run")
+    ap.add_argument("--write", help="rocprofv3 output folder of the WRITE_SIZE run")
+    ap.add_argument("--trace", help="rocprofv3 kernel-trace folder; with --bench-log, write the "
+                    "kernel-trace summary")
+    ap.add_argument("--bench-log", help="stdout of the traced bench.py run")
+    ap.add_argument("--timed", type=int, default=5, help="timed steps of the traced run")
     ap.add_argument("--mfma", help="rocprofv3 output folder of the MFMA counter run; with it, "
                     "write the per-kernel table instead of the traffic record")
-    ap.add_argument("--copy-mib", type=int, required=True, help="calibration copy size of the runs")
+    ap.add_argument("--copy-mib", type=int, default=0, help="calibration copy size of the runs")
     ap.add_argument("--out", required=True)
     ap.add_argument("--title", default="Per-kernel counters")
     ap.add_argument("--command", required=True, help="the counter commands, for the record")
     a = ap.parse_args()
+    if a.trace:
+        write_trace_summary(a.out, a.trace, a.bench_log, a.title, a.command, a.timed)
+        return
+    if not (a.fetch and a.write and a.copy_mib):
+        raise SystemExit("--fetch, --write and --copy-mib are required for counter summaries")
     if a.mfma:
         rows = kernel_table(a.mfma, a.fetch, a.write, a.copy_mib)
         write_kernel_table(a.out, rows, a.title, a.command)
