@@ -310,14 +310,15 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
     if constexpr (!EXACT) {
       bf16x8 vf[C::MT][2];
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int mt = 0; mt < C::MT; ++mt)
           vf[mt][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(Vs + v_off(mt * 32 + r32, ks * 2 + half)));
+      // k-step outer: the two MFMAs into one O tile are MT apart, not back to back
 #pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[nt][mt] = mfma32(vf[mt][ks], pb[nt][ks], o[nt][mt]);
       sched_reads_ahead<2 * C::MT, kPrefetchV, NT>();
