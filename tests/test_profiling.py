@@ -1,0 +1,67 @@
+"""Host logic of the rocprofv3 summaries bench.py relies on (no GPU needed).
+
+The traffic record must scale each byte counter by the calibration copy found in the same
+run, sum both attention-core launches, and be reported only while the attention sources
+it was taken on are unchanged.
+"""
+import csv
+import json
+import os
+
+from token_drafting_amd import profiling
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+          "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+          "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+          "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _write_run(folder, counter, rows):
+    os.makedirs(folder, exist_ok=True)
+    with open(os.path.join(folder, "pmc_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({k: 0 for k in FIELDS} | {
+                "Dispatch_Id": i + 1, "Kernel_Name": name, "Grid_Size": 1024,
+                "Counter_Name": counter, "Counter_Value": value,
+                "Start_Timestamp": 1000 * i, "End_Timestamp": 1000 * i + 500})
+
+
+def test_traffic_record_scales_by_the_copy_and_sums_core_launches(tmp_path):
+    main = "void peagle::(anonymous namespace)::attn_core_kernel<256, false>(peagle::AttnParams)"
+    exact = "void peagle::(anonymous namespace)::attn_core_kernel<256, true>(peagle::AttnParams)"
+    # the 1 MiB copy reads as 512 KiB (128-byte requests counted as 64) and writes 1024 KiB
+    _write_run(tmp_path / "f", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 512.0), (main, 100.0),
+                                              (exact, 10.0), ("other_kernel", 7.0)])
+    _write_run(tmp_path / "w", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1024.0), (main, 50.0),
+                                              (exact, 5.0), ("other_kernel", 3.0)])
+    s = profiling.summarize(str(tmp_path / "f"), str(tmp_path / "w"), copy_mib=1)
+    rec = s["record"]
+    assert rec["fetch_factor_bytes_per_kib"] == 2048.0
+    assert rec["write_factor_bytes_per_kib"] == 1024.0
+    assert rec["core_call_fetch_bytes"] == (100.0 + 10.0) * 2048.0
+    assert rec["core_call_write_bytes"] == (50.0 + 5.0) * 1024.0
+    assert rec["core_call_bytes"] == rec["core_call_fetch_bytes"] + rec["core_call_write_bytes"]
+    assert rec["kernel_source_sha256"] == profiling.kernel_source_digest()
+
+
+def test_recorded_traffic_is_withheld_when_sources_differ(tmp_path):
+    good = {"kernel_source_sha256": profiling.kernel_source_digest(), "core_call_bytes": 123.0}
+    stale = dict(good, kernel_source_sha256="0" * 64)
+    p_good, p_stale = tmp_path / "good.md", tmp_path / "stale.md"
+    p_good.write_text("# summary\n\n" + profiling.RECORD_TAG + " " + json.dumps(good) + "\n")
+    p_stale.write_text(profiling.RECORD_TAG + " " + json.dumps(stale) + "\n")
+    assert profiling.recorded_traffic(str(p_good))["core_call_bytes"] == 123.0
+    assert profiling.recorded_traffic(str(p_stale)) is None
+    assert profiling.recorded_traffic(str(tmp_path / "missing.md")) is None
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
