@@ -22,6 +22,8 @@ Modules:
                 substitution at depths >= 1.
 - ``rope``      rotary embedding gathered by position value.
 - ``attention`` the multi-depth draft attention, with an explicit dense mask.
+- ``decode``    the same attention at inference: K new rows per request at one base
+                position over a KV cache (the flat [context, mask_1 ..] layout).
 - ``verify``    greedy verification and the longest accepted prefix.
 
 Inputs are bf16 bit patterns (uint16) or integer arrays; ``bf16`` converts the
@@ -32,4 +34,4 @@ closed forms, published test outputs, library routines, independent formulations
 or brute force. The SplitMix64 hash is pinned by the generator's published
 outputs for seed 0.
 """
-from . import bf16, cod, fuse, rope, attention, verify  # noqa: F401
+from . import bf16, cod, fuse, rope, attention, decode, verify  # noqa: F401
