@@ -188,6 +188,77 @@ int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,
                          int32_t *draft_tok, int32_t *target_tok, int32_t *accept_len,
                          void *stream);
 
+/*
+ * Draft attention at inference (the decode shape) [N, parity section: at inference one
+ * flat parallel forward over [context, mask_1, ..., mask_{K-1}]; G, "Inference Process":
+ * all depths drafted in one pass, drafting repeats from the last accepted token].
+ *
+ * Request b (of B) has L_b = cu_ctx[b+1] - cu_ctx[b] context tokens in the KV cache and
+ * K new rows: row d sits at position L_b + d (d = 0 the anchor, the last accepted token;
+ * d >= 1 the mask rows). Row d attends to every cache key of its request and to new rows
+ * 0 .. d, i.e. causal attention over the flat sequence: the forward's predicate with a
+ * single anchor. Cache keys are stored already rotated at their positions 0 .. L_b - 1.
+ *
+ * The V cache is kept in attention tiles, one tile per 32 keys of a request:
+ *   v_tiles  bf16[Hkv][ntiles][D][32], ntiles = floor(total_ctx / 32) + B + 1;
+ *            tile floor(cu_ctx[b] / 32) + b + j of a kv head holds keys 32j .. 32j + 31
+ *            of request b transposed (dim-major), zero past L_b, the keys of each group
+ *            of 16 stored in the order 0-3, 8-11, 4-7, 12-15.
+ * peagle_decode_pack_v writes that layout from a natural V cache.
+ */
+
+/* Bytes of the V tile layout for a cache of total_ctx keys over num_reqs requests. */
+size_t peagle_decode_v_tiles_bytes(int64_t total_ctx, int32_t num_reqs, int32_t num_kv_heads,
+                                   int32_t head_dim);
+
+/*
+ * peagle_decode_pack_v -- V cache (natural layout) -> V tiles.
+ *   cu_ctx     int32[B+1]  request starts in the cache, 0 = cu[0] <= ... <= cu[B] = total_ctx
+ *   max_ctx    (host) >= every L_b; bounds the launch
+ *   v_cache    bf16[total_ctx, Hkv, D]
+ *   v_tiles    bf16, v_tiles_bytes >= peagle_decode_v_tiles_bytes(...)   out
+ * Tiles of a request are written in full (zero padded); the spare tiles between
+ * requests are left untouched. head_dim in {64, 128, 256}; 1 <= B <= 65535.
+ */
+int peagle_decode_pack_v(int32_t num_reqs, const int32_t *cu_ctx, int64_t total_ctx,
+                         int32_t max_ctx, const peagle_bf16 *v_cache, int32_t num_kv_heads,
+                         int32_t head_dim, peagle_bf16 *v_tiles, size_t v_tiles_bytes,
+                         void *stream);
+
+/* Bytes of workspace peagle_draft_decode_attn needs for these sizes (0 on bad arguments). */
+size_t peagle_draft_decode_workspace_bytes(int32_t num_reqs, int32_t K, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t max_ctx);
+
+/*
+ * peagle_draft_decode_attn -- the decode-shaped draft attention. Split-KV: the cache
+ * tiles of each (request, kv head) are shared out among several waves whose partial
+ * softmax states a second kernel merges (both enqueued on `stream`).
+ *   cu_ctx         int32[B+1]          as for peagle_decode_pack_v
+ *   total_ctx      (host) cu_ctx[B];   max_ctx (host) >= every L_b
+ *   k_cache        bf16[total_ctx, Hkv, D]   rotated keys
+ *   v_tiles        from peagle_decode_pack_v (same cu_ctx)
+ *   q              bf16[B, K, Hq, D]   pre-RoPE
+ *   k, v           bf16[B, K, Hkv, D]  pre-RoPE k of the new rows; v
+ *   softmax_scale  usually 1/sqrt(D)
+ *   rope_cos/sin   fp32[rope_max_pos+1, D/2] from peagle_rope_table;
+ *                  rope_max_pos >= max_ctx + K - 1
+ *   out            fp32[B, K, Hq, D]   out
+ *   lse            fp32[B, K, Hq]      out, natural-log softmax denominators; may be NULL
+ *   workspace      >= peagle_draft_decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx)
+ *                  bytes, 256-byte aligned scratch
+ * head_dim in {64, 128, 256}; Hq % Hkv == 0; 1 <= K <= 32; 1 <= B <= 65535.
+ * total_ctx = 0 (every request empty) is allowed; k_cache and v_tiles may then be NULL.
+ */
+int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t *cu_ctx,
+                             int64_t total_ctx, int32_t max_ctx, const peagle_bf16 *k_cache,
+                             const peagle_bf16 *v_tiles, size_t v_tiles_bytes,
+                             const peagle_bf16 *q, const peagle_bf16 *k, const peagle_bf16 *v,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             float softmax_scale, const float *rope_cos, const float *rope_sin,
+                             int32_t rope_max_pos, float *out, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

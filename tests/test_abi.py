@@ -131,3 +131,59 @@ def test_workspace_bytes(lib):
     assert 0 < a < b
     assert a % 256 == 0
     assert peagle.attn_workspace_bytes(0, 10, 4, 1, 64) == 0
+
+
+def test_decode_argument_errors(lib):
+    base = dict(B=3, K=4, total=100, max_ctx=60, vtb=1 << 30, Hq=4, Hkv=1, D=64, scale=0.125,
+                max_pos=63, ws=1 << 30)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return _code("peagle_draft_decode_attn", a["B"], a["K"], None, a["total"], a["max_ctx"],
+                     None, None, a["vtb"], None, None, None, a["Hq"], a["Hkv"], a["D"], a["scale"],
+                     None, None, a["max_pos"], None, None, None, a["ws"], None)
+    assert call() == peagle.ERR_ARG                       # NULL pointers
+    assert call(D=96) == peagle.ERR_UNSUPPORTED
+    assert call(K=33) == peagle.ERR_UNSUPPORTED
+    assert call(K=0) == peagle.ERR_ARG
+    assert call(B=0) == peagle.ERR_ARG
+    assert call(B=65536) == peagle.ERR_ARG
+    assert call(Hq=5, Hkv=2) == peagle.ERR_ARG
+    assert call(max_ctx=101) == peagle.ERR_ARG            # above total_ctx
+    assert call(max_pos=62) == peagle.ERR_ARG             # below max_ctx + K - 1
+    assert call(scale=float("inf")) == peagle.ERR_ARG
+    assert _code("peagle_decode_pack_v", 3, None, 100, 60, None, 1, 64, None, 1 << 30,
+                 None) == peagle.ERR_ARG
+    assert _code("peagle_decode_pack_v", 3, None, 100, 60, None, 1, 96, None, 1 << 30,
+                 None) == peagle.ERR_UNSUPPORTED
+
+
+def test_decode_sizes(lib):
+    # V tiles: floor(total / 32) + B + 1 tiles of D x 32 bf16 per kv head
+    assert peagle.decode_v_tiles_bytes(1000, 3, 2, 128) == (1000 // 32 + 3 + 1) * 2 * 128 * 32 * 2
+    assert peagle.decode_v_tiles_bytes(0, 1, 1, 64) == 2 * 64 * 32 * 2
+    assert peagle.decode_v_tiles_bytes(-1, 1, 1, 64) == 0
+    a = peagle.decode_workspace_bytes(8, 4, 4, 1, 256, 32768)
+    b = peagle.decode_workspace_bytes(64, 4, 4, 1, 256, 32768)
+    assert 0 < a < b and a % 256 == 0
+    assert peagle.decode_workspace_bytes(8, 33, 4, 1, 256, 100) == 0
+
+
+def test_decode_tile_bases_never_overlap():
+    """Request b's V tiles start at floor(cu[b] / 32) + b: for any split of a cache into
+    requests the ranges [start, start + ceil(L_b / 32)) are disjoint and below
+    floor(total / 32) + B + 1 (host arithmetic of the layout, no GPU)."""
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        B = int(rng.integers(1, 12))
+        lens = rng.integers(0, 200, B)
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        total = int(cu[-1])
+        ntiles = total // 32 + B + 1
+        prev_end = 0
+        for b in range(B):
+            start = cu[b] // 32 + b
+            end = start + (lens[b] + 31) // 32
+            assert start >= prev_end and end <= ntiles
+            if lens[b]:
+                prev_end = end

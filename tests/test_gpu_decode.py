@@ -1,0 +1,108 @@
+"""GPU parity of the decode-shaped draft attention (K new rows per request over a KV cache)
+against the float64 oracle on the same seeded inputs: out within max|diff| <= 1e-2 and
+relative L2 <= 5e-3, lse within relative L2 1e-3. Small cases are compared in full; the
+full-size inference workloads on sampled requests that the oracle recomputes alone.
+"""
+import numpy as np
+import pytest
+
+from oracle import decode as odec
+from token_drafting_amd import synth
+from tests.helpers import assert_close, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pe():
+    import torch
+    from token_drafting_amd import peagle
+    assert torch.cuda.is_available()
+    peagle.lib()
+    return peagle
+
+
+def _run(pe, inp, lens, K, D, theta, device_inputs=False):
+    """Pack V, build the RoPE table and run the decode attention on device tensors."""
+    cu = inp["cu_ctx"] if device_inputs else to_dev(inp["cu_ctx"])
+    kc = inp["k_cache"] if device_inputs else to_dev(inp["k_cache"])
+    vc = inp["v_cache"] if device_inputs else to_dev(inp["v_cache"])
+    q, k, v = ((inp[t] if device_inputs else to_dev(inp[t])) for t in ("q", "k", "v"))
+    max_ctx = int(max(lens)) if len(lens) else 0
+    cos, sin = pe.rope_table(D, theta, max_ctx + K - 1)
+    vt = pe.decode_pack_v(cu, max_ctx, vc)
+    out, lse, _ = pe.draft_decode_attn(cu, max_ctx, kc, vt, q, k, v, cos, sin)
+    return to_host(out), to_host(lse)
+
+
+DECODE_SMALL = [
+    # (lens, K, Hq, Hkv, D, theta)
+    ([37], 4, 4, 1, 64, 1e4),                             # one request, ragged tile
+    ([0, 1, 31, 32, 33, 100], 4, 4, 1, 256, 1e4),          # empty cache, tile edges
+    ([700, 1500, 64], 8, 32, 8, 128, 5e5),                 # Llama-8B heads, 32 columns a wave
+    ([300, 5], 8, 8, 1, 128, 1e4),                         # G*K = 64: two column groups
+    ([250, 17], 1, 4, 2, 64, 1e4),                         # K = 1: plain decode
+    ([1000, 2000], 32, 4, 1, 256, 1e4),                    # K = 32 (the maximum), 8 groups
+    ([0, 0, 0], 4, 4, 1, 64, 1e4),                         # every cache empty
+    ([5000], 4, 4, 1, 256, 1e4),                           # several partials per request
+    ([400, 90, 3], 8, 8, 2, 64, 1e4),                      # D = 64, two groups per wave
+    ([4097, 1, 2222], 5, 12, 3, 128, 5e5),                 # odd K, G = 4, ragged groups
+]
+
+
+@pytest.mark.parametrize("case", DECODE_SMALL,
+                         ids=[f"B{len(c[0])}K{c[1]}H{c[2]}x{c[3]}D{c[4]}" for c in DECODE_SMALL])
+def test_decode_small_full(pe, case):
+    lens, K, Hq, Hkv, D, theta = case
+    print(f"decode lens={lens} K={K} Hq={Hq} Hkv={Hkv} D={D}", flush=True)
+    inp = synth.decode_inputs(sum(lens) + K, lens, K, Hq, Hkv, D)
+    out, lse = _run(pe, inp, lens, K, D, theta)
+    want = odec.decode_attention(inp["k_cache"], inp["v_cache"], inp["cu_ctx"], inp["q"], inp["k"],
+                                 inp["v"], theta)
+    assert_close(out, want["out"], "out")
+    # With every cache empty a row sees at most K keys and lse is of order 1: rounding the
+    # rotated q and k to bf16 (the MFMA operands) alone moves it by 1.0e-3 relative L2 in
+    # float64 emulation, so that case is held to the attention bar, the others to 1e-3.
+    assert_close(lse, want["lse"], "lse", max_rel_l2=1e-3 if sum(lens) else 5e-3)
+
+
+@pytest.mark.parametrize("name", sorted(synth.DECODE_CONFIGS))
+def test_decode_full_size_sampled(pe, name):
+    """The inference workload at full size, in the launch the bench times; the oracle
+    recomputes every output of a few requests (shortest, longest, seeded others)."""
+    cfg = synth.DECODE_CONFIGS[name]
+    seed = 31
+    lens = synth.decode_lengths(seed, cfg["B"], cfg["ctx_lo"], cfg["ctx_hi"])
+    K, Hq, Hkv, D = cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    print(f"decode {cfg['workload']}: B={cfg['B']} total={int(lens.sum())}", flush=True)
+    inp = synth.decode_inputs_device(seed, lens, K, Hq, Hkv, D)
+    out, lse = _run(pe, inp, lens, K, D, cfg["theta"], device_inputs=True)
+    rng = np.random.default_rng(seed)
+    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
+                    *rng.integers(0, cfg["B"], size=2).tolist()})
+    cu = to_host(inp["cu_ctx"]).astype(np.int64)
+    for b in picks:
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        one = odec.decode_attention(to_host(inp["k_cache"][sl]).view(np.uint16),
+                                    to_host(inp["v_cache"][sl]).view(np.uint16),
+                                    np.array([0, lens[b]]),
+                                    to_host(inp["q"][b:b + 1]).view(np.uint16),
+                                    to_host(inp["k"][b:b + 1]).view(np.uint16),
+                                    to_host(inp["v"][b:b + 1]).view(np.uint16), cfg["theta"])
+        assert_close(out[b:b + 1], one["out"], f"out request {b} (L={lens[b]})")
+        assert_close(lse[b:b + 1], one["lse"], f"lse request {b}", max_rel_l2=1e-3)
+
+
+def test_decode_repeatable_and_workspace_reuse(pe):
+    import torch
+    lens, K, Hq, Hkv, D = [900, 3000], 4, 8, 2, 128
+    inp = synth.decode_inputs(3, lens, K, Hq, Hkv, D)
+    cu, kc, vc = to_dev(inp["cu_ctx"]), to_dev(inp["k_cache"]), to_dev(inp["v_cache"])
+    q, k, v = (to_dev(inp[t]) for t in ("q", "k", "v"))
+    cos, sin = pe.rope_table(D, 1e4, max(lens) + K - 1)
+    vt = pe.decode_pack_v(cu, max(lens), vc)
+    o1, l1, ws = pe.draft_decode_attn(cu, max(lens), kc, vt, q, k, v, cos, sin)
+    ws.fill_(0x7F)                                   # stale workspace contents do not matter
+    o2, l2, _ = pe.draft_decode_attn(cu, max(lens), kc, vt, q, k, v, cos, sin, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -92,6 +92,14 @@ int run_core(const AttnCall& c) {
   return status_of(launch_attn_core(c.a, c.v, c.out, c.lse, c.ws, c.stream));
 }
 
+bool decode_dims_ok(int32_t B, int32_t Hkv, int32_t D) {
+  return B >= 1 && B <= 65535 && Hkv >= 1 && Hkv <= 65535 && (D == 64 || D == 128 || D == 256);
+}
+
+size_t v_tiles_bytes(int64_t total_ctx, int32_t B, int32_t Hkv, int32_t D) {
+  return (size_t)decode_ntiles(total_ctx, B) * Hkv * D * 32 * sizeof(uint16_t);
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,6 +222,78 @@ int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,
   if (num_drafts == 0) return PEAGLE_OK;
   return status_of(launch_accept(num_drafts, K, vocab, draft_logits, target_logits, draft_tok,
                                  target_tok, accept_len, static_cast<hipStream_t>(stream)));
+}
+
+size_t peagle_decode_v_tiles_bytes(int64_t total_ctx, int32_t num_reqs, int32_t num_kv_heads,
+                                   int32_t head_dim) {
+  if (total_ctx < 0 || total_ctx > kMaxI32 || !decode_dims_ok(num_reqs, num_kv_heads, head_dim))
+    return 0;
+  return v_tiles_bytes(total_ctx, num_reqs, num_kv_heads, head_dim);
+}
+
+int peagle_decode_pack_v(int32_t num_reqs, const int32_t* cu_ctx, int64_t total_ctx,
+                         int32_t max_ctx, const peagle_bf16* v_cache, int32_t num_kv_heads,
+                         int32_t head_dim, peagle_bf16* v_tiles, size_t v_tiles_bytes_given,
+                         void* stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PEAGLE_ERR_UNSUPPORTED;
+  if (!decode_dims_ok(num_reqs, num_kv_heads, head_dim)) return PEAGLE_ERR_ARG;
+  if (total_ctx < 0 || total_ctx > kMaxI32 || max_ctx < 0 || max_ctx > total_ctx)
+    return PEAGLE_ERR_ARG;
+  if (!cu_ctx) return PEAGLE_ERR_ARG;
+  if (total_ctx == 0) return PEAGLE_OK;
+  if (!v_cache || !v_tiles || !aligned16(v_cache) || !aligned16(v_tiles)) return PEAGLE_ERR_ARG;
+  if (v_tiles_bytes_given < v_tiles_bytes(total_ctx, num_reqs, num_kv_heads, head_dim))
+    return PEAGLE_ERR_WORKSPACE;
+  return status_of(launch_decode_pack_v(cu_ctx, num_reqs, total_ctx, max_ctx, v_cache,
+                                        num_kv_heads, head_dim, v_tiles,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t peagle_draft_decode_workspace_bytes(int32_t num_reqs, int32_t K, int32_t num_q_heads,
+                                           int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t max_ctx) {
+  if (!decode_dims_ok(num_reqs, num_kv_heads, head_dim) || K < 1 || K > 32 || max_ctx < 0 ||
+      num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  return decode_workspace_bytes(num_reqs, K, num_q_heads, num_kv_heads, head_dim, max_ctx);
+}
+
+int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
+                             int64_t total_ctx, int32_t max_ctx, const peagle_bf16* k_cache,
+                             const peagle_bf16* v_tiles, size_t v_tiles_bytes_given,
+                             const peagle_bf16* q, const peagle_bf16* k, const peagle_bf16* v,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             float softmax_scale, const float* rope_cos, const float* rope_sin,
+                             int32_t rope_max_pos, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PEAGLE_ERR_UNSUPPORTED;
+  if (K > 32) return PEAGLE_ERR_UNSUPPORTED;
+  if (!decode_dims_ok(num_reqs, num_kv_heads, head_dim) || K < 1) return PEAGLE_ERR_ARG;
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0) return PEAGLE_ERR_ARG;
+  if ((int64_t)num_kv_heads * ((num_q_heads / num_kv_heads * K + 31) / 32) > 65535)
+    return PEAGLE_ERR_UNSUPPORTED;
+  if (total_ctx < 0 || total_ctx > kMaxI32 || max_ctx < 0 || max_ctx > total_ctx)
+    return PEAGLE_ERR_ARG;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return PEAGLE_ERR_ARG;
+  if (rope_max_pos < 0 || (int64_t)rope_max_pos < (int64_t)max_ctx + K - 1) return PEAGLE_ERR_ARG;
+  if (!cu_ctx || !q || !k || !v || !rope_cos || !rope_sin || !out || !workspace)
+    return PEAGLE_ERR_ARG;
+  if (total_ctx > 0 && (!k_cache || !v_tiles || !aligned16(k_cache) || !aligned16(v_tiles)))
+    return PEAGLE_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(rope_cos) ||
+      !aligned16(rope_sin) || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return PEAGLE_ERR_ARG;
+  if (total_ctx > 0 &&
+      v_tiles_bytes_given < v_tiles_bytes(total_ctx, num_reqs, num_kv_heads, head_dim))
+    return PEAGLE_ERR_WORKSPACE;
+  if (workspace_bytes <
+      decode_workspace_bytes(num_reqs, K, num_q_heads, num_kv_heads, head_dim, max_ctx))
+    return PEAGLE_ERR_WORKSPACE;
+  DecodeArgs a{num_reqs, K, num_q_heads, num_kv_heads, head_dim, max_ctx, rope_max_pos,
+               total_ctx, softmax_scale};
+  return status_of(launch_decode_attn(a, cu_ctx, k_cache, v_tiles, q, k, v, rope_cos, rope_sin,
+                                      out, lse, static_cast<char*>(workspace),
+                                      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,486 @@
+// Draft attention at inference (the decode shape), gfx950.
+//
+// NeMo Automodel PR 2376, parity section: at inference vLLM runs one flat parallel
+// forward over [context, mask_1, ..., mask_{K-1}]; speculators P-EAGLE guide, "Inference
+// Process": all depths are drafted in one pass and drafting repeats from the last
+// accepted token. Request b has L_b context tokens in the KV cache (keys rotated at their
+// positions 0 .. L_b - 1) and K new rows at positions L_b + d (d = 0: the anchor, the
+// last accepted token; d >= 1: the mask rows). New row d attends to every cache key of
+// its request and to new rows 0 .. d: the forward's predicate with a single anchor.
+//
+// Layouts:
+//   k_cache  [Ltot, Hkv, D] bf16, rotated, natural order.
+//   V tiles  [Hkv][ntiles][D][32] bf16 (decode_pack_v_kernel): tile (cu[b] >> 5) + b + j
+//            of a kv head holds keys 32 j .. 32 j + 31 of request b (zeros past L_b),
+//            dim-major, slot s of a dim row holding key dec_key(s). That is the order in
+//            which a lane's two 16-key score accumulators hand their weights to the
+//            P^T operand of O^T = V^T P^T, so P^T needs no data movement and every V^T
+//            operand is one 16-byte load. The base (cu[b] >> 5) + b never overlaps the
+//            previous request and needs no prefix sum.
+//
+// Kernels (all on the caller's stream):
+//   decode_prep     rotates q and the new keys at L_b + d into the workspace and lays the
+//                   new rows' keys and values out as one extra 32-key tile per
+//                   (request, kv head).
+//   decode_attn     split-KV: a workgroup owns (request, kv head, column group, a slice
+//                   of the cache tiles); its four waves take the slice's tiles in turn.
+//                   A wave holds 16 or 32 query columns (column c of a kv head: q head
+//                   g*G + c / K, depth c % K) and computes S^T = K Q^T and O^T = V^T P^T
+//                   on v_mfma_f32_16x16x32_bf16 with an online softmax in base 2
+//                   (scale folded into one FMA) that rescales only when the running max
+//                   grows by more than 2^8; the weights enter PV as a hi + lo bf16 pair.
+//                   The waves merge through LDS and the workgroup writes one partial
+//                   (O, max, sum).
+//   decode_combine  merges the partials of each (request, kv head, column group).
+// The path is HBM-bound: every cache byte is read once.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace peagle {
+
+namespace {
+
+constexpr int kDecWaves = 4;  // waves per workgroup
+constexpr int kDecTile = 32;  // keys per tile
+constexpr float kDecRescaleLog2 = 8.f;
+
+// 16x16x32 bf16 MFMA: D[16x16] += A[16x32] * B[32x16]. Lane l supplies row l%16 of A and
+// column l%16 of B, 8 values each at the same k positions for both operands; it
+// receives column l%16 of D, rows 4*(l/16) + r for accumulator register r.
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Key held by slot s (0..31) of a V^T tile row: lane group q of the P^T operand holds
+// keys 4q .. 4q + 3 (first score block) then 16 + 4q .. 16 + 4q + 3 (second).
+__host__ __device__ constexpr int dec_key(int s) {
+  return (s & 7) < 4 ? 4 * (s >> 3) + (s & 7) : 16 + 4 * (s >> 3) + (s & 7) - 4;
+}
+
+struct DecodeParams {
+  const int32_t* cu;
+  const uint16_t* kc;    // [Ltot, Hkv, D]
+  const uint16_t* vt;    // V tiles
+  const uint16_t* qr;    // rotated q [B, K, Hq, D]
+  const uint16_t* knew;  // rotated new keys [B, Hkv, 32, D], zero rows past K
+  const uint16_t* vnew;  // new values as a V^T tile [B, Hkv, D, 32]
+  float* part_o;         // [B, Hkv, NCg, NPW, PC, D]
+  float* part_ml;        // [B, Hkv, NCg, NPW, PC, 2]: max (base 2) and sum
+  int B, K, Hq, Hkv, G, GK, NCg, NPW, tpw, max_ctx;
+  int64_t total_ctx, ntiles;
+  float c_log2;
+};
+
+// Context length and cache start of request b; trusted device data, clamped so that every
+// access stays inside the cache.
+__device__ __forceinline__ void request_extent(const int32_t* cu, int b, int64_t total_ctx,
+                                               int max_ctx, int64_t& c0, int& L) {
+  c0 = std::min<int64_t>(std::max(cu[b], 0), total_ctx);
+  L = (int)std::min<int64_t>(std::max<int64_t>((int64_t)cu[b + 1] - c0, 0),
+                             std::min<int64_t>(max_ctx, total_ctx - c0));
+}
+
+// Rotate-half RoPE of one pre-RoPE bf16 row at position pos into bf16 (fp32 arithmetic):
+// dims j and j + D/2 turn by pos * theta^(-2j/D), cos/sin read from the table.
+__device__ __forceinline__ void rope_row(const uint16_t* src, uint16_t* dst, int D, int pos,
+                                         const float* cs, const float* sn, int lane, int nlanes) {
+  const int H = D / 2;
+  for (int j = lane; j < H; j += nlanes) {
+    const float a = bf16_bits_to_f32(src[j]), b = bf16_bits_to_f32(src[j + H]);
+    const float c = cs[(size_t)pos * H + j], s = sn[(size_t)pos * H + j];
+    dst[j] = f32_to_bf16_bits(a * c - b * s);
+    dst[j + H] = f32_to_bf16_bits(b * c + a * s);
+  }
+}
+
+// One workgroup per (request, kv head).
+__global__ __launch_bounds__(256) void decode_prep_kernel(
+    const int32_t* __restrict__ cu, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ cs, const float* __restrict__ sn,
+    uint16_t* __restrict__ qr, uint16_t* __restrict__ knew, uint16_t* __restrict__ vnew, int K,
+    int Hq, int Hkv, int D, int max_ctx, int max_pos, int64_t total_ctx) {
+  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv, G = Hq / Hkv;
+  int64_t c0;
+  int L;
+  request_extent(cu, b, total_ctx, max_ctx, c0, L);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // q rows of this kv head's q heads, every depth
+  for (int r = wave; r < K * G; r += kDecWaves) {
+    const int d = r / G, h = g * G + r % G;
+    const size_t off = (((size_t)b * K + d) * Hq + h) * D;
+    rope_row(q + off, qr + off, D, std::min(L + d, max_pos), cs, sn, lane, 64);
+  }
+  // new keys: rows 0 .. K-1 rotated, rows K .. 31 zero
+  uint16_t* kn = knew + ((size_t)b * Hkv + g) * kDecTile * D;
+  for (int e = wave; e < kDecTile; e += kDecWaves) {
+    if (e < K) {
+      rope_row(k + (((size_t)b * K + e) * Hkv + g) * D, kn + (size_t)e * D, D,
+               std::min(L + e, max_pos), cs, sn, lane, 64);
+    } else {
+      for (int j = lane; j < D; j += 64) kn[(size_t)e * D + j] = 0;
+    }
+  }
+  // new values as a V^T tile
+  uint16_t* vn = vnew + ((size_t)b * Hkv + g) * D * kDecTile;
+  for (int t = threadIdx.x; t < D * kDecTile; t += blockDim.x) {
+    const int dim = t / kDecTile, e = dec_key(t % kDecTile);
+    vn[t] = e < K ? v[(((size_t)b * K + e) * Hkv + g) * D + dim] : (uint16_t)0;
+  }
+}
+
+template <int D, int NCW>
+struct DecodeWave {
+  static constexpr int DK = D / 32, MT = D / 16;
+  bf16x8 qf[NCW][DK];
+  floatx4 o[NCW][MT];
+  float m_run[NCW], l_run[NCW];
+};
+
+// One 32-key tile: rows [0, rows) of kbase (row stride kstride elements) and its V^T tile;
+// column group c keeps keys below lim[c].
+template <int D, int NCW>
+__device__ __forceinline__ void decode_tile(DecodeWave<D, NCW>& w, const uint16_t* kbase,
+                                            size_t kstride, int rows, const uint16_t* vtile,
+                                            const int (&lim)[NCW], float c_log2, int l16,
+                                            int grp) {
+  constexpr int DK = D / 32, MT = D / 16;
+  bf16x8 kf[2][DK];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = std::min(16 * h + l16, rows - 1);
+    const uint16_t* kp = kbase + (size_t)row * kstride + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+      kf[h][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 32 * kk));
+  }
+  bf16x8 vf[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    vf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp));
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+    floatx4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk) s[h] = mfma16(kf[h][kk], w.qf[c][kk], s[h]);
+    }
+    if (lim[c] < kDecTile) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * h + 4 * grp + r >= lim[c]) s[h][r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c_log2;
+    const float m_new = fmaxf(w.m_run[c], mx);
+    if (__any(m_new > w.m_run[c] + kDecRescaleLog2)) {
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(w.m_run[c] - m_new);
+      w.l_run[c] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) w.o[c][mt] *= alpha;
+      w.m_run[c] = m_new;
+    }
+    // P^T as a bf16 pair (hi + lo): about 16 significant bits instead of 8 for two MFMAs
+    // per V^T fragment, which cost nothing next to the cache reads
+    const float mu = w.m_run[c] == -INFINITY ? 0.f : w.m_run[c];
+    bf16x8 ph, pl;
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float pr = __builtin_amdgcn_exp2f(fmaf(s[i >> 2][i & 3], c_log2, -mu));
+      ls += pr;
+      ph[i] = (__bf16)pr;
+      pl[i] = (__bf16)(pr - (float)ph[i]);
+    }
+    w.l_run[c] += ls;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      w.o[c][mt] = mfma16(vf[mt], ph, w.o[c][mt]);
+      w.o[c][mt] = mfma16(vf[mt], pl, w.o[c][mt]);
+    }
+  }
+}
+
+template <int D, int NCW>
+__global__ __launch_bounds__(64 * kDecWaves, 2) void decode_attn_kernel(const DecodeParams p) {
+  constexpr int DK = D / 32, MT = D / 16, PC = 16 * NCW;
+  __shared__ float red_o[kDecWaves][PC][D];
+  __shared__ float red_ml[kDecWaves][PC][2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, grp = lane >> 4;
+  const int wp = blockIdx.x, b = blockIdx.z;
+  const int g = blockIdx.y / p.NCg, cg = blockIdx.y % p.NCg;
+  const int K = p.K, Hkv = p.Hkv;
+  int64_t c0;
+  int L;
+  request_extent(p.cu, b, p.total_ctx, p.max_ctx, c0, L);
+  const int ntiles_b = (L + kDecTile - 1) / kDecTile;
+
+  DecodeWave<D, NCW> w;
+  int dcol[NCW];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+    const int col = std::min((cg * NCW + c) * 16 + l16, p.GK - 1);
+    const int d = col % K, head = g * p.G + col / K;
+    dcol[c] = d;
+    const uint16_t* qrow = p.qr + (((size_t)b * K + d) * p.Hq + head) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+      w.qf[c][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * kk));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) w.o[c][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    w.m_run[c] = -INFINITY;
+    w.l_run[c] = 0.f;
+  }
+
+  // the new rows' keys: one masked tile, row d keeps new keys e <= d
+  if (wp == 0 && wave == 0) {
+    int lim[NCW];
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) lim[c] = dcol[c] + 1;
+    const size_t bg = (size_t)b * Hkv + g;
+    decode_tile<D, NCW>(w, p.knew + bg * kDecTile * D, D, kDecTile, p.vnew + bg * D * kDecTile,
+                        lim, p.c_log2, l16, grp);
+  }
+  // this workgroup's slice of the cache tiles, dealt out to the waves in turn
+  const int t_end = std::min((wp + 1) * p.tpw, ntiles_b);
+  const uint16_t* vbase = p.vt + (((size_t)g * p.ntiles + (c0 >> 5) + b) * D) * kDecTile;
+  for (int t = wp * p.tpw + wave; t < t_end; t += kDecWaves) {
+    const int key0 = t * kDecTile;
+    int lim[NCW];
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) lim[c] = L - key0;
+    decode_tile<D, NCW>(w, p.kc + ((size_t)(c0 + key0) * Hkv + g) * D, (size_t)Hkv * D,
+                        L - key0, vbase + (size_t)t * D * kDecTile, lim, p.c_log2, l16, grp);
+  }
+
+  // merge the four waves through LDS; the workgroup writes one partial
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) {
+    float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<floatx4*>(&red_o[wave][c * 16 + l16][16 * mt + 4 * grp]) = w.o[c][mt];
+    if (grp == 0) {
+      red_ml[wave][c * 16 + l16][0] = w.m_run[c];
+      red_ml[wave][c * 16 + l16][1] = lt;
+    }
+  }
+  __syncthreads();
+  const size_t part = (((size_t)b * Hkv + g) * p.NCg + cg) * p.NPW + wp;
+  for (int t = threadIdx.x; t < PC * (D / 4); t += 64 * kDecWaves) {
+    const int col = t / (D / 4), d4 = (t % (D / 4)) * 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, red_ml[q][col][0]);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int q = 0; q < kDecWaves; ++q) {
+      const float mq = red_ml[q][col][0];
+      const float f = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+      acc += f * *reinterpret_cast<const floatx4*>(&red_o[q][col][d4]);
+      lsum += f * red_ml[q][col][1];
+    }
+    *reinterpret_cast<floatx4*>(p.part_o + (part * PC + col) * D + d4) = acc;
+    if (d4 == 0) {
+      p.part_ml[(part * PC + col) * 2] = M;
+      p.part_ml[(part * PC + col) * 2 + 1] = lsum;
+    }
+  }
+}
+
+// Merge the NPW partials of (request, kv head, column group): out = sum_p 2^(m_p - M) O_p /
+// sum_p 2^(m_p - M) l_p and lse = (M + log2 of that sum) ln 2, M the largest m_p.
+// One thread per (column, 4 dims).
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml,
+                                                             float* __restrict__ out,
+                                                             float* __restrict__ lse, int K, int Hq,
+                                                             int Hkv, int G, int GK, int NCg,
+                                                             int NPW, int PC, int D) {
+  const int item = blockIdx.x, cg = item % NCg, bg = item / NCg, b = bg / Hkv, g = bg % Hkv;
+  const int per_col = D / 4;
+  const int ncols = std::min(PC, GK - cg * PC);
+  const size_t base = (size_t)item * NPW;
+  for (int t = threadIdx.x; t < ncols * per_col; t += blockDim.x) {
+    const int c = t / per_col, d4 = (t % per_col) * 4;
+    float M = -INFINITY;
+    for (int q = 0; q < NPW; ++q) M = fmaxf(M, part_ml[((base + q) * PC + c) * 2]);
+    float lsum = 0.f;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < NPW; ++q) {
+      const float mq = part_ml[((base + q) * PC + c) * 2];
+      if (mq == -INFINITY) continue;
+      const float f = __builtin_amdgcn_exp2f(mq - M);
+      lsum += f * part_ml[((base + q) * PC + c) * 2 + 1];
+      acc += f * *reinterpret_cast<const floatx4*>(part_o + ((base + q) * PC + c) * D + d4);
+    }
+    const int col = cg * PC + c, d = col % K, head = g * G + col / K;
+    *reinterpret_cast<floatx4*>(out + (((size_t)b * K + d) * Hq + head) * D + d4) = acc / lsum;
+    if (lse != nullptr && d4 == 0)
+      lse[((size_t)b * K + d) * Hq + head] = (M + __log2f(lsum)) * 0.69314718055994531f;
+  }
+}
+
+// Natural V [Ltot, Hkv, D] -> V tiles (layout in the header comment). One workgroup per
+// (tile j of request b, kv head g); tiles past the request's end write nothing.
+template <int D>
+__global__ __launch_bounds__(256) void decode_pack_v_kernel(const int32_t* __restrict__ cu,
+                                                            const uint16_t* __restrict__ v,
+                                                            uint16_t* __restrict__ vt,
+                                                            int64_t total_ctx, int max_ctx,
+                                                            int64_t ntiles, int Hkv) {
+  __shared__ uint16_t tile[kDecTile][D + 8];
+  const int j = blockIdx.x, b = blockIdx.y, g = blockIdx.z, tid = threadIdx.x;
+  int64_t c0;
+  int L;
+  request_extent(cu, b, total_ctx, max_ctx, c0, L);
+  if (j * kDecTile >= L) return;
+  constexpr int cpr = D / 8;
+  for (int q = tid; q < kDecTile * cpr; q += 256) {
+    const int key = q / cpr, c = q % cpr, pos = j * kDecTile + key;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (pos < L) val = *reinterpret_cast<const u32x4*>(v + ((size_t)(c0 + pos) * Hkv + g) * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[key][c * 8 + 2 * e] = (uint16_t)(val[e] & 0xFFFFu);
+      tile[key][c * 8 + 2 * e + 1] = (uint16_t)(val[e] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* dst = vt + (((size_t)g * ntiles + (c0 >> 5) + b + j) * D) * kDecTile;
+  for (int q = tid; q < D * kDecTile; q += 256) dst[q] = tile[dec_key(q % kDecTile)][q / kDecTile];
+}
+
+template <typename F>
+hipError_t for_dim(int D, F&& f) {
+  switch (D) {
+    case 64: f(std::integral_constant<int, 64>{}); break;
+    case 128: f(std::integral_constant<int, 128>{}); break;
+    case 256: f(std::integral_constant<int, 256>{}); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct DecodeLayout {
+  size_t qr, knew, vnew, part_o, part_ml, total;
+};
+
+DecodeLayout decode_layout(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                           const DecodePlan& pl) {
+  DecodeLayout l;
+  const size_t parts = (size_t)B * Hkv * pl.ncg * pl.npw * pl.pc;
+  l.qr = 0;
+  l.knew = l.qr + align256((size_t)B * K * Hq * D * 2);
+  l.vnew = l.knew + align256((size_t)B * Hkv * kDecTile * D * 2);
+  l.part_o = l.vnew + align256((size_t)B * Hkv * D * kDecTile * 2);
+  l.part_ml = l.part_o + align256(parts * D * 4);
+  l.total = l.part_ml + align256(parts * 2 * 4);
+  return l;
+}
+
+}  // namespace
+
+int64_t decode_ntiles(int64_t total_ctx, int32_t B) { return (total_ctx >> 5) + B + 1; }
+
+DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx) {
+  DecodePlan pl;
+  const int gk = (Hq / Hkv) * K;
+  // two column groups per wave where the registers allow it (D <= 128)
+  pl.ncw = (D <= 128 && gk > 16) ? 2 : 1;
+  pl.pc = 16 * pl.ncw;
+  pl.ncg = (gk + pl.pc - 1) / pl.pc;
+  const int tiles_max = (max_ctx + kDecTile - 1) / kDecTile;
+  const int64_t items = (int64_t)B * Hkv * pl.ncg;
+  // about 1024 workgroups (two per CU at two waves per SIMD), at least 16 tiles each so
+  // that the partials stay small next to the cache
+  const int64_t want = std::max<int64_t>((1024 + items - 1) / items, 1);
+  const int64_t cap = std::max<int64_t>((tiles_max + 15) / 16, 1);
+  pl.npw = (int)std::min(want, cap);
+  pl.tpw = std::max(1, (tiles_max + pl.npw - 1) / pl.npw);
+  return pl;
+}
+
+size_t decode_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t max_ctx) {
+  return decode_layout(B, K, Hq, Hkv, D, decode_plan(B, K, Hq, Hkv, D, max_ctx)).total;
+}
+
+hipError_t launch_decode_pack_v(const int32_t* cu, int32_t B, int64_t total_ctx, int32_t max_ctx,
+                                const uint16_t* v, int32_t Hkv, int32_t D, uint16_t* vt,
+                                hipStream_t stream) {
+  const int tiles_max = (max_ctx + kDecTile - 1) / kDecTile;
+  if (tiles_max == 0) return hipSuccess;
+  const int64_t ntiles = decode_ntiles(total_ctx, B);
+  return for_dim(D, [&](auto dc) {
+    constexpr int DD = decltype(dc)::value;
+    hipLaunchKernelGGL(decode_pack_v_kernel<DD>, dim3(tiles_max, B, Hkv), dim3(256), 0, stream, cu,
+                       v, vt, total_ctx, max_ctx, ntiles, Hkv);
+  });
+}
+
+hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint16_t* kc,
+                              const uint16_t* vt, const uint16_t* qn, const uint16_t* kn,
+                              const uint16_t* vn, const float* cs, const float* sn, float* out,
+                              float* lse, char* ws, hipStream_t stream) {
+  const DecodePlan pl = decode_plan(a.B, a.K, a.Hq, a.Hkv, a.D, a.max_ctx);
+  const DecodeLayout lay = decode_layout(a.B, a.K, a.Hq, a.Hkv, a.D, pl);
+  DecodeParams p;
+  p.cu = cu;
+  p.kc = kc;
+  p.vt = vt;
+  p.qr = reinterpret_cast<const uint16_t*>(ws + lay.qr);
+  p.knew = reinterpret_cast<const uint16_t*>(ws + lay.knew);
+  p.vnew = reinterpret_cast<const uint16_t*>(ws + lay.vnew);
+  p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
+  p.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
+  p.B = a.B;
+  p.K = a.K;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.G = a.Hq / a.Hkv;
+  p.GK = p.G * a.K;
+  p.NCg = pl.ncg;
+  p.NPW = pl.npw;
+  p.tpw = pl.tpw;
+  p.max_ctx = a.max_ctx;
+  p.total_ctx = a.total_ctx;
+  p.ntiles = decode_ntiles(a.total_ctx, a.B);
+  p.c_log2 = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(a.B * a.Hkv), dim3(256), 0, stream, cu, qn, kn, vn,
+                     cs, sn, reinterpret_cast<uint16_t*>(ws + lay.qr),
+                     reinterpret_cast<uint16_t*>(ws + lay.knew),
+                     reinterpret_cast<uint16_t*>(ws + lay.vnew), a.K, a.Hq, a.Hkv, a.D,
+                     a.max_ctx, a.max_pos, a.total_ctx);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = for_dim(a.D, [&](auto dc) {
+    constexpr int DD = decltype(dc)::value;
+    const dim3 grid(pl.npw, a.Hkv * pl.ncg, a.B);
+    if (pl.ncw == 2) {
+      if constexpr (DD <= 128)
+        hipLaunchKernelGGL((decode_attn_kernel<DD, 2>), grid, dim3(64 * kDecWaves), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((decode_attn_kernel<DD, 1>), grid, dim3(64 * kDecWaves), 0, stream, p);
+    }
+  });
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hkv * pl.ncg), dim3(256), 0, stream,
+                     p.part_o, p.part_ml, out, lse, a.K, a.Hq, a.Hkv, p.G, p.GK, pl.ncg, pl.npw,
+                     pl.pc, a.D);
+  return hipGetLastError();
+}
+
+}  // namespace peagle

@@ -71,4 +71,30 @@ hipError_t launch_accept(int32_t N, int32_t K, int32_t V, const uint16_t* draft,
                          const uint16_t* target, int32_t* draft_tok, int32_t* target_tok,
                          int32_t* accept_len, hipStream_t stream);
 
+// Draft attention at inference: K new rows per request over a KV cache.
+struct DecodeArgs {
+  int32_t B, K, Hq, Hkv, D, max_ctx, max_pos;
+  int64_t total_ctx;
+  float scale;
+};
+// Split of the decode attention: a wave holds ncw groups of 16 query columns (pc = 16 ncw
+// columns); ncg column groups per kv head; npw workgroups (one partial each) per
+// (request, kv head, column group), each over tpw cache tiles of 32 keys.
+struct DecodePlan {
+  int ncw, pc, ncg, npw, tpw;
+};
+DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx);
+size_t decode_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                              int32_t max_ctx);
+// V tiles per kv head of a cache of total_ctx keys over B requests.
+int64_t decode_ntiles(int64_t total_ctx, int32_t B);
+
+hipError_t launch_decode_pack_v(const int32_t* cu, int32_t B, int64_t total_ctx, int32_t max_ctx,
+                                const uint16_t* v, int32_t Hkv, int32_t D, uint16_t* vt,
+                                hipStream_t stream);
+hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint16_t* kc,
+                              const uint16_t* vt, const uint16_t* qn, const uint16_t* kn,
+                              const uint16_t* vn, const float* cs, const float* sn, float* out,
+                              float* lse, char* ws, hipStream_t stream);
+
 }  // namespace peagle

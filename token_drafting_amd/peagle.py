@@ -39,6 +39,11 @@ SIGNATURES = {
     "peagle_draft_attn_prepare": (_ATTN, _i32),
     "peagle_draft_attn_core": (_ATTN, _i32),
     "peagle_accept_prefix": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _p], _i32),
+    "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
+    "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
+    "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "peagle_draft_decode_attn": ([_i32, _i32, _p, _i64, _i32, _p, _p, _sz, _p, _p, _p, _i32,
+                                  _i32, _i32, _f32, _p, _p, _i32, _p, _p, _p, _sz, _p], _i32),
 }
 
 
@@ -201,3 +206,54 @@ def accept_prefix(draft_logits, target_logits, draft_tok=None, target_tok=None, 
         N, K, V, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tok), _ptr(target_tok),
         _ptr(accept_len), _stream()))
     return draft_tok, target_tok, accept_len
+
+
+# ---------------------------------------------------------------- decode shape
+def decode_v_tiles_bytes(total_ctx: int, B: int, Hkv: int, D: int) -> int:
+    return int(lib().peagle_decode_v_tiles_bytes(total_ctx, B, Hkv, D))
+
+
+def decode_pack_v(cu_ctx, max_ctx: int, v_cache, v_tiles=None):
+    """V cache [Ltot, Hkv, D] (natural layout) -> the decode kernel's V tiles (flat bf16)."""
+    _dev(cu_ctx, "cu_ctx")
+    _dev(v_cache, "v_cache")
+    Ltot, Hkv, D = v_cache.shape
+    B = cu_ctx.numel() - 1
+    nbytes = decode_v_tiles_bytes(Ltot, B, Hkv, D)
+    if v_tiles is None:
+        v_tiles = torch.zeros(max(nbytes // 2, 8), dtype=v_cache.dtype, device=v_cache.device)
+    _check("peagle_decode_pack_v", lib().peagle_decode_pack_v(
+        B, _ptr(cu_ctx), Ltot, max_ctx, _ptr(v_cache), Hkv, D, _ptr(v_tiles),
+        v_tiles.numel() * v_tiles.element_size(), _stream()))
+    return v_tiles
+
+
+def decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx) -> int:
+    return int(lib().peagle_draft_decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx))
+
+
+def draft_decode_attn(cu_ctx, max_ctx: int, k_cache, v_tiles, q, k, v, cos, sin, out=None,
+                      lse=None, workspace=None, scale=None):
+    """K new rows per request over a KV cache: q [B, K, Hq, D], k/v [B, K, Hkv, D] (pre-RoPE
+    q and k), k_cache [Ltot, Hkv, D] rotated, v_tiles from decode_pack_v.
+    Returns out [B, K, Hq, D] fp32, lse [B, K, Hq] fp32 and the workspace."""
+    for t, name in ((cu_ctx, "cu_ctx"), (k_cache, "k_cache"), (v_tiles, "v_tiles"), (q, "q"),
+                    (k, "k"), (v, "v"), (cos, "rope_cos"), (sin, "rope_sin")):
+        _dev(t, name)
+    B, K, Hq, D = q.shape
+    Hkv = k.shape[2]
+    Ltot = k_cache.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, K, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, K, Hq), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx),
+                                dtype=torch.uint8, device=dev)
+    _check("peagle_draft_decode_attn", lib().peagle_draft_decode_attn(
+        B, K, _ptr(cu_ctx), Ltot, max_ctx, _ptr(k_cache), _ptr(v_tiles),
+        v_tiles.numel() * v_tiles.element_size(), _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, D,
+        float(scale if scale is not None else 1.0 / math.sqrt(D)), _ptr(cos), _ptr(sin),
+        cos.shape[0] - 1, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse, workspace

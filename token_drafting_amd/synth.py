@@ -25,6 +25,7 @@ import numpy as np
 # Tensor tags: each input draws from default_rng([seed, TAG]).
 TAG_LENGTHS, TAG_AUX, TAG_W, TAG_MASK, TAG_EMBED, TAG_TOKENS = 1, 2, 3, 4, 5, 6
 TAG_Q, TAG_K, TAG_V, TAG_LOGITS = 7, 8, 9, 10
+TAG_CACHE_K, TAG_CACHE_V, TAG_NEW_Q, TAG_NEW_K, TAG_NEW_V = 11, 12, 13, 14, 15
 
 VOCAB_IN = 32000          # input-embedding vocabulary of the synthetic drafter
 PLANT_VALUE_BITS = 0x4180  # bf16 bit pattern of 16.0 (exact), the planted maximum
@@ -43,6 +44,16 @@ CONFIGS = {
     5: dict(workload="llama8b-draft-16k-K8", n=16384, K=8, r=0.7, r_min=0.2, H=4096,
             aux_dim=3 * 4096, Hq=32, Hkv=8, D=128, theta=5.0e5, num_seqs=1,
             verify=dict(drafts=4096, K=8, V=32000, p_plant=0.7)),
+}
+
+# Inference (decode-shaped) workloads: B requests, each with a KV cache of a context length
+# drawn uniform in [ctx_lo, ctx_hi], and K new rows (the anchor and K-1 mask rows). Heads
+# and RoPE base follow the Gemma-270M and Llama-8B shaped draft layers above.
+DECODE_CONFIGS = {
+    "gemma270m": dict(workload="decode-gemma270m-B64-ctx1k-32k-K4", B=64, ctx_lo=1024,
+                      ctx_hi=32768, K=4, Hq=4, Hkv=1, D=256, theta=1.0e4),
+    "llama8b": dict(workload="decode-llama8b-B64-ctx1k-32k-K8", B=64, ctx_lo=1024,
+                    ctx_hi=32768, K=8, Hq=32, Hkv=8, D=128, theta=5.0e5),
 }
 
 
@@ -160,3 +171,49 @@ def verify_logits(seed: int, drafts: int, K: int, V: int, p_plant: float,
             target[i, d, where[i, d]] = PLANT_VALUE_BITS
             planted[i] += 1
     return dict(draft_logits=draft, target_logits=target, planted=planted)
+
+
+def decode_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """Context length of each of B requests, uniform in [lo, hi]."""
+    return _rng(seed, TAG_LENGTHS).integers(lo, hi + 1, size=B).astype(np.int64)
+
+
+def decode_inputs(seed: int, lens, K: int, Hq: int, Hkv: int, D: int) -> dict:
+    """Host inputs of the decode shape: cu_ctx int32 [B+1]; k_cache and v_cache
+    [sum(lens), Hkv, D] (the cache keys are taken as already rotated); q [B, K, Hq, D] and
+    k, v [B, K, Hkv, D] of the new rows (pre-RoPE). bf16 bits of N(0, 1)."""
+    lens = np.asarray(lens, dtype=np.int64)
+    B, L = len(lens), int(lens.sum())
+    return dict(cu_ctx=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                k_cache=normal_bf16(seed, TAG_CACHE_K, (L, Hkv, D)),
+                v_cache=normal_bf16(seed, TAG_CACHE_V, (L, Hkv, D)),
+                q=normal_bf16(seed, TAG_NEW_Q, (B, K, Hq, D)),
+                k=normal_bf16(seed, TAG_NEW_K, (B, K, Hkv, D)),
+                v=normal_bf16(seed, TAG_NEW_V, (B, K, Hkv, D)))
+
+
+def decode_inputs_device(seed: int, lens, K: int, Hq: int, Hkv: int, D: int, device="cuda"):
+    """The same shapes drawn on the device with torch's seeded generator (for caches of
+    gigabytes, where host generation would dominate). N(0, 1) rounded to bf16 (nearest
+    even); returned as int16 bit patterns, cu_ctx as int32."""
+    import torch
+    lens = np.asarray(lens, dtype=np.int64)
+    B, L = len(lens), int(lens.sum())
+
+    def draw(tag, shape):
+        g = torch.Generator(device=device)
+        g.manual_seed(int(seed) * 1000003 + tag)
+        out = torch.empty(shape, dtype=torch.int16, device=device)
+        flat = out.view(-1)
+        step = 1 << 26
+        for lo in range(0, flat.numel(), step):
+            hi = min(flat.numel(), lo + step)
+            x = torch.randn(hi - lo, generator=g, device=device, dtype=torch.float32)
+            flat[lo:hi] = x.to(torch.bfloat16).view(torch.int16)
+        return out
+
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return dict(cu_ctx=torch.from_numpy(cu).to(device),
+                k_cache=draw(TAG_CACHE_K, (L, Hkv, D)), v_cache=draw(TAG_CACHE_V, (L, Hkv, D)),
+                q=draw(TAG_NEW_Q, (B, K, Hq, D)), k=draw(TAG_NEW_K, (B, K, Hkv, D)),
+                v=draw(TAG_NEW_V, (B, K, Hkv, D)))
