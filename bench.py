@@ -11,6 +11,11 @@ RoPE gather + draft attention, and greedy verification. The default workload is 
 Prints one JSON line. `value` is useful draft-attention TFLOP/s over the whole step
 (4 * D * Hq * allowed query-key pairs, divided by the step time); the attention call
 alone, drafted tokens/s and the per-kernel split are reported beside it.
+
+The decode-shaped draft attention (K new rows per request over a KV cache) is timed
+beside it on its two inference workloads and reported under "decode": HBM GB/s of the
+whole call (cache bytes plus new rows and outputs over the call time) and drafted
+tokens/s. `--decode only` prints a line for it alone.
 """
 from __future__ import annotations
 
@@ -37,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="oracle sample size in query rows (0: sized for about 10-20 s of "
                          "host time from the oracle's cost per row, Hq * T * D)")
+    ap.add_argument("--decode", choices=["all", "none", "only"], default="all",
+                    help="also time the decode-shaped draft attention on its inference "
+                         "workloads (all), skip it (none), or time only it (only)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps, "
                          "so a counter run can scale its byte counters against known traffic")
@@ -77,6 +85,19 @@ def main():
     from token_drafting_amd import peagle, synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibration_copy_mib:
+        nbytes = args.calibration_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.decode == "only":
+        res = {name: decode_bench(name, args.steps, args.warmup)
+               for name in sorted(synth.DECODE_CONFIGS)}
+        print(json.dumps({"decode": res}), flush=True)
+        return
     cfg = synth.CONFIGS[args.config]
     seed = args.config
     n, K, Hq, Hkv, D = cfg["n"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"]
@@ -141,15 +162,6 @@ def main():
         mark(5)
         peagle.accept_prefix(dl, tl, dtok, ttok, alen)
         mark(6)
-
-    if args.calibration_copy_mib:
-        nbytes = args.calibration_copy_mib << 20
-        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -216,10 +228,65 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
+    if args.decode == "all":
+        del ws, out, lse, hidden, emb, dl, tl
+        torch.cuda.empty_cache()
+        result["decode"] = {name: decode_bench(name, args.steps, args.warmup)
+                            for name in sorted(synth.DECODE_CONFIGS)}
+
     # ---------------- oracle on the host cores (bounded sample)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, seed, qkv, cu_h, idx_h, off_h, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def decode_bench(name, steps, warmup):
+    """Time peagle_draft_decode_attn (prep, split-KV attention, combine) on one inference
+    workload with its inputs resident in HBM; the V cache is laid out in tiles first, as a
+    server keeps it, and that conversion is not timed."""
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    cfg = synth.DECODE_CONFIGS[name]
+    seed = 31
+    B, K, Hq, Hkv, D = cfg["B"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    lens = synth.decode_lengths(seed, B, cfg["ctx_lo"], cfg["ctx_hi"])
+    inp = synth.decode_inputs_device(seed, lens, K, Hq, Hkv, D)
+    max_ctx = int(lens.max())
+    cos, sin = peagle.rope_table(D, cfg["theta"], max_ctx + K - 1)
+    vt = peagle.decode_pack_v(inp["cu_ctx"], max_ctx, inp["v_cache"])
+    del inp["v_cache"]
+    dev = vt.device
+    out = torch.empty((B, K, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, K, Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(peagle.decode_workspace_bytes(B, K, Hq, Hkv, D, int(lens.sum()), max_ctx),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        peagle.draft_decode_attn(inp["cu_ctx"], max_ctx, inp["k_cache"], vt, inp["q"], inp["k"],
+                                 inp["v"], cos, sin, out, lse, ws)
+
+    for _ in range(warmup):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        call()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    total = int(lens.sum())
+    cache_bytes = 2 * total * Hkv * D * 2
+    io_bytes = B * K * Hq * D * 2 + 2 * B * K * Hkv * D * 2 + B * K * Hq * D * 4 + B * K * Hq * 4
+    gbps = (cache_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    del inp, vt, out, lse, ws
+    torch.cuda.empty_cache()
+    return {"workload": cfg["workload"], "requests": B, "context_tokens": total, "K": K,
+            "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "ms_per_call": round(ms, 4),
+            "bytes_per_call": cache_bytes + io_bytes, "hbm_GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "drafted_tokens_per_s": round(B * K / (ms * 1e-3), 1)}
 
 
 def cpu_baseline(cfg, seed, qkv, cu, idx, depth_off, rows_wanted):

@@ -228,7 +228,7 @@ int peagle_decode_pack_v(int32_t num_reqs, const int32_t *cu_ctx, int64_t total_
 /* Bytes of workspace peagle_draft_decode_attn needs for these sizes (0 on bad arguments). */
 size_t peagle_draft_decode_workspace_bytes(int32_t num_reqs, int32_t K, int32_t num_q_heads,
                                            int32_t num_kv_heads, int32_t head_dim,
-                                           int32_t max_ctx);
+                                           int64_t total_ctx, int32_t max_ctx);
 
 /*
  * peagle_draft_decode_attn -- the decode-shaped draft attention. Split-KV: the cache
@@ -245,7 +245,8 @@ size_t peagle_draft_decode_workspace_bytes(int32_t num_reqs, int32_t K, int32_t 
  *                  rope_max_pos >= max_ctx + K - 1
  *   out            fp32[B, K, Hq, D]   out
  *   lse            fp32[B, K, Hq]      out, natural-log softmax denominators; may be NULL
- *   workspace      >= peagle_draft_decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx)
+ *   workspace      >= peagle_draft_decode_workspace_bytes(B, K, Hq, Hkv, D, total_ctx,
+ *                  max_ctx)
  *                  bytes, 256-byte aligned scratch
  * head_dim in {64, 128, 256}; Hq % Hkv == 0; 1 <= K <= 32; 1 <= B <= 65535.
  * total_ctx = 0 (every request empty) is allowed; k_cache and v_tiles may then be NULL.

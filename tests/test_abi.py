@@ -163,10 +163,11 @@ def test_decode_sizes(lib):
     assert peagle.decode_v_tiles_bytes(1000, 3, 2, 128) == (1000 // 32 + 3 + 1) * 2 * 128 * 32 * 2
     assert peagle.decode_v_tiles_bytes(0, 1, 1, 64) == 2 * 64 * 32 * 2
     assert peagle.decode_v_tiles_bytes(-1, 1, 1, 64) == 0
-    a = peagle.decode_workspace_bytes(8, 4, 4, 1, 256, 32768)
-    b = peagle.decode_workspace_bytes(64, 4, 4, 1, 256, 32768)
+    a = peagle.decode_workspace_bytes(8, 4, 4, 1, 256, 8 * 32768, 32768)
+    b = peagle.decode_workspace_bytes(64, 4, 4, 1, 256, 64 * 32768, 32768)
     assert 0 < a < b and a % 256 == 0
-    assert peagle.decode_workspace_bytes(8, 33, 4, 1, 256, 100) == 0
+    assert peagle.decode_workspace_bytes(8, 33, 4, 1, 256, 1000, 100) == 0
+    assert peagle.decode_workspace_bytes(8, 4, 4, 1, 256, 99, 100) == 0    # total < max
 
 
 def test_decode_tile_bases_never_overlap():

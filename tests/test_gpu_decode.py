@@ -47,6 +47,8 @@ DECODE_SMALL = [
     ([5000], 4, 4, 1, 256, 1e4),                           # several partials per request
     ([400, 90, 3], 8, 8, 2, 64, 1e4),                      # D = 64, two groups per wave
     ([4097, 1, 2222], 5, 12, 3, 128, 5e5),                 # odd K, G = 4, ragged groups
+    ([130, 2000, 47], 4, 16, 4, 256, 1e4),                 # four kv heads a workgroup
+    ([600, 33, 1200], 12, 8, 4, 64, 1e4),                  # same, 32 columns a wave
 ]
 
 

@@ -251,11 +251,13 @@ int peagle_decode_pack_v(int32_t num_reqs, const int32_t* cu_ctx, int64_t total_
 
 size_t peagle_draft_decode_workspace_bytes(int32_t num_reqs, int32_t K, int32_t num_q_heads,
                                            int32_t num_kv_heads, int32_t head_dim,
-                                           int32_t max_ctx) {
+                                           int64_t total_ctx, int32_t max_ctx) {
   if (!decode_dims_ok(num_reqs, num_kv_heads, head_dim) || K < 1 || K > 32 || max_ctx < 0 ||
-      num_q_heads < 1 || num_q_heads % num_kv_heads != 0)
+      total_ctx < max_ctx || total_ctx > kMaxI32 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads != 0)
     return 0;
-  return decode_workspace_bytes(num_reqs, K, num_q_heads, num_kv_heads, head_dim, max_ctx);
+  return decode_workspace_bytes(num_reqs, K, num_q_heads, num_kv_heads, head_dim, total_ctx,
+                                max_ctx);
 }
 
 int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
@@ -272,6 +274,10 @@ int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
   if (num_q_heads < 1 || num_q_heads % num_kv_heads != 0) return PEAGLE_ERR_ARG;
   if ((int64_t)num_kv_heads * ((num_q_heads / num_kv_heads * K + 31) / 32) > 65535)
     return PEAGLE_ERR_UNSUPPORTED;
+  // the combine kernel runs one thread per (request, kv head, column, 4 dims)
+  if ((int64_t)num_reqs * num_kv_heads * ((num_q_heads / num_kv_heads * K + 31) / 32 * 32) *
+          (head_dim / 4) > kMaxI32)
+    return PEAGLE_ERR_UNSUPPORTED;
   if (total_ctx < 0 || total_ctx > kMaxI32 || max_ctx < 0 || max_ctx > total_ctx)
     return PEAGLE_ERR_ARG;
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return PEAGLE_ERR_ARG;
@@ -287,7 +293,7 @@ int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
       v_tiles_bytes_given < v_tiles_bytes(total_ctx, num_reqs, num_kv_heads, head_dim))
     return PEAGLE_ERR_WORKSPACE;
   if (workspace_bytes <
-      decode_workspace_bytes(num_reqs, K, num_q_heads, num_kv_heads, head_dim, max_ctx))
+      decode_workspace_bytes(num_reqs, K, num_q_heads, num_kv_heads, head_dim, total_ctx, max_ctx))
     return PEAGLE_ERR_WORKSPACE;
   DecodeArgs a{num_reqs, K, num_q_heads, num_kv_heads, head_dim, max_ctx, rope_max_pos,
                total_ctx, softmax_scale};

@@ -19,20 +19,22 @@
 //            previous request and needs no prefix sum.
 //
 // Kernels (all on the caller's stream):
-//   decode_prep     rotates q and the new keys at L_b + d into the workspace and lays the
-//                   new rows' keys and values out as one extra 32-key tile per
-//                   (request, kv head).
+//   decode_prep     one thread per rotation pair or element: q rotated at L_b + d, the new
+//                   rows' keys rotated at L_b + e as one extra 32-key tile per (request, kv
+//                   head) (zero rows past K), and their values as that tile's V^T.
 //   decode_attn     split-KV: a workgroup owns (request, kv head, column group, a slice
 //                   of the cache tiles); its four waves take the slice's tiles in turn.
 //                   A wave holds 16 or 32 query columns (column c of a kv head: q head
 //                   g*G + c / K, depth c % K) and computes S^T = K Q^T and O^T = V^T P^T
-//                   on v_mfma_f32_16x16x32_bf16 with an online softmax in base 2
-//                   (scale folded into one FMA) that rescales only when the running max
-//                   grows by more than 2^8; the weights enter PV as a hi + lo bf16 pair.
-//                   The waves merge through LDS and the workgroup writes one partial
+//                   on v_mfma_f32_16x16x32_bf16 with an online softmax in base 2 (scale
+//                   folded into one FMA) that rescales only when the running max grows by
+//                   more than 2^8; the weights enter PV as a hi + lo bf16 pair. The first
+//                   wave of each request's first slice also takes the new rows' tile. The
+//                   waves merge through LDS and the workgroup writes one partial
 //                   (O, max, sum).
 //   decode_combine  merges the partials of each (request, kv head, column group).
-// The path is HBM-bound: every cache byte is read once.
+// The path is HBM-bound: every cache byte is read once. Nothing before a workgroup's first
+// tile loads waits on memory but the request bounds, so its start costs one round trip.
 #include <algorithm>
 
 #include "common.h"
@@ -61,13 +63,13 @@ __host__ __device__ constexpr int dec_key(int s) {
 
 struct DecodeParams {
   const int32_t* cu;
-  const uint16_t* kc;    // [Ltot, Hkv, D]
-  const uint16_t* vt;    // V tiles
+  const uint16_t* kc;  // [Ltot, Hkv, D] rotated
+  const uint16_t* vt;  // V tiles
   const uint16_t* qr;    // rotated q [B, K, Hq, D]
   const uint16_t* knew;  // rotated new keys [B, Hkv, 32, D], zero rows past K
   const uint16_t* vnew;  // new values as a V^T tile [B, Hkv, D, 32]
-  float* part_o;         // [B, Hkv, NCg, NPW, PC, D]
-  float* part_ml;        // [B, Hkv, NCg, NPW, PC, 2]: max (base 2) and sum
+  float* part_o;       // [B, Hkv, NCg, NPW, PC, D]
+  float* part_ml;      // [B, Hkv, NCg, NPW, PC, 2]: max (base 2) and sum
   int B, K, Hq, Hkv, G, GK, NCg, NPW, tpw, max_ctx;
   int64_t total_ctx, ntiles;
   float c_log2;
@@ -82,51 +84,78 @@ __device__ __forceinline__ void request_extent(const int32_t* cu, int b, int64_t
                              std::min<int64_t>(max_ctx, total_ctx - c0));
 }
 
-// Rotate-half RoPE of one pre-RoPE bf16 row at position pos into bf16 (fp32 arithmetic):
-// dims j and j + D/2 turn by pos * theta^(-2j/D), cos/sin read from the table.
-__device__ __forceinline__ void rope_row(const uint16_t* src, uint16_t* dst, int D, int pos,
-                                         const float* cs, const float* sn, int lane, int nlanes) {
-  const int H = D / 2;
-  for (int j = lane; j < H; j += nlanes) {
-    const float a = bf16_bits_to_f32(src[j]), b = bf16_bits_to_f32(src[j + H]);
-    const float c = cs[(size_t)pos * H + j], s = sn[(size_t)pos * H + j];
-    dst[j] = f32_to_bf16_bits(a * c - b * s);
-    dst[j + H] = f32_to_bf16_bits(b * c + a * s);
+// Rotate-half RoPE of dims j0 .. j0 + 7 and their partners j0 + D/2 .. of one pre-RoPE bf16
+// row at position pos, rounded to bf16 (fp32 arithmetic; cos/sin from the table).
+__device__ __forceinline__ void rope8(const uint16_t* src, uint16_t* dst, int j0, int H, int pos,
+                                      const float* cs, const float* sn) {
+  const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(src + j0));
+  const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4*>(src + j0 + H));
+  const floatx4* cp = reinterpret_cast<const floatx4*>(cs + (size_t)pos * H + j0);
+  const floatx4* sp = reinterpret_cast<const floatx4*>(sn + (size_t)pos * H + j0);
+  const floatx4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+  bf16x8 lo, hi;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = (float)a[e], y = (float)b[e];
+    const float c = e < 4 ? c0[e] : c1[e - 4], s = e < 4 ? s0[e] : s1[e - 4];
+    lo[e] = (__bf16)(x * c - y * s);
+    hi[e] = (__bf16)(y * c + x * s);
   }
+  *reinterpret_cast<bf16x8*>(dst + j0) = lo;
+  *reinterpret_cast<bf16x8*>(dst + j0 + H) = hi;
 }
 
-// One workgroup per (request, kv head).
+// Flat grid, 8 outputs per thread, over three ranges: q (B K Hq rows, D/16 threads a row),
+// new keys (B Hkv 32 rows, D/16 threads a row), new V^T (B Hkv D rows of 32 slots, 4
+// threads a row).
 __global__ __launch_bounds__(256) void decode_prep_kernel(
     const int32_t* __restrict__ cu, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ cs, const float* __restrict__ sn,
-    uint16_t* __restrict__ qr, uint16_t* __restrict__ knew, uint16_t* __restrict__ vnew, int K,
-    int Hq, int Hkv, int D, int max_ctx, int max_pos, int64_t total_ctx) {
-  const int b = blockIdx.x / Hkv, g = blockIdx.x % Hkv, G = Hq / Hkv;
+    uint16_t* __restrict__ qr, uint16_t* __restrict__ knew, uint16_t* __restrict__ vnew, int B,
+    int K, int Hq, int Hkv, int D, int max_ctx, int max_pos, int64_t total_ctx) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int H = D / 2, per_row = D / 16;
+  const int64_t nq = (int64_t)B * K * Hq * per_row, nk = (int64_t)B * Hkv * kDecTile * per_row;
+  const int64_t nv = (int64_t)B * Hkv * D * (kDecTile / 8);
   int64_t c0;
   int L;
-  request_extent(cu, b, total_ctx, max_ctx, c0, L);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // q rows of this kv head's q heads, every depth
-  for (int r = wave; r < K * G; r += kDecWaves) {
-    const int d = r / G, h = g * G + r % G;
-    const size_t off = (((size_t)b * K + d) * Hq + h) * D;
-    rope_row(q + off, qr + off, D, std::min(L + d, max_pos), cs, sn, lane, 64);
-  }
-  // new keys: rows 0 .. K-1 rotated, rows K .. 31 zero
-  uint16_t* kn = knew + ((size_t)b * Hkv + g) * kDecTile * D;
-  for (int e = wave; e < kDecTile; e += kDecWaves) {
+  if (t < nq) {
+    const int j0 = (int)(t % per_row) * 8;
+    const int64_t row = t / per_row;  // (b, d, h)
+    const int d = (int)((row / Hq) % K), b = (int)(row / ((int64_t)Hq * K));
+    request_extent(cu, b, total_ctx, max_ctx, c0, L);
+    rope8(q + row * D, qr + row * D, j0, H, std::min(L + d, max_pos), cs, sn);
+  } else if (t < nq + nk) {
+    const int64_t u = t - nq;
+    const int j0 = (int)(u % per_row) * 8;
+    const int64_t row = u / per_row;  // (b, g, e)
+    const int e = (int)(row % kDecTile);
+    const int64_t bg = row / kDecTile;
+    const int g = (int)(bg % Hkv), b = (int)(bg / Hkv);
+    uint16_t* dst = knew + row * D;
     if (e < K) {
-      rope_row(k + (((size_t)b * K + e) * Hkv + g) * D, kn + (size_t)e * D, D,
-               std::min(L + e, max_pos), cs, sn, lane, 64);
+      request_extent(cu, b, total_ctx, max_ctx, c0, L);
+      rope8(k + (((size_t)b * K + e) * Hkv + g) * D, dst, j0, H, std::min(L + e, max_pos), cs, sn);
     } else {
-      for (int j = lane; j < D; j += 64) kn[(size_t)e * D + j] = 0;
+      *reinterpret_cast<u32x4*>(dst + j0) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(dst + j0 + H) = u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  // new values as a V^T tile
-  uint16_t* vn = vnew + ((size_t)b * Hkv + g) * D * kDecTile;
-  for (int t = threadIdx.x; t < D * kDecTile; t += blockDim.x) {
-    const int dim = t / kDecTile, e = dec_key(t % kDecTile);
-    vn[t] = e < K ? v[(((size_t)b * K + e) * Hkv + g) * D + dim] : (uint16_t)0;
+  } else if (t < nq + nk + nv) {
+    const int64_t u = t - nq - nk;
+    const int s0 = (int)(u % (kDecTile / 8)) * 8;
+    const int64_t drow = u / (kDecTile / 8);  // (b, g, dim)
+    const int dim = (int)(drow % D);
+    const int64_t bg = drow / D;
+    const int g = (int)(bg % Hkv), b = (int)(bg / Hkv);
+    bf16x8 out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = dec_key(s0 + i);
+      const uint16_t bits =
+          v[(((size_t)b * K + std::min(e, K - 1)) * Hkv + g) * D + dim];
+      out[i] = __builtin_bit_cast(__bf16, e < K ? bits : (uint16_t)0);
+    }
+    *reinterpret_cast<bf16x8*>(vnew + drow * kDecTile + s0) = out;
   }
 }
 
@@ -138,27 +167,15 @@ struct DecodeWave {
   float m_run[NCW], l_run[NCW];
 };
 
-// One 32-key tile: rows [0, rows) of kbase (row stride kstride elements) and its V^T tile;
-// column group c keeps keys below lim[c].
+// Scores, online softmax and PV of one 32-key tile held in registers: kf[h] are the A
+// fragments of keys 16 h .. 16 h + 15, vf the V^T fragments; column group c keeps the
+// keys below lim[c].
 template <int D, int NCW>
-__device__ __forceinline__ void decode_tile(DecodeWave<D, NCW>& w, const uint16_t* kbase,
-                                            size_t kstride, int rows, const uint16_t* vtile,
-                                            const int (&lim)[NCW], float c_log2, int l16,
-                                            int grp) {
+__device__ __forceinline__ void decode_tile_math(DecodeWave<D, NCW>& w,
+                                                 const bf16x8 (&kf)[2][D / 32],
+                                                 const bf16x8 (&vf)[D / 16],
+                                                 const int (&lim)[NCW], float c_log2, int grp) {
   constexpr int DK = D / 32, MT = D / 16;
-  bf16x8 kf[2][DK];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = std::min(16 * h + l16, rows - 1);
-    const uint16_t* kp = kbase + (size_t)row * kstride + 8 * grp;
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-      kf[h][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 32 * kk));
-  }
-  bf16x8 vf[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    vf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp));
 #pragma unroll
   for (int c = 0; c < NCW; ++c) {
     floatx4 s[2];
@@ -208,20 +225,66 @@ __device__ __forceinline__ void decode_tile(DecodeWave<D, NCW>& w, const uint16_
   }
 }
 
+// One cache tile: rows [0, rows) of kbase (row stride kstride elements) and its V^T tile.
 template <int D, int NCW>
+__device__ __forceinline__ void decode_cache_tile(DecodeWave<D, NCW>& w, const uint16_t* kbase,
+                                                  size_t kstride, int rows,
+                                                  const uint16_t* vtile, float c_log2, int l16,
+                                                  int grp) {
+  constexpr int DK = D / 32, MT = D / 16;
+  bf16x8 kf[2][DK];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = std::min(16 * h + l16, rows - 1);
+    const uint16_t* kp = kbase + (size_t)row * kstride + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+      kf[h][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 32 * kk));
+  }
+  bf16x8 vf[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    vf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp));
+  // every load of the tile is issued before the first wait on any of them: one memory
+  // round trip per tile instead of one for K and then one for V
+  __builtin_amdgcn_sched_barrier(0);
+  int lim[NCW];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) lim[c] = rows;
+  decode_tile_math<D, NCW>(w, kf, vf, lim, c_log2, grp);
+}
+
+// Work split. A workgroup job is (request b, slice of tpw cache tiles, column group, group
+// of HEADS kv heads), the head group fastest. HEADS = 4 (Hkv a multiple of 4): wave w
+// takes kv head 4 gg + w and the whole slice, so the four waves read neighbouring head
+// segments of the same cache rows, and each wave writes its partial. HEADS = 1: the four
+// waves take the slice's tiles in turn (neighbouring tiles at the same time) and merge
+// through LDS into one partial.
+template <int D, int NCW, int HEADS>
 __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_attn_kernel(const DecodeParams p) {
   constexpr int DK = D / 32, MT = D / 16, PC = 16 * NCW;
-  __shared__ float red_o[kDecWaves][PC][D];
-  __shared__ float red_ml[kDecWaves][PC][2];
+  constexpr bool kMerge = HEADS == 1;
+  constexpr int kRedWaves = kMerge ? kDecWaves : 1;
+  __shared__ float red_o[kRedWaves][kMerge ? PC : 1][kMerge ? D : 1];
+  __shared__ float red_ml[kRedWaves][kMerge ? PC : 1][2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int wp = blockIdx.x, b = blockIdx.z;
-  const int g = blockIdx.y / p.NCg, cg = blockIdx.y % p.NCg;
   const int K = p.K, Hkv = p.Hkv;
+  const int ngg = Hkv / HEADS;
+  const int gg = (int)(blockIdx.x % ngg);
+  const int64_t r1 = blockIdx.x / ngg;
+  const int cg = (int)(r1 % p.NCg);
+  const int64_t r2 = r1 / p.NCg;
+  const int slice = (int)(r2 % p.NPW);
+  const int b = (int)(r2 / p.NPW);
+  const int g = HEADS == 1 ? gg : gg * HEADS + wave;
   int64_t c0;
   int L;
   request_extent(p.cu, b, p.total_ctx, p.max_ctx, c0, L);
   const int ntiles_b = (L + kDecTile - 1) / kDecTile;
+  // slices past the request's end hold nothing and write no partial (slice 0 always holds
+  // the new rows' tile); the test is uniform over the workgroup, before any barrier
+  if (slice > 0 && slice * p.tpw >= ntiles_b) return;
 
   DecodeWave<D, NCW> w;
   int dcol[NCW];
@@ -240,95 +303,169 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_attn_kernel(const De
     w.l_run[c] = 0.f;
   }
 
-  // the new rows' keys: one masked tile, row d keeps new keys e <= d
-  if (wp == 0 && wave == 0) {
+  // the new rows' tile (laid out by decode_prep): row d keeps new keys e <= d
+  if (slice == 0 && (HEADS > 1 || wave == 0)) {
+    const size_t bg = (size_t)b * Hkv + g;
+    const uint16_t* kbase = p.knew + bg * kDecTile * D;
+    const uint16_t* vtile = p.vnew + bg * D * kDecTile;
+    bf16x8 kf[2][DK];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kk = 0; kk < DK; ++kk)
+        kf[h][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + (16 * h + l16) * D + 32 * kk + 8 * grp));
+    bf16x8 vf[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      vf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp));
     int lim[NCW];
 #pragma unroll
     for (int c = 0; c < NCW; ++c) lim[c] = dcol[c] + 1;
-    const size_t bg = (size_t)b * Hkv + g;
-    decode_tile<D, NCW>(w, p.knew + bg * kDecTile * D, D, kDecTile, p.vnew + bg * D * kDecTile,
-                        lim, p.c_log2, l16, grp);
+    decode_tile_math<D, NCW>(w, kf, vf, lim, p.c_log2, grp);
   }
-  // this workgroup's slice of the cache tiles, dealt out to the waves in turn
-  const int t_end = std::min((wp + 1) * p.tpw, ntiles_b);
+  // the slice's cache tiles
+  const int t_end = std::min((slice + 1) * p.tpw, ntiles_b);
   const uint16_t* vbase = p.vt + (((size_t)g * p.ntiles + (c0 >> 5) + b) * D) * kDecTile;
-  for (int t = wp * p.tpw + wave; t < t_end; t += kDecWaves) {
+  const int t_step = HEADS == 1 ? kDecWaves : 1;
+  for (int t = slice * p.tpw + (HEADS == 1 ? wave : 0); t < t_end; t += t_step) {
     const int key0 = t * kDecTile;
-    int lim[NCW];
-#pragma unroll
-    for (int c = 0; c < NCW; ++c) lim[c] = L - key0;
-    decode_tile<D, NCW>(w, p.kc + ((size_t)(c0 + key0) * Hkv + g) * D, (size_t)Hkv * D,
-                        L - key0, vbase + (size_t)t * D * kDecTile, lim, p.c_log2, l16, grp);
+    decode_cache_tile<D, NCW>(w, p.kc + ((size_t)(c0 + key0) * Hkv + g) * D, (size_t)Hkv * D,
+                              L - key0, vbase + (size_t)t * D * kDecTile, p.c_log2, l16, grp);
   }
 
-  // merge the four waves through LDS; the workgroup writes one partial
+  const size_t part = (((size_t)b * Hkv + g) * p.NCg + cg) * p.NPW + slice;
+  if constexpr (!kMerge) {
+    // the wave's partial: O^T columns (the lane holds dims 16 mt + 4 grp + r of column
+    // l16), running max and sum
 #pragma unroll
-  for (int c = 0; c < NCW; ++c) {
-    float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    for (int c = 0; c < NCW; ++c) {
+      float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
+      float* po = p.part_o + (part * PC + c * 16 + l16) * D;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      *reinterpret_cast<floatx4*>(&red_o[wave][c * 16 + l16][16 * mt + 4 * grp]) = w.o[c][mt];
-    if (grp == 0) {
-      red_ml[wave][c * 16 + l16][0] = w.m_run[c];
-      red_ml[wave][c * 16 + l16][1] = lt;
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<floatx4*>(po + 16 * mt + 4 * grp) = w.o[c][mt];
+      if (grp == 0) {
+        p.part_ml[(part * PC + c * 16 + l16) * 2] = w.m_run[c];
+        p.part_ml[(part * PC + c * 16 + l16) * 2 + 1] = lt;
+      }
     }
-  }
-  __syncthreads();
-  const size_t part = (((size_t)b * Hkv + g) * p.NCg + cg) * p.NPW + wp;
-  for (int t = threadIdx.x; t < PC * (D / 4); t += 64 * kDecWaves) {
-    const int col = t / (D / 4), d4 = (t % (D / 4)) * 4;
-    float M = -INFINITY;
+  } else {
+    // merge the four waves through LDS; the workgroup writes one partial
 #pragma unroll
-    for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, red_ml[q][col][0]);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
+    for (int c = 0; c < NCW; ++c) {
+      float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
+      lt += __shfl_xor(lt, 32, 64);
 #pragma unroll
-    for (int q = 0; q < kDecWaves; ++q) {
-      const float mq = red_ml[q][col][0];
-      const float f = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
-      acc += f * *reinterpret_cast<const floatx4*>(&red_o[q][col][d4]);
-      lsum += f * red_ml[q][col][1];
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<floatx4*>(&red_o[wave][c * 16 + l16][16 * mt + 4 * grp]) = w.o[c][mt];
+      if (grp == 0) {
+        red_ml[wave][c * 16 + l16][0] = w.m_run[c];
+        red_ml[wave][c * 16 + l16][1] = lt;
+      }
     }
-    *reinterpret_cast<floatx4*>(p.part_o + (part * PC + col) * D + d4) = acc;
-    if (d4 == 0) {
-      p.part_ml[(part * PC + col) * 2] = M;
-      p.part_ml[(part * PC + col) * 2 + 1] = lsum;
+    __syncthreads();
+    for (int t = threadIdx.x; t < PC * (D / 4); t += 64 * kDecWaves) {
+      const int col = t / (D / 4), d4 = (t % (D / 4)) * 4;
+      float M = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, red_ml[q][col][0]);
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      float lsum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kDecWaves; ++q) {
+        const float mq = red_ml[q][col][0];
+        const float f = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+        acc += f * *reinterpret_cast<const floatx4*>(&red_o[q][col][d4]);
+        lsum += f * red_ml[q][col][1];
+      }
+      *reinterpret_cast<floatx4*>(p.part_o + (part * PC + col) * D + d4) = acc;
+      if (d4 == 0) {
+        p.part_ml[(part * PC + col) * 2] = M;
+        p.part_ml[(part * PC + col) * 2 + 1] = lsum;
+      }
     }
   }
 }
 
-// Merge the NPW partials of (request, kv head, column group): out = sum_p 2^(m_p - M) O_p /
-// sum_p 2^(m_p - M) l_p and lse = (M + log2 of that sum) ln 2, M the largest m_p.
-// One thread per (column, 4 dims).
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_o,
-                                                             const float* __restrict__ part_ml,
-                                                             float* __restrict__ out,
-                                                             float* __restrict__ lse, int K, int Hq,
-                                                             int Hkv, int G, int GK, int NCg,
-                                                             int NPW, int PC, int D) {
-  const int item = blockIdx.x, cg = item % NCg, bg = item / NCg, b = bg / Hkv, g = bg % Hkv;
+// Merge the NPW partials of each (request, kv head, column group): out = sum_p 2^(m_p - M)
+// O_p / sum_p 2^(m_p - M) l_p and lse = (M + log2 of that sum) ln 2, M the largest m_p.
+// Eight lanes share one output (column, 4 dims): lane r takes partials r, r + 8, ..., all
+// loads in flight together, and the eight running states merge by shuffles.
+constexpr int kCombLanes = 8;
+__global__ __launch_bounds__(256) void decode_combine_kernel(
+    const int32_t* __restrict__ cu, const float* __restrict__ part_o,
+    const float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse, int K,
+    int Hq, int Hkv, int G, int GK, int NCg, int NPW, int PC, int D, int tpw, int max_ctx,
+    int64_t total_ctx, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t o = t / kCombLanes;
+  const int r = (int)(t % kCombLanes);
+  if (o >= n) return;  // n outputs: the eight lanes of an output leave together
   const int per_col = D / 4;
-  const int ncols = std::min(PC, GK - cg * PC);
+  const int d4 = (int)(o % per_col) * 4;
+  const int c = (int)((o / per_col) % PC);
+  const int64_t item = o / ((int64_t)per_col * PC);
+  const int cg = (int)(item % NCg);
+  const int col = cg * PC + c;
+  if (col >= GK) return;
+  const int64_t bg = item / NCg;
+  const int b = (int)(bg / Hkv), g = (int)(bg % Hkv);
   const size_t base = (size_t)item * NPW;
-  for (int t = threadIdx.x; t < ncols * per_col; t += blockDim.x) {
-    const int c = t / per_col, d4 = (t % per_col) * 4;
-    float M = -INFINITY;
-    for (int q = 0; q < NPW; ++q) M = fmaxf(M, part_ml[((base + q) * PC + c) * 2]);
-    float lsum = 0.f;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < NPW; ++q) {
-      const float mq = part_ml[((base + q) * PC + c) * 2];
-      if (mq == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(mq - M);
-      lsum += f * part_ml[((base + q) * PC + c) * 2 + 1];
-      acc += f * *reinterpret_cast<const floatx4*>(part_o + ((base + q) * PC + c) * D + d4);
+  // only the slices that held cache tiles (and slice 0) wrote a partial
+  int64_t c0;
+  int L;
+  request_extent(cu, b, total_ctx, max_ctx, c0, L);
+  const int nparts = std::min(NPW, std::max(1, ((L + kDecTile - 1) / kDecTile + tpw - 1) / tpw));
+  float M = -INFINITY, lsum = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  // up to 8 partials per lane per round, all loaded before any is used
+  for (int q0 = r; q0 < nparts; q0 += 8 * kCombLanes) {
+    float mq[8], lq[8];
+    floatx4 oq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = std::min(q0 + i * kCombLanes, nparts - 1);
+      mq[i] = part_ml[((base + q) * PC + c) * 2];
+      lq[i] = part_ml[((base + q) * PC + c) * 2 + 1];
+      oq[i] = *reinterpret_cast<const floatx4*>(part_o + ((base + q) * PC + c) * D + d4);
     }
-    const int col = cg * PC + c, d = col % K, head = g * G + col / K;
-    *reinterpret_cast<floatx4*>(out + (((size_t)b * K + d) * Hq + head) * D + d4) = acc / lsum;
-    if (lse != nullptr && d4 == 0)
-      lse[((size_t)b * K + d) * Hq + head] = (M + __log2f(lsum)) * 0.69314718055994531f;
+    float Mr = M;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (q0 + i * kCombLanes < nparts) Mr = fmaxf(Mr, mq[i]);
+    if (Mr == -INFINITY) continue;
+    const float fa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mr);
+    acc *= fa;
+    lsum *= fa;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool use = q0 + i * kCombLanes < nparts && mq[i] != -INFINITY;
+      const float f = use ? __builtin_amdgcn_exp2f(mq[i] - Mr) : 0.f;
+      acc += f * oq[i];
+      lsum += f * lq[i];
+    }
+    M = Mr;
   }
+#pragma unroll
+  for (int sh = 1; sh < kCombLanes; sh <<= 1) {
+    const float Mo = __shfl_xor(M, sh, 64);
+    const float lo = __shfl_xor(lsum, sh, 64);
+    floatx4 ao;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ao[e] = __shfl_xor(acc[e], sh, 64);
+    const float Mn = fmaxf(M, Mo);
+    const float fa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float fb = Mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mo - Mn);
+    acc = fa * acc + fb * ao;
+    lsum = fa * lsum + fb * lo;
+    M = Mn;
+  }
+  if (r != 0) return;
+  const int d = col % K, head = g * G + col / K;
+  *reinterpret_cast<floatx4*>(out + (((size_t)b * K + d) * Hq + head) * D + d4) = acc / lsum;
+  if (lse != nullptr && d4 == 0)
+    lse[((size_t)b * K + d) * Hq + head] = (M + __log2f(lsum)) * 0.69314718055994531f;
 }
 
 // Natural V [Ltot, Hkv, D] -> V tiles (layout in the header comment). One workgroup per
@@ -395,7 +532,8 @@ DecodeLayout decode_layout(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_
 
 int64_t decode_ntiles(int64_t total_ctx, int32_t B) { return (total_ctx >> 5) + B + 1; }
 
-DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx) {
+DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                       int64_t total_ctx, int32_t max_ctx) {
   DecodePlan pl;
   const int gk = (Hq / Hkv) * K;
   // two column groups per wave where the registers allow it (D <= 128)
@@ -403,19 +541,24 @@ DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
   pl.pc = 16 * pl.ncw;
   pl.ncg = (gk + pl.pc - 1) / pl.pc;
   const int tiles_max = (max_ctx + kDecTile - 1) / kDecTile;
-  const int64_t items = (int64_t)B * Hkv * pl.ncg;
-  // about 1024 workgroups (two per CU at two waves per SIMD), at least 16 tiles each so
-  // that the partials stay small next to the cache
-  const int64_t want = std::max<int64_t>((1024 + items - 1) / items, 1);
-  const int64_t cap = std::max<int64_t>((tiles_max + 15) / 16, 1);
-  pl.npw = (int)std::min(want, cap);
-  pl.tpw = std::max(1, (tiles_max + pl.npw - 1) / pl.npw);
+  // Four kv heads per workgroup where Hkv allows it; otherwise the waves share a slice.
+  pl.heads = Hkv % 4 == 0 ? 4 : 1;
+  // Fixed-size slices of a request's tiles. With four heads per workgroup a slice is one
+  // wave's: about 4096 waves with work (two rounds at two waves per SIMD), 8 to 64 tiles
+  // so that the wave's partial stays a few percent of its cache bytes. With shared
+  // slices: about 2048 workgroups with work, 4 to 32 tiles (one partial per workgroup).
+  const int64_t tile_items = ((total_ctx >> 5) + B) * Hkv * pl.ncg;
+  if (pl.heads == 4)
+    pl.tpw = (int)std::min<int64_t>(std::max<int64_t>((tile_items + 4095) / 4096, 8), 64);
+  else
+    pl.tpw = (int)std::min<int64_t>(std::max<int64_t>((tile_items + 2047) / 2048, kDecWaves), 32);
+  pl.npw = std::max(1, (tiles_max + pl.tpw - 1) / pl.tpw);
   return pl;
 }
 
 size_t decode_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
-                              int32_t max_ctx) {
-  return decode_layout(B, K, Hq, Hkv, D, decode_plan(B, K, Hq, Hkv, D, max_ctx)).total;
+                              int64_t total_ctx, int32_t max_ctx) {
+  return decode_layout(B, K, Hq, Hkv, D, decode_plan(B, K, Hq, Hkv, D, total_ctx, max_ctx)).total;
 }
 
 hipError_t launch_decode_pack_v(const int32_t* cu, int32_t B, int64_t total_ctx, int32_t max_ctx,
@@ -435,7 +578,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint
                               const uint16_t* vt, const uint16_t* qn, const uint16_t* kn,
                               const uint16_t* vn, const float* cs, const float* sn, float* out,
                               float* lse, char* ws, hipStream_t stream) {
-  const DecodePlan pl = decode_plan(a.B, a.K, a.Hq, a.Hkv, a.D, a.max_ctx);
+  const DecodePlan pl = decode_plan(a.B, a.K, a.Hq, a.Hkv, a.D, a.total_ctx, a.max_ctx);
   const DecodeLayout lay = decode_layout(a.B, a.K, a.Hq, a.Hkv, a.D, pl);
   DecodeParams p;
   p.cu = cu;
@@ -459,27 +602,37 @@ hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint
   p.total_ctx = a.total_ctx;
   p.ntiles = decode_ntiles(a.total_ctx, a.B);
   p.c_log2 = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(a.B * a.Hkv), dim3(256), 0, stream, cu, qn, kn, vn,
-                     cs, sn, reinterpret_cast<uint16_t*>(ws + lay.qr),
+  const int64_t nprep = (int64_t)a.B * a.K * a.Hq * (a.D / 16) +
+                        (int64_t)a.B * a.Hkv * kDecTile * (a.D / 16) +
+                        (int64_t)a.B * a.Hkv * a.D * (kDecTile / 8);
+  hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0,
+                     stream, cu, qn, kn, vn, cs, sn, reinterpret_cast<uint16_t*>(ws + lay.qr),
                      reinterpret_cast<uint16_t*>(ws + lay.knew),
-                     reinterpret_cast<uint16_t*>(ws + lay.vnew), a.K, a.Hq, a.Hkv, a.D,
+                     reinterpret_cast<uint16_t*>(ws + lay.vnew), a.B, a.K, a.Hq, a.Hkv, a.D,
                      a.max_ctx, a.max_pos, a.total_ctx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = for_dim(a.D, [&](auto dc) {
     constexpr int DD = decltype(dc)::value;
-    const dim3 grid(pl.npw, a.Hkv * pl.ncg, a.B);
+    const int heads = pl.heads;
+    const dim3 grid((unsigned)((int64_t)a.B * pl.npw * pl.ncg * (a.Hkv / heads)));
+    const dim3 block(64 * kDecWaves);
     if (pl.ncw == 2) {
-      if constexpr (DD <= 128)
-        hipLaunchKernelGGL((decode_attn_kernel<DD, 2>), grid, dim3(64 * kDecWaves), 0, stream, p);
+      if constexpr (DD <= 128) {
+        if (heads == 4) hipLaunchKernelGGL((decode_attn_kernel<DD, 2, 4>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((decode_attn_kernel<DD, 2, 1>), grid, block, 0, stream, p);
+      }
     } else {
-      hipLaunchKernelGGL((decode_attn_kernel<DD, 1>), grid, dim3(64 * kDecWaves), 0, stream, p);
+      if (heads == 4) hipLaunchKernelGGL((decode_attn_kernel<DD, 1, 4>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((decode_attn_kernel<DD, 1, 1>), grid, block, 0, stream, p);
     }
   });
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.Hkv * pl.ncg), dim3(256), 0, stream,
-                     p.part_o, p.part_ml, out, lse, a.K, a.Hq, a.Hkv, p.G, p.GK, pl.ncg, pl.npw,
-                     pl.pc, a.D);
+  const int64_t nout = (int64_t)a.B * a.Hkv * pl.ncg * pl.pc * (a.D / 4);
+  const int64_t nthreads = nout * kCombLanes;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
+                     stream, cu, p.part_o, p.part_ml, out, lse, a.K, a.Hq, a.Hkv, p.G, p.GK,
+                     pl.ncg, pl.npw, pl.pc, a.D, pl.tpw, a.max_ctx, a.total_ctx, nout);
   return hipGetLastError();
 }
 

@@ -78,14 +78,15 @@ struct DecodeArgs {
   float scale;
 };
 // Split of the decode attention: a wave holds ncw groups of 16 query columns (pc = 16 ncw
-// columns); ncg column groups per kv head; npw workgroups (one partial each) per
-// (request, kv head, column group), each over tpw cache tiles of 32 keys.
+// columns); ncg column groups per kv head; a request's cache tiles in npw slices of tpw
+// tiles (one partial each per kv head and column group); heads kv heads per workgroup.
 struct DecodePlan {
-  int ncw, pc, ncg, npw, tpw;
+  int ncw, pc, ncg, npw, tpw, heads;
 };
-DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx);
+DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
+                       int64_t total_ctx, int32_t max_ctx);
 size_t decode_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
-                              int32_t max_ctx);
+                              int64_t total_ctx, int32_t max_ctx);
 // V tiles per kv head of a cache of total_ctx keys over B requests.
 int64_t decode_ntiles(int64_t total_ctx, int32_t B);
 

@@ -41,7 +41,7 @@ SIGNATURES = {
     "peagle_accept_prefix": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _p], _i32),
     "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
-    "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32], _sz),
     "peagle_draft_decode_attn": ([_i32, _i32, _p, _i64, _i32, _p, _p, _sz, _p, _p, _p, _i32,
                                   _i32, _i32, _f32, _p, _p, _i32, _p, _p, _p, _sz, _p], _i32),
 }
@@ -228,8 +228,8 @@ def decode_pack_v(cu_ctx, max_ctx: int, v_cache, v_tiles=None):
     return v_tiles
 
 
-def decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx) -> int:
-    return int(lib().peagle_draft_decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx))
+def decode_workspace_bytes(B, K, Hq, Hkv, D, total_ctx, max_ctx) -> int:
+    return int(lib().peagle_draft_decode_workspace_bytes(B, K, Hq, Hkv, D, total_ctx, max_ctx))
 
 
 def draft_decode_attn(cu_ctx, max_ctx: int, k_cache, v_tiles, q, k, v, cos, sin, out=None,
@@ -249,7 +249,7 @@ def draft_decode_attn(cu_ctx, max_ctx: int, k_cache, v_tiles, q, k, v, cos, sin,
     if lse is None:
         lse = torch.empty((B, K, Hq), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty(decode_workspace_bytes(B, K, Hq, Hkv, D, max_ctx),
+        workspace = torch.empty(decode_workspace_bytes(B, K, Hq, Hkv, D, Ltot, max_ctx),
                                 dtype=torch.uint8, device=dev)
     _check("peagle_draft_decode_attn", lib().peagle_draft_decode_attn(
         B, K, _ptr(cu_ctx), Ltot, max_ctx, _ptr(k_cache), _ptr(v_tiles),
