@@ -52,6 +52,7 @@ def parse():
 
 
 TRAFFIC_RECORDS = {4: "profiles/attn_core_gemma270m_32k_K4_traffic.md"}
+DECODE_TRAFFIC_RECORD = "profiles/decode_attn_B64_ctx1k-32k_traffic.md"
 
 
 def traffic_bytes(config):
@@ -282,11 +283,20 @@ def decode_bench(name, steps, warmup):
     gbps = (cache_bytes + io_bytes) / (ms * 1e-3) / 1e9
     del inp, vt, out, lse, ws
     torch.cuda.empty_cache()
+    from token_drafting_amd import profiling
+    rec = profiling.recorded_decode_traffic(
+        os.path.join(os.path.dirname(os.path.abspath(__file__)), DECODE_TRAFFIC_RECORD),
+        cfg["workload"])
     return {"workload": cfg["workload"], "requests": B, "context_tokens": total, "K": K,
             "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "ms_per_call": round(ms, 4),
             "bytes_per_call": cache_bytes + io_bytes, "hbm_GBps": round(gbps, 1),
             "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
-            "drafted_tokens_per_s": round(B * K / (ms * 1e-3), 1)}
+            "drafted_tokens_per_s": round(B * K / (ms * 1e-3), 1),
+            "roofline": {"kernel": "whole peagle_draft_decode_attn call (prep, split-KV "
+                                   "attention, combine)",
+                         "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                         "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                         "traffic": None if rec is None else int(round(rec["call_bytes"]))}}
 
 
 def cpu_baseline(cfg, seed, qkv, cu, idx, depth_off, rows_wanted):

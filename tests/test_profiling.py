@@ -65,3 +65,36 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_decode_traffic_groups_calls_per_workload(tmp_path):
+    """Decode calls are (prep, attention, combine) triples in launch order; bench.py times
+    the workloads in sorted name order, the same number of calls each."""
+    from token_drafting_amd import synth
+    names = sorted(synth.DECODE_CONFIGS)
+    prep = "peagle::(anonymous namespace)::decode_prep_kernel(int const*)"
+    comb = "peagle::(anonymous namespace)::decode_combine_kernel(int const*)"
+    attn = ["void peagle::(anonymous namespace)::decode_attn_kernel<256, 1, 1>(peagle::P)",
+            "void peagle::(anonymous namespace)::decode_attn_kernel<128, 2, 4>(peagle::P)"]
+    f_rows, w_rows = [("__amd_rocclr_copyBuffer", 512.0)], [("__amd_rocclr_copyBuffer", 1024.0)]
+    for i in range(len(names)):
+        for _ in range(2):                       # two calls per workload
+            f_rows += [(prep, 1.0), (attn[i], 100.0 * (i + 1)), (comb, 2.0)]
+            w_rows += [(prep, 1.0), (attn[i], 10.0 * (i + 1)), (comb, 1.0)]
+    _write_run(tmp_path / "f", "FETCH_SIZE", f_rows)
+    _write_run(tmp_path / "w", "WRITE_SIZE", w_rows)
+    s = profiling.summarize(str(tmp_path / "f"), str(tmp_path / "w"), copy_mib=1)
+    rec = s["decode"]
+    assert rec["kernel_source_sha256"] == profiling.kernel_source_digest(profiling.DECODE_SOURCES)
+    for i, name in enumerate(names):
+        d = rec["workloads"][synth.DECODE_CONFIGS[name]["workload"]]
+        assert d["calls"] == 2
+        assert d["call_fetch_bytes"] == (1.0 + 100.0 * (i + 1) + 2.0) * 2048.0
+        assert d["call_write_bytes"] == (1.0 + 10.0 * (i + 1) + 1.0) * 1024.0
+    path = tmp_path / "dec.md"
+    profiling.write_decode_summary(str(path), rec, "cmd")
+    wl = synth.DECODE_CONFIGS[names[0]]["workload"]
+    assert profiling.recorded_decode_traffic(str(path), wl)["calls"] == 2
+    stale = dict(rec, kernel_source_sha256="0" * 64)
+    profiling.write_decode_summary(str(path), stale, "cmd")
+    assert profiling.recorded_decode_traffic(str(path), wl) is None

@@ -546,12 +546,12 @@ DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
   // Fixed-size slices of a request's tiles. With four heads per workgroup a slice is one
   // wave's: about 4096 waves with work (two rounds at two waves per SIMD), 8 to 64 tiles
   // so that the wave's partial stays a few percent of its cache bytes. With shared
-  // slices: about 2048 workgroups with work, 4 to 32 tiles (one partial per workgroup).
+  // slices: about 1024 workgroups with work, 16 to 32 tiles (one partial per workgroup).
   const int64_t tile_items = ((total_ctx >> 5) + B) * Hkv * pl.ncg;
   if (pl.heads == 4)
     pl.tpw = (int)std::min<int64_t>(std::max<int64_t>((tile_items + 4095) / 4096, 8), 64);
   else
-    pl.tpw = (int)std::min<int64_t>(std::max<int64_t>((tile_items + 2047) / 2048, kDecWaves), 32);
+    pl.tpw = (int)std::min<int64_t>(std::max<int64_t>((tile_items + 1023) / 1024, 16), 32);
   pl.npw = std::max(1, (tiles_max + pl.tpw - 1) / pl.tpw);
   return pl;
 }

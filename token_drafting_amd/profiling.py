@@ -23,13 +23,15 @@ from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCES = ("csrc/attn.hip", "csrc/common.h", "csrc/kernels.h")
+DECODE_SOURCES = ("csrc/decode.hip", "csrc/common.h", "csrc/kernels.h")
 CORE_KERNELS = ("attn_core_kernel",)  # both launches (main and exact) of one core call
 RECORD_TAG = "traffic_record:"
+DECODE_TAG = "decode_traffic_record:"
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=ATTN_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in ATTN_SOURCES:
+    for rel in sources:
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -107,7 +109,72 @@ def summarize(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
         "core_call_write_bytes": sum(d.get("write_bytes", 0.0) for d in core),
     }
     rec["core_call_bytes"] = rec["core_call_fetch_bytes"] + rec["core_call_write_bytes"]
-    return {"record": rec, "per_kernel": per_kernel}
+    return {"record": rec, "per_kernel": per_kernel,
+            "decode": _decode_traffic(fetch, write, f_fac, w_fac)}
+
+
+def _decode_traffic(fetch, write, f_fac: float, w_fac: float):
+    """Per-call bytes of the decode attention (prep, attention and combine launches) for
+    each inference workload, or None when the runs hold no decode calls. bench.py times
+    the workloads in sorted name order, the same number of calls each."""
+    from . import synth
+
+    def calls(rows, fac):
+        seq = [(name, kib * fac) for _, name, _, kib in rows
+               if any(k in name for k in ("decode_prep_kernel", "decode_attn_kernel",
+                                          "decode_combine_kernel"))]
+        out = []
+        for i in range(0, len(seq) - 2, 3):
+            (a, x), (b, y), (c, z) = seq[i:i + 3]
+            if "prep" in a and "attn" in b and "combine" in c:
+                out.append((b, x + y + z))
+        return out
+
+    cf, cw = calls(fetch, f_fac), calls(write, w_fac)
+    names = sorted(synth.DECODE_CONFIGS)
+    if not cf or len(cf) != len(cw) or len(cf) % len(names):
+        return None
+    per = len(cf) // len(names)
+    rec = {"kernel_source_sha256": kernel_source_digest(DECODE_SOURCES), "workloads": {}}
+    for i, name in enumerate(names):
+        f = [b for _, b in cf[i * per:(i + 1) * per]]
+        w = [b for _, b in cw[i * per:(i + 1) * per]]
+        rec["workloads"][synth.DECODE_CONFIGS[name]["workload"]] = {
+            "attn_kernel": cf[i * per][0], "calls": per,
+            "call_fetch_bytes": sum(f) / per, "call_write_bytes": sum(w) / per,
+            "call_bytes": (sum(f) + sum(w)) / per}
+    return rec
+
+
+def write_decode_summary(path: str, rec: dict, command: str) -> None:
+    lines = ["# HBM traffic per call: decode-shaped draft attention, inference workloads", "",
+             "Counter runs (each its own process):", "", "```", command, "```", "",
+             "Bytes of one peagle_draft_decode_attn call (prep, split-KV attention and combine "
+             "launches), FETCH_SIZE and WRITE_SIZE scaled by the plain copy of known size in "
+             "the same runs.", "",
+             "| workload | attention kernel | calls | read MB | written MB |", "|---|---|---|---|---|"]
+    for name, d in rec["workloads"].items():
+        lines.append(f"| {name} | `{d['attn_kernel']}` | {d['calls']} | "
+                     f"{d['call_fetch_bytes'] / 1e6:.2f} | {d['call_write_bytes'] / 1e6:.2f} |")
+    lines += ["", f"{DECODE_TAG} {json.dumps(rec)}", ""]
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+
+
+def recorded_decode_traffic(path: str, workload: str):
+    """Bytes per call of one decode workload from the stored record, if it was taken on the
+    current decode sources, else None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith(DECODE_TAG):
+                    rec = json.loads(line[len(DECODE_TAG):])
+                    if rec.get("kernel_source_sha256") != kernel_source_digest(DECODE_SOURCES):
+                        return None
+                    return rec["workloads"].get(workload)
+    except OSError:
+        return None
+    return None
 
 
 def write_summary(path: str, summary: dict, command: str) -> None:
@@ -203,41 +270,77 @@ def write_kernel_table(path: str, rows: list, title: str, command: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+DECODE_KERNELS = ("decode_prep_kernel", "decode_attn_kernel", "decode_combine_kernel")
+
+
+def _decode_calls(rows, n_calls: int):
+    """Per-call durations (first launch start to last launch end, ns) of the decode
+    attention calls in launch order: prep, attention, combine per call."""
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short(r["Kernel_Name"]))
+                 for r in rows if any(k in r["Kernel_Name"] for k in DECODE_KERNELS))
+    calls = []
+    for i in range(0, len(seq) - 2, 3):
+        a, b, c = seq[i], seq[i + 1], seq[i + 2]
+        if "prep" in a[2] and "attn" in b[2] and "combine" in c[2]:
+            calls.append((c[1] - a[0], b[1] - b[0], b[2]))
+    return calls
+
+
 def write_trace_summary(path: str, trace_dir: str, bench_log: str, title: str, command: str,
                         timed: int) -> None:
-    """Kernel-trace summary: per-kernel durations from rocprofv3's kernel trace, and the
-    agreement of the attention launches' last `timed` calls with bench.py's live timing."""
+    """Kernel-trace summary of the library's kernels: per-kernel durations from rocprofv3's
+    kernel trace, and the agreement of the last `timed` calls with bench.py's live timing
+    (attention core of the forward; each decode workload's whole call)."""
     rows = []
     for root, _, files in os.walk(trace_dir):
         for fn in files:
             if fn.endswith("kernel_trace.csv"):
                 with open(os.path.join(root, fn)) as f:
                     rows += list(csv.DictReader(f))
+    rows = [r for r in rows if "peagle::" in r["Kernel_Name"]]
     if not rows:
-        raise SystemExit(f"no kernel trace under {trace_dir}")
+        raise SystemExit(f"no library kernels in the trace under {trace_dir}")
     per = defaultdict(list)
     for r in rows:
         per[_short(r["Kernel_Name"])].append(
             (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
     total = sum(d for v in per.values() for _, d in v)
     lines = [f"# {title}", "", "Command (from the repository root):", "", "    " + command, "",
-             "Durations in microseconds from the kernel trace (all calls, warm-up included).", "",
-             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+             "Durations in microseconds from the kernel trace (all calls, warm-up included); "
+             "library kernels only (the run's input generation and calibration copy are left "
+             "out).", "",
+             "| kernel | calls | avg us | min us | max us | % of library GPU time |",
+             "|---|---|---|---|---|---|"]
     for name, v in sorted(per.items(), key=lambda kv: -sum(d for _, d in kv[1])):
         d = [x for _, x in v]
         lines.append(f"| `{name}` | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {min(d) / 1e3:.1f} | "
                      f"{max(d) / 1e3:.1f} | {100 * sum(d) / total:.2f} |")
     core = [k for k in per if any(c in k for c in CORE_KERNELS)]
     last = sum(sum(d for _, d in sorted(per[k])[-timed:]) / timed for k in core) / 1e3
-    live = None
+    live, dec_live = None, {}
     with open(bench_log) as f:
         for line in f:
             if line.startswith("{"):
-                live = json.loads(line)["stage_ms"]["attn_core"] * 1e3
+                j = json.loads(line)
+                live = j["stage_ms"]["attn_core"] * 1e3 if "stage_ms" in j else None
+                dec_live = j.get("decode", {})
     lines += ["", f"Agreement with the live timing: over the last {timed} calls the attention core "
               f"launches ({', '.join('`' + k + '`' for k in sorted(core))}) average {last:.1f} us "
               f"per call in the trace; bench.py's HIP events on the launch stream measured "
-              f"{live:.1f} us per call in the same run." if live is not None else "", ""]
+              f"{live:.1f} us per call in the same run." if live is not None else ""]
+    calls = _decode_calls(rows, timed)
+    if dec_live and calls:
+        per_wl = len(calls) // len(dec_live)
+        for i, (name, res) in enumerate(sorted(dec_live.items())):
+            mine = calls[i * per_wl:(i + 1) * per_wl][-timed:]
+            call_us = sum(c[0] for c in mine) / len(mine) / 1e3
+            attn_us = sum(c[1] for c in mine) / len(mine) / 1e3
+            lines.append(
+                f"Decode workload {res['workload']}: over its last {len(mine)} calls the trace "
+                f"gives {call_us:.1f} us per call (prep start to combine end; `{mine[0][2]}` "
+                f"{attn_us:.1f} us of it); bench.py measured {res['ms_per_call'] * 1e3:.1f} us "
+                f"per call.")
+    lines.append("")
     with open(path, "w") as f:
         f.write("\n".join(lines))
 
@@ -269,6 +372,8 @@ def main():
                     "write the per-kernel table instead of the traffic record")
     ap.add_argument("--copy-mib", type=int, default=0, help="calibration copy size of the runs")
     ap.add_argument("--out", required=True)
+    ap.add_argument("--decode-out", help="with --fetch/--write: also write the decode "
+                    "attention's per-call traffic record here")
     ap.add_argument("--title", default="Per-kernel counters")
     ap.add_argument("--command", required=True, help="the counter commands, for the record")
     a = ap.parse_args()
@@ -285,6 +390,9 @@ def main():
     s = summarize(a.fetch, a.write, a.copy_mib)
     write_summary(a.out, s, a.command)
     print(json.dumps(s["record"]))
+    if a.decode_out and s["decode"]:
+        write_decode_summary(a.decode_out, s["decode"], a.command)
+        print(json.dumps(s["decode"]))
 
 
 if __name__ == "__main__":
