@@ -24,6 +24,8 @@ Modules:
 - ``attention`` the multi-depth draft attention, with an explicit dense mask.
 - ``decode``    the same attention at inference: K new rows per request at one base
                 position over a KV cache (the flat [context, mask_1 ..] layout).
+- ``layer``     the first draft layer's attention inputs: RMSNorm of the embedding and
+                hidden halves, their concatenation, the QKV projection.
 - ``verify``    greedy verification and the longest accepted prefix.
 
 Inputs are bf16 bit patterns (uint16) or integer arrays; ``bf16`` converts the
@@ -34,4 +36,4 @@ closed forms, published test outputs, library routines, independent formulations
 or brute force. The SplitMix64 hash is pinned by the generator's published
 outputs for seed 0.
 """
-from . import bf16, cod, fuse, rope, attention, decode, verify  # noqa: F401
+from . import bf16, cod, fuse, rope, attention, decode, layer, verify  # noqa: F401
