@@ -189,6 +189,37 @@ int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,
                          void *stream);
 
 /*
+ * The first draft decoder layer's attention inputs [R, "How Speculative Decoding Works",
+ * step 3: the drafter input concatenates embeddings and hidden states; G, "Architecture":
+ * Llama-style decoder layers; N, changelog: depths >= 1 take the ptd token and the
+ * projected mask_hidden]. For every draft row:
+ *   x = [rms(embed) * w_norm_emb, rms(hidden) * w_norm_hidden]   (width 2H, embedding first;
+ *        rms(y) = y / sqrt(mean(y^2) + eps))
+ *   [q | k | v] = x W_qkv^T                                      (bias-free)
+ * All depth >= 1 rows share x, so the projection runs on rows 0 .. n (row n = the first
+ * depth-1 row) and rows n+1 .. T-1 receive row n's q, k and v.
+ *   hidden         fp32[T, H]  from peagle_fuse_inputs (hidden_out); rows 0 .. n are read
+ *   embed          bf16[T, H]  from peagle_fuse_inputs (embed_out); rows 0 .. n are read
+ *   w_norm_emb, w_norm_hidden  bf16[H]
+ *   eps            > 0 (Llama: 1e-6)
+ *   w_qkv          bf16[(Hq + 2 Hkv) D, 2H]  the q, k and v projections stacked by output
+ *                  row (linear-layer layout)
+ *   q              bf16[T, Hq, D]   out, pre-RoPE (the input of peagle_draft_attn_*)
+ *   k, v           bf16[T, Hkv, D]  out
+ *   workspace      >= peagle_layer1_qkv_workspace_bytes(n, T, H) bytes, 256-byte aligned
+ * H a multiple of 32 and head_dim a multiple of 8 (else PEAGLE_ERR_UNSUPPORTED);
+ * Hq % Hkv == 0. The projection runs as bf16 MFMA with fp32 accumulation on the
+ * normalised rows rounded to bf16.
+ */
+size_t peagle_layer1_qkv_workspace_bytes(int64_t n, int64_t T, int32_t H);
+int peagle_layer1_qkv(int64_t n, int32_t K, int64_t T, const float *hidden,
+                      const peagle_bf16 *embed, int32_t H, const peagle_bf16 *w_norm_emb,
+                      const peagle_bf16 *w_norm_hidden, float eps, const peagle_bf16 *w_qkv,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      peagle_bf16 *q, peagle_bf16 *k, peagle_bf16 *v, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * Draft attention at inference (the decode shape) [N, parity section: at inference one
  * flat parallel forward over [context, mask_1, ..., mask_{K-1}]; G, "Inference Process":
  * all depths drafted in one pass, drafting repeats from the last accepted token].

@@ -38,6 +38,32 @@ def assert_close(got, want, what: str, max_abs=MAX_ABS, max_rel_l2=MAX_REL_L2):
     return mabs, rel
 
 
+# Bar for projections whose operands and outputs are bf16 (the first layer's q, k, v),
+# derived from the arithmetic. bf16 keeps 8 significant bits, so rounding the GEMM's
+# input row x moves each term by up to 2^-8 of itself (RMS about 2^-8 / sqrt(3) over a
+# binade), and an output by a sum of 2H such terms: standard deviation about
+# 2^-8 / sqrt(3) * ||x * W_row||, i.e. 0.0023 for unit-RMS x and W ~ N(0, 1/(2H)) (outputs
+# of unit variance, the synthetic recipe), ~0.013 at the extremes of 10^6 outputs;
+# storing the output as bf16 adds up to 2^-8 |q|. Hence 2e-2, absolute below magnitude 1
+# and relative above it; relative L2 keeps 5e-3 (the model gives ~2.5e-3).
+BF16_PROJ_MAX = 2e-2
+
+
+def assert_close_bf16_out(got, want, what: str, max_abs=BF16_PROJ_MAX, max_rel_l2=MAX_REL_L2):
+    """max |got - want| / max(1, |want|) <= max_abs and relative L2 <= max_rel_l2."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    diff = got - want
+    scaled = float((np.abs(diff) / np.maximum(1.0, np.abs(want))).max()) if diff.size else 0.0
+    den = float(np.linalg.norm(want))
+    rel = float(np.linalg.norm(diff)) / den if den > 0 else float(np.linalg.norm(diff))
+    assert scaled <= max_abs, f"{what}: max|diff|/max(1,|want|) {scaled:.3e} > {max_abs}"
+    assert rel <= max_rel_l2, f"{what}: rel-L2 {rel:.3e} > {max_rel_l2}"
+    return scaled, rel
+
+
 def sample_rows(depth_off, cu_seqlens, idx, count=96, seed=0) -> np.ndarray:
     """Rows the oracle recomputes at full size: both ends of every depth, the rows of
     each sequence's first and last anchor, and a seeded random spread."""

@@ -188,3 +188,24 @@ def test_decode_tile_bases_never_overlap():
             assert start >= prev_end and end <= ntiles
             if lens[b]:
                 prev_end = end
+
+
+def test_layer1_argument_errors(lib):
+    base = dict(n=64, K=4, T=150, H=640, eps=1e-6, Hq=4, Hkv=1, D=256, ws=1 << 30)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return _code("peagle_layer1_qkv", a["n"], a["K"], a["T"], None, None, a["H"], None, None,
+                     a["eps"], None, a["Hq"], a["Hkv"], a["D"], None, None, None, None, a["ws"],
+                     None)
+    assert call() == peagle.ERR_ARG                        # NULL pointers
+    assert call(H=48) == peagle.ERR_UNSUPPORTED            # not a multiple of 32
+    assert call(D=12) == peagle.ERR_UNSUPPORTED
+    assert call(T=63) == peagle.ERR_ARG
+    assert call(T=257) == peagle.ERR_ARG                   # T > K n
+    assert call(Hq=5, Hkv=2) == peagle.ERR_ARG
+    assert call(eps=0.0) == peagle.ERR_ARG
+    # rows 0 .. n of [emb, hidden] normalised, bf16: (n + 1) x 2H x 2 bytes, 256-aligned
+    assert peagle.layer1_qkv_workspace_bytes(64, 150, 640) == ((65 * 1280 * 2 + 255) // 256) * 256
+    assert peagle.layer1_qkv_workspace_bytes(64, 64, 640) == 64 * 1280 * 2
+    assert peagle.layer1_qkv_workspace_bytes(0, 10, 640) == 0

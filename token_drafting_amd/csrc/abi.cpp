@@ -6,6 +6,7 @@
 
 #include "peagle.h"
 #include "kernels.h"
+#include "layer.h"
 
 using namespace peagle;
 
@@ -300,6 +301,39 @@ int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
   return status_of(launch_decode_attn(a, cu_ctx, k_cache, v_tiles, q, k, v, rope_cos, rope_sin,
                                       out, lse, static_cast<char*>(workspace),
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t peagle_layer1_qkv_workspace_bytes(int64_t n, int64_t T, int32_t H) {
+  if (n < 1 || T < n || T > kMaxI32 || H < 1) return 0;
+  return layer1_workspace_bytes(n, T, H);
+}
+
+int peagle_layer1_qkv(int64_t n, int32_t K, int64_t T, const float* hidden,
+                      const peagle_bf16* embed, int32_t H, const peagle_bf16* w_norm_emb,
+                      const peagle_bf16* w_norm_hidden, float eps, const peagle_bf16* w_qkv,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      peagle_bf16* q, peagle_bf16* k, peagle_bf16* v, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (n < 1 || n > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return PEAGLE_ERR_ARG;
+  if (T < n || T > (int64_t)K * n || T > kMaxI32) return PEAGLE_ERR_ARG;
+  if (H < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      head_dim < 1)
+    return PEAGLE_ERR_ARG;
+  if (H % 32 != 0 || head_dim % 8 != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if ((int64_t)(num_q_heads + 2 * num_kv_heads) * head_dim > kMaxI32) return PEAGLE_ERR_ARG;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return PEAGLE_ERR_ARG;
+  if (!hidden || !embed || !w_norm_emb || !w_norm_hidden || !w_qkv || !q || !k || !v ||
+      !workspace)
+    return PEAGLE_ERR_ARG;
+  if (!aligned16(hidden) || !aligned16(embed) || !aligned16(w_norm_emb) ||
+      !aligned16(w_norm_hidden) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(k) ||
+      !aligned16(v) || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return PEAGLE_ERR_ARG;
+  if (workspace_bytes < layer1_workspace_bytes(n, T, H)) return PEAGLE_ERR_WORKSPACE;
+  Layer1Args a{(int32_t)n, K, (int32_t)T, H, num_q_heads, num_kv_heads, head_dim, eps};
+  return status_of(launch_layer1_qkv(a, hidden, embed, w_norm_emb, w_norm_hidden, w_qkv, q, k, v,
+                                     static_cast<char*>(workspace),
+                                     static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -39,6 +39,9 @@ SIGNATURES = {
     "peagle_draft_attn_prepare": (_ATTN, _i32),
     "peagle_draft_attn_core": (_ATTN, _i32),
     "peagle_accept_prefix": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _p], _i32),
+    "peagle_layer1_qkv_workspace_bytes": ([_i64, _i64, _i32], _sz),
+    "peagle_layer1_qkv": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _f32, _p, _i32, _i32, _i32, _p,
+                           _p, _p, _p, _sz, _p], _i32),
     "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
     "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32], _sz),
@@ -206,6 +209,35 @@ def accept_prefix(draft_logits, target_logits, draft_tok=None, target_tok=None, 
         N, K, V, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tok), _ptr(target_tok),
         _ptr(accept_len), _stream()))
     return draft_tok, target_tok, accept_len
+
+
+# ---------------------------------------------------------------- first draft layer
+def layer1_qkv_workspace_bytes(n: int, T: int, H: int) -> int:
+    return int(lib().peagle_layer1_qkv_workspace_bytes(n, T, H))
+
+
+def layer1_qkv(n, K, T, hidden, embed, w_norm_emb, w_norm_hidden, w_qkv, Hq, Hkv, D, eps=1e-6,
+               q=None, k=None, v=None, workspace=None):
+    """q [T, Hq, D], k and v [T, Hkv, D] (bf16, pre-RoPE) of the first draft layer from the
+    fused stage's hidden_out [T, H] (fp32) and embed_out [T, H] (bf16)."""
+    for t, name in ((hidden, "hidden"), (embed, "embed"), (w_norm_emb, "w_norm_emb"),
+                    (w_norm_hidden, "w_norm_hidden"), (w_qkv, "w_qkv")):
+        _dev(t, name)
+    H = hidden.shape[1]
+    dev = hidden.device
+    if q is None:
+        q = torch.empty((T, Hq, D), dtype=embed.dtype, device=dev)
+    if k is None:
+        k = torch.empty((T, Hkv, D), dtype=embed.dtype, device=dev)
+    if v is None:
+        v = torch.empty((T, Hkv, D), dtype=embed.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(layer1_qkv_workspace_bytes(n, T, H), dtype=torch.uint8, device=dev)
+    _check("peagle_layer1_qkv", lib().peagle_layer1_qkv(
+        n, K, T, _ptr(hidden), _ptr(embed), H, _ptr(w_norm_emb), _ptr(w_norm_hidden), float(eps),
+        _ptr(w_qkv), Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel(),
+        _stream()))
+    return q, k, v
 
 
 # ---------------------------------------------------------------- decode shape

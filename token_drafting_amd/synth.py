@@ -26,6 +26,7 @@ import numpy as np
 TAG_LENGTHS, TAG_AUX, TAG_W, TAG_MASK, TAG_EMBED, TAG_TOKENS = 1, 2, 3, 4, 5, 6
 TAG_Q, TAG_K, TAG_V, TAG_LOGITS = 7, 8, 9, 10
 TAG_CACHE_K, TAG_CACHE_V, TAG_NEW_Q, TAG_NEW_K, TAG_NEW_V = 11, 12, 13, 14, 15
+TAG_NORM_EMB, TAG_NORM_HID, TAG_WQKV, TAG_L1_HID, TAG_L1_EMB = 16, 17, 18, 19, 20
 
 VOCAB_IN = 32000          # input-embedding vocabulary of the synthetic drafter
 PLANT_VALUE_BITS = 0x4180  # bf16 bit pattern of 16.0 (exact), the planted maximum
@@ -217,3 +218,29 @@ def decode_inputs_device(seed: int, lens, K: int, Hq: int, Hkv: int, D: int, dev
                 k_cache=draw(TAG_CACHE_K, (L, Hkv, D)), v_cache=draw(TAG_CACHE_V, (L, Hkv, D)),
                 q=draw(TAG_NEW_Q, (B, K, Hq, D)), k=draw(TAG_NEW_K, (B, K, Hkv, D)),
                 v=draw(TAG_NEW_V, (B, K, Hkv, D)))
+
+
+def layer1_weights(seed: int, H: int, Hq: int, Hkv: int, D: int) -> dict:
+    """Random-init weights of the first draft layer's attention input: the two RMSNorm
+    weight vectors (bf16 of 1 + N(0, 0.1^2), near the unit init of a trained norm) and the
+    stacked q/k/v projection [(Hq + 2 Hkv) D, 2H] (bf16 of N(0, 1/(2H)), fan-in scaled:
+    unit-RMS rows in give q, k, v of unit variance, the scale of the attention's own
+    synthetic inputs)."""
+    def near_one(tag):
+        x = 1.0 + 0.1 * _rng(seed, tag).standard_normal(H, dtype=np.float32)
+        return f32_to_bf16_bits(x.astype(np.float32))
+    return dict(w_norm_emb=near_one(TAG_NORM_EMB), w_norm_hidden=near_one(TAG_NORM_HID),
+                w_qkv=normal_bf16(seed, TAG_WQKV, ((Hq + 2 * Hkv) * D, 2 * H),
+                                  std=float(1.0 / np.sqrt(2 * H))))
+
+
+def layer1_inputs(seed: int, n: int, T: int, H: int) -> dict:
+    """Stand-ins for the fused stage's outputs with their structure: hidden float32
+    [T, H] and embed bf16 [T, H] of N(0, 1), rows n .. T-1 (the depth >= 1 rows) all equal
+    to row n."""
+    hidden = _rng(seed, TAG_L1_HID).standard_normal((min(T, n + 1), H), dtype=np.float32)
+    embed = normal_bf16(seed, TAG_L1_EMB, (min(T, n + 1), H))
+    if T > n + 1:
+        hidden = np.concatenate([hidden, np.repeat(hidden[n:n + 1], T - n - 1, axis=0)])
+        embed = np.concatenate([embed, np.repeat(embed[n:n + 1], T - n - 1, axis=0)])
+    return dict(hidden=np.ascontiguousarray(hidden), embed=np.ascontiguousarray(embed))
