@@ -229,6 +229,8 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
+    result["layer1_qkv"] = layer1_bench(cfg, seed, n, K, T, hidden, emb, args.steps, args.warmup)
+
     if args.decode == "all":
         del ws, out, lse, hidden, emb, dl, tl
         torch.cuda.empty_cache()
@@ -239,6 +241,47 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, seed, qkv, cu_h, idx_h, off_h, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def layer1_bench(cfg, seed, n, K, T, hidden, emb, steps, warmup):
+    """Time peagle_layer1_qkv (RMSNorm halves and concat, QKV GEMM on rows 0..n, copy of
+    row n to the other depth >= 1 rows) on the step's own fused-stage outputs."""
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    H, Hq, Hkv, D = cfg["H"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    w = synth.layer1_weights(seed, H, Hq, Hkv, D)
+    dev = hidden.device
+    wd = {k2: torch.from_numpy(v2.view(np.int16)).to(dev) for k2, v2 in w.items()}
+    q = torch.empty((T, Hq, D), dtype=torch.int16, device=dev)
+    k = torch.empty((T, Hkv, D), dtype=torch.int16, device=dev)
+    v = torch.empty((T, Hkv, D), dtype=torch.int16, device=dev)
+    ws = torch.empty(peagle.layer1_qkv_workspace_bytes(n, T, H), dtype=torch.uint8, device=dev)
+
+    def call():
+        peagle.layer1_qkv(n, K, T, hidden, emb, wd["w_norm_emb"], wd["w_norm_hidden"], wd["w_qkv"],
+                          Hq, Hkv, D, q=q, k=k, v=v, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        call()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    M = n + 1 if T > n else n
+    N = (Hq + 2 * Hkv) * D
+    flop = 2.0 * M * N * 2 * H
+    del q, k, v, ws
+    torch.cuda.empty_cache()
+    return {"rows_projected": M, "draft_rows": T, "gemm": f"{M}x{N}x{2 * H}",
+            "ms_per_call": round(ms, 4), "gemm_flop": flop,
+            "tflops_whole_call": round(flop / (ms * 1e-3) / 1e12, 1),
+            "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "flop_saved_vs_all_rows": round(1.0 - M / T, 4)}
 
 
 def decode_bench(name, steps, warmup):
