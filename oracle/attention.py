@@ -64,20 +64,27 @@ def draft_attention(q, k, v, idx, depth_off, cu_seqlens, theta: float,
 
     q: bf16 bits [T, Hq, D]; k, v: bf16 bits [T, Hkv, D], all pre-RoPE.
     """
+    return draft_attention_f64(to_f64(q), to_f64(k), to_f64(v), idx, depth_off, cu_seqlens,
+                               theta, scale, rows, block)
+
+
+def draft_attention_f64(q, k, v, idx, depth_off, cu_seqlens, theta: float,
+                        scale: float | None = None, rows=None, block: int = 256) -> dict:
+    """The same on float64 arrays q [T, Hq, D], k and v [T, Hkv, D] (pre-RoPE)."""
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
     scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
     meta = row_meta(idx, depth_off, cu_seqlens)
     rows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
-    kr = rotate(to_f64(k), meta["pos"], theta)             # [T, Hkv, D]
-    vf = to_f64(v)
+    kr = rotate(np.asarray(k, np.float64), meta["pos"], theta)   # [T, Hkv, D]
+    vf = np.asarray(v, np.float64)
     out = np.empty((len(rows), Hq, D), dtype=np.float64)
     lse = np.empty((Hq, len(rows)), dtype=np.float64)
     for b0 in range(0, len(rows), block):
         br = rows[b0:b0 + block]
         mask = allowed_mask(meta, br)                      # [B, T]
-        qr = rotate(to_f64(q[br]), meta["pos"][br], theta)  # [B, Hq, D]
+        qr = rotate(np.asarray(q[br], np.float64), meta["pos"][br], theta)  # [B, Hq, D]
         for h in range(Hq):
             g = h // G
             s = (qr[:, h, :] @ kr[:, g, :].T) * scale       # [B, T]

@@ -1,4 +1,5 @@
-"""Attention inputs of the first draft decoder layer (oracle).
+"""The first draft decoder layer (oracle): attention inputs, attention, output projection,
+MLP and the draft-vocab head.
 
 TEST INFRASTRUCTURE ONLY (see the package header).
 
@@ -23,6 +24,16 @@ Readings (the pages name the pieces, not their formulas):
 - Every depth >= 1 row has the same x (the projected mask_hidden and the ptd embedding),
   so its q, k and v before RoPE are the same in every such row. The oracle does not use
   that: it projects every row.
+- After the attention (module ``attention``), the layer is a Llama decoder layer's second
+  half: h1 = r + o W_o^T with o the attention output flattened over heads; h2 = h1 +
+  W_down (silu(W_gate m) * (W_up m)) with m = rms(h1; w_post) (SwiGLU MLP, bias-free).
+- The residual r: the speculators guide ("Key Parameters") lists a flag that disables
+  normalization before the residual connection, so by default the residual stream starts
+  from the normalised hidden state, r = rms(hidden; w_hidden); with the flag off it is the
+  raw hidden state.
+- The draft-vocab head: logits = rms(h2; w_final) W_head^T (NeMo PR 2376: the P-EAGLE
+  trainer shares EAGLE-3's draft-vocab projection); the draft token of a row is its
+  argmax, lowest index on ties.
 """
 from __future__ import annotations
 
@@ -59,3 +70,50 @@ def layer1_qkv(hidden_f32, embed_bf16, w_emb_bf16, w_hidden_bf16, w_qkv_bf16, Hq
     return layer1_qkv_f64(np.asarray(hidden_f32, np.float64), to_f64(embed_bf16),
                           to_f64(w_emb_bf16), to_f64(w_hidden_bf16), to_f64(w_qkv_bf16), Hq, Hkv,
                           D, eps)
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def post_attention_f64(attn_out, resid, w_o, w_post, w_gate, w_up, w_down,
+                       eps: float = EPS) -> dict:
+    """attn_out [T, Hq, D]; resid [T, H]; w_o [H, Hq D]; w_post [H]; w_gate, w_up [I, H];
+    w_down [H, I]. Returns h1 (after the attention residual) and h2 (after the MLP's)."""
+    a = np.asarray(attn_out, np.float64)
+    h1 = np.asarray(resid, np.float64) + a.reshape(a.shape[0], -1) @ np.asarray(w_o, np.float64).T
+    m = rms_norm(h1, w_post, eps)
+    g = m @ np.asarray(w_gate, np.float64).T
+    u = m @ np.asarray(w_up, np.float64).T
+    h2 = h1 + (silu(g) * u) @ np.asarray(w_down, np.float64).T
+    return dict(h1=h1, h2=h2)
+
+
+def draft_head_f64(h2, w_final, w_head, eps: float = EPS) -> dict:
+    """logits [T, V] = rms(h2; w_final) W_head^T and the argmax token of each row (lowest
+    index on ties)."""
+    logits = rms_norm(h2, w_final, eps) @ np.asarray(w_head, np.float64).T
+    return dict(logits=logits, tokens=np.argmax(logits, axis=-1).astype(np.int32))
+
+
+def layer1_forward_f64(hidden, embed, w: dict, idx, depth_off, cu_seqlens, theta: float,
+                       Hq: int, Hkv: int, D: int, eps: float = EPS,
+                       norm_before_residual: bool = True, rows=None) -> dict:
+    """The whole first layer on float64 arrays: hidden, embed [T, H] of the draft rows;
+    w holds w_norm_emb, w_norm_hidden, w_qkv, w_o, w_post, w_gate, w_up, w_down, w_final,
+    w_head. rows: optional subset of draft rows whose outputs are wanted (the attention
+    still sees every key row)."""
+    from .attention import draft_attention_f64
+
+    qkv = layer1_qkv_f64(hidden, embed, w["w_norm_emb"], w["w_norm_hidden"], w["w_qkv"], Hq, Hkv,
+                         D, eps)
+    att = draft_attention_f64(qkv["q"], qkv["k"], qkv["v"], idx, depth_off, cu_seqlens, theta,
+                              rows=rows)
+    sel = np.arange(len(hidden)) if rows is None else np.asarray(rows)
+    resid = rms_norm(hidden[sel], w["w_norm_hidden"], eps) if norm_before_residual else \
+        np.asarray(hidden, np.float64)[sel]
+    post = post_attention_f64(att["out"], resid, w["w_o"], w["w_post"], w["w_gate"], w["w_up"],
+                              w["w_down"], eps)
+    head = draft_head_f64(post["h2"], w["w_final"], w["w_head"], eps)
+    return dict(q=qkv["q"], k=qkv["k"], v=qkv["v"], attn=att["out"], h1=post["h1"],
+                h2=post["h2"], logits=head["logits"], tokens=head["tokens"])

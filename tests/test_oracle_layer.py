@@ -77,3 +77,109 @@ def test_identical_inputs_give_identical_rows():
     out = layer.layer1_qkv_f64(hid, emb, np.ones(H), np.ones(H), w_qkv, Hq, Hkv, D)
     for key in ("q", "k", "v"):
         assert np.array_equal(out[key][n:], np.broadcast_to(out[key][n], out[key][n:].shape))
+
+
+def _llama_layer(H, I, Hq, Hkv, D, theta, eps, w):
+    """transformers' Llama decoder layer (float64, eager attention) carrying the hidden
+    half of the oracle's weights."""
+    from transformers import LlamaConfig
+    from transformers.models.llama import modeling_llama as m
+    cfg = LlamaConfig(hidden_size=H, intermediate_size=I, num_attention_heads=Hq,
+                      num_key_value_heads=Hkv, head_dim=D, rms_norm_eps=eps,
+                      attention_bias=False, mlp_bias=False,
+                      rope_parameters={"rope_type": "default", "rope_theta": theta})
+    cfg._attn_implementation = "eager"
+    lay = m.LlamaDecoderLayer(cfg, layer_idx=0).double()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    qd, kd = Hq * D, Hkv * D
+    with torch.no_grad():
+        lay.input_layernorm.weight.copy_(t(w["w_norm_hidden"]))
+        lay.self_attn.q_proj.weight.copy_(t(w["w_qkv"][:qd, H:]))
+        lay.self_attn.k_proj.weight.copy_(t(w["w_qkv"][qd:qd + kd, H:]))
+        lay.self_attn.v_proj.weight.copy_(t(w["w_qkv"][qd + kd:, H:]))
+        lay.self_attn.o_proj.weight.copy_(t(w["w_o"]))
+        lay.post_attention_layernorm.weight.copy_(t(w["w_post"]))
+        lay.mlp.gate_proj.weight.copy_(t(w["w_gate"]))
+        lay.mlp.up_proj.weight.copy_(t(w["w_up"]))
+        lay.mlp.down_proj.weight.copy_(t(w["w_down"]))
+    return lay, m.LlamaRotaryEmbedding(cfg)
+
+
+def _weights(rng, H, I, Hq, Hkv, D, V, zero_emb_half=False):
+    w = dict(w_norm_emb=1 + 0.1 * rng.standard_normal(H), w_norm_hidden=1 + 0.1 * rng.standard_normal(H),
+             w_qkv=rng.standard_normal(((Hq + 2 * Hkv) * D, 2 * H)) / np.sqrt(2 * H),
+             w_o=rng.standard_normal((H, Hq * D)) / np.sqrt(Hq * D),
+             w_post=1 + 0.1 * rng.standard_normal(H),
+             w_gate=rng.standard_normal((I, H)) / np.sqrt(H), w_up=rng.standard_normal((I, H)) / np.sqrt(H),
+             w_down=rng.standard_normal((H, I)) / np.sqrt(I),
+             w_final=1 + 0.1 * rng.standard_normal(H), w_head=rng.standard_normal((V, H)) / np.sqrt(H))
+    if zero_emb_half:
+        w["w_qkv"][:, :H] = 0.0
+    return w
+
+
+@pytest.mark.parametrize("n,H,I,Hq,Hkv,D,theta", [(9, 32, 48, 4, 2, 8, 1e4), (40, 64, 96, 4, 1, 16, 5e5)])
+def test_layer_matches_llama_decoder_layer(n, H, I, Hq, Hkv, D, theta):
+    """K = 1 (plain causal attention over one sequence), the embedding half of W_qkv zero and
+    the residual on the raw hidden state: the first draft layer is a Llama decoder layer
+    applied to the hidden state."""
+    rng = np.random.default_rng(n)
+    w = _weights(rng, H, I, Hq, Hkv, D, V=11, zero_emb_half=True)
+    hidden, embed = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    idx, depth_off, cu = np.arange(n), np.array([0, n]), np.array([0, n])
+    got = layer.layer1_forward_f64(hidden, embed, w, idx, depth_off, cu, theta, Hq, Hkv, D,
+                                   eps=1e-6, norm_before_residual=False)
+    lay, rot = _llama_layer(H, I, Hq, Hkv, D, theta, 1e-6, w)
+    x = torch.from_numpy(hidden)[None]
+    pos = torch.arange(n)[None]
+    mask = torch.triu(torch.full((n, n), float("-inf"), dtype=torch.float64), 1)[None, None]
+    with torch.no_grad():
+        want = lay(x, attention_mask=mask, position_ids=pos, position_embeddings=rot(x, pos))[0].numpy()
+    np.testing.assert_allclose(got["h2"], want, rtol=0, atol=2e-6 * np.abs(want).max())
+
+
+def test_mlp_matches_llama_mlp_and_residual_modes():
+    from transformers import LlamaConfig
+    from transformers.models.llama import modeling_llama as m
+    rng = np.random.default_rng(4)
+    T, H, I, Hq, D = 6, 16, 40, 2, 8
+    w = _weights(rng, H, I, Hq, 1, D, V=5)
+    attn = rng.standard_normal((T, Hq, D))
+    hidden = rng.standard_normal((T, H))
+    post = layer.post_attention_f64(attn, hidden, w["w_o"], w["w_post"], w["w_gate"], w["w_up"],
+                                    w["w_down"])
+    mlp = m.LlamaMLP(LlamaConfig(hidden_size=H, intermediate_size=I, mlp_bias=False,
+                                 num_attention_heads=Hq, num_key_value_heads=1)).double()
+    with torch.no_grad():
+        mlp.gate_proj.weight.copy_(torch.from_numpy(w["w_gate"]))
+        mlp.up_proj.weight.copy_(torch.from_numpy(w["w_up"]))
+        mlp.down_proj.weight.copy_(torch.from_numpy(w["w_down"]))
+        m_in = _llama_rms(post["h1"], w["w_post"], 1e-6)
+        want = post["h1"] + mlp(torch.from_numpy(m_in)).numpy()
+    np.testing.assert_allclose(post["h2"], want, rtol=1e-5, atol=1e-6)
+    # the two residual readings differ by exactly rms(hidden) - hidden in h1
+    idx, depth_off, cu = np.arange(T), np.array([0, T]), np.array([0, T])
+    emb = rng.standard_normal((T, H))
+    w2 = _weights(rng, H, I, Hq, 1, D, V=5)
+    a = layer.layer1_forward_f64(hidden, emb, w2, idx, depth_off, cu, 1e4, Hq, 1, D,
+                                 norm_before_residual=True)
+    b = layer.layer1_forward_f64(hidden, emb, w2, idx, depth_off, cu, 1e4, Hq, 1, D,
+                                 norm_before_residual=False)
+    np.testing.assert_allclose(a["h1"] - b["h1"], _llama_rms(hidden, w2["w_norm_hidden"], 1e-6) - hidden,
+                               rtol=1e-5, atol=1e-6)
+
+
+def test_head_argmax_lowest_index_on_ties():
+    rng = np.random.default_rng(6)
+    T, H, V = 5, 8, 7
+    h2 = rng.standard_normal((T, H))
+    w_final = np.ones(H)
+    w_head = np.zeros((V, H))
+    # rows of W_head equal to a unit vector e_j give logits rms(h2)_j; tokens 2 and 5 tie
+    w_head[2, 3] = w_head[5, 3] = 1.0
+    w_head[4, 1] = 1.0
+    out = layer.draft_head_f64(h2, w_final, w_head, eps=1e-6)
+    nh = _llama_rms(h2, w_final, 1e-6)
+    want = np.where(nh[:, 3] >= np.maximum(nh[:, 1], 0.0), 2, np.where(nh[:, 1] > 0.0, 4, 0))
+    np.testing.assert_allclose(out["logits"][:, 2], nh[:, 3], rtol=2e-6)
+    assert np.array_equal(out["tokens"], want)
