@@ -220,6 +220,50 @@ int peagle_layer1_qkv(int64_t n, int32_t K, int64_t T, const float *hidden,
                       size_t workspace_bytes, void *stream);
 
 /*
+ * The rest of the first draft layer [G, "Architecture": Llama-style decoder layers; G,
+ * "Key Parameters": normalization before the residual connection unless disabled].
+ * Per draft row, with o the attention output (heads flattened, width QW = Hq D):
+ *   r  = norm_before_residual ? rms(hidden) * w_norm_hidden : hidden
+ *   h1 = r + o W_o^T
+ *   h2 = h1 + W_down (silu(W_gate m) * (W_up m)),  m = rms(h1) * w_post
+ *   attn_out       fp32[T, QW]        from peagle_draft_attn_fwd (out)
+ *   hidden         fp32[T, H]         from peagle_fuse_inputs (hidden_out)
+ *   w_norm_hidden  bf16[H]            as for peagle_layer1_qkv (read if norm_before_residual)
+ *   w_o            bf16[H, QW];  w_post bf16[H]
+ *   w_gate, w_up   bf16[I, H];   w_down bf16[H, I]
+ *   h2_out         fp32[T, H]   out
+ *   workspace      >= peagle_layer1_post_workspace_bytes(n, T, H, QW, I), 256-byte aligned
+ * H, QW and I multiples of 64 (else PEAGLE_ERR_UNSUPPORTED). Every product is a bf16 MFMA
+ * GEMM with fp32 accumulation on operands rounded to bf16; h1 and h2 stay fp32.
+ */
+size_t peagle_layer1_post_workspace_bytes(int64_t n, int64_t T, int32_t H, int32_t QW,
+                                          int32_t I);
+int peagle_layer1_post(int64_t n, int32_t K, int64_t T, const float *attn_out, int32_t QW,
+                       const float *hidden, int32_t H, const peagle_bf16 *w_norm_hidden,
+                       int32_t norm_before_residual, const peagle_bf16 *w_o,
+                       const peagle_bf16 *w_post, const peagle_bf16 *w_gate,
+                       const peagle_bf16 *w_up, int32_t I, const peagle_bf16 *w_down, float eps,
+                       float *h2_out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * peagle_draft_head -- the draft-vocab head and its argmax [N, description: the P-EAGLE
+ * trainer shares EAGLE-3's draft-vocab projection]:
+ *   token[r] = argmax_v (rms(h[r]) * w_final) . w_head[v]   (lowest v on ties)
+ *   h        fp32[T, H]   (e.g. h2_out of peagle_layer1_post)
+ *   w_final  bf16[H];  w_head bf16[V, H]
+ *   tokens   int32[T]   out
+ *   workspace >= peagle_draft_head_workspace_bytes(T, H, V), 256-byte aligned
+ * The logits are reduced inside the projection (per row and 64 columns) and never stored.
+ * H a multiple of 64 (else PEAGLE_ERR_UNSUPPORTED); V >= 1. The argmax is taken on fp32
+ * logits of bf16 operands: rows whose top two logits are closer than that rounding may
+ * pick either.
+ */
+size_t peagle_draft_head_workspace_bytes(int64_t T, int32_t H, int32_t V);
+int peagle_draft_head(int64_t T, const float *h, int32_t H, const peagle_bf16 *w_final,
+                      const peagle_bf16 *w_head, int32_t V, float eps, int32_t *tokens,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Draft attention at inference (the decode shape) [N, parity section: at inference one
  * flat parallel forward over [context, mask_1, ..., mask_{K-1}]; G, "Inference Process":
  * all depths drafted in one pass, drafting repeats from the last accepted token].

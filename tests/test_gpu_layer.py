@@ -123,3 +123,113 @@ def test_fuse_layer1_attention_chain(pe):
     # and 4.0e-3 relative L2.
     assert_close(to_host(out), want["out"], "chained attention out", max_abs=3e-2,
                  max_rel_l2=1e-2)
+
+
+# ---------------------------------------------------------------- rest of the layer, head
+# The argmax is taken on logits of bf16 operands: where the oracle's top two logits are
+# closer than HEAD_TIE (4x the largest logit error a float64 emulation of the GPU's rounding
+# shows, 7e-3) either token is correct, and the GPU's must score within HEAD_TIE of the
+# best; elsewhere it must be the oracle's.
+HEAD_TIE = 3e-2
+
+
+def check_tokens(got, logits, what, tie=HEAD_TIE):
+    top = np.argmax(logits, axis=1)
+    srt = np.sort(logits, axis=1)
+    clear = (srt[:, -1] - srt[:, -2]) > tie
+    assert np.array_equal(got[clear], top[clear]), f"{what}: {int((got[clear] != top[clear]).sum())} tokens differ"
+    score = logits[np.arange(len(got)), got]
+    assert (score >= srt[:, -1] - tie).all(), f"{what}: a near-tie token scores too low"
+    return int(clear.sum())
+
+
+def _post_case(pe, n, K, T, H, QW, I, V, seed, norm, rows=None):
+    inp = synth.layer1_inputs(seed, n, T, H)
+    att = synth.attention_out_standin(seed, T, QW)
+    w = synth.layer1_post_weights(seed, H, QW, I, V)
+    wl = synth.layer1_weights(seed, H, 4, 1, 64)
+    d = {k: to_dev(v) for k, v in w.items()}
+    h2 = pe.layer1_post(n, K, T, to_dev(att), to_dev(inp["hidden"]), to_dev(wl["w_norm_hidden"]),
+                        d["w_o"], d["w_post"], d["w_gate"], d["w_up"], d["w_down"],
+                        norm_before_residual=norm)
+    tok = pe.draft_head(h2, d["w_final"], d["w_head"])
+    rows = np.arange(T) if rows is None else rows
+    hid = inp["hidden"][rows]
+    resid = olayer.rms_norm(hid, synth_bf16(wl["w_norm_hidden"])) if norm else hid.astype(np.float64)
+    wf = {k: synth_bf16(v) for k, v in w.items()}
+    want = olayer.post_attention_f64(att[rows], resid, wf["w_o"], wf["w_post"], wf["w_gate"],
+                                     wf["w_up"], wf["w_down"])
+    head = olayer.draft_head_f64(want["h2"], wf["w_final"], wf["w_head"])
+    return to_host(h2)[rows], to_host(tok)[rows], want, head
+
+
+POST_SMALL = [
+    # (n, K, H, QW, I, V, norm_before_residual)
+    (300, 4, 640, 1024, 2048, 8192, True),     # Gemma-270M-shaped, draft vocab 8192
+    (300, 4, 640, 1024, 2048, 8192, False),
+    (129, 1, 128, 192, 320, 1000, True),       # K = 1; 2/3/5 k-steps; V not a multiple of 64
+    (77, 8, 256, 256, 512, 64, False),         # V = 64: the last tile's second wave has no column
+    (5, 4, 64, 64, 64, 130, True),             # smallest sizes
+]
+
+
+@pytest.mark.parametrize("case", POST_SMALL, ids=[f"n{c[0]}K{c[1]}H{c[2]}QW{c[3]}I{c[4]}V{c[5]}{'n' if c[6] else 'r'}"
+                                                  for c in POST_SMALL])
+def test_layer1_post_and_head_small_full(pe, case):
+    n, K, H, QW, I, V, norm = case
+    T = int(sum(ocod.retained_counts(n, K, 0.7, 0.2)))
+    print(f"post+head n={n} T={T} H={H} QW={QW} I={I} V={V} norm={norm}", flush=True)
+    h2, tok, want, head = _post_case(pe, n, K, T, H, QW, I, V, seed=n + I, norm=norm)
+    assert_close_bf16_out(h2, want["h2"], "h2")
+    check_tokens(tok, head["logits"], "tokens")
+
+
+@pytest.mark.parametrize("cfg_id", [4, 5])
+def test_layer1_post_and_head_full_size_sampled(pe, cfg_id):
+    cfg = synth.CONFIGS[cfg_id]
+    n, K, H = cfg["n"], cfg["K"], cfg["H"]
+    QW, I = cfg["Hq"] * cfg["D"], synth.LAYER_SHAPES[cfg_id]["I"]
+    T = int(sum(ocod.retained_counts(n, K, cfg["r"], cfg["r_min"])))
+    rng = np.random.default_rng(cfg_id)
+    rows = np.unique(np.concatenate([[0, n - 1, n, T - 1], rng.integers(0, T, 60)]))
+    print(f"post+head config {cfg_id}: T={T} H={H} QW={QW} I={I}, {len(rows)} rows", flush=True)
+    h2, tok, want, head = _post_case(pe, n, K, T, H, QW, I, synth.DRAFT_VOCAB, seed=cfg_id,
+                                     norm=True, rows=rows)
+    assert_close_bf16_out(h2, want["h2"], f"h2 cfg{cfg_id}")
+    check_tokens(tok, head["logits"], f"tokens cfg{cfg_id}")
+
+
+def test_whole_first_layer_chain(pe):
+    """COD -> fused inputs -> q/k/v -> attention -> rest of the layer -> head on the GPU,
+    against the whole-layer oracle fed the fused oracle's outputs: h2 held to the sum of the
+    stages' bars (attention chain 3e-2 + bf16 projections 2e-2), tokens as above."""
+    cfg = dict(synth.CONFIGS[1])
+    n, K, Hq, Hkv, D, H = cfg["n"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["H"]
+    QW, I, V, seed = Hq * D, 512, 1024, 23
+    base = synth.base_inputs(cfg, seed)
+    cu = base["cu_seqlens"]
+    w = synth.layer1_weights(seed, H, Hq, Hkv, D)
+    wp = synth.layer1_post_weights(seed, H, QW, I, V)
+    dw = {k: to_dev(v) for k, v in {**w, **wp}.items()}
+    dcu = to_dev(cu)
+    sel = pe.cod_select(n, K, cfg["r"], cfg["r_min"], seed, dcu)
+    T = sel["T"]
+    hid, emb = pe.fuse_inputs(n, K, T, sel["idx"], to_dev(base["aux"]), to_dev(base["fc_weight"]),
+                              to_dev(base["mask_hidden"]), to_dev(base["tokens"]),
+                              to_dev(base["embed"]), base["ptd_token_id"])
+    q, k, v = pe.layer1_qkv(n, K, T, hid, emb, dw["w_norm_emb"], dw["w_norm_hidden"], dw["w_qkv"],
+                            Hq, Hkv, D)
+    cos, sin = pe.rope_table(D, cfg["theta"], pe.rope_max_pos(n, K))
+    out, _, _ = pe.draft_attn(n, K, sel, dcu, q, k, v, cos, sin)
+    h2 = pe.layer1_post(n, K, T, out, hid, dw["w_norm_hidden"], dw["w_o"], dw["w_post"],
+                        dw["w_gate"], dw["w_up"], dw["w_down"])
+    tok = pe.draft_head(h2, dw["w_final"], dw["w_head"])
+    osel = ocod.cod_select(n, K, cfg["r"], cfg["r_min"], seed, cu)
+    f = ofuse.fuse_inputs(base["aux"], base["fc_weight"], base["mask_hidden"], base["tokens"],
+                          base["embed"], base["ptd_token_id"], osel["idx"], osel["depth_off"])
+    wf = {k2: synth_bf16(v2) for k2, v2 in {**w, **wp}.items()}
+    want = olayer.layer1_forward_f64(f["hidden"], synth_bf16(f["embed_rows"]), wf, osel["idx"],
+                                     osel["depth_off"], cu, cfg["theta"], Hq, Hkv, D)
+    assert_close_bf16_out(to_host(h2), want["h2"], "chained h2", max_abs=5e-2, max_rel_l2=1.5e-2)
+    # the logits inherit h2's chain error (up to ~5e-2 of unit-scale values): wider tie window
+    check_tokens(to_host(tok), want["logits"], "chained tokens", tie=0.1)

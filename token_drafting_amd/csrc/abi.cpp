@@ -336,4 +336,59 @@ int peagle_layer1_qkv(int64_t n, int32_t K, int64_t T, const float* hidden,
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t peagle_layer1_post_workspace_bytes(int64_t n, int64_t T, int32_t H, int32_t QW,
+                                          int32_t I) {
+  if (n < 1 || T < n || T > kMaxI32 || H < 1 || QW < 1 || I < 1) return 0;
+  return layer1_post_workspace_bytes(n, T, H, QW, I);
+}
+
+int peagle_layer1_post(int64_t n, int32_t K, int64_t T, const float* attn_out, int32_t QW,
+                       const float* hidden, int32_t H, const peagle_bf16* w_norm_hidden,
+                       int32_t norm_before_residual, const peagle_bf16* w_o,
+                       const peagle_bf16* w_post, const peagle_bf16* w_gate,
+                       const peagle_bf16* w_up, int32_t I, const peagle_bf16* w_down, float eps,
+                       float* h2_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 1 || n > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return PEAGLE_ERR_ARG;
+  if (T < n || T > (int64_t)K * n || T > kMaxI32) return PEAGLE_ERR_ARG;
+  if (H < 1 || QW < 1 || I < 1) return PEAGLE_ERR_ARG;
+  if (H % 64 != 0 || QW % 64 != 0 || I % 64 != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if ((int64_t)2 * I > kMaxI32 || (int64_t)T * (QW > H ? QW : H) > ((int64_t)1 << 40))
+    return PEAGLE_ERR_ARG;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return PEAGLE_ERR_ARG;
+  if (!attn_out || !hidden || (norm_before_residual && !w_norm_hidden) || !w_o || !w_post ||
+      !w_gate || !w_up || !w_down || !h2_out || !workspace)
+    return PEAGLE_ERR_ARG;
+  if (!aligned16(attn_out) || !aligned16(hidden) ||
+      (norm_before_residual && !aligned16(w_norm_hidden)) || !aligned16(w_o) ||
+      !aligned16(w_post) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+      !aligned16(h2_out) || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return PEAGLE_ERR_ARG;
+  if (workspace_bytes < layer1_post_workspace_bytes(n, T, H, QW, I)) return PEAGLE_ERR_WORKSPACE;
+  Layer1PostArgs a{(int32_t)n, (int32_t)T, H, QW, I, norm_before_residual ? 1 : 0, eps};
+  return status_of(launch_layer1_post(a, attn_out, hidden, w_norm_hidden, w_o, w_post, w_gate,
+                                      w_up, w_down, h2_out, static_cast<char*>(workspace),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t peagle_draft_head_workspace_bytes(int64_t T, int32_t H, int32_t V) {
+  if (T < 1 || T > kMaxI32 || H < 1 || V < 1) return 0;
+  return draft_head_workspace_bytes(T, H, V);
+}
+
+int peagle_draft_head(int64_t T, const float* h, int32_t H, const peagle_bf16* w_final,
+                      const peagle_bf16* w_head, int32_t V, float eps, int32_t* tokens,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 1 || T > kMaxI32 || H < 1 || V < 1) return PEAGLE_ERR_ARG;
+  if (H % 64 != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return PEAGLE_ERR_ARG;
+  if (!h || !w_final || !w_head || !tokens || !workspace) return PEAGLE_ERR_ARG;
+  if (!aligned16(h) || !aligned16(w_final) || !aligned16(w_head) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return PEAGLE_ERR_ARG;
+  if (workspace_bytes < draft_head_workspace_bytes(T, H, V)) return PEAGLE_ERR_WORKSPACE;
+  return status_of(launch_draft_head(T, H, V, eps, h, w_final, w_head, tokens,
+                                     static_cast<char*>(workspace),
+                                     static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -167,22 +167,33 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
     if (ks + 1 < nk) step(ks + 1, As1, Bs1, As0, Bs0);
   }
 
+  if constexpr (Epi::kWaveTile) {
+    // an epilogue that combines lanes gets the wave's whole 128x64 tile, all lanes active
+    epi.wave_tile(acc, m0 + wm * 128, n0 + wn * 64, lane, M, N);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + r32;
-      if (col >= N) continue;
+      for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 64 + j * 32 + r32;
+        if (col >= N) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < M) epi(row, col, acc[i][j][r]);
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < M) epi(row, col, acc[i][j][r]);
+        }
       }
-    }
+  }
 }
+
+// Epilogues are called per element (row, col, value) inside [M) x [N), or, with
+// kWaveTile, once per wave with the wave's accumulators: acc[i][j] is the 32x32 MFMA tile
+// at rows row0 + 32 i, columns col0 + 32 j; lane l holds column l % 32 of it, rows
+// 8 (r / 4) + 4 (l / 32) + r % 4 in register r.
 
 // fp32 row-major store.
 struct StoreF32 {
+  static constexpr bool kWaveTile = false;
   float* C;
   int N;
   __device__ __forceinline__ void operator()(int row, int col, float v) const {

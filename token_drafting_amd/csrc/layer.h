@@ -20,4 +20,22 @@ hipError_t launch_layer1_qkv(const Layer1Args& a, const float* hidden, const uin
                              const uint16_t* w_emb, const uint16_t* w_hid, const uint16_t* w_qkv,
                              uint16_t* q, uint16_t* k, uint16_t* v, char* ws, hipStream_t stream);
 
+// Second half of the first layer: output projection and residual, RMSNorm, SwiGLU MLP and
+// residual. QW = Hq * D (width of the attention output), I = intermediate size.
+struct Layer1PostArgs {
+  int32_t n, T, H, QW, I, norm_before_residual;
+  float eps;
+};
+size_t layer1_post_workspace_bytes(int64_t n, int64_t T, int32_t H, int32_t QW, int32_t I);
+hipError_t launch_layer1_post(const Layer1PostArgs& a, const float* attn, const float* hidden,
+                              const uint16_t* w_hid, const uint16_t* w_o, const uint16_t* w_post,
+                              const uint16_t* w_gate, const uint16_t* w_up,
+                              const uint16_t* w_down, float* h2, char* ws, hipStream_t stream);
+
+// Draft-vocab head: final RMSNorm, projection to V logits, argmax per row (fused).
+size_t draft_head_workspace_bytes(int64_t T, int32_t H, int32_t V);
+hipError_t launch_draft_head(int64_t T, int32_t H, int32_t V, float eps, const float* h,
+                             const uint16_t* w_final, const uint16_t* w_head, int32_t* tokens,
+                             char* ws, hipStream_t stream);
+
 }  // namespace peagle

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void layer1_norm_kernel(const float* __restric
 
 // Column c of the projection goes to q (c < nq), k (next nk) or v (last nk), bf16.
 struct StoreQKV {
+  static constexpr bool kWaveTile = false;
   uint16_t* q;
   uint16_t* k;
   uint16_t* v;

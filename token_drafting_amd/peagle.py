@@ -42,6 +42,11 @@ SIGNATURES = {
     "peagle_layer1_qkv_workspace_bytes": ([_i64, _i64, _i32], _sz),
     "peagle_layer1_qkv": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _f32, _p, _i32, _i32, _i32, _p,
                            _p, _p, _p, _sz, _p], _i32),
+    "peagle_layer1_post_workspace_bytes": ([_i64, _i64, _i32, _i32, _i32], _sz),
+    "peagle_layer1_post": ([_i64, _i32, _i64, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p, _p, _i32,
+                            _p, _f32, _p, _p, _sz, _p], _i32),
+    "peagle_draft_head_workspace_bytes": ([_i64, _i32, _i32], _sz),
+    "peagle_draft_head": ([_i64, _p, _i32, _p, _p, _i32, _f32, _p, _p, _sz, _p], _i32),
     "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
     "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32], _sz),
@@ -238,6 +243,47 @@ def layer1_qkv(n, K, T, hidden, embed, w_norm_emb, w_norm_hidden, w_qkv, Hq, Hkv
         _ptr(w_qkv), Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel(),
         _stream()))
     return q, k, v
+
+
+def layer1_post(n, K, T, attn_out, hidden, w_norm_hidden, w_o, w_post, w_gate, w_up, w_down,
+                eps=1e-6, norm_before_residual=True, h2=None, workspace=None):
+    """h2 [T, H] (fp32) of the first draft layer from the attention output [T, Hq, D] or
+    [T, Hq*D] (fp32) and the fused stage's hidden_out [T, H]."""
+    for t, name in ((attn_out, "attn_out"), (hidden, "hidden"), (w_o, "w_o"), (w_post, "w_post"),
+                    (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _dev(t, name)
+    H = hidden.shape[1]
+    QW = attn_out.numel() // T
+    I = w_gate.shape[0]
+    dev = hidden.device
+    if h2 is None:
+        h2 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().peagle_layer1_post_workspace_bytes(n, T, H, QW, I)),
+                                dtype=torch.uint8, device=dev)
+    _check("peagle_layer1_post", lib().peagle_layer1_post(
+        n, K, T, _ptr(attn_out), QW, _ptr(hidden), H, _ptr(w_norm_hidden),
+        1 if norm_before_residual else 0, _ptr(w_o), _ptr(w_post), _ptr(w_gate), _ptr(w_up), I,
+        _ptr(w_down), float(eps), _ptr(h2), _ptr(workspace), workspace.numel(), _stream()))
+    return h2
+
+
+def draft_head(h, w_final, w_head, eps=1e-6, tokens=None, workspace=None):
+    """Argmax draft token [T] (int32) of rms(h) * w_final projected by w_head [V, H]."""
+    for t, name in ((h, "h"), (w_final, "w_final"), (w_head, "w_head")):
+        _dev(t, name)
+    T, H = h.shape
+    V = w_head.shape[0]
+    dev = h.device
+    if tokens is None:
+        tokens = torch.empty(T, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().peagle_draft_head_workspace_bytes(T, H, V)),
+                                dtype=torch.uint8, device=dev)
+    _check("peagle_draft_head", lib().peagle_draft_head(
+        T, _ptr(h), H, _ptr(w_final), _ptr(w_head), V, float(eps), _ptr(tokens), _ptr(workspace),
+        workspace.numel(), _stream()))
+    return tokens
 
 
 # ---------------------------------------------------------------- decode shape

@@ -27,6 +27,13 @@ TAG_LENGTHS, TAG_AUX, TAG_W, TAG_MASK, TAG_EMBED, TAG_TOKENS = 1, 2, 3, 4, 5, 6
 TAG_Q, TAG_K, TAG_V, TAG_LOGITS = 7, 8, 9, 10
 TAG_CACHE_K, TAG_CACHE_V, TAG_NEW_Q, TAG_NEW_K, TAG_NEW_V = 11, 12, 13, 14, 15
 TAG_NORM_EMB, TAG_NORM_HID, TAG_WQKV, TAG_L1_HID, TAG_L1_EMB = 16, 17, 18, 19, 20
+TAG_WO, TAG_NORM_POST, TAG_WGATE, TAG_WUP, TAG_WDOWN, TAG_NORM_FINAL, TAG_WHEAD, TAG_ATTN = (
+    21, 22, 23, 24, 25, 26, 27, 28)
+
+# Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
+# layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
+LAYER_SHAPES = {2: dict(I=2048), 4: dict(I=2048), 3: dict(I=14336), 5: dict(I=14336)}
+DRAFT_VOCAB = 8192
 
 VOCAB_IN = 32000          # input-embedding vocabulary of the synthetic drafter
 PLANT_VALUE_BITS = 0x4180  # bf16 bit pattern of 16.0 (exact), the planted maximum
@@ -244,3 +251,25 @@ def layer1_inputs(seed: int, n: int, T: int, H: int) -> dict:
         hidden = np.concatenate([hidden, np.repeat(hidden[n:n + 1], T - n - 1, axis=0)])
         embed = np.concatenate([embed, np.repeat(embed[n:n + 1], T - n - 1, axis=0)])
     return dict(hidden=np.ascontiguousarray(hidden), embed=np.ascontiguousarray(embed))
+
+
+def layer1_post_weights(seed: int, H: int, QW: int, I: int, V: int = DRAFT_VOCAB) -> dict:
+    """Random-init weights of the rest of the first layer and the draft head: RMSNorm
+    weights bf16 of 1 + N(0, 0.1^2); projections bf16 of N(0, 1/fan_in) (W_o [H, QW],
+    W_gate and W_up [I, H], W_down [H, I], W_head [V, H])."""
+    def near_one(tag):
+        x = 1.0 + 0.1 * _rng(seed, tag).standard_normal(H, dtype=np.float32)
+        return f32_to_bf16_bits(x.astype(np.float32))
+    return dict(w_o=normal_bf16(seed, TAG_WO, (H, QW), std=float(1 / np.sqrt(QW))),
+                w_post=near_one(TAG_NORM_POST),
+                w_gate=normal_bf16(seed, TAG_WGATE, (I, H), std=float(1 / np.sqrt(H))),
+                w_up=normal_bf16(seed, TAG_WUP, (I, H), std=float(1 / np.sqrt(H))),
+                w_down=normal_bf16(seed, TAG_WDOWN, (H, I), std=float(1 / np.sqrt(I))),
+                w_final=near_one(TAG_NORM_FINAL),
+                w_head=normal_bf16(seed, TAG_WHEAD, (V, H), std=float(1 / np.sqrt(H))))
+
+
+def attention_out_standin(seed: int, T: int, QW: int) -> np.ndarray:
+    """A stand-in for the attention output [T, QW] (float32): softmax-weighted averages of
+    N(0, 1) values have magnitudes below 1; drawn as N(0, 0.3^2)."""
+    return (0.3 * _rng(seed, TAG_ATTN).standard_normal((T, QW), dtype=np.float32)).astype(np.float32)
