@@ -229,7 +229,8 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
-    result["layer1_qkv"] = layer1_bench(cfg, seed, n, K, T, hidden, emb, args.steps, args.warmup)
+    result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, hidden, emb, out,
+                                        args.steps, args.warmup)
 
     if args.decode == "all":
         del ws, out, lse, hidden, emb, dl, tl
@@ -243,25 +244,8 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def layer1_bench(cfg, seed, n, K, T, hidden, emb, steps, warmup):
-    """Time peagle_layer1_qkv (RMSNorm halves and concat, QKV GEMM on rows 0..n, copy of
-    row n to the other depth >= 1 rows) on the step's own fused-stage outputs."""
+def _time_calls(call, steps, warmup):
     import torch
-    from token_drafting_amd import peagle, synth
-
-    H, Hq, Hkv, D = cfg["H"], cfg["Hq"], cfg["Hkv"], cfg["D"]
-    w = synth.layer1_weights(seed, H, Hq, Hkv, D)
-    dev = hidden.device
-    wd = {k2: torch.from_numpy(v2.view(np.int16)).to(dev) for k2, v2 in w.items()}
-    q = torch.empty((T, Hq, D), dtype=torch.int16, device=dev)
-    k = torch.empty((T, Hkv, D), dtype=torch.int16, device=dev)
-    v = torch.empty((T, Hkv, D), dtype=torch.int16, device=dev)
-    ws = torch.empty(peagle.layer1_qkv_workspace_bytes(n, T, H), dtype=torch.uint8, device=dev)
-
-    def call():
-        peagle.layer1_qkv(n, K, T, hidden, emb, wd["w_norm_emb"], wd["w_norm_hidden"], wd["w_qkv"],
-                          Hq, Hkv, D, q=q, k=k, v=v, workspace=ws)
-
     for _ in range(warmup):
         call()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -271,17 +255,59 @@ def layer1_bench(cfg, seed, n, K, T, hidden, emb, steps, warmup):
         call()
         ev[i + 1].record()
     torch.cuda.synchronize()
-    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    return float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+
+
+def layer_bench(cfg_id, cfg, seed, n, K, T, hidden, emb, attn_out, steps, warmup):
+    """Time the first draft layer's other stages on the step's own tensors: attention
+    inputs (RMSNorm halves and concat, QKV GEMM on rows 0..n, copy of row n) from the fused
+    stage's outputs; the rest of the layer (output projection and residual, RMSNorm,
+    SwiGLU MLP and residual) from the step's attention output; the draft-vocab head with
+    its fused argmax on the result."""
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    H, Hq, Hkv, D = cfg["H"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    QW, I, V = Hq * D, synth.LAYER_SHAPES.get(cfg_id, {"I": 4 * H})["I"], synth.DRAFT_VOCAB
+    dev = hidden.device
+    dw = {k2: torch.from_numpy(v2.view(np.int16)).to(dev)
+          for k2, v2 in {**synth.layer1_weights(seed, H, Hq, Hkv, D),
+                         **synth.layer1_post_weights(seed, H, QW, I, V)}.items()}
+    q = torch.empty((T, Hq, D), dtype=torch.int16, device=dev)
+    k = torch.empty((T, Hkv, D), dtype=torch.int16, device=dev)
+    v = torch.empty((T, Hkv, D), dtype=torch.int16, device=dev)
+    ws_qkv = torch.empty(peagle.layer1_qkv_workspace_bytes(n, T, H), dtype=torch.uint8, device=dev)
+    h2 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_post = torch.empty(int(peagle.lib().peagle_layer1_post_workspace_bytes(n, T, H, QW, I)),
+                          dtype=torch.uint8, device=dev)
+    tokens = torch.empty(T, dtype=torch.int32, device=dev)
+    ws_head = torch.empty(int(peagle.lib().peagle_draft_head_workspace_bytes(T, H, V)),
+                          dtype=torch.uint8, device=dev)
+    ms_qkv = _time_calls(lambda: peagle.layer1_qkv(
+        n, K, T, hidden, emb, dw["w_norm_emb"], dw["w_norm_hidden"], dw["w_qkv"], Hq, Hkv, D,
+        q=q, k=k, v=v, workspace=ws_qkv), steps, warmup)
+    ms_post = _time_calls(lambda: peagle.layer1_post(
+        n, K, T, attn_out, hidden, dw["w_norm_hidden"], dw["w_o"], dw["w_post"], dw["w_gate"],
+        dw["w_up"], dw["w_down"], h2=h2, workspace=ws_post), steps, warmup)
+    ms_head = _time_calls(lambda: peagle.draft_head(h2, dw["w_final"], dw["w_head"],
+                                                    tokens=tokens, workspace=ws_head),
+                          steps, warmup)
     M = n + 1 if T > n else n
-    N = (Hq + 2 * Hkv) * D
-    flop = 2.0 * M * N * 2 * H
-    del q, k, v, ws
+    f_qkv = 2.0 * M * (Hq + 2 * Hkv) * D * 2 * H
+    f_post = 2.0 * T * H * (QW + 3 * I)
+    f_head = 2.0 * T * H * V
+    del q, k, v, ws_qkv, h2, ws_post, tokens, ws_head, dw
     torch.cuda.empty_cache()
-    return {"rows_projected": M, "draft_rows": T, "gemm": f"{M}x{N}x{2 * H}",
-            "ms_per_call": round(ms, 4), "gemm_flop": flop,
-            "tflops_whole_call": round(flop / (ms * 1e-3) / 1e12, 1),
-            "frac_bf16_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "flop_saved_vs_all_rows": round(1.0 - M / T, 4)}
+    tf = lambda f, ms: round(f / (ms * 1e-3) / 1e12, 1)
+    return {"intermediate": I, "draft_vocab": V,
+            "qkv": {"rows_projected": M, "draft_rows": T, "gemm": f"{M}x{(Hq + 2 * Hkv) * D}x{2 * H}",
+                    "ms_per_call": round(ms_qkv, 4), "tflops": tf(f_qkv, ms_qkv),
+                    "flop_saved_vs_all_rows": round(1.0 - M / T, 4)},
+            "post": {"gemms": f"{T}x{H}x{QW}, {T}x{2 * I}x{H}, {T}x{H}x{I}",
+                     "ms_per_call": round(ms_post, 4), "tflops": tf(f_post, ms_post)},
+            "head": {"gemm": f"{T}x{V}x{H} with fused argmax", "ms_per_call": round(ms_head, 4),
+                     "tflops": tf(f_head, ms_head)},
+            "layer_ms_excluding_attention": round(ms_qkv + ms_post + ms_head, 4)}
 
 
 def decode_bench(name, steps, warmup):
