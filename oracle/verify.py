@@ -8,6 +8,13 @@ Readings: greedy decoding, so a draft token is correct iff it equals the target'
 argmax at the same depth; draft and target share one vocabulary (identity map);
 argmax takes the lowest index among equal maxima. Logits are bf16; the decision
 is taken on their exact values (float32 upcast is exact).
+
+Draft vocabulary smaller than the target's (NeMo Automodel PR 2376: a draft vocabulary
+of 8192 in its validation run, and out-of-draft-vocab masking among its checks): the
+draft head scores Vd draft ids; a table d2t gives the target id of each draft id; a
+draft token is correct iff its target id equals the target's argmax over the Vt target
+ids. A target argmax outside the table's image can never be matched. (The pages name
+the map, not its encoding; a plain table of target ids is taken here.)
 """
 from __future__ import annotations
 
@@ -42,3 +49,12 @@ def verify(draft_logits, target_logits) -> dict:
     a = argmax_rows(draft_logits)
     b = argmax_rows(target_logits)
     return dict(draft_tok=a, target_tok=b, accept_len=accept_lengths(a, b))
+
+
+def verify_d2t(draft_logits, target_logits, d2t) -> dict:
+    """draft_logits [N, K, Vd], target_logits [N, K, Vt] (bf16 bits), d2t int [Vd].
+    draft_tok holds draft ids; the comparison uses d2t[draft_tok]."""
+    a = argmax_rows(draft_logits)
+    b = argmax_rows(target_logits)
+    mapped = np.asarray(d2t, dtype=np.int64)[a]
+    return dict(draft_tok=a, target_tok=b, accept_len=accept_lengths(mapped, b))

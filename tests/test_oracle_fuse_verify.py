@@ -97,3 +97,43 @@ def test_planted_acceptance_structure():
     assert (L > planted).sum() <= 12
     # mean planted prefix of a geometric stop: sum_{k=1..K} 0.7^k = 2.1993...
     assert abs(planted.mean() - sum(0.7 ** k for k in range(1, K + 1))) < 0.12
+
+
+def test_d2t_identity_reduces_to_shared_vocab():
+    lg = synth.verify_logits(seed=8, drafts=200, K=5, V=300, p_plant=0.7)
+    a = verify.verify(lg["draft_logits"], lg["target_logits"])
+    b = verify.verify_d2t(lg["draft_logits"], lg["target_logits"], np.arange(300))
+    for key in ("draft_tok", "target_tok", "accept_len"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_d2t_brute_force_and_permutation():
+    """Brute force on tiny inputs; relabelling the draft ids (columns and table together)
+    changes draft_tok by the relabelling and nothing else."""
+    rng = np.random.default_rng(9)
+    N, K, Vd, Vt = 40, 4, 12, 30
+    d2t = np.sort(rng.choice(Vt, size=Vd, replace=False))
+    dl = rng.standard_normal((N, K, Vd)).astype(np.float32)
+    tl = rng.standard_normal((N, K, Vt)).astype(np.float32)
+    # plant agreeing maxima along a prefix of each draft
+    for i in range(N):
+        for d in range(rng.integers(0, K + 1)):
+            j = rng.integers(0, Vd)
+            dl[i, d, j], tl[i, d, d2t[j]] = 9.0, 9.0
+    db, tb = _f32_to_bits(dl), _f32_to_bits(tl)
+    got = verify.verify_d2t(db, tb, d2t)
+    dv, tv = to_f64(db), to_f64(tb)
+    for i in range(N):
+        L = 0
+        for d in range(K):
+            da = max(range(Vd), key=lambda t: (dv[i, d, t], -t))
+            ta = max(range(Vt), key=lambda t: (tv[i, d, t], -t))
+            assert got["draft_tok"][i, d] == da and got["target_tok"][i, d] == ta
+            if L == d and d2t[da] == ta:
+                L += 1
+        assert got["accept_len"][i] == L
+    perm = rng.permutation(Vd)                      # new id of draft id j is inv[j]
+    inv = np.argsort(perm)
+    got2 = verify.verify_d2t(db[:, :, perm], tb, d2t[perm])
+    assert np.array_equal(perm[got2["draft_tok"]], got["draft_tok"])
+    assert np.array_equal(got2["accept_len"], got["accept_len"])
