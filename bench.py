@@ -229,6 +229,7 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
+    result["verify_d2t"] = verify_d2t_bench(args.steps, args.warmup)
     result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, hidden, emb, out,
                                         args.steps, args.warmup)
 
@@ -242,6 +243,29 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, seed, qkv, cu_h, idx_h, off_h, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def verify_d2t_bench(steps, warmup, N=4096, K=8, Vd=8192, Vt=32000):
+    """Time peagle_accept_prefix_d2t on 4096 drafts of K = 8 with a draft vocabulary of
+    8192 ids inside a 32000-id target vocabulary (logits drawn on the device with torch's
+    seeded generator; the argmaxes do not change the work)."""
+    import torch
+    from token_drafting_amd import peagle
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(29)
+    dl = torch.randn((N, K, Vd), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    tl = torch.randn((N, K, Vt), generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    d2t = torch.sort(torch.randperm(Vt, generator=g, device="cuda")[:Vd]).values.to(torch.int32)
+    outs = [torch.empty((N, K), dtype=torch.int32, device="cuda") for _ in range(2)]
+    alen = torch.empty(N, dtype=torch.int32, device="cuda")
+    ms = _time_calls(lambda: peagle.accept_prefix_d2t(dl, tl, d2t, outs[0], outs[1], alen), steps,
+                     warmup)
+    nbytes = N * K * (Vd + Vt) * 2 + N * K * 8 + N * 4
+    del dl, tl
+    torch.cuda.empty_cache()
+    return {"drafts": N, "K": K, "draft_vocab": Vd, "target_vocab": Vt, "ms_per_call": round(ms, 4),
+            "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def _time_calls(call, steps, warmup):

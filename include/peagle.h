@@ -189,6 +189,24 @@ int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,
                          void *stream);
 
 /*
+ * peagle_accept_prefix_d2t -- greedy verification with a draft vocabulary smaller than the
+ * target's [N: draft vocabulary 8192 in the validation run; out-of-draft-vocab masking]:
+ * the draft head scores Vd draft ids, d2t[draft id] is the id in the target's vocabulary,
+ * and a draft token is correct iff d2t[its argmax] equals the target's argmax over Vt. A
+ * target argmax outside d2t's image never matches.
+ *   draft_logits   bf16[N, K, Vd];  target_logits bf16[N, K, Vt]
+ *   d2t            int32[Vd]   (device; values are only compared, never used as addresses)
+ *   draft_tok      int32[N, K] out  draft ids (lowest index on ties)
+ *   target_tok     int32[N, K] out  target ids
+ *   accept_len     int32[N]    out
+ */
+int peagle_accept_prefix_d2t(int32_t num_drafts, int32_t K, int32_t draft_vocab,
+                             int32_t target_vocab, const peagle_bf16 *draft_logits,
+                             const peagle_bf16 *target_logits, const int32_t *d2t,
+                             int32_t *draft_tok, int32_t *target_tok, int32_t *accept_len,
+                             void *stream);
+
+/*
  * The first draft decoder layer's attention inputs [R, "How Speculative Decoding Works",
  * step 3: the drafter input concatenates embeddings and hidden states; G, "Architecture":
  * Llama-style decoder layers; N, changelog: depths >= 1 take the ptd token and the

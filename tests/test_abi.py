@@ -123,6 +123,10 @@ def test_rope_and_accept_argument_errors(lib):
     assert _code("peagle_accept_prefix", 4, 65, 100, None, None, None, None, None, None) == peagle.ERR_ARG
     assert _code("peagle_accept_prefix", 4, 8, 0, None, None, None, None, None, None) == peagle.ERR_ARG
     assert _code("peagle_accept_prefix", 4, 8, 100, None, None, None, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_accept_prefix_d2t", 4, 8, 100, 200, None, None, None, None, None, None,
+                 None) == peagle.ERR_ARG
+    assert _code("peagle_accept_prefix_d2t", 4, 8, 0, 200, None, None, None, None, None, None,
+                 None) == peagle.ERR_ARG
 
 
 def test_workspace_bytes(lib):

@@ -264,3 +264,18 @@ def test_accept_prefix_full_size(pe):
     v = synth.CONFIGS[5]["verify"]
     print("accept full size", flush=True)
     _verify_case(pe, v["drafts"], v["K"], v["V"], seed=5, p_plant=v["p_plant"])
+
+
+# ---------------------------------------------------------------- verification, d2t map
+@pytest.mark.parametrize("N,K,Vd,Vt", [(64, 8, 1000, 3000), (33, 1, 64, 65), (17, 5, 8192, 32000),
+                                       (9, 3, 7, 1_000), (4096, 8, 8192, 32000)])
+def test_accept_prefix_d2t_bit_exact(pe, N, K, Vd, Vt):
+    print(f"accept d2t N={N} K={K} Vd={Vd} Vt={Vt}", flush=True)
+    lg = synth.verify_logits_d2t(N + K, N, K, Vd, Vt, 0.7)
+    dt, tt, al = pe.accept_prefix_d2t(to_dev(lg["draft_logits"]), to_dev(lg["target_logits"]),
+                                      to_dev(lg["d2t"]))
+    want = over.verify_d2t(lg["draft_logits"], lg["target_logits"], lg["d2t"])
+    assert np.array_equal(to_host(dt), want["draft_tok"])
+    assert np.array_equal(to_host(tt), want["target_tok"])
+    assert np.array_equal(to_host(al), want["accept_len"])
+    assert (want["accept_len"] >= lg["planted"]).all()

@@ -7,6 +7,7 @@
 #include "peagle.h"
 #include "kernels.h"
 #include "layer.h"
+#include "accept.h"
 
 using namespace peagle;
 
@@ -388,6 +389,21 @@ int peagle_draft_head(int64_t T, const float* h, int32_t H, const peagle_bf16* w
   if (workspace_bytes < draft_head_workspace_bytes(T, H, V)) return PEAGLE_ERR_WORKSPACE;
   return status_of(launch_draft_head(T, H, V, eps, h, w_final, w_head, tokens,
                                      static_cast<char*>(workspace),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int peagle_accept_prefix_d2t(int32_t num_drafts, int32_t K, int32_t draft_vocab,
+                             int32_t target_vocab, const peagle_bf16* draft_logits,
+                             const peagle_bf16* target_logits, const int32_t* d2t,
+                             int32_t* draft_tok, int32_t* target_tok, int32_t* accept_len,
+                             void* stream) {
+  if (num_drafts < 0 || K < 1 || K > PEAGLE_MAX_DEPTHS || draft_vocab < 1 || target_vocab < 1)
+    return PEAGLE_ERR_ARG;
+  if (!draft_logits || !target_logits || !d2t || !draft_tok || !target_tok || !accept_len)
+    return PEAGLE_ERR_ARG;
+  if (num_drafts == 0) return PEAGLE_OK;
+  return status_of(launch_accept_map(num_drafts, K, draft_vocab, target_vocab, draft_logits,
+                                     target_logits, d2t, draft_tok, target_tok, accept_len,
                                      static_cast<hipStream_t>(stream)));
 }
 

@@ -12,7 +12,10 @@
 // order-preserving 16-bit code (sign-magnitude to offset binary, -0 folded onto +0 so
 // that equal values tie). Then wave 0 takes one ballot over the K match bits; the
 // accepted length is the number of trailing ones of that mask.
+#include <algorithm>
+
 #include "common.h"
+#include "accept.h"
 #include "kernels.h"
 
 namespace peagle {
@@ -86,21 +89,26 @@ __device__ uint32_t row_argmax(const uint16_t* __restrict__ row, int V, bool vec
   return ArgKey<Key>::index(best);
 }
 
-template <typename Key>
+// One workgroup per draft: the 2K row argmaxes (draft rows of Vd, target rows of Vt),
+// then one ballot over the K matches. With kMap the draft token's target id is
+// d2t[draft token] (a draft vocabulary smaller than the target's).
+template <typename Key, bool kMap>
 __global__ __launch_bounds__(256) void accept_kernel(const uint16_t* __restrict__ draft,
                                                      const uint16_t* __restrict__ target,
+                                                     const int32_t* __restrict__ d2t,
                                                      int32_t* __restrict__ dtok,
                                                      int32_t* __restrict__ ttok,
-                                                     int32_t* __restrict__ alen, int K, int V,
-                                                     bool vec) {
+                                                     int32_t* __restrict__ alen, int K, int Vd,
+                                                     int Vt, bool vec) {
   __shared__ int32_t toks[2][kMaxDepths];
   const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int r = wave; r < 2 * K; r += 4) {
     const int which = r / K, d = r % K;
+    const int V = which ? Vt : Vd;
     const uint16_t* row = (which ? target : draft) + ((size_t)i * K + d) * V;
     const int32_t tok = (int32_t)row_argmax<Key>(row, V, vec, lane);
     if (lane == 0) {
-      toks[which][d] = tok;
+      toks[which][d] = (kMap && which == 0) ? d2t[tok] : tok;
       (which ? ttok : dtok)[(size_t)i * K + d] = tok;
     }
   }
@@ -118,18 +126,31 @@ __global__ __launch_bounds__(256) void accept_kernel(const uint16_t* __restrict_
 
 }  // namespace
 
+hipError_t launch_accept_map(int32_t N, int32_t K, int32_t Vd, int32_t Vt,
+                             const uint16_t* draft, const uint16_t* target, const int32_t* d2t,
+                             int32_t* draft_tok, int32_t* target_tok, int32_t* accept_len,
+                             hipStream_t stream) {
+  const bool vec = (Vd % 8 == 0) && (Vt % 8 == 0) &&
+                   ((reinterpret_cast<uintptr_t>(draft) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(target) & 15) == 0);
+  const bool wide = std::max(Vd, Vt) > 65536;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(N), dim3(256), 0, stream, draft, target, d2t, draft_tok,
+                       target_tok, accept_len, K, Vd, Vt, vec);
+  };
+  if (d2t == nullptr) {
+    if (!wide) go(accept_kernel<uint32_t, false>); else go(accept_kernel<uint64_t, false>);
+  } else {
+    if (!wide) go(accept_kernel<uint32_t, true>); else go(accept_kernel<uint64_t, true>);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_accept(int32_t N, int32_t K, int32_t V, const uint16_t* draft,
                          const uint16_t* target, int32_t* draft_tok, int32_t* target_tok,
                          int32_t* accept_len, hipStream_t stream) {
-  const bool vec = (V % 8 == 0) && ((reinterpret_cast<uintptr_t>(draft) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(target) & 15) == 0);
-  if (V <= 65536)
-    hipLaunchKernelGGL(accept_kernel<uint32_t>, dim3(N), dim3(256), 0, stream, draft, target,
-                       draft_tok, target_tok, accept_len, K, V, vec);
-  else
-    hipLaunchKernelGGL(accept_kernel<uint64_t>, dim3(N), dim3(256), 0, stream, draft, target,
-                       draft_tok, target_tok, accept_len, K, V, vec);
-  return hipGetLastError();
+  return launch_accept_map(N, K, V, V, draft, target, nullptr, draft_tok, target_tok, accept_len,
+                           stream);
 }
 
 }  // namespace peagle

@@ -47,6 +47,7 @@ SIGNATURES = {
                             _p, _f32, _p, _p, _sz, _p], _i32),
     "peagle_draft_head_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "peagle_draft_head": ([_i64, _p, _i32, _p, _p, _i32, _f32, _p, _p, _sz, _p], _i32),
+    "peagle_accept_prefix_d2t": ([_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p], _i32),
     "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
     "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32], _sz),
@@ -213,6 +214,26 @@ def accept_prefix(draft_logits, target_logits, draft_tok=None, target_tok=None, 
     _check("peagle_accept_prefix", lib().peagle_accept_prefix(
         N, K, V, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tok), _ptr(target_tok),
         _ptr(accept_len), _stream()))
+    return draft_tok, target_tok, accept_len
+
+
+def accept_prefix_d2t(draft_logits, target_logits, d2t, draft_tok=None, target_tok=None,
+                      accept_len=None):
+    """Verification with a draft vocabulary of Vd ids mapped into the target's Vt by d2t."""
+    for t, name in ((draft_logits, "draft_logits"), (target_logits, "target_logits"), (d2t, "d2t")):
+        _dev(t, name)
+    N, K, Vd = draft_logits.shape
+    Vt = target_logits.shape[2]
+    dev = draft_logits.device
+    if draft_tok is None:
+        draft_tok = torch.empty((N, K), dtype=torch.int32, device=dev)
+    if target_tok is None:
+        target_tok = torch.empty((N, K), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(N, dtype=torch.int32, device=dev)
+    _check("peagle_accept_prefix_d2t", lib().peagle_accept_prefix_d2t(
+        N, K, Vd, Vt, _ptr(draft_logits), _ptr(target_logits), _ptr(d2t), _ptr(draft_tok),
+        _ptr(target_tok), _ptr(accept_len), _stream()))
     return draft_tok, target_tok, accept_len
 
 

@@ -29,6 +29,7 @@ TAG_CACHE_K, TAG_CACHE_V, TAG_NEW_Q, TAG_NEW_K, TAG_NEW_V = 11, 12, 13, 14, 15
 TAG_NORM_EMB, TAG_NORM_HID, TAG_WQKV, TAG_L1_HID, TAG_L1_EMB = 16, 17, 18, 19, 20
 TAG_WO, TAG_NORM_POST, TAG_WGATE, TAG_WUP, TAG_WDOWN, TAG_NORM_FINAL, TAG_WHEAD, TAG_ATTN = (
     21, 22, 23, 24, 25, 26, 27, 28)
+TAG_D2T = 29
 
 # Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
 # layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
@@ -273,3 +274,32 @@ def attention_out_standin(seed: int, T: int, QW: int) -> np.ndarray:
     """A stand-in for the attention output [T, QW] (float32): softmax-weighted averages of
     N(0, 1) values have magnitudes below 1; drawn as N(0, 0.3^2)."""
     return (0.3 * _rng(seed, TAG_ATTN).standard_normal((T, QW), dtype=np.float32)).astype(np.float32)
+
+
+def verify_logits_d2t(seed: int, drafts: int, K: int, Vd: int, Vt: int, p_plant: float,
+                      chunk: int = 256) -> dict:
+    """Verification inputs with a draft vocabulary of Vd ids inside a target vocabulary of
+    Vt: d2t is a seeded sorted subset of [0, Vt) (int32 [Vd]); draft logits [drafts, K, Vd]
+    and target logits [drafts, K, Vt] are bf16 bits of N(0, 1), with planted shared maxima
+    (16.0 at draft id j and at target id d2t[j]) along a geometric prefix as in
+    verify_logits."""
+    d2t = np.sort(_rng(seed, TAG_D2T).choice(Vt, size=Vd, replace=False)).astype(np.int32)
+    rng = _rng(seed, TAG_LOGITS)
+    plant_rng = _rng(seed, TAG_LOGITS + 100)
+    draft = np.empty((drafts, K, Vd), dtype=np.uint16)
+    target = np.empty((drafts, K, Vt), dtype=np.uint16)
+    for lo in range(0, drafts, chunk):
+        hi = min(drafts, lo + chunk)
+        draft[lo:hi] = f32_to_bf16_bits(rng.standard_normal((hi - lo) * K * Vd, dtype=np.float32)).reshape(hi - lo, K, Vd)
+        target[lo:hi] = f32_to_bf16_bits(rng.standard_normal((hi - lo) * K * Vt, dtype=np.float32)).reshape(hi - lo, K, Vt)
+    coins = plant_rng.random((drafts, K)) < p_plant
+    where = plant_rng.integers(0, Vd, size=(drafts, K))
+    planted = np.zeros(drafts, dtype=np.int32)
+    for i in range(drafts):
+        for d in range(K):
+            if not coins[i, d]:
+                break
+            draft[i, d, where[i, d]] = PLANT_VALUE_BITS
+            target[i, d, d2t[where[i, d]]] = PLANT_VALUE_BITS
+            planted[i] += 1
+    return dict(draft_logits=draft, target_logits=target, d2t=d2t, planted=planted)
