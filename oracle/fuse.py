@@ -8,10 +8,12 @@ projected target aux hidden states, depths >= 1 consume the reserved
 The speculators P-EAGLE guide ("Architecture") states that the target hidden
 states from the selected layers are concatenated and projected.
 
-Readings: fc has no bias and no fc_norm (both optional on the pages and off
-here); the weight is stored [H, aux_dim] (output-major, as a linear layer's
-weight). Output ``hidden`` is float64 here; the embedding rows are copies of
-bf16 table rows, returned as the same bit patterns.
+Readings: fc has no bias; the weight is stored [H, aux_dim] (output-major, as a
+linear layer's weight). fc_norm (the PR projects mask_hidden "through fc/fc_norm", after
+EAGLE-3.1's toggle) is off by default; when a weight is given it is an RMSNorm of the fc
+output (Llama form, eps 1e-6), applied to the real and the mask projections alike. Output
+``hidden`` is float64 here; the embedding rows are copies of bf16 table rows, returned as
+the same bit patterns.
 """
 from __future__ import annotations
 
@@ -22,10 +24,11 @@ from .cod import row_depths
 
 
 def fuse_inputs(aux, fc_weight, mask_hidden, tokens, embed, ptd_token_id,
-                idx, depth_off, rows=None) -> dict:
+                idx, depth_off, rows=None, fc_norm_weight=None, eps: float = 1e-6) -> dict:
     """hidden [R, H] float64 and embed_rows [R, H] bf16 bits for draft rows.
 
     rows: optional subset of draft rows (default: all T rows, in order).
+    fc_norm_weight: optional bf16 bits [H] of the RMSNorm after fc.
     """
     idx = np.asarray(idx)
     T = len(idx)
@@ -44,4 +47,8 @@ def fuse_inputs(aux, fc_weight, mask_hidden, tokens, embed, ptd_token_id,
     if (~real).any():
         hidden[~real] = y_mask
         embed_rows[~real] = embed[ptd_token_id]
+    if fc_norm_weight is not None:
+        from .layer import rms_norm
+        hidden = rms_norm(hidden, to_f64(fc_norm_weight), eps)
+        y_mask = rms_norm(y_mask, to_f64(fc_norm_weight), eps)
     return dict(hidden=hidden, embed_rows=embed_rows, y_mask=y_mask)

@@ -137,3 +137,31 @@ def test_d2t_brute_force_and_permutation():
     got2 = verify.verify_d2t(db[:, :, perm], tb, d2t[perm])
     assert np.array_equal(perm[got2["draft_tok"]], got["draft_tok"])
     assert np.array_equal(got2["accept_len"], got["accept_len"])
+
+
+def test_fc_norm_is_rmsnorm_of_the_projection():
+    """With an fc_norm weight every row (real and mask) is the Llama RMSNorm of the plain
+    projection, checked against transformers' module; depth >= 1 rows stay equal."""
+    import torch
+    from transformers.models.llama.modeling_llama import LlamaRMSNorm
+    n, K, A, H, vocab, seed = 9, 3, 16, 8, 20, 4
+    rng = np.random.default_rng(seed)
+    aux = synth.f32_to_bf16_bits(rng.standard_normal((n, A)).astype(np.float32))
+    W = synth.f32_to_bf16_bits((0.1 * rng.standard_normal((H, A))).astype(np.float32))
+    mh = synth.f32_to_bf16_bits(rng.standard_normal(A).astype(np.float32))
+    E = synth.f32_to_bf16_bits(rng.standard_normal((vocab, H)).astype(np.float32))
+    tokens = rng.integers(0, vocab - 1, n).astype(np.int32)
+    wn = synth.f32_to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    sel = cod.cod_select(n, K, 0.7, 0.2, seed, np.array([0, n]))
+    plain = fuse.fuse_inputs(aux, W, mh, tokens, E, vocab - 1, sel["idx"], sel["depth_off"])
+    normed = fuse.fuse_inputs(aux, W, mh, tokens, E, vocab - 1, sel["idx"], sel["depth_off"],
+                              fc_norm_weight=wn)
+    m = LlamaRMSNorm(H, eps=1e-6).double()
+    with torch.no_grad():
+        m.weight.copy_(torch.from_numpy(to_f64(wn)))
+        want = m(torch.from_numpy(plain["hidden"])).numpy()
+    np.testing.assert_allclose(normed["hidden"], want, rtol=2e-6, atol=1e-7)
+    assert np.array_equal(normed["embed_rows"], plain["embed_rows"])
+    T = len(sel["idx"])
+    assert np.all(normed["hidden"][n:] == normed["hidden"][n])
+    assert T > n
