@@ -229,6 +229,12 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
 
+    wn = torch.from_numpy(synth.fc_norm_weight(seed, H).view(np.int16)).to(dev)
+    ms_fcn = _time_calls(lambda: peagle.fuse_inputs(
+        n, K, T, sel["idx"], d["aux"], d["fc_weight"], d["mask_hidden"], d["tokens"], d["embed"],
+        base["ptd_token_id"], hidden, emb, fc_norm_weight=wn), args.steps, args.warmup)
+    result["fuse_fc_norm"] = {"ms_per_call": round(ms_fcn, 4),
+                              "ms_without_fc_norm": round(stage_ms["fuse_inputs"], 4)}
     result["verify_d2t"] = verify_d2t_bench(args.steps, args.warmup)
     result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, hidden, emb, out,
                                         args.steps, args.warmup)

@@ -106,6 +106,22 @@ int peagle_fuse_inputs(int64_t n, int32_t K, int64_t T, const int32_t *idx,
                        float *hidden_out, peagle_bf16 *embed_out, void *stream);
 
 /*
+ * peagle_fuse_inputs_fc_norm -- peagle_fuse_inputs with the RMSNorm after fc [N,
+ * description: mask_hidden is projected "through fc/fc_norm", after EAGLE-3.1's toggle]:
+ * every hidden_out row (the projections of aux and of mask_hidden alike) becomes
+ *   row / sqrt(mean(row^2) + eps) * fc_norm_weight,
+ * in fp32. fc_norm_weight bf16[H]; eps > 0 (Llama: 1e-6); other arguments as for
+ * peagle_fuse_inputs. H must be a multiple of 8 (as there).
+ */
+int peagle_fuse_inputs_fc_norm(int64_t n, int32_t K, int64_t T, const int32_t *idx,
+                               const peagle_bf16 *aux, int32_t aux_dim,
+                               const peagle_bf16 *fc_weight, const peagle_bf16 *mask_hidden,
+                               const int32_t *tokens, const peagle_bf16 *embed, int32_t vocab,
+                               int32_t ptd_token_id, int32_t H, const peagle_bf16 *fc_norm_weight,
+                               float eps, float *hidden_out, peagle_bf16 *embed_out,
+                               void *stream);
+
+/*
  * peagle_rope_table -- cos/sin cache indexed by position value [N, RoPE-fix commit]:
  *   cos_out[pos][j] = cos(pos * theta^(-2j/D)), sin_out likewise, j < D/2,
  * angles and cos/sin evaluated in float64, stored fp32, for pos in [0, max_pos].

@@ -81,17 +81,20 @@ def test_cod_select_repeatable(pe):
 
 
 # ---------------------------------------------------------------- fuse
-def _fuse_case(pe, n, K, H, A, seed, rows=None, vocab=32000):
+def _fuse_case(pe, n, K, H, A, seed, rows=None, vocab=32000, fc_norm=False):
     cfg = dict(n=n, K=K, H=H, aux_dim=A, num_seqs=1, vocab_in=vocab)
     base = synth.base_inputs(cfg, seed)
+    wn = synth.fc_norm_weight(seed, H) if fc_norm else None
     sel = ocod.cod_select(n, K, 0.7, 0.2, seed, base["cu_seqlens"])
     T = int(sel["depth_off"][-1])
     dsel = pe.cod_select(n, K, 0.7, 0.2, seed, to_dev(base["cu_seqlens"]))
     hidden, emb = pe.fuse_inputs(n, K, T, dsel["idx"], to_dev(base["aux"]), to_dev(base["fc_weight"]),
                                  to_dev(base["mask_hidden"]), to_dev(base["tokens"]),
-                                 to_dev(base["embed"]), base["ptd_token_id"])
+                                 to_dev(base["embed"]), base["ptd_token_id"],
+                                 fc_norm_weight=None if wn is None else to_dev(wn))
     want = ofuse.fuse_inputs(base["aux"], base["fc_weight"], base["mask_hidden"], base["tokens"],
-                             base["embed"], base["ptd_token_id"], sel["idx"], sel["depth_off"], rows=rows)
+                             base["embed"], base["ptd_token_id"], sel["idx"], sel["depth_off"], rows=rows,
+                             fc_norm_weight=wn)
     h = to_host(hidden)
     e = to_host(emb)
     if rows is not None:
@@ -107,6 +110,17 @@ def _fuse_case(pe, n, K, H, A, seed, rows=None, vocab=32000):
 def test_fuse_small_full(pe, n, K, H, A):
     print(f"fuse n={n} K={K} H={H} A={A}", flush=True)
     h, e, want = _fuse_case(pe, n, K, H, A, seed=11)
+    assert_close(h, want["hidden"], "hidden")
+    assert np.array_equal(e, want["embed_rows"])
+
+
+@pytest.mark.parametrize("n,K,H,A", [(256, 4, 256, 1536), (300, 4, 136, 520), (97, 1, 64, 64),
+                                     (4096, 4, 640, 7680)])
+def test_fuse_fc_norm(pe, n, K, H, A):
+    """The RMSNorm after fc on every row (unit-RMS rows, so the stated absolute bar is also
+    a relative one here)."""
+    print(f"fuse fc_norm n={n} K={K} H={H} A={A}", flush=True)
+    h, e, want = _fuse_case(pe, n, K, H, A, seed=12, fc_norm=True)
     assert_close(h, want["hidden"], "hidden")
     assert np.array_equal(e, want["embed_rows"])
 

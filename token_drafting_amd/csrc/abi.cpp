@@ -7,7 +7,7 @@
 #include "peagle.h"
 #include "kernels.h"
 #include "layer.h"
-#include "accept.h"
+#include "variants.h"
 
 using namespace peagle;
 
@@ -163,6 +163,22 @@ int peagle_fuse_inputs(int64_t n, int32_t K, int64_t T, const int32_t* idx,
   FuseArgs a{(int32_t)n, (int32_t)T, aux_dim, H, vocab, ptd_token_id};
   return status_of(launch_fuse(a, idx, aux, fc_weight, mask_hidden, tokens, embed, hidden_out,
                                embed_out, static_cast<hipStream_t>(stream)));
+}
+
+int peagle_fuse_inputs_fc_norm(int64_t n, int32_t K, int64_t T, const int32_t* idx,
+                               const peagle_bf16* aux, int32_t aux_dim,
+                               const peagle_bf16* fc_weight, const peagle_bf16* mask_hidden,
+                               const int32_t* tokens, const peagle_bf16* embed, int32_t vocab,
+                               int32_t ptd_token_id, int32_t H, const peagle_bf16* fc_norm_weight,
+                               float eps, float* hidden_out, peagle_bf16* embed_out,
+                               void* stream) {
+  if (!fc_norm_weight || !aligned16(fc_norm_weight) || !(eps > 0.f) || !std::isfinite(eps))
+    return PEAGLE_ERR_ARG;
+  const int st = peagle_fuse_inputs(n, K, T, idx, aux, aux_dim, fc_weight, mask_hidden, tokens,
+                                    embed, vocab, ptd_token_id, H, hidden_out, embed_out, stream);
+  if (st != PEAGLE_OK) return st;
+  return status_of(
+      launch_rms_inplace(hidden_out, fc_norm_weight, T, H, eps, static_cast<hipStream_t>(stream)));
 }
 
 int peagle_rope_table(int32_t head_dim, double theta, int32_t max_pos, float* cos_out,

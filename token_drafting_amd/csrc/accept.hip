@@ -15,7 +15,7 @@
 #include <algorithm>
 
 #include "common.h"
-#include "accept.h"
+#include "variants.h"
 #include "kernels.h"
 
 namespace peagle {

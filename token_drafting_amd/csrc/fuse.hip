@@ -24,6 +24,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
+#include "variants.h"
 
 namespace peagle {
 
@@ -186,7 +187,38 @@ __global__ __launch_bounds__(256) void fuse_fill_kernel(
   }
 }
 
+// fc_norm: x[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w in place; one wave per row.
+__global__ __launch_bounds__(256) void rms_inplace_kernel(float* __restrict__ x,
+                                                          const uint16_t* __restrict__ w,
+                                                          int64_t rows, int H, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float* xr = x + r * H;
+  float s = 0.f;
+  for (int j = lane * 4; j < H; j += 256) {
+    const floatx4 v = *reinterpret_cast<const floatx4*>(xr + j);
+    s = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], s))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  const float inv = 1.f / sqrtf(s / (float)H + eps);
+  for (int j = lane * 4; j < H; j += 256) {
+    floatx4 v = *reinterpret_cast<const floatx4*>(xr + j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = v[i] * inv * bf16_bits_to_f32(w[j + i]);
+    *reinterpret_cast<floatx4*>(xr + j) = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rms_inplace(float* x, const uint16_t* w, int64_t rows, int32_t H, float eps,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(rms_inplace_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, x,
+                     w, rows, H, eps);
+  return hipGetLastError();
+}
 
 hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* aux,
                        const uint16_t* fc_weight, const uint16_t* mask_hidden,

@@ -1,5 +1,6 @@
-// Host-side launcher of the verification with a draft vocabulary smaller than the
-// target's. Internal to libpeagle: arguments are validated by the C entry point.
+// Host-side launchers of the variants of the path: verification with a draft vocabulary
+// smaller than the target's, and the RMSNorm after fc. Internal to libpeagle: arguments
+// are validated by the C entry points.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,5 +14,9 @@ hipError_t launch_accept_map(int32_t N, int32_t K, int32_t Vd, int32_t Vt,
                              const uint16_t* draft, const uint16_t* target, const int32_t* d2t,
                              int32_t* draft_tok, int32_t* target_tok, int32_t* accept_len,
                              hipStream_t stream);
+
+// In-place RMSNorm (fp32 rows, bf16 weight) of rows [0, rows) of x [rows, H].
+hipError_t launch_rms_inplace(float* x, const uint16_t* w, int64_t rows, int32_t H, float eps,
+                              hipStream_t stream);
 
 }  // namespace peagle

@@ -47,6 +47,8 @@ SIGNATURES = {
                             _p, _f32, _p, _p, _sz, _p], _i32),
     "peagle_draft_head_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "peagle_draft_head": ([_i64, _p, _i32, _p, _p, _i32, _f32, _p, _p, _sz, _p], _i32),
+    "peagle_fuse_inputs_fc_norm": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32,
+                                    _i32, _p, _f32, _p, _p, _p], _i32),
     "peagle_accept_prefix_d2t": ([_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p], _i32),
     "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
@@ -132,7 +134,7 @@ def cod_select_into(n, K, r, r_min, seed, cu_seqlens, out):
 
 # ---------------------------------------------------------------- fuse
 def fuse_inputs(n, K, T, idx, aux, fc_weight, mask_hidden, tokens, embed, ptd_token_id,
-                hidden_out=None, embed_out=None):
+                hidden_out=None, embed_out=None, fc_norm_weight=None, eps=1e-6):
     H, A = fc_weight.shape
     vocab = embed.shape[0]
     for t, name in ((idx, "idx"), (aux, "aux"), (fc_weight, "fc_weight"),
@@ -143,9 +145,16 @@ def fuse_inputs(n, K, T, idx, aux, fc_weight, mask_hidden, tokens, embed, ptd_to
         hidden_out = torch.empty((T, H), dtype=torch.float32, device=dev)
     if embed_out is None:
         embed_out = torch.empty((T, H), dtype=embed.dtype, device=dev)
-    _check("peagle_fuse_inputs", lib().peagle_fuse_inputs(
-        n, K, T, _ptr(idx), _ptr(aux), A, _ptr(fc_weight), _ptr(mask_hidden), _ptr(tokens),
-        _ptr(embed), vocab, ptd_token_id, H, _ptr(hidden_out), _ptr(embed_out), _stream()))
+    if fc_norm_weight is None:
+        _check("peagle_fuse_inputs", lib().peagle_fuse_inputs(
+            n, K, T, _ptr(idx), _ptr(aux), A, _ptr(fc_weight), _ptr(mask_hidden), _ptr(tokens),
+            _ptr(embed), vocab, ptd_token_id, H, _ptr(hidden_out), _ptr(embed_out), _stream()))
+    else:
+        _dev(fc_norm_weight, "fc_norm_weight")
+        _check("peagle_fuse_inputs_fc_norm", lib().peagle_fuse_inputs_fc_norm(
+            n, K, T, _ptr(idx), _ptr(aux), A, _ptr(fc_weight), _ptr(mask_hidden), _ptr(tokens),
+            _ptr(embed), vocab, ptd_token_id, H, _ptr(fc_norm_weight), float(eps),
+            _ptr(hidden_out), _ptr(embed_out), _stream()))
     return hidden_out, embed_out
 
 

@@ -29,7 +29,7 @@ TAG_CACHE_K, TAG_CACHE_V, TAG_NEW_Q, TAG_NEW_K, TAG_NEW_V = 11, 12, 13, 14, 15
 TAG_NORM_EMB, TAG_NORM_HID, TAG_WQKV, TAG_L1_HID, TAG_L1_EMB = 16, 17, 18, 19, 20
 TAG_WO, TAG_NORM_POST, TAG_WGATE, TAG_WUP, TAG_WDOWN, TAG_NORM_FINAL, TAG_WHEAD, TAG_ATTN = (
     21, 22, 23, 24, 25, 26, 27, 28)
-TAG_D2T = 29
+TAG_D2T, TAG_FC_NORM = 29, 30
 
 # Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
 # layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
@@ -303,3 +303,9 @@ def verify_logits_d2t(seed: int, drafts: int, K: int, Vd: int, Vt: int, p_plant:
             target[i, d, d2t[where[i, d]]] = PLANT_VALUE_BITS
             planted[i] += 1
     return dict(draft_logits=draft, target_logits=target, d2t=d2t, planted=planted)
+
+
+def fc_norm_weight(seed: int, H: int) -> np.ndarray:
+    """bf16 bits of 1 + N(0, 0.1^2): the RMSNorm weight after fc (near its unit init)."""
+    x = 1.0 + 0.1 * _rng(seed, TAG_FC_NORM).standard_normal(H, dtype=np.float32)
+    return f32_to_bf16_bits(x.astype(np.float32))
