@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="oracle sample size in query rows (0: sized for about 10-20 s of "
                          "host time from the oracle's cost per row, Hq * T * D)")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="time only the draft attention at n = 32768 (4 q / 1 kv heads, head "
+                         "dim 256, r = 0.7, r_min = 0.2) for K = 1, 2, 4, 8, 16")
     ap.add_argument("--decode", choices=["all", "none", "only"], default="all",
                     help="also time the decode-shaped draft attention on its inference "
                          "workloads (all), skip it (none), or time only it (only)")
@@ -94,6 +97,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.k_sweep:
+        print(json.dumps({"k_sweep": [k_sweep_point(K, args.steps, args.warmup)
+                                      for K in (1, 2, 4, 8, 16)]}), flush=True)
+        return
     if args.decode == "only":
         res = {name: decode_bench(name, args.steps, args.warmup)
                for name in sorted(synth.DECODE_CONFIGS)}
@@ -249,6 +256,36 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, seed, qkv, cu_h, idx_h, off_h, args.cpu_rows)
     print(json.dumps(result), flush=True)
+
+
+def k_sweep_point(K, steps, warmup, n=32768, Hq=4, Hkv=1, D=256, r=0.7, r_min=0.2,
+                  theta=1.0e4):
+    """Draft attention (prepare + core) for one depth count K on the headline shape; q, k, v
+    drawn on the device (the work does not depend on their values)."""
+    import torch
+    from token_drafting_amd import peagle
+
+    dev = torch.device("cuda:0")
+    cu = torch.tensor([0, n], dtype=torch.int32, device=dev)
+    sel = peagle.cod_select(n, K, r, r_min, K, cu)
+    T = sel["T"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(K)
+    q = torch.randn((T, Hq, D), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+    k = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+    v = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16).view(torch.int16)
+    cos, sin = peagle.rope_table(D, theta, peagle.rope_max_pos(n, K))
+    out, lse, ws = peagle.draft_attn(n, K, sel, cu, q, k, v, cos, sin)
+    ms = _time_calls(lambda: peagle.draft_attn(n, K, sel, cu, q, k, v, cos, sin, out, lse, ws),
+                     steps, warmup)
+    P, _ = useful_pairs(sel["idx"].cpu().numpy(), sel["depth_off"].cpu().numpy(),
+                        np.array([0, n]))
+    tflops = 4.0 * D * Hq * P / (ms * 1e-3) / 1e12
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+    return {"K": K, "draft_rows": T, "useful_pairs_per_head": P, "attention_ms": round(ms, 4),
+            "tflops": round(tflops, 1), "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "drafted_tokens_per_s": round(T / (ms * 1e-3), 1)}
 
 
 def verify_d2t_bench(steps, warmup, N=4096, K=8, Vd=8192, Vt=32000):

@@ -193,6 +193,7 @@ ATTN_SMALL = [
     (600, 4, 0.7, 0.2, 10, [1] * 5 + [595], 16, 1, 64, 1e4),     # one-token sequences, G = 16
     (520, 4, 0.7, 0.2, 11, [260, 260], 32, 8, 128, 5e5),         # Llama-8B heads
     (700, 4, 0.7, 0.2, 12, None, 4, 1, 256, 1e4),                # several workgroups at D=256
+    (300, 16, 0.7, 0.2, 13, [120, 180], 4, 1, 256, 1e4),         # K = 16 (the widest sweep point)
 ]
 
 
