@@ -15,6 +15,16 @@ draft head scores Vd draft ids; a table d2t gives the target id of each draft id
 draft token is correct iff its target id equals the target's argmax over the Vt target
 ids. A target argmax outside the table's image can never be matched. (The pages name
 the map, not its encoding; a plain table of target ids is taken here.)
+
+Sampling acceptance (snxtyle/P_Eagle README, "How Speculative Decoding Works", step 6:
+accepted tokens are used, rejected tokens resampled), read as speculative sampling:
+p = softmax(target logits / tau) and q = softmax(draft logits / tau) at each depth; the
+drafter's token x_d (sampled from q, an input here) is accepted while u_d < p(x_d) / q(x_d)
+for the given uniforms u_d; at the first rejected depth j the next token is drawn from
+the residual max(0, p_j - q_j) (normalised) by inverse CDF: the smallest t whose
+cumulative residual exceeds w * Z, Z the residual's total, w a given uniform. When all K
+depths are accepted the next token is -1 (its bonus draw needs a K+1-th target row, which
+this interface does not take).
 """
 from __future__ import annotations
 
@@ -58,3 +68,40 @@ def verify_d2t(draft_logits, target_logits, d2t) -> dict:
     b = argmax_rows(target_logits)
     mapped = np.asarray(d2t, dtype=np.int64)[a]
     return dict(draft_tok=a, target_tok=b, accept_len=accept_lengths(mapped, b))
+
+
+def softmax_f64(logits_bits, tau: float) -> np.ndarray:
+    x = to_f32(logits_bits).astype(np.float64) / float(tau)
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def residual_f64(draft_row_bits, target_row_bits, tau: float) -> np.ndarray:
+    """max(0, p - q) of one depth (unnormalised)."""
+    return np.maximum(0.0, softmax_f64(target_row_bits, tau) - softmax_f64(draft_row_bits, tau))
+
+
+def speculative_accept(draft_logits, target_logits, draft_tok, u, w, tau: float = 1.0) -> dict:
+    """draft_logits, target_logits [N, K, V] bf16 bits; draft_tok int [N, K]; u [N, K] and
+    w [N] uniforms in [0, 1). Returns accept_len [N], next_tok [N] and the ratios
+    p(x_d) / q(x_d) [N, K]."""
+    N, K, V = draft_logits.shape
+    ratio = np.empty((N, K), dtype=np.float64)
+    accept = np.empty(N, dtype=np.int32)
+    nxt = np.full(N, -1, dtype=np.int32)
+    for i in range(N):
+        for d in range(K):
+            x = int(draft_tok[i, d])
+            p = softmax_f64(target_logits[i, d], tau)[x]
+            q = softmax_f64(draft_logits[i, d], tau)[x]
+            ratio[i, d] = p / q
+        L = 0
+        while L < K and u[i, L] < ratio[i, L]:
+            L += 1
+        accept[i] = L
+        if L < K:
+            r = residual_f64(draft_logits[i, L], target_logits[i, L], tau)
+            c = np.cumsum(r)
+            nxt[i] = int(np.searchsorted(c, w[i] * c[-1], side="right"))
+    return dict(accept_len=accept, next_tok=nxt, ratio=ratio)

@@ -165,3 +165,76 @@ def test_fc_norm_is_rmsnorm_of_the_projection():
     T = len(sel["idx"])
     assert np.all(normed["hidden"][n:] == normed["hidden"][n])
     assert T > n
+
+
+def _spec_inputs(rng, N, K, V, plant=0.0):
+    dl = rng.standard_normal((N, K, V)).astype(np.float32)
+    tl = rng.standard_normal((N, K, V)).astype(np.float32)
+    tok = rng.integers(0, V, (N, K))
+    if plant:
+        for i in range(N):
+            for d in range(K):
+                if rng.random() < plant:
+                    dl[i, d, tok[i, d]] += 3.0
+                    tl[i, d, tok[i, d]] += 3.0
+    return _f32_to_bits(dl), _f32_to_bits(tl), tok
+
+
+def test_speculative_sampling_emits_the_target_distribution():
+    """The defining property: with x ~ q, the token emitted at one depth (x if accepted, the
+    residual draw otherwise) is distributed as p. Monte Carlo over 60000 draws, chi-square
+    against p (the statistic's 99.99% quantile for 5 degrees of freedom is ~25.7)."""
+    rng = np.random.default_rng(11)
+    V, tau, M = 6, 0.8, 60000
+    dl, tl, _ = _spec_inputs(rng, 1, 1, V)
+    q = verify.softmax_f64(dl[0, 0], tau)
+    p = verify.softmax_f64(tl[0, 0], tau)
+    xs = rng.choice(V, size=M, p=q)
+    u, w = rng.random(M), rng.random(M)
+    res = verify.residual_f64(dl[0, 0], tl[0, 0], tau)
+    c = np.cumsum(res)
+    ratio = p[xs] / q[xs]
+    emitted = np.where(u < ratio, xs, np.searchsorted(c, w * c[-1], side="right"))
+    counts = np.bincount(emitted, minlength=V)
+    chi2 = float(np.sum((counts - M * p) ** 2 / (M * p)))
+    assert chi2 < 25.7, chi2
+    # and the oracle's per-draft function takes the same decisions as this vectorised form
+    out = verify.speculative_accept(np.repeat(dl, 50, 0), np.repeat(tl, 50, 0), xs[:50, None],
+                                    u[:50, None], w[:50], tau)
+    assert np.array_equal(out["accept_len"], (u[:50] < ratio[:50]).astype(np.int32))
+    rej = u[:50] >= ratio[:50]
+    assert np.array_equal(out["next_tok"][rej], emitted[:50][rej])
+    assert (out["next_tok"][~rej] == -1).all()
+
+
+def test_speculative_identical_distributions_accept_everything():
+    rng = np.random.default_rng(12)
+    dl, _, tok = _spec_inputs(rng, 20, 5, 40)
+    out = verify.speculative_accept(dl, dl, tok, rng.random((20, 5)), rng.random(20), 1.3)
+    np.testing.assert_allclose(out["ratio"], 1.0, rtol=1e-12)
+    assert (out["accept_len"] == 5).all() and (out["next_tok"] == -1).all()
+
+
+def test_speculative_prefix_rule_and_residual_support():
+    """accept_len is the first depth whose u reaches its ratio; a resampled token always has
+    positive residual mass."""
+    rng = np.random.default_rng(13)
+    N, K, V = 300, 4, 30
+    dl, tl, tok = _spec_inputs(rng, N, K, V, plant=0.6)
+    u, w = rng.random((N, K)), rng.random(N)
+    out = verify.speculative_accept(dl, tl, tok, u, w, 1.0)
+    for i in range(N):
+        L = out["accept_len"][i]
+        assert (u[i, :L] < out["ratio"][i, :L]).all()
+        if L < K:
+            assert u[i, L] >= out["ratio"][i, L]
+            assert verify.residual_f64(dl[i, L], tl[i, L], 1.0)[out["next_tok"][i]] > 0
+    assert 0 < (out["accept_len"] == K).sum() < N
+
+
+def test_softmax_temperature_closed_form():
+    # logits 0 and 1 (exact in bf16): tau = 1 -> e^1 / (1 + e^1); tau = 0.5 -> e^2 / (1 + e^2)
+    bits = _f32_to_bits(np.array([0.0, 1.0]))
+    np.testing.assert_allclose(verify.softmax_f64(bits, 1.0)[1], np.e / (1 + np.e), rtol=1e-14)
+    np.testing.assert_allclose(verify.softmax_f64(bits, 0.5)[1], np.e ** 2 / (1 + np.e ** 2),
+                               rtol=1e-14)
