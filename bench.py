@@ -243,6 +243,7 @@ def main():
     result["fuse_fc_norm"] = {"ms_per_call": round(ms_fcn, 4),
                               "ms_without_fc_norm": round(stage_ms["fuse_inputs"], 4)}
     result["verify_d2t"] = verify_d2t_bench(args.steps, args.warmup)
+    result["verify_sampled"] = verify_sampled_bench(args.steps, args.warmup)
     result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, hidden, emb, out,
                                         args.steps, args.warmup)
 
@@ -309,6 +310,28 @@ def verify_d2t_bench(steps, warmup, N=4096, K=8, Vd=8192, Vt=32000):
     torch.cuda.empty_cache()
     return {"drafts": N, "K": K, "draft_vocab": Vd, "target_vocab": Vt, "ms_per_call": round(ms, 4),
             "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def verify_sampled_bench(steps, warmup, N=4096, K=8, V=32000):
+    """Time peagle_accept_sampled (speculative-sampling verification) on 4096 drafts of
+    K = 8 over a 32000-id vocabulary, inputs of the seeded recipe drawn on the device.
+    Algorithmic bytes: both logit tensors read once plus the per-depth inputs and outputs;
+    the kernel also re-reads the row pair of the rejected depth (residual draw)."""
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    d = synth.sampled_verify_inputs_device(41, N, K, V)
+    alen = torch.empty(N, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(N, dtype=torch.int32, device="cuda")
+    ms = _time_calls(lambda: peagle.accept_sampled(d["draft_logits"], d["target_logits"],
+                                                   d["draft_tok"], d["u"], d["w"], 1.0, alen,
+                                                   nxt), steps, warmup)
+    rejected = int((alen < K).sum())
+    nbytes = N * K * V * 2 * 2 + N * K * 8 + N * 12
+    del d
+    torch.cuda.empty_cache()
+    return {"drafts": N, "K": K, "vocab": V, "rejected_drafts": rejected,
+            "ms_per_call": round(ms, 4), "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def _time_calls(call, steps, warmup):

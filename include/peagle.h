@@ -9,7 +9,8 @@
  *        parallel-drafting training for EAGLE-3 drafts": the PR description
  *        (implementation, checkpoint contract, parity section) and the commit message
  *        of the RoPE fix.
- *   [R]  snxtyle/P_Eagle README: packed conversations isolated by cu_seqlens.
+ *   [R]  snxtyle/P_Eagle README: packed conversations isolated by cu_seqlens; section
+ *        "How Speculative Decoding Works" (accepted tokens kept, rejected ones resampled).
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host). The caller owns all memory;
@@ -221,6 +222,35 @@ int peagle_accept_prefix_d2t(int32_t num_drafts, int32_t K, int32_t draft_vocab,
                              const peagle_bf16 *target_logits, const int32_t *d2t,
                              int32_t *draft_tok, int32_t *target_tok, int32_t *accept_len,
                              void *stream);
+
+/*
+ * peagle_accept_sampled -- verification of sampled drafts [R, "How Speculative Decoding
+ * Works", step 6: accepted draft tokens are kept, a rejected one is resampled], read as
+ * speculative sampling. At depth d, p = softmax(target_logits[i, d] / tau) and
+ * q = softmax(draft_logits[i, d] / tau); the drafter's token x_d is accepted while
+ * u[i, d] * q(x_d) < p(x_d) (u < p / q), and accept_len[i] is the number of leading
+ * accepted depths. At the first rejected depth L the next token is drawn from the
+ * residual r = max(0, p - q): the smallest t whose running sum r_0 + .. + r_t exceeds
+ * w[i] * (r_0 + .. + r_{V-1}). With all K accepted, next_tok[i] = -1.
+ *   draft_logits, target_logits  bf16[N, K, V]  shared vocabulary
+ *   draft_tok     int32[N, K]   the drafter's sampled tokens; one outside [0, V) is
+ *                               rejected
+ *   u             fp32[N, K]    uniforms in [0, 1), one per depth (acceptance)
+ *   w             fp32[N]       uniforms in [0, 1), one per draft (the residual draw)
+ *   temperature   tau > 0 (host)
+ *   accept_len    int32[N] out
+ *   next_tok      int32[N] out  the resampled token, or -1
+ * Arithmetic is fp32: a decision whose float64 margin (|u q - p|, or the distance of
+ * w * Z to a boundary of the running sum) is below fp32 rounding may differ from a
+ * float64 evaluation; the resampled token always has positive fp32 residual weight.
+ * 1 <= K <= PEAGLE_MAX_DEPTHS, V >= 1; with num_drafts = 0 nothing is read and the
+ * pointers may be NULL.
+ */
+int peagle_accept_sampled(int32_t num_drafts, int32_t K, int32_t vocab,
+                          const peagle_bf16 *draft_logits, const peagle_bf16 *target_logits,
+                          const int32_t *draft_tok, const float *u, const float *w,
+                          float temperature, int32_t *accept_len, int32_t *next_tok,
+                          void *stream);
 
 /*
  * The first draft decoder layer's attention inputs [R, "How Speculative Decoding Works",

@@ -83,3 +83,55 @@ def sample_rows(depth_off, cu_seqlens, idx, count=96, seed=0) -> np.ndarray:
         rows.update(hit.tolist())
     rows.update(rng.integers(0, T, size=count).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
+
+
+# Sampling verification decides integers from fp32 arithmetic. A depth's decision is
+# compared with float64 unless u lies within SPEC_RATIO_TOL (relative) of p / q, and the
+# resampled token unless w * Z lies within SPEC_CDF_TOL (absolute, probability units) of a
+# boundary of the residual's running sum; inside those windows either side is valid.
+SPEC_RATIO_TOL = 1e-4
+SPEC_CDF_TOL = 1e-5
+
+
+def check_sampled(inp: dict, tau: float, got_len, got_next, ratio_tol=SPEC_RATIO_TOL,
+                  cdf_tol=SPEC_CDF_TOL, drafts=None) -> dict:
+    """Check accept_len / next_tok of sampling verification against the float64 oracle on
+    the drafts listed (all by default). Exact wherever the oracle's decisions are clear of
+    the windows above; elsewhere the kernel's decisions must lie inside them. Returns
+    counts and the largest miss of each kind (0 for a decision the oracle shares)."""
+    from oracle import verify as over
+    dl, tl, tok = inp["draft_logits"], inp["target_logits"], inp["draft_tok"]
+    u = np.asarray(inp["u"], dtype=np.float64)
+    w = np.asarray(inp["w"], dtype=np.float64)
+    N, K, V = dl.shape
+    drafts = range(N) if drafts is None else drafts
+    sub = [int(i) for i in drafts]
+    want = over.speculative_accept(dl[sub], tl[sub], tok[sub], u[sub], w[sub], tau)
+    stats = dict(drafts=len(sub), exact=0, ratio_miss=0.0, cdf_miss=0.0, rejected=0)
+    for j, i in enumerate(sub):
+        L, t = int(got_len[i]), int(got_next[i])
+        assert 0 <= L <= K, f"draft {i}: accept_len {L} outside [0, {K}]"
+        ratio = want["ratio"][j]
+        for d in range(L):  # accepted: u < ratio, up to the window
+            miss = max(0.0, u[i, d] - ratio[d]) / max(ratio[d], 1e-300)
+            stats["ratio_miss"] = max(stats["ratio_miss"], miss)
+            assert miss <= ratio_tol, f"draft {i} depth {d}: accepted with u {u[i, d]} >= ratio {ratio[d]}"
+        if L == K:
+            assert t == -1, f"draft {i}: all {K} accepted but next_tok {t}"
+        else:
+            stats["rejected"] += 1
+            miss = max(0.0, ratio[L] - u[i, L]) / max(ratio[L], 1e-300)
+            stats["ratio_miss"] = max(stats["ratio_miss"], miss)
+            assert miss <= ratio_tol, f"draft {i} depth {L}: rejected with u {u[i, L]} < ratio {ratio[L]}"
+            assert 0 <= t < V, f"draft {i}: next_tok {t} outside [0, {V})"
+            c = np.cumsum(over.residual_f64(dl[i, L], tl[i, L], tau))
+            theta = w[i] * c[-1]
+            lo = c[t - 1] if t > 0 else 0.0
+            # token t owns the running sums in [lo, c[t]); theta must fall inside
+            miss = max(0.0, lo - theta, theta - c[t] if c[t] <= theta else 0.0)
+            stats["cdf_miss"] = max(stats["cdf_miss"], miss)
+            assert miss <= cdf_tol, (f"draft {i} depth {L}: token {t} spans "
+                                     f"[{lo:.9g}, {c[t]:.9g}) but w*Z = {theta:.9g}")
+        if L == int(want["accept_len"][j]) and t == int(want["next_tok"][j]):
+            stats["exact"] += 1
+    return stats

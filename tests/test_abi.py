@@ -127,6 +127,18 @@ def test_rope_and_accept_argument_errors(lib):
                  None) == peagle.ERR_ARG
     assert _code("peagle_accept_prefix_d2t", 4, 8, 0, 200, None, None, None, None, None, None,
                  None) == peagle.ERR_ARG
+    # sampling verification: null pointers, K beyond 64, empty vocabulary, tau <= 0 or NaN
+    fake = 1 << 20  # never dereferenced: every call below fails its host checks
+    for args in ((4, 8, 100, None, None, None, None, None, 1.0, None, None),
+                 (4, 65, 100, fake, fake, fake, fake, fake, 1.0, fake, fake),
+                 (4, 8, 0, fake, fake, fake, fake, fake, 1.0, fake, fake),
+                 (4, 8, 100, fake, fake, fake, fake, fake, 0.0, fake, fake),
+                 (4, 8, 100, fake, fake, fake, fake, fake, -1.0, fake, fake),
+                 (4, 8, 100, fake, fake, fake, fake, fake, float("nan"), fake, fake),
+                 (-1, 8, 100, fake, fake, fake, fake, fake, 1.0, fake, fake)):
+        assert _code("peagle_accept_sampled", *args, None) == peagle.ERR_ARG, args
+    assert _code("peagle_accept_sampled", 0, 8, 100, None, None, None, None, None, 1.0, None,
+                 None, None) == peagle.OK
 
 
 def test_workspace_bytes(lib):

@@ -423,4 +423,19 @@ int peagle_accept_prefix_d2t(int32_t num_drafts, int32_t K, int32_t draft_vocab,
                                      static_cast<hipStream_t>(stream)));
 }
 
+int peagle_accept_sampled(int32_t num_drafts, int32_t K, int32_t vocab,
+                          const peagle_bf16* draft_logits, const peagle_bf16* target_logits,
+                          const int32_t* draft_tok, const float* u, const float* w,
+                          float temperature, int32_t* accept_len, int32_t* next_tok,
+                          void* stream) {
+  if (num_drafts < 0 || K < 1 || K > PEAGLE_MAX_DEPTHS || vocab < 1) return PEAGLE_ERR_ARG;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return PEAGLE_ERR_ARG;
+  if (num_drafts == 0) return PEAGLE_OK;  // nothing is read: empty tensors may be null
+  if (!draft_logits || !target_logits || !draft_tok || !u || !w || !accept_len || !next_tok)
+    return PEAGLE_ERR_ARG;
+  return status_of(launch_accept_sampled(num_drafts, K, vocab, draft_logits, target_logits,
+                                         draft_tok, u, w, temperature, accept_len, next_tok,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -50,6 +50,7 @@ SIGNATURES = {
     "peagle_fuse_inputs_fc_norm": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32,
                                     _i32, _p, _f32, _p, _p, _p], _i32),
     "peagle_accept_prefix_d2t": ([_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p], _i32),
+    "peagle_accept_sampled": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _f32, _p, _p, _p], _i32),
     "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
     "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32], _sz),
@@ -244,6 +245,29 @@ def accept_prefix_d2t(draft_logits, target_logits, d2t, draft_tok=None, target_t
         N, K, Vd, Vt, _ptr(draft_logits), _ptr(target_logits), _ptr(d2t), _ptr(draft_tok),
         _ptr(target_tok), _ptr(accept_len), _stream()))
     return draft_tok, target_tok, accept_len
+
+
+def accept_sampled(draft_logits, target_logits, draft_tok, u, w, temperature=1.0,
+                   accept_len=None, next_tok=None):
+    """Speculative-sampling verification of sampled drafts: accept_len [N] and the token
+    drawn from the residual at the first rejected depth (next_tok [N], -1 when all K are
+    accepted). draft_tok int32 [N, K]; u fp32 [N, K] and w fp32 [N] uniforms in [0, 1)."""
+    for t, name in ((draft_logits, "draft_logits"), (target_logits, "target_logits"),
+                    (draft_tok, "draft_tok"), (u, "u"), (w, "w")):
+        _dev(t, name)
+    N, K, V = draft_logits.shape
+    if tuple(target_logits.shape) != (N, K, V) or tuple(draft_tok.shape) != (N, K) \
+            or tuple(u.shape) != (N, K) or tuple(w.shape) != (N,):
+        raise ValueError("accept_sampled: shapes do not match [N, K, V] logits")
+    dev = draft_logits.device
+    if accept_len is None:
+        accept_len = torch.empty(N, dtype=torch.int32, device=dev)
+    if next_tok is None:
+        next_tok = torch.empty(N, dtype=torch.int32, device=dev)
+    _check("peagle_accept_sampled", lib().peagle_accept_sampled(
+        N, K, V, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tok), _ptr(u), _ptr(w),
+        float(temperature), _ptr(accept_len), _ptr(next_tok), _stream()))
+    return accept_len, next_tok
 
 
 # ---------------------------------------------------------------- first draft layer

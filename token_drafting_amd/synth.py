@@ -30,6 +30,7 @@ TAG_NORM_EMB, TAG_NORM_HID, TAG_WQKV, TAG_L1_HID, TAG_L1_EMB = 16, 17, 18, 19, 2
 TAG_WO, TAG_NORM_POST, TAG_WGATE, TAG_WUP, TAG_WDOWN, TAG_NORM_FINAL, TAG_WHEAD, TAG_ATTN = (
     21, 22, 23, 24, 25, 26, 27, 28)
 TAG_D2T, TAG_FC_NORM = 29, 30
+TAG_SPEC_LOGITS, TAG_SPEC_TOK, TAG_SPEC_U, TAG_SPEC_W = 31, 32, 33, 34
 
 # Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
 # layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
@@ -309,3 +310,68 @@ def fc_norm_weight(seed: int, H: int) -> np.ndarray:
     """bf16 bits of 1 + N(0, 0.1^2): the RMSNorm weight after fc (near its unit init)."""
     x = 1.0 + 0.1 * _rng(seed, TAG_FC_NORM).standard_normal(H, dtype=np.float32)
     return f32_to_bf16_bits(x.astype(np.float32))
+
+
+def sampled_verify_inputs(seed: int, drafts: int, K: int, V: int, spread: float = 2.0,
+                          noise: float = 0.5, chunk: int = 64) -> dict:
+    """Inputs of sampling verification: draft and target logits [drafts, K, V] (bf16 bits)
+    that share a N(0, spread^2) base and differ by independent N(0, noise^2) terms; one
+    drafted token per row, uniform over the vocabulary, whose draft logit is raised by
+    b ~ U(0, 6) and target logit by b + N(0, 1) so the acceptance ratios spread around 1;
+    uniforms u [drafts, K] and w [drafts] (float32, in [0, 1))."""
+    rng = _rng(seed, TAG_SPEC_LOGITS)
+    draft = np.empty((drafts, K, V), dtype=np.uint16)
+    target = np.empty((drafts, K, V), dtype=np.uint16)
+    trng = _rng(seed, TAG_SPEC_TOK)
+    tok = trng.integers(0, V, size=(drafts, K)).astype(np.int32)
+    b_d = trng.uniform(0.0, 6.0, size=(drafts, K)).astype(np.float32)
+    b_t = (b_d + trng.standard_normal((drafts, K))).astype(np.float32)
+    for lo in range(0, drafts, chunk):
+        hi = min(drafts, lo + chunk)
+        shape = (hi - lo, K, V)
+        base = spread * rng.standard_normal(shape, dtype=np.float32)
+        dl = base + noise * rng.standard_normal(shape, dtype=np.float32)
+        tl = base + noise * rng.standard_normal(shape, dtype=np.float32)
+        ii, dd = np.meshgrid(np.arange(hi - lo), np.arange(K), indexing="ij")
+        dl[ii, dd, tok[lo:hi]] += b_d[lo:hi]
+        tl[ii, dd, tok[lo:hi]] += b_t[lo:hi]
+        draft[lo:hi] = f32_to_bf16_bits(dl)
+        target[lo:hi] = f32_to_bf16_bits(tl)
+    u = _rng(seed, TAG_SPEC_U).random((drafts, K), dtype=np.float32)
+    w = _rng(seed, TAG_SPEC_W).random(drafts, dtype=np.float32)
+    return dict(draft_logits=draft, target_logits=target, draft_tok=tok, u=u, w=w)
+
+
+def sampled_verify_inputs_device(seed: int, drafts: int, K: int, V: int, spread: float = 2.0,
+                                 noise: float = 0.5, device="cuda") -> dict:
+    """The recipe of sampled_verify_inputs drawn on the device with torch's seeded
+    generator (gigabytes of logits at full size). Logits as int16 bf16 bit patterns."""
+    import torch
+
+    def gen(tag):
+        g = torch.Generator(device=device)
+        g.manual_seed(int(seed) * 1000003 + tag)
+        return g
+
+    g_tok, g_log = gen(TAG_SPEC_TOK), gen(TAG_SPEC_LOGITS)
+    tok = torch.randint(0, V, (drafts, K), generator=g_tok, device=device, dtype=torch.int32)
+    b_d = 6.0 * torch.rand((drafts, K), generator=g_tok, device=device)
+    b_t = b_d + torch.randn((drafts, K), generator=g_tok, device=device)
+    draft = torch.empty((drafts, K, V), dtype=torch.int16, device=device)
+    target = torch.empty_like(draft)
+    rows = max(1, (1 << 25) // (K * V))
+    for lo in range(0, drafts, rows):
+        hi = min(drafts, lo + rows)
+        shape = (hi - lo, K, V)
+        base = spread * torch.randn(shape, generator=g_log, device=device)
+        dl = base + noise * torch.randn(shape, generator=g_log, device=device)
+        tl = base + noise * torch.randn(shape, generator=g_log, device=device)
+        idx = tok[lo:hi].long().unsqueeze(-1)
+        dl.scatter_add_(2, idx, b_d[lo:hi].unsqueeze(-1))
+        tl.scatter_add_(2, idx, b_t[lo:hi].unsqueeze(-1))
+        draft[lo:hi] = dl.to(torch.bfloat16).view(torch.int16)
+        target[lo:hi] = tl.to(torch.bfloat16).view(torch.int16)
+        del base, dl, tl
+    u = torch.rand((drafts, K), generator=gen(TAG_SPEC_U), device=device)
+    w = torch.rand(drafts, generator=gen(TAG_SPEC_W), device=device)
+    return dict(draft_logits=draft, target_logits=target, draft_tok=tok, u=u, w=w)
