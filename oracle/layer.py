@@ -1,5 +1,5 @@
-"""The first draft decoder layer (oracle): attention inputs, attention, output projection,
-MLP and the draft-vocab head.
+"""The draft decoder layers (oracle): the first layer's attention inputs, attention, output
+projection and MLP, the layers stacked after it, and the draft-vocab head.
 
 TEST INFRASTRUCTURE ONLY (see the package header).
 
@@ -31,6 +31,11 @@ Readings (the pages name the pieces, not their formulas):
   normalization before the residual connection, so by default the residual stream starts
   from the normalised hidden state, r = rms(hidden; w_hidden); with the flag off it is the
   raw hidden state.
+- Layers stacked after the first (speculators guide, "Key Parameters": the number of
+  decoder layers is a parameter) are plain Llama decoder layers on the draft rows: the
+  residual stream h is the previous layer's h2, x = rms(h; w_norm), q, k, v = x W_qkv^T
+  (W_qkv of shape ((Hq + 2 Hkv) D, H)), the same RoPE, rows and attention predicate as the
+  first layer, then h1 = h + o W_o^T and the same MLP. The head reads the last layer's h2.
 - The draft-vocab head: logits = rms(h2; w_final) W_head^T (NeMo PR 2376: the P-EAGLE
   trainer shares EAGLE-3's draft-vocab projection); the draft token of a row is its
   argmax, lowest index on ties.
@@ -117,3 +122,46 @@ def layer1_forward_f64(hidden, embed, w: dict, idx, depth_off, cu_seqlens, theta
     head = draft_head_f64(post["h2"], w["w_final"], w["w_head"], eps)
     return dict(q=qkv["q"], k=qkv["k"], v=qkv["v"], attn=att["out"], h1=post["h1"],
                 h2=post["h2"], logits=head["logits"], tokens=head["tokens"])
+
+
+def layer_qkv_f64(h, w_norm, w_qkv, Hq: int, Hkv: int, D: int, eps: float = EPS) -> dict:
+    """A stacked layer's attention inputs: h [T, H] (the residual stream); w_norm [H];
+    w_qkv [(Hq + 2 Hkv) D, H]. Returns q [T, Hq, D], k and v [T, Hkv, D] before RoPE."""
+    y = rms_norm(h, w_norm, eps) @ np.asarray(w_qkv, np.float64).T
+    T = y.shape[0]
+    return dict(q=y[:, :Hq * D].reshape(T, Hq, D),
+                k=y[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D),
+                v=y[:, (Hq + Hkv) * D:].reshape(T, Hkv, D))
+
+
+def layer_forward_f64(h, w: dict, idx, depth_off, cu_seqlens, theta: float, Hq: int, Hkv: int,
+                      D: int, eps: float = EPS, rows=None) -> dict:
+    """One stacked layer on float64 arrays. w holds w_norm, w_qkv, w_o, w_post, w_gate,
+    w_up, w_down. rows: optional subset of rows whose outputs are wanted."""
+    from .attention import draft_attention_f64
+
+    h = np.asarray(h, np.float64)
+    qkv = layer_qkv_f64(h, w["w_norm"], w["w_qkv"], Hq, Hkv, D, eps)
+    att = draft_attention_f64(qkv["q"], qkv["k"], qkv["v"], idx, depth_off, cu_seqlens, theta,
+                              rows=rows)
+    sel = np.arange(len(h)) if rows is None else np.asarray(rows)
+    post = post_attention_f64(att["out"], h[sel], w["w_o"], w["w_post"], w["w_gate"], w["w_up"],
+                              w["w_down"], eps)
+    return dict(q=qkv["q"], k=qkv["k"], v=qkv["v"], attn=att["out"], h1=post["h1"],
+                h2=post["h2"])
+
+
+def stack_forward_f64(hidden, embed, w_first: dict, w_layers, idx, depth_off, cu_seqlens,
+                      theta: float, Hq: int, Hkv: int, D: int, eps: float = EPS,
+                      norm_before_residual: bool = True) -> dict:
+    """The first layer, then each stacked layer of w_layers in order, then the head
+    (w_final, w_head of w_first). Returns every layer's h2 and the head's logits and
+    tokens."""
+    first = layer1_forward_f64(hidden, embed, w_first, idx, depth_off, cu_seqlens, theta, Hq, Hkv,
+                               D, eps, norm_before_residual)
+    hs = [first["h2"]]
+    for wl in w_layers:
+        hs.append(layer_forward_f64(hs[-1], wl, idx, depth_off, cu_seqlens, theta, Hq, Hkv, D,
+                                    eps)["h2"])
+    head = draft_head_f64(hs[-1], w_first["w_final"], w_first["w_head"], eps)
+    return dict(h=hs, logits=head["logits"], tokens=head["tokens"])

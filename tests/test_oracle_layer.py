@@ -183,3 +183,94 @@ def test_head_argmax_lowest_index_on_ties():
     want = np.where(nh[:, 3] >= np.maximum(nh[:, 1], 0.0), 2, np.where(nh[:, 1] > 0.0, 4, 0))
     np.testing.assert_allclose(out["logits"][:, 2], nh[:, 3], rtol=2e-6)
     assert np.array_equal(out["tokens"], want)
+
+
+def _stacked_weights(rng, H, I, Hq, Hkv, D):
+    return dict(w_norm=1 + 0.1 * rng.standard_normal(H),
+                w_qkv=rng.standard_normal(((Hq + 2 * Hkv) * D, H)) / np.sqrt(H),
+                w_o=rng.standard_normal((H, Hq * D)) / np.sqrt(Hq * D),
+                w_post=1 + 0.1 * rng.standard_normal(H),
+                w_gate=rng.standard_normal((I, H)) / np.sqrt(H),
+                w_up=rng.standard_normal((I, H)) / np.sqrt(H),
+                w_down=rng.standard_normal((H, I)) / np.sqrt(I))
+
+
+def _as_first_layer_weights(w, H):
+    """The stacked layer's weights in the first layer's slots, the embedding half of
+    W_qkv zero, so that (with the raw residual) the first layer computes the same layer."""
+    w1 = dict(w)
+    w1["w_norm_hidden"] = w["w_norm"]
+    w1["w_norm_emb"] = np.ones(H)
+    w1["w_qkv"] = np.concatenate([np.zeros_like(w["w_qkv"]), w["w_qkv"]], axis=1)
+    return w1
+
+
+def _multi_depth_layout(cu, R):
+    """Draft rows of nested retained sets R[d] (R[0] = every position); returns idx,
+    depth_off and, per row, its depth, anchor and position value p - a_s + d."""
+    idx = np.concatenate([np.asarray(r, dtype=np.int64) for r in R])
+    depth_off = np.concatenate([[0], np.cumsum([len(r) for r in R])])
+    depth = np.concatenate([np.full(len(r), d) for d, r in enumerate(R)])
+    start = np.asarray(cu)[np.searchsorted(cu, idx, side="right") - 1]
+    return idx, depth_off, depth, idx - start + depth, start
+
+
+@pytest.mark.parametrize("cu,R", [
+    ([0, 12], [range(12), [1, 4, 5, 9, 11], [4, 9]]),
+    ([0, 5, 12], [range(12), [0, 3, 4, 6, 10, 11], [3, 6, 11], [6]]),
+])
+def test_stacked_layer_matches_llama_decoder_layer_with_depth_mask(cu, R):
+    """A stacked layer is a Llama decoder layer over the draft rows, with RoPE at the rows'
+    position values and, as its attention mask, the multi-depth predicate written out
+    here pair by pair: row (d, p) sees depth-0 rows of its own sequence at p' <= p and the
+    rows (d', p) of its own anchor for 1 <= d' <= d."""
+    H, I, Hq, Hkv, D, theta = 32, 48, 4, 2, 8, 1e4
+    rng = np.random.default_rng(len(R))
+    w = _stacked_weights(rng, H, I, Hq, Hkv, D)
+    idx, depth_off, depth, pos, start = _multi_depth_layout(cu, R)
+    T = len(idx)
+    h = rng.standard_normal((T, H))
+    got = layer.layer_forward_f64(h, w, idx, depth_off, np.asarray(cu), theta, Hq, Hkv, D)
+    allowed = np.zeros((T, T), dtype=bool)
+    for r in range(T):
+        for c in range(T):
+            same_seq = start[c] == start[r]
+            allowed[r, c] = (depth[c] == 0 and same_seq and idx[c] <= idx[r]) or \
+                (idx[c] == idx[r] and 1 <= depth[c] <= depth[r])
+    w1 = _as_first_layer_weights(w, H)
+    lay, rot = _llama_layer(H, I, Hq, Hkv, D, theta, 1e-6, w1)
+    x = torch.from_numpy(h)[None]
+    p = torch.from_numpy(pos)[None]
+    mask = torch.from_numpy(np.where(allowed, 0.0, -np.inf))[None, None]
+    with torch.no_grad():
+        want = lay(x, attention_mask=mask, position_ids=p, position_embeddings=rot(x, p))[0].numpy()
+    np.testing.assert_allclose(got["h2"], want, rtol=0, atol=2e-6 * np.abs(want).max())
+
+
+def test_stack_matches_llama_layers_in_sequence():
+    """K = 1 and the first layer reduced to a plain Llama layer (embedding half of W_qkv
+    zero, raw residual): the draft stack is transformers' decoder layers applied in turn,
+    then RMSNorm and the head's argmax."""
+    n, H, I, Hq, Hkv, D, theta, V = 10, 32, 48, 4, 2, 8, 1e4, 13
+    rng = np.random.default_rng(7)
+    ws = [_stacked_weights(rng, H, I, Hq, Hkv, D) for _ in range(3)]
+    w1 = _as_first_layer_weights(ws[0], H)
+    w1["w_final"] = 1 + 0.1 * rng.standard_normal(H)
+    w1["w_head"] = rng.standard_normal((V, H)) / np.sqrt(H)
+    hidden, embed = rng.standard_normal((n, H)), rng.standard_normal((n, H))
+    idx, depth_off, cu = np.arange(n), np.array([0, n]), np.array([0, n])
+    got = layer.stack_forward_f64(hidden, embed, w1, ws[1:], idx, depth_off, cu, theta, Hq, Hkv,
+                                  D, norm_before_residual=False)
+    x = torch.from_numpy(hidden)[None]
+    pos = torch.arange(n)[None]
+    mask = torch.triu(torch.full((n, n), float("-inf"), dtype=torch.float64), 1)[None, None]
+    with torch.no_grad():
+        for wl in ws:
+            lay, rot = _llama_layer(H, I, Hq, Hkv, D, theta, 1e-6, _as_first_layer_weights(wl, H))
+            y = lay(x, attention_mask=mask, position_ids=pos, position_embeddings=rot(x, pos))
+            x = y[0] if isinstance(y, tuple) else y     # [1, n, H] either way
+    want_h = x[0].numpy()
+    assert len(got["h"]) == 3
+    np.testing.assert_allclose(got["h"][-1], want_h, rtol=0, atol=2e-6 * np.abs(want_h).max())
+    norm = want_h / np.sqrt(np.mean(want_h ** 2, axis=-1, keepdims=True) + 1e-6) * w1["w_final"]
+    np.testing.assert_array_equal(got["tokens"], np.argmax(norm @ w1["w_head"].T, axis=-1))
