@@ -382,6 +382,20 @@ def layer_bench(cfg_id, cfg, seed, n, K, T, hidden, emb, attn_out, steps, warmup
     ms_head = _time_calls(lambda: peagle.draft_head(h2, dw["w_final"], dw["w_head"],
                                                     tokens=tokens, workspace=ws_head),
                           steps, warmup)
+    # a stacked (2nd) layer on the first layer's output: every row projected
+    w2 = {k2: torch.from_numpy(v2.view(np.int16)).to(dev)
+          for k2, v2 in synth.stacked_layer_weights(seed, 2, H, Hq, Hkv, D, I).items()}
+    ws2_qkv = torch.empty(int(peagle.lib().peagle_layer_qkv_workspace_bytes(T, H)),
+                          dtype=torch.uint8, device=dev)
+    ws2_post = torch.empty(int(peagle.lib().peagle_layer_post_workspace_bytes(T, H, QW, I)),
+                           dtype=torch.uint8, device=dev)
+    h3 = torch.empty_like(h2)
+    ms_qkv2 = _time_calls(lambda: peagle.layer_qkv(h2, w2["w_norm"], w2["w_qkv"], Hq, Hkv, D, q=q,
+                                                   k=k, v=v, workspace=ws2_qkv), steps, warmup)
+    ms_post2 = _time_calls(lambda: peagle.layer_post(attn_out, h2, w2["w_o"], w2["w_post"],
+                                                     w2["w_gate"], w2["w_up"], w2["w_down"],
+                                                     h2=h3, workspace=ws2_post), steps, warmup)
+    del w2, ws2_qkv, ws2_post, h3
     M = n + 1 if T > n else n
     f_qkv = 2.0 * M * (Hq + 2 * Hkv) * D * 2 * H
     f_post = 2.0 * T * H * (QW + 3 * I)
@@ -397,7 +411,12 @@ def layer_bench(cfg_id, cfg, seed, n, K, T, hidden, emb, attn_out, steps, warmup
                      "ms_per_call": round(ms_post, 4), "tflops": tf(f_post, ms_post)},
             "head": {"gemm": f"{T}x{V}x{H} with fused argmax", "ms_per_call": round(ms_head, 4),
                      "tflops": tf(f_head, ms_head)},
-            "layer_ms_excluding_attention": round(ms_qkv + ms_post + ms_head, 4)}
+            "layer_ms_excluding_attention": round(ms_qkv + ms_post + ms_head, 4),
+            "stacked_layer": {
+                "qkv": {"gemm": f"{T}x{(Hq + 2 * Hkv) * D}x{H}", "ms_per_call": round(ms_qkv2, 4),
+                        "tflops": tf(2.0 * T * (Hq + 2 * Hkv) * D * H, ms_qkv2)},
+                "post": {"ms_per_call": round(ms_post2, 4), "tflops": tf(f_post, ms_post2)},
+                "ms_excluding_attention": round(ms_qkv2 + ms_post2, 4)}}
 
 
 def decode_bench(name, steps, warmup):

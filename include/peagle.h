@@ -310,6 +310,38 @@ int peagle_layer1_post(int64_t n, int32_t K, int64_t T, const float *attn_out, i
                        float *h2_out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Stacked draft layers (the 2nd and later) [G, "Key Parameters": the number of decoder
+ * layers is a parameter; G, "Architecture": Llama-style decoder layers]. The residual
+ * stream h is the previous layer's output (h2_out); there is no concatenation and no
+ * separate embedding input. Per draft row:
+ *   x = rms(h) * w_norm;  [q | k | v] = x W_qkv^T                  (peagle_layer_qkv)
+ *   h1 = h + o W_o^T;  h2 = h1 + W_down (silu(W_gate m) * (W_up m)),
+ *   m = rms(h1) * w_post                                           (peagle_layer_post)
+ * with o this layer's attention output from peagle_draft_attn_fwd on its q, k, v (the
+ * same rows, positions and predicate as the first layer).
+ *   h              fp32[T, H]
+ *   w_norm, w_post bf16[H];  w_qkv bf16[(Hq + 2 Hkv) D, H];  w_o bf16[H, QW]
+ *   w_gate, w_up   bf16[I, H];  w_down bf16[H, I]
+ *   q              bf16[T, Hq, D] out;  k, v bf16[T, Hkv, D] out  (before RoPE)
+ *   attn_out       fp32[T, QW];  h2_out fp32[T, H] out (may be h itself: h is consumed by
+ *                  the first product, h2_out written by the last, in stream order)
+ *   workspace      >= the matching *_workspace_bytes, 256-byte aligned
+ * H, QW and I multiples of 64 and D a multiple of 8 (else PEAGLE_ERR_UNSUPPORTED).
+ * Products are bf16 MFMA GEMMs with fp32 accumulation on operands rounded to bf16.
+ */
+size_t peagle_layer_qkv_workspace_bytes(int64_t T, int32_t H);
+int peagle_layer_qkv(int64_t T, const float *h, int32_t H, const peagle_bf16 *w_norm, float eps,
+                     const peagle_bf16 *w_qkv, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, peagle_bf16 *q, peagle_bf16 *k, peagle_bf16 *v,
+                     void *workspace, size_t workspace_bytes, void *stream);
+size_t peagle_layer_post_workspace_bytes(int64_t T, int32_t H, int32_t QW, int32_t I);
+int peagle_layer_post(int64_t T, const float *attn_out, int32_t QW, const float *h, int32_t H,
+                      const peagle_bf16 *w_o, const peagle_bf16 *w_post,
+                      const peagle_bf16 *w_gate, const peagle_bf16 *w_up, int32_t I,
+                      const peagle_bf16 *w_down, float eps, float *h2_out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/*
  * peagle_draft_head -- the draft-vocab head and its argmax [N, description: the P-EAGLE
  * trainer shares EAGLE-3's draft-vocab projection]:
  *   token[r] = argmax_v (rms(h[r]) * w_final) . w_head[v]   (lowest v on ties)

@@ -387,6 +387,62 @@ int peagle_layer1_post(int64_t n, int32_t K, int64_t T, const float* attn_out, i
                                       static_cast<hipStream_t>(stream)));
 }
 
+size_t peagle_layer_qkv_workspace_bytes(int64_t T, int32_t H) {
+  if (T < 1 || T > kMaxI32 || H < 1) return 0;
+  return layer_qkv_workspace_bytes(T, H);
+}
+
+int peagle_layer_qkv(int64_t T, const float* h, int32_t H, const peagle_bf16* w_norm, float eps,
+                     const peagle_bf16* w_qkv, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, peagle_bf16* q, peagle_bf16* k, peagle_bf16* v,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (T < 1 || T > kMaxI32) return PEAGLE_ERR_ARG;
+  if (H < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0 ||
+      head_dim < 1)
+    return PEAGLE_ERR_ARG;
+  if (H % 64 != 0 || head_dim % 8 != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if ((int64_t)(num_q_heads + 2 * num_kv_heads) * head_dim > kMaxI32) return PEAGLE_ERR_ARG;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return PEAGLE_ERR_ARG;
+  if (!h || !w_norm || !w_qkv || !q || !k || !v || !workspace) return PEAGLE_ERR_ARG;
+  if (!aligned16(h) || !aligned16(w_norm) || !aligned16(w_qkv) || !aligned16(q) ||
+      !aligned16(k) || !aligned16(v) || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return PEAGLE_ERR_ARG;
+  if (workspace_bytes < layer_qkv_workspace_bytes(T, H)) return PEAGLE_ERR_WORKSPACE;
+  LayerArgs a{(int32_t)T, H, num_q_heads, num_kv_heads, head_dim, eps};
+  return status_of(launch_layer_qkv(a, h, w_norm, w_qkv, q, k, v, static_cast<char*>(workspace),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t peagle_layer_post_workspace_bytes(int64_t T, int32_t H, int32_t QW, int32_t I) {
+  if (T < 1 || T > kMaxI32 || H < 1 || QW < 1 || I < 1) return 0;
+  return layer1_post_workspace_bytes(T, T, H, QW, I);
+}
+
+int peagle_layer_post(int64_t T, const float* attn_out, int32_t QW, const float* h, int32_t H,
+                      const peagle_bf16* w_o, const peagle_bf16* w_post,
+                      const peagle_bf16* w_gate, const peagle_bf16* w_up, int32_t I,
+                      const peagle_bf16* w_down, float eps, float* h2_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (T < 1 || T > kMaxI32 || H < 1 || QW < 1 || I < 1) return PEAGLE_ERR_ARG;
+  if (H % 64 != 0 || QW % 64 != 0 || I % 64 != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if ((int64_t)2 * I > kMaxI32 || T * (QW > H ? QW : H) > ((int64_t)1 << 40))
+    return PEAGLE_ERR_ARG;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return PEAGLE_ERR_ARG;
+  if (!attn_out || !h || !w_o || !w_post || !w_gate || !w_up || !w_down || !h2_out ||
+      !workspace)
+    return PEAGLE_ERR_ARG;
+  if (!aligned16(attn_out) || !aligned16(h) || !aligned16(w_o) || !aligned16(w_post) ||
+      !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(h2_out) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return PEAGLE_ERR_ARG;
+  if (workspace_bytes < layer1_post_workspace_bytes(T, T, H, QW, I)) return PEAGLE_ERR_WORKSPACE;
+  // the first layer's second half with every row distinct and the raw residual stream
+  Layer1PostArgs a{(int32_t)T, (int32_t)T, H, QW, I, 0, eps};
+  return status_of(launch_layer1_post(a, attn_out, h, nullptr, w_o, w_post, w_gate, w_up, w_down,
+                                      h2_out, static_cast<char*>(workspace),
+                                      static_cast<hipStream_t>(stream)));
+}
+
 size_t peagle_draft_head_workspace_bytes(int64_t T, int32_t H, int32_t V) {
   if (T < 1 || T > kMaxI32 || H < 1 || V < 1) return 0;
   return draft_head_workspace_bytes(T, H, V);

@@ -15,6 +15,11 @@
 // Kernels: layer1_norm_kernel (one wave per row: both RMSNorms, the concatenation, bf16
 // into the workspace), the DMA-fed GEMM of gemm.h with an epilogue that splits the
 // columns into q, k and v (bf16), and layer1_broadcast_kernel (16-byte copies of row n).
+//
+// Layers stacked after the first (speculators P-EAGLE guide, "Key Parameters": the number
+// of decoder layers is a parameter) take the first layer's output h as their residual
+// stream: x = rms(h; w_norm) and [q | k | v] = x W_qkv^T on every row, the depth >= 1 rows
+// having diverged in the first layer's attention.
 #include <algorithm>
 
 #include "common.h"
@@ -146,6 +151,28 @@ hipError_t launch_layer1_qkv(const Layer1Args& a, const float* hidden, const uin
     hipLaunchKernelGGL(layer1_broadcast_kernel, dim3(blocks), dim3(256), 0, stream, q, k, v, a.n,
                        a.T, nq, nk);
   }
+  return hipGetLastError();
+}
+
+size_t layer_qkv_workspace_bytes(int64_t T, int32_t H) {
+  return ((size_t)T * H * 2 + 255) & ~(size_t)255;
+}
+
+hipError_t launch_layer_qkv(const LayerArgs& a, const float* h, const uint16_t* w_norm,
+                            const uint16_t* w_qkv, uint16_t* q, uint16_t* k, uint16_t* v,
+                            char* ws, hipStream_t stream) {
+  const int nq = a.Hq * a.D, nk = a.Hkv * a.D, N = nq + 2 * nk;
+  uint16_t* x = reinterpret_cast<uint16_t*>(ws);
+  hipError_t e = launch_rms_rows(h, w_norm, x, a.T, a.H, a.eps, stream);
+  if (e != hipSuccess) return e;
+  const StoreQKV epi{q, k, v, nq, nk};
+  const dim3 grid(gemm::grid_tiles(a.T, N)), block(gemm::kThreads);
+  if ((a.H / gemm::kDmaK) % gemm::kStages == 0)
+    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, StoreQKV, false>), grid, block, 0,
+                       stream, x, w_qkv, a.T, N, a.H, epi);
+  else
+    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, StoreQKV, true>), grid, block, 0,
+                       stream, x, w_qkv, a.T, N, a.H, epi);
   return hipGetLastError();
 }
 

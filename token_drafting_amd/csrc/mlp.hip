@@ -294,6 +294,13 @@ hipError_t launch_layer1_post(const Layer1PostArgs& a, const float* attn, const 
   return gemm_launch(act, w_down, a.T, a.H, a.I, StoreAdd{h2, h1, a.H}, stream);
 }
 
+hipError_t launch_rms_rows(const float* x, const uint16_t* w, uint16_t* y, int32_t rows,
+                           int32_t H, float eps, hipStream_t stream) {
+  hipLaunchKernelGGL(rms_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, x,
+                     w, y, rows, H, eps);
+  return hipGetLastError();
+}
+
 size_t draft_head_workspace_bytes(int64_t T, int32_t H, int32_t V) {
   return align256((size_t)T * H * 2) + align256((size_t)T * ((V + 63) / 64) * 8);
 }

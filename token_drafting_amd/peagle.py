@@ -45,6 +45,12 @@ SIGNATURES = {
     "peagle_layer1_post_workspace_bytes": ([_i64, _i64, _i32, _i32, _i32], _sz),
     "peagle_layer1_post": ([_i64, _i32, _i64, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p, _p, _i32,
                             _p, _f32, _p, _p, _sz, _p], _i32),
+    "peagle_layer_qkv_workspace_bytes": ([_i64, _i32], _sz),
+    "peagle_layer_qkv": ([_i64, _p, _i32, _p, _f32, _p, _i32, _i32, _i32, _p, _p, _p, _p, _sz,
+                          _p], _i32),
+    "peagle_layer_post_workspace_bytes": ([_i64, _i32, _i32, _i32], _sz),
+    "peagle_layer_post": ([_i64, _p, _i32, _p, _i32, _p, _p, _p, _p, _i32, _p, _f32, _p, _p, _sz,
+                           _p], _i32),
     "peagle_draft_head_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "peagle_draft_head": ([_i64, _p, _i32, _p, _p, _i32, _f32, _p, _p, _sz, _p], _i32),
     "peagle_fuse_inputs_fc_norm": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32,
@@ -318,6 +324,50 @@ def layer1_post(n, K, T, attn_out, hidden, w_norm_hidden, w_o, w_post, w_gate, w
     _check("peagle_layer1_post", lib().peagle_layer1_post(
         n, K, T, _ptr(attn_out), QW, _ptr(hidden), H, _ptr(w_norm_hidden),
         1 if norm_before_residual else 0, _ptr(w_o), _ptr(w_post), _ptr(w_gate), _ptr(w_up), I,
+        _ptr(w_down), float(eps), _ptr(h2), _ptr(workspace), workspace.numel(), _stream()))
+    return h2
+
+
+def layer_qkv(h, w_norm, w_qkv, Hq, Hkv, D, eps=1e-6, q=None, k=None, v=None, workspace=None):
+    """q [T, Hq, D], k and v [T, Hkv, D] (bf16, pre-RoPE) of a stacked draft layer (2nd and
+    later) from the residual stream h [T, H] (fp32, the previous layer's output)."""
+    for t, name in ((h, "h"), (w_norm, "w_norm"), (w_qkv, "w_qkv")):
+        _dev(t, name)
+    T, H = h.shape
+    dev = h.device
+    if q is None:
+        q = torch.empty((T, Hq, D), dtype=w_qkv.dtype, device=dev)
+    if k is None:
+        k = torch.empty((T, Hkv, D), dtype=w_qkv.dtype, device=dev)
+    if v is None:
+        v = torch.empty((T, Hkv, D), dtype=w_qkv.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().peagle_layer_qkv_workspace_bytes(T, H)),
+                                dtype=torch.uint8, device=dev)
+    _check("peagle_layer_qkv", lib().peagle_layer_qkv(
+        T, _ptr(h), H, _ptr(w_norm), float(eps), _ptr(w_qkv), Hq, Hkv, D, _ptr(q), _ptr(k),
+        _ptr(v), _ptr(workspace), workspace.numel(), _stream()))
+    return q, k, v
+
+
+def layer_post(attn_out, h, w_o, w_post, w_gate, w_up, w_down, eps=1e-6, h2=None,
+               workspace=None):
+    """h2 [T, H] (fp32) of a stacked draft layer from its attention output [T, Hq, D] or
+    [T, Hq*D] (fp32) and its input residual stream h [T, H]; h2 may be h."""
+    for t, name in ((attn_out, "attn_out"), (h, "h"), (w_o, "w_o"), (w_post, "w_post"),
+                    (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down")):
+        _dev(t, name)
+    T, H = h.shape
+    QW = attn_out.numel() // T
+    I = w_gate.shape[0]
+    dev = h.device
+    if h2 is None:
+        h2 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().peagle_layer_post_workspace_bytes(T, H, QW, I)),
+                                dtype=torch.uint8, device=dev)
+    _check("peagle_layer_post", lib().peagle_layer_post(
+        T, _ptr(attn_out), QW, _ptr(h), H, _ptr(w_o), _ptr(w_post), _ptr(w_gate), _ptr(w_up), I,
         _ptr(w_down), float(eps), _ptr(h2), _ptr(workspace), workspace.numel(), _stream()))
     return h2
 

@@ -31,6 +31,8 @@ TAG_WO, TAG_NORM_POST, TAG_WGATE, TAG_WUP, TAG_WDOWN, TAG_NORM_FINAL, TAG_WHEAD,
     21, 22, 23, 24, 25, 26, 27, 28)
 TAG_D2T, TAG_FC_NORM = 29, 30
 TAG_SPEC_LOGITS, TAG_SPEC_TOK, TAG_SPEC_U, TAG_SPEC_W = 31, 32, 33, 34
+# stacked layer L >= 2 draws from tags TAG_STACK + 8 (L - 2) + 0 .. 7
+TAG_STACK = 40
 
 # Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
 # layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
@@ -269,6 +271,32 @@ def layer1_post_weights(seed: int, H: int, QW: int, I: int, V: int = DRAFT_VOCAB
                 w_down=normal_bf16(seed, TAG_WDOWN, (H, I), std=float(1 / np.sqrt(I))),
                 w_final=near_one(TAG_NORM_FINAL),
                 w_head=normal_bf16(seed, TAG_WHEAD, (V, H), std=float(1 / np.sqrt(H))))
+
+
+def stacked_layer_weights(seed: int, layer: int, H: int, Hq: int, Hkv: int, D: int,
+                          I: int) -> dict:
+    """Random-init weights of stacked draft layer `layer` (2, 3, ...): RMSNorm weights bf16
+    of 1 + N(0, 0.1^2); projections bf16 of N(0, 1/fan_in) (W_qkv [(Hq + 2 Hkv) D, H], W_o
+    [H, Hq D], W_gate and W_up [I, H], W_down [H, I])."""
+    t0 = TAG_STACK + 8 * (layer - 2)
+
+    def near_one(tag):
+        x = 1.0 + 0.1 * _rng(seed, tag).standard_normal(H, dtype=np.float32)
+        return f32_to_bf16_bits(x.astype(np.float32))
+    QW = Hq * D
+    return dict(w_norm=near_one(t0),
+                w_qkv=normal_bf16(seed, t0 + 1, ((Hq + 2 * Hkv) * D, H), std=float(1 / np.sqrt(H))),
+                w_o=normal_bf16(seed, t0 + 2, (H, QW), std=float(1 / np.sqrt(QW))),
+                w_post=near_one(t0 + 3),
+                w_gate=normal_bf16(seed, t0 + 4, (I, H), std=float(1 / np.sqrt(H))),
+                w_up=normal_bf16(seed, t0 + 5, (I, H), std=float(1 / np.sqrt(H))),
+                w_down=normal_bf16(seed, t0 + 6, (H, I), std=float(1 / np.sqrt(I))))
+
+
+def residual_standin(seed: int, T: int, H: int) -> np.ndarray:
+    """Stand-in for a layer's output h [T, H] (float32 N(0, 1), every row distinct), the
+    input of the next stacked layer."""
+    return _rng(seed, TAG_STACK + 7).standard_normal((T, H), dtype=np.float32)
 
 
 def attention_out_standin(seed: int, T: int, QW: int) -> np.ndarray:
