@@ -97,6 +97,57 @@ def draft_attention_f64(q, k, v, idx, depth_off, cu_seqlens, theta: float,
     return dict(out=out, lse=lse)
 
 
+def draft_attention_backward_f64(q, k, v, idx, depth_off, cu_seqlens, theta: float, dout,
+                                 scale: float | None = None, block: int = 256) -> dict:
+    """Gradients of the draft attention (float64): given dout = dL/d out [T, Hq, D], returns
+    dq [T, Hq, D], dk and dv [T, Hkv, D] with respect to the pre-RoPE inputs, plus dq_rot
+    and dk_rot with respect to the rotated q', k'.
+
+    With P the masked softmax of S = q' k'^T * scale (per row and head):
+      dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+      dq' = dS k' * scale,  dk' = dS^T q' * scale,
+    summed over the q heads sharing a kv head; dq and dk are dq', dk' rotated back (the
+    transpose of the RoPE rotation at each row's position)."""
+    from .rope import rotate_transpose
+
+    q = np.asarray(q, np.float64)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    meta = row_meta(idx, depth_off, cu_seqlens)
+    qr = rotate(q, meta["pos"], theta)
+    kr = rotate(np.asarray(k, np.float64), meta["pos"], theta)
+    vf = np.asarray(v, np.float64)
+    do = np.asarray(dout, np.float64)
+    dq_rot = np.zeros_like(qr)
+    dk_rot = np.zeros((T, Hkv, D))
+    dv = np.zeros((T, Hkv, D))
+    for b0 in range(0, T, block):
+        br = np.arange(b0, min(T, b0 + block))
+        mask = allowed_mask(meta, br)
+        for h in range(Hq):
+            g = h // G
+            s = np.where(mask, (qr[br, h, :] @ kr[:, g, :].T) * scale, -np.inf)
+            P = np.exp(s - s.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dP = do[br, h, :] @ vf[:, g, :].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq_rot[br, h, :] = (dS @ kr[:, g, :]) * scale
+            dk_rot[:, g, :] += (dS.T @ qr[br, h, :]) * scale
+            dv[:, g, :] += P.T @ do[br, h, :]
+    return dict(dq=rotate_transpose(dq_rot, meta["pos"], theta),
+                dk=rotate_transpose(dk_rot, meta["pos"], theta), dv=dv, dq_rot=dq_rot,
+                dk_rot=dk_rot)
+
+
+def draft_attention_backward(q, k, v, idx, depth_off, cu_seqlens, theta: float, dout,
+                             scale: float | None = None) -> dict:
+    """Same on the library's input formats: q, k, v bf16 bits, dout float32."""
+    return draft_attention_backward_f64(to_f64(q), to_f64(k), to_f64(v), idx, depth_off,
+                                        cu_seqlens, theta, dout, scale)
+
+
 def useful_pairs(idx, depth_off, cu_seqlens) -> int:
     """Number of allowed (query row, key row) pairs per head: sum of (p - a_s + 1) + d."""
     meta = row_meta(idx, depth_off, cu_seqlens)

@@ -49,6 +49,16 @@ def rotate(x: np.ndarray, pos, theta: float) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
+def rotate_transpose(y: np.ndarray, pos, theta: float) -> np.ndarray:
+    """The transpose (inverse) of ``rotate`` at the same positions: maps the gradient with
+    respect to the rotated vectors to the gradient with respect to the unrotated ones."""
+    D = y.shape[-1]
+    a = angles(pos, D, theta)[:, None, :]
+    c, s = np.cos(a), np.sin(a)
+    y1, y2 = y[..., : D // 2], y[..., D // 2:]
+    return np.concatenate([y1 * c + y2 * s, y2 * c - y1 * s], axis=-1)
+
+
 def row_positions(idx, depth_off, cu_seqlens) -> np.ndarray:
     """Position value p - a_s + d of every draft row."""
     idx = np.asarray(idx, dtype=np.int64)
