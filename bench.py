@@ -242,6 +242,8 @@ def main():
         base["ptd_token_id"], hidden, emb, fc_norm_weight=wn), args.steps, args.warmup)
     result["fuse_fc_norm"] = {"ms_per_call": round(ms_fcn, 4),
                               "ms_without_fc_norm": round(stage_ms["fuse_inputs"], 4)}
+    result["attn_bwd"] = attn_bwd_bench(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse,
+                                        seed, P, args.steps, args.warmup)
     result["verify_d2t"] = verify_d2t_bench(args.steps, args.warmup)
     result["verify_sampled"] = verify_sampled_bench(args.steps, args.warmup)
     result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, hidden, emb, out,
@@ -310,6 +312,34 @@ def verify_d2t_bench(steps, warmup, N=4096, K=8, Vd=8192, Vt=32000):
     torch.cuda.empty_cache()
     return {"drafts": N, "K": K, "draft_vocab": Vd, "target_vocab": Vt, "ms_per_call": round(ms, 4),
             "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def attn_bwd_bench(n, K, sel, cu, q, k, v, cos, sin, out, lse, seed, pairs, steps, warmup):
+    """Time peagle_draft_attn_bwd on the step's own attention inputs and results (the
+    forward's out and lse), with a seeded N(0, 1) dL/d out. Algorithmic work: five products
+    over the useful (query, key) pairs (S recomputed, dP, dV, dK, dQ), 2 D flop each per
+    pair and q head."""
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dout = torch.from_numpy(synth.attn_grad_out(seed, T, Hq, D)).to(q.device)
+    dq = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty((T, Hkv, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(int(peagle.lib().peagle_draft_attn_bwd_workspace_bytes(n, T, Hq, Hkv, D)),
+                     dtype=torch.uint8, device=q.device)
+    ms = _time_calls(lambda: peagle.draft_attn_bwd(n, K, sel, cu, q, k, v, cos, sin, out, lse,
+                                                   dout, dq, dk, dv, ws), steps, warmup)
+    flop = 10.0 * D * Hq * pairs
+    tf = flop / (ms * 1e-3) / 1e12
+    del dout, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_call": round(ms, 4), "tflops": round(tf, 1),
+            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "includes": "forward preparation (RoPE, row list), dO cast, tile layouts, dK/dV, dQ, "
+                        "inverse RoPE"}
 
 
 def verify_sampled_bench(steps, warmup, N=4096, K=8, V=32000):

@@ -192,6 +192,35 @@ int peagle_draft_attn_core(int64_t n, int32_t K, int64_t T, const int32_t *idx,
                            void *stream);
 
 /*
+ * peagle_draft_attn_bwd -- gradients of peagle_draft_attn_fwd [N, description: the
+ * P-EAGLE trainer backpropagates its masked-depth loss through the same cache_hidden
+ * attention]. Same layout arguments as the forward, plus its results and dL/d out:
+ *   out, lse         fp32[T, Hq, D], fp32[Hq, T]  from peagle_draft_attn_fwd on the same
+ *                    inputs (lse required)
+ *   dout             fp32[T, Hq, D]   dL/d out
+ *   dq               fp32[T, Hq, D]   out  dL/dq  (pre-RoPE q)
+ *   dk, dv           fp32[T, Hkv, D]  out  dL/dk, dL/dv (pre-RoPE k)
+ *   workspace        >= peagle_draft_attn_bwd_workspace_bytes(n, T, Hq, Hkv, D), 256-byte
+ *                    aligned; the forward's preparation is redone at its head
+ * With P the masked softmax: dV = P^T dO, dS = P * (dO V^T - rowsum(dO * O)),
+ * dq' = scale dS k', dk' = scale dS^T q', summed over the q heads of each kv head, and
+ * dq, dk rotated back from the RoPE frame. Products on bf16 MFMA (q', k', v, dO, P and dS
+ * rounded to bf16) with fp32 accumulation; the diagonal-extension keys' dk, dv in fp32.
+ * Every element of dq, dk and dv is written. Shapes as for the forward.
+ */
+size_t peagle_draft_attn_bwd_workspace_bytes(int64_t n, int64_t T, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim);
+int peagle_draft_attn_bwd(int64_t n, int32_t K, int64_t T, const int32_t *idx,
+                          const int32_t *depth_off, const int32_t *row_of,
+                          const int32_t *cu_seqlens, int32_t num_seqs, const peagle_bf16 *q,
+                          const peagle_bf16 *k, const peagle_bf16 *v, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                          const float *rope_cos, const float *rope_sin, int32_t rope_max_pos,
+                          const float *out, const float *lse, const float *dout, float *dq,
+                          float *dk, float *dv, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
  * peagle_accept_prefix -- greedy verification [G, "Inference Process"]: the target
  * checks every draft token in one pass and the longest correct prefix is accepted.
  *   draft_logits, target_logits  bf16[N, K, V]; row [i, d] of target_logits scores the

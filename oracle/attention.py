@@ -141,6 +141,52 @@ def draft_attention_backward_f64(q, k, v, idx, depth_off, cu_seqlens, theta: flo
                 dk_rot=dk_rot)
 
 
+def draft_attention_backward_rows_f64(q, k, v, idx, depth_off, cu_seqlens, theta: float, dout,
+                                      q_rows, k_rows, scale: float | None = None) -> dict:
+    """The same gradients restricted to a subset, for workloads too large for the full
+    oracle: dq of the query rows q_rows, and dk, dv of the key rows k_rows. The softmax of
+    every query row involved (q_rows, and every row that sees one of k_rows) is still taken
+    over all of its keys; only the outputs are restricted."""
+    from .rope import rotate_transpose
+
+    q = np.asarray(q, np.float64)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    meta = row_meta(idx, depth_off, cu_seqlens)
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    kr = rotate(np.asarray(k, np.float64), meta["pos"], theta)
+    vf = np.asarray(v, np.float64)
+    do = np.asarray(dout, np.float64)
+    # query rows that see any of k_rows
+    seers = np.zeros(T, dtype=bool)
+    for b0 in range(0, T, 4096):
+        br = np.arange(b0, min(T, b0 + 4096))
+        seers[br] = allowed_mask(meta, br)[:, k_rows].any(axis=1)
+    rows = np.union1d(q_rows, np.nonzero(seers)[0])
+    qr = rotate(q[rows], meta["pos"][rows], theta)
+    mask = allowed_mask(meta, rows)
+    pos_in = {int(r): i for i, r in enumerate(rows)}
+    dq_rot = np.zeros((len(q_rows), Hq, D))
+    dk_rot = np.zeros((len(k_rows), Hkv, D))
+    dv = np.zeros((len(k_rows), Hkv, D))
+    qi = np.array([pos_in[int(r)] for r in q_rows], dtype=np.int64)
+    for h in range(Hq):
+        g = h // G
+        s = np.where(mask, (qr[:, h, :] @ kr[:, g, :].T) * scale, -np.inf)
+        P = np.exp(s - s.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dP = do[rows, h, :] @ vf[:, g, :].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dq_rot[:, h, :] = (dS[qi] @ kr[:, g, :]) * scale
+        dk_rot[:, g, :] += (dS[:, k_rows].T @ qr[:, h, :]) * scale
+        dv[:, g, :] += P[:, k_rows].T @ do[rows, h, :]
+    return dict(dq=rotate_transpose(dq_rot, meta["pos"][q_rows], theta),
+                dk=rotate_transpose(dk_rot, meta["pos"][k_rows], theta), dv=dv)
+
+
 def draft_attention_backward(q, k, v, idx, depth_off, cu_seqlens, theta: float, dout,
                              scale: float | None = None) -> dict:
     """Same on the library's input formats: q, k, v bf16 bits, dout float32."""

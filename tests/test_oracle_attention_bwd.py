@@ -125,3 +125,22 @@ def test_backward_closed_forms():
         np.testing.assert_allclose(got["dk_rot"][:, g, :].sum(axis=0), 0.0, atol=1e-10)
     for a in cu[:-1]:
         assert np.all(got["dq"][a] == 0.0)  # row a of depth 0 is anchor a
+
+
+def test_row_restricted_backward_equals_full():
+    """The subset form (for full-size workloads) reproduces the full oracle's dq rows and
+    dk, dv key rows: the last depth-0 keys of each sequence, depth >= 1 rows, and spread
+    query rows."""
+    rng = np.random.default_rng(11)
+    cu = np.array([0, 70, 150])
+    idx, depth_off = _layout(150, 4, cu)
+    T, Hq, Hkv, D = len(idx), 4, 2, 16
+    q, k, v, dout = _inputs(rng, T, Hq, Hkv, D)
+    full = oattn.draft_attention_backward_f64(q, k, v, idx, depth_off, cu, 1e4, dout)
+    q_rows = np.array([0, 5, 69, 70, 149, 150, T - 1])
+    k_rows = np.array([66, 69, 146, 149, 150, 200, T - 1])
+    sub = oattn.draft_attention_backward_rows_f64(q, k, v, idx, depth_off, cu, 1e4, dout,
+                                                  q_rows, k_rows)
+    np.testing.assert_allclose(sub["dq"], full["dq"][q_rows], atol=1e-12)
+    np.testing.assert_allclose(sub["dk"], full["dk"][k_rows], atol=1e-12)
+    np.testing.assert_allclose(sub["dv"], full["dv"][k_rows], atol=1e-12)

@@ -7,6 +7,7 @@
 #include "peagle.h"
 #include "kernels.h"
 #include "layer.h"
+#include "bwd.h"
 #include "variants.h"
 
 using namespace peagle;
@@ -228,6 +229,41 @@ int peagle_draft_attn_fwd(PEAGLE_ATTN_ARGS) {
   if (st != PEAGLE_OK) return st;
   st = run_prepare(c);
   return st != PEAGLE_OK ? st : run_core(c);
+}
+
+size_t peagle_draft_attn_bwd_workspace_bytes(int64_t n, int64_t T, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim) {
+  if (n < 1 || T < n || T > kMaxI32 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  return attn_bwd_layout(n, T, num_q_heads, num_kv_heads, head_dim).total;
+}
+
+int peagle_draft_attn_bwd(int64_t n, int32_t K, int64_t T, const int32_t* idx,
+                          const int32_t* depth_off, const int32_t* row_of,
+                          const int32_t* cu_seqlens, int32_t num_seqs, const peagle_bf16* q,
+                          const peagle_bf16* k, const peagle_bf16* v, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                          const float* rope_cos, const float* rope_sin, int32_t rope_max_pos,
+                          const float* out, const float* lse, const float* dout, float* dq,
+                          float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  AttnCall c;
+  int st = attn_check(n, K, T, idx, depth_off, row_of, cu_seqlens, num_seqs, q, k, v,
+                      num_q_heads, num_kv_heads, head_dim, softmax_scale, rope_cos, rope_sin,
+                      rope_max_pos, const_cast<float*>(out), const_cast<float*>(lse), workspace,
+                      workspace_bytes, stream, &c);
+  if (st != PEAGLE_OK) return st;
+  if (!lse || !dout || !dq || !dk || !dv) return PEAGLE_ERR_ARG;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(lse))
+    return PEAGLE_ERR_ARG;
+  const AttnBwdLayout L = attn_bwd_layout(n, T, num_q_heads, num_kv_heads, head_dim);
+  if (workspace_bytes < L.total) return PEAGLE_ERR_WORKSPACE;
+  if (L.ntq > kMaxI32) return PEAGLE_ERR_ARG;
+  st = run_prepare(c);
+  if (st != PEAGLE_OK) return st;
+  return status_of(launch_attn_bwd(c.a, idx, depth_off, cu_seqlens, v, out, lse, dout, rope_cos,
+                                   rope_sin, dq, dk, dv, c.ws, c.stream));
 }
 
 int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,

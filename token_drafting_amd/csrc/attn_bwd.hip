@@ -1,0 +1,805 @@
+// Multi-depth draft attention backward (flash-style, GQA), gfx950.
+//
+// NeMo Automodel PR 2376 (description): the P-EAGLE trainer runs the masked-depth loss
+// through the EAGLE-3 cache_hidden attention, so the drafter's attention is trained through
+// the same predicate as its forward: row (d, p) sees the depth-0 keys p' <= p of its own
+// packed sequence and its own anchor's depth-e rows, 1 <= e <= d. With P the softmax of
+// S = q' k'^T * scale (q', k' rotated by RoPE at the rows' positions), lse from the forward
+// and Delta = rowsum(dO * O):
+//   dP = dO V^T,  dS = P * (dP - Delta),  dq' = scale dS k',  dk' = scale dS^T q',
+//   dV = P^T dO,
+// summed over the q heads of a kv head; dq and dk are dq', dk' rotated back (RoPE is an
+// orthogonal map, so its transpose is the rotation by the opposite angle).
+//
+// Work decomposition:
+//   dq   query-major, like the forward: a workgroup takes half of one chunk's 256 query
+//        slots (4 waves of 32) and streams the chunk's depth-0 key tiles through LDS, then
+//        the chunk's diagonal keys. Per 32-key tile: S^T = K Q^T and dP^T = V dO^T (the
+//        lane holds one query column and 16 keys), P and dS in registers, then
+//        dq'^T += K^T dS^T with K^T tiles laid out like the forward's V^T tiles.
+//   dk, dv of depth-0 keys: key-major. A workgroup owns 128 consecutive keys (a wave per
+//        32) of one kv head and streams every query tile that can see them: the query
+//        slots (anchor-major rows x G heads) of the anchors from the block's first key to
+//        the end of its last key's sequence, pre-cut into 32-slot tiles in both row and
+//        transposed layouts. Per tile: S = Q K^T and dP = dO V^T (the lane holds one key
+//        column and 16 slots), then dV^T += dO^T P and dK^T += Q^T dS with the lane's
+//        own P and dS as the B operands.
+//   dk, dv of depth >= 1 keys: a depth-e row is seen only by its own anchor's rows of
+//        depth >= e (at most K - e rows x G heads): one wave per key row and kv head on
+//        the vector units.
+// Tiles move global -> LDS by global_load_lds_dwordx4 into two buffers (tile t+1 streams
+// while tile t is computed). Operands are bf16 (q', k', v, dO, P, dS) with fp32
+// accumulation; P is exact up to rounding because lse is the forward's. Every path uses
+// the same bf16-rounded dO, Delta included.
+#include <algorithm>
+
+#include "bwd.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace peagle {
+
+namespace {
+
+constexpr int KT = 32;  // keys (or query slots) per tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BCfg {
+  static constexpr int KROW = D * 2 + 16;                       // padded row of a row tile
+  static constexpr int KBUF = (KT * KROW + 1023) / 1024 * 1024;  // whole DMA blocks
+  static constexpr int TBYTES = D * KT * 2;                       // transposed tile [D][32]
+  static constexpr int DK = D / 16;                               // k-steps over D
+  static constexpr int MT = D / 32;                               // 32-row tiles of D
+};
+
+// Transposed tiles: row d holds 32 entries (64 bytes) in the order that makes a 16-byte
+// read one MFMA operand (inside each 16-group: 0-3, 8-11, 4-7, 12-15); the 16-byte chunk
+// index is XOR-ed with bits 2-3 of d in LDS to spread the rows over the banks.
+__device__ __forceinline__ int t_off(int d, int chunk) {
+  return d * (KT * 2) + ((chunk ^ ((d >> 2) & 3)) << 4);
+}
+// Entry x (0..31) of a transposed row sits in chunk tchunk(x) at element telem(x).
+__device__ __forceinline__ int tchunk(int x) { return 2 * (x >> 4) + ((x & 7) >> 2); }
+__device__ __forceinline__ int telem(int x) { return 4 * ((x & 15) >> 3) + (x & 3); }
+// Inverse: the entry stored at (chunk, element).
+__device__ __forceinline__ int tentry(int chunk, int e) {
+  return 16 * (chunk >> 1) + 8 * (e >> 2) + 4 * (chunk & 1) + (e & 3);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const void* p) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
+}
+
+struct BwdParams {
+  const int4* qinfo;        // anchor-major list: (row, anchor, depth, sequence start)
+  const int32_t* qstart;    // first list entry of each anchor [n + 1]
+  const int32_t* cu;        // cu_seqlens [S + 1]
+  const int2* chunks;
+  const int32_t* nchunks;
+  const uint16_t* qr;       // q' [T, Hq, D]
+  const uint16_t* kr;       // k' [T + 32, Hkv, D]
+  const uint16_t* v;        // v  [T, Hkv, D]
+  const uint16_t* vpad;     // depth-0 v [n + 32, Hkv, D], zero past n
+  const uint16_t* kt;       // depth-0 k'^T tiles [Hkv][ntiles][D][32]
+  const uint16_t* dob;      // bf16 dO [T, Hq, D]
+  const float* lse;         // [Hq, T], natural log
+  const float* dlt;         // Delta [Hq, T]
+  const uint16_t* qtr;      // query tiles, rows [Hkv][ntq][32][D]
+  const uint16_t* qtt;      // and transposed [Hkv][ntq][D][32]
+  const uint16_t* dtr;
+  const uint16_t* dtt;
+  const int4* smeta;        // per slot: (anchor, sequence start, lse * log2 e, Delta)
+  float* dq;
+  float* dk;
+  float* dv;
+  int n, T, S, Hq, Hkv, G, QR, ntiles;
+  int64_t ntq;
+  float scale, c_log2;
+};
+
+// dO rounded to bf16 and Delta[h, row] = sum_d bf16(dO) * O in fp32. Delta takes the same
+// rounded dO as dP = dO V^T, so that each row of dS = P (dP - Delta) still sums to zero (a
+// Delta from the unrounded dO leaves a bias in every dS row that dominates dq on rows with
+// thousands of keys). A group of D/8 threads per (row, head), 8 elements each.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dout_kernel(const float* __restrict__ dout,
+                                                       const float* __restrict__ out,
+                                                       uint16_t* __restrict__ dob,
+                                                       float* __restrict__ dlt, int T, int Hq) {
+  constexpr int CPR = D / 8;
+  const size_t item = blockIdx.x * (size_t)256 + threadIdx.x;
+  const size_t total = (size_t)T * Hq * CPR;
+  const bool on = item < total;
+  const size_t pair = item / CPR;
+  const int c = (int)(item % CPR);
+  float acc = 0.f;
+  if (on) {
+    const float* a = dout + pair * D + c * 8;
+    const float* b = out + pair * D + c * 8;
+    const floatx4 a0 = *reinterpret_cast<const floatx4*>(a);
+    const floatx4 a1 = *reinterpret_cast<const floatx4*>(a + 4);
+    const floatx4 b0 = *reinterpret_cast<const floatx4*>(b);
+    const floatx4 b1 = *reinterpret_cast<const floatx4*>(b + 4);
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = (__bf16)a0[i];
+      o[i + 4] = (__bf16)a1[i];
+      acc = fmaf((float)o[i], b0[i], acc);
+      acc = fmaf((float)o[i + 4], b1[i], acc);
+    }
+    *reinterpret_cast<bf16x8*>(dob + pair * D + c * 8) = o;
+  }
+#pragma unroll
+  for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (on && c == 0) {
+    const size_t row = pair / Hq, h = pair % Hq;
+    dlt[h * T + row] = acc;
+  }
+}
+
+// Rows [0, nrows) of src [*, Hkv, D] as transposed 32-row tiles [Hkv][ntiles][D][32]
+// (rows past nrows read as zero).
+template <int D>
+__global__ __launch_bounds__(256) void transpose_tiles_kernel(const uint16_t* __restrict__ src,
+                                                              uint16_t* __restrict__ dst,
+                                                              int nrows, int Hkv, int ntiles) {
+  __shared__ uint16_t tile[KT][D + 8];
+  const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  constexpr int CPR = D / 8;
+  for (int q = tid; q < KT * CPR; q += 256) {
+    const int x = q / CPR, c = q % CPR, row = t * KT + x;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (row < nrows) val = *reinterpret_cast<const u32x4*>(src + ((size_t)row * Hkv + g) * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      tile[x][c * 8 + 2 * w] = (uint16_t)(val[w] & 0xFFFFu);
+      tile[x][c * 8 + 2 * w + 1] = (uint16_t)(val[w] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* out = dst + ((size_t)g * ntiles + t) * D * KT;
+  for (int q = tid; q < D * 4; q += 256) {
+    const int d = q >> 2, chunk = q & 3;
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      o[w] = (uint32_t)tile[tentry(chunk, 2 * w)][d] |
+             ((uint32_t)tile[tentry(chunk, 2 * w + 1)][d] << 16);
+    *reinterpret_cast<u32x4*>(out + (size_t)d * KT + chunk * 8) = o;
+  }
+}
+
+// vpad rows [0, n + 32): v's depth-0 rows, then 32 rows of zeros (the last key tile).
+__global__ __launch_bounds__(256) void vpad_kernel(const uint16_t* __restrict__ v,
+                                                   uint16_t* __restrict__ vpad, int n, int Hkv,
+                                                   int D) {
+  const size_t per_row = (size_t)Hkv * D / 8, total = (size_t)(n + KT) * per_row;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
+       t += (size_t)gridDim.x * blockDim.x) {
+    const size_t row = t / per_row;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (row < (size_t)n) val = *reinterpret_cast<const u32x4*>(v + t * 8);
+    *reinterpret_cast<u32x4*>(vpad + t * 8) = val;
+  }
+}
+
+// Query tile t of kv head g: slots 32t .. 32t+31 of the list (entry s / G, head
+// g G + s % G). Writes q' and dO of each slot in row layout and transposed, and the
+// slot's metadata. Slots past the list get zero data and anchor -1 (never visible).
+template <int D>
+__global__ __launch_bounds__(256) void qtile_kernel(const BwdParams p, uint16_t* __restrict__ qtr,
+                                                    uint16_t* __restrict__ qtt,
+                                                    uint16_t* __restrict__ dtr,
+                                                    uint16_t* __restrict__ dtt,
+                                                    int4* __restrict__ smeta) {
+  __shared__ uint16_t tq[KT][D + 8], td[KT][D + 8];
+  const int64_t t = blockIdx.x;
+  const int g = blockIdx.y, tid = threadIdx.x;
+  constexpr int CPR = D / 8;
+  const size_t tb = (size_t)g * p.ntq + t;
+  for (int q = tid; q < KT * CPR; q += 256) {
+    const int x = q / CPR, c = q % CPR;
+    const int64_t s = t * KT + x, e = s / p.G;
+    const int h = g * p.G + (int)(s % p.G);
+    u32x4 vq = {0u, 0u, 0u, 0u}, vd = {0u, 0u, 0u, 0u};
+    if (e < p.T) {
+      const int row = min(max(p.qinfo[e].x, 0), p.T - 1);
+      const size_t off = ((size_t)row * p.Hq + h) * D + c * 8;
+      vq = *reinterpret_cast<const u32x4*>(p.qr + off);
+      vd = *reinterpret_cast<const u32x4*>(p.dob + off);
+    }
+    *reinterpret_cast<u32x4*>(qtr + (tb * KT + x) * D + c * 8) = vq;
+    *reinterpret_cast<u32x4*>(dtr + (tb * KT + x) * D + c * 8) = vd;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      tq[x][c * 8 + 2 * w] = (uint16_t)(vq[w] & 0xFFFFu);
+      tq[x][c * 8 + 2 * w + 1] = (uint16_t)(vq[w] >> 16);
+      td[x][c * 8 + 2 * w] = (uint16_t)(vd[w] & 0xFFFFu);
+      td[x][c * 8 + 2 * w + 1] = (uint16_t)(vd[w] >> 16);
+    }
+  }
+  if (tid < KT) {
+    const int64_t s = t * KT + tid, e = s / p.G;
+    int4 m = make_int4(-1, -1, 0, 0);
+    if (e < p.T) {
+      const int4 qi = p.qinfo[e];
+      const int row = min(max(qi.x, 0), p.T - 1);
+      const size_t li = (size_t)(g * p.G + (int)(s % p.G)) * p.T + row;
+      m = make_int4(qi.y, qi.w, __float_as_int(p.lse[li] * kLog2e), __float_as_int(p.dlt[li]));
+    }
+    smeta[tb * KT + tid] = m;
+  }
+  __syncthreads();
+  for (int q = tid; q < D * 4; q += 256) {
+    const int d = q >> 2, chunk = q & 3;
+    u32x4 oq, od;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int a = tentry(chunk, 2 * w), b = tentry(chunk, 2 * w + 1);
+      oq[w] = (uint32_t)tq[a][d] | ((uint32_t)tq[b][d] << 16);
+      od[w] = (uint32_t)td[a][d] | ((uint32_t)td[b][d] << 16);
+    }
+    *reinterpret_cast<u32x4*>(qtt + (tb * D + d) * KT + chunk * 8) = oq;
+    *reinterpret_cast<u32x4*>(dtt + (tb * D + d) * KT + chunk * 8) = od;
+  }
+}
+
+// dk' (WK) and / or dv (WV) of the depth-0 keys [k0, k0 + 128) of kv head g. With both,
+// a lane holds its key's k' and v fragments and two accumulators; for D >= 128 that does
+// not fit the register file, so the two run as separate passes (the dV pass needs neither
+// v nor dP, and each pass streams three of the four query tiles).
+template <int D, bool WK, bool WV>
+__global__ __launch_bounds__(256) void dkdv_kernel(const BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int RQ = 0, RD = C::KBUF, RQT = 2 * C::KBUF, RDT = RQT + C::TBYTES;
+  constexpr int RM = RDT + C::TBYTES, STAGE = RM + 1024;
+  constexpr int NR = C::KBUF / 1024, NTB = C::TBYTES / 1024;
+  __shared__ __attribute__((aligned(1024))) char buf0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char buf1[STAGE];
+  __shared__ int s_rng[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int g = blockIdx.x % p.Hkv, kb = blockIdx.x / p.Hkv;
+  const int k0 = kb * kBwdKeys;
+  if (k0 >= p.n) return;
+  const int k1 = min(k0 + kBwdKeys, p.n) - 1;
+  if (tid == 0) {
+    // visible to: anchors from k0 to the end of k1's sequence (all their depths, heads)
+    const int s1 = min(max(upper_index(p.cu, p.S + 1, k1), 0), p.S - 1);
+    const int end = min(max(p.cu[s1 + 1], k1 + 1), p.n);
+    const int64_t e0 = min(max(p.qstart[k0], 0), p.T);
+    const int64_t e1 = min(max((int64_t)p.qstart[end], e0), (int64_t)p.T);
+    s_rng[0] = (int)(e0 * p.G / KT);
+    s_rng[1] = (int)((e1 * p.G + KT - 1) / KT);
+  }
+  __syncthreads();
+  const int t0 = s_rng[0], t1 = s_rng[1];
+
+  const int key = k0 + wave * KT + r32;
+  const bool key_on = key <= k1;
+  const int kc = min(key, k1);
+  const int key_lo = p.qinfo[min(max(p.qstart[kc], 0), p.T - 1)].w;
+  bf16x8 kf[C::DK], vf[WK ? C::DK : 1];
+  {
+    const uint16_t* krow = p.kr + ((size_t)kc * p.Hkv + g) * D + half * 8;
+    const uint16_t* vrow = p.v + ((size_t)kc * p.Hkv + g) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) {
+      kf[kk] = ld8(krow + kk * 16);
+      if constexpr (WK) vf[kk] = ld8(vrow + kk * 16);
+    }
+  }
+  floatx16 dkt[WK ? C::MT : 1], dvt[WV ? C::MT : 1];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (WK) dkt[mt][r] = 0.f;
+      if constexpr (WV) dvt[mt][r] = 0.f;
+    }
+
+  auto issue = [&](int t, char* dst) {
+    const size_t tb = (size_t)g * p.ntq + t;
+    const char* bq = uniform_opaque(reinterpret_cast<const char*>(p.qtr + tb * KT * D));
+    const char* bd = uniform_opaque(reinterpret_cast<const char*>(p.dtr + tb * KT * D));
+    const char* bqt = uniform_opaque(reinterpret_cast<const char*>(p.qtt + tb * KT * D));
+    const char* bdt = uniform_opaque(reinterpret_cast<const char*>(p.dtt + tb * KT * D));
+#pragma unroll
+    for (int j = 0; j < (NR + 3) / 4; ++j) {
+      const int b = wave + 4 * j;
+      if (b < NR) {
+        const int P = b * 1024 + lane * 16;
+        const int x = P / C::KROW, off = P - x * C::KROW;
+        const uint32_t o = (x < KT && off < D * 2) ? (uint32_t)(x * D * 2 + off) : 0u;
+        dma16(bq + lane_opaque(o), dst + RQ + b * 1024);
+        if constexpr (WK) dma16(bd + lane_opaque(o), dst + RD + b * 1024);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < (NTB + 3) / 4; ++j) {
+      const int b = wave + 4 * j;
+      if (b < NTB) {
+        const int P = b * 1024 + lane * 16;
+        const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 2) & 3);
+        const uint32_t o = (uint32_t)((d * KT + c * 8) * 2);
+        if constexpr (WK) dma16(bqt + lane_opaque(o), dst + RQT + b * 1024);
+        if constexpr (WV) dma16(bdt + lane_opaque(o), dst + RDT + b * 1024);
+      }
+    }
+    if (wave == 0)
+      dma16(reinterpret_cast<const char*>(p.smeta + tb * KT) + (lane & 31) * 16, dst + RM);
+  };
+
+  auto compute = [&](const char* B) {
+    floatx16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    const char* qb = B + RQ + r32 * C::KROW + half * 16;
+    const char* db = B + RD + r32 * C::KROW + half * 16;
+    // scheduling barriers between the phases keep each phase's LDS fragments from being
+    // hoisted into the previous one (the register file holds k', v and the accumulators)
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) s = mfma32(ld8(qb + kk * 32), kf[kk], s);
+    sched_reads_ahead<C::DK, 2, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (WK) {
+#pragma unroll
+      for (int kk = 0; kk < C::DK; ++kk) dp = mfma32(ld8(db + kk * 32), vf[kk], dp);
+      sched_reads_ahead<C::DK, 2, 1>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int4* meta = reinterpret_cast<const int4*>(B + RM);
+    bf16x8 pb[2], sb[2];
+    // two halves of 8 slots, so that only 8 slots' metadata are live at once
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int r = 8 * hh; r < 8 * hh + 8; ++r) {
+        const int4 m = meta[8 * (r >> 2) + 4 * half + (r & 3)];
+        const bool ok = key_on && m.y == key_lo && m.x >= key;
+        const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], p.c_log2, -__int_as_float(m.z))) : 0.f;
+        pb[r >> 3][r & 7] = (__bf16)pr;
+        if constexpr (WK) sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - __int_as_float(m.w)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt) {
+        const int o = t_off(mt * 32 + r32, ks * 2 + half);
+        if constexpr (WV) dvt[mt] = mfma32(ld8(B + RDT + o), pb[ks], dvt[mt]);
+        if constexpr (WK) dkt[mt] = mfma32(ld8(B + RQT + o), sb[ks], dkt[mt]);
+      }
+    sched_reads_ahead<2 * C::MT * ((WK ? 1 : 0) + (WV ? 1 : 0)), 2, 1>();
+  };
+
+  // one compute body with the buffer chosen at run time: two inlined copies (one per
+  // buffer) made the register allocator shuttle the accumulators between them
+  if (t0 < t1) issue(t0, buf0);
+  for (int t = t0; t < t1; ++t) {
+    const bool odd = ((t - t0) & 1) != 0;
+    wait_dma();
+    __syncthreads();  // tile t landed in its buffer; the other one is free
+    if (t + 1 < t1) issue(t + 1, odd ? buf0 : buf1);
+    compute(odd ? buf1 : buf0);
+  }
+
+  if (key_on) {
+    float* dkr = p.dk + ((size_t)key * p.Hkv + g) * D;
+    float* dvr = p.dv + ((size_t)key * p.Hkv + g) * D;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        floatx4 a, b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (WK) a[j] = dkt[mt][4 * i + j] * p.scale;
+          if constexpr (WV) b[j] = dvt[mt][4 * i + j];
+        }
+        if constexpr (WK) *reinterpret_cast<floatx4*>(dkr + mt * 32 + 8 * i + 4 * half) = a;
+        if constexpr (WV) *reinterpret_cast<floatx4*>(dvr + mt * 32 + 8 * i + 4 * half) = b;
+      }
+  }
+}
+
+// dk' and dv of the depth >= 1 rows: wave per (row j, kv head g); lane holds d = lane + 64 i.
+template <int D>
+__global__ __launch_bounds__(256) void diag_kernel(const BwdParams p, const int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ depth_off, int K) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = blockIdx.x * (int64_t)4 + (threadIdx.x >> 6);
+  if (w >= (int64_t)(p.T - p.n) * p.Hkv) return;
+  const int j = p.n + (int)(w / p.Hkv), g = (int)(w % p.Hkv);
+  const int e = min(max(upper_index(depth_off, K + 1, j), 1), K - 1);  // depth of row j
+  const int anchor = min(max(idx[j], 0), p.n - 1);
+  const int q0 = min(max(p.qstart[anchor], 0), p.T);
+  const int q1 = min(max(p.qstart[anchor + 1], q0), p.T);
+  float kv[E], vv[E], dk[E], dv[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const size_t o = ((size_t)j * p.Hkv + g) * D + lane + 64 * i;
+    kv[i] = bf16_bits_to_f32(p.kr[o]);
+    vv[i] = bf16_bits_to_f32(p.v[o]);
+    dk[i] = dv[i] = 0.f;
+  }
+  for (int ent = q0 + e; ent < q1; ++ent) {  // the anchor's rows of depth >= e
+    const int row = min(max(p.qinfo[ent].x, 0), p.T - 1);
+    for (int hl = 0; hl < p.G; ++hl) {
+      const int h = g * p.G + hl;
+      float qv[E], dov[E], sd = 0.f, pd = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const size_t o = ((size_t)row * p.Hq + h) * D + lane + 64 * i;
+        qv[i] = bf16_bits_to_f32(p.qr[o]);
+        dov[i] = bf16_bits_to_f32(p.dob[o]);  // the rounded dO that Delta was formed with
+        sd = fmaf(qv[i], kv[i], sd);
+        pd = fmaf(dov[i], vv[i], pd);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        sd += __shfl_xor(sd, o, 64);
+        pd += __shfl_xor(pd, o, 64);
+      }
+      const size_t li = (size_t)h * p.T + row;
+      const float pr = __expf(sd * p.scale - p.lse[li]);
+      const float ds = pr * (pd - p.dlt[li]) * p.scale;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        dv[i] = fmaf(pr, dov[i], dv[i]);
+        dk[i] = fmaf(ds, qv[i], dk[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const size_t o = ((size_t)j * p.Hkv + g) * D + lane + 64 * i;
+    p.dk[o] = dk[i];
+    p.dv[o] = dv[i];
+  }
+}
+
+// dq' of half of a chunk's query slots (4 waves of 32).
+template <int D>
+__global__ __launch_bounds__(256) void dq_kernel(const BwdParams p) {
+  using C = BCfg<D>;
+  constexpr int NR = C::KBUF / 1024, NTB = C::TBYTES / 1024;
+  __shared__ __attribute__((aligned(1024))) char Ks0[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char Ks1[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char Vs0[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char Vs1[C::KBUF];
+  __shared__ __attribute__((aligned(1024))) char Ts0[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char Ts1[C::TBYTES];
+  __shared__ int s_range[6];
+  __shared__ int s_kp[KT], s_kd[KT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, half = lane >> 5;
+  const int hs = blockIdx.x & 1, rest = blockIdx.x >> 1;
+  const int g = rest % p.Hkv;
+  const int chunk = *p.nchunks - 1 - rest / p.Hkv;  // longest prefixes first
+  if (chunk < 0) return;
+  const int n = p.n, T = p.T, Hkv = p.Hkv;
+  const int2 ch = p.chunks[chunk];
+  const int j0 = min(max(ch.x, 0), T - 1);
+  const int jn = min(max(ch.y, 1), T - j0);
+  if (tid == 0) {
+    const int4 first = p.qinfo[j0], last = p.qinfo[j0 + jn - 1];
+    const int p_first = min(max(first.y, 0), n - 1), p_last = min(max(last.y, 0), n - 1);
+    const int lo_first = min(max(first.w, 0), p_first), lo_last = min(max(last.w, 0), p_last);
+    s_range[0] = lo_first;
+    s_range[1] = p_last;
+    s_range[2] = lo_last;
+    s_range[3] = p_first;
+    s_range[4] = min(max(p.qstart[p_first], 0), T);
+    s_range[5] = min(max(p.qstart[p_last + 1], 0), T);
+  }
+  __syncthreads();
+  const int k_lo = s_range[0], k_hi = s_range[1], full_lo = s_range[2], full_hi = s_range[3];
+  const int dg_lo = s_range[4], dg_hi = s_range[5];
+
+  const int slot = hs * 128 + wave * 32 + r32;
+  const int rl = slot % p.QR, hl = slot / p.QR;
+  const bool q_on = rl < jn;
+  const int4 qi = p.qinfo[j0 + min(rl, jn - 1)];
+  const int q_row = min(max(qi.x, 0), T - 1);
+  const int q_p = min(max(qi.y, 0), n - 1);
+  const int q_d = qi.z;
+  const int q_lo = min(max(qi.w, 0), q_p);
+  const int q_head = g * p.G + hl;
+  bf16x8 qf[C::DK], df[C::DK];
+  {
+    const size_t o = ((size_t)q_row * p.Hq + q_head) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) {
+      qf[kk] = ld8(p.qr + o + kk * 16);
+      df[kk] = ld8(p.dob + o + kk * 16);
+    }
+  }
+  const size_t li = (size_t)q_head * T + q_row;
+  const float lse2 = p.lse[li] * kLog2e, delta = p.dlt[li];
+  floatx16 acc[C::MT];
+#pragma unroll
+  for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+
+  // mode 0: no mask, 1: context range, 2: diagonal keys (meta in s_kp / s_kd)
+  auto compute = [&](const char* Ks, const char* Vs, const char* Ts, int mode, int key0) {
+    floatx16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    const char* kb = Ks + r32 * C::KROW + half * 16;
+    const char* vb = Vs + r32 * C::KROW + half * 16;
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) s = mfma32(ld8(kb + kk * 32), qf[kk], s);
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk) dp = mfma32(ld8(vb + kk * 32), df[kk], dp);
+    bf16x8 sb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kl = 8 * (r >> 2) + 4 * half + (r & 3);
+      bool ok = true;
+      if (mode == 1) {
+        const int key = key0 + kl;
+        ok = key >= q_lo && key <= q_p;
+      } else if (mode == 2) {
+        const int kp = s_kp[kl], kd = s_kd[kl];
+        ok = kp == q_p && kd >= 1 && kd <= q_d;
+      }
+      const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], p.c_log2, -lse2)) : 0.f;
+      sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - delta));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < C::MT; ++mt)
+        acc[mt] = mfma32(ld8(Ts + t_off(mt * 32 + r32, ks * 2 + half)), sb[ks], acc[mt]);
+  };
+
+  // ---- causal context: depth-0 key tiles ----
+  auto issue = [&](int t, char* Kd, char* Vd, char* Td) {
+    const char* bk = uniform_opaque(reinterpret_cast<const char*>(p.kr + ((size_t)t * KT * Hkv + g) * D));
+    const char* bv = uniform_opaque(reinterpret_cast<const char*>(p.vpad + ((size_t)t * KT * Hkv + g) * D));
+    const char* bt = uniform_opaque(reinterpret_cast<const char*>(p.kt + ((size_t)g * p.ntiles + t) * (size_t)(D * KT)));
+#pragma unroll
+    for (int j = 0; j < (NR + 3) / 4; ++j) {
+      const int b = wave + 4 * j;
+      if (b < NR) {
+        const int P = b * 1024 + lane * 16;
+        const int x = P / C::KROW, off = P - x * C::KROW;
+        const uint32_t o = (x < KT && off < D * 2) ? (uint32_t)(x * Hkv * D * 2 + off) : 0u;
+        dma16(bk + lane_opaque(o), Kd + b * 1024);
+        dma16(bv + lane_opaque(o), Vd + b * 1024);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < (NTB + 3) / 4; ++j) {
+      const int b = wave + 4 * j;
+      if (b < NTB) {
+        const int P = b * 1024 + lane * 16;
+        const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 2) & 3);
+        dma16(bt + lane_opaque((uint32_t)((d * KT + c * 8) * 2)), Td + b * 1024);
+      }
+    }
+  };
+  const int t_first = k_lo / KT, t_last = k_hi / KT;
+  issue(t_first, Ks0, Vs0, Ts0);
+  for (int t = t_first; t <= t_last; t += 2) {
+    wait_dma();
+    __syncthreads();
+    if (t + 1 <= t_last) issue(t + 1, Ks1, Vs1, Ts1);
+    {
+      const int key0 = t * KT;
+      const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
+      compute(Ks0, Vs0, Ts0, full ? 0 : 1, key0);
+    }
+    if (t + 1 > t_last) break;
+    wait_dma();
+    __syncthreads();
+    if (t + 2 <= t_last) issue(t + 2, Ks0, Vs0, Ts0);
+    {
+      const int key0 = (t + 1) * KT;
+      const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
+      compute(Ks1, Vs1, Ts1, full ? 0 : 1, key0);
+    }
+  }
+
+  // ---- diagonal extension: depth >= 1 rows of the chunk's anchors ----
+  for (int jb = dg_lo; jb < dg_hi; jb += KT) {
+    __syncthreads();
+    if (tid < KT) {
+      const int jk = jb + tid;
+      int kp = -1, kd = 0;
+      if (jk < dg_hi) {
+        const int4 e = p.qinfo[jk];
+        kp = e.y;
+        kd = e.z;
+      }
+      s_kp[tid] = kp;
+      s_kd[tid] = kd;
+    }
+    for (int q = tid; q < KT * (D / 8); q += 256) {
+      const int x = q / (D / 8), c = q % (D / 8), jk = jb + x;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (jk < dg_hi) {
+        const int row = min(max(p.qinfo[jk].x, 0), T - 1);
+        kv = *reinterpret_cast<const u32x4*>(p.kr + ((size_t)row * Hkv + g) * D + c * 8);
+        vv = *reinterpret_cast<const u32x4*>(p.v + ((size_t)row * Hkv + g) * D + c * 8);
+      }
+      *reinterpret_cast<u32x4*>(Ks0 + x * C::KROW + c * 16) = kv;
+      *reinterpret_cast<u32x4*>(Vs0 + x * C::KROW + c * 16) = vv;
+      const int tc = tchunk(x), te = telem(x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(Ts0 + t_off(c * 8 + e, tc) + te * 2) =
+            (uint16_t)((kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+    __syncthreads();
+    compute(Ks0, Vs0, Ts0, 2, 0);
+  }
+
+  if (q_on) {
+    float* dst = p.dq + ((size_t)q_row * p.Hq + q_head) * D;
+#pragma unroll
+    for (int mt = 0; mt < C::MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        floatx4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = acc[mt][4 * i + j] * p.scale;
+        *reinterpret_cast<floatx4*>(dst + mt * 32 + 8 * i + 4 * half) = w;
+      }
+  }
+}
+
+// dq = R^T dq', dk = R^T dk' in place (R: the RoPE rotation at the row's position).
+__global__ __launch_bounds__(256) void unrotate_kernel(const int4* __restrict__ qinfo,
+                                                       const float* __restrict__ cs,
+                                                       const float* __restrict__ sn,
+                                                       float* __restrict__ dq,
+                                                       float* __restrict__ dk, int T, int Hq,
+                                                       int Hkv, int D, int max_pos) {
+  const int hd = D / 2, H = Hq + Hkv;
+  const size_t total = (size_t)T * H * hd;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
+       t += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = t / ((size_t)H * hd);
+    const int rem = (int)(t % ((size_t)H * hd)), h = rem / hd, j = rem % hd;
+    const int4 qi = qinfo[e];
+    const int row = min(max(qi.x, 0), T - 1);
+    const int pos = min(max(qi.y - qi.w + qi.z, 0), max_pos);
+    const float c = cs[(size_t)pos * hd + j], s = sn[(size_t)pos * hd + j];
+    float* x = h < Hq ? dq + ((size_t)row * Hq + h) * D : dk + ((size_t)row * Hkv + (h - Hq)) * D;
+    const float a = x[j], b = x[j + hd];
+    x[j] = a * c + b * s;
+    x[j + hd] = b * c - a * s;
+  }
+}
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <typename F>
+hipError_t for_d(int D, F&& f) {
+  switch (D) {
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    case 256: return f(std::integral_constant<int, 256>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+AttnBwdLayout attn_bwd_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D) {
+  AttnBwdLayout L;
+  const int64_t G = Hq / std::max(1, Hkv);
+  const size_t ntiles = (size_t)((n + KT - 1) / KT);
+  L.ntq = (T * G + KT - 1) / KT;
+  const size_t tile_bytes = (size_t)Hkv * L.ntq * KT * D * 2;
+  size_t off = attn_layout(n, T, Hq, Hkv, D).total;
+  L.fwd = 0;
+  L.dob = off;   off += al256((size_t)T * Hq * D * 2);
+  L.dlt = off;   off += al256((size_t)T * Hq * 4);
+  L.kt = off;    off += al256(ntiles * KT * Hkv * D * 2);
+  L.vpad = off;  off += al256((size_t)(n + KT) * Hkv * D * 2);
+  L.qtr = off;   off += al256(tile_bytes);
+  L.qtt = off;   off += al256(tile_bytes);
+  L.dtr = off;   off += al256(tile_bytes);
+  L.dtt = off;   off += al256(tile_bytes);
+  L.smeta = off; off += al256((size_t)Hkv * L.ntq * KT * 16);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t* depth_off,
+                           const int32_t* cu_seqlens, const uint16_t* v, const float* out,
+                           const float* lse, const float* dout, const float* rope_cos,
+                           const float* rope_sin, float* dq, float* dk, float* dv, char* ws,
+                           hipStream_t stream) {
+  const AttnLayout F = attn_layout(a.n, a.T, a.Hq, a.Hkv, a.D);
+  const AttnBwdLayout L = attn_bwd_layout(a.n, a.T, a.Hq, a.Hkv, a.D);
+  BwdParams p;
+  p.qinfo = reinterpret_cast<const int4*>(ws + F.qinfo);
+  p.qstart = reinterpret_cast<const int32_t*>(ws + F.qstart);
+  p.cu = cu_seqlens;
+  p.chunks = reinterpret_cast<const int2*>(ws + F.chunks);
+  p.nchunks = reinterpret_cast<const int32_t*>(ws + F.nchunks);
+  p.qr = reinterpret_cast<const uint16_t*>(ws + F.qrot);
+  p.kr = reinterpret_cast<const uint16_t*>(ws + F.krot);
+  p.v = v;
+  p.vpad = reinterpret_cast<const uint16_t*>(ws + L.vpad);
+  p.kt = reinterpret_cast<const uint16_t*>(ws + L.kt);
+  p.dob = reinterpret_cast<const uint16_t*>(ws + L.dob);
+  p.lse = lse;
+  p.dlt = reinterpret_cast<const float*>(ws + L.dlt);
+  p.qtr = reinterpret_cast<const uint16_t*>(ws + L.qtr);
+  p.qtt = reinterpret_cast<const uint16_t*>(ws + L.qtt);
+  p.dtr = reinterpret_cast<const uint16_t*>(ws + L.dtr);
+  p.dtt = reinterpret_cast<const uint16_t*>(ws + L.dtt);
+  p.smeta = reinterpret_cast<const int4*>(ws + L.smeta);
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.n = a.n;
+  p.T = a.T;
+  p.S = a.S;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.G = a.Hq / a.Hkv;
+  p.QR = kAttnSlots / p.G;
+  p.ntiles = (a.n + KT - 1) / KT;
+  p.ntq = L.ntq;
+  p.scale = a.scale;
+  p.c_log2 = a.scale * kLog2e;
+  uint16_t* dob = reinterpret_cast<uint16_t*>(ws + L.dob);
+  float* dlt = reinterpret_cast<float*>(ws + L.dlt);
+  const int chunk_bound = std::min(F.max_chunks, (a.T + p.QR - 1) / p.QR + a.S);
+  const int nkb = (a.n + kBwdKeys - 1) / kBwdKeys;
+
+  return for_d(a.D, [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    const size_t items = (size_t)a.T * a.Hq * (D / 8);
+    hipLaunchKernelGGL(bwd_dout_kernel<D>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
+                       stream, dout, out, dob, dlt, a.T, a.Hq);
+    hipLaunchKernelGGL(transpose_tiles_kernel<D>, dim3(p.ntiles, a.Hkv), dim3(256), 0, stream,
+                       p.kr, const_cast<uint16_t*>(p.kt), a.n, a.Hkv, p.ntiles);
+    {
+      const size_t work = (size_t)(a.n + KT) * a.Hkv * D / 8;
+      const unsigned blocks = (unsigned)std::min<size_t>((work + 255) / 256, 65536);
+      hipLaunchKernelGGL(vpad_kernel, dim3(blocks), dim3(256), 0, stream, v,
+                         const_cast<uint16_t*>(p.vpad), a.n, a.Hkv, D);
+    }
+    hipLaunchKernelGGL(qtile_kernel<D>, dim3((unsigned)L.ntq, a.Hkv), dim3(256), 0, stream, p,
+                       const_cast<uint16_t*>(p.qtr), const_cast<uint16_t*>(p.qtt),
+                       const_cast<uint16_t*>(p.dtr), const_cast<uint16_t*>(p.dtt),
+                       const_cast<int4*>(p.smeta));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if constexpr (D <= 64) {
+      hipLaunchKernelGGL((dkdv_kernel<D, true, true>), dim3(nkb * a.Hkv), dim3(256), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, false, true>), dim3(nkb * a.Hkv), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<D, true, false>), dim3(nkb * a.Hkv), dim3(256), 0, stream, p);
+    }
+    if (a.T > a.n) {
+      const int64_t waves = (int64_t)(a.T - a.n) * a.Hkv;
+      hipLaunchKernelGGL(diag_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
+                         p, idx, depth_off, a.K);
+    }
+    hipLaunchKernelGGL(dq_kernel<D>, dim3(chunk_bound * a.Hkv * 2), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t work = (size_t)a.T * (a.Hq + a.Hkv) * (D / 2);
+    const unsigned blocks = (unsigned)std::min<size_t>((work + 255) / 256, 1 << 20);
+    hipLaunchKernelGGL(unrotate_kernel, dim3(blocks), dim3(256), 0, stream, p.qinfo, rope_cos,
+                       rope_sin, dq, dk, a.T, a.Hq, a.Hkv, D, a.max_pos);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace peagle

@@ -38,6 +38,10 @@ SIGNATURES = {
     "peagle_draft_attn_fwd": (_ATTN, _i32),
     "peagle_draft_attn_prepare": (_ATTN, _i32),
     "peagle_draft_attn_core": (_ATTN, _i32),
+    "peagle_draft_attn_bwd_workspace_bytes": ([_i64, _i64, _i32, _i32, _i32], _sz),
+    "peagle_draft_attn_bwd": ([_i64, _i32, _i64, _p, _p, _p, _p, _i32, _p, _p, _p, _i32, _i32,
+                               _i32, _f32, _p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
+                              _i32),
     "peagle_accept_prefix": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _p], _i32),
     "peagle_layer1_qkv_workspace_bytes": ([_i64, _i64, _i32], _sz),
     "peagle_layer1_qkv": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _f32, _p, _i32, _i32, _i32, _p,
@@ -213,6 +217,35 @@ def draft_attn(n, K, sel, cu_seqlens, q, k, v, cos, sin, out=None, lse=None, wor
     _check(fn, getattr(lib(), fn)(*_attn_args(n, K, sel, cu_seqlens, q, k, v, cos, sin, out,
                                                lse, workspace, scale)))
     return out, lse, workspace
+
+
+def draft_attn_bwd(n, K, sel, cu_seqlens, q, k, v, cos, sin, out, lse, dout, dq=None, dk=None,
+                   dv=None, workspace=None, scale=None):
+    """dq [T, Hq, D], dk and dv [T, Hkv, D] (fp32, with respect to the pre-RoPE inputs) of
+    the draft attention, from the forward's out and lse on the same inputs and dout."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (cos, "rope_cos"), (sin, "rope_sin"),
+                    (out, "out"), (lse, "lse"), (dout, "dout")):
+        _dev(t, name)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    if dq is None:
+        dq = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    if dk is None:
+        dk = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().peagle_draft_attn_bwd_workspace_bytes(n, T, Hq, Hkv, D)),
+                                dtype=torch.uint8, device=dev)
+    S = cu_seqlens.numel() - 1
+    _check("peagle_draft_attn_bwd", lib().peagle_draft_attn_bwd(
+        n, K, T, _ptr(sel["idx"]), _ptr(sel["depth_off"]), _ptr(sel["row_of"]), _ptr(cu_seqlens),
+        S, _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, D,
+        float(scale if scale is not None else 1.0 / math.sqrt(D)), _ptr(cos), _ptr(sin),
+        cos.shape[0] - 1, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel(), _stream()))
+    return dq, dk, dv, workspace
 
 
 # ---------------------------------------------------------------- verify

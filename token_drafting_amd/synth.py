@@ -33,6 +33,7 @@ TAG_D2T, TAG_FC_NORM = 29, 30
 TAG_SPEC_LOGITS, TAG_SPEC_TOK, TAG_SPEC_U, TAG_SPEC_W = 31, 32, 33, 34
 # stacked layer L >= 2 draws from tags TAG_STACK + 8 (L - 2) + 0 .. 7
 TAG_STACK = 40
+TAG_DOUT = 35
 
 # Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
 # layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
@@ -403,3 +404,8 @@ def sampled_verify_inputs_device(seed: int, drafts: int, K: int, V: int, spread:
     u = torch.rand((drafts, K), generator=gen(TAG_SPEC_U), device=device)
     w = torch.rand(drafts, generator=gen(TAG_SPEC_W), device=device)
     return dict(draft_logits=draft, target_logits=target, draft_tok=tok, u=u, w=w)
+
+
+def attn_grad_out(seed: int, T: int, Hq: int, D: int) -> np.ndarray:
+    """dL/d out of the draft attention [T, Hq, D]: float32 N(0, 1) (the backward's input)."""
+    return _rng(seed, TAG_DOUT).standard_normal((T, Hq, D), dtype=np.float32)
