@@ -225,3 +225,24 @@ def test_layer1_argument_errors(lib):
     assert peagle.layer1_qkv_workspace_bytes(64, 150, 640) == ((65 * 1280 * 2 + 255) // 256) * 256
     assert peagle.layer1_qkv_workspace_bytes(64, 64, 640) == 64 * 1280 * 2
     assert peagle.layer1_qkv_workspace_bytes(0, 10, 640) == 0
+
+
+def test_attn_bwd_argument_errors(lib):
+    """Host checks of peagle_draft_attn_bwd; fake aligned addresses are never dereferenced
+    because every call below fails before anything is enqueued."""
+    f = 1 << 20
+    n, K, T, Hq, Hkv, D = 256, 4, 648, 4, 1, 64
+    need = peagle.lib().peagle_draft_attn_bwd_workspace_bytes(n, T, Hq, Hkv, D)
+    fwd = peagle.attn_workspace_bytes(n, T, Hq, Hkv, D)
+    assert need > fwd > 0
+    assert peagle.lib().peagle_draft_attn_bwd_workspace_bytes(n, T, 3, 2, D) == 0
+
+    def call(D=D, lse=f, dout=f, dq=f, ws_bytes=need, scale=0.125):
+        return _code("peagle_draft_attn_bwd", n, K, T, f, f, f, f, 1, f, f, f, Hq, Hkv, D, scale,
+                     f, f, n + K, f, lse, dout, dq, f, f, f, ws_bytes, None)
+    assert call(D=96) == peagle.ERR_UNSUPPORTED
+    assert call(lse=None) == peagle.ERR_ARG
+    assert call(dout=None) == peagle.ERR_ARG
+    assert call(dq=f + 4) == peagle.ERR_ARG          # misaligned
+    assert call(scale=0.0) == peagle.ERR_ARG
+    assert call(ws_bytes=fwd) == peagle.ERR_WORKSPACE

@@ -94,6 +94,7 @@ struct BwdParams {
   float* dk;
   float* dv;
   int n, T, S, Hq, Hkv, G, QR, ntiles;
+  int nkb, seg_len;  // key blocks; query tiles per segment of a key block's range
   int64_t ntq;
   float scale, c_log2;
 };
@@ -246,22 +247,39 @@ __global__ __launch_bounds__(256) void qtile_kernel(const BwdParams p, uint16_t*
   }
 }
 
-// dk' (WK) and / or dv (WV) of the depth-0 keys [k0, k0 + 128) of kv head g. With both,
+// Zero fp32 x[0, count) (16 bytes per thread step).
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, size_t count4) {
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < count4;
+       t += (size_t)gridDim.x * blockDim.x)
+    *reinterpret_cast<floatx4*>(x + 4 * t) = floatx4{0.f, 0.f, 0.f, 0.f};
+}
+
+// dk' (WK) and / or dv (WV) of the depth-0 keys [k0, k0 + 128) of kv head g, from one
+// segment of the query tiles that see them (the first key blocks are seen by nearly every
+// tile, the last by few: segments of at most seg_len tiles keep the workgroups even).
+// Segments add into zeroed outputs with fp32 atomics. With both,
 // a lane holds its key's k' and v fragments and two accumulators; for D >= 128 that does
 // not fit the register file, so the two run as separate passes (the dV pass needs neither
 // v nor dP, and each pass streams three of the four query tiles).
 template <int D, bool WK, bool WV>
 __global__ __launch_bounds__(256) void dkdv_kernel(const BwdParams p) {
   using C = BCfg<D>;
-  constexpr int RQ = 0, RD = C::KBUF, RQT = 2 * C::KBUF, RDT = RQT + C::TBYTES;
-  constexpr int RM = RDT + C::TBYTES, STAGE = RM + 1024;
+  // LDS regions of one stage, only those the pass reads (the dV pass then fits twice per
+  // CU next to another workgroup)
+  constexpr int RQ = 0;
+  constexpr int RD = RQ + C::KBUF;
+  constexpr int RQT = RD + (WK ? C::KBUF : 0);
+  constexpr int RDT = RQT + (WK ? C::TBYTES : 0);
+  constexpr int RM = RDT + (WV ? C::TBYTES : 0);
+  constexpr int STAGE = RM + 1024;
   constexpr int NR = C::KBUF / 1024, NTB = C::TBYTES / 1024;
   __shared__ __attribute__((aligned(1024))) char buf0[STAGE];
   __shared__ __attribute__((aligned(1024))) char buf1[STAGE];
   __shared__ int s_rng[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, half = lane >> 5;
-  const int g = blockIdx.x % p.Hkv, kb = blockIdx.x / p.Hkv;
+  const int g = blockIdx.x % p.Hkv, rest = blockIdx.x / p.Hkv;
+  const int kb = rest % p.nkb, seg = rest / p.nkb;
   const int k0 = kb * kBwdKeys;
   if (k0 >= p.n) return;
   const int k1 = min(k0 + kBwdKeys, p.n) - 1;
@@ -271,11 +289,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const BwdParams p) {
     const int end = min(max(p.cu[s1 + 1], k1 + 1), p.n);
     const int64_t e0 = min(max(p.qstart[k0], 0), p.T);
     const int64_t e1 = min(max((int64_t)p.qstart[end], e0), (int64_t)p.T);
-    s_rng[0] = (int)(e0 * p.G / KT);
-    s_rng[1] = (int)((e1 * p.G + KT - 1) / KT);
+    const int64_t a = e0 * p.G / KT, b = (e1 * p.G + KT - 1) / KT;
+    const int64_t ts = a + (int64_t)seg * p.seg_len;
+    s_rng[0] = (int)std::min(ts, b);
+    s_rng[1] = (int)std::min(ts + p.seg_len, b);
   }
   __syncthreads();
   const int t0 = s_rng[0], t1 = s_rng[1];
+  if (t0 >= t1) return;  // an empty segment (the same for the whole workgroup)
 
   const int key = k0 + wave * KT + r32;
   const bool key_on = key <= k1;
@@ -393,16 +414,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        floatx4 a, b;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if constexpr (WK) a[j] = dkt[mt][4 * i + j] * p.scale;
-          if constexpr (WV) b[j] = dvt[mt][4 * i + j];
+          const int d = mt * 32 + 8 * i + 4 * half + j;
+          if constexpr (WK) unsafeAtomicAdd(dkr + d, dkt[mt][4 * i + j] * p.scale);
+          if constexpr (WV) unsafeAtomicAdd(dvr + d, dvt[mt][4 * i + j]);
         }
-        if constexpr (WK) *reinterpret_cast<floatx4*>(dkr + mt * 32 + 8 * i + 4 * half) = a;
-        if constexpr (WV) *reinterpret_cast<floatx4*>(dvr + mt * 32 + 8 * i + 4 * half) = b;
-      }
   }
 }
 
@@ -754,6 +772,10 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
   p.QR = kAttnSlots / p.G;
   p.ntiles = (a.n + KT - 1) / KT;
   p.ntq = L.ntq;
+  p.nkb = (a.n + kBwdKeys - 1) / kBwdKeys;
+  // up to 16 segments per key block, at least 32 tiles each
+  const int nseg = (int)std::min<int64_t>(16, std::max<int64_t>(1, L.ntq / 32));
+  p.seg_len = (int)((L.ntq + nseg - 1) / nseg);
   p.scale = a.scale;
   p.c_log2 = a.scale * kLog2e;
   uint16_t* dob = reinterpret_cast<uint16_t*>(ws + L.dob);
@@ -780,11 +802,18 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
                        const_cast<int4*>(p.smeta));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    {
+      const size_t count4 = (size_t)a.n * a.Hkv * D / 4;  // depth-0 rows of dk and dv
+      const unsigned zb = (unsigned)std::min<size_t>((count4 + 255) / 256, 65536);
+      hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, stream, dk, count4);
+      hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, stream, dv, count4);
+    }
+    const dim3 kgrid((unsigned)((int64_t)nkb * a.Hkv * nseg));
     if constexpr (D <= 64) {
-      hipLaunchKernelGGL((dkdv_kernel<D, true, true>), dim3(nkb * a.Hkv), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<D, true, true>), kgrid, dim3(256), 0, stream, p);
     } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, false, true>), dim3(nkb * a.Hkv), dim3(256), 0, stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<D, true, false>), dim3(nkb * a.Hkv), dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<D, false, true>), kgrid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((dkdv_kernel<D, true, false>), kgrid, dim3(256), 0, stream, p);
     }
     if (a.T > a.n) {
       const int64_t waves = (int64_t)(a.T - a.n) * a.Hkv;
