@@ -36,4 +36,4 @@ closed forms, published test outputs, library routines, independent formulations
 or brute force. The SplitMix64 hash is pinned by the generator's published
 outputs for seed 0.
 """
-from . import bf16, cod, fuse, rope, attention, decode, layer, verify  # noqa: F401
+from . import bf16, cod, fuse, rope, attention, decode, layer, verify, loss  # noqa: F401
