@@ -244,6 +244,7 @@ def main():
                               "ms_without_fc_norm": round(stage_ms["fuse_inputs"], 4)}
     result["attn_bwd"] = attn_bwd_bench(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse,
                                         seed, P, args.steps, args.warmup)
+    result["depth_ce"] = depth_ce_bench(sel["depth_off"], args.steps, args.warmup)
     result["verify_d2t"] = verify_d2t_bench(args.steps, args.warmup)
     result["verify_sampled"] = verify_sampled_bench(args.steps, args.warmup)
     result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, hidden, emb, out,
@@ -340,6 +341,33 @@ def attn_bwd_bench(n, K, sel, cu, q, k, v, cos, sin, out, lse, seed, pairs, step
             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "includes": "forward preparation (RoPE, row list), dO cast, tile layouts, dK/dV, dQ, "
                         "inverse RoPE"}
+
+
+def depth_ce_bench(depth_off, steps, warmup, V=8192):
+    """Time peagle_depth_ce (depth-weighted cross-entropy and its bf16 gradient) over the
+    step's draft rows and the 8192-id draft vocabulary; logits N(0, 4) and uniform labels
+    drawn on the device with torch's seeded generator. Algorithmic bytes: the logits read
+    once and the gradient written once (plus labels)."""
+    import torch
+    from token_drafting_amd import peagle
+
+    T = int(depth_off[-1].item())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(37)
+    logits = (2.0 * torch.randn((T, V), generator=g, device="cuda")).to(torch.bfloat16).view(torch.int16)
+    labels = torch.randint(0, V, (T,), generator=g, device="cuda", dtype=torch.int32)
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    dl = torch.empty(depth_off.numel() - 1, dtype=torch.float32, device="cuda")
+    grad = torch.empty_like(logits)
+    ws = torch.empty(int(peagle.lib().peagle_depth_ce_workspace_bytes(T, depth_off.numel() - 1)),
+                     dtype=torch.uint8, device="cuda")
+    ms = _time_calls(lambda: peagle.depth_ce(depth_off, logits, labels, 0.8, True, loss, dl, grad,
+                                             ws), steps, warmup)
+    nbytes = 2 * T * V * 2 + T * 4
+    del logits, grad
+    torch.cuda.empty_cache()
+    return {"rows": T, "vocab": V, "ms_per_call": round(ms, 4),
+            "hbm_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1), "loss": round(float(loss.item()), 4)}
 
 
 def verify_sampled_bench(steps, warmup, N=4096, K=8, V=32000):

@@ -221,6 +221,31 @@ int peagle_draft_attn_bwd(int64_t n, int32_t K, int64_t T, const int32_t *idx,
                           void *stream);
 
 /*
+ * peagle_depth_ce -- depth-weighted cross-entropy of the draft rows and its gradient
+ * [N, description: the parallel masked-depth loss with the 0.8**d weighted-mean schedule
+ * and the draft-vocab projection; validation: starting loss ~ ln(draft vocab);
+ * out-of-draft-vocab masking]. Per depth d, L_d = mean over the depth's rows whose label
+ * lies in [0, V) of lse(logits) - logits[label]; the loss is
+ * sum_d decay^d L_d / sum_d decay^d over the depths with at least one such row.
+ *   depth_off   int32[K+1]   (device) first row of each depth, depth_off[K] = T
+ *   logits      bf16[T, V]   draft-vocab logits of the draft rows
+ *   labels      int32[T]     draft-vocab id each row should predict; -1 (or any id outside
+ *                            [0, V)) masks the row
+ *   decay       in (0, 1]    0.8 in the pages' schedule
+ *   loss_out    fp32[1] out
+ *   depth_loss  fp32[K] out or NULL; NaN for a depth with no unmasked row
+ *   dlogits     bf16[T, V] out or NULL: d loss / d logits (zero rows where masked)
+ *   workspace   >= peagle_depth_ce_workspace_bytes(T, K), 256-byte aligned
+ * Row statistics in fp32, the reductions over rows in fp64 in a fixed order: the same
+ * inputs give the same loss bit for bit.
+ */
+size_t peagle_depth_ce_workspace_bytes(int64_t T, int32_t K);
+int peagle_depth_ce(int64_t T, int32_t K, int32_t vocab, const int32_t *depth_off,
+                    const peagle_bf16 *logits, const int32_t *labels, float decay,
+                    float *loss_out, float *depth_loss, peagle_bf16 *dlogits, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
  * peagle_accept_prefix -- greedy verification [G, "Inference Process"]: the target
  * checks every draft token in one pass and the longest correct prefix is accepted.
  *   draft_logits, target_logits  bf16[N, K, V]; row [i, d] of target_logits scores the

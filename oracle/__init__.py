@@ -26,7 +26,9 @@ Modules:
                 position over a KV cache (the flat [context, mask_1 ..] layout).
 - ``layer``     the first draft layer's attention inputs: RMSNorm of the embedding and
                 hidden halves, their concatenation, the QKV projection.
-- ``verify``    greedy verification and the longest accepted prefix.
+- ``verify``    greedy verification and the longest accepted prefix, the d2t variant and
+                sampling acceptance.
+- ``loss``      the depth-weighted cross-entropy of the draft rows and its gradient.
 
 Inputs are bf16 bit patterns (uint16) or integer arrays; ``bf16`` converts the
 bit patterns to float64 exactly.

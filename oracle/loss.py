@@ -30,10 +30,11 @@ from .bf16 import to_f64
 
 
 def depth_weighted_ce_f64(logits, labels, depth_off, decay: float = 0.8, want_grad=True,
-                          block: int = 2048) -> dict:
+                          block: int = 2048, grad_rows=None) -> dict:
     """logits [T, V] (float64 or bf16 bits), labels int [T] (-1: masked), depth_off [K+1].
     Returns loss, depth_loss [K] (nan where a depth has no unmasked row), row_loss [T]
-    (0 for masked rows), count [K] and, with want_grad, grad [T, V]."""
+    (0 for masked rows), count [K] and, with want_grad, grad [T, V] (or, with grad_rows,
+    the gradient of those rows only, for workloads too large for the whole tensor)."""
     logits = to_f64(logits) if np.asarray(logits).dtype == np.uint16 else np.asarray(logits, np.float64)
     labels = np.asarray(labels, dtype=np.int64)
     depth_off = np.asarray(depth_off, dtype=np.int64)
@@ -59,7 +60,18 @@ def depth_weighted_ce_f64(logits, labels, depth_off, decay: float = 0.8, want_gr
             total += decay ** d * depth_loss[d]
     out = dict(loss=total / W if W > 0 else 0.0, depth_loss=depth_loss, row_loss=row_loss,
                count=count)
-    if want_grad:
+    if want_grad and grad_rows is not None:
+        gr = np.asarray(grad_rows, dtype=np.int64)
+        dep = np.searchsorted(depth_off, gr, side="right") - 1
+        g = np.exp(logits[gr] - lse[gr, None])
+        for i, (r, d) in enumerate(zip(gr, dep)):
+            if not valid[r] or count[d] == 0:
+                g[i] = 0.0
+                continue
+            g[i, labels[r]] -= 1.0
+            g[i] *= decay ** d / (W * count[d])
+        out["grad"] = g
+    elif want_grad:
         grad = np.zeros((T, V))
         for d in range(K):
             if count[d] == 0:

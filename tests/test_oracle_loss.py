@@ -73,3 +73,15 @@ def test_single_depth_is_the_plain_mean():
     got = oloss.depth_weighted_ce_f64(x, labels, np.array([0, 30]), want_grad=False)
     lse = np.log(np.exp(x).sum(axis=1))
     assert abs(got["loss"] - np.mean(lse - x[np.arange(30), labels])) < 1e-12
+
+
+def test_gradient_of_chosen_rows_equals_the_full_gradient():
+    rng = np.random.default_rng(4)
+    off = _layout([20, 14, 0, 9])
+    T, V = int(off[-1]), 13
+    x, labels = rng.standard_normal((T, V)), rng.integers(0, V, T)
+    labels[[2, 21]] = -1
+    full = oloss.depth_weighted_ce_f64(x, labels, off)
+    rows = np.array([0, 2, 19, 20, 21, 33, T - 1])
+    sub = oloss.depth_weighted_ce_f64(x, labels, off, grad_rows=rows)
+    np.testing.assert_allclose(sub["grad"], full["grad"][rows], atol=1e-15)

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpeagle.so")
 SOURCES = ["abi.cpp", "cod.hip", "fuse.hip", "rope.hip", "attn.hip", "accept.hip", "decode.hip", "layer.hip", "mlp.hip",
-           "sample.hip", "attn_bwd.hip"]
+           "sample.hip", "attn_bwd.hip",
+           "loss.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

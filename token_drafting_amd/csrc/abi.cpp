@@ -266,6 +266,25 @@ int peagle_draft_attn_bwd(int64_t n, int32_t K, int64_t T, const int32_t* idx,
                                    rope_sin, dq, dk, dv, c.ws, c.stream));
 }
 
+size_t peagle_depth_ce_workspace_bytes(int64_t T, int32_t K) {
+  if (T < 1 || T > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return 0;
+  return depth_ce_workspace_bytes(T, K);
+}
+
+int peagle_depth_ce(int64_t T, int32_t K, int32_t vocab, const int32_t* depth_off,
+                    const peagle_bf16* logits, const int32_t* labels, float decay,
+                    float* loss_out, float* depth_loss, peagle_bf16* dlogits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (T < 1 || T > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS || vocab < 1) return PEAGLE_ERR_ARG;
+  if (!(decay > 0.f) || !(decay <= 1.f)) return PEAGLE_ERR_ARG;
+  if (!depth_off || !logits || !labels || !loss_out || !workspace) return PEAGLE_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PEAGLE_ERR_ARG;
+  if (workspace_bytes < depth_ce_workspace_bytes(T, K)) return PEAGLE_ERR_WORKSPACE;
+  return status_of(launch_depth_ce(T, K, vocab, depth_off, logits, labels, decay, loss_out,
+                                   depth_loss, dlogits, static_cast<char*>(workspace),
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int peagle_accept_prefix(int32_t num_drafts, int32_t K, int32_t vocab,
                          const peagle_bf16* draft_logits, const peagle_bf16* target_logits,
                          int32_t* draft_tok, int32_t* target_tok, int32_t* accept_len,

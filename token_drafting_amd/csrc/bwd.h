@@ -1,5 +1,6 @@
-// Host-side launcher of the draft attention backward. Internal to libpeagle: arguments are
-// validated by the C entry point, which runs the forward's preparation (rotated q and k,
+// Host-side launchers of the training side: the draft attention backward and the
+// depth-weighted cross-entropy. Internal to libpeagle: arguments are validated by the C
+// entry points; the backward's runs the forward's preparation (rotated q and k,
 // anchor-major row list, chunk table) into the head of the same workspace first.
 #pragma once
 
@@ -28,6 +29,14 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
                            const int32_t* cu_seqlens, const uint16_t* v, const float* out,
                            const float* lse, const float* dout, const float* rope_cos,
                            const float* rope_sin, float* dq, float* dk, float* dv, char* ws,
+                           hipStream_t stream);
+
+// Depth-weighted cross-entropy: workspace holds the per-row losses (fp32 [T]) and the
+// per-depth counts of unmasked rows (int32 [K]).
+size_t depth_ce_workspace_bytes(int64_t T, int32_t K);
+hipError_t launch_depth_ce(int64_t T, int32_t K, int32_t V, const int32_t* depth_off,
+                           const uint16_t* logits, const int32_t* labels, float decay,
+                           float* loss_out, float* depth_loss, uint16_t* dlogits, char* ws,
                            hipStream_t stream);
 
 }  // namespace peagle

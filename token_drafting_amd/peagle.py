@@ -43,6 +43,8 @@ SIGNATURES = {
                                _i32, _f32, _p, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _sz, _p],
                               _i32),
     "peagle_accept_prefix": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _p], _i32),
+    "peagle_depth_ce_workspace_bytes": ([_i64, _i32], _sz),
+    "peagle_depth_ce": ([_i64, _i32, _i32, _p, _p, _p, _f32, _p, _p, _p, _p, _sz, _p], _i32),
     "peagle_layer1_qkv_workspace_bytes": ([_i64, _i64, _i32], _sz),
     "peagle_layer1_qkv": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _f32, _p, _i32, _i32, _i32, _p,
                            _p, _p, _p, _sz, _p], _i32),
@@ -246,6 +248,31 @@ def draft_attn_bwd(n, K, sel, cu_seqlens, q, k, v, cos, sin, out, lse, dout, dq=
         cos.shape[0] - 1, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), workspace.numel(), _stream()))
     return dq, dk, dv, workspace
+
+
+def depth_ce(depth_off, logits, labels, decay=0.8, want_grad=True, loss=None, depth_loss=None,
+             dlogits=None, workspace=None):
+    """Depth-weighted cross-entropy: loss [1] (fp32), per-depth losses [K] and, with
+    want_grad, d loss / d logits [T, V] (bf16 bits, int16)."""
+    for t, name in ((depth_off, "depth_off"), (logits, "logits"), (labels, "labels")):
+        _dev(t, name)
+    T, V = logits.shape
+    K = depth_off.numel() - 1
+    dev = logits.device
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+    if depth_loss is None:
+        depth_loss = torch.empty(K, dtype=torch.float32, device=dev)
+    if want_grad and dlogits is None:
+        dlogits = torch.empty((T, V), dtype=torch.int16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib().peagle_depth_ce_workspace_bytes(T, K)),
+                                dtype=torch.uint8, device=dev)
+    _check("peagle_depth_ce", lib().peagle_depth_ce(
+        T, K, V, _ptr(depth_off), _ptr(logits), _ptr(labels), float(decay), _ptr(loss),
+        _ptr(depth_loss), _ptr(dlogits) if want_grad else None, _ptr(workspace),
+        workspace.numel(), _stream()))
+    return loss, depth_loss, dlogits
 
 
 # ---------------------------------------------------------------- verify

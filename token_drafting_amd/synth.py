@@ -34,6 +34,7 @@ TAG_SPEC_LOGITS, TAG_SPEC_TOK, TAG_SPEC_U, TAG_SPEC_W = 31, 32, 33, 34
 # stacked layer L >= 2 draws from tags TAG_STACK + 8 (L - 2) + 0 .. 7
 TAG_STACK = 40
 TAG_DOUT = 35
+TAG_CE_LOGITS, TAG_CE_LABELS = 36, 37
 
 # Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
 # layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
@@ -409,3 +410,13 @@ def sampled_verify_inputs_device(seed: int, drafts: int, K: int, V: int, spread:
 def attn_grad_out(seed: int, T: int, Hq: int, D: int) -> np.ndarray:
     """dL/d out of the draft attention [T, Hq, D]: float32 N(0, 1) (the backward's input)."""
     return _rng(seed, TAG_DOUT).standard_normal((T, Hq, D), dtype=np.float32)
+
+
+def ce_inputs(seed: int, T: int, V: int, p_mask: float = 0.05, spread: float = 2.0) -> dict:
+    """Draft-vocab logits [T, V] (bf16 bits of N(0, spread^2)) and labels [T] (int32,
+    uniform over [0, V), a p_mask share set to -1: targets outside the draft vocabulary)."""
+    logits = normal_bf16(seed, TAG_CE_LOGITS, (T, V), std=spread)
+    rng = _rng(seed, TAG_CE_LABELS)
+    labels = rng.integers(0, V, size=T).astype(np.int32)
+    labels[rng.random(T) < p_mask] = -1
+    return dict(logits=logits, labels=labels)
