@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, size_t
 // not fit the register file, so the two run as separate passes (the dV pass needs neither
 // v nor dP, and each pass streams three of the four query tiles).
 template <int D, bool WK, bool WV>
-__global__ __launch_bounds__(256) void dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(const BwdParams p) {
   using C = BCfg<D>;
   // LDS regions of one stage, only those the pass reads (the dV pass then fits twice per
   // CU next to another workgroup)
@@ -397,15 +397,24 @@ __global__ __launch_bounds__(256) void dkdv_kernel(const BwdParams p) {
     sched_reads_ahead<2 * C::MT * ((WK ? 1 : 0) + (WV ? 1 : 0)), 2, 1>();
   };
 
-  // one compute body with the buffer chosen at run time: two inlined copies (one per
-  // buffer) made the register allocator shuttle the accumulators between them
-  if (t0 < t1) issue(t0, buf0);
-  for (int t = t0; t < t1; ++t) {
-    const bool odd = ((t - t0) & 1) != 0;
+  // two tiles per iteration over two static buffers, one loop exit, odd last tile after
+  // the loop (as in dq_kernel)
+  issue(t0, buf0);
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
     wait_dma();
-    __syncthreads();  // tile t landed in its buffer; the other one is free
-    if (t + 1 < t1) issue(t + 1, odd ? buf0 : buf1);
-    compute(odd ? buf1 : buf0);
+    __syncthreads();  // tile t landed in buffer 0; buffer 1 is free
+    issue(t + 1, buf1);
+    compute(buf0);
+    wait_dma();
+    __syncthreads();  // tile t+1 landed in buffer 1; buffer 0 is free
+    if (t + 2 < t1) issue(t + 2, buf0);
+    compute(buf1);
+  }
+  if (t < t1) {
+    wait_dma();
+    __syncthreads();
+    compute(buf0);
   }
 
   if (key_on) {
@@ -482,8 +491,9 @@ __global__ __launch_bounds__(256) void diag_kernel(const BwdParams p, const int3
 }
 
 // dq' of half of a chunk's query slots (4 waves of 32).
+// Two waves per SIMD at D <= 128 (registers and LDS both fit twice); one at D = 256.
 template <int D>
-__global__ __launch_bounds__(256) void dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdParams p) {
   using C = BCfg<D>;
   constexpr int NR = C::KBUF / 1024, NTB = C::TBYTES / 1024;
   __shared__ __attribute__((aligned(1024))) char Ks0[C::KBUF];
@@ -605,26 +615,28 @@ __global__ __launch_bounds__(256) void dq_kernel(const BwdParams p) {
       }
     }
   };
+  // Two tiles per iteration, each buffer a distinct static array (so that LDS reads of one
+  // buffer do not wait on the DMA into the other), a single loop exit, and an odd last
+  // tile after the loop (an exit between the two halves made the register allocator
+  // shuttle the accumulators).
   const int t_first = k_lo / KT, t_last = k_hi / KT;
+  auto full_tile = [&](int key0) { return key0 >= full_lo && key0 + KT - 1 <= full_hi; };
   issue(t_first, Ks0, Vs0, Ts0);
-  for (int t = t_first; t <= t_last; t += 2) {
+  int t = t_first;
+  for (; t + 1 <= t_last; t += 2) {
     wait_dma();
-    __syncthreads();
-    if (t + 1 <= t_last) issue(t + 1, Ks1, Vs1, Ts1);
-    {
-      const int key0 = t * KT;
-      const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
-      compute(Ks0, Vs0, Ts0, full ? 0 : 1, key0);
-    }
-    if (t + 1 > t_last) break;
+    __syncthreads();  // tile t landed in buffer 0; buffer 1 is free
+    issue(t + 1, Ks1, Vs1, Ts1);
+    compute(Ks0, Vs0, Ts0, full_tile(t * KT) ? 0 : 1, t * KT);
     wait_dma();
-    __syncthreads();
+    __syncthreads();  // tile t+1 landed in buffer 1; buffer 0 is free
     if (t + 2 <= t_last) issue(t + 2, Ks0, Vs0, Ts0);
-    {
-      const int key0 = (t + 1) * KT;
-      const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
-      compute(Ks1, Vs1, Ts1, full ? 0 : 1, key0);
-    }
+    compute(Ks1, Vs1, Ts1, full_tile((t + 1) * KT) ? 0 : 1, (t + 1) * KT);
+  }
+  if (t == t_last) {
+    wait_dma();
+    __syncthreads();
+    compute(Ks0, Vs0, Ts0, full_tile(t * KT) ? 0 : 1, t * KT);
   }
 
   // ---- diagonal extension: depth >= 1 rows of the chunk's anchors ----
