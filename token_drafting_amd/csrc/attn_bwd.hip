@@ -254,10 +254,13 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, size_t
     *reinterpret_cast<floatx4*>(x + 4 * t) = floatx4{0.f, 0.f, 0.f, 0.f};
 }
 
-// dk' (WK) and / or dv (WV) of the depth-0 keys [k0, k0 + 128) of kv head g, from one
-// segment of the query tiles that see them (the first key blocks are seen by nearly every
-// tile, the last by few: segments of at most seg_len tiles keep the workgroups even).
-// Segments add into zeroed outputs with fp32 atomics. With both,
+// dk' (WK) and / or dv (WV) of the depth-0 keys [k0, k0 + 128) of kv head g, from the
+// query tiles that see them inside one absolute segment of seg_len tiles of the list.
+// Workgroups are ordered segment-major, so those running at the same time stream the same
+// few segments and the tiles come from HBM about once per segment (later blocks hit the
+// caches), instead of once per key block; and no workgroup takes more than seg_len tiles
+// (the first key blocks are seen by nearly every tile, the last by few). Segments add
+// into zeroed outputs with fp32 atomics. With both,
 // a lane holds its key's k' and v fragments and two accumulators; for D >= 128 that does
 // not fit the register file, so the two run as separate passes (the dV pass needs neither
 // v nor dP, and each pass streams three of the four query tiles).
@@ -289,10 +292,11 @@ __global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(co
     const int end = min(max(p.cu[s1 + 1], k1 + 1), p.n);
     const int64_t e0 = min(max(p.qstart[k0], 0), p.T);
     const int64_t e1 = min(max((int64_t)p.qstart[end], e0), (int64_t)p.T);
+    // this block's tiles [a, b) within absolute segment seg of the tile list
     const int64_t a = e0 * p.G / KT, b = (e1 * p.G + KT - 1) / KT;
-    const int64_t ts = a + (int64_t)seg * p.seg_len;
-    s_rng[0] = (int)std::min(ts, b);
-    s_rng[1] = (int)std::min(ts + p.seg_len, b);
+    const int64_t ts = (int64_t)seg * p.seg_len;
+    s_rng[0] = (int)std::max(a, ts);
+    s_rng[1] = (int)std::min(b, ts + p.seg_len);
   }
   __syncthreads();
   const int t0 = s_rng[0], t1 = s_rng[1];
@@ -785,9 +789,9 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
   p.ntiles = (a.n + KT - 1) / KT;
   p.ntq = L.ntq;
   p.nkb = (a.n + kBwdKeys - 1) / kBwdKeys;
-  // up to 16 segments per key block, at least 32 tiles each
-  const int nseg = (int)std::min<int64_t>(16, std::max<int64_t>(1, L.ntq / 32));
-  p.seg_len = (int)((L.ntq + nseg - 1) / nseg);
+  // absolute segments of the tile list: about 16 for large lists, 32 to 512 tiles each
+  p.seg_len = (int)std::min<int64_t>(512, std::max<int64_t>(32, (L.ntq + 15) / 16));
+  const int nseg = (int)((L.ntq + p.seg_len - 1) / p.seg_len);
   p.scale = a.scale;
   p.c_log2 = a.scale * kLog2e;
   uint16_t* dob = reinterpret_cast<uint16_t*>(ws + L.dob);
