@@ -104,7 +104,9 @@ def main():
     if args.decode == "only":
         res = {name: decode_bench(name, args.steps, args.warmup)
                for name in sorted(synth.DECODE_CONFIGS)}
-        print(json.dumps({"decode": res}), flush=True)
+        loop = {name: decode_loop_bench(name, args.steps, args.warmup)
+                for name in sorted(synth.DECODE_CONFIGS)}
+        print(json.dumps({"decode": res, "decode_loop": loop}), flush=True)
         return
     cfg = synth.CONFIGS[args.config]
     seed = args.config
@@ -255,6 +257,8 @@ def main():
         torch.cuda.empty_cache()
         result["decode"] = {name: decode_bench(name, args.steps, args.warmup)
                             for name in sorted(synth.DECODE_CONFIGS)}
+        result["decode_loop"] = {name: decode_loop_bench(name, args.steps, args.warmup)
+                                 for name in sorted(synth.DECODE_CONFIGS)}
 
     # ---------------- oracle on the host cores (bounded sample)
     if not args.no_cpu_baseline:
@@ -533,6 +537,73 @@ def decode_bench(name, steps, warmup):
                          "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                          "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
                          "traffic": None if rec is None else int(round(rec["call_bytes"]))}}
+
+
+def decode_loop_bench(name, steps, warmup):
+    """Time one iteration of the decode loop on an inference workload over a cache that
+    grows in place: decode attention of the K new rows over the current lengths,
+    verification of [B, K, 32000] draft/target logits, and the append of accept_len + 1
+    rows per request (keys rotated at their positions, values into their V tiles). Each
+    request's capacity is its context plus room for every timed iteration; inputs drawn on
+    the device with torch's seeded generator."""
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    cfg = synth.DECODE_CONFIGS[name]
+    B, K, Hq, Hkv, D = cfg["B"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"]
+    lens0 = synth.decode_lengths(31, B, cfg["ctx_lo"], cfg["ctx_hi"])
+    cap = lens0 + (K + 1) * (steps + warmup + 1)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(cap)]).astype(np.int32)).cuda()
+    total, max_cap = int(cap.sum()), int(cap.max())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(43)
+
+    def bf16(shape):
+        return torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16).view(torch.int16)
+    kc, v_full = bf16((total, Hkv, D)), bf16((total, Hkv, D))
+    lens = [torch.from_numpy(lens0.astype(np.int32)).cuda(), torch.empty(B, dtype=torch.int32, device="cuda")]
+    vt = peagle.decode_pack_v_lens(cu, lens[0], max_cap, v_full)
+    del v_full
+    q, k, v = bf16((B, K, Hq, D)), bf16((B, K, Hkv, D)), bf16((B, K, Hkv, D))
+    dl, tl = bf16((B, K, 32000)), bf16((B, K, 32000))
+    k_app, v_app = bf16((B, K + 1, Hkv, D)), bf16((B, K + 1, Hkv, D))
+    cos, sin = peagle.rope_table(D, cfg["theta"], max_cap + K - 1)
+    out = torch.empty((B, K, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, K, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(peagle.decode_workspace_bytes(B, K, Hq, Hkv, D, total, max_cap),
+                     dtype=torch.uint8, device="cuda")
+    dtok = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ttok, alen = torch.empty_like(dtok), torch.empty(B, dtype=torch.int32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def iteration(i, e=None):
+        src, dst = lens[i % 2], lens[(i + 1) % 2]
+        if e is not None:
+            e[0].record()
+        peagle.draft_decode_attn_lens(cu, src, max_cap, kc, vt, q, k, v, cos, sin, out, lse, ws)
+        if e is not None:
+            e[1].record()
+        peagle.accept_prefix(dl, tl, dtok, ttok, alen)
+        if e is not None:
+            e[2].record()
+        peagle.decode_append(cu, src, alen, 1, max_cap, k_app, v_app, cos, sin, kc, vt, dst)
+        if e is not None:
+            e[3].record()
+
+    for i in range(warmup):
+        iteration(i)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        iteration(warmup + i, ev[i])
+    torch.cuda.synchronize()
+    part = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(3)] for i in range(steps)])
+    grown = int((lens[(warmup + steps) % 2].cpu().numpy() - lens0).sum())
+    del kc, vt, ws, dl, tl
+    torch.cuda.empty_cache()
+    m = part.mean(axis=0)
+    return {"workload": cfg["workload"], "ms_per_iteration": round(float(m.sum()), 4),
+            "decode_attn_ms": round(float(m[0]), 4), "verify_ms": round(float(m[1]), 4),
+            "append_ms": round(float(m[2]), 4), "context_tokens_added": grown}
 
 
 def cpu_baseline(cfg, seed, qkv, cu, idx, depth_off, rows_wanted):

@@ -485,6 +485,49 @@ int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t *cu_ctx,
                              int32_t rope_max_pos, float *out, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/*
+ * The decode loop over a cache that grows in place [G, "Inference Process": drafting
+ * repeats from the last accepted token]: each request owns a capacity in the cache and
+ * a current length inside it, and after verification the newly committed tokens' keys
+ * and values are appended where they belong instead of repacking the cache.
+ *   cu_cap      int32[B+1]  (device) starts and capacities: request b owns cache rows
+ *                           [cu_cap[b], cu_cap[b+1]) and V tiles laid out as for
+ *                           peagle_decode_pack_v over those capacities
+ *   lens        int32[B]    (device) current context lengths, 0 <= lens[b] <= capacity
+ *   total_cap = cu_cap[B];  max_cap >= every capacity (it bounds the work split)
+ * peagle_decode_pack_v_lens: V tiles of the first lens[b] rows of each request, zeros in
+ *   the rest of each capacity (appended rows and masked slots then never meet stale data).
+ * peagle_draft_decode_attn_lens: peagle_draft_decode_attn with L_b = lens[b]; the new rows
+ *   sit at positions lens[b] + d. rope_max_pos >= max_cap + K - 1.
+ * peagle_decode_append: request b takes m_b = n_new[b] + n_add new rows (rows 0 .. m_b - 1
+ *   of k_new, v_new bf16[B, max_new, Hkv, D], pre-RoPE) at positions lens_in[b] + j: keys
+ *   rotated at those positions into k_cache, values into their V-tile slots. Rows past the
+ *   capacity are dropped. lens_out[b] = min(lens_in[b] + m_b, capacity) (lens_out and
+ *   lens_in distinct). With n_new = accept_len from verification and n_add = 1, the
+ *   accepted drafts and the next anchor join the context. rope_max_pos >= max_cap - 1.
+ */
+int peagle_decode_pack_v_lens(int32_t num_reqs, const int32_t *cu_cap, const int32_t *lens,
+                              int64_t total_cap, int32_t max_cap, const peagle_bf16 *v_cache,
+                              int32_t num_kv_heads, int32_t head_dim, peagle_bf16 *v_tiles,
+                              size_t v_tiles_bytes, void *stream);
+int peagle_draft_decode_attn_lens(int32_t num_reqs, int32_t K, const int32_t *cu_cap,
+                                  const int32_t *lens, int64_t total_cap, int32_t max_cap,
+                                  const peagle_bf16 *k_cache, const peagle_bf16 *v_tiles,
+                                  size_t v_tiles_bytes, const peagle_bf16 *q,
+                                  const peagle_bf16 *k, const peagle_bf16 *v,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  float softmax_scale, const float *rope_cos,
+                                  const float *rope_sin, int32_t rope_max_pos, float *out,
+                                  float *lse, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+int peagle_decode_append(int32_t num_reqs, const int32_t *cu_cap, const int32_t *lens_in,
+                         const int32_t *n_new, int32_t n_add, int32_t max_new,
+                         const peagle_bf16 *k_new, const peagle_bf16 *v_new,
+                         int32_t num_kv_heads, int32_t head_dim, const float *rope_cos,
+                         const float *rope_sin, int32_t rope_max_pos, int64_t total_cap,
+                         int32_t max_cap, peagle_bf16 *k_cache, peagle_bf16 *v_tiles,
+                         size_t v_tiles_bytes, int32_t *lens_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -246,3 +246,27 @@ def test_attn_bwd_argument_errors(lib):
     assert call(dq=f + 4) == peagle.ERR_ARG          # misaligned
     assert call(scale=0.0) == peagle.ERR_ARG
     assert call(ws_bytes=fwd) == peagle.ERR_WORKSPACE
+
+
+def test_decode_loop_argument_errors(lib):
+    """Host checks of the grow-in-place decode entries (fake aligned addresses, never
+    dereferenced: every call fails before anything is enqueued)."""
+    f = 1 << 20
+    B, Hkv, D, total, maxc = 4, 1, 64, 400, 120
+    big = 1 << 30
+    # append: lens_out must differ from lens_in; n_add within [0, max_new]; capacity bounds
+    def app(lens_in=f, lens_out=f + 256, n_add=1, max_new=5, max_pos=maxc, D=D, vt_bytes=big):
+        return _code("peagle_decode_append", B, f, lens_in, f, n_add, max_new, f, f, Hkv, D, f, f,
+                     max_pos, total, maxc, f, f, vt_bytes, lens_out, None)
+    assert app(lens_out=f) == peagle.ERR_ARG
+    assert app(n_add=6) == peagle.ERR_ARG
+    assert app(n_add=-1) == peagle.ERR_ARG
+    assert app(max_new=0) == peagle.ERR_ARG
+    assert app(max_pos=maxc - 2) == peagle.ERR_ARG
+    assert app(D=96) == peagle.ERR_UNSUPPORTED
+    assert app(vt_bytes=16) == peagle.ERR_WORKSPACE
+    # decode attention over lengths: lens required
+    assert _code("peagle_draft_decode_attn_lens", B, 4, f, None, total, maxc, f, f, big, f, f, f,
+                 4, Hkv, D, 0.125, f, f, maxc + 3, f, f, f, big, None) == peagle.ERR_ARG
+    assert _code("peagle_decode_pack_v_lens", B, f, None, total, maxc, f, Hkv, D, f, big,
+                 None) == peagle.ERR_ARG

@@ -333,14 +333,15 @@ size_t peagle_draft_decode_workspace_bytes(int32_t num_reqs, int32_t K, int32_t 
                                 max_ctx);
 }
 
-int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
-                             int64_t total_ctx, int32_t max_ctx, const peagle_bf16* k_cache,
-                             const peagle_bf16* v_tiles, size_t v_tiles_bytes_given,
-                             const peagle_bf16* q, const peagle_bf16* k, const peagle_bf16* v,
-                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                             float softmax_scale, const float* rope_cos, const float* rope_sin,
-                             int32_t rope_max_pos, float* out, float* lse, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+static int decode_attn_entry(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
+                             const int32_t* lens, int64_t total_ctx, int32_t max_ctx,
+                             const peagle_bf16* k_cache, const peagle_bf16* v_tiles,
+                             size_t v_tiles_bytes_given, const peagle_bf16* q,
+                             const peagle_bf16* k, const peagle_bf16* v, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                             const float* rope_cos, const float* rope_sin, int32_t rope_max_pos,
+                             float* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PEAGLE_ERR_UNSUPPORTED;
   if (K > 32) return PEAGLE_ERR_UNSUPPORTED;
   if (!decode_dims_ok(num_reqs, num_kv_heads, head_dim) || K < 1) return PEAGLE_ERR_ARG;
@@ -370,9 +371,88 @@ int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
     return PEAGLE_ERR_WORKSPACE;
   DecodeArgs a{num_reqs, K, num_q_heads, num_kv_heads, head_dim, max_ctx, rope_max_pos,
                total_ctx, softmax_scale};
-  return status_of(launch_decode_attn(a, cu_ctx, k_cache, v_tiles, q, k, v, rope_cos, rope_sin,
-                                      out, lse, static_cast<char*>(workspace),
-                                      static_cast<hipStream_t>(stream)));
+  return status_of(launch_decode_attn_lens(a, cu_ctx, lens, k_cache, v_tiles, q, k, v, rope_cos,
+                                           rope_sin, out, lse, static_cast<char*>(workspace),
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int peagle_draft_decode_attn(int32_t num_reqs, int32_t K, const int32_t* cu_ctx,
+                             int64_t total_ctx, int32_t max_ctx, const peagle_bf16* k_cache,
+                             const peagle_bf16* v_tiles, size_t v_tiles_bytes_given,
+                             const peagle_bf16* q, const peagle_bf16* k, const peagle_bf16* v,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             float softmax_scale, const float* rope_cos, const float* rope_sin,
+                             int32_t rope_max_pos, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return decode_attn_entry(num_reqs, K, cu_ctx, nullptr, total_ctx, max_ctx, k_cache, v_tiles,
+                           v_tiles_bytes_given, q, k, v, num_q_heads, num_kv_heads, head_dim,
+                           softmax_scale, rope_cos, rope_sin, rope_max_pos, out, lse, workspace,
+                           workspace_bytes, stream);
+}
+
+int peagle_draft_decode_attn_lens(int32_t num_reqs, int32_t K, const int32_t* cu_cap,
+                                  const int32_t* lens, int64_t total_cap, int32_t max_cap,
+                                  const peagle_bf16* k_cache, const peagle_bf16* v_tiles,
+                                  size_t v_tiles_bytes_given, const peagle_bf16* q,
+                                  const peagle_bf16* k, const peagle_bf16* v,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  float softmax_scale, const float* rope_cos,
+                                  const float* rope_sin, int32_t rope_max_pos, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (!lens) return PEAGLE_ERR_ARG;
+  return decode_attn_entry(num_reqs, K, cu_cap, lens, total_cap, max_cap, k_cache, v_tiles,
+                           v_tiles_bytes_given, q, k, v, num_q_heads, num_kv_heads, head_dim,
+                           softmax_scale, rope_cos, rope_sin, rope_max_pos, out, lse, workspace,
+                           workspace_bytes, stream);
+}
+
+int peagle_decode_pack_v_lens(int32_t num_reqs, const int32_t* cu_cap, const int32_t* lens,
+                              int64_t total_cap, int32_t max_cap, const peagle_bf16* v_cache,
+                              int32_t num_kv_heads, int32_t head_dim, peagle_bf16* v_tiles,
+                              size_t v_tiles_bytes_given, void* stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PEAGLE_ERR_UNSUPPORTED;
+  if (!decode_dims_ok(num_reqs, num_kv_heads, head_dim)) return PEAGLE_ERR_ARG;
+  if (total_cap < 0 || total_cap > kMaxI32 || max_cap < 0 || max_cap > total_cap)
+    return PEAGLE_ERR_ARG;
+  if (!cu_cap || !lens) return PEAGLE_ERR_ARG;
+  if (total_cap == 0) return PEAGLE_OK;
+  if (!v_cache || !v_tiles || !aligned16(v_cache) || !aligned16(v_tiles)) return PEAGLE_ERR_ARG;
+  if (v_tiles_bytes_given < v_tiles_bytes(total_cap, num_reqs, num_kv_heads, head_dim))
+    return PEAGLE_ERR_WORKSPACE;
+  return status_of(launch_decode_pack_v_lens(cu_cap, lens, num_reqs, total_cap, max_cap, v_cache,
+                                             num_kv_heads, head_dim, v_tiles,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int peagle_decode_append(int32_t num_reqs, const int32_t* cu_cap, const int32_t* lens_in,
+                         const int32_t* n_new, int32_t n_add, int32_t max_new,
+                         const peagle_bf16* k_new, const peagle_bf16* v_new,
+                         int32_t num_kv_heads, int32_t head_dim, const float* rope_cos,
+                         const float* rope_sin, int32_t rope_max_pos, int64_t total_cap,
+                         int32_t max_cap, peagle_bf16* k_cache, peagle_bf16* v_tiles,
+                         size_t v_tiles_bytes_given, int32_t* lens_out, void* stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PEAGLE_ERR_UNSUPPORTED;
+  if (!decode_dims_ok(num_reqs, num_kv_heads, head_dim)) return PEAGLE_ERR_ARG;
+  if (max_new < 1 || n_add < 0 || n_add > max_new) return PEAGLE_ERR_ARG;
+  if ((int64_t)num_reqs * max_new * num_kv_heads * (head_dim / 16 + head_dim / 8) + num_reqs >
+      kMaxI32)
+    return PEAGLE_ERR_UNSUPPORTED;
+  if (total_cap < 1 || total_cap > kMaxI32 || max_cap < 1 || max_cap > total_cap)
+    return PEAGLE_ERR_ARG;
+  if (rope_max_pos < 0 || rope_max_pos < max_cap - 1) return PEAGLE_ERR_ARG;
+  if (!cu_cap || !lens_in || !n_new || !k_new || !v_new || !rope_cos || !rope_sin || !k_cache ||
+      !v_tiles || !lens_out || lens_out == lens_in)
+    return PEAGLE_ERR_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_tiles) ||
+      !aligned16(rope_cos) || !aligned16(rope_sin))
+    return PEAGLE_ERR_ARG;
+  if (v_tiles_bytes_given < v_tiles_bytes(total_cap, num_reqs, num_kv_heads, head_dim))
+    return PEAGLE_ERR_WORKSPACE;
+  return status_of(launch_decode_append(cu_cap, lens_in, n_new, n_add, max_new, k_new, v_new,
+                                        rope_cos, rope_sin, rope_max_pos, k_cache, v_tiles,
+                                        lens_out, num_reqs, num_kv_heads, head_dim, max_cap,
+                                        total_cap, static_cast<hipStream_t>(stream)));
 }
 
 size_t peagle_layer1_qkv_workspace_bytes(int64_t n, int64_t T, int32_t H) {

@@ -39,6 +39,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "variants.h"
 
 namespace peagle {
 
@@ -63,6 +64,7 @@ __host__ __device__ constexpr int dec_key(int s) {
 
 struct DecodeParams {
   const int32_t* cu;
+  const int32_t* lens;  // current lengths inside the capacities, or null
   const uint16_t* kc;  // [Ltot, Hkv, D] rotated
   const uint16_t* vt;  // V tiles
   const uint16_t* qr;    // rotated q [B, K, Hq, D]
@@ -75,13 +77,23 @@ struct DecodeParams {
   float c_log2;
 };
 
-// Context length and cache start of request b; trusted device data, clamped so that every
-// access stays inside the cache.
-__device__ __forceinline__ void request_extent(const int32_t* cu, int b, int64_t total_ctx,
-                                               int max_ctx, int64_t& c0, int& L) {
+// Cache start, capacity and context length of request b: cu gives the starts and
+// capacities (cu[b + 1] - cu[b]); lens, when given, the current lengths inside them (a
+// cache that grows in place), else a request fills its capacity. Trusted device data,
+// clamped so that every access stays inside the cache.
+__device__ __forceinline__ void request_extent(const int32_t* cu, const int32_t* lens, int b,
+                                               int64_t total_ctx, int max_ctx, int64_t& c0,
+                                               int& L, int& cap) {
   c0 = std::min<int64_t>(std::max(cu[b], 0), total_ctx);
-  L = (int)std::min<int64_t>(std::max<int64_t>((int64_t)cu[b + 1] - c0, 0),
-                             std::min<int64_t>(max_ctx, total_ctx - c0));
+  cap = (int)std::min<int64_t>(std::max<int64_t>((int64_t)cu[b + 1] - c0, 0),
+                               std::min<int64_t>(max_ctx, total_ctx - c0));
+  L = lens != nullptr ? std::min(std::max(lens[b], 0), cap) : cap;
+}
+__device__ __forceinline__ void request_extent(const int32_t* cu, const int32_t* lens, int b,
+                                               int64_t total_ctx, int max_ctx, int64_t& c0,
+                                               int& L) {
+  int cap;
+  request_extent(cu, lens, b, total_ctx, max_ctx, c0, L, cap);
 }
 
 // Rotate-half RoPE of dims j0 .. j0 + 7 and their partners j0 + D/2 .. of one pre-RoPE bf16
@@ -109,7 +121,8 @@ __device__ __forceinline__ void rope8(const uint16_t* src, uint16_t* dst, int j0
 // new keys (B Hkv 32 rows, D/16 threads a row), new V^T (B Hkv D rows of 32 slots, 4
 // threads a row).
 __global__ __launch_bounds__(256) void decode_prep_kernel(
-    const int32_t* __restrict__ cu, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ lens,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ cs, const float* __restrict__ sn,
     uint16_t* __restrict__ qr, uint16_t* __restrict__ knew, uint16_t* __restrict__ vnew, int B,
     int K, int Hq, int Hkv, int D, int max_ctx, int max_pos, int64_t total_ctx) {
@@ -123,7 +136,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(
     const int j0 = (int)(t % per_row) * 8;
     const int64_t row = t / per_row;  // (b, d, h)
     const int d = (int)((row / Hq) % K), b = (int)(row / ((int64_t)Hq * K));
-    request_extent(cu, b, total_ctx, max_ctx, c0, L);
+    request_extent(cu, lens, b, total_ctx, max_ctx, c0, L);
     rope8(q + row * D, qr + row * D, j0, H, std::min(L + d, max_pos), cs, sn);
   } else if (t < nq + nk) {
     const int64_t u = t - nq;
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(
     const int g = (int)(bg % Hkv), b = (int)(bg / Hkv);
     uint16_t* dst = knew + row * D;
     if (e < K) {
-      request_extent(cu, b, total_ctx, max_ctx, c0, L);
+      request_extent(cu, lens, b, total_ctx, max_ctx, c0, L);
       rope8(k + (((size_t)b * K + e) * Hkv + g) * D, dst, j0, H, std::min(L + e, max_pos), cs, sn);
     } else {
       *reinterpret_cast<u32x4*>(dst + j0) = u32x4{0u, 0u, 0u, 0u};
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_attn_kernel(const De
   const int g = HEADS == 1 ? gg : gg * HEADS + wave;
   int64_t c0;
   int L;
-  request_extent(p.cu, b, p.total_ctx, p.max_ctx, c0, L);
+  request_extent(p.cu, p.lens, b, p.total_ctx, p.max_ctx, c0, L);
   const int ntiles_b = (L + kDecTile - 1) / kDecTile;
   // slices past the request's end hold nothing and write no partial (slice 0 always holds
   // the new rows' tile); the test is uniform over the workgroup, before any barrier
@@ -394,7 +407,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_attn_kernel(const De
 // loads in flight together, and the eight running states merge by shuffles.
 constexpr int kCombLanes = 8;
 __global__ __launch_bounds__(256) void decode_combine_kernel(
-    const int32_t* __restrict__ cu, const float* __restrict__ part_o,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ lens, const float* __restrict__ part_o,
     const float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse, int K,
     int Hq, int Hkv, int G, int GK, int NCg, int NPW, int PC, int D, int tpw, int max_ctx,
     int64_t total_ctx, int64_t n) {
@@ -415,7 +428,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
   // only the slices that held cache tiles (and slice 0) wrote a partial
   int64_t c0;
   int L;
-  request_extent(cu, b, total_ctx, max_ctx, c0, L);
+  request_extent(cu, lens, b, total_ctx, max_ctx, c0, L);
   const int nparts = std::min(NPW, std::max(1, ((L + kDecTile - 1) / kDecTile + tpw - 1) / tpw));
   float M = -INFINITY, lsum = 0.f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -472,6 +485,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(
 // (tile j of request b, kv head g); tiles past the request's end write nothing.
 template <int D>
 __global__ __launch_bounds__(256) void decode_pack_v_kernel(const int32_t* __restrict__ cu,
+                                                            const int32_t* __restrict__ lens,
                                                             const uint16_t* __restrict__ v,
                                                             uint16_t* __restrict__ vt,
                                                             int64_t total_ctx, int max_ctx,
@@ -479,9 +493,9 @@ __global__ __launch_bounds__(256) void decode_pack_v_kernel(const int32_t* __res
   __shared__ uint16_t tile[kDecTile][D + 8];
   const int j = blockIdx.x, b = blockIdx.y, g = blockIdx.z, tid = threadIdx.x;
   int64_t c0;
-  int L;
-  request_extent(cu, b, total_ctx, max_ctx, c0, L);
-  if (j * kDecTile >= L) return;
+  int L, cap;
+  request_extent(cu, lens, b, total_ctx, max_ctx, c0, L, cap);
+  if (j * kDecTile >= cap) return;  // tiles up to the capacity; zeros past the length
   constexpr int cpr = D / 8;
   for (int q = tid; q < kDecTile * cpr; q += 256) {
     const int key = q / cpr, c = q % cpr, pos = j * kDecTile + key;
@@ -528,6 +542,63 @@ DecodeLayout decode_layout(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_
   return l;
 }
 
+// Position of key x (0..31) in a V^T tile row: the inverse of dec_key.
+__device__ __forceinline__ int dec_slot(int x) {
+  return x < 16 ? 8 * (x >> 2) + (x & 3) : 8 * ((x - 16) >> 2) + 4 + (x & 3);
+}
+
+// A cache that grows in place (speculators P-EAGLE guide, "Inference Process": drafting
+// repeats from the last accepted token, so the newly committed tokens join the context).
+// Request b takes m_b = n_new[b] + n_add rows j = 0 .. m_b - 1 of k_new / v_new
+// [B, max_new, Hkv, D] (pre-RoPE) at positions L_b + j: k rotated at that position into
+// cache row c0 + L_b + j, v into slot dec_slot((L_b + j) & 31) of the request's V tile
+// (L_b + j) >> 5. Rows past the capacity are dropped; lens_out[b] = min(L_b + m_b, cap).
+// Flat grid over three ranges: k (D/16 threads a row), v (D/8 threads a row), lengths.
+__global__ __launch_bounds__(256) void decode_append_kernel(
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ lens_in,
+    const int32_t* __restrict__ n_new, int n_add, int max_new, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const float* __restrict__ cs, const float* __restrict__ sn,
+    int max_pos, uint16_t* __restrict__ kc, uint16_t* __restrict__ vt,
+    int32_t* __restrict__ lens_out, int B, int Hkv, int D, int max_ctx, int64_t total_ctx,
+    int64_t ntiles) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int H = D / 2;
+  const int64_t rows = (int64_t)B * max_new * Hkv;
+  const int64_t nk = rows * (D / 16), nv = rows * (D / 8);
+  int64_t c0;
+  int L, cap;
+  if (t < nk + nv) {
+    const bool is_k = t < nk;
+    const int64_t u = is_k ? t : t - nk;
+    const int per_row = is_k ? D / 16 : D / 8;
+    const int c = (int)(u % per_row);
+    const int64_t row = u / per_row;  // (b, j, g)
+    const int g = (int)(row % Hkv);
+    const int j = (int)((row / Hkv) % max_new);
+    const int b = (int)(row / ((int64_t)Hkv * max_new));
+    request_extent(cu, lens_in, b, total_ctx, max_ctx, c0, L, cap);
+    const int m = std::min(std::max(n_new[b] + n_add, 0), max_new);
+    if (j >= m || L + j >= cap) return;
+    const int key = L + j;
+    const uint16_t* src = (is_k ? k_new : v_new) + (size_t)row * D;
+    if (is_k) {
+      rope8(src, kc + ((size_t)(c0 + key) * Hkv + g) * D, c * 8, H, std::min(key, max_pos), cs, sn);
+    } else {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(src + c * 8);
+      uint16_t* tile = vt + (((size_t)g * ntiles + (c0 >> 5) + b + (key >> 5)) * D) * kDecTile;
+      const int slot = dec_slot(key & 31);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        tile[(size_t)(c * 8 + e) * kDecTile + slot] = (uint16_t)((val[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+  } else if (t < nk + nv + B) {
+    const int b = (int)(t - nk - nv);
+    request_extent(cu, lens_in, b, total_ctx, max_ctx, c0, L, cap);
+    const int m = std::min(std::max(n_new[b] + n_add, 0), max_new);
+    lens_out[b] = std::min(L + m, cap);
+  }
+}
+
 }  // namespace
 
 int64_t decode_ntiles(int64_t total_ctx, int32_t B) { return (total_ctx >> 5) + B + 1; }
@@ -564,13 +635,19 @@ size_t decode_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int
 hipError_t launch_decode_pack_v(const int32_t* cu, int32_t B, int64_t total_ctx, int32_t max_ctx,
                                 const uint16_t* v, int32_t Hkv, int32_t D, uint16_t* vt,
                                 hipStream_t stream) {
+  return launch_decode_pack_v_lens(cu, nullptr, B, total_ctx, max_ctx, v, Hkv, D, vt, stream);
+}
+
+hipError_t launch_decode_pack_v_lens(const int32_t* cu, const int32_t* lens, int32_t B,
+                                     int64_t total_ctx, int32_t max_ctx, const uint16_t* v,
+                                     int32_t Hkv, int32_t D, uint16_t* vt, hipStream_t stream) {
   const int tiles_max = (max_ctx + kDecTile - 1) / kDecTile;
   if (tiles_max == 0) return hipSuccess;
   const int64_t ntiles = decode_ntiles(total_ctx, B);
   return for_dim(D, [&](auto dc) {
     constexpr int DD = decltype(dc)::value;
     hipLaunchKernelGGL(decode_pack_v_kernel<DD>, dim3(tiles_max, B, Hkv), dim3(256), 0, stream, cu,
-                       v, vt, total_ctx, max_ctx, ntiles, Hkv);
+                       lens, v, vt, total_ctx, max_ctx, ntiles, Hkv);
   });
 }
 
@@ -578,10 +655,19 @@ hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint
                               const uint16_t* vt, const uint16_t* qn, const uint16_t* kn,
                               const uint16_t* vn, const float* cs, const float* sn, float* out,
                               float* lse, char* ws, hipStream_t stream) {
+  return launch_decode_attn_lens(a, cu, nullptr, kc, vt, qn, kn, vn, cs, sn, out, lse, ws, stream);
+}
+
+hipError_t launch_decode_attn_lens(const DecodeArgs& a, const int32_t* cu, const int32_t* lens,
+                                   const uint16_t* kc, const uint16_t* vt, const uint16_t* qn,
+                                   const uint16_t* kn, const uint16_t* vn, const float* cs,
+                                   const float* sn, float* out, float* lse, char* ws,
+                                   hipStream_t stream) {
   const DecodePlan pl = decode_plan(a.B, a.K, a.Hq, a.Hkv, a.D, a.total_ctx, a.max_ctx);
   const DecodeLayout lay = decode_layout(a.B, a.K, a.Hq, a.Hkv, a.D, pl);
   DecodeParams p;
   p.cu = cu;
+  p.lens = lens;
   p.kc = kc;
   p.vt = vt;
   p.qr = reinterpret_cast<const uint16_t*>(ws + lay.qr);
@@ -606,7 +692,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint
                         (int64_t)a.B * a.Hkv * kDecTile * (a.D / 16) +
                         (int64_t)a.B * a.Hkv * a.D * (kDecTile / 8);
   hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0,
-                     stream, cu, qn, kn, vn, cs, sn, reinterpret_cast<uint16_t*>(ws + lay.qr),
+                     stream, cu, lens, qn, kn, vn, cs, sn, reinterpret_cast<uint16_t*>(ws + lay.qr),
                      reinterpret_cast<uint16_t*>(ws + lay.knew),
                      reinterpret_cast<uint16_t*>(ws + lay.vnew), a.B, a.K, a.Hq, a.Hkv, a.D,
                      a.max_ctx, a.max_pos, a.total_ctx);
@@ -631,8 +717,26 @@ hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint
   const int64_t nout = (int64_t)a.B * a.Hkv * pl.ncg * pl.pc * (a.D / 4);
   const int64_t nthreads = nout * kCombLanes;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
-                     stream, cu, p.part_o, p.part_ml, out, lse, a.K, a.Hq, a.Hkv, p.G, p.GK,
+                     stream, cu, lens, p.part_o, p.part_ml, out, lse, a.K, a.Hq, a.Hkv, p.G, p.GK,
                      pl.ncg, pl.npw, pl.pc, a.D, pl.tpw, a.max_ctx, a.total_ctx, nout);
+  return hipGetLastError();
+}
+
+}  // namespace peagle
+
+namespace peagle {
+
+hipError_t launch_decode_append(const int32_t* cu, const int32_t* lens_in, const int32_t* n_new,
+                                int32_t n_add, int32_t max_new, const uint16_t* k_new,
+                                const uint16_t* v_new, const float* cs, const float* sn,
+                                int32_t max_pos, uint16_t* kc, uint16_t* vt, int32_t* lens_out,
+                                int32_t B, int32_t Hkv, int32_t D, int32_t max_ctx,
+                                int64_t total_ctx, hipStream_t stream) {
+  const int64_t rows = (int64_t)B * max_new * Hkv;
+  const int64_t work = rows * (D / 16) + rows * (D / 8) + B;
+  hipLaunchKernelGGL(decode_append_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0,
+                     stream, cu, lens_in, n_new, n_add, max_new, k_new, v_new, cs, sn, max_pos, kc,
+                     vt, lens_out, B, Hkv, D, max_ctx, total_ctx, decode_ntiles(total_ctx, B));
   return hipGetLastError();
 }
 

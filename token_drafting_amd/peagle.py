@@ -68,6 +68,12 @@ SIGNATURES = {
     "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32], _sz),
     "peagle_draft_decode_attn": ([_i32, _i32, _p, _i64, _i32, _p, _p, _sz, _p, _p, _p, _i32,
                                   _i32, _i32, _f32, _p, _p, _i32, _p, _p, _p, _sz, _p], _i32),
+    "peagle_draft_decode_attn_lens": ([_i32, _i32, _p, _p, _i64, _i32, _p, _p, _sz, _p, _p, _p,
+                                       _i32, _i32, _i32, _f32, _p, _p, _i32, _p, _p, _p, _sz,
+                                       _p], _i32),
+    "peagle_decode_pack_v_lens": ([_i32, _p, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
+    "peagle_decode_append": ([_i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _p, _p, _i32,
+                              _i64, _i32, _p, _p, _sz, _p, _p], _i32),
 }
 
 
@@ -499,3 +505,65 @@ def draft_decode_attn(cu_ctx, max_ctx: int, k_cache, v_tiles, q, k, v, cos, sin,
         float(scale if scale is not None else 1.0 / math.sqrt(D)), _ptr(cos), _ptr(sin),
         cos.shape[0] - 1, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
     return out, lse, workspace
+
+
+# ---------------------------------------------------------------- decode loop
+def decode_pack_v_lens(cu_cap, lens, max_cap: int, v_cache, v_tiles=None):
+    """V tiles of a cache with per-request capacities (cu_cap) holding lens[b] rows each;
+    zeros in the rest of every capacity."""
+    for t, name in ((cu_cap, "cu_cap"), (lens, "lens"), (v_cache, "v_cache")):
+        _dev(t, name)
+    Ltot, Hkv, D = v_cache.shape
+    B = cu_cap.numel() - 1
+    nbytes = decode_v_tiles_bytes(Ltot, B, Hkv, D)
+    if v_tiles is None:
+        v_tiles = torch.zeros(max(nbytes // 2, 8), dtype=v_cache.dtype, device=v_cache.device)
+    _check("peagle_decode_pack_v_lens", lib().peagle_decode_pack_v_lens(
+        B, _ptr(cu_cap), _ptr(lens), Ltot, max_cap, _ptr(v_cache), Hkv, D, _ptr(v_tiles),
+        v_tiles.numel() * v_tiles.element_size(), _stream()))
+    return v_tiles
+
+
+def draft_decode_attn_lens(cu_cap, lens, max_cap: int, k_cache, v_tiles, q, k, v, cos, sin,
+                           out=None, lse=None, workspace=None, scale=None):
+    """draft_decode_attn over a cache that grows in place: request b's context is the first
+    lens[b] rows of its capacity [cu_cap[b], cu_cap[b+1])."""
+    for t, name in ((cu_cap, "cu_cap"), (lens, "lens"), (k_cache, "k_cache"), (v_tiles, "v_tiles"),
+                    (q, "q"), (k, "k"), (v, "v"), (cos, "rope_cos"), (sin, "rope_sin")):
+        _dev(t, name)
+    B, K, Hq, D = q.shape
+    Hkv = k.shape[2]
+    Ltot = k_cache.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, K, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, K, Hq), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(B, K, Hq, Hkv, D, Ltot, max_cap),
+                                dtype=torch.uint8, device=dev)
+    _check("peagle_draft_decode_attn_lens", lib().peagle_draft_decode_attn_lens(
+        B, K, _ptr(cu_cap), _ptr(lens), Ltot, max_cap, _ptr(k_cache), _ptr(v_tiles),
+        v_tiles.numel() * v_tiles.element_size(), _ptr(q), _ptr(k), _ptr(v), Hq, Hkv, D,
+        float(scale if scale is not None else 1.0 / math.sqrt(D)), _ptr(cos), _ptr(sin),
+        cos.shape[0] - 1, _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream()))
+    return out, lse, workspace
+
+
+def decode_append(cu_cap, lens_in, n_new, n_add, max_cap: int, k_new, v_new, cos, sin, k_cache,
+                  v_tiles, lens_out=None):
+    """Append n_new[b] + n_add rows of k_new / v_new [B, max_new, Hkv, D] (pre-RoPE) to each
+    request's context; returns the new lengths."""
+    for t, name in ((cu_cap, "cu_cap"), (lens_in, "lens_in"), (n_new, "n_new"), (k_new, "k_new"),
+                    (v_new, "v_new"), (cos, "rope_cos"), (sin, "rope_sin"), (k_cache, "k_cache"),
+                    (v_tiles, "v_tiles")):
+        _dev(t, name)
+    B, max_new, Hkv, D = k_new.shape
+    if lens_out is None:
+        lens_out = torch.empty_like(lens_in)
+    _check("peagle_decode_append", lib().peagle_decode_append(
+        B, _ptr(cu_cap), _ptr(lens_in), _ptr(n_new), int(n_add), max_new, _ptr(k_new),
+        _ptr(v_new), Hkv, D, _ptr(cos), _ptr(sin), cos.shape[0] - 1, k_cache.shape[0], max_cap,
+        _ptr(k_cache), _ptr(v_tiles), v_tiles.numel() * v_tiles.element_size(), _ptr(lens_out),
+        _stream()))
+    return lens_out
