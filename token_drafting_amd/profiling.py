@@ -8,8 +8,8 @@ counter. The record also stores a digest of the kernel's source files; bench.py 
 the traffic only while the sources still match, since a changed kernel moves different
 bytes.
 
-    python -m token_drafting_amd.profiling --fetch gpurun_out/pmc_fetch \\
-        --write gpurun_out/pmc_write --copy-mib 1024 --out profiles/<name>.md --command "..."
+    python -m token_drafting_amd.profiling --fetch <runs>/pmc_fetch \\
+        --write <runs>/pmc_write --copy-mib 1024 --out profiles/<name>.md --command "..."
 """
 from __future__ import annotations
 
