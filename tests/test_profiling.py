@@ -98,3 +98,13 @@ def test_decode_traffic_groups_calls_per_workload(tmp_path):
     stale = dict(rec, kernel_source_sha256="0" * 64)
     profiling.write_decode_summary(str(path), stale, "cmd")
     assert profiling.recorded_decode_traffic(str(path), wl) is None
+
+
+def test_decode_calls_grouped_by_workload_runs():
+    """Plain decode calls of each workload come first (sorted names, different attention
+    kernels), then the decode loop's: each workload's record takes its own first run."""
+    from token_drafting_amd.profiling import _workload_runs
+    seq = [("k256", 1), ("k256", 2), ("k128", 3), ("k128", 4), ("k256", 5), ("k128", 6)]
+    runs = _workload_runs(seq, 2)
+    assert [[x for _, x in r] for r in runs] == [[1, 2], [3, 4]]
+    assert _workload_runs(seq[:2], 2) == [seq[:2]]

@@ -113,10 +113,23 @@ def summarize(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
             "decode": _decode_traffic(fetch, write, f_fac, w_fac)}
 
 
+def _workload_runs(calls, n: int):
+    """The first n runs of consecutive calls with the same attention kernel (element 0 of
+    each call). bench.py times the plain decode call of each inference workload in sorted
+    name order, then the decode loop's calls; the workloads use different attention
+    kernels, so run i holds workload i's plain calls."""
+    runs = []
+    for c in calls:
+        if runs and runs[-1][0][0] == c[0]:
+            runs[-1].append(c)
+        else:
+            runs.append([c])
+    return runs[:n]
+
+
 def _decode_traffic(fetch, write, f_fac: float, w_fac: float):
     """Per-call bytes of the decode attention (prep, attention and combine launches) for
-    each inference workload, or None when the runs hold no decode calls. bench.py times
-    the workloads in sorted name order, the same number of calls each."""
+    each inference workload, or None when the runs hold no decode calls."""
     from . import synth
 
     def calls(rows, fac):
@@ -130,17 +143,15 @@ def _decode_traffic(fetch, write, f_fac: float, w_fac: float):
                 out.append((b, x + y + z))
         return out
 
-    cf, cw = calls(fetch, f_fac), calls(write, w_fac)
     names = sorted(synth.DECODE_CONFIGS)
-    if not cf or len(cf) != len(cw) or len(cf) % len(names):
+    rf, rw = _workload_runs(calls(fetch, f_fac), len(names)), _workload_runs(calls(write, w_fac), len(names))
+    if len(rf) != len(names) or [len(r) for r in rf] != [len(r) for r in rw]:
         return None
-    per = len(cf) // len(names)
     rec = {"kernel_source_sha256": kernel_source_digest(DECODE_SOURCES), "workloads": {}}
-    for i, name in enumerate(names):
-        f = [b for _, b in cf[i * per:(i + 1) * per]]
-        w = [b for _, b in cw[i * per:(i + 1) * per]]
+    for name, runf, runw in zip(names, rf, rw):
+        f, w, per = [b for _, b in runf], [b for _, b in runw], len(runf)
         rec["workloads"][synth.DECODE_CONFIGS[name]["workload"]] = {
-            "attn_kernel": cf[i * per][0], "calls": per,
+            "attn_kernel": runf[0][0], "calls": per,
             "call_fetch_bytes": sum(f) / per, "call_write_bytes": sum(w) / per,
             "call_bytes": (sum(f) + sum(w)) / per}
     return rec
@@ -330,9 +341,10 @@ def write_trace_summary(path: str, trace_dir: str, bench_log: str, title: str, c
               f"{live:.1f} us per call in the same run." if live is not None else ""]
     calls = _decode_calls(rows, timed)
     if dec_live and calls:
-        per_wl = len(calls) // len(dec_live)
-        for i, (name, res) in enumerate(sorted(dec_live.items())):
-            mine = calls[i * per_wl:(i + 1) * per_wl][-timed:]
+        # calls are (duration, attention duration, attention kernel): key the runs on the kernel
+        runs = _workload_runs([(c[2], c) for c in calls], len(dec_live))
+        for (name, res), run in zip(sorted(dec_live.items()), runs):
+            mine = [c for _, c in run][-timed:]
             call_us = sum(c[0] for c in mine) / len(mine) / 1e3
             attn_us = sum(c[1] for c in mine) / len(mine) / 1e3
             lines.append(
