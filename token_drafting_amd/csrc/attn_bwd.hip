@@ -17,13 +17,13 @@
 //        the chunk's diagonal keys. Per 32-key tile: S^T = K Q^T and dP^T = V dO^T (the
 //        lane holds one query column and 16 keys), P and dS in registers, then
 //        dq'^T += K^T dS^T with K^T tiles laid out like the forward's V^T tiles.
-//   dk, dv of depth-0 keys: key-major. A workgroup owns 128 consecutive keys (a wave per
-//        32) of one kv head and streams every query tile that can see them: the query
+//   dk, dv of depth-0 keys: key-major. A workgroup owns 128 consecutive keys (8 waves of
+//        16) of one kv head and streams every query tile that can see them: the query
 //        slots (anchor-major rows x G heads) of the anchors from the block's first key to
 //        the end of its last key's sequence, pre-cut into 32-slot tiles in both row and
-//        transposed layouts. Per tile: S = Q K^T and dP = dO V^T (the lane holds one key
-//        column and 16 slots), then dV^T += dO^T P and dK^T += Q^T dS with the lane's
-//        own P and dS as the B operands.
+//        transposed layouts. Per tile, on 16x16x32 MFMAs: S = Q K^T and dP = dO V^T (the
+//        lane holds one key column and 8 slots), then dV^T += dO^T P and dK^T += Q^T dS
+//        with the lane's own P and dS as the B operands.
 //   dk, dv of depth >= 1 keys: a depth-e row is seen only by its own anchor's rows of
 //        depth >= e (at most K - e rows x G heads): one wave per key row and kv head on
 //        the vector units.
@@ -66,6 +66,22 @@ __device__ __forceinline__ int telem(int x) { return 4 * ((x & 15) >> 3) + (x & 
 __device__ __forceinline__ int tentry(int chunk, int e) {
   return 16 * (chunk >> 1) + 8 * (e >> 2) + 4 * (chunk & 1) + (e & 3);
 }
+
+// 16x16x32 bf16 MFMA: lane l supplies row l%16 of A and column l%16 of B, 8 values each at
+// k positions 8 (l/16) .. + 7; it receives column l%16 of D, rows 4 (l/16) + r.
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Slot stored at position p (0..31) of a transposed query-tile row, for the key-major
+// pass: a lane of the 16x16x32 MFMA holds slots 4 q .. 4 q + 3 of the first 16-slot score
+// block and 16 + 4 q .. of the second, which are its B-operand positions 8 q .. 8 q + 7.
+__device__ __forceinline__ int qt_slot(int pos) {
+  return (pos & 7) < 4 ? 4 * (pos >> 3) + (pos & 7) : 16 + 4 * (pos >> 3) + (pos & 7) - 4;
+}
+
+constexpr int kBwdWaves = 8;               // waves of the key-major pass, 16 keys each
+constexpr int kBwdThreads = 64 * kBwdWaves;
 
 __device__ __forceinline__ bf16x8 ld8(const void* p) {
   return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
@@ -238,7 +254,7 @@ __global__ __launch_bounds__(256) void qtile_kernel(const BwdParams p, uint16_t*
     u32x4 oq, od;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int a = tentry(chunk, 2 * w), b = tentry(chunk, 2 * w + 1);
+      const int a = qt_slot(chunk * 8 + 2 * w), b = qt_slot(chunk * 8 + 2 * w + 1);
       oq[w] = (uint32_t)tq[a][d] | ((uint32_t)tq[b][d] << 16);
       od[w] = (uint32_t)td[a][d] | ((uint32_t)td[b][d] << 16);
     }
@@ -260,15 +276,20 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, size_t
 // few segments and the tiles come from HBM about once per segment (later blocks hit the
 // caches), instead of once per key block; and no workgroup takes more than seg_len tiles
 // (the first key blocks are seen by nearly every tile, the last by few). Segments add
-// into zeroed outputs with fp32 atomics. With both,
-// a lane holds its key's k' and v fragments and two accumulators; for D >= 128 that does
-// not fit the register file, so the two run as separate passes (the dV pass needs neither
-// v nor dP, and each pass streams three of the four query tiles).
+// into zeroed outputs with fp32 atomics.
+//
+// v_mfma_f32_16x16x32_bf16 with 16 keys per wave and 8 waves: a lane holds the k' and v
+// fragments of one key for half of a 32-key wave's registers, so the pass keeps two waves
+// per SIMD. Per 32-slot tile: S = Q K^T and dP = dO V^T as two 16-slot blocks (the lane
+// holds key l%16, slots 16 mi + 4 (l/16) + r), then dV^T += dO^T P and dK^T += Q^T dS with
+// the lane's 8 weights as the B operand: positions 8 (l/16) .. + 7 of a k-step are slots
+// qt_slot(...), the order the transposed query tiles are stored in.
 template <int D, bool WK, bool WV>
-__global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
   using C = BCfg<D>;
-  // LDS regions of one stage, only those the pass reads (the dV pass then fits twice per
-  // CU next to another workgroup)
+  constexpr int DS = D / 32;  // k-steps of S and dP over D
+  constexpr int MB = D / 16;  // 16-row blocks of dK^T and dV^T
+  // LDS regions of one stage, only those the pass reads
   constexpr int RQ = 0;
   constexpr int RD = RQ + C::KBUF;
   constexpr int RQT = RD + (WK ? C::KBUF : 0);
@@ -280,7 +301,7 @@ __global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(co
   __shared__ __attribute__((aligned(1024))) char buf1[STAGE];
   __shared__ int s_rng[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r32 = lane & 31, half = lane >> 5;
+  const int l16 = lane & 15, q4 = lane >> 4;
   const int g = blockIdx.x % p.Hkv, rest = blockIdx.x / p.Hkv;
   const int kb = rest % p.nkb, seg = rest / p.nkb;
   const int k0 = kb * kBwdKeys;
@@ -302,28 +323,26 @@ __global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(co
   const int t0 = s_rng[0], t1 = s_rng[1];
   if (t0 >= t1) return;  // an empty segment (the same for the whole workgroup)
 
-  const int key = k0 + wave * KT + r32;
+  const int key = k0 + wave * 16 + l16;
   const bool key_on = key <= k1;
   const int kc = min(key, k1);
   const int key_lo = p.qinfo[min(max(p.qstart[kc], 0), p.T - 1)].w;
-  bf16x8 kf[C::DK], vf[WK ? C::DK : 1];
+  bf16x8 kf[DS], vf[WK ? DS : 1];
   {
-    const uint16_t* krow = p.kr + ((size_t)kc * p.Hkv + g) * D + half * 8;
-    const uint16_t* vrow = p.v + ((size_t)kc * p.Hkv + g) * D + half * 8;
+    const uint16_t* krow = p.kr + ((size_t)kc * p.Hkv + g) * D + q4 * 8;
+    const uint16_t* vrow = p.v + ((size_t)kc * p.Hkv + g) * D + q4 * 8;
 #pragma unroll
-    for (int kk = 0; kk < C::DK; ++kk) {
-      kf[kk] = ld8(krow + kk * 16);
-      if constexpr (WK) vf[kk] = ld8(vrow + kk * 16);
+    for (int kk = 0; kk < DS; ++kk) {
+      kf[kk] = ld8(krow + kk * 32);
+      if constexpr (WK) vf[kk] = ld8(vrow + kk * 32);
     }
   }
-  floatx16 dkt[WK ? C::MT : 1], dvt[WV ? C::MT : 1];
+  floatx4 dkt[WK ? MB : 1], dvt[WV ? MB : 1];
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if constexpr (WK) dkt[mt][r] = 0.f;
-      if constexpr (WV) dvt[mt][r] = 0.f;
-    }
+  for (int mb = 0; mb < MB; ++mb) {
+    if constexpr (WK) dkt[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (WV) dvt[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto issue = [&](int t, char* dst) {
     const size_t tb = (size_t)g * p.ntq + t;
@@ -332,8 +351,8 @@ __global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(co
     const char* bqt = uniform_opaque(reinterpret_cast<const char*>(p.qtt + tb * KT * D));
     const char* bdt = uniform_opaque(reinterpret_cast<const char*>(p.dtt + tb * KT * D));
 #pragma unroll
-    for (int j = 0; j < (NR + 3) / 4; ++j) {
-      const int b = wave + 4 * j;
+    for (int j = 0; j < (NR + kBwdWaves - 1) / kBwdWaves; ++j) {
+      const int b = wave + kBwdWaves * j;
       if (b < NR) {
         const int P = b * 1024 + lane * 16;
         const int x = P / C::KROW, off = P - x * C::KROW;
@@ -343,8 +362,8 @@ __global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(co
       }
     }
 #pragma unroll
-    for (int j = 0; j < (NTB + 3) / 4; ++j) {
-      const int b = wave + 4 * j;
+    for (int j = 0; j < (NTB + kBwdWaves - 1) / kBwdWaves; ++j) {
+      const int b = wave + kBwdWaves * j;
       if (b < NTB) {
         const int P = b * 1024 + lane * 16;
         const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 2) & 3);
@@ -358,47 +377,37 @@ __global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(co
   };
 
   auto compute = [&](const char* B) {
-    floatx16 s, dp;
+    floatx4 s[2], dp[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-    const char* qb = B + RQ + r32 * C::KROW + half * 16;
-    const char* db = B + RD + r32 * C::KROW + half * 16;
-    // scheduling barriers between the phases keep each phase's LDS fragments from being
-    // hoisted into the previous one (the register file holds k', v and the accumulators)
+    for (int mi = 0; mi < 2; ++mi) {
+      s[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dp[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const char* qb = B + RQ + (16 * mi + l16) * C::KROW + q4 * 16;
 #pragma unroll
-    for (int kk = 0; kk < C::DK; ++kk) s = mfma32(ld8(qb + kk * 32), kf[kk], s);
-    sched_reads_ahead<C::DK, 2, 1>();
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (WK) {
+      for (int kk = 0; kk < DS; ++kk) s[mi] = mfma16(ld8(qb + kk * 64), kf[kk], s[mi]);
+      if constexpr (WK) {
+        const char* db = B + RD + (16 * mi + l16) * C::KROW + q4 * 16;
 #pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) dp = mfma32(ld8(db + kk * 32), vf[kk], dp);
-      sched_reads_ahead<C::DK, 2, 1>();
-      __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < DS; ++kk) dp[mi] = mfma16(ld8(db + kk * 64), vf[kk], dp[mi]);
+      }
     }
     const int4* meta = reinterpret_cast<const int4*>(B + RM);
-    bf16x8 pb[2], sb[2];
-    // two halves of 8 slots, so that only 8 slots' metadata are live at once
+    bf16x8 pb, sb;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-      for (int r = 8 * hh; r < 8 * hh + 8; ++r) {
-        const int4 m = meta[8 * (r >> 2) + 4 * half + (r & 3)];
-        const bool ok = key_on && m.y == key_lo && m.x >= key;
-        const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], p.c_log2, -__int_as_float(m.z))) : 0.f;
-        pb[r >> 3][r & 7] = (__bf16)pr;
-        if constexpr (WK) sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - __int_as_float(m.w)));
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int e = 0; e < 8; ++e) {
+      const int mi = e >> 2, r = e & 3;
+      const int4 m = meta[16 * mi + 4 * q4 + r];
+      const bool ok = key_on && m.y == key_lo && m.x >= key;
+      const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[mi][r], p.c_log2, -__int_as_float(m.z))) : 0.f;
+      pb[e] = (__bf16)pr;
+      if constexpr (WK) sb[e] = (__bf16)(pr * (dp[mi][r] - __int_as_float(m.w)));
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < C::MT; ++mt) {
-        const int o = t_off(mt * 32 + r32, ks * 2 + half);
-        if constexpr (WV) dvt[mt] = mfma32(ld8(B + RDT + o), pb[ks], dvt[mt]);
-        if constexpr (WK) dkt[mt] = mfma32(ld8(B + RQT + o), sb[ks], dkt[mt]);
-      }
-    sched_reads_ahead<2 * C::MT * ((WK ? 1 : 0) + (WV ? 1 : 0)), 2, 1>();
+    for (int mb = 0; mb < MB; ++mb) {
+      const int o = t_off(16 * mb + l16, q4);
+      if constexpr (WV) dvt[mb] = mfma16(ld8(B + RDT + o), pb, dvt[mb]);
+      if constexpr (WK) dkt[mb] = mfma16(ld8(B + RQT + o), sb, dkt[mb]);
+    }
   };
 
   // two tiles per iteration over two static buffers, one loop exit, odd last tile after
@@ -425,15 +434,13 @@ __global__ __launch_bounds__(256, (D <= 128 || !WK) ? 2 : 1) void dkdv_kernel(co
     float* dkr = p.dk + ((size_t)key * p.Hkv + g) * D;
     float* dvr = p.dv + ((size_t)key * p.Hkv + g) * D;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = mt * 32 + 8 * i + 4 * half + j;
-          if constexpr (WK) unsafeAtomicAdd(dkr + d, dkt[mt][4 * i + j] * p.scale);
-          if constexpr (WV) unsafeAtomicAdd(dvr + d, dvt[mt][4 * i + j]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * mb + 4 * q4 + r;
+        if constexpr (WK) unsafeAtomicAdd(dkr + d, dkt[mb][r] * p.scale);
+        if constexpr (WV) unsafeAtomicAdd(dvr + d, dvt[mb][r]);
+      }
   }
 }
 
@@ -825,12 +832,7 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
       hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, stream, dv, count4);
     }
     const dim3 kgrid((unsigned)((int64_t)nkb * a.Hkv * nseg));
-    if constexpr (D <= 64) {
-      hipLaunchKernelGGL((dkdv_kernel<D, true, true>), kgrid, dim3(256), 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, false, true>), kgrid, dim3(256), 0, stream, p);
-      hipLaunchKernelGGL((dkdv_kernel<D, true, false>), kgrid, dim3(256), 0, stream, p);
-    }
+    hipLaunchKernelGGL((dkdv_kernel<D, true, true>), kgrid, dim3(kBwdThreads), 0, stream, p);
     if (a.T > a.n) {
       const int64_t waves = (int64_t)(a.T - a.n) * a.Hkv;
       hipLaunchKernelGGL(diag_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,

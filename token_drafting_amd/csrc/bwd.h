@@ -15,7 +15,7 @@ namespace peagle {
 // Query slots of one kv head (draft rows of the anchor-major list x its G q heads) are cut
 // into tiles of this many slots for the key-major pass.
 constexpr int kBwdSlots = 32;
-// Depth-0 keys per workgroup of the key-major pass (4 waves of 32).
+// Depth-0 keys per workgroup of the key-major pass (8 waves of 16).
 constexpr int kBwdKeys = 128;
 
 // The backward's own workspace regions, after the forward's (offsets from the start).
