@@ -142,10 +142,14 @@ def test_rope_and_accept_argument_errors(lib):
 
 
 def test_workspace_bytes(lib):
-    a = peagle.attn_workspace_bytes(4096, 10375, 4, 1, 256)
-    b = peagle.attn_workspace_bytes(4096, 12000, 4, 1, 256)
+    # enough chunks for the whole chip: no key-range split, size grows with T
+    a = peagle.attn_workspace_bytes(32768, 83001, 4, 1, 256)
+    b = peagle.attn_workspace_bytes(32768, 90000, 4, 1, 256)
     assert 0 < a < b
     assert a % 256 == 0
+    # 163 chunks: split in up to 4 segments, so three fp32 partial outputs of [T, Hq, D]
+    c = peagle.attn_workspace_bytes(4096, 10375, 4, 1, 256)
+    assert c % 256 == 0 and c >= 3 * 10375 * 4 * 256 * 4
     assert peagle.attn_workspace_bytes(0, 10, 4, 1, 64) == 0
 
 

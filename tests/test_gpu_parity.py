@@ -194,6 +194,10 @@ ATTN_SMALL = [
     (520, 4, 0.7, 0.2, 11, [260, 260], 32, 8, 128, 5e5),         # Llama-8B heads
     (700, 4, 0.7, 0.2, 12, None, 4, 1, 256, 1e4),                # several workgroups at D=256
     (300, 16, 0.7, 0.2, 13, [120, 180], 4, 1, 256, 1e4),         # K = 16 (the widest sweep point)
+    # key-range split: few chunks, so each long chunk is cut into up to 4 segments; the
+    # second sequence starts off a tile boundary
+    (1500, 4, 0.7, 0.2, 14, [700, 800], 8, 2, 128, 5e5),
+    (2000, 4, 0.7, 0.2, 15, None, 4, 1, 256, 1e4),
 ]
 
 
@@ -219,6 +223,18 @@ def test_attention_full_size_sampled(pe, cfg_id):
                            cfg["D"], cfg["theta"], rows=rows)
     assert_close(o, want["out"], f"out cfg{cfg_id}")
     assert_close(l, want["lse"], f"lse cfg{cfg_id}", max_rel_l2=1e-3)
+
+
+def test_attention_unsplit_small(pe):
+    # 16 kv heads with one q head each: enough workgroups that chunks are not split
+    n, K, seed, H, D = 3300, 4, 16, 16, 64
+    cu = np.array([0, n], dtype=np.int32)
+    sel = ocod.cod_select(n, K, 0.7, 0.2, seed, cu)
+    rows = sample_rows(sel["depth_off"], cu, sel["idx"], count=96, seed=seed)
+    print(f"attention unsplit n={n} Hq=Hkv={H} D={D}: {len(rows)} sampled rows", flush=True)
+    o, l, want = _attn_run(pe, n, K, 0.7, 0.2, seed, cu, H, H, D, 1e4, rows=rows)
+    assert_close(o, want["out"], "out")
+    assert_close(l, want["lse"], "lse", max_rel_l2=1e-3)
 
 
 def test_attention_prepare_core_equals_fwd(pe):

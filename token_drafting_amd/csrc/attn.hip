@@ -54,6 +54,7 @@
 // lane's 16 k-step reads share one base address. V^T tiles: rows of 32 keys (64 bytes),
 // 16-byte chunk index XOR ((d >> 2) & 3).
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -89,7 +90,8 @@ __device__ __forceinline__ int v_off(int d, int chunk) {
 
 // Read-ahead depths (D = 256, 2 waves per SIMD): 2 K fragments and 3 V fragments are what
 // fits in the 256-register budget beside O (128), Q (64) and S (16); one more spills a Q
-// fragment to scratch inside the loop, whose reload then waits on the tile DMA.
+// fragment to scratch inside the loop, whose reload then waits on the tile DMA. The split
+// variant keeps its segment bounds live as well and reads V one fragment less ahead.
 constexpr int kPrefetchK = 2, kPrefetchV = 3;
 
 struct AttnParams {
@@ -106,13 +108,67 @@ struct AttnParams {
   const uint16_t* v;
   float* out;
   float* lse;
-  int n, T, S, Hq, Hkv, G, QR, ntiles, exact_per_seq, max_chunks;
+  int32_t* segs;  // [chunk * Hkv + g]: segments of the chunk (1: not split)
+  int2* items;    // split main kernel's work list: (chunk * Hkv + g, segment | nseg << 8)
+  int32_t* nitems;
+  float* part;    // [segment - 1][T][Hq][D]: unnormalised O of segments 1.. of split chunks
+  float2* ml;     // [segment][Hq][T]: (reference max, sum) of each segment of split chunks
+  int n, T, S, Hq, Hkv, G, QR, ntiles, exact_per_seq, max_chunks, nsplit;
+  int budget;  // work items that run at once beside the short chunks (one round)
+  int exact_r0;  // exact kernel: first row of its grid (0: short chunks, S*exact_per_seq: redo)
   float c_log2;
 };
 
+// Key range of a chunk (rows j0 .. j0 + jn - 1 of the anchor-major list, one sequence):
+// every row sees keys from k_lo (the sequence start) up to its own anchor, so the range is
+// [k_lo, k_hi] and keys [full_lo, full_hi] are seen by every row.
+struct ChunkKeys {
+  int k_lo, k_hi, full_lo, full_hi, p_first, p_last;
+};
+__device__ __forceinline__ ChunkKeys chunk_keys(const AttnParams& p, int j0, int jn) {
+  const int4 first = p.qinfo[j0], last = p.qinfo[j0 + jn - 1];
+  ChunkKeys c;
+  c.p_first = min(max(first.y, 0), p.n - 1);
+  c.p_last = min(max(last.y, 0), p.n - 1);
+  c.k_lo = min(max(first.w, 0), c.p_first);
+  c.k_hi = c.p_last;
+  c.full_lo = min(max(last.w, 0), c.p_last);
+  c.full_hi = c.p_first;
+  return c;
+}
+
+// Key-range split of a chunk's context tiles [t_first, t_last] into nseg segments. Segment
+// j > 0 starts at tile b_j, a tile wholly inside [full_lo, full_hi]: every row sees all its
+// keys, so each segment's first tile fixes a finite reference max for every row. A chunk
+// with no such tile past its first is not split (splittable = false).
+struct SegPlan {
+  int t_first, t_last, ntl, bmin, bmax;
+  bool splittable;
+  __device__ int bound(int j, int nseg) const {
+    return min(max(t_first + (int)((int64_t)j * ntl / nseg), bmin), bmax);
+  }
+};
+__device__ __forceinline__ SegPlan seg_plan(const ChunkKeys& c) {
+  SegPlan s;
+  s.t_first = c.k_lo / KT;
+  s.t_last = c.k_hi / KT;
+  s.ntl = s.t_last - s.t_first + 1;
+  s.bmin = max(s.t_first + 1, (c.full_lo + KT - 1) / KT);
+  s.bmax = min(s.t_last, (c.full_hi + 1) / KT - 1);
+  s.splittable = s.bmin <= s.bmax;
+  return s;
+}
+// Segments of a chunk for a segment length of L tiles, at most nsplit.
+__device__ __forceinline__ int seg_count(int ntl, int L, int nsplit) {
+  return max(1, min(nsplit, (ntl + L - 1) / L));
+}
+constexpr int kMinSplitTiles = 8;  // shorter segments do not pay for their partial's merge
+constexpr int kItemsMaxEntries = 4096;  // (chunk, kv head) entries the length search holds
+
 // EXACT = false: the main kernel, every chunk with a long context span. EXACT = true:
-// chunks with a short span, and chunks the main kernel flagged for a redo.
-template <int D, bool EXACT>
+// chunks with a short span, and chunks the main kernel flagged for a redo. SPLIT (main
+// kernel only): each chunk's context is cut into segments run by separate workgroups.
+template <int D, bool EXACT, bool SPLIT>
 __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void attn_core_kernel(
     const AttnParams p) {
   constexpr int NT = EXACT ? kExactNT : kMainNT;
@@ -130,11 +186,11 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, half = lane >> 5;
   const int bid = blockIdx.x;
-  const int g = bid % p.Hkv;
-  int chunk;
+  int g = bid % p.Hkv;
+  int chunk, seg = 0, nseg = 1;
   bool redo = false;
   if constexpr (EXACT) {
-    const int r = bid / p.Hkv;
+    const int r = p.exact_r0 + bid / p.Hkv;
     const int n_short = p.S * p.exact_per_seq;
     if (r < n_short) {  // one of the first chunks of a sequence
       const int s = r / p.exact_per_seq, j = r % p.exact_per_seq;
@@ -148,8 +204,18 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   } else {
     // Chunks are listed sequence by sequence, anchors ascending: the last ones have the
     // longest prefixes, so they are dispatched first. The grid is sized for the largest
-    // possible chunk count; blocks past the actual count exit.
-    chunk = *p.nchunks - 1 - bid / p.Hkv;
+    // possible chunk count; blocks past the actual count exit. With a key-range split the
+    // blocks take the items of the work list, which is in the same order.
+    if constexpr (SPLIT) {
+      if (bid >= *p.nitems) return;
+      const int2 it = p.items[bid];
+      g = it.x % p.Hkv;
+      chunk = it.x / p.Hkv;
+      seg = it.y & 255;
+      nseg = max(it.y >> 8, 1);
+    } else {
+      chunk = *p.nchunks - 1 - bid / p.Hkv;
+    }
     if (chunk < 0) return;
   }
   const int n = p.n, T = p.T, Hkv = p.Hkv;
@@ -158,15 +224,13 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   const int jn = min(max(ch.y, 1), T - j0);
 
   if (tid == 0) {
-    const int4 first = p.qinfo[j0], last = p.qinfo[j0 + jn - 1];
-    const int p_first = min(max(first.y, 0), n - 1), p_last = min(max(last.y, 0), n - 1);
-    const int lo_first = min(max(first.w, 0), p_first), lo_last = min(max(last.w, 0), p_last);
-    s_range[0] = lo_first;  // first key of any row
-    s_range[1] = p_last;    // last key of any row
-    s_range[2] = lo_last;   // keys in [lo_last, p_first] are seen by every row
-    s_range[3] = p_first;
-    s_range[4] = min(max(p.qstart[p_first], 0), T);     // diagonal keys: entries of the
-    s_range[5] = min(max(p.qstart[p_last + 1], 0), T);  // chunk's anchors in the list
+    const ChunkKeys c = chunk_keys(p, j0, jn);
+    s_range[0] = c.k_lo;     // first key of any row
+    s_range[1] = c.k_hi;     // last key of any row
+    s_range[2] = c.full_lo;  // keys in [full_lo, full_hi] are seen by every row
+    s_range[3] = c.full_hi;
+    s_range[4] = min(max(p.qstart[c.p_first], 0), T);     // diagonal keys: entries of the
+    s_range[5] = min(max(p.qstart[c.p_last + 1], 0), T);  // chunk's anchors in the list
     s_redo = 0;
   }
   __syncthreads();
@@ -174,6 +238,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   const int dg_lo = s_range[4], dg_hi = s_range[5];
   const bool is_short = (k_hi - k_lo + 1) <= kShortSpan;  // uniform over the workgroup
   if (EXACT ? (!is_short && !redo) : is_short) return;
+
 
   // Query slots of this lane: NT columns of 32 (lanes l and l+32 share a column, each
   // holding 16 of the 32 keys of a tile).
@@ -321,7 +386,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
         for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[nt][mt] = mfma32(vf[mt][ks], pb[nt][ks], o[nt][mt]);
-      sched_reads_ahead<2 * C::MT, kPrefetchV, NT>();
+      sched_reads_ahead<2 * C::MT, SPLIT ? kPrefetchV - 1 : kPrefetchV, NT>();
     } else {
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
@@ -381,21 +446,29 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
     dma_v(t, Vd);
   };
 
+  // Context tiles of this workgroup: all of [t_first, t_last], or one segment of them. The
+  // last segment also takes the masked edge tiles and the diagonal keys.
   const int t_first = k_lo / KT, t_last = k_hi / KT;
-  issue(t_first, Ks0, Kl0, Vs0);
-  for (int t = t_first; t <= t_last; t += 2) {
+  int t_begin = t_first, t_end = t_last;
+  if constexpr (SPLIT) {  // segment seg of the nseg the work list chose for this chunk
+    const SegPlan sp = seg_plan(ChunkKeys{k_lo, k_hi, full_lo, full_hi, 0, 0});
+    if (seg > 0) t_begin = sp.bound(seg, nseg);
+    if (seg < nseg - 1) t_end = sp.bound(seg + 1, nseg) - 1;
+  }
+  if (!SPLIT || t_begin <= t_end) issue(t_begin, Ks0, Kl0, Vs0);
+  for (int t = t_begin; t <= t_end; t += 2) {
     wait_dma();
     __syncthreads();  // tile t landed in buffer 0; buffer 1 is free
-    if (t + 1 <= t_last) issue(t + 1, Ks1, Kl1, Vs1);
+    if (t + 1 <= t_end) issue(t + 1, Ks1, Kl1, Vs1);
     {
       const int key0 = t * KT;
       const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
-      compute(Ks0, Kl0, Vs0, full ? 0 : 1, key0, t == t_first);
+      compute(Ks0, Kl0, Vs0, full ? 0 : 1, key0, t == t_begin);
     }
-    if (t + 1 > t_last) break;
+    if (t + 1 > t_end) break;
     wait_dma();
     __syncthreads();  // tile t+1 landed in buffer 1; buffer 0 is free
-    if (t + 2 <= t_last) issue(t + 2, Ks0, Kl0, Vs0);
+    if (t + 2 <= t_end) issue(t + 2, Ks0, Kl0, Vs0);
     {
       const int key0 = (t + 1) * KT;
       const bool full = key0 >= full_lo && key0 + KT - 1 <= full_hi;
@@ -404,7 +477,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   }
 
   // ---- diagonal extension: depth >= 1 rows of the chunk's anchors ----
-  for (int jb = dg_lo; jb < dg_hi; jb += KT) {
+  for (int jb = seg == nseg - 1 ? dg_lo : dg_hi; jb < dg_hi; jb += KT) {
     __syncthreads();
     if (tid < KT) {
       const int jk = jb + tid;
@@ -443,14 +516,18 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   }
 
   // ---- epilogue: O / l, lse; the main kernel flags rows whose sum left the safe range ----
+  // A segment of a split chunk stores its unnormalised O (segment 0 into out, segment j
+  // into part[j - 1]) and its (reference max, sum); the combine kernel merges them.
+  const bool partial = SPLIT && nseg > 1;
   bool bad = false;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const float lt = l_run[nt] + __shfl_xor(l_run[nt], 32, 64);
     if constexpr (!EXACT) bad |= q_on[nt] && !(lt <= kSumLimit);
-    const float inv = 1.f / lt;
+    const float inv = partial ? 1.f : 1.f / lt;
     if (q_on[nt]) {
-      float* dst = p.out + ((size_t)q_row[nt] * p.Hq + q_head[nt]) * D;
+      float* dst = (SPLIT && seg > 0 ? p.part + (size_t)(seg - 1) * T * p.Hq * D : p.out) +
+                   ((size_t)q_row[nt] * p.Hq + q_head[nt]) * D;
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
@@ -460,8 +537,12 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
           for (int j = 0; j < 4; ++j) w[j] = o[nt][mt][4 * i + j] * inv;
           *reinterpret_cast<floatx4*>(dst + mt * 32 + 8 * i + 4 * half) = w;
         }
-      if (p.lse != nullptr && half == 0)
+      if (partial) {
+        if (half == 0)
+          p.ml[((size_t)seg * p.Hq + q_head[nt]) * T + q_row[nt]] = make_float2(m_run[nt], lt);
+      } else if (p.lse != nullptr && half == 0) {
         p.lse[(size_t)q_head[nt] * T + q_row[nt]] = (m_run[nt] + __log2f(lt)) * 0.69314718055994531f;
+      }
     }
   }
   if constexpr (!EXACT) {
@@ -471,6 +552,180 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   } else {
     if (redo && tid == 0) p.flags[chunk * Hkv + g] = 0;
   }
+}
+
+// Work list of the split main kernel, one workgroup. Every (chunk, kv head) entry, heaviest
+// chunks first, gets one item per segment; chunks with a short span (run by the exact
+// kernel) get none. The segment length L is chosen from the chunks' actual spans: the
+// smallest L (>= kMinSplitTiles) whose item count fits p.budget, the workgroups that run at
+// once, so the split finishes in one round bounded by the longest segment. 1024 candidate
+// lengths are counted in parallel, one per thread. If none fits, nothing is split. Also
+// writes each entry's segment count for the merge.
+__global__ __launch_bounds__(1024) void attn_items_kernel(const AttnParams p) {
+  __shared__ int s_ntl[kItemsMaxEntries];  // tiles (splittable), -1 (not splittable), 0 (short)
+  __shared__ int s_wave[16];
+  __shared__ int s_carry, s_best, s_maxntl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nc = min(max(*p.nchunks, 0), p.max_chunks);
+  const int total = nc * p.Hkv;
+  const bool search = total <= kItemsMaxEntries;
+  if (tid == 0) {
+    s_carry = 0;
+    s_best = 1 << 30;  // no split
+    s_maxntl = 0;
+  }
+  __syncthreads();
+  auto entry = [&](int i, int& key, SegPlan& sp) {
+    const int chunk = nc - 1 - i / p.Hkv, g = i % p.Hkv;
+    key = chunk * p.Hkv + g;
+    const int2 ch = p.chunks[chunk];
+    const int j0 = min(max(ch.x, 0), p.T - 1);
+    const int jn = min(max(ch.y, 1), p.T - j0);
+    const ChunkKeys c = chunk_keys(p, j0, jn);
+    sp = seg_plan(c);
+    return c.k_hi - c.k_lo + 1 > kShortSpan;  // else short
+  };
+  if (search) {
+    int mx = 0;
+    for (int i = tid; i < total; i += 1024) {
+      int key;
+      SegPlan sp;
+      const bool on = entry(i, key, sp);
+      const int v = !on ? 0 : (sp.splittable ? sp.ntl : -1);
+      s_ntl[i] = v;
+      mx = max(mx, v);
+    }
+    atomicMax(&s_maxntl, mx);
+    __syncthreads();
+    const int lo = kMinSplitTiles, hi = max(s_maxntl, lo);
+    const int step = (hi - lo + 1024) / 1024;
+    const int L = lo + tid * step;
+    if (L <= hi) {
+      int cnt = 0;
+      for (int i = 0; i < total; ++i) {
+        const int v = s_ntl[i];
+        cnt += v > 0 ? seg_count(v, L, p.nsplit) : (v < 0 ? 1 : 0);
+      }
+      if (cnt <= p.budget) atomicMin(&s_best, L);
+    }
+    __syncthreads();
+  }
+  const int L = s_best;
+  for (int base = 0; base < total; base += 1024) {
+    const int i = base + tid;
+    int nseg = 0, key = 0;
+    SegPlan sp;
+    if (i < total) {
+      if (entry(i, key, sp)) nseg = sp.splittable ? seg_count(sp.ntl, L, p.nsplit) : 1;
+      p.segs[key] = max(nseg, 1);
+    }
+    // exclusive scan of nseg over the block
+    int incl = nseg;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int before = s_carry;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    const int at = before + incl - nseg;
+    for (int j = 0; j < nseg; ++j) p.items[at + j] = make_int2(key, j | (nseg << 8));
+    __syncthreads();
+    if (tid == 1023) s_carry = at + nseg;
+    __syncthreads();
+  }
+  if (tid == 0) *p.nitems = s_carry;
+}
+
+// Merge of the segments of split chunks. Slot (row, head) of a chunk cut into nseg
+// segments: M = max_j m_j, w_j = 2^(m_j - M), out = sum_j w_j O_j / sum_j w_j l_j,
+// lse = (M + log2 sum_j w_j l_j) ln 2. One wave per slot, D / 64 floats per lane; blocks
+// (chunk * Hkv + g, 4 of the chunk's 256 slots), so every slot's loads are in flight at
+// once. Chunks flagged for a redo are skipped: the exact kernel rewrites them afterwards.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
+  constexpr int VW = D / 64;
+  const int g = blockIdx.x % p.Hkv;
+  const int chunk = blockIdx.x / p.Hkv;
+  if (chunk >= min(*p.nchunks, p.max_chunks)) return;
+  const int nseg = min(p.segs[chunk * p.Hkv + g], p.nsplit);
+  if (nseg <= 1 || p.flags[chunk * p.Hkv + g] != 0) return;
+  const int2 ch = p.chunks[chunk];
+  const int j0 = min(max(ch.x, 0), p.T - 1);
+  const int jn = min(max(ch.y, 1), p.T - j0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t seg_stride = (size_t)p.T * p.Hq * D;
+  const int s = blockIdx.y * 4 + wave;
+  if (s < jn * p.G) {
+    const int rl = s % jn, h = g * p.G + s / jn;
+    const int row = min(max(p.qinfo[j0 + rl].x, 0), p.T - 1);
+    float2 ml[kMaxAttnSplit];
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMaxAttnSplit; ++j)
+      if (j < nseg) {
+        ml[j] = p.ml[((size_t)j * p.Hq + h) * p.T + row];
+        M = fmaxf(M, ml[j].x);
+      }
+    float L = 0.f, acc[VW];
+#pragma unroll
+    for (int e = 0; e < VW; ++e) acc[e] = 0.f;
+    const size_t off = ((size_t)row * p.Hq + h) * D + lane * VW;
+#pragma unroll
+    for (int j = 0; j < kMaxAttnSplit; ++j)
+      if (j < nseg) {
+        const float w = ml[j].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[j].x - M);
+        L += w * ml[j].y;
+        const float* src = (j == 0 ? p.out : p.part + (size_t)(j - 1) * seg_stride) + off;
+#pragma unroll
+        for (int e = 0; e < VW; ++e) acc[e] += w * src[e];
+      }
+    const float inv = 1.f / L;
+    float* dst = p.out + off;
+#pragma unroll
+    for (int e = 0; e < VW; ++e) dst[e] = acc[e] * inv;
+    if (p.lse != nullptr && lane == 0)
+      p.lse[(size_t)h * p.T + row] = (M + __log2f(L)) * 0.69314718055994531f;
+  }
+}
+
+// Second stream per device for the short chunks, which do not depend on the main kernel:
+// they can overlap it instead of running after it. Default priority, created on first use;
+// the lock also keeps two concurrent calls from interleaving their fork and join events.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+int device_cus() {
+  static int cus[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cus[dev] <= 0 &&
+      hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = 256;
+  return cus[dev];
+}
+
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& s = g_side[dev];
+  if (s.stream == nullptr && !s.failed) {
+    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
+      s.failed = true;  // run the short chunks on the caller's stream instead
+      (void)hipGetLastError();
+    }
+  }
+  return s.failed ? nullptr : &s;
 }
 
 }  // namespace
@@ -492,6 +747,12 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p.v = v;
   p.out = out;
   p.lse = lse;
+  p.segs = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + L.segs);
+  p.items = reinterpret_cast<int2*>(const_cast<char*>(ws) + L.items);
+  p.nitems = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + L.nitems);
+  p.part = reinterpret_cast<float*>(const_cast<char*>(ws) + L.part);
+  p.ml = reinterpret_cast<float2*>(const_cast<char*>(ws) + L.ml);
+  p.nsplit = attn_split_plan(a.n, a.T, a.Hq, a.Hkv).nsplit;
   p.n = a.n;
   p.T = a.T;
   p.S = a.S;
@@ -503,17 +764,68 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p.exact_per_seq = attn_exact_chunks_per_seq(a.K, p.QR);
   p.max_chunks = L.max_chunks;
   p.c_log2 = a.scale * 1.4426950408889634f;
-  // main kernel first (it may flag chunks), then short and flagged chunks
+  // Short chunks on the side stream, concurrently with the main kernel (and the work list
+  // and merge of a split); then the chunks the main kernel flagged, once both are done.
   // chunk count <= ceil(T / QR) + S (each sequence adds at most one partial chunk)
   const int chunk_bound = std::min(L.max_chunks, (a.T + p.QR - 1) / p.QR + a.S);
-  const dim3 main_grid(chunk_bound * a.Hkv);
-  const dim3 exact_grid((a.S * p.exact_per_seq + chunk_bound) * a.Hkv);
+  const int n_short = a.S * p.exact_per_seq;
+  const dim3 main_grid(chunk_bound * a.Hkv * p.nsplit);
+  const dim3 combine_grid(chunk_bound * a.Hkv, kAttnSlots / 4);
+  const dim3 short_grid(n_short * a.Hkv), redo_grid(chunk_bound * a.Hkv);
+  AttnParams p_short = p, p_redo = p;
+  p_short.exact_r0 = 0;
+  p_redo.exact_r0 = n_short;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  // Overlap pays when the short chunks are a latency tail (a few workgroups per sequence
+  // of a long single context); when they are a sizeable share of the work (many packed
+  // sequences), the fork and join cost more than running them in turn.
+  SideStream* side = n_short * a.Hkv <= device_cus() / 4 ? side_stream() : nullptr;
+  if (p.nsplit > 1) {
+    // one round of the split main kernel: its resident workgroups over the chip, less the
+    // short chunks' workgroups that run beside it
+    int per_cu = 1;
+    hipError_t eo = hipErrorInvalidValue;
+#define PEAGLE_OCC(DD)                                                                      \
+  eo = hipOccupancyMaxActiveBlocksPerMultiprocessor(                                        \
+      &per_cu, reinterpret_cast<const void*>(&attn_core_kernel<DD, false, true>),           \
+      Cfg<DD, kMainNT>::TH, 0)
+    switch (a.D) {
+      case 64: PEAGLE_OCC(64); break;
+      case 128: PEAGLE_OCC(128); break;
+      case 256: PEAGLE_OCC(256); break;
+      default: break;
+    }
+#undef PEAGLE_OCC
+    if (eo != hipSuccess) per_cu = 1;
+    p.budget = std::max(1, std::max(1, per_cu) * device_cus() - n_short * a.Hkv);
+  }
+  hipStream_t short_stream = stream;
+  if (side != nullptr && hipEventRecord(side->fork, stream) == hipSuccess &&
+      hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess)
+    short_stream = side->stream;
 #define PEAGLE_CORE(DD)                                                                       \
   do {                                                                                        \
-    hipLaunchKernelGGL((attn_core_kernel<DD, false>), main_grid, dim3(Cfg<DD, kMainNT>::TH), \
-                       0, stream, p);                                                         \
-    hipLaunchKernelGGL((attn_core_kernel<DD, true>), exact_grid, dim3(Cfg<DD, kExactNT>::TH), \
-                       0, stream, p);                                                         \
+    hipLaunchKernelGGL((attn_core_kernel<DD, true, false>), short_grid,                       \
+                       dim3(Cfg<DD, kExactNT>::TH), 0, short_stream, p_short);                \
+    if (short_stream != stream) {                                                             \
+      const hipError_t ej = hipEventRecord(side->join, short_stream);                         \
+      if (ej != hipSuccess) return ej;                                                        \
+    }                                                                                         \
+    if (p.nsplit > 1) {                                                                       \
+      hipLaunchKernelGGL(attn_items_kernel, dim3(1), dim3(1024), 0, stream, p);               \
+      hipLaunchKernelGGL((attn_core_kernel<DD, false, true>), main_grid,                      \
+                         dim3(Cfg<DD, kMainNT>::TH), 0, stream, p);                           \
+      hipLaunchKernelGGL((attn_combine_kernel<DD>), combine_grid, dim3(256), 0, stream, p);   \
+    } else {                                                                                  \
+      hipLaunchKernelGGL((attn_core_kernel<DD, false, false>), main_grid,                     \
+                         dim3(Cfg<DD, kMainNT>::TH), 0, stream, p);                           \
+    }                                                                                         \
+    if (short_stream != stream) {                                                             \
+      const hipError_t ew = hipStreamWaitEvent(stream, side->join, 0);                        \
+      if (ew != hipSuccess) return ew;                                                        \
+    }                                                                                         \
+    hipLaunchKernelGGL((attn_core_kernel<DD, true, false>), redo_grid,                        \
+                       dim3(Cfg<DD, kExactNT>::TH), 0, stream, p_redo);                       \
   } while (0)
   switch (a.D) {
     case 64: PEAGLE_CORE(64); break;

@@ -35,11 +35,22 @@ hipError_t launch_rope_table(int32_t head_dim, double theta, int32_t max_pos, fl
 
 // Workspace of the draft attention, carved from one caller-provided buffer.
 struct AttnLayout {
-  size_t qinfo, qstart, qrot, krot, krot_lo, vt, chunks, nchunks, seq_chunk, flags, blocksum, total;
+  size_t qinfo, qstart, qrot, krot, krot_lo, vt, chunks, nchunks, seq_chunk, flags, blocksum,
+      segs, items, nitems, part, ml, total;
   int max_chunks;
 };
 AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D);
 int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv);
+
+// Key-range split of the attention's main kernel, for grids that would not fill the chip:
+// a chunk's context tiles are cut into at most nsplit segments, each run by its own
+// workgroup (the segment length is chosen on the device from the chunks' spans); a merge
+// kernel combines their partial softmax states. nsplit = 1 when there are enough chunks.
+constexpr int kMaxAttnSplit = 4;
+struct AttnSplit {
+  int nsplit;
+};
+AttnSplit attn_split_plan(int64_t n, int64_t T, int32_t Hq, int32_t Hkv);
 
 // Query slots (rows x q heads of one kv head) per attention workgroup: a chunk holds
 // kAttnSlots / G consecutive rows of the anchor-major list.

@@ -298,6 +298,17 @@ int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv) {
   return (int)((T + QR - 1) / QR + n);
 }
 
+// Enough workgroups for two per CU (256 CUs) need no split; below that, up to
+// kMaxAttnSplit segments per chunk.
+constexpr int kSplitBlocks = 512;
+
+AttnSplit attn_split_plan(int64_t n, int64_t T, int32_t Hq, int32_t Hkv) {
+  (void)n;
+  const int64_t QR = kAttnSlots / std::max(1, Hq / std::max(1, Hkv));
+  const int64_t blocks = std::max<int64_t>(1, (T + QR - 1) / QR) * std::max(1, Hkv);
+  return AttnSplit{blocks >= kSplitBlocks ? 1 : kMaxAttnSplit};
+}
+
 AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D) {
   AttnLayout L;
   const size_t ntiles = (size_t)((n + 31) / 32);
@@ -315,6 +326,15 @@ AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D)
   L.seq_chunk = off; off += align256((size_t)(n + 1) * sizeof(int32_t));
   L.flags = off;  off += align256((size_t)L.max_chunks * Hkv * sizeof(int32_t));
   L.blocksum = off; off += align256((size_t)((n + 1023) / 1024) * sizeof(int32_t));
+  // split attention: segment count per (chunk, kv head), the work list of (chunk, segment)
+  // items; partial O of segments 1.. (segment 0 keeps its partial in the output);
+  // per-segment (reference max, sum) of every row
+  const AttnSplit sp = attn_split_plan(n, T, Hq, Hkv);
+  L.segs = off;   off += align256((size_t)L.max_chunks * Hkv * sizeof(int32_t));
+  L.items = off;  off += align256((size_t)L.max_chunks * Hkv * sp.nsplit * sizeof(int2));
+  L.nitems = off; off += 256;
+  L.part = off;   off += align256((size_t)(sp.nsplit - 1) * T * Hq * D * sizeof(float));
+  L.ml = off;     off += sp.nsplit > 1 ? align256((size_t)sp.nsplit * Hq * T * 2 * sizeof(float)) : 0;
   L.total = off;
   return L;
 }
