@@ -237,6 +237,55 @@ def test_attention_unsplit_small(pe):
     assert_close(l, want["lse"], "lse", max_rel_l2=1e-3)
 
 
+def _attn_run_qkv(pe, n, K, sel, cu, q, k, v, theta, rows=None):
+    import torch
+    T, Hq, D = q.shape
+    dsel = pe.cod_select(n, K, 0.7, 0.2, int(sel["seed"]), to_dev(cu))
+    cos, sin = pe.rope_table(D, theta, pe.rope_max_pos(n, K))
+    # a workspace full of non-zero bytes: nothing may read what the call did not write
+    ws = torch.full((pe.attn_workspace_bytes(n, T, Hq, k.shape[1], D),), 0x41, dtype=torch.uint8,
+                    device="cuda")
+    out, lse, _ = pe.draft_attn(n, K, dsel, to_dev(cu), to_dev(q), to_dev(k), to_dev(v), cos, sin,
+                                workspace=ws)
+    want = oattn.draft_attention(q, k, v, sel["idx"], sel["depth_off"], cu, theta, rows=rows)
+    o, l = to_host(out), to_host(lse)
+    if rows is not None:
+        o, l = o[rows], l[:, rows]
+    return o, l, want
+
+
+@pytest.mark.parametrize("n,Hq,Hkv,D,seed", [(2000, 4, 1, 64, 31),     # few chunks: key-range split
+                                             (1500, 4, 1, 256, 33),
+                                             (3300, 16, 16, 64, 32)])  # many workgroups: no split
+def test_attention_score_jump_redo(pe, n, Hq, Hkv, D, seed):
+    """Scores that rise far above a row's first tile (past 2^64 in the fixed-max sum) send
+    the chunk to the rescaling kernel. q and the depth-0 keys at positions >= 256 carry
+    16 and 4 sqrt(D) in the lowest-frequency rotary pair; at theta = 1e9 that pair does
+    not rotate (fp32 cos = 1), so those scores reach ~64 exactly in bf16 while the first
+    tile's stay near N(0, 1)."""
+    K, theta = 4, 1e9
+    cu = np.array([0, n], dtype=np.int32)
+    sel = ocod.cod_select(n, K, 0.7, 0.2, seed, cu)
+    sel["seed"] = seed
+    T = int(sel["depth_off"][-1])
+    qkv = synth.qkv_inputs(seed, T, Hq, Hkv, D)
+    q, k, v = qkv["q"].copy(), qkv["k"].copy(), qkv["v"].copy()
+    j = D // 2 - 1
+    q[:, :, j] = synth.f32_to_bf16_bits(np.array([16.0], np.float32))[0]
+    q[:, :, D - 1] = 0
+    k[:n, :, D - 1] = 0
+    k[:256, :, j] = 0
+    k[256:n, :, j] = synth.f32_to_bf16_bits(np.array([4.0 * np.sqrt(D)], np.float32))[0]
+    rows = None
+    if n > 2500:
+        rows = sample_rows(sel["depth_off"], cu, sel["idx"], count=96, seed=seed)
+    print(f"attention score jump n={n} Hq={Hq} Hkv={Hkv} T={T}", flush=True)
+    o, l, want = _attn_run_qkv(pe, n, K, sel, cu, q, k, v, theta, rows=rows)
+    assert (want["lse"] > 40).any()   # the jump is there
+    assert_close(o, want["out"], "out")
+    assert_close(l, want["lse"], "lse", max_rel_l2=1e-3)
+
+
 def test_attention_prepare_core_equals_fwd(pe):
     import torch
     n, K, seed = 333, 4, 21

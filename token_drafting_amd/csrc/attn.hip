@@ -442,7 +442,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   };
   auto issue = [&](int t, char* Kd, char* Kld, char* Vd) {
     dma_k(p.kr, t, Kd);
-    if constexpr (EXACT) dma_k(p.kr_lo, t, Kld);
+    if (EXACT && !redo) dma_k(p.kr_lo, t, Kld);
     dma_v(t, Vd);
   };
 
@@ -454,6 +454,16 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
     const SegPlan sp = seg_plan(ChunkKeys{k_lo, k_hi, full_lo, full_hi, 0, 0});
     if (seg > 0) t_begin = sp.bound(seg, nseg);
     if (seg < nseg - 1) t_end = sp.bound(seg + 1, nseg) - 1;
+  }
+  if constexpr (EXACT) {
+    // k_lo exists only for the first kShortSpan positions of each sequence (the short
+    // chunks). A chunk redone for its softmax sum is past them: it runs on k' alone, its
+    // k_lo buffers held at zero (the first barrier below orders these stores).
+    if (redo)
+      for (int q = tid; q < C::KBUF / 16; q += C::TH) {
+        *reinterpret_cast<u32x4*>(Kl0 + q * 16) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(Kl1 + q * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
   }
   if (!SPLIT || t_begin <= t_end) issue(t_begin, Ks0, Kl0, Vs0);
   for (int t = t_begin; t <= t_end; t += 2) {
@@ -497,7 +507,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
         const int row = min(max(p.qinfo[jk].x, 0), T - 1);
         kv = *reinterpret_cast<const u32x4*>(p.kr + ((size_t)row * Hkv + g) * D + c * 8);
         vv = *reinterpret_cast<const u32x4*>(p.v + ((size_t)row * Hkv + g) * D + c * 8);
-        if constexpr (EXACT) kl = *reinterpret_cast<const u32x4*>(p.kr_lo + ((size_t)row * Hkv + g) * D + c * 8);
+        if (EXACT && !redo) kl = *reinterpret_cast<const u32x4*>(p.kr_lo + ((size_t)row * Hkv + g) * D + c * 8);
       }
       *reinterpret_cast<u32x4*>(Ks0 + key * C::KROW + c * 16) = kv;
       if constexpr (EXACT) *reinterpret_cast<u32x4*>(Kl0 + key * C::KROW + c * 16) = kl;
