@@ -230,7 +230,7 @@ def main():
             "attn_prepare_rope_GBps": round(rope_bytes / (stage_ms["attn_prepare"] * 1e-3) / 1e9, 1),
             "accept_prefix_GBps": round(verify_bytes / (stage_ms["accept_prefix"] * 1e-3) / 1e9, 1),
         },
-        "roofline": {"kernel": "attn_core_kernel (both launches of peagle_draft_attn_core)",
+        "roofline": {"kernel": "attn_core_kernel (the launches of one peagle_draft_attn_core call)",
                      "bound": "mfma", "achieved": round(core_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(core_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.config)},

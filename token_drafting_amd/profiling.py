@@ -24,7 +24,8 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 ATTN_SOURCES = ("csrc/attn.hip", "csrc/common.h", "csrc/kernels.h")
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/common.h", "csrc/kernels.h")
-CORE_KERNELS = ("attn_core_kernel",)  # both launches (main and exact) of one core call
+# the launches of one core call: main (or work list, split and merge) and exact kernels
+CORE_KERNELS = ("attn_core_kernel", "attn_items_kernel", "attn_combine_kernel")
 RECORD_TAG = "traffic_record:"
 DECODE_TAG = "decode_traffic_record:"
 
@@ -84,6 +85,12 @@ def _calibration(rows, copy_bytes: int, counter: str) -> float:
     return copy_bytes / kib
 
 
+def _is_main_core(name: str) -> bool:
+    """attn_core_kernel<D, false, split>: the main kernel, one dispatch per core call."""
+    m = re.match(r"attn_core_kernel<\s*\d+\s*,\s*(\w+)", name)
+    return bool(m) and m.group(1) == "false"
+
+
 def summarize(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
     copy_bytes = copy_mib << 20
     fetch, write = _read(fetch_dir, "FETCH_SIZE"), _read(write_dir, "WRITE_SIZE")
@@ -100,13 +107,20 @@ def summarize(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
             d = per_kernel.setdefault(name, {"calls": len(v)})
             d[key + "_kib_raw"] = sum(v) / len(v)
             d[key + "_bytes"] = sum(v) / len(v) * fac
-    core = [d for name, d in per_kernel.items() if any(k in name for k in CORE_KERNELS)]
+    core = {name: d for name, d in per_kernel.items() if any(k in name for k in CORE_KERNELS)}
+    # one main-kernel dispatch per core call; the exact kernel runs twice per call (short
+    # chunks, then the redo pass), so a call's bytes are each kernel's total over the calls
+    n_calls = max(1, sum(d["calls"] for name, d in core.items() if _is_main_core(name)))
+
+    def per_call(key):
+        return sum(d.get(key, 0.0) * d["calls"] for d in core.values()) / n_calls
+
     rec = {
         "kernel_source_sha256": kernel_source_digest(),
         "fetch_factor_bytes_per_kib": f_fac,
         "write_factor_bytes_per_kib": w_fac,
-        "core_call_fetch_bytes": sum(d.get("fetch_bytes", 0.0) for d in core),
-        "core_call_write_bytes": sum(d.get("write_bytes", 0.0) for d in core),
+        "core_call_fetch_bytes": per_call("fetch_bytes"),
+        "core_call_write_bytes": per_call("write_bytes"),
     }
     rec["core_call_bytes"] = rec["core_call_fetch_bytes"] + rec["core_call_write_bytes"]
     return {"record": rec, "per_kernel": per_kernel,
@@ -210,7 +224,7 @@ def write_summary(path: str, summary: dict, command: str) -> None:
         lines.append(f"| `{name}` | {d['calls']} | {d.get('fetch_kib_raw', 0):.1f} | "
                      f"{d.get('write_kib_raw', 0):.1f} | {d.get('fetch_bytes', 0) / 1e6:.2f} | "
                      f"{d.get('write_bytes', 0) / 1e6:.2f} |")
-    lines += ["", f"Attention core call (both launches): "
+    lines += ["", f"Attention core call (all its launches): "
               f"{rec['core_call_fetch_bytes'] / 1e6:.1f} MB read + "
               f"{rec['core_call_write_bytes'] / 1e6:.1f} MB written.", "",
               f"{RECORD_TAG} {json.dumps(rec)}", ""]
@@ -327,7 +341,22 @@ def write_trace_summary(path: str, trace_dir: str, bench_log: str, title: str, c
         lines.append(f"| `{name}` | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {min(d) / 1e3:.1f} | "
                      f"{max(d) / 1e3:.1f} | {100 * sum(d) / total:.2f} |")
     core = [k for k in per if any(c in k for c in CORE_KERNELS)]
-    last = sum(sum(d for _, d in sorted(per[k])[-timed:]) / timed for k in core) / 1e3
+    # A core call's launches sit between the step's other kernels in start order; the short
+    # chunks' launch runs on a second stream and overlaps the main kernel, so a call lasts
+    # from its first launch's start to its last launch's end.
+    seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short(r["Kernel_Name"]))
+                 for r in rows)
+    spans, cur = [], None
+    for st, en, name in seq:
+        if any(c in name for c in CORE_KERNELS):
+            cur = [st, en] if cur is None else [cur[0], max(cur[1], en)]
+        elif cur is not None:
+            spans.append(cur)
+            cur = None
+    if cur is not None:
+        spans.append(cur)
+    mine = spans[-timed:]
+    last = sum(en - st for st, en in mine) / max(1, len(mine)) / 1e3
     live, dec_live = None, {}
     with open(bench_log) as f:
         for line in f:
@@ -336,9 +365,10 @@ def write_trace_summary(path: str, trace_dir: str, bench_log: str, title: str, c
                 live = j["stage_ms"]["attn_core"] * 1e3 if "stage_ms" in j else None
                 dec_live = j.get("decode", {})
     lines += ["", f"Agreement with the live timing: over the last {timed} calls the attention core "
-              f"launches ({', '.join('`' + k + '`' for k in sorted(core))}) average {last:.1f} us "
-              f"per call in the trace; bench.py's HIP events on the launch stream measured "
-              f"{live:.1f} us per call in the same run." if live is not None else ""]
+              f"launches ({', '.join('`' + k + '`' for k in sorted(core))}) span {last:.1f} us "
+              f"per call in the trace (first start to last end); bench.py's HIP events on the "
+              f"launch stream measured {live:.1f} us per call in the same run."
+              if live is not None else ""]
     calls = _decode_calls(rows, timed)
     if dec_live and calls:
         # calls are (duration, attention duration, attention kernel): key the runs on the kernel
