@@ -786,10 +786,13 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p_short.exact_r0 = 0;
   p_redo.exact_r0 = n_short;
   std::lock_guard<std::mutex> lock(g_side_mu);
-  // Overlap pays when the short chunks are a latency tail (a few workgroups per sequence
-  // of a long single context); when they are a sizeable share of the work (many packed
-  // sequences), the fork and join cost more than running them in turn.
-  SideStream* side = n_short * a.Hkv <= device_cus() / 4 ? side_stream() : nullptr;
+  // Overlap pays when the short chunks are a latency tail (a few workgroups per sequence)
+  // beside a main kernel long enough to hide them. With many packed sequences they are a
+  // sizeable share of the work, and under kOverlapMinKeys of context the whole call is
+  // short: there the fork and join (~10 us) cost more than running them in turn.
+  constexpr int kOverlapMinKeys = 2048;
+  SideStream* side = (n_short * a.Hkv <= device_cus() / 4 && a.n >= kOverlapMinKeys)
+                         ? side_stream() : nullptr;
   if (p.nsplit > 1) {
     // one round of the split main kernel: its resident workgroups over the chip, less the
     // short chunks' workgroups that run beside it

@@ -299,14 +299,16 @@ int attn_max_chunks(int64_t n, int64_t T, int32_t Hq, int32_t Hkv) {
 }
 
 // Enough workgroups for two per CU (256 CUs) need no split; below that, up to
-// kMaxAttnSplit segments per chunk.
-constexpr int kSplitBlocks = 512;
+// kMaxAttnSplit segments per chunk. A chunk spans at most n keys: with fewer than
+// kSplitMinTiles 32-key tiles none can be cut into two segments of the work list's
+// 8-tile minimum, and the split's extra launches would be pure overhead.
+constexpr int kSplitBlocks = 512, kSplitMinTiles = 16;
 
 AttnSplit attn_split_plan(int64_t n, int64_t T, int32_t Hq, int32_t Hkv) {
-  (void)n;
   const int64_t QR = kAttnSlots / std::max(1, Hq / std::max(1, Hkv));
   const int64_t blocks = std::max<int64_t>(1, (T + QR - 1) / QR) * std::max(1, Hkv);
-  return AttnSplit{blocks >= kSplitBlocks ? 1 : kMaxAttnSplit};
+  const bool split = blocks < kSplitBlocks && (n + 31) / 32 >= kSplitMinTiles;
+  return AttnSplit{split ? kMaxAttnSplit : 1};
 }
 
 AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D) {
