@@ -114,6 +114,21 @@ def test_fuse_small_full(pe, n, K, H, A):
     assert np.array_equal(e, want["embed_rows"])
 
 
+# the wide-tile GEMM (256 x 320 and 256 x 256 tiles, taken when the grid fills the chip),
+# with a ragged last row block; rows sampled around both ends and the ragged tail
+@pytest.mark.parametrize("n,K,H,A", [(8200, 2, 2560, 256), (4100, 1, 4096, 384)])
+def test_fuse_wide_tiles(pe, n, K, H, A):
+    print(f"fuse wide n={n} K={K} H={H} A={A}", flush=True)
+    rng = np.random.default_rng(n)
+    last = (n // 256) * 256
+    extra = np.arange(n, n + 3) if K > 1 else np.arange(0)   # depth-1 rows: the mask row
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(last - 8, n), extra,
+                                     rng.integers(0, n, 120)]))
+    h, e, want = _fuse_case(pe, n, K, H, A, seed=13, rows=rows, vocab=1000)
+    assert_close(h, want["hidden"], "hidden")
+    assert np.array_equal(e, want["embed_rows"])
+
+
 @pytest.mark.parametrize("n,K,H,A", [(256, 4, 256, 1536), (300, 4, 136, 520), (97, 1, 64, 64),
                                      (4096, 4, 640, 7680)])
 def test_fuse_fc_norm(pe, n, K, H, A):

@@ -12,8 +12,9 @@
 // first depth-1 row; the fill kernel copies it to the remaining depth >= 1 rows and
 // gathers the embedding rows.
 //
-// The projection runs on the DMA-fed GEMM of gemm.h when 3 H_target is a multiple of
-// 192. Otherwise fc_gemm, register-staged: C[M,N] = A[M,K] * B[N,K]^T, bf16 in, fp32
+// The projection runs on the wide DMA-fed GEMM of gemm.h (256 x 320 or 256 x 256 tiles)
+// when 3 H_target is a multiple of 128, H a multiple of 320 or 256 and the grid fills the
+// chip; else on the 256 x 128 DMA-fed GEMM when 3 H_target is a multiple of 192. Otherwise fc_gemm, register-staged: C[M,N] = A[M,K] * B[N,K]^T, bf16 in, fp32
 // accumulate and out, on v_mfma_f32_32x32x16_bf16. Workgroup tile 256x128x64, 4 waves in
 // 2x2, wave tile 128x64 (4x2 MFMA tiles). Both operands are K-contiguous, so each MFMA operand is one
 // 16-byte LDS read; LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by
@@ -226,7 +227,26 @@ hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* au
                        uint16_t* embed_out, hipStream_t stream) {
   (void)idx;  // depth-0 row r is anchor r; depth >= 1 rows need no anchor
   hipError_t e;
-  if (a.aux_dim % (gemm::kStages * gemm::kDmaK) == 0) {
+  // The wide tile needs a full round of workgroups (256 CUs): with fewer (e.g. 4096 rows
+  // at H = 640: 32 tiles) the 256x128 tile's larger grid is faster.
+  constexpr int kWideMinTiles = 256;
+  int wide = gemm::wide_width(a.H, a.aux_dim);
+  if (wide != 0 && (a.H / wide) * ((a.n + BM - 1) / BM) < kWideMinTiles) wide = 0;
+  if (wide != 0) {
+    // depth-0 rows on the wide DMA-fed kernel, the mask row (first depth-1 row) on its own
+    const dim3 grid((unsigned)((a.H / wide) * ((a.n + BM - 1) / BM)));
+    if (wide == 320)
+      hipLaunchKernelGGL((gemm::dma_gemm_wide_kernel<320, gemm::StoreF32>), grid,
+                         dim3(gemm::kWideThreads), 0, stream, aux, fc_weight, (int)a.n, a.H,
+                         a.aux_dim, gemm::StoreF32{hidden_out, a.H});
+    else
+      hipLaunchKernelGGL((gemm::dma_gemm_wide_kernel<256, gemm::StoreF32>), grid,
+                         dim3(gemm::kWideThreads), 0, stream, aux, fc_weight, (int)a.n, a.H,
+                         a.aux_dim, gemm::StoreF32{hidden_out, a.H});
+    if (a.T > a.n)
+      hipLaunchKernelGGL(fc_row_kernel, dim3((a.H + 3) / 4), dim3(256), 0, stream, mask_hidden,
+                         fc_weight, hidden_out + (size_t)a.n * a.H, a.H, a.aux_dim);
+  } else if (a.aux_dim % (gemm::kStages * gemm::kDmaK) == 0) {
     // depth-0 rows on the DMA-fed kernel, the mask row (first depth-1 row) on its own
     const dim3 grid(((a.H + BN - 1) / BN) * ((a.n + BM - 1) / BM));
     hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, gemm::StoreF32, false>), grid, dim3(kThreads),

@@ -186,6 +186,117 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
   }
 }
 
+// Wide variant: workgroup tile 256 x BNW (BNW = 256 or 320; N a multiple of BNW), 8 waves
+// of 64 x BNW/2 (2 x BNW/64 MFMA tiles), two waves per SIMD. A 64-wide k step moves
+// (256 + BNW) x 128 bytes for 2 x 256 x BNW x 64 FLOP: 1.5x (BNW = 256) to 1.66x (320)
+// fewer bytes per FLOP than the 256x128 tile. That is what bounds these projections: the
+// operand stream a CU can keep in flight (~16 B per clock measured), not the MFMA pipe. The
+// LDS holds a two-stage ring (144 KB at BNW = 320): step k+1 streams in while step k is
+// computed, one barrier per step. K must be a multiple of 2 x 64. Per-element epilogues.
+constexpr int kWideThreads = 512, kWideWaves = kWideThreads / 64, kWideDK = 64;
+
+template <int BNW, typename Epi>
+__global__ __launch_bounds__(kWideThreads) void dma_gemm_wide_kernel(const uint16_t* __restrict__ A,
+                                                                     const uint16_t* __restrict__ W,
+                                                                     int M, int N, int K, Epi epi) {
+  static_assert(!Epi::kWaveTile, "per-element epilogues only");
+  constexpr int DK = kWideDK;
+  constexpr int kABytes = BM * DK * 2, kBBytes = BNW * DK * 2;
+  constexpr int kADma = kABytes / 1024 / kWideWaves, kBDma = kBBytes / 1024 / kWideWaves;
+  static_assert(kABytes % (1024 * kWideWaves) == 0 && kBBytes % (1024 * kWideWaves) == 0, "DMA split");
+  constexpr int kRowsPerDma = 1024 / (DK * 2), kChunks = DK / 8;
+  constexpr int NI = 2, NJ = BNW / 64, WN = BNW / 2;  // MFMA tiles per wave, wave columns
+  __shared__ __attribute__((aligned(1024))) char As0[kABytes];
+  __shared__ __attribute__((aligned(1024))) char As1[kABytes];
+  __shared__ __attribute__((aligned(1024))) char Bs0[kBBytes];
+  __shared__ __attribute__((aligned(1024))) char Bs1[kBBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ntn = N / BNW;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BNW;
+  const int r32 = lane & 31, half = lane >> 5;
+
+  uint32_t aoff[kADma], boff[kBDma];
+#pragma unroll
+  for (int j = 0; j < kADma; ++j) {
+    const int row = (wave + j * kWideWaves) * kRowsPerDma + lane / kChunks;
+    const int g = (lane % kChunks) ^ dswz_key<DK>(row);
+    aoff[j] = (uint32_t)(((size_t)(min(m0 + row, M - 1) - m0) * K + g * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < kBDma; ++j) {
+    const int row = (wave + j * kWideWaves) * kRowsPerDma + lane / kChunks;
+    const int g = (lane % kChunks) ^ dswz_key<DK>(row);
+    boff[j] = (uint32_t)(((size_t)(min(n0 + row, N - 1) - n0) * K + g * 8) * 2);
+  }
+  auto issue = [&](int ks, char* Ad, char* Bd) {
+    const char* ab = uniform_opaque(reinterpret_cast<const char*>(A + (size_t)m0 * K + (size_t)ks * DK));
+    const char* bb = uniform_opaque(reinterpret_cast<const char*>(W + (size_t)n0 * K + (size_t)ks * DK));
+#pragma unroll
+    for (int j = 0; j < kADma; ++j) dma16(ab + lane_opaque(aoff[j]), Ad + (wave + j * kWideWaves) * 1024);
+#pragma unroll
+    for (int j = 0; j < kBDma; ++j) dma16(bb + lane_opaque(boff[j]), Bd + (wave + j * kWideWaves) * 1024);
+  };
+
+  floatx16 acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const char* As, const char* Bs) {
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks) {
+      bf16x8 af[NI], bfr[NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        af[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(As + dswz<DK>(wm * 64 + i * 32 + r32, ks * 2 + half)));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        bfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(Bs + dswz<DK>(wn * WN + j * 32 + r32, ks * 2 + half)));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  const int nk = K / DK;  // even
+  issue(0, As0, Bs0);
+  for (int ks = 0; ks < nk; ks += 2) {
+    wait_vm<0>();
+    __syncthreads();  // step ks landed in stage 0; stage 1 is free
+    issue(ks + 1, As1, Bs1);
+    compute(As0, Bs0);
+    wait_vm<0>();
+    __syncthreads();  // step ks+1 landed in stage 1; stage 0 is free
+    if (ks + 2 < nk) issue(ks + 2, As0, Bs0);
+    compute(As1, Bs1);
+  }
+
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + wn * WN + j * 32 + r32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row < M) epi(row, col, acc[i][j][r]);
+      }
+    }
+}
+
+// Width of the wide variant for an N x K problem, or 0 if it does not apply.
+inline int wide_width(int N, int K) {
+  if (K % (2 * kWideDK) != 0 || N <= 0) return 0;
+  return N % 320 == 0 ? 320 : N % 256 == 0 ? 256 : 0;
+}
+
 // Epilogues are called per element (row, col, value) inside [M) x [N), or, with
 // kWaveTile, once per wave with the wave's accumulators: acc[i][j] is the 32x32 MFMA tile
 // at rows row0 + 32 i, columns col0 + 32 j; lane l holds column l % 32 of it, rows
