@@ -227,31 +227,12 @@ hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* au
                        uint16_t* embed_out, hipStream_t stream) {
   (void)idx;  // depth-0 row r is anchor r; depth >= 1 rows need no anchor
   hipError_t e;
-  // The wide tile needs a full round of workgroups (256 CUs): with fewer (e.g. 4096 rows
-  // at H = 640: 32 tiles) the 256x128 tile's larger grid is faster.
-  constexpr int kWideMinTiles = 256;
-  int wide = gemm::wide_width(a.H, a.aux_dim);
-  if (wide != 0 && (a.H / wide) * ((a.n + BM - 1) / BM) < kWideMinTiles) wide = 0;
-  if (wide != 0) {
-    // depth-0 rows on the wide DMA-fed kernel, the mask row (first depth-1 row) on its own
-    const dim3 grid((unsigned)((a.H / wide) * ((a.n + BM - 1) / BM)));
-    if (wide == 320)
-      hipLaunchKernelGGL((gemm::dma_gemm_wide_kernel<320, gemm::StoreF32>), grid,
-                         dim3(gemm::kWideThreads), 0, stream, aux, fc_weight, (int)a.n, a.H,
-                         a.aux_dim, gemm::StoreF32{hidden_out, a.H});
-    else
-      hipLaunchKernelGGL((gemm::dma_gemm_wide_kernel<256, gemm::StoreF32>), grid,
-                         dim3(gemm::kWideThreads), 0, stream, aux, fc_weight, (int)a.n, a.H,
-                         a.aux_dim, gemm::StoreF32{hidden_out, a.H});
-    if (a.T > a.n)
-      hipLaunchKernelGGL(fc_row_kernel, dim3((a.H + 3) / 4), dim3(256), 0, stream, mask_hidden,
-                         fc_weight, hidden_out + (size_t)a.n * a.H, a.H, a.aux_dim);
-  } else if (a.aux_dim % (gemm::kStages * gemm::kDmaK) == 0) {
-    // depth-0 rows on the DMA-fed kernel, the mask row (first depth-1 row) on its own
-    const dim3 grid(((a.H + BN - 1) / BN) * ((a.n + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, gemm::StoreF32, false>), grid, dim3(kThreads),
-                       0, stream, aux, fc_weight, (int)a.n, a.H, a.aux_dim,
-                       gemm::StoreF32{hidden_out, a.H});
+  if (gemm::wide_width(a.n, a.H, a.aux_dim) != 0 ||
+      a.aux_dim % (gemm::kStages * gemm::kDmaK) == 0) {
+    // depth-0 rows on a DMA-fed kernel, the mask row (first depth-1 row) on its own
+    e = gemm::launch_dma_gemm(aux, fc_weight, (int)a.n, a.H, a.aux_dim,
+                              gemm::StoreF32{hidden_out, a.H}, stream);
+    if (e != hipSuccess) return e;
     if (a.T > a.n)
       hipLaunchKernelGGL(fc_row_kernel, dim3((a.H + 3) / 4), dim3(256), 0, stream, mask_hidden,
                          fc_weight, hidden_out + (size_t)a.n * a.H, a.H, a.aux_dim);

@@ -291,10 +291,44 @@ __global__ __launch_bounds__(kWideThreads) void dma_gemm_wide_kernel(const uint1
     }
 }
 
-// Width of the wide variant for an N x K problem, or 0 if it does not apply.
-inline int wide_width(int N, int K) {
-  if (K % (2 * kWideDK) != 0 || N <= 0) return 0;
-  return N % 320 == 0 ? 320 : N % 256 == 0 ? 256 : 0;
+// Width of the wide variant for an M x N x K problem, or 0 if it does not apply: K a
+// multiple of 128, N of 320 or 256, and a full round of workgroups (256 CUs; with fewer,
+// the 256x128 tile's larger grid is faster, e.g. 4096 x 640: 32 wide tiles against 80).
+constexpr int kWideMinTiles = 256;
+inline int wide_width(int M, int N, int K) {
+  if (K % (2 * kWideDK) != 0 || N <= 0 || M <= 0) return 0;
+  const int w = N % 320 == 0 ? 320 : N % 256 == 0 ? 256 : 0;
+  if (w == 0 || (long long)(N / w) * ((M + BM - 1) / BM) < kWideMinTiles) return 0;
+  return w;
+}
+
+// C = A W^T through the fastest DMA-fed kernel that applies: the wide tile (per-element
+// epilogues, see wide_width), else the 256x128 tile (K a multiple of 64; with a tail
+// step when K / 64 is not a multiple of 3).
+template <typename Epi>
+hipError_t launch_dma_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K,
+                           const Epi& epi, hipStream_t stream) {
+  const int wide = Epi::kWaveTile ? 0 : wide_width(M, N, K);
+  if constexpr (!Epi::kWaveTile) {
+    if (wide != 0) {
+      const dim3 grid((unsigned)((N / wide) * ((M + BM - 1) / BM)));
+      if (wide == 320)
+        hipLaunchKernelGGL((dma_gemm_wide_kernel<320, Epi>), grid, dim3(kWideThreads), 0, stream,
+                           A, W, M, N, K, epi);
+      else
+        hipLaunchKernelGGL((dma_gemm_wide_kernel<256, Epi>), grid, dim3(kWideThreads), 0, stream,
+                           A, W, M, N, K, epi);
+      return hipGetLastError();
+    }
+  }
+  const dim3 grid(grid_tiles(M, N));
+  if ((K / kDmaK) % kStages == 0)
+    hipLaunchKernelGGL((dma_gemm_kernel<kDmaK, Epi, false>), grid, dim3(kThreads), 0, stream, A,
+                       W, M, N, K, epi);
+  else
+    hipLaunchKernelGGL((dma_gemm_kernel<kDmaK, Epi, true>), grid, dim3(kThreads), 0, stream, A, W,
+                       M, N, K, epi);
+  return hipGetLastError();
 }
 
 // Epilogues are called per element (row, col, value) inside [M) x [N), or, with

@@ -135,15 +135,7 @@ hipError_t launch_layer1_qkv(const Layer1Args& a, const float* hidden, const uin
                      w_emb, w_hid, x, M, a.H, a.eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const StoreQKV epi{q, k, v, nq, nk};
-  const dim3 grid(gemm::grid_tiles(M, N)), block(gemm::kThreads);
-  if ((K / gemm::kDmaK) % gemm::kStages == 0)
-    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, StoreQKV, false>), grid, block, 0,
-                       stream, x, w_qkv, M, N, K, epi);
-  else
-    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, StoreQKV, true>), grid, block, 0,
-                       stream, x, w_qkv, M, N, K, epi);
-  e = hipGetLastError();
+  e = gemm::launch_dma_gemm(x, w_qkv, M, N, K, StoreQKV{q, k, v, nq, nk}, stream);
   if (e != hipSuccess) return e;
   if (a.T > a.n + 1) {
     const size_t work = (size_t)(a.T - a.n - 1) * (N / 8);
@@ -165,15 +157,7 @@ hipError_t launch_layer_qkv(const LayerArgs& a, const float* h, const uint16_t* 
   uint16_t* x = reinterpret_cast<uint16_t*>(ws);
   hipError_t e = launch_rms_rows(h, w_norm, x, a.T, a.H, a.eps, stream);
   if (e != hipSuccess) return e;
-  const StoreQKV epi{q, k, v, nq, nk};
-  const dim3 grid(gemm::grid_tiles(a.T, N)), block(gemm::kThreads);
-  if ((a.H / gemm::kDmaK) % gemm::kStages == 0)
-    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, StoreQKV, false>), grid, block, 0,
-                       stream, x, w_qkv, a.T, N, a.H, epi);
-  else
-    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, StoreQKV, true>), grid, block, 0,
-                       stream, x, w_qkv, a.T, N, a.H, epi);
-  return hipGetLastError();
+  return gemm::launch_dma_gemm(x, w_qkv, a.T, N, a.H, StoreQKV{q, k, v, nq, nk}, stream);
 }
 
 }  // namespace peagle

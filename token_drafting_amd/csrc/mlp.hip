@@ -223,14 +223,7 @@ __global__ __launch_bounds__(256) void argmax_keys_kernel(const uint64_t* __rest
 template <typename Epi>
 hipError_t gemm_launch(const uint16_t* A, const uint16_t* W, int M, int N, int K, const Epi& epi,
                        hipStream_t stream) {
-  const dim3 grid(gemm::grid_tiles(M, N)), block(gemm::kThreads);
-  if ((K / gemm::kDmaK) % gemm::kStages == 0)
-    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, Epi, false>), grid, block, 0, stream, A,
-                       W, M, N, K, epi);
-  else
-    hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, Epi, true>), grid, block, 0, stream, A,
-                       W, M, N, K, epi);
-  return hipGetLastError();
+  return gemm::launch_dma_gemm(A, W, M, N, K, epi, stream);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
