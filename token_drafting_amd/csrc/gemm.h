@@ -192,14 +192,16 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
 // fewer bytes per FLOP than the 256x128 tile. That is what bounds these projections: the
 // operand stream a CU can keep in flight (~16 B per clock measured), not the MFMA pipe. The
 // LDS holds a two-stage ring (144 KB at BNW = 320): step k+1 streams in while step k is
-// computed, one barrier per step. K must be a multiple of 2 x 64. Per-element epilogues.
+// computed, one barrier per step. K must be a multiple of 2 x 64. Epilogues that combine
+// lanes get the wave's 64 x BNW/2 tile (acc[2][BNW/64]); they need BNW = 256, so that a
+// wave's columns are whole 64-column chunks.
 constexpr int kWideThreads = 512, kWideWaves = kWideThreads / 64, kWideDK = 64;
 
 template <int BNW, typename Epi>
 __global__ __launch_bounds__(kWideThreads) void dma_gemm_wide_kernel(const uint16_t* __restrict__ A,
                                                                      const uint16_t* __restrict__ W,
                                                                      int M, int N, int K, Epi epi) {
-  static_assert(!Epi::kWaveTile, "per-element epilogues only");
+  static_assert(!Epi::kWaveTile || BNW == 256, "lane-combining epilogues take 64-column chunks");
   constexpr int DK = kWideDK;
   constexpr int kABytes = BM * DK * 2, kBBytes = BNW * DK * 2;
   constexpr int kADma = kABytes / 1024 / kWideWaves, kBDma = kBBytes / 1024 / kWideWaves;
@@ -278,48 +280,54 @@ __global__ __launch_bounds__(kWideThreads) void dma_gemm_wide_kernel(const uint1
     compute(As1, Bs1);
   }
 
+  if constexpr (Epi::kWaveTile) {
+    epi.wave_tile(acc, m0 + wm * 64, n0 + wn * WN, lane, M, N);
+  } else {
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + wn * WN + j * 32 + r32;
+      for (int j = 0; j < NJ; ++j) {
+        const int col = n0 + wn * WN + j * 32 + r32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < M) epi(row, col, acc[i][j][r]);
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < M) epi(row, col, acc[i][j][r]);
+        }
       }
-    }
+  }
 }
 
 // Width of the wide variant for an M x N x K problem, or 0 if it does not apply: K a
 // multiple of 128, N of 320 or 256, and a full round of workgroups (256 CUs; with fewer,
 // the 256x128 tile's larger grid is faster, e.g. 4096 x 640: 32 wide tiles against 80).
+// Epilogues that combine lanes (wave_tile) take only the 256-wide tile.
 constexpr int kWideMinTiles = 256;
-inline int wide_width(int M, int N, int K) {
+inline int wide_width(int M, int N, int K, bool lane_combining = false) {
   if (K % (2 * kWideDK) != 0 || N <= 0 || M <= 0) return 0;
-  const int w = N % 320 == 0 ? 320 : N % 256 == 0 ? 256 : 0;
+  const int w = (N % 320 == 0 && !lane_combining) ? 320 : N % 256 == 0 ? 256 : 0;
   if (w == 0 || (long long)(N / w) * ((M + BM - 1) / BM) < kWideMinTiles) return 0;
   return w;
 }
 
-// C = A W^T through the fastest DMA-fed kernel that applies: the wide tile (per-element
-// epilogues, see wide_width), else the 256x128 tile (K a multiple of 64; with a tail
-// step when K / 64 is not a multiple of 3).
+// C = A W^T through the fastest DMA-fed kernel that applies: the wide tile (see
+// wide_width), else the 256x128 tile (K a multiple of 64; with a tail step when K / 64 is
+// not a multiple of 3).
 template <typename Epi>
 hipError_t launch_dma_gemm(const uint16_t* A, const uint16_t* W, int M, int N, int K,
                            const Epi& epi, hipStream_t stream) {
-  const int wide = Epi::kWaveTile ? 0 : wide_width(M, N, K);
-  if constexpr (!Epi::kWaveTile) {
-    if (wide != 0) {
-      const dim3 grid((unsigned)((N / wide) * ((M + BM - 1) / BM)));
-      if (wide == 320)
+  const int wide = wide_width(M, N, K, Epi::kWaveTile);
+  if (wide != 0) {
+    const dim3 grid((unsigned)((N / wide) * ((M + BM - 1) / BM)));
+    if constexpr (!Epi::kWaveTile) {
+      if (wide == 320) {
         hipLaunchKernelGGL((dma_gemm_wide_kernel<320, Epi>), grid, dim3(kWideThreads), 0, stream,
                            A, W, M, N, K, epi);
-      else
-        hipLaunchKernelGGL((dma_gemm_wide_kernel<256, Epi>), grid, dim3(kWideThreads), 0, stream,
-                           A, W, M, N, K, epi);
-      return hipGetLastError();
+        return hipGetLastError();
+      }
     }
+    hipLaunchKernelGGL((dma_gemm_wide_kernel<256, Epi>), grid, dim3(kWideThreads), 0, stream, A,
+                       W, M, N, K, epi);
+    return hipGetLastError();
   }
   const dim3 grid(grid_tiles(M, N));
   if ((K / kDmaK) % kStages == 0)

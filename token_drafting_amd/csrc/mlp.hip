@@ -143,13 +143,15 @@ struct StoreSwiGLU {
   static constexpr bool kWaveTile = true;
   uint16_t* act;
   int I;
-  __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[4][2], int row0, int col0,
+  // acc[i][j]: the 32x32 MFMA tile at rows row0 + 32 i, columns col0 + 32 j
+  template <int NI, int NJ>
+  __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
                                             int lane, int M, int N) const {
     const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         const int colb = col0 + 32 * j;  // packed columns colb .. colb + 31: 16 gate, 16 up
         const int out_col = (colb >> 5) * 16 + r32;
 #pragma unroll
@@ -170,39 +172,45 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Per row and per wave (64 columns): the largest (value, lowest column) as one 64-bit
-// key, keys [M, ceil(N / 64)].
+// Per row and per 64-column chunk: the largest (value, lowest column) as one 64-bit key,
+// keys [M, ceil(N / 64)]. A wave tile is NJ / 2 whole chunks (col0 a multiple of 64).
 struct StoreArgmaxKeys {
   static constexpr bool kWaveTile = true;
   uint64_t* keys;
   int nchunks;
-  __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[4][2], int row0, int col0,
+  template <int NI, int NJ>
+  __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
                                             int lane, int M, int N) const {
+    static_assert(NJ % 2 == 0, "whole 64-column chunks");
     const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < NJ / 2; ++c) {
+      const int cc = col0 + 64 * c;  // this chunk's first column
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        uint64_t best = 0;
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = col0 + 32 * j + r32;
-          const uint64_t k = col < N ? ((uint64_t)order_key(acc[i][j][r]) << 32) |
-                                           (uint64_t)(0xFFFFFFFFu - (uint32_t)col)
-                                     : 0;
-          best = k > best ? k : best;
+        for (int r = 0; r < 16; ++r) {
+          uint64_t best = 0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = cc + 32 * j + r32;
+            const uint64_t k = col < N ? ((uint64_t)order_key(acc[i][2 * c + j][r]) << 32) |
+                                             (uint64_t)(0xFFFFFFFFu - (uint32_t)col)
+                                       : 0;
+            best = k > best ? k : best;
+          }
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) {
+            const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
+            const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
+            const uint64_t other = ((uint64_t)hi << 32) | lo;
+            best = other > best ? other : best;
+          }
+          const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          // a chunk whose 64 columns all lie past N (the last tile) has no key
+          if (r32 == 0 && row < M && cc < N) keys[(size_t)row * nchunks + (cc >> 6)] = best;
         }
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
-          const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
-          const uint64_t other = ((uint64_t)hi << 32) | lo;
-          best = other > best ? other : best;
-        }
-        const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-        // a wave whose 64 columns all lie past N (the last tile) owns no chunk
-        if (r32 == 0 && row < M && col0 < N) keys[(size_t)row * nchunks + (col0 >> 6)] = best;
-      }
+    }
   }
 };
 
