@@ -9,7 +9,9 @@
 // convention, frequencies theta^(-2j/D); applied to q and k, not v.
 //
 // Kernels:
-//   rope_table_kernel    cos/sin [max_pos+1, D/2] fp32, angles and cos/sin in fp64.
+//   rope_table_kernel    cos/sin [max_pos+1, D/2] fp32, angles and cos/sin in fp64
+//                        (direct sincos every 16th position of a thread, fp64 angle
+//                        addition between).
 //   qcount/qlist_kernel  anchor-major list of draft rows (all depths of anchor 0, then
 //                        of anchor 1, ...) with per-row (row, anchor, depth, seq start),
 //                        and qstart[p] = first entry of anchor p.
@@ -28,22 +30,33 @@ namespace peagle {
 
 namespace {
 
+// One thread per (frequency j, position residue p0 < P): the inverse frequency once, then
+// positions p0, p0 + P, ... advance by the fp64 rotation through P theta_j (angle
+// addition), re-anchored with a direct sincos every kRopeAnchor steps; the rotation's
+// rounding (~1e-16 per step) stays far below the fp32 table's. Consecutive threads take
+// consecutive j, so each position's row is written contiguously.
+constexpr int kRopeAnchor = 16;
 __global__ __launch_bounds__(256) void rope_table_kernel(float* __restrict__ cos_out,
                                                          float* __restrict__ sin_out, int half,
-                                                         int D, double theta, int max_pos) {
-  __shared__ double inv[512];  // theta^(-2j/D) for j < D/2 (D <= 1024)
-  for (int j = threadIdx.x; j < half && j < 512; j += blockDim.x)
-    inv[j] = pow(theta, -2.0 * (double)j / (double)D);
-  __syncthreads();
-  const size_t total = (size_t)(max_pos + 1) * half;
-  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
-       t += (size_t)gridDim.x * blockDim.x) {
-    const int pos = (int)(t / half), j = (int)(t % half);
-    const double ang = (double)pos * (j < 512 ? inv[j] : pow(theta, -2.0 * (double)j / (double)D));
-    double sn, cs;
-    sincos(ang, &sn, &cs);
-    cos_out[t] = (float)cs;
-    sin_out[t] = (float)sn;
+                                                         int D, double theta, int max_pos, int P) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int j = (int)(t % half);
+  const int64_t p0 = t / half;
+  if (p0 >= P || p0 > max_pos) return;
+  const double inv = pow(theta, -2.0 * (double)j / (double)D);
+  double step_s, step_c, sn = 0.0, cs = 1.0;
+  sincos((double)P * inv, &step_s, &step_c);
+  int k = 0;
+  for (int64_t pos = p0; pos <= max_pos; pos += P, ++k) {
+    if (k % kRopeAnchor == 0) {
+      sincos((double)pos * inv, &sn, &cs);
+    } else {
+      const double c2 = fma(cs, step_c, -sn * step_s);
+      sn = fma(sn, step_c, cs * step_s);
+      cs = c2;
+    }
+    cos_out[pos * half + j] = (float)cs;
+    sin_out[pos * half + j] = (float)sn;
   }
 }
 
@@ -282,10 +295,13 @@ hipError_t launch_for_d(int D, F&& f) {
 hipError_t launch_rope_table(int32_t head_dim, double theta, int32_t max_pos, float* cos_out,
                              float* sin_out, hipStream_t stream) {
   const int half = head_dim / 2;
-  const size_t total = (size_t)(max_pos + 1) * half;
-  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  // position stride: ~128K threads, each taking every P-th position
+  const int P = (int)std::min<int64_t>((int64_t)max_pos + 1,
+                                       std::max<int64_t>(1, ((int64_t)1 << 17) / half));
+  const int64_t threads = (int64_t)P * half;
+  const int blocks = (int)((threads + 255) / 256);
   hipLaunchKernelGGL(rope_table_kernel, dim3(blocks), dim3(256), 0, stream, cos_out, sin_out, half,
-                     head_dim, theta, max_pos);
+                     head_dim, theta, max_pos, P);
   return hipGetLastError();
 }
 
