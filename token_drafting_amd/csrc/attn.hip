@@ -92,7 +92,11 @@ __device__ __forceinline__ int v_off(int d, int chunk) {
 // fits in the 256-register budget beside O (128), Q (64) and S (16); one more spills a Q
 // fragment to scratch inside the loop, whose reload then waits on the tile DMA. The split
 // variant keeps its segment bounds live as well and reads V one fragment less ahead.
+// D = 128 has registers to spare: 4 K and 6 V fragments ahead (measured ~2% faster than
+// 2 / 3 at 55266 rows, 32/8 heads; 8 / 8 gained less).
 constexpr int kPrefetchK = 2, kPrefetchV = 3;
+template <int D> constexpr int prefetch_k() { return D == 128 ? 4 : kPrefetchK; }
+template <int D> constexpr int prefetch_v() { return D == 128 ? 6 : kPrefetchV; }
 
 struct AttnParams {
   const int4* qinfo;
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
       for (int r = 0; r < 16; ++r) s[nt][r] = 0.f;
     const char* kbase = Ks + r32 * C::KROW + half * 16;
     if constexpr (!EXACT) {
-      // K fragments are read kPrefetchK steps ahead of the MFMA that uses them, so LDS
+      // K fragments are read prefetch_k<D>() steps ahead of the MFMA that uses them, so LDS
       // latency overlaps the MFMA chain instead of stalling each step.
       bf16x8 kf[C::DK];
 #pragma unroll
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
       for (int kk = 0; kk < C::DK; ++kk)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(kf[kk], qf[nt][kk], s[nt]);
-      sched_reads_ahead<C::DK, kPrefetchK, NT>();
+      sched_reads_ahead<C::DK, prefetch_k<D>(), NT>();
     } else {
 #pragma unroll
       for (int kk = 0; kk < C::DK; ++kk) {
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
         for (int mt = 0; mt < C::MT; ++mt)
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) o[nt][mt] = mfma32(vf[mt][ks], pb[nt][ks], o[nt][mt]);
-      sched_reads_ahead<2 * C::MT, SPLIT ? kPrefetchV - 1 : kPrefetchV, NT>();
+      sched_reads_ahead<2 * C::MT, SPLIT ? prefetch_v<D>() - 1 : prefetch_v<D>(), NT>();
     } else {
 #pragma unroll
       for (int mt = 0; mt < C::MT; ++mt)
