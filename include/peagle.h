@@ -157,6 +157,11 @@ size_t peagle_draft_attn_workspace_bytes(int64_t n, int64_t T, int32_t num_q_hea
  *                    device memory, 256-byte aligned; its contents are scratch
  * head_dim in {64, 128, 256}; Hq % Hkv == 0 and 256 % (Hq/Hkv) == 0.
  * Equal to peagle_draft_attn_prepare followed by peagle_draft_attn_core.
+ * Streams: all work is ordered after earlier work on `stream` and before later work on
+ * it. The core may run part of its kernels on a second stream the library creates once
+ * per device (default priority, kept until the process ends), forked from `stream` by an
+ * event and joined back into it before the call returns; calls from several host threads
+ * serialize their enqueueing on an internal lock.
  */
 int peagle_draft_attn_fwd(int64_t n, int32_t K, int64_t T, const int32_t *idx,
                           const int32_t *depth_off, const int32_t *row_of,
