@@ -108,3 +108,48 @@ def test_decode_calls_grouped_by_workload_runs():
     runs = _workload_runs(seq, 2)
     assert [[x for _, x in r] for r in runs] == [[1, 2], [3, 4]]
     assert _workload_runs(seq[:2], 2) == [seq[:2]]
+
+
+def test_core_call_bytes_take_each_kernel_total_per_call(tmp_path):
+    # two core calls: one main dispatch each, the exact kernel twice each (short chunks,
+    # then the redo pass); a call's bytes are each kernel's total over the calls
+    main = "void peagle::attn_core_kernel<256, false, false>(peagle::AttnParams)"
+    exact = "void peagle::attn_core_kernel<256, true, false>(peagle::AttnParams)"
+    rows = [("__amd_rocclr_copyBuffer", 512.0), (exact, 10.0), (main, 100.0), (exact, 2.0),
+            (exact, 10.0), (main, 100.0), (exact, 2.0)]
+    _write_run(tmp_path / "f", "FETCH_SIZE", rows)
+    _write_run(tmp_path / "w", "WRITE_SIZE", [(n, 2 * v if "copy" in n else v) for n, v in rows])
+    rec = profiling.summarize(str(tmp_path / "f"), str(tmp_path / "w"), copy_mib=1)["record"]
+    kib_per_call = 100.0 + 10.0 + 2.0
+    assert abs(rec["core_call_fetch_bytes"] - kib_per_call * 2048.0) < 1e-6
+    assert abs(rec["core_call_write_bytes"] - kib_per_call * 1024.0) < 1e-6
+
+
+def test_trace_agreement_takes_each_core_call_wall_span(tmp_path):
+    # the short-chunk launch runs on a second stream and overlaps the main kernel: a call
+    # lasts from its first launch's start to its last launch's end, not the sum
+    trace = tmp_path / "trace"
+    os.makedirs(trace)
+    names = {"main": "void peagle::attn_core_kernel<256, false, false>(peagle::AttnParams)",
+             "short": "void peagle::attn_core_kernel<256, true, false>(peagle::AttnParams)",
+             "prep": "void peagle::rope_rotate_kernel<unsigned int>(int)",
+             "acc": "void peagle::accept_kernel<unsigned int, false>(int)"}
+    launches = []
+    t = 0
+    for _ in range(3):   # prep, then main [t+10, t+1010] beside short [t+20, t+520], redo, accept
+        launches += [("prep", t, t + 5), ("short", t + 20, t + 520), ("main", t + 10, t + 1010),
+                     ("short", t + 1012, t + 1016), ("acc", t + 1020, t + 1100)]
+        t += 2000
+    with open(trace / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for k, st, en in launches:
+            w.writerow({"Kernel_Name": names[k], "Start_Timestamp": st * 1000,
+                        "End_Timestamp": en * 1000})
+    log = tmp_path / "bench.log"
+    log.write_text(json.dumps({"stage_ms": {"attn_core": 1.006}}) + "\n")
+    out = tmp_path / "summary.md"
+    profiling.write_trace_summary(str(out), str(trace), str(log), "t", "cmd", timed=2)
+    text = out.read_text()
+    assert "span 1006.0 us per call" in text   # 10 .. 1016, not 1000 + 500 + 4
+    assert "measured 1006.0 us" in text
