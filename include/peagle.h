@@ -28,7 +28,9 @@
  *   - Notation: n tokens in the packed buffer, S packed sequences, K depths, T draft
  *     rows. Draft rows are depth-major; inside a depth they ascend by anchor. Depth 0
  *     keeps every position, so draft row p of depth 0 is anchor p.
- *   - The library keeps no state and is safe to call from several threads.
+ *   - The library keeps no state beyond a per-device cache of the compute-unit count,
+ *     creates no streams or events, and is safe to call from several threads (calls
+ *     that share an output or workspace buffer must not overlap).
  */
 #ifndef PEAGLE_H_
 #define PEAGLE_H_
@@ -157,11 +159,11 @@ size_t peagle_draft_attn_workspace_bytes(int64_t n, int64_t T, int32_t num_q_hea
  *                    device memory, 256-byte aligned; its contents are scratch
  * head_dim in {64, 128, 256}; Hq % Hkv == 0 and 256 % (Hq/Hkv) == 0.
  * Equal to peagle_draft_attn_prepare followed by peagle_draft_attn_core.
- * Streams: all work is ordered after earlier work on `stream` and before later work on
- * it. The core may run part of its kernels on a second stream the library creates once
- * per device (default priority, kept until the process ends), forked from `stream` by an
- * event and joined back into it before the call returns; calls from several host threads
- * serialize their enqueueing on an internal lock.
+ * Streams: every kernel goes on `stream` alone, ordered after earlier work on it and
+ * before later work on it; the call creates no streams or events and takes no locks, so
+ * it can be recorded into a HIP graph. Two calls that share a workspace must not overlap.
+ * T is checked only against n <= T <= K*n: the call takes no r / r_min, so the caller
+ * must pass the T that peagle_cod_counts gave for the idx / depth_off / row_of in use.
  */
 int peagle_draft_attn_fwd(int64_t n, int32_t K, int64_t T, const int32_t *idx,
                           const int32_t *depth_off, const int32_t *row_of,

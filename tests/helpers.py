@@ -85,6 +85,37 @@ def sample_rows(depth_off, cu_seqlens, idx, count=96, seed=0) -> np.ndarray:
     return np.array(sorted(r for r in rows if 0 <= r < T), dtype=np.int64)
 
 
+def chunk_rows(depth_off, cu_seqlens, idx, group: int, seed=0, inside=1) -> np.ndarray:
+    """Rows that touch every workgroup of the attention forward. The kernel visits draft
+    rows in anchor-major order (all depths of an anchor, anchors ascending) and gives each
+    workgroup QR = 256 / group consecutive entries of one sequence's part of that list.
+    Returned: the first and last entry of every such chunk, ``inside`` seeded random
+    entries of each, and every entry of the first and last chunk of the buffer."""
+    rng = np.random.default_rng(seed)
+    depth_off = np.asarray(depth_off, dtype=np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
+    T = int(depth_off[-1])
+    depth = np.repeat(np.arange(len(depth_off) - 1), np.diff(depth_off))
+    order = np.lexsort((depth, idx))          # anchor-major: by anchor, then by depth
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    starts = np.searchsorted(idx[order], cu, side="left")   # list entry of each sequence start
+    QR = 256 // group
+    rows = []
+    chunks = []
+    for s in range(len(cu) - 1):
+        a, b = int(starts[s]), int(starts[s + 1])
+        for c0 in range(a, b, QR):
+            chunks.append((c0, min(c0 + QR, b)))
+    for c0, c1 in chunks:
+        rows += [c0, c1 - 1]
+        rows += rng.integers(c0, c1, size=inside).tolist()
+    if chunks:
+        for c0, c1 in (chunks[0], chunks[-1]):
+            rows += list(range(c0, c1))
+    ent = np.unique(np.asarray(rows, dtype=np.int64))
+    return np.unique(order[ent[(ent >= 0) & (ent < T)]])
+
+
 # Sampling verification decides integers from fp32 arithmetic. A depth's decision is
 # compared with float64 unless u lies within SPEC_RATIO_TOL (relative) of p / q, and the
 # resampled token unless w * Z lies within SPEC_CDF_TOL (absolute, probability units) of a

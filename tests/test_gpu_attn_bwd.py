@@ -92,6 +92,44 @@ def _check_grad(got, want, what):
     assert e["rel_l2"] <= 5e-3, (what, e)
 
 
+def test_attention_bwd_mid_size_full(pe):
+    """The 4096-token Gemma-shaped workload (T = 10375, one kv head, D = 256) in full: the
+    early depth-0 keys are seen by thousands of rows, so their dk and dv sum many query
+    tiles. Every element of dq, dk and dv against the oracle, on workspace and outputs
+    pre-filled with non-zero bytes (nothing may read what the call did not write)."""
+    import torch
+    cfg_id = 2
+    cfg = synth.CONFIGS[cfg_id]
+    n, K, Hq, Hkv, D, theta = cfg["n"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["theta"]
+    cu = synth.cu_seqlens_for(cfg, cfg_id)
+    sel = ocod.cod_select(n, K, cfg["r"], cfg["r_min"], cfg_id, cu)
+    T = int(sel["depth_off"][-1])
+    print(f"attention bwd config {cfg_id} in full: n={n} T={T}", flush=True)
+    qkv = synth.qkv_inputs(cfg_id, T, Hq, Hkv, D)
+    dout = synth.attn_grad_out(cfg_id, T, Hq, D)
+    dcu = to_dev(cu)
+    dsel = pe.cod_select(n, K, cfg["r"], cfg["r_min"], cfg_id, dcu)
+    cos, sin = pe.rope_table(D, theta, pe.rope_max_pos(n, K))
+    q, k, v = to_dev(qkv["q"]), to_dev(qkv["k"]), to_dev(qkv["v"])
+    out, lse, _ = pe.draft_attn(n, K, dsel, dcu, q, k, v, cos, sin)
+    wsb = int(pe.lib().peagle_draft_attn_bwd_workspace_bytes(n, T, Hq, Hkv, D))
+    ws = torch.full((wsb,), 0x41, dtype=torch.uint8, device="cuda")
+    dq = torch.full((T, Hq, D), 3.0, dtype=torch.float32, device="cuda")
+    dk = torch.full((T, Hkv, D), 3.0, dtype=torch.float32, device="cuda")
+    dv = torch.full((T, Hkv, D), 3.0, dtype=torch.float32, device="cuda")
+    pe.draft_attn_bwd(n, K, dsel, dcu, q, k, v, cos, sin, out, lse, to_dev(dout), dq=dq, dk=dk,
+                      dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    want = oattn.draft_attention_backward(qkv["q"], qkv["k"], qkv["v"], sel["idx"],
+                                          sel["depth_off"], cu, theta, dout)
+    got = dict(dq=to_host(dq), dk=to_host(dk), dv=to_host(dv))
+    for name in ("dq", "dk", "dv"):
+        _check_grad(got[name], want[name], f"{name} cfg{cfg_id}")
+    # the keys with the most query tiles behind them, element by element on their own
+    for name in ("dk", "dv"):
+        _check_grad(got[name][:64], want[name][:64], f"{name} cfg{cfg_id} first 64 keys")
+
+
 @pytest.mark.parametrize("cfg_id", [4, 5])
 def test_attention_bwd_full_size_sampled(pe, cfg_id):
     """The full-size workloads in the launch the bench times: dq of sampled query rows;

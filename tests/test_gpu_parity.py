@@ -15,7 +15,7 @@ from oracle import fuse as ofuse
 from oracle import rope as orope
 from oracle import verify as over
 from token_drafting_amd import synth
-from tests.helpers import assert_close, sample_rows, to_dev, to_host
+from tests.helpers import assert_close, chunk_rows, sample_rows, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -228,16 +228,61 @@ def test_attention_small_full(pe, case):
 
 @pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
 def test_attention_full_size_sampled(pe, cfg_id):
+    """Full-size workloads in the launch the bench times. out and lse start as NaN, so a
+    row that no workgroup writes shows; the oracle recomputes both ends of every depth and
+    sequence, a seeded spread, and the first, last and one inner entry of every
+    workgroup's chunk (all entries of the first and last chunk)."""
+    import torch
     cfg = synth.CONFIGS[cfg_id]
-    n, K = cfg["n"], cfg["K"]
+    n, K, Hq, Hkv, D, theta = cfg["n"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["theta"]
     cu = synth.cu_seqlens_for(cfg, cfg_id)
     sel = ocod.cod_select(n, K, cfg["r"], cfg["r_min"], cfg_id, cu)
-    rows = sample_rows(sel["depth_off"], cu, sel["idx"], count=64, seed=cfg_id)
-    print(f"attention config {cfg_id}: {len(rows)} sampled rows", flush=True)
-    o, l, want = _attn_run(pe, n, K, cfg["r"], cfg["r_min"], cfg_id, cu, cfg["Hq"], cfg["Hkv"],
-                           cfg["D"], cfg["theta"], rows=rows)
-    assert_close(o, want["out"], f"out cfg{cfg_id}")
-    assert_close(l, want["lse"], f"lse cfg{cfg_id}", max_rel_l2=1e-3)
+    rows = np.union1d(sample_rows(sel["depth_off"], cu, sel["idx"], count=64, seed=cfg_id),
+                      chunk_rows(sel["depth_off"], cu, sel["idx"], Hq // Hkv, seed=cfg_id))
+    T = int(sel["depth_off"][-1])
+    print(f"attention config {cfg_id}: {len(rows)} sampled rows of {T}", flush=True)
+    qkv = synth.qkv_inputs(cfg_id, T, Hq, Hkv, D)
+    dcu = to_dev(cu)
+    dsel = pe.cod_select(n, K, cfg["r"], cfg["r_min"], cfg_id, dcu)
+    cos, sin = pe.rope_table(D, theta, pe.rope_max_pos(n, K))
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((Hq, T), float("nan"), dtype=torch.float32, device="cuda")
+    pe.draft_attn(n, K, dsel, dcu, to_dev(qkv["q"]), to_dev(qkv["k"]), to_dev(qkv["v"]), cos, sin,
+                  out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), "rows left unwritten (NaN) or non-finite"
+    assert bool(torch.isfinite(lse).all()), "lse left unwritten (NaN) or non-finite"
+    want = oattn.draft_attention(qkv["q"], qkv["k"], qkv["v"], sel["idx"], sel["depth_off"], cu,
+                                 theta, rows=rows)
+    assert_close(to_host(out)[rows], want["out"], f"out cfg{cfg_id}")
+    assert_close(to_host(lse)[:, rows], want["lse"], f"lse cfg{cfg_id}", max_rel_l2=1e-3)
+
+
+# v = 1 everywhere makes every output 1: a softmax average of ones. The main kernel weighs
+# V by P rounded to bf16 (relative error <= 2^-9) and divides by the fp32 sum of the
+# unrounded P, so each output is a weighted mean of values in [1 - 2^-9, 1 + 2^-9].
+UNIT_V_TOL = 2.0 ** -9 + 1e-6
+
+
+@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
+def test_attention_full_size_unit_v(pe, cfg_id):
+    """Every row and head of the full-size workloads, against the closed form above."""
+    import torch
+    cfg = synth.CONFIGS[cfg_id]
+    n, K, Hq, Hkv, D, theta = cfg["n"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg["theta"]
+    cu = synth.cu_seqlens_for(cfg, cfg_id)
+    dcu = to_dev(cu)
+    dsel = pe.cod_select(n, K, cfg["r"], cfg["r_min"], cfg_id, dcu)
+    T = dsel["T"]
+    print(f"attention unit v config {cfg_id}: T={T}", flush=True)
+    qkv = synth.qkv_inputs(cfg_id, T, Hq, Hkv, D)
+    one = synth.f32_to_bf16_bits(np.array([1.0], np.float32))[0]
+    v = torch.full((T, Hkv, D), int(one), dtype=torch.int16, device="cuda")
+    cos, sin = pe.rope_table(D, theta, pe.rope_max_pos(n, K))
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    pe.draft_attn(n, K, dsel, dcu, to_dev(qkv["q"]), to_dev(qkv["k"]), v, cos, sin, out=out)
+    err = float((out - 1.0).abs().max())      # NaN (an unwritten row) propagates
+    assert err <= UNIT_V_TOL, f"max |out - 1| = {err:.3e}"
 
 
 def test_attention_unsplit_small(pe):
@@ -314,6 +359,43 @@ def test_attention_prepare_core_equals_fwd(pe):
     pe.draft_attn(n, K, sel, to_dev(cu), q, k, v, cos, sin, out=o2, lse=l2, workspace=ws, phase="core")
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)   # deterministic: no atomics
+
+
+@pytest.mark.parametrize("n,Hq,Hkv,D", [(2000, 4, 1, 256),     # key-range split, merge
+                                         (3300, 16, 16, 64)])   # unsplit main kernel
+def test_attention_graph_replay(pe, n, Hq, Hkv, D):
+    """The forward recorded into a HIP graph (the library creates no streams or events and
+    enqueues only kernels) replays to the eager result. Between replays the inputs change
+    in place and eager work runs; every replay is compared with an eager call on the same
+    inputs, bit for bit (the forward has no atomics)."""
+    import torch
+    K, seed = 4, 41
+    cu = to_dev(np.array([0, n], dtype=np.int32))
+    sel = pe.cod_select(n, K, 0.7, 0.2, seed, cu)
+    T = sel["T"]
+    cos, sin = pe.rope_table(D, 1e4, pe.rope_max_pos(n, K))
+    qkv = [synth.qkv_inputs(seed + i, T, Hq, Hkv, D) for i in range(3)]
+    q, k, v = (to_dev(qkv[0][t]) for t in ("q", "k", "v"))
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pe.attn_workspace_bytes(n, T, Hq, Hkv, D), dtype=torch.uint8, device="cuda")
+    pe.draft_attn(n, K, sel, cu, q, k, v, cos, sin, out=out, lse=lse, workspace=ws)  # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pe.draft_attn(n, K, sel, cu, q, k, v, cos, sin, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for i in (0, 1, 2, 0):
+        print(f"graph replay n={n} inputs {i}", flush=True)
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            t.copy_(to_dev(qkv[i][name]))
+        ref_out, ref_lse, _ = pe.draft_attn(n, K, sel, cu, q, k, v, cos, sin)
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"replay {i}"
 
 
 # ---------------------------------------------------------------- verification

@@ -54,7 +54,7 @@
 // lane's 16 k-step reads share one base address. V^T tiles: rows of 32 keys (64 bytes),
 // 16-byte chunk index XOR ((d >> 2) & 3).
 #include <algorithm>
-#include <mutex>
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -118,8 +118,7 @@ struct AttnParams {
   float* part;    // [segment - 1][T][Hq][D]: unnormalised O of segments 1.. of split chunks
   float2* ml;     // [segment][Hq][T]: (reference max, sum) of each segment of split chunks
   int n, T, S, Hq, Hkv, G, QR, ntiles, exact_per_seq, max_chunks, nsplit;
-  int budget;  // work items that run at once beside the short chunks (one round)
-  int exact_r0;  // exact kernel: first row of its grid (0: short chunks, S*exact_per_seq: redo)
+  int budget;  // work items the split main kernel runs at once (one round)
   float c_log2;
 };
 
@@ -194,7 +193,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
   int chunk, seg = 0, nseg = 1;
   bool redo = false;
   if constexpr (EXACT) {
-    const int r = p.exact_r0 + bid / p.Hkv;
+    const int r = bid / p.Hkv;  // short chunks first, then every chunk (redo if flagged)
     const int n_short = p.S * p.exact_per_seq;
     if (r < n_short) {  // one of the first chunks of a sequence
       const int s = r / p.exact_per_seq, j = r % p.exact_per_seq;
@@ -705,41 +704,21 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   }
 }
 
-// Second stream per device for the short chunks, which do not depend on the main kernel:
-// they can overlap it instead of running after it. Default priority, created on first use;
-// the lock also keeps two concurrent calls from interleaving their fork and join events.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
 constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-SideStream g_side[kMaxDevices];
 
+// Compute units of the current device, cached per device (every thread that fills an
+// entry stores the same value, so relaxed atomics suffice).
 int device_cus() {
-  static int cus[kMaxDevices] = {0};
+  static std::atomic<int> cus[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  if (cus[dev] <= 0 &&
-      hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus[dev] = 256;
-  return cus[dev];
-}
-
-SideStream* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& s = g_side[dev];
-  if (s.stream == nullptr && !s.failed) {
-    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess) {
-      s.failed = true;  // run the short chunks on the caller's stream instead
-      (void)hipGetLastError();
-    }
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return s.failed ? nullptr : &s;
+  return c;
 }
 
 }  // namespace
@@ -778,28 +757,17 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p.exact_per_seq = attn_exact_chunks_per_seq(a.K, p.QR);
   p.max_chunks = L.max_chunks;
   p.c_log2 = a.scale * 1.4426950408889634f;
-  // Short chunks on the side stream, concurrently with the main kernel (and the work list
-  // and merge of a split); then the chunks the main kernel flagged, once both are done.
+  // The main kernel (or the split's work list, segments and merge), then one launch of the
+  // exact kernel for the short chunks and for the chunks the main kernel flagged. All on
+  // the caller's stream: the library keeps no streams or events of its own.
   // chunk count <= ceil(T / QR) + S (each sequence adds at most one partial chunk)
   const int chunk_bound = std::min(L.max_chunks, (a.T + p.QR - 1) / p.QR + a.S);
   const int n_short = a.S * p.exact_per_seq;
   const dim3 main_grid(chunk_bound * a.Hkv * p.nsplit);
   const dim3 combine_grid(chunk_bound * a.Hkv, kAttnSlots / 4);
-  const dim3 short_grid(n_short * a.Hkv), redo_grid(chunk_bound * a.Hkv);
-  AttnParams p_short = p, p_redo = p;
-  p_short.exact_r0 = 0;
-  p_redo.exact_r0 = n_short;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  // Overlap pays when the short chunks are a latency tail (a few workgroups per sequence)
-  // beside a main kernel long enough to hide them. With many packed sequences they are a
-  // sizeable share of the work, and under kOverlapMinKeys of context the whole call is
-  // short: there the fork and join (~10 us) cost more than running them in turn.
-  constexpr int kOverlapMinKeys = 2048;
-  SideStream* side = (n_short * a.Hkv <= device_cus() / 4 && a.n >= kOverlapMinKeys)
-                         ? side_stream() : nullptr;
+  const dim3 exact_grid((n_short + chunk_bound) * a.Hkv);
   if (p.nsplit > 1) {
-    // one round of the split main kernel: its resident workgroups over the chip, less the
-    // short chunks' workgroups that run beside it
+    // one round of the split main kernel: its resident workgroups over the chip
     int per_cu = 1;
     hipError_t eo = hipErrorInvalidValue;
 #define PEAGLE_OCC(DD)                                                                      \
@@ -814,20 +782,10 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
     }
 #undef PEAGLE_OCC
     if (eo != hipSuccess) per_cu = 1;
-    p.budget = std::max(1, std::max(1, per_cu) * device_cus() - n_short * a.Hkv);
+    p.budget = std::max(1, per_cu) * device_cus();
   }
-  hipStream_t short_stream = stream;
-  if (side != nullptr && hipEventRecord(side->fork, stream) == hipSuccess &&
-      hipStreamWaitEvent(side->stream, side->fork, 0) == hipSuccess)
-    short_stream = side->stream;
 #define PEAGLE_CORE(DD)                                                                       \
   do {                                                                                        \
-    hipLaunchKernelGGL((attn_core_kernel<DD, true, false>), short_grid,                       \
-                       dim3(Cfg<DD, kExactNT>::TH), 0, short_stream, p_short);                \
-    if (short_stream != stream) {                                                             \
-      const hipError_t ej = hipEventRecord(side->join, short_stream);                         \
-      if (ej != hipSuccess) return ej;                                                        \
-    }                                                                                         \
     if (p.nsplit > 1) {                                                                       \
       hipLaunchKernelGGL(attn_items_kernel, dim3(1), dim3(1024), 0, stream, p);               \
       hipLaunchKernelGGL((attn_core_kernel<DD, false, true>), main_grid,                      \
@@ -837,12 +795,8 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
       hipLaunchKernelGGL((attn_core_kernel<DD, false, false>), main_grid,                     \
                          dim3(Cfg<DD, kMainNT>::TH), 0, stream, p);                           \
     }                                                                                         \
-    if (short_stream != stream) {                                                             \
-      const hipError_t ew = hipStreamWaitEvent(stream, side->join, 0);                        \
-      if (ew != hipSuccess) return ew;                                                        \
-    }                                                                                         \
-    hipLaunchKernelGGL((attn_core_kernel<DD, true, false>), redo_grid,                        \
-                       dim3(Cfg<DD, kExactNT>::TH), 0, stream, p_redo);                       \
+    hipLaunchKernelGGL((attn_core_kernel<DD, true, false>), exact_grid,                       \
+                       dim3(Cfg<DD, kExactNT>::TH), 0, stream, p);                            \
   } while (0)
   switch (a.D) {
     case 64: PEAGLE_CORE(64); break;

@@ -341,9 +341,9 @@ def write_trace_summary(path: str, trace_dir: str, bench_log: str, title: str, c
         lines.append(f"| `{name}` | {len(d)} | {sum(d) / len(d) / 1e3:.1f} | {min(d) / 1e3:.1f} | "
                      f"{max(d) / 1e3:.1f} | {100 * sum(d) / total:.2f} |")
     core = [k for k in per if any(c in k for c in CORE_KERNELS)]
-    # A core call's launches sit between the step's other kernels in start order; the short
-    # chunks' launch runs on a second stream and overlaps the main kernel, so a call lasts
-    # from its first launch's start to its last launch's end.
+    # A core call's launches sit between the step's other kernels in start order; a call
+    # lasts from its first launch's start to its last launch's end (were any two of its
+    # launches to overlap, the span still counts the time once).
     seq = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short(r["Kernel_Name"]))
                  for r in rows)
     spans, cur = [], None
