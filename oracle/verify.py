@@ -23,8 +23,11 @@ drafter's token x_d (sampled from q, an input here) is accepted while u_d < p(x_
 for the given uniforms u_d; at the first rejected depth j the next token is drawn from
 the residual max(0, p_j - q_j) (normalised) by inverse CDF: the smallest t whose
 cumulative residual exceeds w * Z, Z the residual's total, w a given uniform. When all K
-depths are accepted the next token is -1 (its bonus draw needs a K+1-th target row, which
-this interface does not take).
+depths are accepted the next token is -1 in ``speculative_accept``. With a K+1-th target
+row (the target's distribution after the last drafted token, which the target's one
+verification pass also yields), ``speculative_accept_bonus`` draws that extra token from
+p_K = softmax(target row K / tau) by the same inverse CDF with w, so every draft then
+emits accept_len + 1 tokens.
 """
 from __future__ import annotations
 
@@ -105,3 +108,16 @@ def speculative_accept(draft_logits, target_logits, draft_tok, u, w, tau: float 
             c = np.cumsum(r)
             nxt[i] = int(np.searchsorted(c, w[i] * c[-1], side="right"))
     return dict(accept_len=accept, next_tok=nxt, ratio=ratio)
+
+
+def speculative_accept_bonus(draft_logits, target_logits, draft_tok, u, w, tau: float = 1.0) -> dict:
+    """As ``speculative_accept`` with target_logits [N, K + 1, V]: rows 0..K-1 verify the K
+    depths; when all K are accepted, next_tok is drawn from p_K = softmax(target row K / tau)
+    by inverse CDF: the smallest t with p_0 + .. + p_t > w * (p_0 + .. + p_{V-1})."""
+    N, K, V = draft_logits.shape
+    assert target_logits.shape == (N, K + 1, V), target_logits.shape
+    out = speculative_accept(draft_logits, target_logits[:, :K], draft_tok, u, w, tau)
+    for i in np.nonzero(out["accept_len"] == K)[0]:
+        c = np.cumsum(softmax_f64(target_logits[i, K], tau))
+        out["next_tok"][i] = int(np.searchsorted(c, w[i] * c[-1], side="right"))
+    return out

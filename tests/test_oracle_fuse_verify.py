@@ -207,6 +207,52 @@ def test_speculative_sampling_emits_the_target_distribution():
     assert (out["next_tok"][~rej] == -1).all()
 
 
+def test_speculative_bonus_draw_emits_the_next_target_distribution():
+    """With a K+1-th target row, a draft whose K tokens are all accepted emits one more token,
+    and that token is distributed as p_K = softmax(row K / tau): chi-square over the
+    accepted drafts of 60000 (99.99% quantile for 5 degrees of freedom ~25.7). Drafts with a
+    rejection keep the residual draw of the K-row interface."""
+    rng = np.random.default_rng(17)
+    V, tau, M, K = 6, 0.9, 60000, 1
+    dl, tl, _ = _spec_inputs(rng, 1, K + 1, V)        # depth rows 0 (draft) and 0, 1 (target)
+    q = verify.softmax_f64(dl[0, 0], tau)
+    p0 = verify.softmax_f64(tl[0, 0], tau)
+    pk = verify.softmax_f64(tl[0, 1], tau)
+    xs = rng.choice(V, size=M, p=q)
+    u, w = rng.random((M, 1)), rng.random(M)
+    out = verify.speculative_accept_bonus(np.repeat(dl[:, :1], M, 0), np.repeat(tl, M, 0),
+                                          xs[:, None], u, w, tau)
+    acc = out["accept_len"] == K
+    assert 0 < acc.sum() < M
+    counts = np.bincount(out["next_tok"][acc], minlength=V)
+    n_acc = int(acc.sum())
+    chi2 = float(np.sum((counts - n_acc * pk) ** 2 / (n_acc * pk)))
+    assert chi2 < 25.7, chi2
+    # acceptance itself follows p0 / q (the probability of accepting is sum_x min(p0, q))
+    assert abs(acc.mean() - np.minimum(p0, q).sum()) < 5 * np.sqrt(0.25 / M)
+    plain = verify.speculative_accept(np.repeat(dl[:, :1], M, 0), np.repeat(tl[:, :1], M, 0),
+                                      xs[:, None], u, w, tau)
+    assert np.array_equal(plain["accept_len"], out["accept_len"])
+    assert np.array_equal(plain["next_tok"][~acc], out["next_tok"][~acc])
+    assert (plain["next_tok"][acc] == -1).all()
+
+
+def test_speculative_bonus_point_mass():
+    """A bonus row with one dominant logit gives that token for every accepted draft."""
+    rng = np.random.default_rng(19)
+    N, K, V = 40, 3, 50
+    dl, tl, tok = _spec_inputs(rng, N, K + 1, V, plant=1.0)
+    dl = dl[:, :K]
+    tok = tok[:, :K]
+    tl = tl.copy()
+    tl[:, K, :] = _f32_to_bits(np.full(V, -30.0, np.float32))
+    tl[:, K, 7] = _f32_to_bits(np.array([30.0], np.float32))[0]
+    out = verify.speculative_accept_bonus(dl, tl, tok, np.zeros((N, K)), rng.random(N), 1.0)
+    acc = out["accept_len"] == K
+    assert acc.any()
+    assert (out["next_tok"][acc] == 7).all()
+
+
 def test_speculative_identical_distributions_accept_everything():
     rng = np.random.default_rng(12)
     dl, _, tok = _spec_inputs(rng, 20, 5, 40)
