@@ -80,11 +80,18 @@ int peagle_cod_counts(int64_t n, int32_t K, double r, double r_min, int64_t *m, 
  *   depth_off     int32[K+1] out   first draft row of each depth (prefix sum of m)
  *   cu_seqlens_d  int32[K*(S+1)] out  [d][s] = kept anchors of depth d below cu[s]
  *   row_of        int32[K*n] out   [d][p] = draft row of (d, p), or -1 if not kept
- * Requires n < 2^31 and T as given by peagle_cod_counts.
+ *   workspace     >= peagle_cod_workspace_bytes(n, K) bytes of device memory, 256-byte
+ *                 aligned (per-depth thresholds and per-block kept counts); its contents
+ *                 are scratch and need no initialisation
+ * Requires n < 2^31 and T as given by peagle_cod_counts. Work is O(n K): one workgroup
+ * hashes the buffer twice for the thresholds and once for per-block counts, then one
+ * workgroup per 1024 positions compacts its block.
  */
+size_t peagle_cod_workspace_bytes(int64_t n, int32_t K); /* 0 on bad arguments */
 int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
                       const int32_t *cu_seqlens, int32_t num_seqs, int32_t *idx,
-                      int32_t *depth_off, int32_t *cu_seqlens_d, int32_t *row_of, void *stream);
+                      int32_t *depth_off, int32_t *cu_seqlens_d, int32_t *row_of,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * peagle_fuse_inputs -- fused input stage [N, description; G, "Architecture"]. Depth 0
@@ -312,6 +319,22 @@ int peagle_accept_sampled(int32_t num_drafts, int32_t K, int32_t vocab,
                           const int32_t *draft_tok, const float *u, const float *w,
                           float temperature, int32_t *accept_len, int32_t *next_tok,
                           void *stream);
+
+/*
+ * peagle_accept_sampled_bonus -- peagle_accept_sampled with the bonus token [R, "How
+ * Speculative Decoding Works": the target verifies every drafted token in one pass, which
+ * also gives its distribution after the last one]. target_logits holds K + 1 rows per
+ * draft, bf16[N, K + 1, V]: rows 0 .. K-1 verify the K depths as in peagle_accept_sampled;
+ * when all K are accepted, next_tok[i] is drawn from p_K = softmax(target row K / tau): the
+ * smallest t whose running sum p_0 + .. + p_t exceeds w[i] * (p_0 + .. + p_{V-1}). Every
+ * draft thus yields accept_len[i] + 1 tokens and next_tok is never -1. Other arguments,
+ * arithmetic and limits as for peagle_accept_sampled.
+ */
+int peagle_accept_sampled_bonus(int32_t num_drafts, int32_t K, int32_t vocab,
+                                const peagle_bf16 *draft_logits, const peagle_bf16 *target_logits,
+                                const int32_t *draft_tok, const float *u, const float *w,
+                                float temperature, int32_t *accept_len, int32_t *next_tok,
+                                void *stream);
 
 /*
  * The first draft decoder layer's attention inputs [R, "How Speculative Decoding Works",

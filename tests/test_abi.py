@@ -71,8 +71,21 @@ def test_cod_argument_errors(lib):
                 (10, 4, 1.5, 0.2), (10, 4, 0.7, -0.1), (10, 4, 0.7, 1.1), (10, 4, float("nan"), 0.2)]:
         assert _code("peagle_cod_counts", *bad, None, C.byref(T)) == peagle.ERR_ARG
     # valid counts, NULL device pointers -> refused
-    assert _code("peagle_cod_select", 10, 4, 0.7, 0.2, 1, None, 1, None, None, None, None, None) == peagle.ERR_ARG
-    assert _code("peagle_cod_select", 10, 4, 0.7, 0.2, 1, None, 0, None, None, None, None, None) == peagle.ERR_ARG
+    assert _code("peagle_cod_select", 10, 4, 0.7, 0.2, 1, None, 1, None, None, None, None, None, 0,
+                 None) == peagle.ERR_ARG
+    assert _code("peagle_cod_select", 10, 4, 0.7, 0.2, 1, None, 0, None, None, None, None, None, 0,
+                 None) == peagle.ERR_ARG
+    # a workspace below peagle_cod_workspace_bytes is refused before any launch (the
+    # pointers are never dereferenced on this path)
+    fake = C.c_void_p(1 << 20)
+    need = peagle.cod_workspace_bytes(5000, 4)
+    assert need >= 64 * 8 + 5 * 4 * 4 and need % 256 == 0
+    assert _code("peagle_cod_select", 5000, 4, 0.7, 0.2, 1, fake, 1, fake, fake, fake, fake, fake,
+                 need - 1, None) == peagle.ERR_WORKSPACE
+    assert _code("peagle_cod_select", 5000, 4, 0.7, 0.2, 1, fake, 1, fake, fake, fake, fake,
+                 C.c_void_p((1 << 20) + 16), need, None) == peagle.ERR_ARG   # misaligned
+    assert peagle.cod_workspace_bytes(0, 4) == 0 and peagle.cod_workspace_bytes(10, 65) == 0
+
 
 
 def test_fuse_argument_errors(lib):

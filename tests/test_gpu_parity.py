@@ -47,6 +47,9 @@ COD_CASES = [
     (4, 3, 0.1, 0.0, 3, None),                       # empty depths
     (777, 3, 1.0, 0.2, 12, [100] * 7 + [77]),         # r = 1 keeps everything
     (100000, 6, 0.8, 0.05, 77, [30000, 30000, 40000]),
+    # 2^22 positions: 1024 hashes per 12-bit bin on average, so the threshold search takes
+    # its radix-select fallback for bins past 1024 candidates
+    (1 << 22, 4, 0.7, 0.2, 99, [1 << 21, (1 << 21) - 5, 5]),
 ]
 
 
@@ -72,12 +75,17 @@ def test_cod_select_bit_exact(pe, case):
 
 
 def test_cod_select_repeatable(pe):
+    """Two calls agree bit for bit, the second on a workspace and outputs full of 0xFF bytes
+    (the workspace needs no initialisation)."""
     import torch
     cu = to_dev(np.array([0, 4096], dtype=np.int32))
     a = pe.cod_select(4096, 4, 0.7, 0.2, 5, cu)
-    b = pe.cod_select(4096, 4, 0.7, 0.2, 5, cu)
-    for key in ("idx", "row_of"):
-        assert torch.equal(a[key], b[key])
+    b = {k: (v.fill_(-1) if isinstance(v, torch.Tensor) and v.dtype == torch.int32 else v)
+         for k, v in pe.cod_select(4096, 4, 0.7, 0.2, 5, cu).items()}
+    b["workspace"].fill_(255)
+    pe.cod_select_into(4096, 4, 0.7, 0.2, 5, cu, b)
+    for key in ("idx", "depth_off", "cu_seqlens_d", "row_of"):
+        assert torch.equal(a[key], b[key]), key
 
 
 # ---------------------------------------------------------------- fuse

@@ -124,15 +124,23 @@ int peagle_cod_counts(int64_t n, int32_t K, double r, double r_min, int64_t* m, 
   return counts(n, K, r, r_min, m, T);
 }
 
-int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
-                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t* idx,
-                      int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of, void* stream) {
+size_t peagle_cod_workspace_bytes(int64_t n, int32_t K) {
+  if (n < 1 || n > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return 0;
+  return cod_workspace_bytes(n, K);
+}
+
+static int cod_select_entry(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
+                            const int32_t* cu_seqlens, int32_t num_seqs, int32_t* idx,
+                            int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   int64_t m[PEAGLE_MAX_DEPTHS], T = 0;
   const int st = counts(n, K, r, r_min, m, &T);
   if (st != PEAGLE_OK) return st;
   if (T > kMaxI32 || (int64_t)K * n > ((int64_t)1 << 40)) return PEAGLE_ERR_ARG;
   if (num_seqs < 1 || num_seqs > n) return PEAGLE_ERR_ARG;
   if (!cu_seqlens || !idx || !depth_off || !cu_seqlens_d || !row_of) return PEAGLE_ERR_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PEAGLE_ERR_ARG;
+  if (workspace_bytes < cod_workspace_bytes(n, K)) return PEAGLE_ERR_WORKSPACE;
   CodArgs a{};
   a.n = (int32_t)n;
   a.K = K;
@@ -144,8 +152,17 @@ int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t see
     a.off[d + 1] = a.off[d] + (int32_t)m[d];
   }
   return status_of(launch_cod_select(a, cu_seqlens, idx, depth_off, cu_seqlens_d, row_of,
-                                     static_cast<hipStream_t>(stream)));
+                                     workspace, static_cast<hipStream_t>(stream)));
 }
+
+int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
+                      const int32_t* cu_seqlens, int32_t num_seqs, int32_t* idx,
+                      int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return cod_select_entry(n, K, r, r_min, seed, cu_seqlens, num_seqs, idx, depth_off,
+                          cu_seqlens_d, row_of, workspace, workspace_bytes, stream);
+}
+
 
 int peagle_fuse_inputs(int64_t n, int32_t K, int64_t T, const int32_t* idx,
                        const peagle_bf16* aux, int32_t aux_dim, const peagle_bf16* fc_weight,
@@ -614,19 +631,37 @@ int peagle_accept_prefix_d2t(int32_t num_drafts, int32_t K, int32_t draft_vocab,
                                      static_cast<hipStream_t>(stream)));
 }
 
-int peagle_accept_sampled(int32_t num_drafts, int32_t K, int32_t vocab,
-                          const peagle_bf16* draft_logits, const peagle_bf16* target_logits,
-                          const int32_t* draft_tok, const float* u, const float* w,
-                          float temperature, int32_t* accept_len, int32_t* next_tok,
-                          void* stream) {
+static int accept_sampled_entry(int32_t num_drafts, int32_t K, int32_t vocab,
+                                const peagle_bf16* draft_logits, const peagle_bf16* target_logits,
+                                const int32_t* draft_tok, const float* u, const float* w,
+                                float temperature, bool bonus, int32_t* accept_len,
+                                int32_t* next_tok, void* stream) {
   if (num_drafts < 0 || K < 1 || K > PEAGLE_MAX_DEPTHS || vocab < 1) return PEAGLE_ERR_ARG;
   if (!(temperature > 0.f) || !std::isfinite(temperature)) return PEAGLE_ERR_ARG;
   if (num_drafts == 0) return PEAGLE_OK;  // nothing is read: empty tensors may be null
   if (!draft_logits || !target_logits || !draft_tok || !u || !w || !accept_len || !next_tok)
     return PEAGLE_ERR_ARG;
   return status_of(launch_accept_sampled(num_drafts, K, vocab, draft_logits, target_logits,
-                                         draft_tok, u, w, temperature, accept_len, next_tok,
-                                         static_cast<hipStream_t>(stream)));
+                                         draft_tok, u, w, temperature, bonus, accept_len,
+                                         next_tok, static_cast<hipStream_t>(stream)));
+}
+
+int peagle_accept_sampled(int32_t num_drafts, int32_t K, int32_t vocab,
+                          const peagle_bf16* draft_logits, const peagle_bf16* target_logits,
+                          const int32_t* draft_tok, const float* u, const float* w,
+                          float temperature, int32_t* accept_len, int32_t* next_tok,
+                          void* stream) {
+  return accept_sampled_entry(num_drafts, K, vocab, draft_logits, target_logits, draft_tok, u, w,
+                              temperature, false, accept_len, next_tok, stream);
+}
+
+int peagle_accept_sampled_bonus(int32_t num_drafts, int32_t K, int32_t vocab,
+                                const peagle_bf16* draft_logits, const peagle_bf16* target_logits,
+                                const int32_t* draft_tok, const float* u, const float* w,
+                                float temperature, int32_t* accept_len, int32_t* next_tok,
+                                void* stream) {
+  return accept_sampled_entry(num_drafts, K, vocab, draft_logits, target_logits, draft_tok, u, w,
+                              temperature, true, accept_len, next_tok, stream);
 }
 
 }  // extern "C"

@@ -8,15 +8,19 @@
 // The hash is a bijection, so the m_d-th smallest hash is a unique threshold and depth d
 // keeps exactly the p with hash <= threshold.
 //
-// One workgroup of 1024 threads per block of 1024 positions. The thresholds are cheap
-// (a few passes of hashing over n), so every workgroup derives them itself and no
-// workgroup waits on another:
-//   1. a 12-bit histogram of the hashes locates, for every depth, the bin that holds the
-//      m_d-th smallest hash; the handful of hashes in that bin are ranked directly (an
-//      8-bit radix select is the fallback for a bin with more than 1024 hashes);
-//   2. the workgroup counts the kept positions of every depth before its block;
-//   3. ordered compaction of its own block with wave ballots (coalesced idx / row_of);
-//   4. cu_seqlens_d for the sequence starts inside its block.
+// Two launches, each hash computed where it is needed (re-hashing is cheaper than
+// storing 8 bytes per position):
+//   cod_threshold_kernel (one workgroup of 1024 threads, O(n)):
+//     1. a 12-bit histogram of all n hashes locates, for every depth, the bin that holds
+//        the m_d-th smallest hash; the handful of hashes in that bin (n / 4096 on
+//        average) are ranked directly (an 8-bit radix select is the fallback for a bin
+//        with more than 1024 hashes);
+//     2. one more pass counts, for every 1024-position block, the positions each depth
+//        keeps there, and writes the exclusive prefix of those counts over the blocks;
+//     thresholds and prefixes go to the caller's workspace.
+//   cod_compact_kernel (one workgroup per block of 1024 positions):
+//     3. ordered compaction of its block with wave ballots (coalesced idx / row_of);
+//     4. cu_seqlens_d for the sequence starts inside its block.
 #include "common.h"
 #include "kernels.h"
 
@@ -88,18 +92,26 @@ __device__ uint64_t radix_select(const CodArgs& a, int rank, uint32_t* hist, uin
   return prefix;
 }
 
-__global__ __launch_bounds__(kThreads) void cod_select_kernel(
-    CodArgs a, const int32_t* __restrict__ cu, int32_t* __restrict__ idx,
-    int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
-  constexpr int kBinBits = 12, kBins = 1 << kBinBits, kPerThread = kBins / kThreads;
-  constexpr int kCand = 1024;
+constexpr int kBinBits = 12, kBins = 1 << kBinBits;
+constexpr int kCand = 1024;    // candidate hashes held at once (all depths together)
+constexpr int kCache = 32768;  // positions whose hash's top 32 bits stay in LDS
+
+// Depth d needs its own threshold search: it keeps some but not all positions, and not the
+// same number as depth d - 1 (equal counts give equal thresholds).
+__device__ __forceinline__ bool own_search(const CodArgs& a, int d) {
+  const int m = a.m[d];
+  return m > 0 && m < a.n && (d == 0 || a.m[d - 1] != m);
+}
+
+__global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
+    CodArgs a, uint64_t* __restrict__ thr_out, int32_t* __restrict__ before_out) {
+  constexpr int kPerThread = kBins / kThreads;
   __shared__ uint32_t hist[kBins];
   __shared__ uint64_t cand[kCand];
+  __shared__ uint32_t hcache[kCache];
   __shared__ uint64_t thr[kMaxDepths];
   __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths];
-  __shared__ uint64_t wmask[kMaxDepths][kWaves];
-  __shared__ int32_t wsum[8][kWaves];
-  __shared__ int32_t before_blk[kMaxDepths];
+  __shared__ int32_t cbase[kMaxDepths + 1], cfill[kMaxDepths];
   __shared__ int32_t sh[kWaves];
   __shared__ uint64_t s_prefix;
   __shared__ int32_t s_rank, s_count;
@@ -108,15 +120,23 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int n = a.n, K = a.K;
+  const int ncache = min(n, kCache);
+  auto hash_of = [&](int p) { return splitmix64(a.seed ^ (uint64_t)p); };
+  auto top32 = [&](int p) -> uint32_t {
+    return p < ncache ? hcache[p] : (uint32_t)(hash_of(p) >> 32);
+  };
 
   // 1. thresholds: keep p at depth d iff hash(p) <= thr[d] (m_d == 0 keeps nothing).
   //    One histogram of the top 12 hash bits serves every depth: its prefix sums give the
-  //    bin holding the m_d-th smallest hash and the rank inside that bin; the bin's few
-  //    hashes (n / 4096 on average) are then ranked directly.
+  //    bin holding the m_d-th smallest hash and the rank inside that bin. The top 32 bits
+  //    of the first kCache hashes stay in LDS for the later passes.
   for (int b = tid; b < kBins; b += kThreads) hist[b] = 0;
   __syncthreads();
-  for (int p = tid; p < n; p += kThreads)
-    atomicAdd(&hist[splitmix64(a.seed ^ (uint64_t)p) >> (64 - kBinBits)], 1u);
+  for (int p = tid; p < n; p += kThreads) {
+    const uint64_t h = hash_of(p);
+    if (p < ncache) hcache[p] = (uint32_t)(h >> 32);
+    atomicAdd(&hist[h >> (64 - kBinBits)], 1u);
+  }
   __syncthreads();
   {
     uint32_t mine[kPerThread];
@@ -142,75 +162,119 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
     }
   }
   __syncthreads();
-  for (int d = 0; d < K; ++d) {
-    const int m = a.m[d];
-    if (m >= n || m == 0) {
-      if (tid == 0) thr[d] = ~0ull;
-      continue;
+  // candidate regions of the depths with their own search, one pool for all of them
+  if (tid == 0) {
+    int c = 0;
+    for (int d = 0; d < K; ++d) {
+      cbase[d] = c;
+      cfill[d] = 0;
+      if (own_search(a, d)) c += (int)hist[bin_of[d]];
     }
-    if (d > 0 && a.m[d - 1] == m) {  // same count, same threshold
-      if (tid == 0) thr[d] = thr[d - 1];
-      continue;
-    }
-    const uint32_t b = (uint32_t)bin_of[d];
-    if (hist[b] > (uint32_t)kCand) {  // pathological bin: full radix select
-      const uint64_t t = radix_select(a, m, hist + 0, &s_prefix, &s_rank);
-      if (tid == 0) thr[d] = t;
-      __syncthreads();
-      // the histogram was overwritten: rebuild it for the depths still to come
-      for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
-      __syncthreads();
-      for (int p = tid; p < n; p += kThreads)
-        atomicAdd(&hist[splitmix64(a.seed ^ (uint64_t)p) >> (64 - kBinBits)], 1u);
-      __syncthreads();
-      continue;
-    }
-    if (tid == 0) s_count = 0;
-    __syncthreads();
-    for (int p = tid; p < n; p += kThreads) {
-      const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
-      if ((h >> (64 - kBinBits)) == b) cand[atomicAdd(&s_count, 1)] = h;
-    }
-    __syncthreads();
-    const int c = s_count, want = rank_in_bin[d] - 1;
-    for (int i = tid; i < c; i += kThreads) {
-      const uint64_t h = cand[i];
-      int smaller = 0;
-      for (int j = 0; j < c; ++j) smaller += cand[j] < h;
-      if (smaller == want) thr[d] = h;  // hashes are distinct: exactly one writer
-    }
-    __syncthreads();
+    cbase[K] = c;
   }
   __syncthreads();
-
-  // 2. kept positions of every depth before this workgroup's block: one pass over
-  //    [0, base), eight depths per pass, reduced over the workgroup.
-  const int base = blockIdx.x * kThreads;
-  for (int d0 = 0; d0 < K; d0 += 8) {
-    int c[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) c[j] = 0;
-    for (int p = tid; p < base; p += kThreads) {
-      const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (d0 + j < K) c[j] += (a.m[d0 + j] > 0 && h <= thr[d0 + j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int v = c[j];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-      if (lane == 0) wsum[j][wave] = v;
+  if (cbase[K] <= kCand) {
+    // one pass gathers every depth's candidates, then each candidate ranks itself inside
+    // its depth's region (the region's hashes are distinct: exactly one has the rank)
+    for (int p = tid; p < n; p += kThreads) {
+      const int t = (int)(top32(p) >> (32 - kBinBits));
+      for (int d = 0; d < K; ++d)
+        if (own_search(a, d) && t == bin_of[d]) cand[cbase[d] + atomicAdd(&cfill[d], 1)] = hash_of(p);
     }
     __syncthreads();
-    if (tid < 8 && d0 + tid < K) {
-      int v = 0;
-      for (int w = 0; w < kWaves; ++w) v += wsum[tid][w];
-      before_blk[d0 + tid] = v;
+    for (int i = tid; i < cbase[K]; i += kThreads) {
+      int d = 0;
+      while (cbase[d + 1] <= i) ++d;
+      const uint64_t h = cand[i];
+      int smaller = 0;
+      for (int j = cbase[d]; j < cbase[d + 1]; ++j) smaller += cand[j] < h;
+      if (smaller == rank_in_bin[d] - 1) thr[d] = h;
     }
     __syncthreads();
+  } else {
+    // depth by depth: the bin's hashes ranked directly, or a radix select for a bin with
+    // more than kCand hashes
+    for (int d = 0; d < K; ++d) {
+      if (!own_search(a, d)) continue;
+      const uint32_t b = (uint32_t)bin_of[d];
+      if (hist[b] > (uint32_t)kCand) {
+        const uint64_t t = radix_select(a, a.m[d], reinterpret_cast<uint32_t*>(cand), &s_prefix, &s_rank);
+        if (tid == 0) thr[d] = t;
+        __syncthreads();
+        continue;
+      }
+      if (tid == 0) s_count = 0;
+      __syncthreads();
+      for (int p = tid; p < n; p += kThreads)
+        if ((top32(p) >> (32 - kBinBits)) == b) cand[atomicAdd(&s_count, 1)] = hash_of(p);
+      __syncthreads();
+      const int c = s_count, want = rank_in_bin[d] - 1;
+      for (int i = tid; i < c; i += kThreads) {
+        const uint64_t h = cand[i];
+        int smaller = 0;
+        for (int j = 0; j < c; ++j) smaller += cand[j] < h;
+        if (smaller == want) thr[d] = h;
+      }
+      __syncthreads();
+    }
   }
+  if (tid == 0)
+    for (int d = 0; d < K; ++d)
+      if (!own_search(a, d)) thr[d] = (a.m[d] >= n || a.m[d] == 0 || d == 0) ? ~0ull : thr[d - 1];
+  __syncthreads();
+
+  // 2. kept positions of every depth in each block of kThreads positions: a wave per
+  //    block, one ballot per depth and 64 positions; lane d carries depth d's count. The
+  //    full hash is needed only where the top 32 bits tie a threshold's.
+  const int nb = (n + kThreads - 1) / kThreads;
+  for (int b = wave; b < nb; b += kWaves) {
+    int c = 0;
+    for (int j = 0; j < kThreads; j += kWave) {
+      const int p = b * kThreads + j + lane;
+      const bool inside = p < n;
+      const uint32_t t = inside ? top32(p) : 0u;
+      for (int d = 0; d < K; ++d) {
+        const uint32_t th = (uint32_t)(thr[d] >> 32);
+        const bool keep = inside && a.m[d] > 0 && (t < th || (t == th && hash_of(p) <= thr[d]));
+        const uint64_t ball = __ballot(keep);
+        if (lane == d) c += __popcll(ball);
+      }
+    }
+    if (lane < K) before_out[(size_t)b * K + lane] = c;
+  }
+  __syncthreads();
+  // exclusive prefix over the blocks, per depth, in place
+  for (int d = 0; d < K; ++d) {
+    int carry = 0;
+    for (int b0 = 0; b0 < nb; b0 += kThreads) {
+      const int b = b0 + tid;
+      const int v = b < nb ? before_out[(size_t)b * K + d] : 0;
+      int total;
+      const int ex = block_scan_excl(v, sh, &total);
+      if (b < nb) before_out[(size_t)b * K + d] = carry + ex;
+      carry += total;
+    }
+  }
+  if (tid < K) thr_out[tid] = thr[tid];
+}
+
+__global__ __launch_bounds__(kThreads) void cod_compact_kernel(
+    CodArgs a, const int32_t* __restrict__ cu, const uint64_t* __restrict__ thr_in,
+    const int32_t* __restrict__ before_in, int32_t* __restrict__ idx,
+    int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
+  __shared__ uint64_t thr[kMaxDepths];
+  __shared__ uint64_t wmask[kMaxDepths][kWaves];
+  __shared__ int32_t before_blk[kMaxDepths];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n = a.n, K = a.K;
+  const int base = blockIdx.x * kThreads;
+  if (tid < K) {
+    thr[tid] = thr_in[tid];
+    before_blk[tid] = before_in[(size_t)blockIdx.x * K + tid];
+  }
+  __syncthreads();
 
   // 3. ordered compaction of the block [base, base + 1024): a wave ballot per depth gives
   //    each lane its rank inside the wave, the wave masks in LDS give the rank inside
@@ -258,11 +322,21 @@ __global__ __launch_bounds__(kThreads) void cod_select_kernel(
 
 }  // namespace
 
+// Workspace: the kMaxDepths thresholds, then the [blocks][K] exclusive prefixes.
+size_t cod_workspace_bytes(int64_t n, int32_t K) {
+  const size_t nb = (size_t)((n + kThreads - 1) / kThreads);
+  const size_t bytes = (size_t)kMaxDepths * sizeof(uint64_t) + nb * (size_t)K * sizeof(int32_t);
+  return (bytes + 255) & ~(size_t)255;
+}
+
 hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_t* idx,
                              int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL(cod_select_kernel, dim3((a.n + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, a, cu_seqlens, idx, depth_off, cu_seqlens_d, row_of);
+                             void* workspace, hipStream_t stream) {
+  uint64_t* thr = static_cast<uint64_t*>(workspace);
+  int32_t* before = reinterpret_cast<int32_t*>(thr + kMaxDepths);
+  hipLaunchKernelGGL(cod_threshold_kernel, dim3(1), dim3(kThreads), 0, stream, a, thr, before);
+  hipLaunchKernelGGL(cod_compact_kernel, dim3((a.n + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     stream, a, cu_seqlens, thr, before, idx, depth_off, cu_seqlens_d, row_of);
   return hipGetLastError();
 }
 

@@ -17,9 +17,11 @@ struct CodArgs {
   int32_t off[kMaxDepths + 1];
 };
 
+size_t cod_workspace_bytes(int64_t n, int32_t K);
+
 hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_t* idx,
                              int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
-                             hipStream_t stream);
+                             void* workspace, hipStream_t stream);
 
 struct FuseArgs {
   int32_t n, T, aux_dim, H, vocab, ptd;

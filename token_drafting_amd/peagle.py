@@ -30,7 +30,9 @@ SIGNATURES = {
     "peagle_status_string": ([_i32], C.c_char_p),
     "peagle_version": ([], _i32),
     "peagle_cod_counts": ([_i64, _i32, _f64, _f64, _p, _p], _i32),
-    "peagle_cod_select": ([_i64, _i32, _f64, _f64, _u64, _p, _i32, _p, _p, _p, _p, _p], _i32),
+    "peagle_cod_workspace_bytes": ([_i64, _i32], _sz),
+    "peagle_cod_select": ([_i64, _i32, _f64, _f64, _u64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p],
+                          _i32),
     "peagle_fuse_inputs": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32, _i32,
                             _p, _p, _p], _i32),
     "peagle_rope_table": ([_i32, _f64, _i32, _p, _p, _p], _i32),
@@ -63,6 +65,8 @@ SIGNATURES = {
                                     _i32, _p, _f32, _p, _p, _p], _i32),
     "peagle_accept_prefix_d2t": ([_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p], _i32),
     "peagle_accept_sampled": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _f32, _p, _p, _p], _i32),
+    "peagle_accept_sampled_bonus": ([_i32, _i32, _i32, _p, _p, _p, _p, _p, _f32, _p, _p, _p],
+                                    _i32),
     "peagle_decode_v_tiles_bytes": ([_i64, _i32, _i32, _i32], _sz),
     "peagle_decode_pack_v": ([_i32, _p, _i64, _i32, _p, _i32, _i32, _p, _sz, _p], _i32),
     "peagle_draft_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i64, _i32], _sz),
@@ -129,8 +133,12 @@ def cod_counts(n: int, K: int, r: float, r_min: float) -> tuple[list, int]:
     return list(m), T.value
 
 
+def cod_workspace_bytes(n: int, K: int) -> int:
+    return int(lib().peagle_cod_workspace_bytes(n, K))
+
+
 def cod_select(n: int, K: int, r: float, r_min: float, seed: int, cu_seqlens: torch.Tensor):
-    """Returns dict(m, T, idx, depth_off, cu_seqlens_d [K,S+1], row_of [K,n])."""
+    """Returns dict(m, T, idx, depth_off, cu_seqlens_d [K,S+1], row_of [K,n], workspace)."""
     _dev(cu_seqlens, "cu_seqlens")
     m, T = cod_counts(n, K, r, r_min)
     S = cu_seqlens.numel() - 1
@@ -139,16 +147,20 @@ def cod_select(n: int, K: int, r: float, r_min: float, seed: int, cu_seqlens: to
                idx=torch.empty(T, dtype=torch.int32, device=dev),
                depth_off=torch.empty(K + 1, dtype=torch.int32, device=dev),
                cu_seqlens_d=torch.empty((K, S + 1), dtype=torch.int32, device=dev),
-               row_of=torch.empty((K, n), dtype=torch.int32, device=dev))
+               row_of=torch.empty((K, n), dtype=torch.int32, device=dev),
+               workspace=torch.empty(cod_workspace_bytes(n, K), dtype=torch.uint8, device=dev))
     cod_select_into(n, K, r, r_min, seed, cu_seqlens, out)
     return out
 
 
 def cod_select_into(n, K, r, r_min, seed, cu_seqlens, out):
+    """Writes idx, depth_off, cu_seqlens_d and row_of of ``out`` (using its workspace)."""
     S = cu_seqlens.numel() - 1
+    ws = out["workspace"]
     _check("peagle_cod_select", lib().peagle_cod_select(
         n, K, r, r_min, seed & ((1 << 64) - 1), _ptr(cu_seqlens), S, _ptr(out["idx"]),
-        _ptr(out["depth_off"]), _ptr(out["cu_seqlens_d"]), _ptr(out["row_of"]), _stream()))
+        _ptr(out["depth_off"]), _ptr(out["cu_seqlens_d"]), _ptr(out["row_of"]), _ptr(ws),
+        ws.numel(), _stream()))
 
 
 # ---------------------------------------------------------------- fuse
@@ -322,21 +334,25 @@ def accept_prefix_d2t(draft_logits, target_logits, d2t, draft_tok=None, target_t
 def accept_sampled(draft_logits, target_logits, draft_tok, u, w, temperature=1.0,
                    accept_len=None, next_tok=None):
     """Speculative-sampling verification of sampled drafts: accept_len [N] and the token
-    drawn from the residual at the first rejected depth (next_tok [N], -1 when all K are
-    accepted). draft_tok int32 [N, K]; u fp32 [N, K] and w fp32 [N] uniforms in [0, 1)."""
+    drawn from the residual at the first rejected depth (next_tok [N]). draft_tok int32
+    [N, K]; u fp32 [N, K] and w fp32 [N] uniforms in [0, 1). target_logits [N, K, V]: all K
+    accepted gives next_tok -1; [N, K + 1, V]: row K is the bonus distribution, drawn from
+    when all K are accepted."""
     for t, name in ((draft_logits, "draft_logits"), (target_logits, "target_logits"),
                     (draft_tok, "draft_tok"), (u, "u"), (w, "w")):
         _dev(t, name)
     N, K, V = draft_logits.shape
-    if tuple(target_logits.shape) != (N, K, V) or tuple(draft_tok.shape) != (N, K) \
-            or tuple(u.shape) != (N, K) or tuple(w.shape) != (N,):
+    bonus = tuple(target_logits.shape) == (N, K + 1, V)
+    if not (bonus or tuple(target_logits.shape) == (N, K, V)) or \
+            tuple(draft_tok.shape) != (N, K) or tuple(u.shape) != (N, K) or tuple(w.shape) != (N,):
         raise ValueError("accept_sampled: shapes do not match [N, K, V] logits")
     dev = draft_logits.device
     if accept_len is None:
         accept_len = torch.empty(N, dtype=torch.int32, device=dev)
     if next_tok is None:
         next_tok = torch.empty(N, dtype=torch.int32, device=dev)
-    _check("peagle_accept_sampled", lib().peagle_accept_sampled(
+    fn = "peagle_accept_sampled_bonus" if bonus else "peagle_accept_sampled"
+    _check(fn, getattr(lib(), fn)(
         N, K, V, _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tok), _ptr(u), _ptr(w),
         float(temperature), _ptr(accept_len), _ptr(next_tok), _stream()))
     return accept_len, next_tok
