@@ -127,7 +127,7 @@ SPEC_CDF_TOL = 1e-5
 def check_sampled(inp: dict, tau: float, got_len, got_next, ratio_tol=SPEC_RATIO_TOL,
                   cdf_tol=SPEC_CDF_TOL, drafts=None) -> dict:
     """Check accept_len / next_tok of sampling verification against the float64 oracle on
-    the drafts listed (all by default). Exact wherever the oracle's decisions are clear of
+    the drafts listed (all by default); target logits with K + 1 rows check the bonus draw. Exact wherever the oracle's decisions are clear of
     the windows above; elsewhere the kernel's decisions must lie inside them. Returns
     counts and the largest miss of each kind (0 for a decision the oracle shares)."""
     from oracle import verify as over
@@ -137,7 +137,9 @@ def check_sampled(inp: dict, tau: float, got_len, got_next, ratio_tol=SPEC_RATIO
     N, K, V = dl.shape
     drafts = range(N) if drafts is None else drafts
     sub = [int(i) for i in drafts]
-    want = over.speculative_accept(dl[sub], tl[sub], tok[sub], u[sub], w[sub], tau)
+    bonus = tl.shape[1] == K + 1
+    want = (over.speculative_accept_bonus if bonus else over.speculative_accept)(
+        dl[sub], tl[sub], tok[sub], u[sub], w[sub], tau)
     stats = dict(drafts=len(sub), exact=0, ratio_miss=0.0, cdf_miss=0.0, rejected=0)
     for j, i in enumerate(sub):
         L, t = int(got_len[i]), int(got_next[i])
@@ -147,8 +149,17 @@ def check_sampled(inp: dict, tau: float, got_len, got_next, ratio_tol=SPEC_RATIO
             miss = max(0.0, u[i, d] - ratio[d]) / max(ratio[d], 1e-300)
             stats["ratio_miss"] = max(stats["ratio_miss"], miss)
             assert miss <= ratio_tol, f"draft {i} depth {d}: accepted with u {u[i, d]} >= ratio {ratio[d]}"
-        if L == K:
+        if L == K and tl.shape[1] == K:
             assert t == -1, f"draft {i}: all {K} accepted but next_tok {t}"
+        elif L == K:   # bonus draw from p_K, the target's K+1-th row
+            assert 0 <= t < V, f"draft {i}: bonus token {t} outside [0, {V})"
+            c = np.cumsum(over.softmax_f64(tl[i, K], tau))
+            theta = w[i] * c[-1]
+            lo = c[t - 1] if t > 0 else 0.0
+            miss = max(0.0, lo - theta, theta - c[t] if c[t] <= theta else 0.0)
+            stats["cdf_miss"] = max(stats["cdf_miss"], miss)
+            assert miss <= cdf_tol, (f"draft {i}: bonus token {t} spans "
+                                     f"[{lo:.9g}, {c[t]:.9g}) but w*Z = {theta:.9g}")
         else:
             stats["rejected"] += 1
             miss = max(0.0, ratio[L] - u[i, L]) / max(ratio[L], 1e-300)

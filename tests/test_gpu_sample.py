@@ -53,6 +53,41 @@ def test_sampled_small_full(pe, case):
     assert st["exact"] >= int(0.9 * N), st
 
 
+BONUS = [(64, 8, 32000, 1.0), (48, 4, 1000, 0.7), (37, 5, 1001, 1.3), (20, 1, 8, 1.0)]
+
+
+@pytest.mark.parametrize("case", BONUS, ids=[f"N{c[0]}K{c[1]}V{c[2]}t{c[3]}" for c in BONUS])
+def test_sampled_bonus_small_full(pe, case):
+    """A K+1-th target row: drafts with all K accepted draw the bonus token from it; the
+    others are unchanged from the K-row call."""
+    N, K, V, tau = case
+    print(f"accept_sampled bonus N={N} K={K} V={V} tau={tau}", flush=True)
+    inp = synth.with_bonus_row(synth.sampled_verify_inputs(29 + K, N, K, V), 29 + K)
+    alen, nxt = _run(pe, inp, tau)
+    assert (nxt >= 0).all() and (nxt < V).all()
+    st = check_sampled(inp, tau, alen, nxt)
+    print(st, flush=True)
+    assert st["exact"] >= int(0.9 * N), st
+    plain = dict(inp, target_logits=np.ascontiguousarray(inp["target_logits"][:, :K]))
+    alen0, nxt0 = _run(pe, plain, tau)
+    assert np.array_equal(alen0, alen)
+    assert np.array_equal(nxt0[alen < K], nxt[alen < K]) and (nxt0[alen == K] == -1).all()
+    if K <= 4:
+        assert (alen == K).any()
+
+
+def test_sampled_bonus_identical_rows(pe):
+    """p == q accepts all K depths, so every draft draws its bonus token."""
+    N, K, V = 32, 8, 4096
+    inp = synth.sampled_verify_inputs(3, N, K, V)
+    inp["target_logits"] = inp["draft_logits"].copy()
+    inp = synth.with_bonus_row(inp, 3)
+    alen, nxt = _run(pe, inp, 1.0)
+    assert (alen == K).all()
+    st = check_sampled(inp, 1.0, alen, nxt)
+    assert st["exact"] >= int(0.9 * N), st
+
+
 def test_sampled_identical_rows_accept_all(pe):
     """p == q: every ratio is 1 (fp32 included, both rows being the same bits), u < 1
     accepts all depths and no token is drawn."""

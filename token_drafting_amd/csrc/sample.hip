@@ -5,7 +5,9 @@
 // logits / tau) and q = softmax(draft logits / tau) at each depth, the drafter's token x_d
 // is accepted while u_d < p(x_d) / q(x_d); at the first rejected depth j the next token is
 // the smallest t whose cumulative residual max(0, p_j - q_j) exceeds w * Z (Z the
-// residual's total). All K accepted: the next token is -1.
+// residual's total). All K accepted: the next token is -1, or, given a K+1-th target row
+// (kBonus), the bonus token drawn from p_K = softmax(target row K / tau) by the same
+// inverse CDF with w.
 //
 // One workgroup (4 waves) per draft; the logits are read as chunks of 8 consecutive
 // tokens a lane (16-byte loads when V % 8 == 0):
@@ -90,34 +92,45 @@ __device__ __forceinline__ void row_stats(const uint16_t* row, int V, float inv_
   }
 }
 
-// Residual weights max(0, p_t - q_t) of tokens j .. j+7 (0 past `end`).
+// Residual weights max(0, p_t - q_t) of tokens j .. j+7 (0 past `end`); with drow == NULL
+// (the bonus row) the weights are p_t alone.
 template <bool kVec>
 __device__ __forceinline__ void resid_chunk(const uint16_t* trow, const uint16_t* drow, int j,
                                             int end, float inv_tau, float mp, float isp,
                                             float mq, float isq, float (&r)[kChunk]) {
-  float xt[kChunk], xd[kChunk];
+  float xt[kChunk];
   load_chunk<kVec>(trow, j, end, inv_tau, xt);
+  if (drow == nullptr) {
+#pragma unroll
+    for (int e = 0; e < kChunk; ++e) r[e] = __expf(xt[e] - mp) * isp;
+    return;
+  }
+  float xd[kChunk];
   load_chunk<kVec>(drow, j, end, inv_tau, xd);
 #pragma unroll
   for (int e = 0; e < kChunk; ++e)
     r[e] = fmaxf(__expf(xt[e] - mp) * isp - __expf(xd[e] - mq) * isq, 0.f);
 }
 
-template <bool kVec>
+// kBonus: target holds K + 1 rows per draft (row K: the bonus distribution).
+template <bool kVec, bool kBonus>
 __global__ __launch_bounds__(64 * kSpecWaves) void spec_accept_kernel(
     const uint16_t* __restrict__ draft, const uint16_t* __restrict__ target,
     const int32_t* __restrict__ dtok, const float* __restrict__ u, const float* __restrict__ w,
     float inv_tau, int K, int V, int32_t* __restrict__ alen, int32_t* __restrict__ next) {
-  __shared__ float st_m[2][kMaxDepths], st_s[2][kMaxDepths];
+  __shared__ float st_m[2][kMaxDepths + 1], st_s[2][kMaxDepths + 1];
   __shared__ float seg_sum[kSpecWaves];
   __shared__ int s_L;
   const int i = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int KT = K + (kBonus ? 1 : 0);  // target rows per draft
+  const uint16_t* tdraft = target + (size_t)i * KT * V;  // this draft's target rows
 
-  // 1. (max, sum) of every draft (which = 0) and target (which = 1) row, a wave per row
-  for (int r = wave; r < 2 * K; r += kSpecWaves) {
-    const int which = r / K, d = r % K;
+  // 1. (max, sum) of every draft row (which = 0) and target row (which = 1), a wave per row
+  for (int r = wave; r < K + KT; r += kSpecWaves) {
+    const int which = r < K ? 0 : 1, d = which ? r - K : r;
     float m, s;
-    row_stats<kVec>((which ? target : draft) + ((size_t)i * K + d) * V, V, inv_tau, lane, m, s);
+    row_stats<kVec>(which ? tdraft + (size_t)d * V : draft + ((size_t)i * K + d) * V, V, inv_tau,
+                    lane, m, s);
     if (lane == 0) {
       st_m[which][d] = m;
       st_s[which][d] = s;
@@ -132,8 +145,8 @@ __global__ __launch_bounds__(64 * kSpecWaves) void spec_accept_kernel(
       const size_t rd = (size_t)i * K + lane;
       const int x = dtok[rd];
       if (x >= 0 && x < V) {  // a token outside the vocabulary is rejected
-        const float p = __expf(bf16_bits_to_f32(target[rd * V + x]) * inv_tau - st_m[1][lane]) /
-                        st_s[1][lane];
+        const float p = __expf(bf16_bits_to_f32(tdraft[(size_t)lane * V + x]) * inv_tau -
+                               st_m[1][lane]) / st_s[1][lane];
         const float q = __expf(bf16_bits_to_f32(draft[rd * V + x]) * inv_tau - st_m[0][lane]) /
                         st_s[0][lane];
         ok = u[rd] * q < p;
@@ -144,20 +157,21 @@ __global__ __launch_bounds__(64 * kSpecWaves) void spec_accept_kernel(
       const int L = min((int)__builtin_ctzll(miss), K);
       alen[i] = L;
       s_L = L;
-      if (L == K) next[i] = -1;
+      if (L == K && !kBonus) next[i] = -1;
     }
   }
   __syncthreads();
   const int L = s_L;
-  if (L >= K) return;  // the same for every wave of the workgroup
+  if (L >= K && !kBonus) return;  // the same for every wave of the workgroup
 
-  // 3. inverse-CDF draw from the residual at depth L. Segment totals first (wave q sums
-  //    tokens [q * seg, (q + 1) * seg), seg a multiple of the chunk), then the wave whose
-  //    segment holds w * Z walks its chunks in order with a wave prefix sum.
-  const size_t base = ((size_t)i * K + L) * V;
-  const uint16_t* trow = target + base;
-  const uint16_t* drow = draft + base;
-  const float mp = st_m[1][L], isp = 1.f / st_s[1][L], mq = st_m[0][L], isq = 1.f / st_s[0][L];
+  // 3. inverse-CDF draw from the residual at depth L (or from the bonus row's p_K when all
+  //    K are accepted). Segment totals first (wave q sums tokens [q * seg, (q + 1) * seg),
+  //    seg a multiple of the chunk), then the wave whose segment holds w * Z walks its
+  //    chunks in order with a wave prefix sum.
+  const uint16_t* trow = tdraft + (size_t)L * V;
+  const uint16_t* drow = L < K ? draft + ((size_t)i * K + L) * V : nullptr;
+  const float mp = st_m[1][L], isp = 1.f / st_s[1][L];
+  const float mq = L < K ? st_m[0][L] : 0.f, isq = L < K ? 1.f / st_s[0][L] : 0.f;
   const int seg = (V + kSpecWaves * kChunk - 1) / (kSpecWaves * kChunk) * kChunk;
   const int s0 = min(wave * seg, V), s1 = min(s0 + seg, V);
   float part = 0.f;
@@ -189,7 +203,8 @@ __global__ __launch_bounds__(64 * kSpecWaves) void spec_accept_kernel(
   }
   if (owner < 0) owner = last, off = off_last;
   if (owner < 0) {  // no residual weight at fp32 (p == q at depth L): keep the draft token
-    if (threadIdx.x == 0) next[i] = dtok[(size_t)i * K + L];
+    // (a bonus row always has weight: its largest logit gives p = 1 / sum >= 1 / V)
+    if (threadIdx.x == 0) next[i] = L < K ? dtok[(size_t)i * K + L] : 0;
     return;
   }
   if (wave != owner) return;
@@ -241,16 +256,21 @@ __global__ __launch_bounds__(64 * kSpecWaves) void spec_accept_kernel(
 
 hipError_t launch_accept_sampled(int32_t N, int32_t K, int32_t V, const uint16_t* draft,
                                  const uint16_t* target, const int32_t* draft_tok,
-                                 const float* u, const float* w, float temperature,
+                                 const float* u, const float* w, float temperature, bool bonus,
                                  int32_t* accept_len, int32_t* next_tok, hipStream_t stream) {
   const bool vec = V % kChunk == 0 && (reinterpret_cast<uintptr_t>(draft) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(target) & 15) == 0;
-  if (vec)
-    hipLaunchKernelGGL(spec_accept_kernel<true>, dim3(N), dim3(64 * kSpecWaves), 0, stream, draft,
-                       target, draft_tok, u, w, 1.f / temperature, K, V, accept_len, next_tok);
-  else
-    hipLaunchKernelGGL(spec_accept_kernel<false>, dim3(N), dim3(64 * kSpecWaves), 0, stream, draft,
-                       target, draft_tok, u, w, 1.f / temperature, K, V, accept_len, next_tok);
+  const dim3 grid(N), block(64 * kSpecWaves);
+  const float inv_tau = 1.f / temperature;
+#define PEAGLE_SPEC(VEC, BONUS)                                                                \
+  hipLaunchKernelGGL((spec_accept_kernel<VEC, BONUS>), grid, block, 0, stream, draft, target,  \
+                     draft_tok, u, w, inv_tau, K, V, accept_len, next_tok)
+  if (vec) {
+    if (bonus) PEAGLE_SPEC(true, true); else PEAGLE_SPEC(true, false);
+  } else {
+    if (bonus) PEAGLE_SPEC(false, true); else PEAGLE_SPEC(false, false);
+  }
+#undef PEAGLE_SPEC
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ hipError_t launch_rms_inplace(float* x, const uint16_t* w, int64_t rows, int32_t
 // K depths are accepted); temperature > 0.
 hipError_t launch_accept_sampled(int32_t N, int32_t K, int32_t V, const uint16_t* draft,
                                  const uint16_t* target, const int32_t* draft_tok,
-                                 const float* u, const float* w, float temperature,
+                                 const float* u, const float* w, float temperature, bool bonus,
                                  int32_t* accept_len, int32_t* next_tok, hipStream_t stream);
 
 // Decode over a cache with per-request capacities (cu: starts and capacities) and current

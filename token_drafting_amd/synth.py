@@ -35,6 +35,7 @@ TAG_SPEC_LOGITS, TAG_SPEC_TOK, TAG_SPEC_U, TAG_SPEC_W = 31, 32, 33, 34
 TAG_STACK = 40
 TAG_DOUT = 35
 TAG_CE_LOGITS, TAG_CE_LABELS = 36, 37
+TAG_SPEC_BONUS = 38   # (40 and up belong to the stacked layers)
 
 # Rest of the draft layer: MLP intermediate size of the Gemma-3-270M and Llama-3-8B shaped
 # layers, and the draft vocabulary (8192 in the NeMo PR's validation run).
@@ -185,6 +186,35 @@ def verify_logits(seed: int, drafts: int, K: int, V: int, p_plant: float,
             target[i, d, where[i, d]] = PLANT_VALUE_BITS
             planted[i] += 1
     return dict(draft_logits=draft, target_logits=target, planted=planted)
+
+
+def verify_logits_device(seed: int, drafts: int, K: int, V: int, p_plant: float,
+                         device="cuda") -> dict:
+    """The recipe of verify_logits drawn on the device with torch's seeded generator
+    (gigabytes of logits at full size): N(0, 1) bf16 logits, and along a geometric prefix
+    of depths (each planted with probability p_plant while all earlier ones were) 16.0 at
+    one uniform position of both rows. Logits as int16 bf16 bit patterns."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + TAG_LOGITS)
+    draft = torch.empty((drafts, K, V), dtype=torch.int16, device=device)
+    target = torch.empty_like(draft)
+    rows = max(1, (1 << 25) // (K * V))
+    for lo in range(0, drafts, rows):
+        hi = min(drafts, lo + rows)
+        draft[lo:hi] = torch.randn((hi - lo, K, V), generator=g, device=device).to(
+            torch.bfloat16).view(torch.int16)
+        target[lo:hi] = torch.randn((hi - lo, K, V), generator=g, device=device).to(
+            torch.bfloat16).view(torch.int16)
+    coins = torch.rand((drafts, K), generator=g, device=device) < p_plant
+    planted = torch.cumprod(coins.to(torch.int32), dim=1).bool()      # leading run only
+    where = torch.randint(0, V, (drafts, K), generator=g, device=device)
+    flat = (torch.arange(drafts * K, device=device) * V + where.flatten())[planted.flatten()]
+    draft.view(-1)[flat] = PLANT_VALUE_BITS
+    target.view(-1)[flat] = PLANT_VALUE_BITS
+    return dict(draft_logits=draft, target_logits=target,
+                planted=planted.sum(dim=1).to(torch.int32))
 
 
 def decode_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
@@ -370,6 +400,15 @@ def sampled_verify_inputs(seed: int, drafts: int, K: int, V: int, spread: float 
     u = _rng(seed, TAG_SPEC_U).random((drafts, K), dtype=np.float32)
     w = _rng(seed, TAG_SPEC_W).random(drafts, dtype=np.float32)
     return dict(draft_logits=draft, target_logits=target, draft_tok=tok, u=u, w=w)
+
+
+def with_bonus_row(inp: dict, seed: int, spread: float = 2.0) -> dict:
+    """The same inputs with a K+1-th target row per draft (the target's distribution after
+    the last drafted token): bf16 of N(0, spread^2) logits, target_logits [drafts, K+1, V]."""
+    N, K, V = inp["target_logits"].shape
+    rng = _rng(seed, TAG_SPEC_BONUS)
+    row = f32_to_bf16_bits(spread * rng.standard_normal((N, 1, V), dtype=np.float32))
+    return dict(inp, target_logits=np.concatenate([inp["target_logits"], row], axis=1))
 
 
 def sampled_verify_inputs_device(seed: int, drafts: int, K: int, V: int, spread: float = 2.0,
