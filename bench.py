@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--decode", choices=["all", "none", "only"], default="all",
                     help="also time the decode-shaped draft attention on its inference "
                          "workloads (all), skip it (none), or time only it (only)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other four workloads and the depth sweep on the Llama-8B "
+                         "shape")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps, "
                          "so a counter run can scale its byte counters against known traffic")
@@ -86,7 +89,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from token_drafting_amd import peagle, synth
+    from token_drafting_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibration_copy_mib:
@@ -108,8 +111,107 @@ def main():
                 for name in sorted(synth.DECODE_CONFIGS)}
         print(json.dumps({"decode": res, "decode_loop": loop}), flush=True)
         return
+
+    head, ctx = step_bench(args.config, args.steps, args.warmup, cpu=not args.no_cpu_baseline,
+                           cpu_rows=args.cpu_rows, keep=True)
     cfg = synth.CONFIGS[args.config]
-    seed = args.config
+    result = {
+        "metric": "draft-attn fwd TFLOP/s + drafted tokens/s, 32K ctx K=4; % of bf16 MFMA peak",
+        "value": head["step_attn_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"],
+        "attn_core_tflops": head["attn_core_tflops"],
+        "attn_core_frac_bf16_peak": head["attn_core_frac_bf16_peak"],
+        "drafted_tokens_per_s": head["drafted_tokens_per_s"],
+        "pipeline_tokens_per_s": head["pipeline_tokens_per_s"],
+        "stage_ms": head["stage_ms"],
+        "stage_rate": head["stage_rate"],
+        "stage_rate_cold": head["stage_rate_cold"],
+        "roofline": {"kernel": "attn_core_kernel (the launches of one peagle_draft_attn_core call)",
+                     "bound": "mfma", "achieved": head["attn_core_tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": head["attn_core_frac_bf16_peak"],
+                     "traffic": traffic_bytes(args.config)},
+        "input_gen_s": head["input_gen_s"],
+        "wall_s_timed": head["wall_s_timed"],
+    }
+    if "cpu_baseline" in head:
+        result["cpu_baseline"] = head["cpu_baseline"]
+
+    seed, n, K, T, H = args.config, cfg["n"], cfg["K"], head["config"]["draft_rows"], cfg["H"]
+    d, sel, q, k, v = ctx["d"], ctx["sel"], ctx["q"], ctx["k"], ctx["v"]
+    from token_drafting_amd import peagle
+    wn = torch.from_numpy(synth.fc_norm_weight(seed, H).view(np.int16)).to(q.device)
+    ms_fcn = _time_calls(lambda: peagle.fuse_inputs(
+        n, K, T, sel["idx"], d["aux"], d["fc_weight"], d["mask_hidden"], d["tokens"], d["embed"],
+        ctx["ptd"], ctx["hidden"], ctx["emb"], fc_norm_weight=wn), args.steps, args.warmup)
+    result["fuse_fc_norm"] = {"ms_per_call": round(ms_fcn, 4),
+                              "ms_without_fc_norm": head["stage_ms"]["fuse_inputs"]}
+    result["attn_bwd"] = attn_bwd_bench(n, K, sel, d["cu_seqlens"], q, k, v, ctx["cos"], ctx["sin"],
+                                        ctx["out"], ctx["lse"], seed, head["config"][
+                                            "useful_pairs_per_head"], args.steps, args.warmup)
+    result["depth_ce"] = depth_ce_bench(sel["depth_off"], args.steps, args.warmup)
+    result["verify_d2t"] = verify_d2t_bench(args.steps, args.warmup)
+    result["verify_sampled"] = verify_sampled_bench(args.steps, args.warmup)
+    result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, ctx["hidden"], ctx["emb"],
+                                        ctx["out"], args.steps, args.warmup)
+    del d, sel, q, k, v, wn
+    ctx.clear()
+    torch.cuda.empty_cache()
+
+    if args.decode == "all":
+        result["decode"] = {name: decode_bench(name, args.steps, args.warmup)
+                            for name in sorted(synth.DECODE_CONFIGS)}
+        result["decode_loop"] = {name: decode_loop_bench(name, args.steps, args.warmup)
+                                 for name in sorted(synth.DECODE_CONFIGS)}
+    if not args.headline_only:
+        # the other four workloads, each a whole step of its own with the oracle beside it
+        result["configs"] = {}
+        for c in sorted(synth.CONFIGS):
+            if c != args.config:
+                result["configs"][str(c)] = step_bench(c, args.steps, args.warmup,
+                                                       cpu=not args.no_cpu_baseline)[0]
+                torch.cuda.empty_cache()
+        # depth sweep on the Llama-8B-shaped drafter at n = 16384
+        result["k_sweep_llama8b_16k"] = [
+            k_sweep_point(Kx, args.steps, args.warmup, n=16384, Hq=32, Hkv=8, D=128,
+                          theta=5.0e5) for Kx in (1, 2, 4, 8)]
+    print(json.dumps(result), flush=True)
+
+
+def _cold_ms(call, evict, reps):
+    """Mean time of `call` with the 256 MB last-level cache (MALL) evicted before each rep by
+    writing `evict` (>= 512 MB) on the same stream."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for i in range(reps):
+        evict.fill_(i + 1)
+        ev[i][0].record()
+        call()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+
+def step_bench(cfg_id, steps, warmup, cpu=True, cpu_rows=0, keep=False):
+    """One workload: W untimed and K timed steps of the whole path (COD select, fused
+    inputs, RoPE table, attention prepare + core, verification), per-stage HIP events, then
+    the HBM-bound stages again with the last-level cache evicted (cold), and the oracle on a
+    bounded sample. Returns (summary dict, tensors kept for further timing when `keep`)."""
+    import torch
+    from token_drafting_amd import peagle, synth
+
+    cfg = synth.CONFIGS[cfg_id]
+    seed = cfg_id
     n, K, Hq, Hkv, D = cfg["n"], cfg["K"], cfg["Hq"], cfg["Hkv"], cfg["D"]
     dev = torch.device("cuda:0")
 
@@ -118,17 +220,18 @@ def main():
             a = a.view(np.int16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    # ---------------- inputs (host, seeded) -> HBM
+    # ---------------- inputs (seeded) -> HBM
     t0 = time.time()
     m, T = peagle.cod_counts(n, K, cfg["r"], cfg["r_min"])
     base = synth.base_inputs(cfg, seed)
     qkv = synth.qkv_inputs(seed, T, Hq, Hkv, D)
     vcfg = cfg.get("verify") or dict(drafts=4096, K=K, V=32000, p_plant=0.7)
-    logits = synth.verify_logits(seed, vcfg["drafts"], vcfg["K"], vcfg["V"], vcfg["p_plant"])
+    logits = synth.verify_logits_device(seed, vcfg["drafts"], vcfg["K"], vcfg["V"], vcfg["p_plant"])
     cu_h = base["cu_seqlens"]
-    d = {k: to_dev(v) for k, v in base.items() if isinstance(v, np.ndarray)}
+    d = {k2: to_dev(v2) for k2, v2 in base.items() if isinstance(v2, np.ndarray)}
     q, k, v = (to_dev(qkv[t]) for t in ("q", "k", "v"))
-    dl, tl = to_dev(logits["draft_logits"]), to_dev(logits["target_logits"])
+    dl, tl = logits["draft_logits"], logits["target_logits"]
+    torch.cuda.synchronize()
     gen_s = time.time() - t0
 
     S = cu_h.size - 1
@@ -137,7 +240,9 @@ def main():
     sel = dict(m=m, T=T, idx=torch.empty(T, dtype=torch.int32, device=dev),
                depth_off=torch.empty(K + 1, dtype=torch.int32, device=dev),
                cu_seqlens_d=torch.empty((K, S + 1), dtype=torch.int32, device=dev),
-               row_of=torch.empty((K, n), dtype=torch.int32, device=dev))
+               row_of=torch.empty((K, n), dtype=torch.int32, device=dev),
+               workspace=torch.empty(peagle.cod_workspace_bytes(n, K), dtype=torch.uint8,
+                                     device=dev))
     hidden = torch.empty((T, H), dtype=torch.float32, device=dev)
     emb = torch.empty((T, H), dtype=torch.int16, device=dev)
     cos = torch.empty((max_pos + 1, D // 2), dtype=torch.float32, device=dev)
@@ -152,41 +257,50 @@ def main():
     lib = peagle.lib()
 
     stages = ["cod_select", "fuse_inputs", "rope_table", "attn_prepare", "attn_core", "accept_prefix"]
+    calls = [
+        lambda: peagle.cod_select_into(n, K, cfg["r"], cfg["r_min"], seed, d["cu_seqlens"], sel),
+        lambda: peagle.fuse_inputs(n, K, T, sel["idx"], d["aux"], d["fc_weight"], d["mask_hidden"],
+                                   d["tokens"], d["embed"], base["ptd_token_id"], hidden, emb),
+        lambda: peagle._check("peagle_rope_table", lib.peagle_rope_table(
+            D, cfg["theta"], max_pos, peagle._ptr(cos), peagle._ptr(sin), peagle._stream())),
+        lambda: peagle.draft_attn(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse, ws,
+                                  phase="prepare"),
+        lambda: peagle.draft_attn(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse, ws,
+                                  phase="core"),
+        lambda: peagle.accept_prefix(dl, tl, dtok, ttok, alen),
+    ]
 
     def step(ev=None):
-        def mark(i):
+        for i, call in enumerate(calls):
             if ev is not None:
                 ev[i].record()
-        mark(0)
-        peagle.cod_select_into(n, K, cfg["r"], cfg["r_min"], seed, d["cu_seqlens"], sel)
-        mark(1)
-        peagle.fuse_inputs(n, K, T, sel["idx"], d["aux"], d["fc_weight"], d["mask_hidden"],
-                           d["tokens"], d["embed"], base["ptd_token_id"], hidden, emb)
-        mark(2)
-        peagle._check("peagle_rope_table", lib.peagle_rope_table(
-            D, cfg["theta"], max_pos, peagle._ptr(cos), peagle._ptr(sin), peagle._stream()))
-        mark(3)
-        peagle.draft_attn(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse, ws, phase="prepare")
-        mark(4)
-        peagle.draft_attn(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse, ws, phase="core")
-        mark(5)
-        peagle.accept_prefix(dl, tl, dtok, ttok, alen)
-        mark(6)
+            call()
+        if ev is not None:
+            ev[len(calls)].record()
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(6)] for i in range(args.steps)])
+    per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(len(calls))]
+                    for i in range(steps)])
     stage_ms = dict(zip(stages, per.mean(axis=0).tolist()))
-    ms_step = wall * 1e3 / args.steps
+    ms_step = wall * 1e3 / steps
+
+    # HBM-bound stages with the last-level cache evicted before each call
+    evict = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_reps = max(3, min(steps, 10))
+    cold_ms = {name: _cold_ms(calls[i], evict, cold_reps)
+               for i, name in enumerate(stages) if name in ("cod_select", "attn_prepare",
+                                                            "accept_prefix")}
+    del evict
 
     # ---------------- accounting
     idx_h = sel["idx"].cpu().numpy()
@@ -196,74 +310,58 @@ def main():
     core_ms = stage_ms["attn_core"]
     attn_call_ms = stage_ms["attn_prepare"] + core_ms
     core_tflops = attn_flop / (core_ms * 1e-3) / 1e12
-    value = attn_flop / (ms_step * 1e-3) / 1e12
     # algorithmic bytes of the HBM-bound stages
     rope_bytes = T * (Hq + Hkv) * D * 2 * 2 + T * D * 4
     verify_bytes = 2 * Nd * Kv * vcfg["V"] * 2 + 8 * Nd * Kv + 4 * Nd
     cod_bytes = 4 * T + 4 * K * n + 4 * K * (S + 1) + 4 * (K + 1)
     fc_flop = 2.0 * (n + 1) * cfg["aux_dim"] * H
 
-    result = {
-        "metric": "draft-attn fwd TFLOP/s + drafted tokens/s, 32K ctx K=4; % of bf16 MFMA peak",
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+    def gbps(nbytes, ms):
+        return round(nbytes / (ms * 1e-3) / 1e9, 2)
+
+    summary = {
         "config": {"workload": cfg["workload"], "n": n, "K": K, "r": cfg["r"], "r_min": cfg["r_min"],
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "draft_rows": T,
-                   "useful_pairs_per_head": P, "verify": f"{Nd}x{Kv}x{vcfg['V']}"},
+                   "packed_sequences": S, "useful_pairs_per_head": P,
+                   "verify": f"{Nd}x{Kv}x{vcfg['V']}"},
+        "ms_per_step": round(ms_step, 4),
+        "step_attn_tflops": round(attn_flop / (ms_step * 1e-3) / 1e12, 3),
         "attn_core_tflops": round(core_tflops, 2),
         "attn_core_frac_bf16_peak": round(core_tflops / PEAK_BF16_TFLOPS, 4),
         "drafted_tokens_per_s": round(T / (attn_call_ms * 1e-3), 1),
         "pipeline_tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "stage_ms": {k2: round(v2, 4) for k2, v2 in stage_ms.items()},
         "stage_rate": {
-            "cod_select_GBps": round(cod_bytes / (stage_ms["cod_select"] * 1e-3) / 1e9, 2),
+            "cod_select_GBps": gbps(cod_bytes, stage_ms["cod_select"]),
             "fuse_fc_TFLOPs": round(fc_flop / (stage_ms["fuse_inputs"] * 1e-3) / 1e12, 2),
-            "attn_prepare_rope_GBps": round(rope_bytes / (stage_ms["attn_prepare"] * 1e-3) / 1e9, 1),
-            "accept_prefix_GBps": round(verify_bytes / (stage_ms["accept_prefix"] * 1e-3) / 1e9, 1),
+            "fuse_fc_frac_bf16_peak": round(fc_flop / (stage_ms["fuse_inputs"] * 1e-3) / 1e12
+                                            / PEAK_BF16_TFLOPS, 4),
+            "attn_prepare_rope_GBps": gbps(rope_bytes, stage_ms["attn_prepare"]),
+            "accept_prefix_GBps": gbps(verify_bytes, stage_ms["accept_prefix"]),
         },
-        "roofline": {"kernel": "attn_core_kernel (the launches of one peagle_draft_attn_core call)",
-                     "bound": "mfma", "achieved": round(core_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(core_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_bytes(args.config)},
+        "stage_rate_cold": {
+            "note": "the 256 MB last-level cache evicted (512 MB written) before each call",
+            "cod_select_GBps": gbps(cod_bytes, cold_ms["cod_select"]),
+            "attn_prepare_rope_GBps": gbps(rope_bytes, cold_ms["attn_prepare"]),
+            "accept_prefix_GBps": gbps(verify_bytes, cold_ms["accept_prefix"]),
+            "frac_hbm_peak": {
+                "cod_select": round(cod_bytes / (cold_ms["cod_select"] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                "attn_prepare_rope": round(rope_bytes / (cold_ms["attn_prepare"] * 1e-3) / 1e9
+                                           / PEAK_HBM_GBPS, 4),
+                "accept_prefix": round(verify_bytes / (cold_ms["accept_prefix"] * 1e-3) / 1e9
+                                       / PEAK_HBM_GBPS, 4)},
+        },
         "input_gen_s": round(gen_s, 1),
         "wall_s_timed": round(wall, 4),
     }
-
-    wn = torch.from_numpy(synth.fc_norm_weight(seed, H).view(np.int16)).to(dev)
-    ms_fcn = _time_calls(lambda: peagle.fuse_inputs(
-        n, K, T, sel["idx"], d["aux"], d["fc_weight"], d["mask_hidden"], d["tokens"], d["embed"],
-        base["ptd_token_id"], hidden, emb, fc_norm_weight=wn), args.steps, args.warmup)
-    result["fuse_fc_norm"] = {"ms_per_call": round(ms_fcn, 4),
-                              "ms_without_fc_norm": round(stage_ms["fuse_inputs"], 4)}
-    result["attn_bwd"] = attn_bwd_bench(n, K, sel, d["cu_seqlens"], q, k, v, cos, sin, out, lse,
-                                        seed, P, args.steps, args.warmup)
-    result["depth_ce"] = depth_ce_bench(sel["depth_off"], args.steps, args.warmup)
-    result["verify_d2t"] = verify_d2t_bench(args.steps, args.warmup)
-    result["verify_sampled"] = verify_sampled_bench(args.steps, args.warmup)
-    result["draft_layer"] = layer_bench(args.config, cfg, seed, n, K, T, hidden, emb, out,
-                                        args.steps, args.warmup)
-
-    if args.decode == "all":
-        del ws, out, lse, hidden, emb, dl, tl
-        torch.cuda.empty_cache()
-        result["decode"] = {name: decode_bench(name, args.steps, args.warmup)
-                            for name in sorted(synth.DECODE_CONFIGS)}
-        result["decode_loop"] = {name: decode_loop_bench(name, args.steps, args.warmup)
-                                 for name in sorted(synth.DECODE_CONFIGS)}
-
-    # ---------------- oracle on the host cores (bounded sample)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, seed, qkv, cu_h, idx_h, off_h, args.cpu_rows)
-    print(json.dumps(result), flush=True)
+    if cpu:
+        summary["cpu_baseline"] = cpu_baseline(cfg, seed, qkv, cu_h, idx_h, off_h, cpu_rows)
+    ctx = {}
+    if keep:
+        ctx = dict(d=d, sel=sel, q=q, k=k, v=v, cos=cos, sin=sin, out=out, lse=lse,
+                   hidden=hidden, emb=emb, ptd=base["ptd_token_id"])
+    del dl, tl, logits, ws
+    return summary, ctx
 
 
 def k_sweep_point(K, steps, warmup, n=32768, Hq=4, Hkv=1, D=256, r=0.7, r_min=0.2,
