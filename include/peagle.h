@@ -94,6 +94,25 @@ int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t see
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * peagle_cod_select_noalloc -- peagle_cod_select for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and outputs without the workspace. Its scratch (the
+ * thresholds and per-block counts) is a static device array of
+ * PEAGLE_COD_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until the process
+ * ends; the call allocates and frees nothing. The first call on a device looks up the
+ * array's address there (hipGetSymbolAddress). Limit: peagle_cod_workspace_bytes(n, K) must
+ * not exceed PEAGLE_COD_NOALLOC_SCRATCH_BYTES (e.g. n <= 33.5M at K = 8), else
+ * PEAGLE_ERR_WORKSPACE and nothing is enqueued. All calls on one GPU share the array: calls
+ * that may overlap on that GPU (other streams, other threads) race and must be ordered by
+ * the caller. The scratch needs no clearing: every call writes what it reads.
+ */
+#define PEAGLE_COD_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+int peagle_cod_select_noalloc(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
+                              const int32_t *cu_seqlens, int32_t num_seqs, int32_t *idx,
+                              int32_t *depth_off, int32_t *cu_seqlens_d, int32_t *row_of,
+                              void *stream);
+
+/*
  * peagle_fuse_inputs -- fused input stage [N, description; G, "Architecture"]. Depth 0
  * rows take fc(aux[p]) and the embedding of tokens[p]; depth >= 1 rows take
  * fc(mask_hidden) and the embedding of ptd_token_id. fc is a bias-free linear layer

@@ -85,7 +85,17 @@ def test_cod_argument_errors(lib):
     assert _code("peagle_cod_select", 5000, 4, 0.7, 0.2, 1, fake, 1, fake, fake, fake, fake,
                  C.c_void_p((1 << 20) + 16), need, None) == peagle.ERR_ARG   # misaligned
     assert peagle.cod_workspace_bytes(0, 4) == 0 and peagle.cod_workspace_bytes(10, 65) == 0
-
+    # the allocation-free variant refuses sizes past its static scratch on the host
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "peagle.h")).read()
+    m = re.search(r"#define PEAGLE_COD_NOALLOC_SCRATCH_BYTES \(\(size_t\)1 << (\d+)\)", hdr)
+    assert m and (1 << int(m.group(1))) == peagle.COD_NOALLOC_SCRATCH_BYTES
+    big = 1 << 24
+    assert peagle.cod_workspace_bytes(big, 64) > peagle.COD_NOALLOC_SCRATCH_BYTES
+    assert _code("peagle_cod_select_noalloc", big, 64, 0.7, 0.2, 1, fake, 1, fake, fake, fake,
+                 fake, None) == peagle.ERR_WORKSPACE
+    assert _code("peagle_cod_select_noalloc", 10, 4, 0.7, 0.2, 1, None, 1, None, None, None,
+                 None, None) == peagle.ERR_ARG
 
 
 def test_fuse_argument_errors(lib):

@@ -132,15 +132,21 @@ size_t peagle_cod_workspace_bytes(int64_t n, int32_t K) {
 static int cod_select_entry(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t* idx,
                             int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, bool noalloc, void* stream) {
   int64_t m[PEAGLE_MAX_DEPTHS], T = 0;
   const int st = counts(n, K, r, r_min, m, &T);
   if (st != PEAGLE_OK) return st;
   if (T > kMaxI32 || (int64_t)K * n > ((int64_t)1 << 40)) return PEAGLE_ERR_ARG;
   if (num_seqs < 1 || num_seqs > n) return PEAGLE_ERR_ARG;
   if (!cu_seqlens || !idx || !depth_off || !cu_seqlens_d || !row_of) return PEAGLE_ERR_ARG;
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PEAGLE_ERR_ARG;
-  if (workspace_bytes < cod_workspace_bytes(n, K)) return PEAGLE_ERR_WORKSPACE;
+  if (noalloc) {
+    static_assert(kCodNoAllocScratchBytes == PEAGLE_COD_NOALLOC_SCRATCH_BYTES, "scratch size");
+    if (cod_workspace_bytes(n, K) > kCodNoAllocScratchBytes) return PEAGLE_ERR_WORKSPACE;
+    if (cod_noalloc_scratch(&workspace) != hipSuccess) return PEAGLE_ERR_HIP;
+  } else {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return PEAGLE_ERR_ARG;
+    if (workspace_bytes < cod_workspace_bytes(n, K)) return PEAGLE_ERR_WORKSPACE;
+  }
   CodArgs a{};
   a.n = (int32_t)n;
   a.K = K;
@@ -160,9 +166,16 @@ int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t see
                       int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
                       void* workspace, size_t workspace_bytes, void* stream) {
   return cod_select_entry(n, K, r, r_min, seed, cu_seqlens, num_seqs, idx, depth_off,
-                          cu_seqlens_d, row_of, workspace, workspace_bytes, stream);
+                          cu_seqlens_d, row_of, workspace, workspace_bytes, false, stream);
 }
 
+int peagle_cod_select_noalloc(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
+                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t* idx,
+                              int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
+                              void* stream) {
+  return cod_select_entry(n, K, r, r_min, seed, cu_seqlens, num_seqs, idx, depth_off,
+                          cu_seqlens_d, row_of, nullptr, 0, true, stream);
+}
 
 int peagle_fuse_inputs(int64_t n, int32_t K, int64_t T, const int32_t* idx,
                        const peagle_bf16* aux, int32_t aux_dim, const peagle_bf16* fc_weight,

@@ -21,10 +21,17 @@
 //   cod_compact_kernel (one workgroup per block of 1024 positions):
 //     3. ordered compaction of its block with wave ballots (coalesced idx / row_of);
 //     4. cu_seqlens_d for the sequence starts inside its block.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace peagle {
+
+// Scratch of the allocation-free entry point: thresholds and per-block prefixes, the same
+// layout as a caller's workspace. Each device holds its own copy for the life of the
+// process; host code reaches it only through the address hipGetSymbolAddress returns.
+__device__ __align__(256) char scratch[kCodNoAllocScratchBytes];
 
 namespace {
 
@@ -338,6 +345,26 @@ hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_
   hipLaunchKernelGGL(cod_compact_kernel, dim3((a.n + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      stream, a, cu_seqlens, thr, before, idx, depth_off, cu_seqlens_d, row_of);
   return hipGetLastError();
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on the current device, looked up on the first call there
+// (concurrent first calls look up and store the same address).
+hipError_t cod_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace peagle

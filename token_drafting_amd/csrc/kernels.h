@@ -18,7 +18,9 @@ struct CodArgs {
 };
 
 size_t cod_workspace_bytes(int64_t n, int32_t K);
-
+// Size of the static device scratch used by the allocation-free COD entry point.
+constexpr size_t kCodNoAllocScratchBytes = (size_t)1 << 20;
+hipError_t cod_noalloc_scratch(void** ptr);
 hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_t* idx,
                              int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
                              void* workspace, hipStream_t stream);

@@ -31,6 +31,8 @@ SIGNATURES = {
     "peagle_version": ([], _i32),
     "peagle_cod_counts": ([_i64, _i32, _f64, _f64, _p, _p], _i32),
     "peagle_cod_workspace_bytes": ([_i64, _i32], _sz),
+    "peagle_cod_select_noalloc": ([_i64, _i32, _f64, _f64, _u64, _p, _i32, _p, _p, _p, _p, _p],
+                                  _i32),
     "peagle_cod_select": ([_i64, _i32, _f64, _f64, _u64, _p, _i32, _p, _p, _p, _p, _p, _sz, _p],
                           _i32),
     "peagle_fuse_inputs": ([_i64, _i32, _i64, _p, _p, _i32, _p, _p, _p, _p, _i32, _i32, _i32,
@@ -161,6 +163,20 @@ def cod_select_into(n, K, r, r_min, seed, cu_seqlens, out):
         n, K, r, r_min, seed & ((1 << 64) - 1), _ptr(cu_seqlens), S, _ptr(out["idx"]),
         _ptr(out["depth_off"]), _ptr(out["cu_seqlens_d"]), _ptr(out["row_of"]), _ptr(ws),
         ws.numel(), _stream()))
+
+
+COD_NOALLOC_SCRATCH_BYTES = 1 << 20   # PEAGLE_COD_NOALLOC_SCRATCH_BYTES
+
+
+def cod_select_noalloc(n: int, K: int, r: float, r_min: float, seed: int, cu_seqlens, out):
+    """peagle_cod_select_noalloc into the caller's tensors out[idx, depth_off, cu_seqlens_d,
+    row_of] (no workspace: the library's static device scratch)."""
+    _dev(cu_seqlens, "cu_seqlens")
+    S = cu_seqlens.numel() - 1
+    _check("peagle_cod_select_noalloc", lib().peagle_cod_select_noalloc(
+        n, K, r, r_min, seed & ((1 << 64) - 1), _ptr(cu_seqlens), S, _ptr(out["idx"]),
+        _ptr(out["depth_off"]), _ptr(out["cu_seqlens_d"]), _ptr(out["row_of"]), _stream()))
+    return out
 
 
 # ---------------------------------------------------------------- fuse
