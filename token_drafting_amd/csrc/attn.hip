@@ -38,16 +38,18 @@
 // below 2^64, and floating point keeps the same relative precision at any scale. The O
 // accumulators are then touched only by MFMAs inside the loop and stay in AGPRs. A row
 // whose sum exceeds 2^64 (a later score more than ~40 above the first tile's maximum,
-// in base-2 units) flags its chunk, and the second kernel recomputes the chunk with a
-// rescaling online softmax.
+// in base-2 units) marks its chunk, which is then recomputed on the exact path with a
+// rescaling online softmax: by the same workgroup when the key range is not split, else
+// by a redo launch after the segments are merged.
 //
 // Precision. Rounding q', k' and P to bf16 perturbs each score by ~1e-3 and each weight
 // by up to 2^-9; for a row whose output mixes only a handful of keys that moves it by
 // up to ~1e-2 (outputs there reach |v| ~ 5). Chunks whose context span is short
-// (<= kShortSpan keys: the first anchors of each sequence) run in the second kernel,
-// which also carries k' = k_hi + k_lo (k_lo from the RoPE kernel, two MFMAs per step of
-// S^T) and P = P_hi + P_lo (two MFMAs per step of PV); q' stays bf16. Rows with many
-// keys average the rounding out and take the plain path.
+// (<= kShortSpan keys: the first anchors of each sequence) take the exact path, which
+// carries k' = k_hi + k_lo (k_lo from the RoPE kernel, two MFMAs per step of S^T) and
+// P = P_hi + P_lo (two MFMAs per step of PV); q' stays bf16. Rows with many keys average
+// the rounding out and take the plain path. Both paths live in one kernel: the short
+// chunks are its last blocks (they fill the tail behind the long chunks).
 //
 // LDS layouts. K tiles: one 16-byte-padded row per key (stride 2D + 16 bytes), so the
 // 32 keys a half-wave reads at one head-dim offset fall in distinct bank groups and a
@@ -119,6 +121,7 @@ struct AttnParams {
   float2* ml;     // [segment][Hq][T]: (reference max, sum) of each segment of split chunks
   int n, T, S, Hq, Hkv, G, QR, ntiles, exact_per_seq, max_chunks, nsplit;
   int budget;  // work items the split main kernel runs at once (one round)
+  int main_blocks;  // unsplit launch: blocks of the main path (chunk bound x kv heads)
   float c_log2;
 };
 
@@ -168,59 +171,44 @@ __device__ __forceinline__ int seg_count(int ntl, int L, int nsplit) {
 constexpr int kMinSplitTiles = 8;  // shorter segments do not pay for their partial's merge
 constexpr int kItemsMaxEntries = 4096;  // (chunk, kv head) entries the length search holds
 
-// EXACT = false: the main kernel, every chunk with a long context span. EXACT = true:
-// chunks with a short span, and chunks the main kernel flagged for a redo. SPLIT (main
-// kernel only): each chunk's context is cut into segments run by separate workgroups.
+// LDS of one workgroup, shared by the main and the exact paths: double-buffered K, V^T and
+// (exact path) k_lo tiles, plus the chunk's key range and the diagonal keys' metadata.
+template <int D>
+struct AttnLds {
+  using C = Cfg<D, 1>;
+  alignas(1024) char Ks0[C::KBUF];
+  alignas(1024) char Ks1[C::KBUF];
+  alignas(1024) char Vs0[C::VBYTES];
+  alignas(1024) char Vs1[C::VBYTES];
+  alignas(1024) char Kl0[C::KBUF];
+  alignas(1024) char Kl1[C::KBUF];
+  int range[6];
+  int kp[KT], kd[KT];
+  int bad;  // main path: some row's fixed-reference sum left the safe range
+};
+
+// One (chunk, kv head) of the attention, or one segment of it (SPLIT). EXACT = false: the
+// main path, chunks with a long context span (a short chunk returns at once); it sets
+// L.bad when a row's sum overflowed. EXACT = true: chunks with a short span (k' and P
+// split into bf16 pairs), or with `redo` a chunk the main path flagged (rescaling online
+// softmax on k' alone). Every thread of the workgroup calls it with the same arguments.
 template <int D, bool EXACT, bool SPLIT>
-__global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void attn_core_kernel(
-    const AttnParams p) {
+__device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, int chunk, int g,
+                                           int seg, int nseg, bool redo) {
   constexpr int NT = EXACT ? kExactNT : kMainNT;
   using C = Cfg<D, NT>;
-  __shared__ __attribute__((aligned(1024))) char Ks0[C::KBUF];
-  __shared__ __attribute__((aligned(1024))) char Ks1[C::KBUF];
-  __shared__ __attribute__((aligned(1024))) char Vs0[C::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char Vs1[C::VBYTES];
-  __shared__ __attribute__((aligned(1024))) char Kl0[EXACT ? C::KBUF : 16];
-  __shared__ __attribute__((aligned(1024))) char Kl1[EXACT ? C::KBUF : 16];
-  __shared__ int s_range[6];
-  __shared__ int s_kp[KT], s_kd[KT];
-  __shared__ int s_redo;
+  char* const Ks0 = L.Ks0;
+  char* const Ks1 = L.Ks1;
+  char* const Vs0 = L.Vs0;
+  char* const Vs1 = L.Vs1;
+  char* const Kl0 = L.Kl0;
+  char* const Kl1 = L.Kl1;
+  int* const s_range = L.range;
+  int* const s_kp = L.kp;
+  int* const s_kd = L.kd;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, half = lane >> 5;
-  const int bid = blockIdx.x;
-  int g = bid % p.Hkv;
-  int chunk, seg = 0, nseg = 1;
-  bool redo = false;
-  if constexpr (EXACT) {
-    const int r = bid / p.Hkv;  // short chunks first, then every chunk (redo if flagged)
-    const int n_short = p.S * p.exact_per_seq;
-    if (r < n_short) {  // one of the first chunks of a sequence
-      const int s = r / p.exact_per_seq, j = r % p.exact_per_seq;
-      chunk = p.seq_chunk[s] + j;
-      if (chunk >= p.seq_chunk[s + 1]) return;
-    } else {            // a chunk the main kernel flagged
-      chunk = r - n_short;
-      if (chunk >= *p.nchunks || p.flags[chunk * p.Hkv + g] == 0) return;
-      redo = true;
-    }
-  } else {
-    // Chunks are listed sequence by sequence, anchors ascending: the last ones have the
-    // longest prefixes, so they are dispatched first. The grid is sized for the largest
-    // possible chunk count; blocks past the actual count exit. With a key-range split the
-    // blocks take the items of the work list, which is in the same order.
-    if constexpr (SPLIT) {
-      if (bid >= *p.nitems) return;
-      const int2 it = p.items[bid];
-      g = it.x % p.Hkv;
-      chunk = it.x / p.Hkv;
-      seg = it.y & 255;
-      nseg = max(it.y >> 8, 1);
-    } else {
-      chunk = *p.nchunks - 1 - bid / p.Hkv;
-    }
-    if (chunk < 0) return;
-  }
   const int n = p.n, T = p.T, Hkv = p.Hkv;
   const int2 ch = p.chunks[chunk];
   const int j0 = min(max(ch.x, 0), T - 1);
@@ -234,7 +222,7 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
     s_range[3] = c.full_hi;
     s_range[4] = min(max(p.qstart[c.p_first], 0), T);     // diagonal keys: entries of the
     s_range[5] = min(max(p.qstart[c.p_last + 1], 0), T);  // chunk's anchors in the list
-    s_redo = 0;
+    L.bad = 0;
   }
   __syncthreads();
   const int k_lo = s_range[0], k_hi = s_range[1], full_lo = s_range[2], full_hi = s_range[3];
@@ -559,12 +547,67 @@ __global__ __launch_bounds__(2 * kAttnSlots / (EXACT ? kExactNT : kMainNT)) void
     }
   }
   if constexpr (!EXACT) {
-    if (__any(bad) && lane == 0) s_redo = 1;
-    __syncthreads();
-    if (tid == 0 && s_redo) p.flags[chunk * Hkv + g] = 1;
-  } else {
-    if (redo && tid == 0) p.flags[chunk * Hkv + g] = 0;
+    if (__any(bad) && lane == 0) L.bad = 1;
   }
+}
+
+// Roles of the attention launches.
+//   kRoleMain  (the key range is not split): blocks [0, main_blocks) take the chunks
+//              heaviest first on the main path, and redo their own chunk with the exact
+//              path when a row's sum overflowed; the blocks after them take the short
+//              chunks, so those fill the tail of the launch.
+//   kRoleSplit (key-range split): blocks [0, short_blocks) take the short chunks, the rest
+//              the (chunk, segment) work list; an overflow flags the chunk.
+//   kRoleRedo  (after the split's merge): the flagged chunks, exact path.
+enum { kRoleMain = 0, kRoleSplit = 1, kRoleRedo = 2 };
+
+template <int D, int ROLE>
+__global__ __launch_bounds__(2 * kAttnSlots) void attn_core_kernel(const AttnParams p) {
+  static_assert(kMainNT == kExactNT, "one LDS layout for both paths");
+  __shared__ AttnLds<D> L;
+  const int bid = blockIdx.x;
+  const int short_blocks = p.S * p.exact_per_seq * p.Hkv;
+  if constexpr (ROLE == kRoleRedo) {
+    const int chunk = bid / p.Hkv, g = bid % p.Hkv;
+    if (chunk >= min(*p.nchunks, p.max_chunks) || p.flags[chunk * p.Hkv + g] == 0) return;
+    attn_chunk<D, true, false>(p, L, chunk, g, 0, 1, true);
+    if (threadIdx.x == 0) p.flags[chunk * p.Hkv + g] = 0;
+    return;
+  }
+  const int sb = ROLE == kRoleMain ? bid - p.main_blocks : bid;
+  int chunk, g;
+  bool redo = false;
+  if (sb >= 0 && sb < short_blocks) {  // one of the first chunks of a sequence
+    const int r = sb / p.Hkv;
+    const int s = r / p.exact_per_seq, j = r % p.exact_per_seq;
+    g = sb % p.Hkv;
+    chunk = p.seq_chunk[s] + j;
+    if (chunk >= p.seq_chunk[s + 1]) return;
+  } else if constexpr (ROLE == kRoleMain) {
+    // Chunks are listed sequence by sequence, anchors ascending: the last ones have the
+    // longest prefixes, so they are dispatched first. The grid is sized for the largest
+    // possible chunk count; blocks past the actual count exit.
+    chunk = *p.nchunks - 1 - bid / p.Hkv;
+    g = bid % p.Hkv;
+    if (chunk < 0) return;
+    attn_chunk<D, false, false>(p, L, chunk, g, 0, 1, false);
+    __syncthreads();
+    if (!L.bad) return;
+    __syncthreads();  // every wave has read L.bad before the redo clears it
+    redo = true;
+  } else {
+    // the work list of the split, in the same heaviest-first order
+    const int item = sb - short_blocks;
+    if (item >= *p.nitems) return;
+    const int2 it = p.items[item];
+    g = it.x % p.Hkv;
+    chunk = it.x / p.Hkv;
+    attn_chunk<D, false, true>(p, L, chunk, g, it.y & 255, max(it.y >> 8, 1), false);
+    __syncthreads();
+    if (threadIdx.x == 0 && L.bad) p.flags[chunk * p.Hkv + g] = 1;
+    return;
+  }
+  attn_chunk<D, true, false>(p, L, chunk, g, 0, 1, redo);
 }
 
 // Work list of the split main kernel, one workgroup. Every (chunk, kv head) entry, heaviest
@@ -757,23 +800,29 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p.exact_per_seq = attn_exact_chunks_per_seq(a.K, p.QR);
   p.max_chunks = L.max_chunks;
   p.c_log2 = a.scale * 1.4426950408889634f;
-  // The main kernel (or the split's work list, segments and merge), then one launch of the
-  // exact kernel for the short chunks and for the chunks the main kernel flagged. All on
-  // the caller's stream: the library keeps no streams or events of its own.
+  // Unsplit: one launch, the main path's blocks heaviest chunk first, then the short chunks
+  // (exact path) filling the tail; a chunk whose sums overflow is redone by its own block.
+  // Split: the work list, one launch of the short chunks and the segments, the merge, then
+  // the redo of flagged chunks. All on the caller's stream: the library keeps no streams or
+  // events of its own.
   // chunk count <= ceil(T / QR) + S (each sequence adds at most one partial chunk)
   const int chunk_bound = std::min(L.max_chunks, (a.T + p.QR - 1) / p.QR + a.S);
-  const int n_short = a.S * p.exact_per_seq;
-  const dim3 main_grid(chunk_bound * a.Hkv * p.nsplit);
+  const int short_blocks = a.S * p.exact_per_seq * a.Hkv;
+  p.main_blocks = chunk_bound * a.Hkv;
+  const dim3 main_grid(p.main_blocks + short_blocks);
+  const dim3 split_grid(short_blocks + chunk_bound * a.Hkv * p.nsplit);
   const dim3 combine_grid(chunk_bound * a.Hkv, kAttnSlots / 4);
-  const dim3 exact_grid((n_short + chunk_bound) * a.Hkv);
+  const dim3 redo_grid(chunk_bound * a.Hkv);
+  const dim3 block(2 * kAttnSlots);
   if (p.nsplit > 1) {
-    // one round of the split main kernel: its resident workgroups over the chip
+    // one round of the split launch: its resident workgroups over the chip, less the short
+    // chunks' workgroups that run beside the segments
     int per_cu = 1;
     hipError_t eo = hipErrorInvalidValue;
 #define PEAGLE_OCC(DD)                                                                      \
   eo = hipOccupancyMaxActiveBlocksPerMultiprocessor(                                        \
-      &per_cu, reinterpret_cast<const void*>(&attn_core_kernel<DD, false, true>),           \
-      Cfg<DD, kMainNT>::TH, 0)
+      &per_cu, reinterpret_cast<const void*>(&attn_core_kernel<DD, kRoleSplit>),            \
+      2 * kAttnSlots, 0)
     switch (a.D) {
       case 64: PEAGLE_OCC(64); break;
       case 128: PEAGLE_OCC(128); break;
@@ -782,21 +831,18 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
     }
 #undef PEAGLE_OCC
     if (eo != hipSuccess) per_cu = 1;
-    p.budget = std::max(1, per_cu) * device_cus();
+    p.budget = std::max(1, std::max(1, per_cu) * device_cus() - short_blocks);
   }
 #define PEAGLE_CORE(DD)                                                                       \
   do {                                                                                        \
     if (p.nsplit > 1) {                                                                       \
       hipLaunchKernelGGL(attn_items_kernel, dim3(1), dim3(1024), 0, stream, p);               \
-      hipLaunchKernelGGL((attn_core_kernel<DD, false, true>), main_grid,                      \
-                         dim3(Cfg<DD, kMainNT>::TH), 0, stream, p);                           \
+      hipLaunchKernelGGL((attn_core_kernel<DD, kRoleSplit>), split_grid, block, 0, stream, p); \
       hipLaunchKernelGGL((attn_combine_kernel<DD>), combine_grid, dim3(256), 0, stream, p);   \
+      hipLaunchKernelGGL((attn_core_kernel<DD, kRoleRedo>), redo_grid, block, 0, stream, p);  \
     } else {                                                                                  \
-      hipLaunchKernelGGL((attn_core_kernel<DD, false, false>), main_grid,                     \
-                         dim3(Cfg<DD, kMainNT>::TH), 0, stream, p);                           \
+      hipLaunchKernelGGL((attn_core_kernel<DD, kRoleMain>), main_grid, block, 0, stream, p);  \
     }                                                                                         \
-    hipLaunchKernelGGL((attn_core_kernel<DD, true, false>), exact_grid,                       \
-                       dim3(Cfg<DD, kExactNT>::TH), 0, stream, p);                            \
   } while (0)
   switch (a.D) {
     case 64: PEAGLE_CORE(64); break;
