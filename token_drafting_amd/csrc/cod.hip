@@ -113,7 +113,7 @@ __device__ __forceinline__ bool own_search(const CodArgs& a, int d) {
 __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
     CodArgs a, uint64_t* __restrict__ thr_out, int32_t* __restrict__ before_out) {
   constexpr int kPerThread = kBins / kThreads;
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kBins];  // 12-bit histogram; later the per-block kept counts
   __shared__ uint64_t cand[kCand];
   __shared__ uint32_t hcache[kCache];
   __shared__ uint64_t thr[kMaxDepths];
@@ -132,6 +132,11 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
   auto top32 = [&](int p) -> uint32_t {
     return p < ncache ? hcache[p] : (uint32_t)(hash_of(p) >> 32);
   };
+  // Depth d's parameters sit in lane d of every wave (K <= 64) and are broadcast with
+  // readlane inside the loops, instead of indexing the kernel arguments there.
+  auto bcast = [](int v, int d) { return __builtin_amdgcn_readlane(v, d); };
+  const int m_v = lane < K ? a.m[lane] : 0;
+  const bool own_v = lane < K && own_search(a, lane);
 
   // 1. thresholds: keep p at depth d iff hash(p) <= thr[d] (m_d == 0 keeps nothing).
   //    One histogram of the top 12 hash bits serves every depth: its prefix sums give the
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
     for (int i = 0; i < kPerThread; ++i) {
       const int b = tid * kPerThread + i;
       for (int d = 0; d < K; ++d) {
-        const int m = a.m[d];
+        const int m = bcast(m_v, d);
         if (m > before && m <= before + (int)mine[i]) {
           bin_of[d] = b;
           rank_in_bin[d] = m - before;
@@ -183,10 +188,11 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
   if (cbase[K] <= kCand) {
     // one pass gathers every depth's candidates, then each candidate ranks itself inside
     // its depth's region (the region's hashes are distinct: exactly one has the rank)
+    const int bin_v = own_v ? bin_of[lane] : -1;
     for (int p = tid; p < n; p += kThreads) {
       const int t = (int)(top32(p) >> (32 - kBinBits));
       for (int d = 0; d < K; ++d)
-        if (own_search(a, d) && t == bin_of[d]) cand[cbase[d] + atomicAdd(&cfill[d], 1)] = hash_of(p);
+        if (t == bcast(bin_v, d)) cand[cbase[d] + atomicAdd(&cfill[d], 1)] = hash_of(p);
     }
     __syncthreads();
     for (int i = tid; i < cbase[K]; i += kThreads) {
@@ -205,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
       if (!own_search(a, d)) continue;
       const uint32_t b = (uint32_t)bin_of[d];
       if (hist[b] > (uint32_t)kCand) {
-        const uint64_t t = radix_select(a, a.m[d], reinterpret_cast<uint32_t*>(cand), &s_prefix, &s_rank);
+        const uint64_t t = radix_select(a, a.m[d], reinterpret_cast<uint32_t*>(cand), &s_prefix,
+                                        &s_rank);
         if (tid == 0) thr[d] = t;
         __syncthreads();
         continue;
@@ -232,8 +239,13 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
 
   // 2. kept positions of every depth in each block of kThreads positions: a wave per
   //    block, one ballot per depth and 64 positions; lane d carries depth d's count. The
-  //    full hash is needed only where the top 32 bits tie a threshold's.
+  //    full hash is needed only where the top 32 bits tie a threshold's. The counts go to
+  //    LDS (the histogram's space, no longer needed) when they fit, else to before_out.
   const int nb = (n + kThreads - 1) / kThreads;
+  const bool in_lds = nb * K <= kBins;
+  int32_t* const cnt = in_lds ? reinterpret_cast<int32_t*>(hist) : before_out;
+  const uint32_t thr_hi_v = lane < K ? (uint32_t)(thr[lane] >> 32) : 0u;
+  const uint32_t thr_lo_v = lane < K ? (uint32_t)thr[lane] : 0u;
   for (int b = wave; b < nb; b += kWaves) {
     int c = 0;
     for (int j = 0; j < kThreads; j += kWave) {
@@ -241,21 +253,23 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
       const bool inside = p < n;
       const uint32_t t = inside ? top32(p) : 0u;
       for (int d = 0; d < K; ++d) {
-        const uint32_t th = (uint32_t)(thr[d] >> 32);
-        const bool keep = inside && a.m[d] > 0 && (t < th || (t == th && hash_of(p) <= thr[d]));
+        const uint32_t th = (uint32_t)bcast((int)thr_hi_v, d);
+        bool keep = inside && bcast(m_v, d) > 0 && t <= th;
+        if (keep && t == th)
+          keep = (uint32_t)hash_of(p) <= (uint32_t)bcast((int)thr_lo_v, d);
         const uint64_t ball = __ballot(keep);
         if (lane == d) c += __popcll(ball);
       }
     }
-    if (lane < K) before_out[(size_t)b * K + lane] = c;
+    if (lane < K) cnt[(size_t)b * K + lane] = c;
   }
   __syncthreads();
-  // exclusive prefix over the blocks, per depth, in place
+  // exclusive prefix over the blocks, per depth, into before_out
   for (int d = 0; d < K; ++d) {
     int carry = 0;
     for (int b0 = 0; b0 < nb; b0 += kThreads) {
       const int b = b0 + tid;
-      const int v = b < nb ? before_out[(size_t)b * K + d] : 0;
+      const int v = b < nb ? cnt[(size_t)b * K + d] : 0;
       int total;
       const int ex = block_scan_excl(v, sh, &total);
       if (b < nb) before_out[(size_t)b * K + d] = carry + ex;
