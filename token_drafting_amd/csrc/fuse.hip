@@ -22,6 +22,8 @@
 // and serves 16 lanes of a 16-byte read per cycle: rows 2i and 2i+1 fill the two halves
 // of a bank row, and the swizzle gives the 8 even (odd) rows of a 16-row group 8
 // different chunk slots.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm.h"
 #include "kernels.h"
@@ -188,6 +190,46 @@ __global__ __launch_bounds__(256) void fuse_fill_kernel(
   }
 }
 
+// The K-split fc GEMM's partials summed in a fixed order, in place: out = (out + p1) + p2
+// (p2 may be null), over `count` float4s.
+__global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ out,
+                                                        const float* __restrict__ p1,
+                                                        const float* __restrict__ p2,
+                                                        size_t count) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += stride) {
+    floatx4 o = reinterpret_cast<const floatx4*>(out)[i];
+    const floatx4 b = reinterpret_cast<const floatx4*>(p1)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += b[e];
+    if (p2 != nullptr) {
+      const floatx4 c = reinterpret_cast<const floatx4*>(p2)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] += c[e];
+    }
+    reinterpret_cast<floatx4*>(out)[i] = o;
+  }
+}
+
+// Ranges of the reduction the fc GEMM is cut into: 1, or up to 3 when its 256x128 tile grid
+// leaves at least half the chip idle. Partial 0 goes to hidden_out rows [0, n); partials 1
+// and 2 to space the call writes only afterwards: hidden_out rows n+1 .. (the depth >= 1
+// copies) and embed_out, when each holds n x H floats. Each range must be a whole number of
+// 64-wide k steps.
+int fc_splits(const FuseArgs& a, int cus) {
+  const int tiles = (int)gemm::grid_tiles(a.n, a.H);
+  if (gemm::wide_width(a.n, a.H, a.aux_dim) != 0 || a.aux_dim % gemm::kDmaK != 0 ||
+      2 * tiles > cus)
+    return 1;
+  const size_t part = (size_t)a.n * a.H * sizeof(float);
+  const bool in_hidden = (int64_t)a.T - a.n - 1 >= a.n;
+  const bool in_embed = (size_t)a.T * a.H * sizeof(uint16_t) >= part;
+  const int nks = a.aux_dim / gemm::kDmaK;
+  int s = std::min(1 + (int)in_hidden + (int)in_embed, (cus + tiles - 1) / tiles);
+  while (s > 1 && nks % s != 0) --s;
+  return s;
+}
+
 // fc_norm: x[r] = x[r] / sqrt(mean(x[r]^2) + eps) * w in place; one wave per row.
 __global__ __launch_bounds__(256) void rms_inplace_kernel(float* __restrict__ x,
                                                           const uint16_t* __restrict__ w,
@@ -227,8 +269,36 @@ hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* au
                        uint16_t* embed_out, hipStream_t stream) {
   (void)idx;  // depth-0 row r is anchor r; depth >= 1 rows need no anchor
   hipError_t e;
-  if (gemm::wide_width(a.n, a.H, a.aux_dim) != 0 ||
-      a.aux_dim % (gemm::kStages * gemm::kDmaK) == 0) {
+  int cus = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int splits = fc_splits(a, cus);
+  if (splits > 1) {
+    // the reduction in `splits` ranges of K, one workgroup per (tile, range), then the
+    // partials summed in order into hidden_out rows [0, n)
+    float* p1 = hidden_out + (size_t)(a.n + 1) * a.H;
+    float* p2 = splits > 2 ? reinterpret_cast<float*>(embed_out) : nullptr;
+    const gemm::StoreF32Parts parts{{hidden_out, p1, p2 != nullptr ? p2 : p1}, a.H};
+    const int klen = a.aux_dim / splits;
+    const dim3 grid(gemm::grid_tiles(a.n, a.H) * splits);
+    if ((klen / gemm::kDmaK) % gemm::kStages == 0)
+      hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, gemm::StoreF32Parts, false, true>),
+                         grid, dim3(gemm::kThreads), 0, stream, aux, fc_weight, (int)a.n, a.H,
+                         klen, parts, a.aux_dim);
+    else
+      hipLaunchKernelGGL((gemm::dma_gemm_kernel<gemm::kDmaK, gemm::StoreF32Parts, true, true>),
+                         grid, dim3(gemm::kThreads), 0, stream, aux, fc_weight, (int)a.n, a.H,
+                         klen, parts, a.aux_dim);
+    const size_t count = (size_t)a.n * a.H / 4;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)std::min<size_t>((count + 255) / 256, 8192)),
+                       dim3(256), 0, stream, hidden_out, p1, p2, count);
+    if (a.T > a.n)
+      hipLaunchKernelGGL(fc_row_kernel, dim3((a.H + 3) / 4), dim3(256), 0, stream, mask_hidden,
+                         fc_weight, hidden_out + (size_t)a.n * a.H, a.H, a.aux_dim);
+  } else if (gemm::wide_width(a.n, a.H, a.aux_dim) != 0 ||
+             a.aux_dim % (gemm::kStages * gemm::kDmaK) == 0) {
     // depth-0 rows on a DMA-fed kernel, the mask row (first depth-1 row) on its own
     e = gemm::launch_dma_gemm(aux, fc_weight, (int)a.n, a.H, a.aux_dim,
                               gemm::StoreF32{hidden_out, a.H}, stream);

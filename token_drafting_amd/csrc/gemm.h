@@ -54,10 +54,12 @@ inline unsigned grid_tiles(int M, int N) {
   return (unsigned)(((N + BN - 1) / BN) * ((M + BM - 1) / BM));
 }
 
-template <int DK, typename Epi, bool kTail>
+// kSplitK: the reduction is cut into gridDim.x / tiles equal ranges of K columns (K is then
+// one range's length, lda the operands' row stride); range s goes to epilogue epi.part(s).
+template <int DK, typename Epi, bool kTail, bool kSplitK = false>
 __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __restrict__ A,
                                                             const uint16_t* __restrict__ W, int M,
-                                                            int N, int K, Epi epi) {
+                                                            int N, int K, Epi epi, int lda = 0) {
   constexpr int kABytes = BM * DK * 2, kBBytes = BN * DK * 2;
   constexpr int kADma = kABytes / 1024 / kWaves, kBDma = kBBytes / 1024 / kWaves;  // per wave
   static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "DMA split");
@@ -72,7 +74,13 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ntn = (N + BN - 1) / BN;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  // with a split, consecutive ids (one XCD) take the N tiles of one M block and K range
+  const int vt = xcd_tile(blockIdx.x, gridDim.x);
+  const int tiles = kSplitK ? ntn * ((M + BM - 1) / BM) : (int)gridDim.x;
+  const int tile = kSplitK ? vt % tiles : vt;
+  const int split = kSplitK ? vt / tiles : 0;
+  const int ld = kSplitK ? lda : K;
+  const size_t kbase = (size_t)split * K;  // first K column of this block's range
   const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
   const int r32 = lane & 31, half = lane >> 5;
 
@@ -82,17 +90,17 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
   for (int j = 0; j < kADma; ++j) {
     const int row = (wave + j * kWaves) * kRowsPerDma + lane / kChunks;
     const int g = (lane % kChunks) ^ dswz_key<DK>(row);
-    aoff[j] = (uint32_t)(((size_t)(min(m0 + row, M - 1) - m0) * K + g * 8) * 2);
+    aoff[j] = (uint32_t)(((size_t)(min(m0 + row, M - 1) - m0) * ld + g * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < kBDma; ++j) {
     const int row = (wave + j * kWaves) * kRowsPerDma + lane / kChunks;
     const int g = (lane % kChunks) ^ dswz_key<DK>(row);
-    boff[j] = (uint32_t)(((size_t)(min(n0 + row, N - 1) - n0) * K + g * 8) * 2);
+    boff[j] = (uint32_t)(((size_t)(min(n0 + row, N - 1) - n0) * ld + g * 8) * 2);
   }
   auto issue = [&](int ks, char* Ad, char* Bd) {
-    const char* ab = uniform_opaque(reinterpret_cast<const char*>(A + (size_t)m0 * K + (size_t)ks * DK));
-    const char* bb = uniform_opaque(reinterpret_cast<const char*>(W + (size_t)n0 * K + (size_t)ks * DK));
+    const char* ab = uniform_opaque(reinterpret_cast<const char*>(A + (size_t)m0 * ld + kbase + (size_t)ks * DK));
+    const char* bb = uniform_opaque(reinterpret_cast<const char*>(W + (size_t)n0 * ld + kbase + (size_t)ks * DK));
 #pragma unroll
     for (int j = 0; j < kADma; ++j) dma16(ab + lane_opaque(aoff[j]), Ad + (wave + j * kWaves) * 1024);
 #pragma unroll
@@ -171,6 +179,9 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
     // an epilogue that combines lanes gets the wave's whole 128x64 tile, all lanes active
     epi.wave_tile(acc, m0 + wm * 128, n0 + wn * 64, lane, M, N);
   } else {
+    const auto out = [&] {
+      if constexpr (kSplitK) return epi.part(split); else return epi;
+    }();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -180,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (row < M) epi(row, col, acc[i][j][r]);
+          if (row < M) out(row, col, acc[i][j][r]);
         }
       }
   }
@@ -343,6 +354,24 @@ hipError_t launch_dma_gemm(const uint16_t* A, const uint16_t* W, int M, int N, i
 // kWaveTile, once per wave with the wave's accumulators: acc[i][j] is the 32x32 MFMA tile
 // at rows row0 + 32 i, columns col0 + 32 j; lane l holds column l % 32 of it, rows
 // 8 (r / 4) + 4 (l / 32) + r % 4 in register r.
+
+// fp32 row-major stores of the K ranges of a split GEMM: range s into C[s] (up to 3).
+struct StoreF32Parts {
+  static constexpr bool kWaveTile = false;
+  float* C[3];
+  int N;
+  struct Part {
+    static constexpr bool kWaveTile = false;
+    float* C;
+    int N;
+    __device__ __forceinline__ void operator()(int row, int col, float v) const {
+      C[(size_t)row * N + col] = v;
+    }
+  };
+  __device__ __forceinline__ Part part(int s) const {
+    return Part{s == 0 ? C[0] : s == 1 ? C[1] : C[2], N};
+  }
+};
 
 // fp32 row-major store.
 struct StoreF32 {
