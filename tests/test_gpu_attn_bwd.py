@@ -130,6 +130,34 @@ def test_attention_bwd_mid_size_full(pe):
         _check_grad(got[name][:64], want[name][:64], f"{name} cfg{cfg_id} first 64 keys")
 
 
+@pytest.mark.parametrize("n,K,Hq,Hkv,D,lens", [(4096, 4, 4, 1, 256, None),
+                                               (3000, 4, 32, 8, 128, [1000, 1200, 800])])
+def test_attention_bwd_bit_reproducible(pe, n, K, Hq, Hkv, D, lens):
+    """Two calls on the same inputs give the same bits: dK and dV sum their query segments
+    in a fixed order (no atomics), dq and the depth >= 1 rows have one writer each."""
+    import torch
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32) if lens else \
+        np.array([0, n], dtype=np.int32)
+    seed = 51
+    dcu = to_dev(cu)
+    dsel = pe.cod_select(n, K, 0.7, 0.2, seed, dcu)
+    T = dsel["T"]
+    print(f"attention bwd repeat n={n} T={T} Hq={Hq} Hkv={Hkv} D={D}", flush=True)
+    qkv = synth.qkv_inputs(seed, T, Hq, Hkv, D)
+    dout = to_dev(synth.attn_grad_out(seed, T, Hq, D))
+    cos, sin = pe.rope_table(D, 1e4, pe.rope_max_pos(n, K))
+    q, k, v = to_dev(qkv["q"]), to_dev(qkv["k"]), to_dev(qkv["v"])
+    out, lse, _ = pe.draft_attn(n, K, dsel, dcu, q, k, v, cos, sin)
+    first = pe.draft_attn_bwd(n, K, dsel, dcu, q, k, v, cos, sin, out, lse, dout)[:3]
+    ws = torch.full((int(pe.lib().peagle_draft_attn_bwd_workspace_bytes(n, T, Hq, Hkv, D)),),
+                    0x7F, dtype=torch.uint8, device="cuda")
+    second = pe.draft_attn_bwd(n, K, dsel, dcu, q, k, v, cos, sin, out, lse, dout,
+                               workspace=ws)[:3]
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv"), first, second):
+        assert torch.equal(x, y), name
+
+
 @pytest.mark.parametrize("cfg_id", [4, 5])
 def test_attention_bwd_full_size_sampled(pe, cfg_id):
     """The full-size workloads in the launch the bench times: dq of sampled query rows;

@@ -109,6 +109,7 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
+  float* part;              // per-segment dK'^T, dV^T partials [nseg][2][n][Hkv][D]
   int n, T, S, Hq, Hkv, G, QR, ntiles;
   int nkb, seg_len;  // key blocks; query tiles per segment of a key block's range
   int64_t ntq;
@@ -263,11 +264,16 @@ __global__ __launch_bounds__(256) void qtile_kernel(const BwdParams p, uint16_t*
   }
 }
 
-// Zero fp32 x[0, count) (16 bytes per thread step).
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, size_t count4) {
-  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < count4;
-       t += (size_t)gridDim.x * blockDim.x)
-    *reinterpret_cast<floatx4*>(x + 4 * t) = floatx4{0.f, 0.f, 0.f, 0.f};
+// Query tiles [a, b) of one kv head's tile list that can see depth-0 keys [k0, k1]: the
+// slots of the anchors from k0 to the end of k1's sequence (all their depths and heads).
+__device__ __forceinline__ void key_block_tiles(const BwdParams& p, int k0, int k1, int64_t& a,
+                                                int64_t& b) {
+  const int s1 = min(max(upper_index(p.cu, p.S + 1, k1), 0), p.S - 1);
+  const int end = min(max(p.cu[s1 + 1], k1 + 1), p.n);
+  const int64_t e0 = min(max(p.qstart[k0], 0), p.T);
+  const int64_t e1 = min(max((int64_t)p.qstart[end], e0), (int64_t)p.T);
+  a = e0 * p.G / KT;
+  b = (e1 * p.G + KT - 1) / KT;
 }
 
 // dk' (WK) and / or dv (WV) of the depth-0 keys [k0, k0 + 128) of kv head g, from the
@@ -275,8 +281,9 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ x, size_t
 // Workgroups are ordered segment-major, so those running at the same time stream the same
 // few segments and the tiles come from HBM about once per segment (later blocks hit the
 // caches), instead of once per key block; and no workgroup takes more than seg_len tiles
-// (the first key blocks are seen by nearly every tile, the last by few). Segments add
-// into zeroed outputs with fp32 atomics.
+// (the first key blocks are seen by nearly every tile, the last by few). Each segment
+// stores its partial sums in its own slab of the workspace; dkdv_sum_kernel adds a key
+// block's segments in a fixed order, so the result does not depend on timing.
 //
 // v_mfma_f32_16x16x32_bf16 with 16 keys per wave and 8 waves: a lane holds the k' and v
 // fragments of one key for half of a 32-key wave's registers, so the pass keeps two waves
@@ -308,13 +315,9 @@ __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
   if (k0 >= p.n) return;
   const int k1 = min(k0 + kBwdKeys, p.n) - 1;
   if (tid == 0) {
-    // visible to: anchors from k0 to the end of k1's sequence (all their depths, heads)
-    const int s1 = min(max(upper_index(p.cu, p.S + 1, k1), 0), p.S - 1);
-    const int end = min(max(p.cu[s1 + 1], k1 + 1), p.n);
-    const int64_t e0 = min(max(p.qstart[k0], 0), p.T);
-    const int64_t e1 = min(max((int64_t)p.qstart[end], e0), (int64_t)p.T);
     // this block's tiles [a, b) within absolute segment seg of the tile list
-    const int64_t a = e0 * p.G / KT, b = (e1 * p.G + KT - 1) / KT;
+    int64_t a, b;
+    key_block_tiles(p, k0, k1, a, b);
     const int64_t ts = (int64_t)seg * p.seg_len;
     s_rng[0] = (int)std::max(a, ts);
     s_rng[1] = (int)std::min(b, ts + p.seg_len);
@@ -431,16 +434,50 @@ __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
   }
 
   if (key_on) {
-    float* dkr = p.dk + ((size_t)key * p.Hkv + g) * D;
-    float* dvr = p.dv + ((size_t)key * p.Hkv + g) * D;
+    const size_t plane = (size_t)p.n * p.Hkv * D;  // one of dK', dV of one segment
+    float* dkr = p.part + 2 * (size_t)seg * plane + ((size_t)key * p.Hkv + g) * D;
+    float* dvr = dkr + plane;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      const int d = 16 * mb + 4 * q4;
+      if constexpr (WK) *reinterpret_cast<floatx4*>(dkr + d) = dkt[mb];
+      if constexpr (WV) *reinterpret_cast<floatx4*>(dvr + d) = dvt[mb];
+    }
+  }
+}
+
+// dk' and dv of the depth-0 keys: the sum of the partials of the segments that hold tiles
+// seeing the key's block, in segment order; dk' takes the softmax scale. One thread per
+// (key, kv head, 4 of D).
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_sum_kernel(const BwdParams p) {
+  const size_t total = (size_t)p.n * p.Hkv * (D / 4);
+  const size_t plane = (size_t)p.n * p.Hkv * D;
+  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
+       t += (size_t)gridDim.x * blockDim.x) {
+    const int key = (int)(t / ((size_t)p.Hkv * (D / 4)));
+    const int k0 = key / kBwdKeys * kBwdKeys;
+    const int k1 = min(k0 + kBwdKeys, p.n) - 1;
+    int64_t a, b;
+    key_block_tiles(p, k0, k1, a, b);
+    floatx4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    if (a < b) {
+      const int s0 = (int)(a / p.seg_len), s1 = (int)((b - 1) / p.seg_len);
+      for (int sg = s0; sg <= s1; ++sg) {
+        const float* base = p.part + 2 * (size_t)sg * plane + 4 * t;
+        const floatx4 k = *reinterpret_cast<const floatx4*>(base);
+        const floatx4 v = *reinterpret_cast<const floatx4*>(base + plane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = 16 * mb + 4 * q4 + r;
-        if constexpr (WK) unsafeAtomicAdd(dkr + d, dkt[mb][r] * p.scale);
-        if constexpr (WV) unsafeAtomicAdd(dvr + d, dvt[mb][r]);
+        for (int e = 0; e < 4; ++e) {
+          sk[e] += k[e];
+          sv[e] += v[e];
+        }
       }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sk[e] *= p.scale;
+    *reinterpret_cast<floatx4*>(p.dk + 4 * t) = sk;
+    *reinterpret_cast<floatx4*>(p.dv + 4 * t) = sv;
   }
 }
 
@@ -776,6 +813,10 @@ AttnBwdLayout attn_bwd_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int
   L.dtr = off;   off += al256(tile_bytes);
   L.dtt = off;   off += al256(tile_bytes);
   L.smeta = off; off += al256((size_t)Hkv * L.ntq * KT * 16);
+  // absolute segments of the tile list: about 16 for large lists, 32 to 512 tiles each
+  L.seg_len = (int)std::min<int64_t>(512, std::max<int64_t>(32, (L.ntq + 15) / 16));
+  L.nseg = (int)((L.ntq + L.seg_len - 1) / L.seg_len);
+  L.part = off;  off += al256((size_t)L.nseg * 2 * n * Hkv * D * 4);
   L.total = off;
   return L;
 }
@@ -809,6 +850,7 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
+  p.part = reinterpret_cast<float*>(ws + L.part);
   p.n = a.n;
   p.T = a.T;
   p.S = a.S;
@@ -819,9 +861,8 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
   p.ntiles = (a.n + KT - 1) / KT;
   p.ntq = L.ntq;
   p.nkb = (a.n + kBwdKeys - 1) / kBwdKeys;
-  // absolute segments of the tile list: about 16 for large lists, 32 to 512 tiles each
-  p.seg_len = (int)std::min<int64_t>(512, std::max<int64_t>(32, (L.ntq + 15) / 16));
-  const int nseg = (int)((L.ntq + p.seg_len - 1) / p.seg_len);
+  p.seg_len = L.seg_len;
+  const int nseg = L.nseg;
   p.scale = a.scale;
   p.c_log2 = a.scale * kLog2e;
   uint16_t* dob = reinterpret_cast<uint16_t*>(ws + L.dob);
@@ -848,14 +889,13 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
                        const_cast<int4*>(p.smeta));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    {
-      const size_t count4 = (size_t)a.n * a.Hkv * D / 4;  // depth-0 rows of dk and dv
-      const unsigned zb = (unsigned)std::min<size_t>((count4 + 255) / 256, 65536);
-      hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, stream, dk, count4);
-      hipLaunchKernelGGL(zero_kernel, dim3(zb), dim3(256), 0, stream, dv, count4);
-    }
     const dim3 kgrid((unsigned)((int64_t)nkb * a.Hkv * nseg));
     hipLaunchKernelGGL((dkdv_kernel<D, true, true>), kgrid, dim3(kBwdThreads), 0, stream, p);
+    {
+      const size_t count4 = (size_t)a.n * a.Hkv * D / 4;  // depth-0 rows of dk and dv
+      const unsigned sb = (unsigned)std::min<size_t>((count4 + 255) / 256, 65536);
+      hipLaunchKernelGGL(dkdv_sum_kernel<D>, dim3(sb), dim3(256), 0, stream, p);
+    }
     if (a.T > a.n) {
       const int64_t waves = (int64_t)(a.T - a.n) * a.Hkv;
       hipLaunchKernelGGL(diag_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,

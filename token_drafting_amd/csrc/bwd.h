@@ -20,8 +20,10 @@ constexpr int kBwdKeys = 128;
 
 // The backward's own workspace regions, after the forward's (offsets from the start).
 struct AttnBwdLayout {
-  size_t fwd, dob, dlt, kt, vpad, qtr, qtt, dtr, dtt, smeta, total;
-  int64_t ntq;  // query tiles per kv head
+  size_t fwd, dob, dlt, kt, vpad, qtr, qtt, dtr, dtt, smeta, part, total;
+  int64_t ntq;   // query tiles per kv head
+  int seg_len;   // query tiles per segment of the key-major pass
+  int nseg;      // segments of the tile list
 };
 AttnBwdLayout attn_bwd_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D);
 
