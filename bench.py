@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--decode", choices=["all", "none", "only"], default="all",
                     help="also time the decode-shaped draft attention on its inference "
                          "workloads (all), skip it (none), or time only it (only)")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the step of the chosen workload (no draft layers, backward, "
+                         "loss or verification variants)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other four workloads and the depth sweep on the Llama-8B "
                          "shape")
@@ -57,7 +60,9 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_RECORDS = {4: "profiles/attn_core_gemma270m_32k_K4_traffic.md"}
+TRAFFIC_RECORDS = {4: "profiles/attn_core_gemma270m_32k_K4_traffic.md",
+                   5: "profiles/attn_core_llama8b_16k_K8_traffic.md",
+                   3: "profiles/attn_core_packed8_llama8b_4k_traffic.md"}
 DECODE_TRAFFIC_RECORD = "profiles/decode_attn_B64_ctx1k-32k_traffic.md"
 
 
@@ -147,6 +152,9 @@ def main():
     if "cpu_baseline" in head:
         result["cpu_baseline"] = head["cpu_baseline"]
 
+    if args.step_only:
+        print(json.dumps(result), flush=True)
+        return
     seed, n, K, T, H = args.config, cfg["n"], cfg["K"], head["config"]["draft_rows"], cfg["H"]
     d, sel, q, k, v = ctx["d"], ctx["sel"], ctx["q"], ctx["k"], ctx["v"]
     from token_drafting_amd import peagle
@@ -351,6 +359,10 @@ def step_bench(cfg_id, steps, warmup, cpu=True, cpu_rows=0, keep=False):
                 "accept_prefix": round(verify_bytes / (cold_ms["accept_prefix"] * 1e-3) / 1e9
                                        / PEAK_HBM_GBPS, 4)},
         },
+        "roofline": {"kernel": "attention core (the launches of one peagle_draft_attn_core call)",
+                     "bound": "mfma", "achieved": round(core_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(core_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_bytes(cfg_id)},
         "input_gen_s": round(gen_s, 1),
         "wall_s_timed": round(wall, 4),
     }

@@ -126,7 +126,9 @@ int peagle_cod_select_noalloc(int64_t n, int32_t K, double r, double r_min, uint
  *   hidden_out    fp32[T, H]   out
  *   embed_out     bf16[T, H]   out
  * aux_dim and H must be multiples of 8. ptd_token_id must lie in [0, vocab)
- * (required and range-checked, as in [N]'s recipe arguments).
+ * (required and range-checked, as in [N]'s recipe arguments). hidden_out and embed_out are
+ * written in full; before its final writes the call may keep partial sums of the fc
+ * reduction in them (their previous contents are ignored).
  */
 int peagle_fuse_inputs(int64_t n, int32_t K, int64_t T, const int32_t *idx,
                        const peagle_bf16 *aux, int32_t aux_dim, const peagle_bf16 *fc_weight,

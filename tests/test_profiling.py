@@ -29,8 +29,8 @@ def _write_run(folder, counter, rows):
 
 
 def test_traffic_record_scales_by_the_copy_and_sums_core_launches(tmp_path):
-    main = "void peagle::(anonymous namespace)::attn_core_kernel<256, false>(peagle::AttnParams)"
-    exact = "void peagle::(anonymous namespace)::attn_core_kernel<256, true>(peagle::AttnParams)"
+    main = "void peagle::(anonymous namespace)::attn_core_kernel<256, 0>(peagle::AttnParams)"
+    exact = "void peagle::(anonymous namespace)::attn_items_kernel(peagle::AttnParams)"
     # the 1 MiB copy reads as 512 KiB (128-byte requests counted as 64) and writes 1024 KiB
     _write_run(tmp_path / "f", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 512.0), (main, 100.0),
                                               (exact, 10.0), ("other_kernel", 7.0)])
@@ -111,12 +111,13 @@ def test_decode_calls_grouped_by_workload_runs():
 
 
 def test_core_call_bytes_take_each_kernel_total_per_call(tmp_path):
-    # two core calls: one main dispatch each, the exact kernel twice each (short chunks,
-    # then the redo pass); a call's bytes are each kernel's total over the calls
-    main = "void peagle::attn_core_kernel<256, false, false>(peagle::AttnParams)"
-    exact = "void peagle::attn_core_kernel<256, true, false>(peagle::AttnParams)"
-    rows = [("__amd_rocclr_copyBuffer", 512.0), (exact, 10.0), (main, 100.0), (exact, 2.0),
-            (exact, 10.0), (main, 100.0), (exact, 2.0)]
+    # two split core calls: work list, segments (role 1), merge and redo (role 2) each; a
+    # call's bytes are each kernel's total over the calls
+    main = "void peagle::attn_core_kernel<256, 1>(peagle::AttnParams)"
+    items = "void peagle::attn_items_kernel(peagle::AttnParams)"
+    redo = "void peagle::attn_core_kernel<256, 2>(peagle::AttnParams)"
+    rows = [("__amd_rocclr_copyBuffer", 512.0), (items, 10.0), (main, 100.0), (redo, 2.0),
+            (items, 10.0), (main, 100.0), (redo, 2.0)]
     _write_run(tmp_path / "f", "FETCH_SIZE", rows)
     _write_run(tmp_path / "w", "WRITE_SIZE", [(n, 2 * v if "copy" in n else v) for n, v in rows])
     rec = profiling.summarize(str(tmp_path / "f"), str(tmp_path / "w"), copy_mib=1)["record"]
@@ -126,12 +127,12 @@ def test_core_call_bytes_take_each_kernel_total_per_call(tmp_path):
 
 
 def test_trace_agreement_takes_each_core_call_wall_span(tmp_path):
-    # the short-chunk launch runs on a second stream and overlaps the main kernel: a call
-    # lasts from its first launch's start to its last launch's end, not the sum
+    # a call lasts from its first launch's start to its last launch's end: overlapping
+    # launches count once, not as the sum of their durations
     trace = tmp_path / "trace"
     os.makedirs(trace)
-    names = {"main": "void peagle::attn_core_kernel<256, false, false>(peagle::AttnParams)",
-             "short": "void peagle::attn_core_kernel<256, true, false>(peagle::AttnParams)",
+    names = {"main": "void peagle::attn_core_kernel<256, 1>(peagle::AttnParams)",
+             "short": "void peagle::attn_core_kernel<256, 2>(peagle::AttnParams)",
              "prep": "void peagle::rope_rotate_kernel<unsigned int>(int)",
              "acc": "void peagle::accept_kernel<unsigned int, false>(int)"}
     launches = []

@@ -86,9 +86,10 @@ def _calibration(rows, copy_bytes: int, counter: str) -> float:
 
 
 def _is_main_core(name: str) -> bool:
-    """attn_core_kernel<D, false, split>: the main kernel, one dispatch per core call."""
+    """attn_core_kernel<D, role> with role 0 (one launch for the whole call) or 1 (the split
+    path's segments): one such dispatch per core call."""
     m = re.match(r"attn_core_kernel<\s*\d+\s*,\s*(\w+)", name)
-    return bool(m) and m.group(1) == "false"
+    return bool(m) and m.group(1) in ("0", "1")
 
 
 def summarize(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
@@ -108,8 +109,8 @@ def summarize(fetch_dir: str, write_dir: str, copy_mib: int) -> dict:
             d[key + "_kib_raw"] = sum(v) / len(v)
             d[key + "_bytes"] = sum(v) / len(v) * fac
     core = {name: d for name, d in per_kernel.items() if any(k in name for k in CORE_KERNELS)}
-    # one main-kernel dispatch per core call; the exact kernel runs twice per call (short
-    # chunks, then the redo pass), so a call's bytes are each kernel's total over the calls
+    # one role-0 or role-1 dispatch per core call; a split call adds the work list, merge and
+    # redo launches, so a call's bytes are each kernel's total over the calls
     n_calls = max(1, sum(d["calls"] for name, d in core.items() if _is_main_core(name)))
 
     def per_call(key):
@@ -235,6 +236,9 @@ def write_summary(path: str, summary: dict, command: str) -> None:
 SIMDS = 256 * 4  # MI355X: 256 CUs x 4 SIMDs
 XCDS = 8
 MFMA_BF16_FLOP_PER_MOP = 512  # SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512-FLOP units
+MAX_ENGINE_GHZ = 2.4  # MI355X peak engine clock
+# runtime and torch kernels of a bench run (copies, fills, torch's random draws and scans)
+FOREIGN_KERNELS = ("copyBuffer", "fillBuffer", "rocprim::", "elementwise_kernel", "at::native")
 
 
 def kernel_table(mfma_dir: str, fetch_dir: str, write_dir: str, copy_mib: int) -> list:
@@ -259,7 +263,7 @@ def kernel_table(mfma_dir: str, fetch_dir: str, write_dir: str, copy_mib: int) -
             acc[v["name"]][key + "_dur"].append(v["dur_ns"])
     rows = []
     for name, a in acc.items():
-        if "copyBuffer" in name or name.startswith("at::") or not a["dur"]:
+        if not a["dur"] or any(x in name for x in FOREIGN_KERNELS) or name.startswith("at::"):
             continue
         mean = lambda x: sum(x) / len(x) if x else 0.0
         dur = mean(a["dur"]) * 1e-9
@@ -288,8 +292,13 @@ def write_kernel_table(path: str, rows: list, title: str, command: str) -> None:
              "| kernel | calls | us | bf16 TFLOP/s | MFMA busy | clock GHz | read MB | written MB | HBM GB/s |",
              "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
+        # a derived clock above the engine's maximum means the counter window was wider than
+        # the dispatch: its MFMA-busy denominator is then inflated, so the share is withheld
+        ok = r["clock_ghz"] <= MAX_ENGINE_GHZ
+        busy = f"{100 * r['mfma_busy']:.1f}%" if ok else "n/a"
+        clock = f"{r['clock_ghz']:.2f}" if ok else f"({r['clock_ghz']:.2f}, window > dispatch)"
         lines.append(f"| `{r['kernel']}` | {r['calls']} | {r['us']:.1f} | {r['bf16_tflops']:.1f} | "
-                     f"{100 * r['mfma_busy']:.1f}% | {r['clock_ghz']:.2f} | {r['read_mb']:.2f} | "
+                     f"{busy} | {clock} | {r['read_mb']:.2f} | "
                      f"{r['write_mb']:.2f} | {r['hbm_gbps']:.0f} |")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
