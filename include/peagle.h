@@ -83,9 +83,10 @@ int peagle_cod_counts(int64_t n, int32_t K, double r, double r_min, int64_t *m, 
  *   workspace     >= peagle_cod_workspace_bytes(n, K) bytes of device memory, 256-byte
  *                 aligned (per-depth thresholds and per-block kept counts); its contents
  *                 are scratch and need no initialisation
- * Requires n < 2^31 and T as given by peagle_cod_counts. Work is O(n K): one workgroup
- * hashes the buffer twice for the thresholds and once for per-block counts, then one
- * workgroup per 1024 positions compacts its block.
+ * Requires n < 2^31 and T as given by peagle_cod_counts. Work is O(n K) in two launches:
+ * up to n = 65536 a hash pass and a select pass, each a workgroup per 1024 positions;
+ * beyond, one workgroup finds the thresholds and per-block counts, then a workgroup per
+ * 1024 positions compacts its block.
  */
 size_t peagle_cod_workspace_bytes(int64_t n, int32_t K); /* 0 on bad arguments */
 int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t seed,
@@ -101,7 +102,8 @@ int peagle_cod_select(int64_t n, int32_t K, double r, double r_min, uint64_t see
  * PEAGLE_COD_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until the process
  * ends; the call allocates and frees nothing. The first call on a device looks up the
  * array's address there (hipGetSymbolAddress). Limit: peagle_cod_workspace_bytes(n, K) must
- * not exceed PEAGLE_COD_NOALLOC_SCRATCH_BYTES (e.g. n <= 33.5M at K = 8), else
+ * not exceed PEAGLE_COD_NOALLOC_SCRATCH_BYTES (every n up to 65536; then e.g. n <= 33.5M at
+ * K = 8), else
  * PEAGLE_ERR_WORKSPACE and nothing is enqueued. All calls on one GPU share the array: calls
  * that may overlap on that GPU (other streams, other threads) race and must be ordered by
  * the caller. The scratch needs no clearing: every call writes what it reads.

@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
   __shared__ uint64_t thr[kMaxDepths];
   __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths];
   __shared__ int32_t cbase[kMaxDepths + 1], cfill[kMaxDepths];
+  __shared__ int8_t bin_depth[kBins];  // the depth whose candidate bin this is, -1, or -2 (several)
   __shared__ int32_t sh[kWaves];
   __shared__ uint64_t s_prefix;
   __shared__ int32_t s_rank, s_count;
@@ -136,7 +137,6 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
   // readlane inside the loops, instead of indexing the kernel arguments there.
   auto bcast = [](int v, int d) { return __builtin_amdgcn_readlane(v, d); };
   const int m_v = lane < K ? a.m[lane] : 0;
-  const bool own_v = lane < K && own_search(a, lane);
 
   // 1. thresholds: keep p at depth d iff hash(p) <= thr[d] (m_d == 0 keeps nothing).
   //    One histogram of the top 12 hash bits serves every depth: its prefix sums give the
@@ -187,12 +187,23 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
   __syncthreads();
   if (cbase[K] <= kCand) {
     // one pass gathers every depth's candidates, then each candidate ranks itself inside
-    // its depth's region (the region's hashes are distinct: exactly one has the rank)
-    const int bin_v = own_v ? bin_of[lane] : -1;
+    // its depth's region (the region's hashes are distinct: exactly one has the rank). A
+    // byte map of the bins tells a position in one lookup whether it is a candidate.
+    for (int b = tid; b < kBins; b += kThreads) bin_depth[b] = -1;
+    __syncthreads();
+    if (tid == 0)
+      for (int d = 0; d < K; ++d)
+        if (own_search(a, d)) bin_depth[bin_of[d]] = bin_depth[bin_of[d]] == -1 ? (int8_t)d : (int8_t)-2;
+    __syncthreads();
     for (int p = tid; p < n; p += kThreads) {
       const int t = (int)(top32(p) >> (32 - kBinBits));
-      for (int d = 0; d < K; ++d)
-        if (t == bcast(bin_v, d)) cand[cbase[d] + atomicAdd(&cfill[d], 1)] = hash_of(p);
+      const int bd = bin_depth[t];
+      if (bd >= 0) {
+        cand[cbase[bd] + atomicAdd(&cfill[bd], 1)] = hash_of(p);
+      } else if (bd == -2) {  // a bin shared by several depths
+        for (int d = 0; d < K; ++d)
+          if (own_search(a, d) && bin_of[d] == t) cand[cbase[d] + atomicAdd(&cfill[d], 1)] = hash_of(p);
+      }
     }
     __syncthreads();
     for (int i = tid; i < cbase[K]; i += kThreads) {
@@ -238,30 +249,40 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
   __syncthreads();
 
   // 2. kept positions of every depth in each block of kThreads positions: a wave per
-  //    block, one ballot per depth and 64 positions; lane d carries depth d's count. The
-  //    full hash is needed only where the top 32 bits tie a threshold's. The counts go to
-  //    LDS (the histogram's space, no longer needed) when they fit, else to before_out.
+  //    block holds the block's top hash bits in registers and, depth after depth (each
+  //    threshold a wave-uniform value), counts them with one ballot per 64 positions;
+  //    the full hash is needed only where the top 32 bits tie the threshold's. The counts
+  //    go to LDS (the histogram's space, no longer needed) when they fit, else to
+  //    before_out.
   const int nb = (n + kThreads - 1) / kThreads;
   const bool in_lds = nb * K <= kBins;
   int32_t* const cnt = in_lds ? reinterpret_cast<int32_t*>(hist) : before_out;
-  const uint32_t thr_hi_v = lane < K ? (uint32_t)(thr[lane] >> 32) : 0u;
-  const uint32_t thr_lo_v = lane < K ? (uint32_t)thr[lane] : 0u;
+  constexpr int kPer = kThreads / kWave;  // positions of a block per lane
   for (int b = wave; b < nb; b += kWaves) {
-    int c = 0;
-    for (int j = 0; j < kThreads; j += kWave) {
-      const int p = b * kThreads + j + lane;
-      const bool inside = p < n;
-      const uint32_t t = inside ? top32(p) : 0u;
-      for (int d = 0; d < K; ++d) {
-        const uint32_t th = (uint32_t)bcast((int)thr_hi_v, d);
-        bool keep = inside && bcast(m_v, d) > 0 && t <= th;
-        if (keep && t == th)
-          keep = (uint32_t)hash_of(p) <= (uint32_t)bcast((int)thr_lo_v, d);
-        const uint64_t ball = __ballot(keep);
-        if (lane == d) c += __popcll(ball);
-      }
+    uint32_t t[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = b * kThreads + j * kWave + lane;
+      t[j] = p < n ? top32(p) : 0xFFFFFFFFu;
     }
-    if (lane < K) cnt[(size_t)b * K + lane] = c;
+    for (int d = 0; d < K; ++d) {
+      int c = 0;
+      if (a.m[d] > 0) {
+        const uint64_t th = thr[d];
+        const uint32_t hi = (uint32_t)(th >> 32);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int p = b * kThreads + j * kWave + lane;
+          // positions past n carry top bits of all ones: they reach the tie branch at most,
+          // which rejects them
+          bool keep = t[j] <= hi;
+          if (__ballot(t[j] == hi) != 0ull && t[j] == hi)  // rare: compare the low bits
+            keep = p < n && hash_of(p) <= th;
+          c += __popcll(__ballot(keep));
+        }
+      }
+      if (lane == 0) cnt[(size_t)b * K + d] = c;
+    }
   }
   __syncthreads();
   // exclusive prefix over the blocks, per depth, into before_out
@@ -279,30 +300,24 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
   if (tid < K) thr_out[tid] = thr[tid];
 }
 
-__global__ __launch_bounds__(kThreads) void cod_compact_kernel(
-    CodArgs a, const int32_t* __restrict__ cu, const uint64_t* __restrict__ thr_in,
-    const int32_t* __restrict__ before_in, int32_t* __restrict__ idx,
-    int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
-  __shared__ uint64_t thr[kMaxDepths];
-  __shared__ uint64_t wmask[kMaxDepths][kWaves];
-  __shared__ int32_t before_blk[kMaxDepths];
+// Steps 3-4 for the block [base, base + kThreads), given every depth's threshold and this
+// block's exclusive prefix of kept positions (LDS), and this thread's hash h:
+//   3. ordered compaction with wave ballots: a lane's rank inside its wave, the wave masks in
+//      LDS give the rank inside the block (coalesced idx / row_of);
+//   4. kept anchors of depth d before each sequence start that falls in this block (the
+//      last block also owns cu = n).
+__device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu,
+                              const uint64_t* thr, const int32_t* before_blk,
+                              uint64_t (*wmask)[kWaves], uint64_t h, int32_t* __restrict__ idx,
+                              int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d,
+                              int32_t* __restrict__ row_of) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int n = a.n, K = a.K;
   const int base = blockIdx.x * kThreads;
-  if (tid < K) {
-    thr[tid] = thr_in[tid];
-    before_blk[tid] = before_in[(size_t)blockIdx.x * K + tid];
-  }
-  __syncthreads();
-
-  // 3. ordered compaction of the block [base, base + 1024): a wave ballot per depth gives
-  //    each lane its rank inside the wave, the wave masks in LDS give the rank inside
-  //    the block.
   const int p = base + tid;
   const bool inside = p < n;
-  const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
   for (int d = 0; d < K; ++d) {
     const bool keep = inside && a.m[d] > 0 && h <= thr[d];
     const uint64_t ball = __ballot(keep);
@@ -319,9 +334,6 @@ __global__ __launch_bounds__(kThreads) void cod_compact_kernel(
       if (keep && r < a.off[d + 1]) idx[r] = p;
     }
   }
-
-  // 4. kept anchors of depth d before each sequence start that falls in this block (the
-  //    last block also owns cu = n).
   for (int t = tid; t < K * (a.S + 1); t += kThreads) {
     const int d = t / (a.S + 1), s = t % (a.S + 1);
     const int x = cu[s];
@@ -341,23 +353,271 @@ __global__ __launch_bounds__(kThreads) void cod_compact_kernel(
   if (blockIdx.x == 0 && tid <= K) depth_off[tid] = a.off[tid];
 }
 
+__global__ __launch_bounds__(kThreads) void cod_compact_kernel(
+    CodArgs a, const int32_t* __restrict__ cu, const uint64_t* __restrict__ thr_in,
+    const int32_t* __restrict__ before_in, int32_t* __restrict__ idx,
+    int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
+  __shared__ uint64_t thr[kMaxDepths];
+  __shared__ uint64_t wmask[kMaxDepths][kWaves];
+  __shared__ int32_t before_blk[kMaxDepths];
+  const int tid = threadIdx.x;
+  if (tid < a.K) {
+    thr[tid] = thr_in[tid];
+    before_blk[tid] = before_in[(size_t)blockIdx.x * a.K + tid];
+  }
+  __syncthreads();
+  const int p = blockIdx.x * kThreads + tid;
+  compact_block(a, cu, thr, before_blk, wmask, splitmix64(a.seed ^ (uint64_t)p), idx, depth_off,
+                cu_d, row_of);
+}
+
+// ---- one-pass path for buffers of at most kSmallBlocks blocks ----
+// cod_hash_kernel: a workgroup per block stores its positions' hashes and the histogram of
+// their top 8 bits. cod_select_small_kernel: every workgroup rebuilds, from those, the
+// global histogram, each depth's bin and rank, the candidates and thresholds (the same in
+// every workgroup: a few hundred hashes per depth at these sizes), and its own prefix of
+// kept positions, then compacts its block. Two launches, no single-workgroup stage.
+constexpr int kSmallBlocks = 64;
+constexpr int kCoarseBins = 256;
+constexpr int kPool = 4096;  // candidate hashes held at once
+
+__global__ __launch_bounds__(kThreads) void cod_hash_kernel(CodArgs a, uint64_t* __restrict__ hashes,
+                                                           uint32_t* __restrict__ bhist) {
+  __shared__ uint32_t h8[kCoarseBins];
+  const int tid = threadIdx.x, p = blockIdx.x * kThreads + tid;
+  if (tid < kCoarseBins) h8[tid] = 0;
+  __syncthreads();
+  if (p < a.n) {
+    const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
+    hashes[p] = h;
+    atomicAdd(&h8[h >> 56], 1u);
+  }
+  __syncthreads();
+  if (tid < kCoarseBins) bhist[(size_t)blockIdx.x * kCoarseBins + tid] = h8[tid];
+}
+
+__global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
+    CodArgs a, const int32_t* __restrict__ cu, const uint64_t* __restrict__ hashes,
+    const uint32_t* __restrict__ bhist, int32_t* __restrict__ idx, int32_t* __restrict__ depth_off,
+    int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
+  __shared__ uint32_t ghist[kCoarseBins];  // all blocks
+  __shared__ uint32_t phist[kCoarseBins];  // the blocks before this one
+  __shared__ uint64_t cand[kPool];
+  __shared__ int32_t cpos[kPool];
+  __shared__ uint64_t thr[kMaxDepths];
+  __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths], below[kMaxDepths];
+  __shared__ int32_t cbase[kMaxDepths + 1], cfill[kMaxDepths];
+  __shared__ int32_t before_blk[kMaxDepths], kept_cnt[kMaxDepths];
+  __shared__ int8_t bin_depth[kCoarseBins];
+  __shared__ uint64_t wmask[kMaxDepths][kWaves];
+  __shared__ int32_t sh[kWaves];
+  __shared__ uint64_t s_prefix;
+  __shared__ int32_t s_rank;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int n = a.n, K = a.K, nb = gridDim.x, blk = blockIdx.x;
+  const int base = blk * kThreads;
+  constexpr int kParts = kThreads / kCoarseBins;  // threads per bin for the sums
+
+  // global histogram of the top 8 bits, and that of the blocks before this one: each bin
+  // summed by kParts threads over interleaved blocks
+  if (tid < kCoarseBins) {
+    ghist[tid] = 0;
+    phist[tid] = 0;
+    bin_depth[tid] = -1;
+  }
+  if (tid < kMaxDepths) kept_cnt[tid] = 0;
+  __syncthreads();
+  {
+    const int x = tid % kCoarseBins, part = tid / kCoarseBins;
+    constexpr int kPerPart = kSmallBlocks / kParts;  // all of a thread's loads in flight at once
+    uint32_t v[kPerPart];
+#pragma unroll
+    for (int i = 0; i < kPerPart; ++i) {
+      const int j = part + i * kParts;
+      v[i] = j < nb ? bhist[(size_t)j * kCoarseBins + x] : 0u;
+    }
+    uint32_t all = 0, pre = 0;
+#pragma unroll
+    for (int i = 0; i < kPerPart; ++i) {
+      all += v[i];
+      pre += part + i * kParts < blk ? v[i] : 0u;
+    }
+    atomicAdd(&ghist[x], all);
+    atomicAdd(&phist[x], pre);
+  }
+  __syncthreads();
+  // inclusive prefix sums of both histograms over the bins, by wave 0 (4 bins per lane)
+  if (tid < kWave) {
+    uint32_t g[4], q[4], gs = 0, qs = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      g[i] = ghist[4 * lane + i];
+      q[i] = phist[4 * lane + i];
+      gs += g[i];
+      qs += q[i];
+    }
+    uint32_t gx = gs, qx = qs;  // inclusive scan over the lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t gy = __shfl_up(gx, o, kWave), qy = __shfl_up(qx, o, kWave);
+      if (lane >= o) {
+        gx += gy;
+        qx += qy;
+      }
+    }
+    gx -= gs;
+    qx -= qs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gx += g[i];
+      qx += q[i];
+      ghist[4 * lane + i] = gx;  // now inclusive prefixes
+      phist[4 * lane + i] = qx;
+    }
+  }
+  __syncthreads();
+  // depth d: the bin holding the m_d-th smallest hash (prefix before < m_d <= prefix through
+  // it), the rank inside it, and the positions before this block in the bins below it (all
+  // kept at depth d)
+  if (tid < kCoarseBins) {
+    const uint32_t gin = ghist[tid], gex = tid > 0 ? ghist[tid - 1] : 0u;
+    const uint32_t pex = tid > 0 ? phist[tid - 1] : 0u;
+    for (int d = 0; d < K; ++d) {
+      const uint32_t m = (uint32_t)a.m[d];
+      if (m > gex && m <= gin) {
+        bin_of[d] = tid;
+        rank_in_bin[d] = (int)(m - gex);
+        below[d] = (int)pex;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int c = 0;
+    for (int d = 0; d < K; ++d) {
+      cbase[d] = c;
+      cfill[d] = 0;
+      if (own_search(a, d)) {
+        c += (int)(ghist[bin_of[d]] - (bin_of[d] > 0 ? ghist[bin_of[d] - 1] : 0u));
+        bin_depth[bin_of[d]] = bin_depth[bin_of[d]] == -1 ? (int8_t)d : (int8_t)-2;
+      }
+    }
+    cbase[K] = c;
+  }
+  __syncthreads();
+  if (cbase[K] <= kPool) {
+    // candidates of every depth with its own search, with their positions; the hashes are
+    // loaded sixteen at a time before any is examined
+    constexpr int kBatch = 16;
+    for (int p0 = tid; p0 < n; p0 += kBatch * kThreads) {
+      uint64_t hb[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int p = p0 + i * kThreads;
+        hb[i] = p < n ? hashes[p] : 0ull;
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int p = p0 + i * kThreads;
+        if (p >= n) break;
+        const uint64_t h = hb[i];
+        const int t = (int)(h >> 56);
+        const int bd = bin_depth[t];
+        if (bd >= 0) {
+          const int slot = cbase[bd] + atomicAdd(&cfill[bd], 1);
+          cand[slot] = h;
+          cpos[slot] = p;
+        } else if (bd == -2) {  // a bin shared by several depths
+          for (int d = 0; d < K; ++d)
+            if (own_search(a, d) && bin_of[d] == t) {
+              const int slot = cbase[d] + atomicAdd(&cfill[d], 1);
+              cand[slot] = h;
+              cpos[slot] = p;
+            }
+        }
+      }
+    }
+    __syncthreads();
+    // each candidate ranks itself inside its depth's region (distinct hashes: one match)
+    for (int i = tid; i < cbase[K]; i += kThreads) {
+      int d = 0;
+      while (cbase[d + 1] <= i) ++d;
+      const uint64_t h = cand[i];
+      int smaller = 0;
+      for (int j = cbase[d]; j < cbase[d + 1]; ++j) smaller += cand[j] < h;
+      if (smaller == rank_in_bin[d] - 1) thr[d] = h;
+    }
+    __syncthreads();
+    // kept positions before this block: those in the bins below, and the candidates of the
+    // depth's bin before the block that do not exceed its threshold
+    for (int i = tid; i < cbase[K]; i += kThreads) {
+      int d = 0;
+      while (cbase[d + 1] <= i) ++d;
+      if (cpos[i] < base && cand[i] <= thr[d]) atomicAdd(&kept_cnt[d], 1);
+    }
+    __syncthreads();
+    if (tid < K && own_search(a, tid)) before_blk[tid] = below[tid] + kept_cnt[tid];
+  } else {
+    // a bin too full for the pool (not expected at these sizes): radix select over every
+    // hash, then count the kept positions before the block
+    for (int d = 0; d < K; ++d) {
+      if (!own_search(a, d)) continue;
+      const uint64_t t = radix_select(a, a.m[d], reinterpret_cast<uint32_t*>(cand), &s_prefix, &s_rank);
+      int c = 0;
+      for (int p = tid; p < base; p += kThreads) c += hashes[p] <= t;
+      int total;
+      (void)block_scan_excl(c, sh, &total);
+      if (tid == 0) {
+        thr[d] = t;
+        before_blk[d] = total;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  if (tid == 0)
+    for (int d = 0; d < K; ++d) {
+      if (own_search(a, d)) continue;
+      const bool all = a.m[d] >= n || d == 0, none = a.m[d] == 0;
+      thr[d] = (all || none) ? ~0ull : thr[d - 1];
+      before_blk[d] = none ? 0 : all ? base : before_blk[d - 1];
+    }
+  __syncthreads();
+  const int p = base + tid;
+  compact_block(a, cu, thr, before_blk, wmask, p < n ? hashes[p] : 0ull, idx, depth_off, cu_d,
+                row_of);
+}
+
 }  // namespace
 
-// Workspace: the kMaxDepths thresholds, then the [blocks][K] exclusive prefixes.
+// Workspace: up to kSmallBlocks blocks, the n hashes then the per-block histograms of the
+// one-pass path; else the kMaxDepths thresholds, then the [blocks][K] exclusive prefixes.
 size_t cod_workspace_bytes(int64_t n, int32_t K) {
   const size_t nb = (size_t)((n + kThreads - 1) / kThreads);
-  const size_t bytes = (size_t)kMaxDepths * sizeof(uint64_t) + nb * (size_t)K * sizeof(int32_t);
+  const size_t bytes = nb <= (size_t)kSmallBlocks
+                           ? (size_t)n * sizeof(uint64_t) + nb * kCoarseBins * sizeof(uint32_t)
+                           : (size_t)kMaxDepths * sizeof(uint64_t) + nb * (size_t)K * sizeof(int32_t);
   return (bytes + 255) & ~(size_t)255;
 }
 
 hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_t* idx,
                              int32_t* depth_off, int32_t* cu_seqlens_d, int32_t* row_of,
                              void* workspace, hipStream_t stream) {
+  const int nb = (a.n + kThreads - 1) / kThreads;
+  if (nb <= kSmallBlocks) {
+    uint64_t* hashes = static_cast<uint64_t*>(workspace);
+    uint32_t* bhist = reinterpret_cast<uint32_t*>(hashes + a.n);
+    hipLaunchKernelGGL(cod_hash_kernel, dim3(nb), dim3(kThreads), 0, stream, a, hashes, bhist);
+    hipLaunchKernelGGL(cod_select_small_kernel, dim3(nb), dim3(kThreads), 0, stream, a, cu_seqlens,
+                       hashes, bhist, idx, depth_off, cu_seqlens_d, row_of);
+    return hipGetLastError();
+  }
   uint64_t* thr = static_cast<uint64_t*>(workspace);
   int32_t* before = reinterpret_cast<int32_t*>(thr + kMaxDepths);
   hipLaunchKernelGGL(cod_threshold_kernel, dim3(1), dim3(kThreads), 0, stream, a, thr, before);
-  hipLaunchKernelGGL(cod_compact_kernel, dim3((a.n + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     stream, a, cu_seqlens, thr, before, idx, depth_off, cu_seqlens_d, row_of);
+  hipLaunchKernelGGL(cod_compact_kernel, dim3(nb), dim3(kThreads), 0, stream, a, cu_seqlens, thr,
+                     before, idx, depth_off, cu_seqlens_d, row_of);
   return hipGetLastError();
 }
 
