@@ -510,8 +510,9 @@ size_t peagle_draft_decode_workspace_bytes(int32_t num_reqs, int32_t K, int32_t 
 
 /*
  * peagle_draft_decode_attn -- the decode-shaped draft attention. Split-KV: the cache
- * tiles of each (request, kv head) are shared out among several waves whose partial
- * softmax states a second kernel merges (both enqueued on `stream`).
+ * tiles of all requests are cut into equal ranges, one workgroup per CU, and a last
+ * kernel merges the partial softmax states a range leaves for each request it touches
+ * (three launches, all enqueued on `stream`; nothing is allocated or synchronized).
  *   cu_ctx         int32[B+1]          as for peagle_decode_pack_v
  *   total_ctx      (host) cu_ctx[B];   max_ctx (host) >= every L_b
  *   k_cache        bf16[total_ctx, Hkv, D]   rotated keys

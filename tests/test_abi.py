@@ -233,6 +233,56 @@ def test_decode_tile_bases_never_overlap():
                 prev_end = end
 
 
+def test_decode_range_split_covers_each_request_once():
+    """The decode attention's work split, as host arithmetic (no GPU): request b takes
+    max(1, ceil(L_b / 32)) slots from rstart[b]; range r of P takes slots [r len,
+    (r + 1) len) with len = ceil(S / P), starting at the request that holds slot r len;
+    each (range, request) pair it meets writes partial slot r + b. Checked: every slot of
+    every request is taken by exactly one range, partial slots are unique and below
+    P + B, and a request's partials are exactly slots r + b for r = s_b / len ..
+    (e_b - 1) / len, the list the merge reads."""
+    rng = np.random.default_rng(11)
+    for trial in range(1500):
+        B = int(rng.integers(1, 300))
+        lens = rng.integers(0, int(rng.choice([2, 40, 1000, 40000])), B)
+        if trial % 9 == 0:
+            lens[:] = 0
+        nt = np.maximum(1, (lens + 31) // 32)
+        rstart = np.concatenate([[0], np.cumsum(nt)]).astype(np.int64)
+        S = int(rstart[-1])
+        assert S <= int(lens.sum()) // 32 + B          # the bound the workspace is sized by
+        P = int(rng.integers(1, 1100))
+        ln = (S + P - 1) // P
+        rfirst = {}
+        for b in range(B):                              # each request writes its ranges
+            for r in range((int(rstart[b]) + ln - 1) // ln, (int(rstart[b + 1]) + ln - 1) // ln):
+                assert r not in rfirst
+                rfirst[r] = b
+        taken = {b: [] for b in range(B)}
+        slots = set()
+        for r in range(P):
+            t0 = r * ln
+            if t0 >= S:
+                continue
+            t1 = min(t0 + ln, S)
+            b = rfirst[r]
+            while b < B and rstart[b] < t1:
+                j0, j1 = max(t0, rstart[b]) - rstart[b], min(t1, rstart[b + 1]) - rstart[b]
+                assert j0 < j1
+                slot = r + b
+                assert slot not in slots and slot < P + B
+                slots.add(slot)
+                taken[b].append((j0, j1, slot))
+                b += 1
+        for b in range(B):
+            segs = sorted(taken[b])
+            assert [j for s in segs for j in s[:2]][0] == 0
+            assert all(segs[i][1] == segs[i + 1][0] for i in range(len(segs) - 1))
+            assert segs[-1][1] == nt[b]
+            r0, r1 = int(rstart[b]) // ln, (int(rstart[b + 1]) - 1) // ln
+            assert sorted(s[2] for s in segs) == [r + b for r in range(r0, r1 + 1)]
+
+
 def test_layer1_argument_errors(lib):
     base = dict(n=64, K=4, T=150, H=640, eps=1e-6, Hq=4, Hkv=1, D=256, ws=1 << 30)
 

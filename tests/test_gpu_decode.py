@@ -49,6 +49,9 @@ DECODE_SMALL = [
     ([4097, 1, 2222], 5, 12, 3, 128, 5e5),                 # odd K, G = 4, ragged groups
     ([130, 2000, 47], 4, 16, 4, 256, 1e4),                 # four kv heads a workgroup
     ([600, 33, 1200], 12, 8, 4, 64, 1e4),                  # same, 32 columns a wave
+    # more tile slots than ranges: ranges of several tiles that cross request boundaries
+    ([20000, 3, 9000, 40, 0, 12000], 4, 4, 1, 64, 1e4),
+    ([9000, 7, 16000, 2, 31], 8, 32, 8, 128, 5e5),
 ]
 
 
@@ -71,7 +74,9 @@ def test_decode_small_full(pe, case):
 @pytest.mark.parametrize("name", sorted(synth.DECODE_CONFIGS))
 def test_decode_full_size_sampled(pe, name):
     """The inference workload at full size, in the launch the bench times; the oracle
-    recomputes every output of a few requests (shortest, longest, seeded others)."""
+    recomputes every output of several requests (first, last, shortest, longest, seeded
+    others; at this size every request spans several ranges and shares one with a
+    neighbour)."""
     cfg = synth.DECODE_CONFIGS[name]
     seed = 31
     lens = synth.decode_lengths(seed, cfg["B"], cfg["ctx_lo"], cfg["ctx_hi"])
@@ -80,8 +85,8 @@ def test_decode_full_size_sampled(pe, name):
     inp = synth.decode_inputs_device(seed, lens, K, Hq, Hkv, D)
     out, lse = _run(pe, inp, lens, K, D, cfg["theta"], device_inputs=True)
     rng = np.random.default_rng(seed)
-    picks = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
-                    *rng.integers(0, cfg["B"], size=2).tolist()})
+    picks = sorted({0, cfg["B"] - 1, int(np.argmin(lens)), int(np.argmax(lens)),
+                    *rng.integers(0, cfg["B"], size=4).tolist()})
     cu = to_host(inp["cu_ctx"]).astype(np.int64)
     for b in picks:
         sl = slice(int(cu[b]), int(cu[b + 1]))

@@ -747,6 +747,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnParams p) {
   }
 }
 
+}  // namespace
+
 constexpr int kMaxDevices = 64;
 
 // Compute units of the current device, cached per device (every thread that fills an
@@ -763,8 +765,6 @@ int device_cus() {
   }
   return c;
 }
-
-}  // namespace
 
 hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, float* lse,
                             const char* ws, hipStream_t stream) {

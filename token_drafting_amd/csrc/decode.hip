@@ -21,20 +21,25 @@
 // Kernels (all on the caller's stream):
 //   decode_prep     one thread per rotation pair or element: q rotated at L_b + d, the new
 //                   rows' keys rotated at L_b + e as one extra 32-key tile per (request, kv
-//                   head) (zero rows past K), and their values as that tile's V^T.
-//   decode_attn     split-KV: a workgroup owns (request, kv head, column group, a slice
-//                   of the cache tiles); its four waves take the slice's tiles in turn.
-//                   A wave holds 16 or 32 query columns (column c of a kv head: q head
-//                   g*G + c / K, depth c % K) and computes S^T = K Q^T and O^T = V^T P^T
-//                   on v_mfma_f32_16x16x32_bf16 with an online softmax in base 2 (scale
-//                   folded into one FMA) that rescales only when the running max grows by
-//                   more than 2^8; the weights enter PV as a hi + lo bf16 pair. The first
-//                   wave of each request's first slice also takes the new rows' tile. The
-//                   waves merge through LDS and the workgroup writes one partial
-//                   (O, max, sum).
-//   decode_combine  merges the partials of each (request, kv head, column group).
-// The path is HBM-bound: every cache byte is read once. Nothing before a workgroup's first
-// tile loads waits on memory but the request bounds, so its start costs one round trip.
+//                   head) (zero rows past K), and their values as that tile's V^T. Its last
+//                   workgroup lays out the work split (below).
+//   decode_attn     split-KV over a compact tile space: request b takes nt_b =
+//                   max(1, ceil(L_b / 32)) consecutive tile slots (one at least, for its new
+//                   rows), and the space is cut into P equal ranges, one per workgroup and
+//                   (kv head group, column group), P sized so that every workgroup is
+//                   resident at once. A range may cross request boundaries: it leaves one
+//                   partial (O, max, sum) per request it touches, in slot range + request,
+//                   which no other (range, request) pair shares since both are ordered.
+//                   Every workgroup streams the same number of cache bytes, so the launch
+//                   ends without a tail of late workgroups. A wave holds 16 or 32 query
+//                   columns (column c of a kv head: q head g*G + c / K, depth c % K) and
+//                   computes S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with
+//                   an online softmax in base 2 (scale folded into one FMA) that rescales
+//                   only when the running max grows by more than 2^8; the weights enter PV
+//                   as a hi + lo bf16 pair. The range holding a request's first slot also
+//                   takes its new rows' tile.
+//   decode_combine  merges the partials of each (request, kv head, column).
+// The path is HBM-bound: every cache byte is read once.
 #include <algorithm>
 
 #include "common.h"
@@ -48,6 +53,9 @@ namespace {
 constexpr int kDecWaves = 4;  // waves per workgroup
 constexpr int kDecTile = 32;  // keys per tile
 constexpr float kDecRescaleLog2 = 8.f;
+// Bound on the workgroups of one launch that the workspace provides partials for; the
+// launch takes one workgroup per CU.
+constexpr int kDecMaxWorkgroups = 1024;
 
 // 16x16x32 bf16 MFMA: D[16x16] += A[16x32] * B[32x16]. Lane l supplies row l%16 of A and
 // column l%16 of B, 8 values each at the same k positions for both operands; it
@@ -70,9 +78,12 @@ struct DecodeParams {
   const uint16_t* qr;    // rotated q [B, K, Hq, D]
   const uint16_t* knew;  // rotated new keys [B, Hkv, 32, D], zero rows past K
   const uint16_t* vnew;  // new values as a V^T tile [B, Hkv, D, 32]
-  float* part_o;       // [B, Hkv, NCg, NPW, PC, D]
-  float* part_ml;      // [B, Hkv, NCg, NPW, PC, 2]: max (base 2) and sum
-  int B, K, Hq, Hkv, G, GK, NCg, NPW, tpw, max_ctx;
+  const int32_t* rstart;  // [B + 1] first tile slot of each request, then the total S
+  const int32_t* rfirst;  // [P] request holding the first slot of each range
+  const int32_t* rlen;    // tile slots per range
+  float* part_o;       // [P + B, Hkv, NCg, PC, D]
+  float* part_ml;      // [P + B, Hkv, NCg, PC, 2]: max (base 2) and sum
+  int B, K, Hq, Hkv, G, GK, NCg, max_ctx;
   int64_t total_ctx, ntiles;
   float c_log2;
 };
@@ -117,15 +128,67 @@ __device__ __forceinline__ void rope8(const uint16_t* src, uint16_t* dst, int j0
   *reinterpret_cast<bf16x8*>(dst + j0 + H) = hi;
 }
 
+// Tile slots of request b: max(1, ceil(L_b / 32)).
+__device__ __forceinline__ int request_slots(const int32_t* cu, const int32_t* lens, int b,
+                                             int64_t total_ctx, int max_ctx) {
+  int64_t c0;
+  int L;
+  request_extent(cu, lens, b, total_ctx, max_ctx, c0, L);
+  return std::max(1, (L + kDecTile - 1) / kDecTile);
+}
+
+// The work split, by one workgroup of 256 threads: rstart[b] = sum of the slots of the
+// requests before b (rstart[B] = S), len = ceil(S / P) slots per range, and rfirst[r] = the
+// request holding slot r len, for every range with r len < S (the others hold nothing).
+// Thread i takes ceil(B / 256) consecutive requests; their totals are scanned in LDS.
+__device__ void decode_ranges(const int32_t* __restrict__ cu, const int32_t* __restrict__ lens,
+                              int B, int64_t total_ctx, int max_ctx, int P,
+                              int32_t* __restrict__ rstart, int32_t* __restrict__ rfirst,
+                              int32_t* __restrict__ rlen) {
+  __shared__ int scan[256];
+  const int tid = threadIdx.x;
+  const int per = (B + 255) / 256;
+  const int lo = std::min(tid * per, B), hi = std::min(lo + per, B);
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) sum += request_slots(cu, lens, b, total_ctx, max_ctx);
+  scan[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int S = scan[255];  // >= B >= 1
+  const int len = (S + P - 1) / P;
+  int run = scan[tid] - sum;
+  for (int b = lo; b < hi; ++b) {
+    const int end = run + request_slots(cu, lens, b, total_ctx, max_ctx);
+    rstart[b] = run;
+    // ranges whose first slot lies in [run, end)
+    for (int r = (run + len - 1) / len; (int64_t)r * len < end; ++r) rfirst[r] = b;
+    run = end;
+  }
+  if (tid == 0) {
+    rstart[B] = S;
+    *rlen = len;
+  }
+}
+
 // Flat grid, 8 outputs per thread, over three ranges: q (B K Hq rows, D/16 threads a row),
 // new keys (B Hkv 32 rows, D/16 threads a row), new V^T (B Hkv D rows of 32 slots, 4
-// threads a row).
+// threads a row); one more workgroup, the last, lays out the work split.
 __global__ __launch_bounds__(256) void decode_prep_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ lens,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ cs, const float* __restrict__ sn,
     uint16_t* __restrict__ qr, uint16_t* __restrict__ knew, uint16_t* __restrict__ vnew, int B,
-    int K, int Hq, int Hkv, int D, int max_ctx, int max_pos, int64_t total_ctx) {
+    int K, int Hq, int Hkv, int D, int max_ctx, int max_pos, int64_t total_ctx, int P,
+    int32_t* __restrict__ rstart, int32_t* __restrict__ rfirst, int32_t* __restrict__ rlen) {
+  if (blockIdx.x == gridDim.x - 1) {
+    decode_ranges(cu, lens, B, total_ctx, max_ctx, P, rstart, rfirst, rlen);
+    return;
+  }
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int H = D / 2, per_row = D / 16;
   const int64_t nq = (int64_t)B * K * Hq * per_row, nk = (int64_t)B * Hkv * kDecTile * per_row;
@@ -238,43 +301,52 @@ __device__ __forceinline__ void decode_tile_math(DecodeWave<D, NCW>& w,
   }
 }
 
-// One cache tile: rows [0, rows) of kbase (row stride kstride elements) and its V^T tile.
-template <int D, int NCW>
-__device__ __forceinline__ void decode_cache_tile(DecodeWave<D, NCW>& w, const uint16_t* kbase,
-                                                  size_t kstride, int rows,
-                                                  const uint16_t* vtile, float c_log2, int l16,
-                                                  int grp) {
+// One cache tile in registers: kf[h] the A fragments of keys 16 h .. 16 h + 15, vf the V^T
+// fragments.
+template <int D>
+struct CacheTile {
+  bf16x8 kf[2][D / 32];
+  bf16x8 vf[D / 16];
+};
+
+// Issue the loads of one cache tile: rows [0, rows) of kbase (row stride kstride elements;
+// rows past the end repeat the last one and are masked) and its V^T tile. Every cache byte
+// is read once per call, so the loads are nontemporal: they stream past the caches instead
+// of evicting lines that are still wanted (measured 8% faster).
+template <int D, bool kIssueAll>
+__device__ __forceinline__ void load_cache_tile(CacheTile<D>& t, const uint16_t* kbase,
+                                                size_t kstride, int rows,
+                                                const uint16_t* vtile, int l16, int grp) {
   constexpr int DK = D / 32, MT = D / 16;
-  bf16x8 kf[2][DK];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int row = std::min(16 * h + l16, rows - 1);
     const uint16_t* kp = kbase + (size_t)row * kstride + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk)
-      kf[h][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kp + 32 * kk));
+      t.kf[h][kk] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * kk)));
   }
-  bf16x8 vf[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    vf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp));
-  // every load of the tile is issued before the first wait on any of them: one memory
-  // round trip per tile instead of one for K and then one for V
-  __builtin_amdgcn_sched_barrier(0);
-  int lim[NCW];
-#pragma unroll
-  for (int c = 0; c < NCW; ++c) lim[c] = rows;
-  decode_tile_math<D, NCW>(w, kf, vf, lim, c_log2, grp);
+    t.vf[mt] = as_bf16x8(__builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp)));
+  // kIssueAll: every load of the tile is issued before the first wait on any of them, one
+  // memory round trip per tile instead of one for K and then one for V (without this
+  // barrier the compiler sinks the V loads below the scores under register pressure: 18%
+  // slower). With a second tile in flight the compiler's own order measured 1.5% faster.
+  if constexpr (kIssueAll) __builtin_amdgcn_sched_barrier(0);
 }
 
-// Work split. A workgroup job is (request b, slice of tpw cache tiles, column group, group
-// of HEADS kv heads), the head group fastest. HEADS = 4 (Hkv a multiple of 4): wave w
-// takes kv head 4 gg + w and the whole slice, so the four waves read neighbouring head
-// segments of the same cache rows, and each wave writes its partial. HEADS = 1: the four
-// waves take the slice's tiles in turn (neighbouring tiles at the same time) and merge
-// through LDS into one partial.
+// Work split. A workgroup job is (range r of the tile slots, column group, group of HEADS
+// kv heads), the head group fastest. HEADS = 4 (Hkv a multiple of 4): wave w takes kv head
+// 4 gg + w and every tile of the range, so the four waves read neighbouring head segments
+// of the same cache rows, and each wave writes its partials. HEADS = 1: the four waves take
+// the tiles of each request segment in turn (neighbouring tiles at the same time) and merge
+// through LDS into one partial per segment. Segment bounds are uniform over the workgroup,
+// so every barrier is reached by all waves.
 template <int D, int NCW, int HEADS>
-__global__ __launch_bounds__(64 * kDecWaves, 2) void decode_attn_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * kDecWaves, HEADS == 1 ? 1 : 2) void decode_attn_kernel(
+    const DecodeParams p) {
   constexpr int DK = D / 32, MT = D / 16, PC = 16 * NCW;
   constexpr bool kMerge = HEADS == 1;
   constexpr int kRedWaves = kMerge ? kDecWaves : 1;
@@ -285,196 +357,216 @@ __global__ __launch_bounds__(64 * kDecWaves, 2) void decode_attn_kernel(const De
   const int K = p.K, Hkv = p.Hkv;
   const int ngg = Hkv / HEADS;
   const int gg = (int)(blockIdx.x % ngg);
-  const int64_t r1 = blockIdx.x / ngg;
-  const int cg = (int)(r1 % p.NCg);
-  const int64_t r2 = r1 / p.NCg;
-  const int slice = (int)(r2 % p.NPW);
-  const int b = (int)(r2 / p.NPW);
+  const int r1 = (int)(blockIdx.x / ngg);
+  const int cg = r1 % p.NCg;
+  const int r = r1 / p.NCg;
   const int g = HEADS == 1 ? gg : gg * HEADS + wave;
-  int64_t c0;
-  int L;
-  request_extent(p.cu, p.lens, b, p.total_ctx, p.max_ctx, c0, L);
-  const int ntiles_b = (L + kDecTile - 1) / kDecTile;
-  // slices past the request's end hold nothing and write no partial (slice 0 always holds
-  // the new rows' tile); the test is uniform over the workgroup, before any barrier
-  if (slice > 0 && slice * p.tpw >= ntiles_b) return;
+  const int len = *p.rlen, S = p.rstart[p.B];
+  const int t0 = r * len;
+  if (t0 >= S) return;  // uniform: ranges past the last slot hold nothing
+  const int t1 = std::min(t0 + len, S);
 
-  DecodeWave<D, NCW> w;
-  int dcol[NCW];
-#pragma unroll
-  for (int c = 0; c < NCW; ++c) {
-    const int col = std::min((cg * NCW + c) * 16 + l16, p.GK - 1);
-    const int d = col % K, head = g * p.G + col / K;
-    dcol[c] = d;
-    const uint16_t* qrow = p.qr + (((size_t)b * K + d) * p.Hq + head) * D + 8 * grp;
-#pragma unroll
-    for (int kk = 0; kk < DK; ++kk)
-      w.qf[c][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * kk));
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) w.o[c][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    w.m_run[c] = -INFINITY;
-    w.l_run[c] = 0.f;
-  }
+  for (int b = p.rfirst[r]; b < p.B; ++b) {
+    const int sb = p.rstart[b];
+    if (sb >= t1) break;
+    const int eb = p.rstart[b + 1];
+    int64_t c0;
+    int L;
+    request_extent(p.cu, p.lens, b, p.total_ctx, p.max_ctx, c0, L);
+    const int j0 = std::max(t0, sb) - sb, j1 = std::min(t1, eb) - sb;  // tiles of b here
 
-  // the new rows' tile (laid out by decode_prep): row d keeps new keys e <= d
-  if (slice == 0 && (HEADS > 1 || wave == 0)) {
-    const size_t bg = (size_t)b * Hkv + g;
-    const uint16_t* kbase = p.knew + bg * kDecTile * D;
-    const uint16_t* vtile = p.vnew + bg * D * kDecTile;
-    bf16x8 kf[2][DK];
+    DecodeWave<D, NCW> w;
+    int dcol[NCW];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int c = 0; c < NCW; ++c) {
+      const int col = std::min((cg * NCW + c) * 16 + l16, p.GK - 1);
+      const int d = col % K, head = g * p.G + col / K;
+      dcol[c] = d;
+      const uint16_t* qrow = p.qr + (((size_t)b * K + d) * p.Hq + head) * D + 8 * grp;
 #pragma unroll
       for (int kk = 0; kk < DK; ++kk)
-        kf[h][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + (16 * h + l16) * D + 32 * kk + 8 * grp));
-    bf16x8 vf[MT];
+        w.qf[c][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * kk));
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      vf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp));
-    int lim[NCW];
-#pragma unroll
-    for (int c = 0; c < NCW; ++c) lim[c] = dcol[c] + 1;
-    decode_tile_math<D, NCW>(w, kf, vf, lim, p.c_log2, grp);
-  }
-  // the slice's cache tiles
-  const int t_end = std::min((slice + 1) * p.tpw, ntiles_b);
-  const uint16_t* vbase = p.vt + (((size_t)g * p.ntiles + (c0 >> 5) + b) * D) * kDecTile;
-  const int t_step = HEADS == 1 ? kDecWaves : 1;
-  for (int t = slice * p.tpw + (HEADS == 1 ? wave : 0); t < t_end; t += t_step) {
-    const int key0 = t * kDecTile;
-    decode_cache_tile<D, NCW>(w, p.kc + ((size_t)(c0 + key0) * Hkv + g) * D, (size_t)Hkv * D,
-                              L - key0, vbase + (size_t)t * D * kDecTile, p.c_log2, l16, grp);
-  }
+      for (int mt = 0; mt < MT; ++mt) w.o[c][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      w.m_run[c] = -INFINITY;
+      w.l_run[c] = 0.f;
+    }
 
-  const size_t part = (((size_t)b * Hkv + g) * p.NCg + cg) * p.NPW + slice;
-  if constexpr (!kMerge) {
-    // the wave's partial: O^T columns (the lane holds dims 16 mt + 4 grp + r of column
-    // l16), running max and sum
+    // the new rows' tile (laid out by decode_prep), with the request's first slot: row d
+    // keeps new keys e <= d
+    if (j0 == 0 && (HEADS > 1 || wave == 0)) {
+      const size_t bg = (size_t)b * Hkv + g;
+      const uint16_t* kbase = p.knew + bg * kDecTile * D;
+      const uint16_t* vtile = p.vnew + bg * D * kDecTile;
+      bf16x8 kf[2][DK];
 #pragma unroll
-    for (int c = 0; c < NCW; ++c) {
-      float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
-      lt += __shfl_xor(lt, 32, 64);
-      float* po = p.part_o + (part * PC + c * 16 + l16) * D;
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        *reinterpret_cast<floatx4*>(po + 16 * mt + 4 * grp) = w.o[c][mt];
-      if (grp == 0) {
-        p.part_ml[(part * PC + c * 16 + l16) * 2] = w.m_run[c];
-        p.part_ml[(part * PC + c * 16 + l16) * 2 + 1] = lt;
-      }
-    }
-  } else {
-    // merge the four waves through LDS; the workgroup writes one partial
-#pragma unroll
-    for (int c = 0; c < NCW; ++c) {
-      float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
-      lt += __shfl_xor(lt, 32, 64);
+        for (int kk = 0; kk < DK; ++kk)
+          kf[h][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + (16 * h + l16) * D + 32 * kk + 8 * grp));
+      bf16x8 vf[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        *reinterpret_cast<floatx4*>(&red_o[wave][c * 16 + l16][16 * mt + 4 * grp]) = w.o[c][mt];
-      if (grp == 0) {
-        red_ml[wave][c * 16 + l16][0] = w.m_run[c];
-        red_ml[wave][c * 16 + l16][1] = lt;
+        vf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp));
+      int lim[NCW];
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) lim[c] = dcol[c] + 1;
+      decode_tile_math<D, NCW>(w, kf, vf, lim, p.c_log2, grp);
+    }
+    // the segment's cache tiles (a request with no context has one slot and no tile)
+    const int j_end = std::min(j1, (L + kDecTile - 1) / kDecTile);
+    const uint16_t* vbase = p.vt + (((size_t)g * p.ntiles + (c0 >> 5) + b) * D) * kDecTile;
+    // HEADS = 1: two tiles in registers, the loads of the next tile in flight while this
+    // one is computed (one wave per SIMD leaves the registers for it; measured 7% faster at
+    // D = 256). HEADS = 4 keeps one tile a wave: four waves of one CU already stream four
+    // heads of the same keys, and the second buffer measured 1.5% slower there.
+    const int j_step = HEADS == 1 ? kDecWaves : 1;
+    const int j_first = j0 + (HEADS == 1 ? wave : 0);
+    auto issue = [&](CacheTile<D>& t, int j) {
+      const int key0 = j * kDecTile;
+      load_cache_tile<D, HEADS != 1>(t, p.kc + ((size_t)(c0 + key0) * Hkv + g) * D,
+                                     (size_t)Hkv * D, L - key0,
+                                     vbase + (size_t)j * D * kDecTile, l16, grp);
+    };
+    auto compute = [&](const CacheTile<D>& t, int j) {
+      int lim[NCW];
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) lim[c] = L - j * kDecTile;
+      decode_tile_math<D, NCW>(w, t.kf, t.vf, lim, p.c_log2, grp);
+    };
+    if constexpr (HEADS != 1) {
+      for (int j = j_first; j < j_end; ++j) {
+        CacheTile<D> t;
+        issue(t, j);
+        compute(t, j);
+      }
+    } else if (j_first < j_end) {
+      CacheTile<D> ta, tb;
+      issue(ta, j_first);
+      for (int j = j_first; j < j_end; j += 2 * j_step) {
+        const int jn = j + j_step;
+        if (jn < j_end) issue(tb, jn);
+        compute(ta, j);
+        if (jn >= j_end) break;
+        if (jn + j_step < j_end) issue(ta, jn + j_step);
+        compute(tb, jn);
       }
     }
-    __syncthreads();
-    for (int t = threadIdx.x; t < PC * (D / 4); t += 64 * kDecWaves) {
-      const int col = t / (D / 4), d4 = (t % (D / 4)) * 4;
-      float M = -INFINITY;
+
+    const size_t part = ((size_t)(r + b) * Hkv + g) * p.NCg + cg;
+    if constexpr (!kMerge) {
+      // the wave's partial: O^T columns (the lane holds dims 16 mt + 4 grp + r of column
+      // l16), running max and sum
 #pragma unroll
-      for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, red_ml[q][col][0]);
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      float lsum = 0.f;
+      for (int c = 0; c < NCW; ++c) {
+        float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        float* po = p.part_o + (part * PC + c * 16 + l16) * D;
 #pragma unroll
-      for (int q = 0; q < kDecWaves; ++q) {
-        const float mq = red_ml[q][col][0];
-        const float f = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
-        acc += f * *reinterpret_cast<const floatx4*>(&red_o[q][col][d4]);
-        lsum += f * red_ml[q][col][1];
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<floatx4*>(po + 16 * mt + 4 * grp) = w.o[c][mt];
+        if (grp == 0) {
+          p.part_ml[(part * PC + c * 16 + l16) * 2] = w.m_run[c];
+          p.part_ml[(part * PC + c * 16 + l16) * 2 + 1] = lt;
+        }
       }
-      *reinterpret_cast<floatx4*>(p.part_o + (part * PC + col) * D + d4) = acc;
-      if (d4 == 0) {
-        p.part_ml[(part * PC + col) * 2] = M;
-        p.part_ml[(part * PC + col) * 2 + 1] = lsum;
+    } else {
+      // merge the four waves through LDS; the workgroup writes one partial
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) {
+        float lt = w.l_run[c] + __shfl_xor(w.l_run[c], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<floatx4*>(&red_o[wave][c * 16 + l16][16 * mt + 4 * grp]) = w.o[c][mt];
+        if (grp == 0) {
+          red_ml[wave][c * 16 + l16][0] = w.m_run[c];
+          red_ml[wave][c * 16 + l16][1] = lt;
+        }
       }
+      __syncthreads();
+      for (int t = threadIdx.x; t < PC * (D / 4); t += 64 * kDecWaves) {
+        const int col = t / (D / 4), d4 = (t % (D / 4)) * 4;
+        float M = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, red_ml[q][col][0]);
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        float lsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < kDecWaves; ++q) {
+          const float mq = red_ml[q][col][0];
+          const float f = mq == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+          acc += f * *reinterpret_cast<const floatx4*>(&red_o[q][col][d4]);
+          lsum += f * red_ml[q][col][1];
+        }
+        *reinterpret_cast<floatx4*>(p.part_o + (part * PC + col) * D + d4) = acc;
+        if (d4 == 0) {
+          p.part_ml[(part * PC + col) * 2] = M;
+          p.part_ml[(part * PC + col) * 2 + 1] = lsum;
+        }
+      }
+      __syncthreads();  // the LDS is written again by the next segment
     }
   }
 }
 
-// Merge the NPW partials of each (request, kv head, column group): out = sum_p 2^(m_p - M)
-// O_p / sum_p 2^(m_p - M) l_p and lse = (M + log2 of that sum) ln 2, M the largest m_p.
-// Eight lanes share one output (column, 4 dims): lane r takes partials r, r + 8, ..., all
-// loads in flight together, and the eight running states merge by shuffles.
-constexpr int kCombLanes = 8;
+// Merge the partials of each (request, kv head, column): request b's slots [s_b, e_b)
+// meet ranges r0 = s_b / len .. (e_b - 1) / len, whose partials sit in slots r + b.
+// out = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r and lse = (M + log2 of that sum) ln 2,
+// M the largest m_r. One thread per output (column, 4 dims), dims fastest: a wave reads whole
+// partial rows; up to 8 partials are loaded before any is used.
 __global__ __launch_bounds__(256) void decode_combine_kernel(
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ lens, const float* __restrict__ part_o,
-    const float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse, int K,
-    int Hq, int Hkv, int G, int GK, int NCg, int NPW, int PC, int D, int tpw, int max_ctx,
-    int64_t total_ctx, int64_t n) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t o = t / kCombLanes;
-  const int r = (int)(t % kCombLanes);
-  if (o >= n) return;  // n outputs: the eight lanes of an output leave together
+    const int32_t* __restrict__ rstart, const int32_t* __restrict__ rlen,
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, float* __restrict__ out,
+    float* __restrict__ lse, int K, int Hq, int Hkv, int G, int GK, int NCg, int PC, int D,
+    int64_t n) {
+  const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= n) return;
   const int per_col = D / 4;
   const int d4 = (int)(o % per_col) * 4;
   const int c = (int)((o / per_col) % PC);
-  const int64_t item = o / ((int64_t)per_col * PC);
+  const int64_t item = o / ((int64_t)per_col * PC);  // (b, g, cg)
   const int cg = (int)(item % NCg);
   const int col = cg * PC + c;
   if (col >= GK) return;
   const int64_t bg = item / NCg;
   const int b = (int)(bg / Hkv), g = (int)(bg % Hkv);
-  const size_t base = (size_t)item * NPW;
-  // only the slices that held cache tiles (and slice 0) wrote a partial
-  int64_t c0;
-  int L;
-  request_extent(cu, lens, b, total_ctx, max_ctx, c0, L);
-  const int nparts = std::min(NPW, std::max(1, ((L + kDecTile - 1) / kDecTile + tpw - 1) / tpw));
+  const int len = *rlen, sb = rstart[b], eb = rstart[b + 1];
+  const int r0 = sb / len, nparts = (eb - 1) / len - r0 + 1;
+  const size_t slot_stride = (size_t)Hkv * NCg;  // partial units per slot
+  const size_t base = ((size_t)(r0 + b) * Hkv + g) * NCg + cg;
   float M = -INFINITY, lsum = 0.f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  // up to 8 partials per lane per round, all loaded before any is used
-  for (int q0 = r; q0 < nparts; q0 += 8 * kCombLanes) {
+  for (int q0 = 0; q0 < nparts; q0 += 8) {
     float mq[8], lq[8];
     floatx4 oq[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int q = std::min(q0 + i * kCombLanes, nparts - 1);
-      mq[i] = part_ml[((base + q) * PC + c) * 2];
-      lq[i] = part_ml[((base + q) * PC + c) * 2 + 1];
-      oq[i] = *reinterpret_cast<const floatx4*>(part_o + ((base + q) * PC + c) * D + d4);
+      mq[i] = -INFINITY;
+      lq[i] = 0.f;
+      oq[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (q0 + i < nparts) {  // uniform over the threads of one (request, head, column)
+        const size_t u = (base + (size_t)(q0 + i) * slot_stride) * PC + c;
+        mq[i] = part_ml[u * 2];
+        lq[i] = part_ml[u * 2 + 1];
+        oq[i] = *reinterpret_cast<const floatx4*>(part_o + u * D + d4);
+      }
     }
     float Mr = M;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (q0 + i * kCombLanes < nparts) Mr = fmaxf(Mr, mq[i]);
+    for (int i = 0; i < 8; ++i) Mr = fmaxf(Mr, mq[i]);
     if (Mr == -INFINITY) continue;
     const float fa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mr);
     acc *= fa;
     lsum *= fa;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bool use = q0 + i * kCombLanes < nparts && mq[i] != -INFINITY;
-      const float f = use ? __builtin_amdgcn_exp2f(mq[i] - Mr) : 0.f;
+      const float f = mq[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq[i] - Mr);
       acc += f * oq[i];
       lsum += f * lq[i];
     }
     M = Mr;
   }
-#pragma unroll
-  for (int sh = 1; sh < kCombLanes; sh <<= 1) {
-    const float Mo = __shfl_xor(M, sh, 64);
-    const float lo = __shfl_xor(lsum, sh, 64);
-    floatx4 ao;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ao[e] = __shfl_xor(acc[e], sh, 64);
-    const float Mn = fmaxf(M, Mo);
-    const float fa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-    const float fb = Mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mo - Mn);
-    acc = fa * acc + fb * ao;
-    lsum = fa * lsum + fb * lo;
-    M = Mn;
-  }
-  if (r != 0) return;
   const int d = col % K, head = g * G + col / K;
   *reinterpret_cast<floatx4*>(out + (((size_t)b * K + d) * Hq + head) * D + d4) = acc / lsum;
   if (lse != nullptr && d4 == 0)
@@ -526,19 +618,22 @@ hipError_t for_dim(int D, F&& f) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct DecodeLayout {
-  size_t qr, knew, vnew, part_o, part_ml, total;
+  size_t qr, knew, vnew, part_o, part_ml, rstart, rfirst, rlen, total;
 };
 
 DecodeLayout decode_layout(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                            const DecodePlan& pl) {
   DecodeLayout l;
-  const size_t parts = (size_t)B * Hkv * pl.ncg * pl.npw * pl.pc;
+  const size_t parts = (size_t)pl.nslots * Hkv * pl.ncg * pl.pc;
   l.qr = 0;
   l.knew = l.qr + align256((size_t)B * K * Hq * D * 2);
   l.vnew = l.knew + align256((size_t)B * Hkv * kDecTile * D * 2);
   l.part_o = l.vnew + align256((size_t)B * Hkv * D * kDecTile * 2);
   l.part_ml = l.part_o + align256(parts * D * 4);
-  l.total = l.part_ml + align256(parts * 2 * 4);
+  l.rstart = l.part_ml + align256(parts * 2 * 4);
+  l.rfirst = l.rstart + align256(((size_t)B + 1) * 4);
+  l.rlen = l.rfirst + align256((size_t)pl.max_ranges * 4);
+  l.total = l.rlen + 256;
   return l;
 }
 
@@ -605,25 +700,23 @@ int64_t decode_ntiles(int64_t total_ctx, int32_t B) { return (total_ctx >> 5) + 
 
 DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                        int64_t total_ctx, int32_t max_ctx) {
+  (void)max_ctx;
   DecodePlan pl;
   const int gk = (Hq / Hkv) * K;
   // two column groups per wave where the registers allow it (D <= 128)
   pl.ncw = (D <= 128 && gk > 16) ? 2 : 1;
   pl.pc = 16 * pl.ncw;
   pl.ncg = (gk + pl.pc - 1) / pl.pc;
-  const int tiles_max = (max_ctx + kDecTile - 1) / kDecTile;
-  // Four kv heads per workgroup where Hkv allows it; otherwise the waves share a slice.
+  // Four kv heads per workgroup where Hkv allows it; otherwise the waves share a range.
   pl.heads = Hkv % 4 == 0 ? 4 : 1;
-  // Fixed-size slices of a request's tiles. With four heads per workgroup a slice is one
-  // wave's: about 4096 waves with work (two rounds at two waves per SIMD), 8 to 64 tiles
-  // so that the wave's partial stays a few percent of its cache bytes. With shared
-  // slices: about 1024 workgroups with work, 16 to 32 tiles (one partial per workgroup).
-  const int64_t tile_items = ((total_ctx >> 5) + B) * Hkv * pl.ncg;
-  if (pl.heads == 4)
-    pl.tpw = (int)std::min<int64_t>(std::max<int64_t>((tile_items + 4095) / 4096, 8), 64);
-  else
-    pl.tpw = (int)std::min<int64_t>(std::max<int64_t>((tile_items + 1023) / 1024, 16), 32);
-  pl.npw = std::max(1, (tiles_max + pl.tpw - 1) / pl.tpw);
+  pl.wg_per_range = pl.ncg * (Hkv / pl.heads);
+  // The launch picks the range count for the device (every workgroup resident at once);
+  // the workspace holds up to kDecMaxWorkgroups workgroups' worth, and no more ranges than
+  // the (total_ctx / 32 + B bounded) tile slots.
+  const int64_t slots_max = (total_ctx >> 5) + B;
+  pl.max_ranges = (int)std::max<int64_t>(
+      1, std::min<int64_t>(slots_max, std::max(1, kDecMaxWorkgroups / pl.wg_per_range)));
+  pl.nslots = pl.max_ranges + B;
   return pl;
 }
 
@@ -658,6 +751,7 @@ hipError_t launch_decode_attn(const DecodeArgs& a, const int32_t* cu, const uint
   return launch_decode_attn_lens(a, cu, nullptr, kc, vt, qn, kn, vn, cs, sn, out, lse, ws, stream);
 }
 
+
 hipError_t launch_decode_attn_lens(const DecodeArgs& a, const int32_t* cu, const int32_t* lens,
                                    const uint16_t* kc, const uint16_t* vt, const uint16_t* qn,
                                    const uint16_t* kn, const uint16_t* vn, const float* cs,
@@ -673,6 +767,9 @@ hipError_t launch_decode_attn_lens(const DecodeArgs& a, const int32_t* cu, const
   p.qr = reinterpret_cast<const uint16_t*>(ws + lay.qr);
   p.knew = reinterpret_cast<const uint16_t*>(ws + lay.knew);
   p.vnew = reinterpret_cast<const uint16_t*>(ws + lay.vnew);
+  p.rstart = reinterpret_cast<const int32_t*>(ws + lay.rstart);
+  p.rfirst = reinterpret_cast<const int32_t*>(ws + lay.rfirst);
+  p.rlen = reinterpret_cast<const int32_t*>(ws + lay.rlen);
   p.part_o = reinterpret_cast<float*>(ws + lay.part_o);
   p.part_ml = reinterpret_cast<float*>(ws + lay.part_ml);
   p.B = a.B;
@@ -682,43 +779,49 @@ hipError_t launch_decode_attn_lens(const DecodeArgs& a, const int32_t* cu, const
   p.G = a.Hq / a.Hkv;
   p.GK = p.G * a.K;
   p.NCg = pl.ncg;
-  p.NPW = pl.npw;
-  p.tpw = pl.tpw;
   p.max_ctx = a.max_ctx;
   p.total_ctx = a.total_ctx;
   p.ntiles = decode_ntiles(a.total_ctx, a.B);
   p.c_log2 = a.scale * 1.4426950408889634f;
+
+  // ranges: one workgroup per CU, all resident at once and each with the same number of
+  // cache bytes. Measured on 256 CUs: one workgroup per CU is 5-7% faster than two (half
+  // the partials, and the same bandwidth from fewer streams), 1.5 or 0.5 far slower.
+  const int64_t want = (int64_t)device_cus() / pl.wg_per_range;
+  const int P = (int)std::max<int64_t>(1, std::min<int64_t>(want, pl.max_ranges));
+
   const int64_t nprep = (int64_t)a.B * a.K * a.Hq * (a.D / 16) +
                         (int64_t)a.B * a.Hkv * kDecTile * (a.D / 16) +
                         (int64_t)a.B * a.Hkv * a.D * (kDecTile / 8);
-  hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(decode_prep_kernel, dim3((unsigned)((nprep + 255) / 256 + 1)), dim3(256), 0,
                      stream, cu, lens, qn, kn, vn, cs, sn, reinterpret_cast<uint16_t*>(ws + lay.qr),
                      reinterpret_cast<uint16_t*>(ws + lay.knew),
                      reinterpret_cast<uint16_t*>(ws + lay.vnew), a.B, a.K, a.Hq, a.Hkv, a.D,
-                     a.max_ctx, a.max_pos, a.total_ctx);
+                     a.max_ctx, a.max_pos, a.total_ctx, P,
+                     reinterpret_cast<int32_t*>(ws + lay.rstart),
+                     reinterpret_cast<int32_t*>(ws + lay.rfirst),
+                     reinterpret_cast<int32_t*>(ws + lay.rlen));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = for_dim(a.D, [&](auto dc) {
     constexpr int DD = decltype(dc)::value;
-    const int heads = pl.heads;
-    const dim3 grid((unsigned)((int64_t)a.B * pl.npw * pl.ncg * (a.Hkv / heads)));
+    const dim3 grid((unsigned)((int64_t)P * pl.wg_per_range));
     const dim3 block(64 * kDecWaves);
     if (pl.ncw == 2) {
       if constexpr (DD <= 128) {
-        if (heads == 4) hipLaunchKernelGGL((decode_attn_kernel<DD, 2, 4>), grid, block, 0, stream, p);
+        if (pl.heads == 4) hipLaunchKernelGGL((decode_attn_kernel<DD, 2, 4>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((decode_attn_kernel<DD, 2, 1>), grid, block, 0, stream, p);
       }
     } else {
-      if (heads == 4) hipLaunchKernelGGL((decode_attn_kernel<DD, 1, 4>), grid, block, 0, stream, p);
+      if (pl.heads == 4) hipLaunchKernelGGL((decode_attn_kernel<DD, 1, 4>), grid, block, 0, stream, p);
       else hipLaunchKernelGGL((decode_attn_kernel<DD, 1, 1>), grid, block, 0, stream, p);
     }
   });
   if (e != hipSuccess) return e;
   const int64_t nout = (int64_t)a.B * a.Hkv * pl.ncg * pl.pc * (a.D / 4);
-  const int64_t nthreads = nout * kCombLanes;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0,
-                     stream, cu, lens, p.part_o, p.part_ml, out, lse, a.K, a.Hq, a.Hkv, p.G, p.GK,
-                     pl.ncg, pl.npw, pl.pc, a.D, pl.tpw, a.max_ctx, a.total_ctx, nout);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0,
+                     stream, p.rstart, p.rlen, p.part_o, p.part_ml, out, lse, a.K, a.Hq, a.Hkv,
+                     p.G, p.GK, pl.ncg, pl.pc, a.D, nout);
   return hipGetLastError();
 }
 

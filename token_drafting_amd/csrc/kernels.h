@@ -93,15 +93,18 @@ struct DecodeArgs {
   float scale;
 };
 // Split of the decode attention: a wave holds ncw groups of 16 query columns (pc = 16 ncw
-// columns); ncg column groups per kv head; a request's cache tiles in npw slices of tpw
-// tiles (one partial each per kv head and column group); heads kv heads per workgroup.
+// columns); ncg column groups per kv head; heads kv heads per workgroup, so wg_per_range
+// workgroups per range of tile slots; up to max_ranges ranges, and nslots = max_ranges + B
+// partial slots per (kv head, column group).
 struct DecodePlan {
-  int ncw, pc, ncg, npw, tpw, heads;
+  int ncw, pc, ncg, heads, wg_per_range, max_ranges, nslots;
 };
 DecodePlan decode_plan(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                        int64_t total_ctx, int32_t max_ctx);
 size_t decode_workspace_bytes(int32_t B, int32_t K, int32_t Hq, int32_t Hkv, int32_t D,
                               int64_t total_ctx, int32_t max_ctx);
+// Compute units of the current device (cached per device; 256 if the runtime cannot say).
+int device_cus();
 // V tiles per kv head of a cache of total_ctx keys over B requests.
 int64_t decode_ntiles(int64_t total_ctx, int32_t B);
 
