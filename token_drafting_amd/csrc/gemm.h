@@ -22,10 +22,19 @@
 // at the same time on one XCD and fetch that block from HBM once.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace peagle {
 namespace gemm {
+
+// Epilogues with kBlock = true take the wave's whole tile through wave_tile() without
+// combining lanes, so any tile width suits them; kWaveTile ones combine lanes.
+template <typename E, typename = void>
+struct takes_block : std::false_type {};
+template <typename E>
+struct takes_block<E, std::void_t<decltype(E::kBlock)>> : std::bool_constant<E::kBlock> {};
 
 constexpr int BM = 256, BN = 128;
 constexpr int kThreads = 256;
@@ -175,8 +184,9 @@ __global__ __launch_bounds__(kThreads) void dma_gemm_kernel(const uint16_t* __re
     if (ks + 1 < nk) step(ks + 1, As1, Bs1, As0, Bs0);
   }
 
-  if constexpr (Epi::kWaveTile) {
-    // an epilogue that combines lanes gets the wave's whole 128x64 tile, all lanes active
+  if constexpr (Epi::kWaveTile || takes_block<Epi>::value) {
+    // an epilogue that combines lanes, or reads before it writes, gets the wave's whole
+    // 128x64 tile, all lanes active
     epi.wave_tile(acc, m0 + wm * 128, n0 + wn * 64, lane, M, N);
   } else {
     const auto out = [&] {
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(kWideThreads) void dma_gemm_wide_kernel(const uint1
     compute(As1, Bs1);
   }
 
-  if constexpr (Epi::kWaveTile) {
+  if constexpr (Epi::kWaveTile || takes_block<Epi>::value) {
     epi.wave_tile(acc, m0 + wm * 64, n0 + wn * WN, lane, M, N);
   } else {
 #pragma unroll

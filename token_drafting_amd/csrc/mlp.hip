@@ -110,31 +110,76 @@ __global__ __launch_bounds__(256) void pack_gate_up_kernel(const uint16_t* __res
   }
 }
 
+// out = acc + src (fp32, row stride N) over a wave's tile, with src scaled by inv[min(row,
+// n)] * w[col] when norm. Each MFMA tile loads all its src values before it stores any
+// result: with per-element read-then-write, every load would wait
+// behind the previous store (the compiler cannot move a load above a store it may alias;
+// the restrict-qualified pointers tell it they never do). Rows past M and columns past N
+// load clamped addresses and store nothing.
+template <int NI, int NJ>
+__device__ __forceinline__ void add_tile(const floatx16 (&acc)[NI][NJ], float* __restrict__ out,
+                                         const float* __restrict__ src,
+                                         const float* __restrict__ inv,
+                                         const uint16_t* __restrict__ w, int N, int n, bool norm,
+                                         int row0, int col0, int lane, int M) {
+  const int r32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float rs[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = min(row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3), M - 1);
+      rs[r] = norm ? inv[min(row, n)] : 1.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = col0 + 32 * j + r32;
+      const int colc = min(col, N - 1);
+      const float wc = norm ? bf16_bits_to_f32(w[colc]) : 1.f;
+      float pre[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = min(row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3), M - 1);
+        pre[r] = src[(size_t)row * N + colc] * rs[r] * wc;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (row < M && col < N) out[(size_t)row * N + col] = acc[i][j][r] + pre[r];
+      }
+    }
+  }
+}
+
 // h1 = residual + acc: the residual is hidden (or rms(hidden) w_hidden, with the row's
 // 1/rms from inv; rows past n share row n's input).
 struct StoreResidual {
   static constexpr bool kWaveTile = false;
+  static constexpr bool kBlock = true;
   float* out;
   const float* hidden;
   const float* inv;
   const uint16_t* w;
   int N, n;
   bool norm;
-  __device__ __forceinline__ void operator()(int row, int col, float v) const {
-    float r = hidden[(size_t)row * N + col];
-    if (norm) r = r * inv[min(row, n)] * bf16_bits_to_f32(w[col]);
-    out[(size_t)row * N + col] = v + r;
+  template <int NI, int NJ>
+  __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
+                                            int lane, int M, int) const {
+    add_tile<NI, NJ>(acc, out, hidden, inv, w, N, n, norm, row0, col0, lane, M);
   }
 };
 
 // out = acc + add (fp32).
 struct StoreAdd {
   static constexpr bool kWaveTile = false;
+  static constexpr bool kBlock = true;
   float* out;
   const float* add;
   int N;
-  __device__ __forceinline__ void operator()(int row, int col, float v) const {
-    out[(size_t)row * N + col] = v + add[(size_t)row * N + col];
+  template <int NI, int NJ>
+  __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
+                                            int lane, int M, int) const {
+    add_tile<NI, NJ>(acc, out, add, nullptr, nullptr, N, 0, false, row0, col0, lane, M);
   }
 };
 
