@@ -104,6 +104,7 @@ struct AttnParams {
   const int4* qinfo;
   const int32_t* qstart;
   const int2* chunks;
+  const int4* cmeta;  // [2 chunk], [2 chunk + 1]: the chunk's entries, key range, diagonal
   const int32_t* nchunks;
   const int32_t* seq_chunk;
   int32_t* flags;  // [chunk * Hkv + g]: the main kernel asks for a redo
@@ -127,21 +128,11 @@ struct AttnParams {
 
 // Key range of a chunk (rows j0 .. j0 + jn - 1 of the anchor-major list, one sequence):
 // every row sees keys from k_lo (the sequence start) up to its own anchor, so the range is
-// [k_lo, k_hi] and keys [full_lo, full_hi] are seen by every row.
+// [k_lo, k_hi] and keys [full_lo, full_hi] are seen by every row (the prepare stage's
+// chunk metadata holds them).
 struct ChunkKeys {
   int k_lo, k_hi, full_lo, full_hi, p_first, p_last;
 };
-__device__ __forceinline__ ChunkKeys chunk_keys(const AttnParams& p, int j0, int jn) {
-  const int4 first = p.qinfo[j0], last = p.qinfo[j0 + jn - 1];
-  ChunkKeys c;
-  c.p_first = min(max(first.y, 0), p.n - 1);
-  c.p_last = min(max(last.y, 0), p.n - 1);
-  c.k_lo = min(max(first.w, 0), c.p_first);
-  c.k_hi = c.p_last;
-  c.full_lo = min(max(last.w, 0), c.p_last);
-  c.full_hi = c.p_first;
-  return c;
-}
 
 // Key-range split of a chunk's context tiles [t_first, t_last] into nseg segments. Segment
 // j > 0 starts at tile b_j, a tile wholly inside [full_lo, full_hi]: every row sees all its
@@ -182,7 +173,6 @@ struct AttnLds {
   alignas(1024) char Vs1[C::VBYTES];
   alignas(1024) char Kl0[C::KBUF];
   alignas(1024) char Kl1[C::KBUF];
-  int range[6];
   int kp[KT], kd[KT];
   int bad;  // main path: some row's fixed-reference sum left the safe range
 };
@@ -203,55 +193,29 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
   char* const Vs1 = L.Vs1;
   char* const Kl0 = L.Kl0;
   char* const Kl1 = L.Kl1;
-  int* const s_range = L.range;
   int* const s_kp = L.kp;
   int* const s_kd = L.kd;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, half = lane >> 5;
   const int n = p.n, T = p.T, Hkv = p.Hkv;
-  const int2 ch = p.chunks[chunk];
-  const int j0 = min(max(ch.x, 0), T - 1);
-  const int jn = min(max(ch.y, 1), T - j0);
-
-  if (tid == 0) {
-    const ChunkKeys c = chunk_keys(p, j0, jn);
-    s_range[0] = c.k_lo;     // first key of any row
-    s_range[1] = c.k_hi;     // last key of any row
-    s_range[2] = c.full_lo;  // keys in [full_lo, full_hi] are seen by every row
-    s_range[3] = c.full_hi;
-    s_range[4] = min(max(p.qstart[c.p_first], 0), T);     // diagonal keys: entries of the
-    s_range[5] = min(max(p.qstart[c.p_last + 1], 0), T);  // chunk's anchors in the list
-    L.bad = 0;
-  }
+  // the chunk's metadata, laid out by the prepare stage: one uniform load
+  const int4 cm0 = p.cmeta[2 * chunk], cm1 = p.cmeta[2 * chunk + 1];
+  const int j0 = cm0.x, jn = cm0.y;
+  const int k_lo = cm0.z, k_hi = cm0.w;          // first and last key of any row
+  const int full_lo = cm1.x, full_hi = cm1.y;    // keys every row sees
+  const int dg_lo = cm1.z, dg_hi = cm1.w;        // list entries of the chunk's anchors
+  if (tid == 0) L.bad = 0;
   __syncthreads();
-  const int k_lo = s_range[0], k_hi = s_range[1], full_lo = s_range[2], full_hi = s_range[3];
-  const int dg_lo = s_range[4], dg_hi = s_range[5];
   const bool is_short = (k_hi - k_lo + 1) <= kShortSpan;  // uniform over the workgroup
   if (EXACT ? (!is_short && !redo) : is_short) return;
 
 
   // Query slots of this lane: NT columns of 32 (lanes l and l+32 share a column, each
-  // holding 16 of the 32 keys of a tile).
+  // holding 16 of the 32 keys of a tile); loaded once the first tile's DMA is in flight.
   int q_row[NT], q_head[NT], q_p[NT], q_d[NT], q_lo[NT];
   bool q_on[NT];
   bf16x8 qf[NT][C::DK];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int slot = wave * 32 * NT + nt * 32 + r32;
-    const int rl = slot % p.QR, hl = slot / p.QR;
-    q_on[nt] = rl < jn;
-    const int4 qi = p.qinfo[j0 + min(rl, jn - 1)];
-    q_row[nt] = min(max(qi.x, 0), T - 1);
-    q_p[nt] = min(max(qi.y, 0), n - 1);
-    q_d[nt] = qi.z;
-    q_lo[nt] = min(max(qi.w, 0), q_p[nt]);
-    q_head[nt] = g * p.G + hl;
-    const uint16_t* qrow = p.qr + ((size_t)q_row[nt] * p.Hq + q_head[nt]) * D + half * 8;
-#pragma unroll
-    for (int kk = 0; kk < C::DK; ++kk)
-      qf[nt][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kk * 16));
-  }
 
   floatx16 o[NT][C::MT];
   float m_run[NT], l_run[NT];
@@ -457,6 +421,24 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
       }
   }
   if (!SPLIT || t_begin <= t_end) issue(t_begin, Ks0, Kl0, Vs0);
+  // the query fragments: the row list entry, then the rotated q row (two round trips that
+  // overlap the first tile's)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int slot = wave * 32 * NT + nt * 32 + r32;
+    const int rl = slot % p.QR, hl = slot / p.QR;
+    q_on[nt] = rl < jn;
+    const int4 qi = p.qinfo[j0 + min(rl, jn - 1)];
+    q_row[nt] = min(max(qi.x, 0), T - 1);
+    q_p[nt] = min(max(qi.y, 0), n - 1);
+    q_d[nt] = qi.z;
+    q_lo[nt] = min(max(qi.w, 0), q_p[nt]);
+    q_head[nt] = g * p.G + hl;
+    const uint16_t* qrow = p.qr + ((size_t)q_row[nt] * p.Hq + q_head[nt]) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < C::DK; ++kk)
+      qf[nt][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kk * 16));
+  }
   for (int t = t_begin; t <= t_end; t += 2) {
     wait_dma();
     __syncthreads();  // tile t landed in buffer 0; buffer 1 is free
@@ -634,10 +616,8 @@ __global__ __launch_bounds__(1024) void attn_items_kernel(const AttnParams p) {
   auto entry = [&](int i, int& key, SegPlan& sp) {
     const int chunk = nc - 1 - i / p.Hkv, g = i % p.Hkv;
     key = chunk * p.Hkv + g;
-    const int2 ch = p.chunks[chunk];
-    const int j0 = min(max(ch.x, 0), p.T - 1);
-    const int jn = min(max(ch.y, 1), p.T - j0);
-    const ChunkKeys c = chunk_keys(p, j0, jn);
+    const int4 cm0 = p.cmeta[2 * chunk], cm1 = p.cmeta[2 * chunk + 1];
+    const ChunkKeys c{cm0.z, cm0.w, cm1.x, cm1.y, 0, 0};
     sp = seg_plan(c);
     return c.k_hi - c.k_lo + 1 > kShortSpan;  // else short
   };
@@ -773,6 +753,7 @@ hipError_t launch_attn_core(const AttnArgs& a, const uint16_t* v, float* out, fl
   p.qinfo = reinterpret_cast<const int4*>(ws + L.qinfo);
   p.qstart = reinterpret_cast<const int32_t*>(ws + L.qstart);
   p.chunks = reinterpret_cast<const int2*>(ws + L.chunks);
+  p.cmeta = reinterpret_cast<const int4*>(ws + L.cmeta);
   p.nchunks = reinterpret_cast<const int32_t*>(ws + L.nchunks);
   p.seq_chunk = reinterpret_cast<const int32_t*>(ws + L.seq_chunk);
   p.flags = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + L.flags);

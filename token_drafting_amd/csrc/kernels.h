@@ -39,8 +39,8 @@ hipError_t launch_rope_table(int32_t head_dim, double theta, int32_t max_pos, fl
 
 // Workspace of the draft attention, carved from one caller-provided buffer.
 struct AttnLayout {
-  size_t qinfo, qstart, qrot, krot, krot_lo, vt, chunks, nchunks, seq_chunk, flags, blocksum,
-      segs, items, nitems, part, ml, total;
+  size_t qinfo, qstart, qrot, krot, krot_lo, vt, chunks, cmeta, nchunks, seq_chunk, flags,
+      blocksum, segs, items, nitems, part, ml, total;
   int max_chunks;
 };
 AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D);

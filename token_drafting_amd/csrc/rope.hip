@@ -164,11 +164,21 @@ __global__ __launch_bounds__(kScanThreads) void chunk_count_kernel(
 // Chunk table entries (first list entry, entry count), one thread per chunk: the chunk's
 // sequence is the last s with seq_chunk[s] <= c (empty sequences share their successor's
 // start, so the last one is the non-empty sequence). Also clears the per-(chunk, kv head)
-// redo flags.
+// redo flags, and writes the chunk's key metadata, which the attention workgroups then
+// read in one load instead of a chain of dependent ones:
+//   cmeta[2c]     = (j0, jn, k_lo, k_hi): the chunk's list entries (clamped to the list) and
+//                   its key range (rows see keys from their sequence start up to their
+//                   own anchor: k_lo = the first row's sequence start, k_hi = the last
+//                   row's anchor);
+//   cmeta[2c + 1] = (full_lo, full_hi, dg_lo, dg_hi): keys every row sees, and the list
+//                   entries of the chunk's anchors (their depth >= 1 rows are the
+//                   diagonal keys).
 __global__ __launch_bounds__(256) void chunk_fill_kernel(
     const int32_t* __restrict__ cu, const int32_t* __restrict__ qstart,
-    const int32_t* __restrict__ seq_chunk, const int32_t* __restrict__ nchunks, int n, int S,
-    int QR, int max_chunks, int2* __restrict__ chunks, int32_t* __restrict__ flags, int nflags) {
+    const int4* __restrict__ qinfo, const int32_t* __restrict__ seq_chunk,
+    const int32_t* __restrict__ nchunks, int n, int T, int S, int QR, int max_chunks,
+    int2* __restrict__ chunks, int4* __restrict__ cmeta, int32_t* __restrict__ flags,
+    int nflags) {
   const int nc = min(max(*nchunks, 0), max_chunks);
   const int stride = gridDim.x * blockDim.x;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nflags; i += stride) flags[i] = 0;
@@ -177,7 +187,16 @@ __global__ __launch_bounds__(256) void chunk_fill_kernel(
     const int j = c - seq_chunk[s];
     const int a = min(max(cu[s], 0), n), e = min(max(cu[s + 1], 0), n);
     const int first = qstart[a], rows = max(qstart[e] - first, 0);
-    chunks[c] = make_int2(first + j * QR, min(QR, rows - j * QR));
+    const int2 ch = make_int2(first + j * QR, min(QR, rows - j * QR));
+    chunks[c] = ch;
+    const int j0 = min(max(ch.x, 0), T - 1);
+    const int jn = min(max(ch.y, 1), T - j0);
+    const int4 qa = qinfo[j0], qb = qinfo[j0 + jn - 1];
+    const int p_first = min(max(qa.y, 0), n - 1), p_last = min(max(qb.y, 0), n - 1);
+    cmeta[2 * c] = make_int4(j0, jn, min(max(qa.w, 0), p_first), p_last);
+    cmeta[2 * c + 1] = make_int4(min(max(qb.w, 0), p_last), p_first,
+                                 min(max(qstart[p_first], 0), T),
+                                 min(max(qstart[p_last + 1], 0), T));
   }
 }
 
@@ -340,6 +359,7 @@ AttnLayout attn_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D)
   L.vt = off;     off += align256(ntiles * 32 * Hkv * D * 2);
   L.max_chunks = attn_max_chunks(n, T, Hq, Hkv);
   L.chunks = off; off += align256((size_t)L.max_chunks * sizeof(int2));
+  L.cmeta = off;  off += align256((size_t)L.max_chunks * 2 * sizeof(int4));
   L.nchunks = off; off += 256;
   L.seq_chunk = off; off += align256((size_t)(n + 1) * sizeof(int32_t));
   L.flags = off;  off += align256((size_t)L.max_chunks * Hkv * sizeof(int32_t));
@@ -388,7 +408,8 @@ hipError_t launch_attn_prepare(const AttnArgs& a, const int32_t* idx, const int3
                                            (int64_t)L.max_chunks * a.Hkv);
     const int blocks = (int)std::min<int64_t>((work + 255) / 256, 2048);
     hipLaunchKernelGGL(chunk_fill_kernel, dim3(blocks), dim3(256), 0, stream, cu_seqlens, qstart,
-                       seq_chunk, nchunks, a.n, a.S, QR, L.max_chunks, chunks,
+                       qinfo, seq_chunk, nchunks, a.n, a.T, a.S, QR, L.max_chunks, chunks,
+                       reinterpret_cast<int4*>(ws + L.cmeta),
                        reinterpret_cast<int32_t*>(ws + L.flags), L.max_chunks * a.Hkv);
   }
   hipError_t e = hipGetLastError();
