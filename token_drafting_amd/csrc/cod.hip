@@ -404,6 +404,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
   __shared__ uint32_t phist[kCoarseBins];  // the blocks before this one
   __shared__ uint64_t cand[kPool];
   __shared__ int32_t cpos[kPool];
+  __shared__ int32_t csmall[kPool];  // candidates of the same depth below each candidate
   __shared__ uint64_t thr[kMaxDepths];
   __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths], below[kMaxDepths];
   __shared__ int32_t cbase[kMaxDepths + 1], cfill[kMaxDepths];
@@ -427,6 +428,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     bin_depth[tid] = -1;
   }
   if (tid < kMaxDepths) kept_cnt[tid] = 0;
+  for (int i = tid; i < kPool; i += kThreads) csmall[i] = 0;
   __syncthreads();
   {
     const int x = tid % kCoarseBins, part = tid / kCoarseBins;
@@ -539,14 +541,33 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
       }
     }
     __syncthreads();
-    // each candidate ranks itself inside its depth's region (distinct hashes: one match)
-    for (int i = tid; i < cbase[K]; i += kThreads) {
+    // each candidate ranks itself inside its depth's region (distinct hashes: one match);
+    // `per` threads share one candidate's comparisons, eight reads in flight each
+    const int ctot = cbase[K];
+    const int per = max(1, kThreads / max(ctot, 1));
+    for (int t = tid; t < ctot * per; t += kThreads) {
+      const int i = t / per, part = t - i * per;
       int d = 0;
       while (cbase[d + 1] <= i) ++d;
       const uint64_t h = cand[i];
+      const int j1 = cbase[d + 1];
       int smaller = 0;
-      for (int j = cbase[d]; j < cbase[d + 1]; ++j) smaller += cand[j] < h;
-      if (smaller == rank_in_bin[d] - 1) thr[d] = h;
+      int j = cbase[d] + part;
+      for (; j + 7 * per < j1; j += 8 * per) {
+        uint64_t c[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = cand[j + e * per];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) smaller += c[e] < h;
+      }
+      for (; j < j1; j += per) smaller += cand[j] < h;
+      atomicAdd(&csmall[i], smaller);
+    }
+    __syncthreads();
+    for (int i = tid; i < ctot; i += kThreads) {
+      int d = 0;
+      while (cbase[d + 1] <= i) ++d;
+      if (csmall[i] == rank_in_bin[d] - 1) thr[d] = cand[i];
     }
     __syncthreads();
     // kept positions before this block: those in the bins below, and the candidates of the
