@@ -637,10 +637,18 @@ __global__ __launch_bounds__(1024) void attn_items_kernel(const AttnParams p) {
     const int step = (hi - lo + 1024) / 1024;
     const int L = lo + tid * step;
     if (L <= hi) {
+      // seg_count for every entry, with ceil(v / L) from a float reciprocal corrected to
+      // the exact integer (v + L - 1 < 2^24): integer division is a long instruction
+      // sequence, and this loop runs total times in each of the 1024 threads
+      const float inv = 1.f / (float)L;
       int cnt = 0;
       for (int i = 0; i < total; ++i) {
         const int v = s_ntl[i];
-        cnt += v > 0 ? seg_count(v, L, p.nsplit) : (v < 0 ? 1 : 0);
+        const int x = v + L - 1;
+        int q = (int)((float)x * inv);
+        q -= q * L > x ? 1 : 0;
+        q += (q + 1) * L <= x ? 1 : 0;
+        cnt += v > 0 ? max(1, min(p.nsplit, q)) : (v < 0 ? 1 : 0);
       }
       if (cnt <= p.budget) atomicMin(&s_best, L);
     }
