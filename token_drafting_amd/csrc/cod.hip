@@ -306,9 +306,10 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
 //      LDS give the rank inside the block (coalesced idx / row_of);
 //   4. kept anchors of depth d before each sequence start that falls in this block (the
 //      last block also owns cu = n).
-__device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu,
+__device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu, int cu_first,
                               const uint64_t* thr, const int32_t* before_blk,
-                              uint64_t (*wmask)[kWaves], uint64_t h, int32_t* __restrict__ idx,
+                              uint64_t (*wmask)[kWaves], int32_t (*wpre)[kWaves], uint64_t h,
+                              int32_t* __restrict__ idx,
                               int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d,
                               int32_t* __restrict__ row_of) {
   const int tid = threadIdx.x;
@@ -324,11 +325,23 @@ __device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu,
     if (lane == 0) wmask[d][wave] = ball;
   }
   __syncthreads();
+  // kept positions of the waves before each wave, per depth (lane w of wave d sums the
+  // popcounts of waves 0..w-1)
+  for (int d = wave; d < K; d += kWaves) {
+    const int c = lane < kWaves ? __popcll(wmask[d][lane]) : 0;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < kWaves; o <<= 1) {
+      const int y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    if (lane < kWaves) wpre[d][lane] = x - c;
+  }
+  __syncthreads();
   for (int d = 0; d < K; ++d) {
     const uint64_t ball = wmask[d][wave];
     const bool keep = (ball >> lane) & 1ull;
-    int r = a.off[d] + before_blk[d] + __popcll(ball & ((1ull << lane) - 1ull));
-    for (int w = 0; w < wave; ++w) r += __popcll(wmask[d][w]);
+    const int r = a.off[d] + before_blk[d] + wpre[d][wave] + __popcll(ball & ((1ull << lane) - 1ull));
     if (inside) {
       row_of[(size_t)d * n + p] = keep ? r : -1;
       if (keep && r < a.off[d + 1]) idx[r] = p;
@@ -336,7 +349,7 @@ __device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu,
   }
   for (int t = tid; t < K * (a.S + 1); t += kThreads) {
     const int d = t / (a.S + 1), s = t % (a.S + 1);
-    const int x = cu[s];
+    const int x = t == tid ? cu_first : cu[s];
     const bool mine = (x >= base && x < base + kThreads && x < n) ||
                       (x >= n && blockIdx.x == gridDim.x - 1);
     if (!mine) continue;
@@ -345,8 +358,7 @@ __device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu,
       v = a.m[d];
     } else {
       const int off = x - base, w = off >> 6, l = off & 63;
-      v = before_blk[d] + __popcll(wmask[d][w] & ((1ull << l) - 1ull));
-      for (int j = 0; j < w; ++j) v += __popcll(wmask[d][j]);
+      v = before_blk[d] + wpre[d][w] + __popcll(wmask[d][w] & ((1ull << l) - 1ull));
     }
     cu_d[t] = v;
   }
@@ -359,6 +371,7 @@ __global__ __launch_bounds__(kThreads) void cod_compact_kernel(
     int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
   __shared__ uint64_t thr[kMaxDepths];
   __shared__ uint64_t wmask[kMaxDepths][kWaves];
+  __shared__ int32_t wpre[kMaxDepths][kWaves];
   __shared__ int32_t before_blk[kMaxDepths];
   const int tid = threadIdx.x;
   if (tid < a.K) {
@@ -367,77 +380,142 @@ __global__ __launch_bounds__(kThreads) void cod_compact_kernel(
   }
   __syncthreads();
   const int p = blockIdx.x * kThreads + tid;
-  compact_block(a, cu, thr, before_blk, wmask, splitmix64(a.seed ^ (uint64_t)p), idx, depth_off,
-                cu_d, row_of);
+  const int cu_first = tid < a.K * (a.S + 1) ? cu[tid % (a.S + 1)] : 0;
+  compact_block(a, cu, cu_first, thr, before_blk, wmask, wpre, splitmix64(a.seed ^ (uint64_t)p),
+                idx, depth_off, cu_d, row_of);
 }
 
 // ---- one-pass path for buffers of at most kSmallBlocks blocks ----
-// cod_hash_kernel: a workgroup per block stores its positions' hashes and the histogram of
-// their top 8 bits. cod_select_small_kernel: every workgroup rebuilds, from those, the
-// global histogram, each depth's bin and rank, the candidates and thresholds (the same in
-// every workgroup: a few hundred hashes per depth at these sizes), and its own prefix of
-// kept positions, then compacts its block. Two launches, no single-workgroup stage.
+// cod_hash_kernel: a workgroup per block hashes its positions and stores them sorted by
+// the hash's top 8 bits (a counting sort in LDS: the block's hashes and positions grouped
+// by that byte, with each group's count and start). cod_select_small_kernel: every
+// workgroup rebuilds, from the counts, the global histogram and each depth's bin and rank;
+// loads only those bins' groups (a few hundred hashes per depth at these sizes); finds each
+// threshold by a second 8-bit histogram over the candidates and a rank among the few that
+// share the threshold's sub-bin; counts its own prefix of kept positions; then compacts
+// its block. Two launches, no single-workgroup stage.
 constexpr int kSmallBlocks = 64;
 constexpr int kCoarseBins = 256;
 constexpr int kPool = 4096;  // candidate hashes held at once
 
-__global__ __launch_bounds__(kThreads) void cod_hash_kernel(CodArgs a, uint64_t* __restrict__ hashes,
-                                                           uint32_t* __restrict__ bhist) {
+struct SmallWs {
+  uint64_t* shash;  // [blocks][kThreads] hashes grouped by top byte
+  int32_t* spos;    // their positions
+  uint32_t* bcnt;   // [blocks][kCoarseBins] group sizes
+  uint32_t* bstart; // [blocks][kCoarseBins] group starts inside the block
+};
+
+__host__ __device__ inline SmallWs small_ws(void* ws, int nb) {
+  char* b = static_cast<char*>(ws);
+  SmallWs w;
+  w.shash = reinterpret_cast<uint64_t*>(b);
+  b += (size_t)nb * kThreads * sizeof(uint64_t);
+  w.spos = reinterpret_cast<int32_t*>(b);
+  b += (size_t)nb * kThreads * sizeof(int32_t);
+  w.bcnt = reinterpret_cast<uint32_t*>(b);
+  b += (size_t)nb * kCoarseBins * sizeof(uint32_t);
+  w.bstart = reinterpret_cast<uint32_t*>(b);
+  return w;
+}
+
+__global__ __launch_bounds__(kThreads) void cod_hash_kernel(CodArgs a, SmallWs w) {
   __shared__ uint32_t h8[kCoarseBins];
-  const int tid = threadIdx.x, p = blockIdx.x * kThreads + tid;
+  __shared__ uint32_t st[kCoarseBins];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int blk = blockIdx.x, p = blk * kThreads + tid;
   if (tid < kCoarseBins) h8[tid] = 0;
   __syncthreads();
-  if (p < a.n) {
-    const uint64_t h = splitmix64(a.seed ^ (uint64_t)p);
-    hashes[p] = h;
-    atomicAdd(&h8[h >> 56], 1u);
+  const bool inside = p < a.n;
+  uint64_t h = 0;
+  int t = 0;
+  uint32_t slot = 0;
+  if (inside) {
+    h = splitmix64(a.seed ^ (uint64_t)p);
+    t = (int)(h >> 56);
+    slot = atomicAdd(&h8[t], 1u);
   }
   __syncthreads();
-  if (tid < kCoarseBins) bhist[(size_t)blockIdx.x * kCoarseBins + tid] = h8[tid];
+  // exclusive scan of the group sizes by wave 0 (4 bins per lane)
+  if (tid < kWave) {
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = h8[4 * lane + i];
+      sum += c[i];
+    }
+    uint32_t x = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    x -= sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t g = (size_t)blk * kCoarseBins + 4 * lane + i;
+      st[4 * lane + i] = x;
+      w.bstart[g] = x;
+      w.bcnt[g] = c[i];
+      x += c[i];
+    }
+  }
+  __syncthreads();
+  if (inside) {
+    const size_t o = (size_t)blk * kThreads + st[t] + slot;
+    w.shash[o] = h;
+    w.spos[o] = p;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
-    CodArgs a, const int32_t* __restrict__ cu, const uint64_t* __restrict__ hashes,
-    const uint32_t* __restrict__ bhist, int32_t* __restrict__ idx, int32_t* __restrict__ depth_off,
-    int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
+    CodArgs a, const int32_t* __restrict__ cu, const SmallWs w, int32_t* __restrict__ idx,
+    int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d, int32_t* __restrict__ row_of) {
   __shared__ uint32_t ghist[kCoarseBins];  // all blocks
   __shared__ uint32_t phist[kCoarseBins];  // the blocks before this one
   __shared__ uint64_t cand[kPool];
   __shared__ int32_t cpos[kPool];
-  __shared__ int32_t csmall[kPool];  // candidates of the same depth below each candidate
+  __shared__ int32_t goff[kMaxDepths][kSmallBlocks + 1];  // a depth's candidates before block j
+  __shared__ uint32_t gst[kMaxDepths][kSmallBlocks];      // start of the bin's group in block j
+  __shared__ uint32_t hist2[kWaves][kCoarseBins];         // second-level histograms
+  __shared__ uint64_t sub_list[kWaves][kWave];
+  __shared__ int32_t sub_cnt[kWaves], sub_bin[kWaves], sub_rank[kWaves];
   __shared__ uint64_t thr[kMaxDepths];
   __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths], below[kMaxDepths];
-  __shared__ int32_t cbase[kMaxDepths + 1], cfill[kMaxDepths];
+  __shared__ int32_t cbase[kMaxDepths + 1];
   __shared__ int32_t before_blk[kMaxDepths], kept_cnt[kMaxDepths];
-  __shared__ int8_t bin_depth[kCoarseBins];
   __shared__ uint64_t wmask[kMaxDepths][kWaves];
+  __shared__ int32_t wpre[kMaxDepths][kWaves];
   __shared__ int32_t sh[kWaves];
   __shared__ uint64_t s_prefix;
   __shared__ int32_t s_rank;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int n = a.n, K = a.K, nb = gridDim.x, blk = blockIdx.x;
   const int base = blk * kThreads;
   constexpr int kParts = kThreads / kCoarseBins;  // threads per bin for the sums
+  constexpr int kPerPart = kSmallBlocks / kParts;
+
+  // the compaction's sequence starts, loaded now so that their latency is hidden
+  const int ncu = K * (a.S + 1);
+  const int cu_first = tid < ncu ? cu[tid % (a.S + 1)] : 0;
 
   // global histogram of the top 8 bits, and that of the blocks before this one: each bin
-  // summed by kParts threads over interleaved blocks
+  // summed by kParts threads over interleaved blocks (the group starts are kept in
+  // registers for the candidate bins)
   if (tid < kCoarseBins) {
     ghist[tid] = 0;
     phist[tid] = 0;
-    bin_depth[tid] = -1;
   }
   if (tid < kMaxDepths) kept_cnt[tid] = 0;
-  for (int i = tid; i < kPool; i += kThreads) csmall[i] = 0;
   __syncthreads();
+  const int x = tid % kCoarseBins, part = tid / kCoarseBins;
+  uint32_t v[kPerPart], gs[kPerPart];
   {
-    const int x = tid % kCoarseBins, part = tid / kCoarseBins;
-    constexpr int kPerPart = kSmallBlocks / kParts;  // all of a thread's loads in flight at once
-    uint32_t v[kPerPart];
 #pragma unroll
     for (int i = 0; i < kPerPart; ++i) {
       const int j = part + i * kParts;
-      v[i] = j < nb ? bhist[(size_t)j * kCoarseBins + x] : 0u;
+      v[i] = j < nb ? w.bcnt[(size_t)j * kCoarseBins + x] : 0u;
+      gs[i] = j < nb ? w.bstart[(size_t)j * kCoarseBins + x] : 0u;
     }
     uint32_t all = 0, pre = 0;
 #pragma unroll
@@ -451,15 +529,15 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
   __syncthreads();
   // inclusive prefix sums of both histograms over the bins, by wave 0 (4 bins per lane)
   if (tid < kWave) {
-    uint32_t g[4], q[4], gs = 0, qs = 0;
+    uint32_t g[4], q[4], gsum = 0, qsum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       g[i] = ghist[4 * lane + i];
       q[i] = phist[4 * lane + i];
-      gs += g[i];
-      qs += q[i];
+      gsum += g[i];
+      qsum += q[i];
     }
-    uint32_t gx = gs, qx = qs;  // inclusive scan over the lanes
+    uint32_t gx = gsum, qx = qsum;  // inclusive scan over the lanes
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const uint32_t gy = __shfl_up(gx, o, kWave), qy = __shfl_up(qx, o, kWave);
@@ -468,8 +546,8 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
         qx += qy;
       }
     }
-    gx -= gs;
-    qx -= qs;
+    gx -= gsum;
+    qx -= qsum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       gx += g[i];
@@ -499,80 +577,158 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     int c = 0;
     for (int d = 0; d < K; ++d) {
       cbase[d] = c;
-      cfill[d] = 0;
       if (own_search(a, d)) {
-        c += (int)(ghist[bin_of[d]] - (bin_of[d] > 0 ? ghist[bin_of[d] - 1] : 0u));
-        bin_depth[bin_of[d]] = bin_depth[bin_of[d]] == -1 ? (int8_t)d : (int8_t)-2;
+        const int b = bin_of[d];
+        c += (int)(ghist[b] - (b > 0 ? ghist[b - 1] : 0u));
       }
     }
     cbase[K] = c;
   }
-  __syncthreads();
-  if (cbase[K] <= kPool) {
-    // candidates of every depth with its own search, with their positions; the hashes are
-    // loaded sixteen at a time before any is examined
-    constexpr int kBatch = 16;
-    for (int p0 = tid; p0 < n; p0 += kBatch * kThreads) {
-      uint64_t hb[kBatch];
+  // the threads of each depth's bin leave its group sizes and starts per block
+  for (int d = 0; d < K; ++d) {
+    if (!own_search(a, d) || bin_of[d] != x) continue;
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int p = p0 + i * kThreads;
-        hb[i] = p < n ? hashes[p] : 0ull;
+    for (int i = 0; i < kPerPart; ++i) {
+      const int j = part + i * kParts;
+      if (j < nb) {
+        goff[d][j + 1] = (int)v[i];
+        gst[d][j] = gs[i];
+      }
+    }
+  }
+  __syncthreads();
+  // per depth, the exclusive prefix of the group sizes over the blocks (one wave per depth)
+  for (int d = wave; d < K; d += kWaves) {
+    if (!own_search(a, d)) continue;
+    const int c = lane < nb ? goff[d][lane + 1] : 0;
+    int y = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int z = __shfl_up(y, o, kWave);
+      if (lane >= o) y += z;
+    }
+    if (lane < nb) goff[d][lane + 1] = y;
+    if (lane == 0) goff[d][0] = 0;
+  }
+  __syncthreads();
+  const int ctot = cbase[K];
+  if (ctot <= kPool) {
+    // candidates: candidate i of depth d is entry i - goff[d][j] of the bin's group in the
+    // block j with goff[d][j] <= i < goff[d][j + 1]; four loads in flight per thread
+    constexpr int kBatch = 4;
+    for (int i0 = tid; i0 < ctot; i0 += kBatch * kThreads) {
+      size_t src[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const int i = i0 + e * kThreads;
+        src[e] = 0;
+        if (i < ctot) {
+          int d = 0;
+          while (cbase[d + 1] <= i) ++d;
+          const int c = i - cbase[d];
+          int lo = 0, hi = nb - 1;  // the last block whose prefix is <= c
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (goff[d][mid] <= c) lo = mid;
+            else hi = mid - 1;
+          }
+          src[e] = (size_t)lo * kThreads + gst[d][lo] + (c - goff[d][lo]);
+        }
+      }
+      uint64_t hv[kBatch];
+      int32_t pv[kBatch];
+#pragma unroll
+      for (int e = 0; e < kBatch; ++e) {
+        const bool ok = i0 + e * kThreads < ctot;
+        hv[e] = ok ? w.shash[src[e]] : 0ull;
+        pv[e] = ok ? w.spos[src[e]] : 0;
       }
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int p = p0 + i * kThreads;
-        if (p >= n) break;
-        const uint64_t h = hb[i];
-        const int t = (int)(h >> 56);
-        const int bd = bin_depth[t];
-        if (bd >= 0) {
-          const int slot = cbase[bd] + atomicAdd(&cfill[bd], 1);
-          cand[slot] = h;
-          cpos[slot] = p;
-        } else if (bd == -2) {  // a bin shared by several depths
-          for (int d = 0; d < K; ++d)
-            if (own_search(a, d) && bin_of[d] == t) {
-              const int slot = cbase[d] + atomicAdd(&cfill[d], 1);
-              cand[slot] = h;
-              cpos[slot] = p;
-            }
+      for (int e = 0; e < kBatch; ++e) {
+        const int i = i0 + e * kThreads;
+        if (i < ctot) {
+          cand[i] = hv[e];
+          cpos[i] = pv[e];
         }
       }
     }
     __syncthreads();
-    // each candidate ranks itself inside its depth's region (distinct hashes: one match);
-    // `per` threads share one candidate's comparisons, eight reads in flight each
-    const int ctot = cbase[K];
-    const int per = max(1, kThreads / max(ctot, 1));
-    for (int t = tid; t < ctot * per; t += kThreads) {
-      const int i = t / per, part = t - i * per;
-      int d = 0;
-      while (cbase[d + 1] <= i) ++d;
-      const uint64_t h = cand[i];
-      const int j1 = cbase[d + 1];
-      int smaller = 0;
-      int j = cbase[d] + part;
-      for (; j + 7 * per < j1; j += 8 * per) {
-        uint64_t c[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = cand[j + e * per];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) smaller += c[e] < h;
+    // thresholds, a wave per depth: the next 8 bits' histogram over the depth's candidates
+    // locates the sub-bin holding its rank; the sub-bin's few members are ranked directly
+    // (a full ranking of the depth's candidates if more than a wave's worth share it)
+    for (int q0 = 0; q0 < K; q0 += kWaves) {
+      const int d = q0 + wave;
+      const bool act = d < K && own_search(a, d);
+      if (act) {
+        for (int b = lane; b < kCoarseBins; b += kWave) hist2[wave][b] = 0;
+        if (lane == 0) sub_cnt[wave] = 0;
       }
-      for (; j < j1; j += per) smaller += cand[j] < h;
-      atomicAdd(&csmall[i], smaller);
+      __syncthreads();
+      if (act) {
+        for (int i = cbase[d] + lane; i < cbase[d + 1]; i += kWave)
+          atomicAdd(&hist2[wave][(cand[i] >> 48) & 255u], 1u);
+      }
+      __syncthreads();
+      if (act) {
+        uint32_t c[4], sum = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          c[k] = hist2[wave][4 * lane + k];
+          sum += c[k];
+        }
+        uint32_t y = sum;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+          const uint32_t z = __shfl_up(y, o, kWave);
+          if (lane >= o) y += z;
+        }
+        y -= sum;
+        const uint32_t r = (uint32_t)rank_in_bin[d];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (r > y && r <= y + c[k]) {
+            sub_bin[wave] = 4 * lane + k;
+            sub_rank[wave] = (int)(r - y);
+          }
+          y += c[k];
+        }
+      }
+      __syncthreads();
+      if (act) {
+        const uint32_t sb = (uint32_t)sub_bin[wave];
+        for (int i = cbase[d] + lane; i < cbase[d + 1]; i += kWave) {
+          const uint64_t h = cand[i];
+          if (((h >> 48) & 255u) == sb) {
+            const int k = atomicAdd(&sub_cnt[wave], 1);
+            if (k < kWave) sub_list[wave][k] = h;
+          }
+        }
+      }
+      __syncthreads();
+      if (act) {
+        const int m = sub_cnt[wave];
+        if (m <= kWave) {
+          if (lane < m) {
+            const uint64_t h = sub_list[wave][lane];
+            int smaller = 0;
+            for (int k = 0; k < m; ++k) smaller += sub_list[wave][k] < h;
+            if (smaller == sub_rank[wave] - 1) thr[d] = h;
+          }
+        } else {
+          const int j0 = cbase[d], j1 = cbase[d + 1];
+          for (int i = j0 + lane; i - lane < j1; i += kWave) {
+            const uint64_t h = i < j1 ? cand[i] : 0ull;
+            int smaller = 0;
+            for (int j = j0; j < j1; ++j) smaller += cand[j] < h;
+            if (i < j1 && smaller == rank_in_bin[d] - 1) thr[d] = h;
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    for (int i = tid; i < ctot; i += kThreads) {
-      int d = 0;
-      while (cbase[d + 1] <= i) ++d;
-      if (csmall[i] == rank_in_bin[d] - 1) thr[d] = cand[i];
-    }
-    __syncthreads();
     // kept positions before this block: those in the bins below, and the candidates of the
-    // depth's bin before the block that do not exceed its threshold
-    for (int i = tid; i < cbase[K]; i += kThreads) {
+    // depth's bin from the blocks before it that do not exceed its threshold
+    for (int i = tid; i < ctot; i += kThreads) {
       int d = 0;
       while (cbase[d + 1] <= i) ++d;
       if (cpos[i] < base && cand[i] <= thr[d]) atomicAdd(&kept_cnt[d], 1);
@@ -586,7 +742,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
       if (!own_search(a, d)) continue;
       const uint64_t t = radix_select(a, a.m[d], reinterpret_cast<uint32_t*>(cand), &s_prefix, &s_rank);
       int c = 0;
-      for (int p = tid; p < base; p += kThreads) c += hashes[p] <= t;
+      for (int p = tid; p < base; p += kThreads) c += splitmix64(a.seed ^ (uint64_t)p) <= t;
       int total;
       (void)block_scan_excl(c, sh, &total);
       if (tid == 0) {
@@ -606,18 +762,20 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     }
   __syncthreads();
   const int p = base + tid;
-  compact_block(a, cu, thr, before_blk, wmask, p < n ? hashes[p] : 0ull, idx, depth_off, cu_d,
-                row_of);
+  compact_block(a, cu, cu_first, thr, before_blk, wmask, wpre,
+                p < n ? splitmix64(a.seed ^ (uint64_t)p) : 0ull, idx, depth_off, cu_d, row_of);
 }
 
 }  // namespace
 
-// Workspace: up to kSmallBlocks blocks, the n hashes then the per-block histograms of the
-// one-pass path; else the kMaxDepths thresholds, then the [blocks][K] exclusive prefixes.
+// Workspace: up to kSmallBlocks blocks, the one-pass path's grouped hashes and positions,
+// then the per-block group sizes and starts; else the kMaxDepths thresholds, then the
+// [blocks][K] exclusive prefixes.
 size_t cod_workspace_bytes(int64_t n, int32_t K) {
   const size_t nb = (size_t)((n + kThreads - 1) / kThreads);
   const size_t bytes = nb <= (size_t)kSmallBlocks
-                           ? (size_t)n * sizeof(uint64_t) + nb * kCoarseBins * sizeof(uint32_t)
+                           ? nb * kThreads * (sizeof(uint64_t) + sizeof(int32_t)) +
+                                 2 * nb * kCoarseBins * sizeof(uint32_t)
                            : (size_t)kMaxDepths * sizeof(uint64_t) + nb * (size_t)K * sizeof(int32_t);
   return (bytes + 255) & ~(size_t)255;
 }
@@ -627,11 +785,10 @@ hipError_t launch_cod_select(const CodArgs& a, const int32_t* cu_seqlens, int32_
                              void* workspace, hipStream_t stream) {
   const int nb = (a.n + kThreads - 1) / kThreads;
   if (nb <= kSmallBlocks) {
-    uint64_t* hashes = static_cast<uint64_t*>(workspace);
-    uint32_t* bhist = reinterpret_cast<uint32_t*>(hashes + a.n);
-    hipLaunchKernelGGL(cod_hash_kernel, dim3(nb), dim3(kThreads), 0, stream, a, hashes, bhist);
+    const SmallWs w = small_ws(workspace, nb);
+    hipLaunchKernelGGL(cod_hash_kernel, dim3(nb), dim3(kThreads), 0, stream, a, w);
     hipLaunchKernelGGL(cod_select_small_kernel, dim3(nb), dim3(kThreads), 0, stream, a, cu_seqlens,
-                       hashes, bhist, idx, depth_off, cu_seqlens_d, row_of);
+                       w, idx, depth_off, cu_seqlens_d, row_of);
     return hipGetLastError();
   }
   uint64_t* thr = static_cast<uint64_t*>(workspace);
