@@ -401,8 +401,7 @@ constexpr int kPool = 4096;  // candidate hashes held at once
 struct SmallWs {
   uint64_t* shash;  // [blocks][kThreads] hashes grouped by top byte
   int32_t* spos;    // their positions
-  uint32_t* bcnt;   // [blocks][kCoarseBins] group sizes
-  uint32_t* bstart; // [blocks][kCoarseBins] group starts inside the block
+  uint32_t* group;  // [blocks][kCoarseBins] group size | group start inside the block << 16
 };
 
 __host__ __device__ inline SmallWs small_ws(void* ws, int nb) {
@@ -412,10 +411,21 @@ __host__ __device__ inline SmallWs small_ws(void* ws, int nb) {
   b += (size_t)nb * kThreads * sizeof(uint64_t);
   w.spos = reinterpret_cast<int32_t*>(b);
   b += (size_t)nb * kThreads * sizeof(int32_t);
-  w.bcnt = reinterpret_cast<uint32_t*>(b);
-  b += (size_t)nb * kCoarseBins * sizeof(uint32_t);
-  w.bstart = reinterpret_cast<uint32_t*>(b);
+  w.group = reinterpret_cast<uint32_t*>(b);
   return w;
+}
+
+// Orders this wave's LDS accesses before and after it (the lanes of one wave exchange data
+// through LDS without a workgroup barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, kWave);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, kWave);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __global__ __launch_bounds__(kThreads) void cod_hash_kernel(CodArgs a, SmallWs w) {
@@ -452,10 +462,8 @@ __global__ __launch_bounds__(kThreads) void cod_hash_kernel(CodArgs a, SmallWs w
     x -= sum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const size_t g = (size_t)blk * kCoarseBins + 4 * lane + i;
       st[4 * lane + i] = x;
-      w.bstart[g] = x;
-      w.bcnt[g] = c[i];
+      w.group[(size_t)blk * kCoarseBins + 4 * lane + i] = c[i] | (x << 16);
       x += c[i];
     }
   }
@@ -478,11 +486,10 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
   __shared__ uint32_t gst[kMaxDepths][kSmallBlocks];      // start of the bin's group in block j
   __shared__ uint32_t hist2[kWaves][kCoarseBins];         // second-level histograms
   __shared__ uint64_t sub_list[kWaves][kWave];
-  __shared__ int32_t sub_cnt[kWaves], sub_bin[kWaves], sub_rank[kWaves];
   __shared__ uint64_t thr[kMaxDepths];
   __shared__ int32_t bin_of[kMaxDepths], rank_in_bin[kMaxDepths], below[kMaxDepths];
   __shared__ int32_t cbase[kMaxDepths + 1];
-  __shared__ int32_t before_blk[kMaxDepths], kept_cnt[kMaxDepths];
+  __shared__ int32_t before_blk[kMaxDepths];
   __shared__ uint64_t wmask[kMaxDepths][kWaves];
   __shared__ int32_t wpre[kMaxDepths][kWaves];
   __shared__ int32_t sh[kWaves];
@@ -500,28 +507,27 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
   const int cu_first = tid < ncu ? cu[tid % (a.S + 1)] : 0;
 
   // global histogram of the top 8 bits, and that of the blocks before this one: each bin
-  // summed by kParts threads over interleaved blocks (the group starts are kept in
-  // registers for the candidate bins)
+  // summed by kParts threads over interleaved blocks (the group words stay in registers
+  // for the candidate bins)
   if (tid < kCoarseBins) {
     ghist[tid] = 0;
     phist[tid] = 0;
   }
-  if (tid < kMaxDepths) kept_cnt[tid] = 0;
   __syncthreads();
   const int x = tid % kCoarseBins, part = tid / kCoarseBins;
-  uint32_t v[kPerPart], gs[kPerPart];
+  uint32_t gw[kPerPart];
   {
 #pragma unroll
     for (int i = 0; i < kPerPart; ++i) {
       const int j = part + i * kParts;
-      v[i] = j < nb ? w.bcnt[(size_t)j * kCoarseBins + x] : 0u;
-      gs[i] = j < nb ? w.bstart[(size_t)j * kCoarseBins + x] : 0u;
+      gw[i] = j < nb ? w.group[(size_t)j * kCoarseBins + x] : 0u;
     }
     uint32_t all = 0, pre = 0;
 #pragma unroll
     for (int i = 0; i < kPerPart; ++i) {
-      all += v[i];
-      pre += part + i * kParts < blk ? v[i] : 0u;
+      const uint32_t v = gw[i] & 0xFFFFu;
+      all += v;
+      pre += part + i * kParts < blk ? v : 0u;
     }
     atomicAdd(&ghist[x], all);
     atomicAdd(&phist[x], pre);
@@ -591,90 +597,82 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     for (int i = 0; i < kPerPart; ++i) {
       const int j = part + i * kParts;
       if (j < nb) {
-        goff[d][j + 1] = (int)v[i];
-        gst[d][j] = gs[i];
+        goff[d][j + 1] = (int)(gw[i] & 0xFFFFu);
+        gst[d][j] = gw[i] >> 16;
       }
     }
-  }
-  __syncthreads();
-  // per depth, the exclusive prefix of the group sizes over the blocks (one wave per depth)
-  for (int d = wave; d < K; d += kWaves) {
-    if (!own_search(a, d)) continue;
-    const int c = lane < nb ? goff[d][lane + 1] : 0;
-    int y = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int z = __shfl_up(y, o, kWave);
-      if (lane >= o) y += z;
-    }
-    if (lane < nb) goff[d][lane + 1] = y;
-    if (lane == 0) goff[d][0] = 0;
   }
   __syncthreads();
   const int ctot = cbase[K];
   if (ctot <= kPool) {
-    // candidates: candidate i of depth d is entry i - goff[d][j] of the bin's group in the
-    // block j with goff[d][j] <= i < goff[d][j + 1]; four loads in flight per thread
-    constexpr int kBatch = 4;
-    for (int i0 = tid; i0 < ctot; i0 += kBatch * kThreads) {
-      size_t src[kBatch];
+    // a wave per depth with its own search, no workgroup barriers: the depth's candidates,
+    // its threshold, and its kept positions before this block
+    for (int d = wave; d < K; d += kWaves) {
+      if (!own_search(a, d)) continue;
+      const int j0 = cbase[d], cnt = cbase[d + 1] - j0;
+      // 1. the bin's candidates before each block (exclusive prefix over the blocks)
+      {
+        const int c = lane < nb ? goff[d][lane + 1] : 0;
+        int y = c;
 #pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int i = i0 + e * kThreads;
-        src[e] = 0;
-        if (i < ctot) {
-          int d = 0;
-          while (cbase[d + 1] <= i) ++d;
-          const int c = i - cbase[d];
-          int lo = 0, hi = nb - 1;  // the last block whose prefix is <= c
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (goff[d][mid] <= c) lo = mid;
-            else hi = mid - 1;
+        for (int o = 1; o < kWave; o <<= 1) {
+          const int z = __shfl_up(y, o, kWave);
+          if (lane >= o) y += z;
+        }
+        if (lane < nb) goff[d][lane + 1] = y;
+        if (lane == 0) goff[d][0] = 0;
+      }
+      wave_lds_sync();
+      // 2. candidate c is entry c - goff[j] of the bin's group in the block j with
+      //    goff[j] <= c < goff[j + 1]; four loads in flight per lane
+      constexpr int kBatch = 4;
+      for (int c0 = 0; c0 < cnt; c0 += kBatch * kWave) {
+        size_t src[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          const int c = c0 + e * kWave + lane;
+          src[e] = 0;
+          if (c < cnt) {
+            int lo = 0, hi = nb - 1;  // the last block whose prefix is <= c
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (goff[d][mid] <= c) lo = mid;
+              else hi = mid - 1;
+            }
+            src[e] = (size_t)lo * kThreads + gst[d][lo] + (c - goff[d][lo]);
           }
-          src[e] = (size_t)lo * kThreads + gst[d][lo] + (c - goff[d][lo]);
+        }
+        uint64_t hv[kBatch];
+        int32_t pv[kBatch];
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          const bool ok = c0 + e * kWave + lane < cnt;
+          hv[e] = ok ? w.shash[src[e]] : 0ull;
+          pv[e] = ok ? w.spos[src[e]] : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < kBatch; ++e) {
+          const int c = c0 + e * kWave + lane;
+          if (c < cnt) {
+            cand[j0 + c] = hv[e];
+            cpos[j0 + c] = pv[e];
+          }
         }
       }
-      uint64_t hv[kBatch];
-      int32_t pv[kBatch];
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const bool ok = i0 + e * kThreads < ctot;
-        hv[e] = ok ? w.shash[src[e]] : 0ull;
-        pv[e] = ok ? w.spos[src[e]] : 0;
-      }
-#pragma unroll
-      for (int e = 0; e < kBatch; ++e) {
-        const int i = i0 + e * kThreads;
-        if (i < ctot) {
-          cand[i] = hv[e];
-          cpos[i] = pv[e];
-        }
-      }
-    }
-    __syncthreads();
-    // thresholds, a wave per depth: the next 8 bits' histogram over the depth's candidates
-    // locates the sub-bin holding its rank; the sub-bin's few members are ranked directly
-    // (a full ranking of the depth's candidates if more than a wave's worth share it)
-    for (int q0 = 0; q0 < K; q0 += kWaves) {
-      const int d = q0 + wave;
-      const bool act = d < K && own_search(a, d);
-      if (act) {
-        for (int b = lane; b < kCoarseBins; b += kWave) hist2[wave][b] = 0;
-        if (lane == 0) sub_cnt[wave] = 0;
-      }
-      __syncthreads();
-      if (act) {
-        for (int i = cbase[d] + lane; i < cbase[d + 1]; i += kWave)
-          atomicAdd(&hist2[wave][(cand[i] >> 48) & 255u], 1u);
-      }
-      __syncthreads();
-      if (act) {
-        uint32_t c[4], sum = 0;
+      // 3. histogram of the next 8 bits over the candidates: the sub-bin holding the rank
+      uint32_t* h2 = hist2[wave];
+      for (int b = lane; b < kCoarseBins; b += kWave) h2[b] = 0;
+      wave_lds_sync();
+      for (int c = lane; c < cnt; c += kWave) atomicAdd(&h2[(cand[j0 + c] >> 48) & 255u], 1u);
+      wave_lds_sync();
+      const uint32_t r = (uint32_t)rank_in_bin[d];
+      int sb = 0, r2 = 0;
+      {
+        uint32_t hc[4], sum = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          c[k] = hist2[wave][4 * lane + k];
-          sum += c[k];
+          hc[k] = h2[4 * lane + k];
+          sum += hc[k];
         }
         uint32_t y = sum;
 #pragma unroll
@@ -683,58 +681,63 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
           if (lane >= o) y += z;
         }
         y -= sum;
-        const uint32_t r = (uint32_t)rank_in_bin[d];
+        int my_sb = -1, my_r2 = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          if (r > y && r <= y + c[k]) {
-            sub_bin[wave] = 4 * lane + k;
-            sub_rank[wave] = (int)(r - y);
+          if (r > y && r <= y + hc[k]) {
+            my_sb = 4 * lane + k;
+            my_r2 = (int)(r - y);
           }
-          y += c[k];
+          y += hc[k];
+        }
+        const int src = __ffsll((unsigned long long)__ballot(my_sb >= 0)) - 1;
+        sb = __shfl(my_sb, src, kWave);
+        r2 = __shfl(my_r2, src, kWave);
+      }
+      // 4. the sub-bin's members, compacted by ballot
+      int m = 0;
+      for (int c0 = 0; c0 < cnt; c0 += kWave) {
+        const int c = c0 + lane;
+        const uint64_t h = c < cnt ? cand[j0 + c] : 0ull;
+        const bool mine = c < cnt && (int)((h >> 48) & 255u) == sb;
+        const uint64_t ball = __ballot(mine);
+        const int slot = m + __popcll(ball & ((1ull << lane) - 1ull));
+        if (mine && slot < kWave) sub_list[wave][slot] = h;
+        m += __popcll(ball);
+      }
+      wave_lds_sync();
+      // 5. the member of rank r2 among them (every candidate of the depth if a wave's worth
+      //    or more share the sub-bin)
+      uint64_t thr_d = 0;
+      if (m <= kWave) {
+        const uint64_t h = lane < m ? sub_list[wave][lane] : 0ull;
+        int smaller = 0;
+        for (int k = 0; k < m; ++k) smaller += sub_list[wave][k] < h;
+        const uint64_t sel = __ballot(lane < m && smaller == r2 - 1);
+        thr_d = lane_u64(h, __ffsll((unsigned long long)sel) - 1);
+      } else {
+        for (int c0 = 0; c0 < cnt; c0 += kWave) {
+          const int c = c0 + lane;
+          const uint64_t h = c < cnt ? cand[j0 + c] : 0ull;
+          int smaller = 0;
+          for (int j = 0; j < cnt; ++j) smaller += cand[j0 + j] < h;
+          const uint64_t sel = __ballot(c < cnt && smaller == (int)r - 1);
+          if (sel) thr_d = lane_u64(h, __ffsll((unsigned long long)sel) - 1);
         }
       }
-      __syncthreads();
-      if (act) {
-        const uint32_t sb = (uint32_t)sub_bin[wave];
-        for (int i = cbase[d] + lane; i < cbase[d + 1]; i += kWave) {
-          const uint64_t h = cand[i];
-          if (((h >> 48) & 255u) == sb) {
-            const int k = atomicAdd(&sub_cnt[wave], 1);
-            if (k < kWave) sub_list[wave][k] = h;
-          }
-        }
+      // 6. kept positions before this block: those in the bins below, and the bin's
+      //    candidates from the blocks before it that do not exceed the threshold
+      const int nbefore = goff[d][blk];
+      int kept = 0;
+      for (int c0 = 0; c0 < nbefore; c0 += kWave) {
+        const int c = c0 + lane;
+        kept += __popcll(__ballot(c < nbefore && cand[j0 + c] <= thr_d));
       }
-      __syncthreads();
-      if (act) {
-        const int m = sub_cnt[wave];
-        if (m <= kWave) {
-          if (lane < m) {
-            const uint64_t h = sub_list[wave][lane];
-            int smaller = 0;
-            for (int k = 0; k < m; ++k) smaller += sub_list[wave][k] < h;
-            if (smaller == sub_rank[wave] - 1) thr[d] = h;
-          }
-        } else {
-          const int j0 = cbase[d], j1 = cbase[d + 1];
-          for (int i = j0 + lane; i - lane < j1; i += kWave) {
-            const uint64_t h = i < j1 ? cand[i] : 0ull;
-            int smaller = 0;
-            for (int j = j0; j < j1; ++j) smaller += cand[j] < h;
-            if (i < j1 && smaller == rank_in_bin[d] - 1) thr[d] = h;
-          }
-        }
+      if (lane == 0) {
+        thr[d] = thr_d;
+        before_blk[d] = below[d] + kept;
       }
-      __syncthreads();
     }
-    // kept positions before this block: those in the bins below, and the candidates of the
-    // depth's bin from the blocks before it that do not exceed its threshold
-    for (int i = tid; i < ctot; i += kThreads) {
-      int d = 0;
-      while (cbase[d + 1] <= i) ++d;
-      if (cpos[i] < base && cand[i] <= thr[d]) atomicAdd(&kept_cnt[d], 1);
-    }
-    __syncthreads();
-    if (tid < K && own_search(a, tid)) before_blk[tid] = below[tid] + kept_cnt[tid];
   } else {
     // a bin too full for the pool (not expected at these sizes): radix select over every
     // hash, then count the kept positions before the block
@@ -769,13 +772,13 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
 }  // namespace
 
 // Workspace: up to kSmallBlocks blocks, the one-pass path's grouped hashes and positions,
-// then the per-block group sizes and starts; else the kMaxDepths thresholds, then the
+// then the per-block group words (size and start); else the kMaxDepths thresholds, then the
 // [blocks][K] exclusive prefixes.
 size_t cod_workspace_bytes(int64_t n, int32_t K) {
   const size_t nb = (size_t)((n + kThreads - 1) / kThreads);
   const size_t bytes = nb <= (size_t)kSmallBlocks
                            ? nb * kThreads * (sizeof(uint64_t) + sizeof(int32_t)) +
-                                 2 * nb * kCoarseBins * sizeof(uint32_t)
+                                 nb * kCoarseBins * sizeof(uint32_t)
                            : (size_t)kMaxDepths * sizeof(uint64_t) + nb * (size_t)K * sizeof(int32_t);
   return (bytes + 255) & ~(size_t)255;
 }
