@@ -81,8 +81,10 @@ int peagle_cod_counts(int64_t n, int32_t K, double r, double r_min, int64_t *m, 
  *   cu_seqlens_d  int32[K*(S+1)] out  [d][s] = kept anchors of depth d below cu[s]
  *   row_of        int32[K*n] out   [d][p] = draft row of (d, p), or -1 if not kept
  *   workspace     >= peagle_cod_workspace_bytes(n, K) bytes of device memory, 256-byte
- *                 aligned (per-depth thresholds and per-block kept counts); its contents
- *                 are scratch and need no initialisation
+ *                 aligned (up to n = 65536 the hashes grouped by their top byte per block
+ *                 of 1024 positions, with the groups' sizes; beyond, per-depth thresholds
+ *                 and per-block kept counts); its contents are scratch and need no
+ *                 initialisation
  * Requires n < 2^31 and T as given by peagle_cod_counts. Work is O(n K) in two launches:
  * up to n = 65536 a hash pass and a select pass, each a workgroup per 1024 positions;
  * beyond, one workgroup finds the thresholds and per-block counts, then a workgroup per

@@ -8,8 +8,9 @@
 // The hash is a bijection, so the m_d-th smallest hash is a unique threshold and depth d
 // keeps exactly the p with hash <= threshold.
 //
-// Two launches, each hash computed where it is needed (re-hashing is cheaper than
-// storing 8 bytes per position):
+// Up to 64 blocks of 1024 positions, a hash pass and a select pass (below, before the
+// workspace sizes). Beyond, two launches, each hash computed where it is needed
+// (re-hashing is cheaper than storing 8 bytes per position):
 //   cod_threshold_kernel (one workgroup of 1024 threads, O(n)):
 //     1. a 12-bit histogram of all n hashes locates, for every depth, the bin that holds
 //        the m_d-th smallest hash; the handful of hashes in that bin (n / 4096 on
