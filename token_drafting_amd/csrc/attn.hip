@@ -596,12 +596,15 @@ __global__ __launch_bounds__(2 * kAttnSlots) void attn_core_kernel(const AttnPar
 // chunks first, gets one item per segment; chunks with a short span (run by the exact
 // kernel) get none. The segment length L is chosen from the chunks' actual spans: the
 // smallest L (>= kMinSplitTiles) whose item count fits p.budget, the workgroups that run at
-// once, so the split finishes in one round bounded by the longest segment. 1024 candidate
-// lengths are counted in parallel, one per thread. If none fits, nothing is split. Also
-// writes each entry's segment count for the merge.
+// once, so the split finishes in one round bounded by the longest segment. The candidates
+// are 1024 evenly spaced lengths; the item count does not grow with L, so the first that
+// fits is bracketed in three rounds (strides 64, 4, 1), each wave counting one candidate
+// over all entries. If none fits, nothing is split. Also writes each entry's segment count
+// for the merge.
 __global__ __launch_bounds__(1024) void attn_items_kernel(const AttnParams p) {
   __shared__ int s_ntl[kItemsMaxEntries];  // tiles (splittable), -1 (not splittable), 0 (short)
   __shared__ int s_wave[16];
+  __shared__ int s_fits[16];
   __shared__ int s_carry, s_best, s_maxntl;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = min(max(*p.nchunks, 0), p.max_chunks);
@@ -635,23 +638,46 @@ __global__ __launch_bounds__(1024) void attn_items_kernel(const AttnParams p) {
     __syncthreads();
     const int lo = kMinSplitTiles, hi = max(s_maxntl, lo);
     const int step = (hi - lo + 1024) / 1024;
-    const int L = lo + tid * step;
-    if (L <= hi) {
+    const int ng = min(1024, (hi - lo) / step + 1);  // candidates lo + i * step, i < ng
+    // fits(i): candidate i's item count is within the budget (true past the last one)
+    auto fits = [&](int i) {
+      if (i >= ng) return true;
+      const int L = lo + i * step;
       // seg_count for every entry, with ceil(v / L) from a float reciprocal corrected to
       // the exact integer (v + L - 1 < 2^24): integer division is a long instruction
-      // sequence, and this loop runs total times in each of the 1024 threads
+      // sequence
       const float inv = 1.f / (float)L;
       int cnt = 0;
-      for (int i = 0; i < total; ++i) {
-        const int v = s_ntl[i];
+      for (int e = lane; e < total; e += 64) {
+        const int v = s_ntl[e];
         const int x = v + L - 1;
         int q = (int)((float)x * inv);
         q -= q * L > x ? 1 : 0;
         q += (q + 1) * L <= x ? 1 : 0;
         cnt += v > 0 ? max(1, min(p.nsplit, q)) : (v < 0 ? 1 : 0);
       }
-      if (cnt <= p.budget) atomicMin(&s_best, L);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+      return cnt <= p.budget;
+    };
+    // The first fitting index lies in [base, base + 16 * stride) (1024 when none does);
+    // wave w tests the last index of its sub-range, and the first wave whose test fits
+    // narrows the range to that sub-range. Strides 64, 4, 1: the last range holds 4
+    // indices, and the waves past them test indices that fit whenever the range's last one
+    // does.
+    int base = 0;
+    for (int stride = 64;; stride = stride == 64 ? 4 : 1) {
+      const int probe = base + (wave + 1) * stride - 1;
+      const bool f = (stride > 1 || wave < 4) ? fits(probe) : true;
+      if (lane == 0) s_fits[wave] = f ? 1 : 0;
+      __syncthreads();
+      int w = 0;
+      while (w < 16 && !s_fits[w]) ++w;
+      base += w * stride;
+      __syncthreads();
+      if (stride == 1) break;
     }
+    if (tid == 0 && base < ng) s_best = lo + base * step;
     __syncthreads();
   }
   const int L = s_best;
