@@ -495,7 +495,16 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
       }
     }
     __syncthreads();
-    compute(Ks0, Kl0, Vs0, 2, 0, false);
+    // Entries are anchor-major, so the tile's anchors run from s_kp[0] to that of its last
+    // entry. A wave none of whose rows has its anchor in that run (or a depth >= 1) would
+    // get only -inf scores from the tile, zero weights and an unchanged O: it skips it.
+    bool sees = false;
+    {
+      const int a_lo = s_kp[0], a_hi = s_kp[min(KT, dg_hi - jb) - 1];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sees |= q_d[nt] >= 1 && q_p[nt] >= a_lo && q_p[nt] <= a_hi;
+    }
+    if (__any(sees)) compute(Ks0, Kl0, Vs0, 2, 0, false);
   }
 
   // ---- epilogue: O / l, lse; the main kernel flags rows whose sum left the safe range ----
