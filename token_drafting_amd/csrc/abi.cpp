@@ -40,6 +40,17 @@ int counts(int64_t n, int32_t K, double r, double r_min, int64_t* m, int64_t* T)
   return PEAGLE_OK;
 }
 
+// Attention shapes the kernels take: every product behind the workspace layout stays far
+// inside size_t ((T + 32) Hq D elements at most 2^44).
+int attn_shape(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D) {
+  if (n < 1 || n > kMaxI32 || T < n || T > kMaxI32) return PEAGLE_ERR_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PEAGLE_ERR_ARG;
+  if (D != 64 && D != 128 && D != 256) return PEAGLE_ERR_UNSUPPORTED;
+  if (kAttnSlots % (Hq / Hkv) != 0) return PEAGLE_ERR_UNSUPPORTED;
+  if ((double)(T + 32) * (double)Hq * (double)D > (double)((int64_t)1 << 44)) return PEAGLE_ERR_ARG;
+  return PEAGLE_OK;
+}
+
 struct AttnCall {
   AttnArgs a;
   const int32_t *idx, *depth_off, *row_of, *cu;
@@ -55,14 +66,13 @@ int attn_check(int64_t n, int32_t K, int64_t T, const int32_t* idx, const int32_
                const peagle_bf16* k, const peagle_bf16* v, int32_t Hq, int32_t Hkv, int32_t D,
                float scale, const float* cs, const float* sn, int32_t max_pos, float* out,
                float* lse, void* ws, size_t ws_bytes, void* stream, AttnCall* call) {
-  if (n < 1 || n > kMaxI32 || K < 1 || K > PEAGLE_MAX_DEPTHS) return PEAGLE_ERR_ARG;
-  if (T < n || T > (int64_t)K * n || T > kMaxI32) return PEAGLE_ERR_ARG;
+  if (K < 1 || K > PEAGLE_MAX_DEPTHS) return PEAGLE_ERR_ARG;
+  const int shape = attn_shape(n, T, Hq, Hkv, D);
+  if (shape != PEAGLE_OK) return shape;
+  if (T > (int64_t)K * n) return PEAGLE_ERR_ARG;
   if (S < 1 || S > n) return PEAGLE_ERR_ARG;
-  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PEAGLE_ERR_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return PEAGLE_ERR_ARG;
   if ((int64_t)max_pos < n + K - 2) return PEAGLE_ERR_ARG;
-  if (D != 64 && D != 128 && D != 256) return PEAGLE_ERR_UNSUPPORTED;
-  if (kAttnSlots % (Hq / Hkv) != 0) return PEAGLE_ERR_UNSUPPORTED;
   if (ws_bytes < attn_layout(n, T, Hq, Hkv, D).total) return PEAGLE_ERR_WORKSPACE;
   if (!idx || !depth_off || !row_of || !cu || !q || !k || !v || !cs || !sn || !out || !ws)
     return PEAGLE_ERR_ARG;
@@ -216,7 +226,7 @@ int peagle_rope_table(int32_t head_dim, double theta, int32_t max_pos, float* co
                       float* sin_out, void* stream) {
   if (head_dim < 2 || head_dim % 2 != 0 || max_pos < 0) return PEAGLE_ERR_ARG;
   if (!std::isfinite(theta) || !(theta > 0.0)) return PEAGLE_ERR_ARG;
-  if ((int64_t)(max_pos + 1) * (head_dim / 2) > kMaxI32) return PEAGLE_ERR_ARG;
+  if (((int64_t)max_pos + 1) * (head_dim / 2) > kMaxI32) return PEAGLE_ERR_ARG;
   if (!cos_out || !sin_out) return PEAGLE_ERR_ARG;
   return status_of(
       launch_rope_table(head_dim, theta, max_pos, cos_out, sin_out, static_cast<hipStream_t>(stream)));
@@ -224,8 +234,7 @@ int peagle_rope_table(int32_t head_dim, double theta, int32_t max_pos, float* co
 
 size_t peagle_draft_attn_workspace_bytes(int64_t n, int64_t T, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim) {
-  if (n < 1 || T < n || T > kMaxI32 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
-    return 0;
+  if (attn_shape(n, T, num_q_heads, num_kv_heads, head_dim) != PEAGLE_OK) return 0;
   return attn_layout(n, T, num_q_heads, num_kv_heads, head_dim).total;
 }
 
@@ -263,9 +272,7 @@ int peagle_draft_attn_fwd(PEAGLE_ATTN_ARGS) {
 
 size_t peagle_draft_attn_bwd_workspace_bytes(int64_t n, int64_t T, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim) {
-  if (n < 1 || T < n || T > kMaxI32 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
-      num_q_heads % num_kv_heads != 0)
-    return 0;
+  if (attn_shape(n, T, num_q_heads, num_kv_heads, head_dim) != PEAGLE_OK) return 0;
   return attn_bwd_layout(n, T, num_q_heads, num_kv_heads, head_dim).total;
 }
 
