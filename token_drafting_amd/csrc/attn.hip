@@ -421,6 +421,36 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
       }
   }
   if (!SPLIT || t_begin <= t_end) issue(t_begin, Ks0, Kl0, Vs0);
+  // The diagonal keys' data of the first kPreDiag tiles (D <= 128, where registers are to
+  // spare): the list entry of this thread's key, then its K (and k_lo) and V chunk, loaded
+  // beside the query fragments' own two round trips and held through the context loop, so
+  // the diagonal phase after it does not wait on them.
+  const int jd0 = seg == nseg - 1 ? dg_lo : dg_hi;  // first diagonal tile
+  constexpr int kPreDiag = D <= 128 ? 2 : 0;
+  constexpr int kPreSlots = kPreDiag > 0 ? kPreDiag : 1;
+  int4 pre_e[kPreSlots];  // entry jb + tid, for s_kp / s_kd (threads below KT)
+  u32x4 pre_k[kPreSlots], pre_v[kPreSlots], pre_l[kPreSlots];
+  if constexpr (kPreDiag > 0) {
+    int pre_row[kPreSlots];
+#pragma unroll
+    for (int i = 0; i < kPreDiag; ++i) {
+      const int jb = jd0 + i * KT;
+      const int jk = jb + tid / (D / 8);
+      pre_e[i] = tid < KT && jb + tid < dg_hi ? p.qinfo[jb + tid] : int4{-1, 0, 0, 0};
+      pre_row[i] = tid < C::KCH && jk < dg_hi ? min(max(p.qinfo[jk].x, 0), T - 1) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kPreDiag; ++i) {
+      const int c = tid % (D / 8);
+      pre_k[i] = pre_v[i] = pre_l[i] = u32x4{0u, 0u, 0u, 0u};
+      if (pre_row[i] >= 0) {
+        const size_t at = ((size_t)pre_row[i] * Hkv + g) * D + c * 8;
+        pre_k[i] = *reinterpret_cast<const u32x4*>(p.kr + at);
+        pre_v[i] = *reinterpret_cast<const u32x4*>(p.v + at);
+        if (EXACT && !redo) pre_l[i] = *reinterpret_cast<const u32x4*>(p.kr_lo + at);
+      }
+    }
+  }
   // the query fragments: the row list entry, then the rotated q row (two round trips that
   // overlap the first tile's)
 #pragma unroll
@@ -460,12 +490,20 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
   }
 
   // ---- diagonal extension: depth >= 1 rows of the chunk's anchors ----
-  for (int jb = seg == nseg - 1 ? dg_lo : dg_hi; jb < dg_hi; jb += KT) {
+  for (int jb = jd0; jb < dg_hi; jb += KT) {
     __syncthreads();
+    const int di = (jb - jd0) / KT;  // diagonal tile index: the first kPreDiag are loaded
     if (tid < KT) {
       const int jk = jb + tid;
       int kp = -1, kd = 0;
-      if (jk < dg_hi) {
+      if (di < kPreDiag) {
+#pragma unroll
+        for (int i = 0; i < kPreDiag; ++i)
+          if (i == di) {
+            kp = jk < dg_hi ? pre_e[i].y : -1;
+            kd = jk < dg_hi ? pre_e[i].z : 0;
+          }
+      } else if (jk < dg_hi) {
         const int4 e = p.qinfo[jk];
         kp = e.y;
         kd = e.z;
@@ -476,7 +514,15 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
     for (int q = tid; q < C::KCH; q += C::TH) {
       const int key = q / (D / 8), c = q % (D / 8), jk = jb + key;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u}, kl = {0u, 0u, 0u, 0u};
-      if (jk < dg_hi) {
+      if (di < kPreDiag && q == tid) {
+#pragma unroll
+        for (int i = 0; i < kPreDiag; ++i)
+          if (i == di) {
+            kv = pre_k[i];
+            vv = pre_v[i];
+            kl = pre_l[i];
+          }
+      } else if (jk < dg_hi) {
         const int row = min(max(p.qinfo[jk].x, 0), T - 1);
         kv = *reinterpret_cast<const u32x4*>(p.kr + ((size_t)row * Hkv + g) * D + c * 8);
         vv = *reinterpret_cast<const u32x4*>(p.v + ((size_t)row * Hkv + g) * D + c * 8);
