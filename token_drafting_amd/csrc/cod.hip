@@ -111,6 +111,25 @@ __device__ __forceinline__ bool own_search(const CodArgs& a, int d) {
   return m > 0 && m < a.n && (d == 0 || a.m[d - 1] != m);
 }
 
+// The per-depth parameters in LDS: kernel arguments indexed by a depth in a loop cost a
+// serialized scalar load per iteration, LDS reads do not.
+struct DepthLds {
+  int32_t m[kMaxDepths];
+  int32_t off[kMaxDepths + 1];
+  int8_t own[kMaxDepths];  // own_search
+};
+
+// Threads 0 .. K fill dl (callers order it with a barrier before use).
+__device__ __forceinline__ void load_depths(const CodArgs& a, DepthLds& dl) {
+  const int t = threadIdx.x;
+  if (t < a.K) {
+    dl.m[t] = a.m[t];
+    dl.off[t] = a.off[t];
+    dl.own[t] = own_search(a, t) ? 1 : 0;
+  }
+  if (t == a.K) dl.off[t] = a.off[t];
+}
+
 __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
     CodArgs a, uint64_t* __restrict__ thr_out, int32_t* __restrict__ before_out) {
   constexpr int kPerThread = kBins / kThreads;
@@ -307,8 +326,8 @@ __global__ __launch_bounds__(kThreads) void cod_threshold_kernel(
 //      LDS give the rank inside the block (coalesced idx / row_of);
 //   4. kept anchors of depth d before each sequence start that falls in this block (the
 //      last block also owns cu = n).
-__device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu, int cu_first,
-                              const uint64_t* thr, const int32_t* before_blk,
+__device__ void compact_block(const CodArgs& a, const DepthLds& dl, const int32_t* __restrict__ cu,
+                              int cu_first, const uint64_t* thr, const int32_t* before_blk,
                               uint64_t (*wmask)[kWaves], int32_t (*wpre)[kWaves], uint64_t h,
                               int32_t* __restrict__ idx,
                               int32_t* __restrict__ depth_off, int32_t* __restrict__ cu_d,
@@ -321,7 +340,7 @@ __device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu, 
   const int p = base + tid;
   const bool inside = p < n;
   for (int d = 0; d < K; ++d) {
-    const bool keep = inside && a.m[d] > 0 && h <= thr[d];
+    const bool keep = inside && dl.m[d] > 0 && h <= thr[d];
     const uint64_t ball = __ballot(keep);
     if (lane == 0) wmask[d][wave] = ball;
   }
@@ -342,10 +361,10 @@ __device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu, 
   for (int d = 0; d < K; ++d) {
     const uint64_t ball = wmask[d][wave];
     const bool keep = (ball >> lane) & 1ull;
-    const int r = a.off[d] + before_blk[d] + wpre[d][wave] + __popcll(ball & ((1ull << lane) - 1ull));
+    const int r = dl.off[d] + before_blk[d] + wpre[d][wave] + __popcll(ball & ((1ull << lane) - 1ull));
     if (inside) {
       row_of[(size_t)d * n + p] = keep ? r : -1;
-      if (keep && r < a.off[d + 1]) idx[r] = p;
+      if (keep && r < dl.off[d + 1]) idx[r] = p;
     }
   }
   for (int t = tid; t < K * (a.S + 1); t += kThreads) {
@@ -356,14 +375,14 @@ __device__ void compact_block(const CodArgs& a, const int32_t* __restrict__ cu, 
     if (!mine) continue;
     int v;
     if (x >= n) {
-      v = a.m[d];
+      v = dl.m[d];
     } else {
       const int off = x - base, w = off >> 6, l = off & 63;
       v = before_blk[d] + wpre[d][w] + __popcll(wmask[d][w] & ((1ull << l) - 1ull));
     }
     cu_d[t] = v;
   }
-  if (blockIdx.x == 0 && tid <= K) depth_off[tid] = a.off[tid];
+  if (blockIdx.x == 0 && tid <= K) depth_off[tid] = dl.off[tid];
 }
 
 __global__ __launch_bounds__(kThreads) void cod_compact_kernel(
@@ -374,7 +393,9 @@ __global__ __launch_bounds__(kThreads) void cod_compact_kernel(
   __shared__ uint64_t wmask[kMaxDepths][kWaves];
   __shared__ int32_t wpre[kMaxDepths][kWaves];
   __shared__ int32_t before_blk[kMaxDepths];
+  __shared__ DepthLds dl;
   const int tid = threadIdx.x;
+  load_depths(a, dl);
   if (tid < a.K) {
     thr[tid] = thr_in[tid];
     before_blk[tid] = before_in[(size_t)blockIdx.x * a.K + tid];
@@ -382,8 +403,8 @@ __global__ __launch_bounds__(kThreads) void cod_compact_kernel(
   __syncthreads();
   const int p = blockIdx.x * kThreads + tid;
   const int cu_first = tid < a.K * (a.S + 1) ? cu[tid % (a.S + 1)] : 0;
-  compact_block(a, cu, cu_first, thr, before_blk, wmask, wpre, splitmix64(a.seed ^ (uint64_t)p),
-                idx, depth_off, cu_d, row_of);
+  compact_block(a, dl, cu, cu_first, thr, before_blk, wmask, wpre,
+                splitmix64(a.seed ^ (uint64_t)p), idx, depth_off, cu_d, row_of);
 }
 
 // ---- one-pass path for buffers of at most kSmallBlocks blocks ----
@@ -496,6 +517,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
   __shared__ int32_t sh[kWaves];
   __shared__ uint64_t s_prefix;
   __shared__ int32_t s_rank;
+  __shared__ DepthLds dl;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int n = a.n, K = a.K, nb = gridDim.x, blk = blockIdx.x;
@@ -514,6 +536,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     ghist[tid] = 0;
     phist[tid] = 0;
   }
+  load_depths(a, dl);
   __syncthreads();
   const int x = tid % kCoarseBins, part = tid / kCoarseBins;
   uint32_t gw[kPerPart];
@@ -571,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     const uint32_t gin = ghist[tid], gex = tid > 0 ? ghist[tid - 1] : 0u;
     const uint32_t pex = tid > 0 ? phist[tid - 1] : 0u;
     for (int d = 0; d < K; ++d) {
-      const uint32_t m = (uint32_t)a.m[d];
+      const uint32_t m = (uint32_t)dl.m[d];
       if (m > gex && m <= gin) {
         bin_of[d] = tid;
         rank_in_bin[d] = (int)(m - gex);
@@ -584,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     int c = 0;
     for (int d = 0; d < K; ++d) {
       cbase[d] = c;
-      if (own_search(a, d)) {
+      if (dl.own[d]) {
         const int b = bin_of[d];
         c += (int)(ghist[b] - (b > 0 ? ghist[b - 1] : 0u));
       }
@@ -593,7 +616,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
   }
   // the threads of each depth's bin leave its group sizes and starts per block
   for (int d = 0; d < K; ++d) {
-    if (!own_search(a, d) || bin_of[d] != x) continue;
+    if (!dl.own[d] || bin_of[d] != x) continue;
 #pragma unroll
     for (int i = 0; i < kPerPart; ++i) {
       const int j = part + i * kParts;
@@ -609,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     // a wave per depth with its own search, no workgroup barriers: the depth's candidates,
     // its threshold, and its kept positions before this block
     for (int d = wave; d < K; d += kWaves) {
-      if (!own_search(a, d)) continue;
+      if (!dl.own[d]) continue;
       const int j0 = cbase[d], cnt = cbase[d + 1] - j0;
       // 1. the bin's candidates before each block (exclusive prefix over the blocks)
       {
@@ -743,8 +766,8 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
     // a bin too full for the pool (not expected at these sizes): radix select over every
     // hash, then count the kept positions before the block
     for (int d = 0; d < K; ++d) {
-      if (!own_search(a, d)) continue;
-      const uint64_t t = radix_select(a, a.m[d], reinterpret_cast<uint32_t*>(cand), &s_prefix, &s_rank);
+      if (!dl.own[d]) continue;
+      const uint64_t t = radix_select(a, dl.m[d], reinterpret_cast<uint32_t*>(cand), &s_prefix, &s_rank);
       int c = 0;
       for (int p = tid; p < base; p += kThreads) c += splitmix64(a.seed ^ (uint64_t)p) <= t;
       int total;
@@ -759,14 +782,14 @@ __global__ __launch_bounds__(kThreads) void cod_select_small_kernel(
   __syncthreads();
   if (tid == 0)
     for (int d = 0; d < K; ++d) {
-      if (own_search(a, d)) continue;
-      const bool all = a.m[d] >= n || d == 0, none = a.m[d] == 0;
+      if (dl.own[d]) continue;
+      const bool all = dl.m[d] >= n || d == 0, none = dl.m[d] == 0;
       thr[d] = (all || none) ? ~0ull : thr[d - 1];
       before_blk[d] = none ? 0 : all ? base : before_blk[d - 1];
     }
   __syncthreads();
   const int p = base + tid;
-  compact_block(a, cu, cu_first, thr, before_blk, wmask, wpre,
+  compact_block(a, dl, cu, cu_first, thr, before_blk, wmask, wpre,
                 p < n ? splitmix64(a.seed ^ (uint64_t)p) : 0ull, idx, depth_off, cu_d, row_of);
 }
 
