@@ -62,7 +62,9 @@ def parse():
 
 TRAFFIC_RECORDS = {4: "profiles/attn_core_gemma270m_32k_K4_traffic.md",
                    5: "profiles/attn_core_llama8b_16k_K8_traffic.md",
-                   3: "profiles/attn_core_packed8_llama8b_4k_traffic.md"}
+                   3: "profiles/attn_core_packed8_llama8b_4k_traffic.md",
+                   2: "profiles/attn_core_gemma270m_4k_traffic.md",
+                   1: "profiles/attn_core_tiny256_traffic.md"}
 DECODE_TRAFFIC_RECORD = "profiles/decode_attn_B64_ctx1k-32k_traffic.md"
 
 
