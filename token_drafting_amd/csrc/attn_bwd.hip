@@ -48,24 +48,7 @@ template <int D>
 struct BCfg {
   static constexpr int KROW = D * 2 + 16;                       // padded row of a row tile
   static constexpr int KBUF = (KT * KROW + 1023) / 1024 * 1024;  // whole DMA blocks
-  static constexpr int TBYTES = D * KT * 2;                       // transposed tile [D][32]
-  static constexpr int DK = D / 16;                               // k-steps over D
-  static constexpr int MT = D / 32;                               // 32-row tiles of D
 };
-
-// Transposed tiles: row d holds 32 entries (64 bytes) in the order that makes a 16-byte
-// read one MFMA operand (inside each 16-group: 0-3, 8-11, 4-7, 12-15); the 16-byte chunk
-// index is XOR-ed with bits 2-3 of d in LDS to spread the rows over the banks.
-__device__ __forceinline__ int t_off(int d, int chunk) {
-  return d * (KT * 2) + ((chunk ^ ((d >> 2) & 3)) << 4);
-}
-// Entry x (0..31) of a transposed row sits in chunk tchunk(x) at element telem(x).
-__device__ __forceinline__ int tchunk(int x) { return 2 * (x >> 4) + ((x & 7) >> 2); }
-__device__ __forceinline__ int telem(int x) { return 4 * ((x & 15) >> 3) + (x & 3); }
-// Inverse: the entry stored at (chunk, element).
-__device__ __forceinline__ int tentry(int chunk, int e) {
-  return 16 * (chunk >> 1) + 8 * (e >> 2) + 4 * (chunk & 1) + (e & 3);
-}
 
 // 16x16x32 bf16 MFMA: lane l supplies row l%16 of A and column l%16 of B, 8 values each at
 // k positions 8 (l/16) .. + 7; it receives column l%16 of D, rows 4 (l/16) + r.
@@ -101,7 +84,6 @@ struct BwdParams {
   const uint16_t* kr;       // k' [T + 32, Hkv, D]
   const uint16_t* v;        // v  [T, Hkv, D]
   const uint16_t* vpad;     // depth-0 v [n + 32, Hkv, D], zero past n
-  const uint16_t* kt;       // depth-0 k'^T tiles [Hkv][ntiles][D][32]
   const uint16_t* dob;      // bf16 dO [T, Hq, D]
   const float* lse;         // [Hq, T], natural log
   const float* dlt;         // Delta [Hq, T]
@@ -112,7 +94,7 @@ struct BwdParams {
   float* dk;
   float* dv;
   float* part;              // per-segment dK'^T, dV^T partials [nseg][2][n][Hkv][D]
-  int n, T, S, Hq, Hkv, G, QR, ntiles;
+  int n, T, S, Hq, Hkv, G, QR;
   int nkb, seg_len;  // key blocks; query tiles per segment of a key block's range
   int64_t ntq;
   float scale, c_log2;
@@ -156,38 +138,6 @@ __global__ __launch_bounds__(256) void bwd_dout_kernel(const float* __restrict__
   if (on && c == 0) {
     const size_t row = pair / Hq, h = pair % Hq;
     dlt[h * T + row] = acc;
-  }
-}
-
-// Rows [0, nrows) of src [*, Hkv, D] as transposed 32-row tiles [Hkv][ntiles][D][32]
-// (rows past nrows read as zero).
-template <int D>
-__global__ __launch_bounds__(256) void transpose_tiles_kernel(const uint16_t* __restrict__ src,
-                                                              uint16_t* __restrict__ dst,
-                                                              int nrows, int Hkv, int ntiles) {
-  __shared__ uint16_t tile[KT][D + 8];
-  const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  constexpr int CPR = D / 8;
-  for (int q = tid; q < KT * CPR; q += 256) {
-    const int x = q / CPR, c = q % CPR, row = t * KT + x;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (row < nrows) val = *reinterpret_cast<const u32x4*>(src + ((size_t)row * Hkv + g) * D + c * 8);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      tile[x][c * 8 + 2 * w] = (uint16_t)(val[w] & 0xFFFFu);
-      tile[x][c * 8 + 2 * w + 1] = (uint16_t)(val[w] >> 16);
-    }
-  }
-  __syncthreads();
-  uint16_t* out = dst + ((size_t)g * ntiles + t) * D * KT;
-  for (int q = tid; q < D * 4; q += 256) {
-    const int d = q >> 2, chunk = q & 3;
-    u32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      o[w] = (uint32_t)tile[tentry(chunk, 2 * w)][d] |
-             ((uint32_t)tile[tentry(chunk, 2 * w + 1)][d] << 16);
-    *reinterpret_cast<u32x4*>(out + (size_t)d * KT + chunk * 8) = o;
   }
 }
 
@@ -513,27 +463,29 @@ __global__ __launch_bounds__(256) void diag_kernel(const BwdParams p, const int3
   }
 }
 
-// dq' of half of a chunk's query slots (4 waves of 32).
-// Two waves per SIMD at D <= 128 (registers and LDS both fit twice); one at D = 256.
+// dq' of half of a chunk's query slots, eight waves of 16 slots on 16x16x32 MFMAs. A
+// wave holds its slots' q' and dO fragments (the B operands of S^T = K Q^T and
+// dP^T = V dO^T, rows of K and V the A operands from LDS) and dq'^T (16 dims x 16 slots per
+// tile of the accumulator): 128 registers at D = 256 where 32 slots a wave take 256, so two
+// waves share a SIMD. The A operand of dq'^T += K'^T dS^T comes from the row-major K tile by
+// LDS transpose reads, in the key order of the lane's dS weights (4 q4 .. 4 q4 + 3, then
+// 16 + 4 q4 ..), so no transposed copy of K is needed.
 template <int D>
-__global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdParams p) {
-  // LDS fragments are read PFQ MFMAs ahead: at D = 256 a SIMD runs one wave, so nothing
-  // else hides the LDS latency in front of each MFMA (30.5 -> 29.3 ms for the whole
-  // backward at 83001 rows; flat at D = 128, where two waves share a SIMD)
-  constexpr int PFQ = 4;
+__global__ __launch_bounds__(512, D <= 128 ? 2 : 1) void dq_kernel(const BwdParams p) {
   using C = BCfg<D>;
-  constexpr int NR = C::KBUF / 1024, NTB = C::TBYTES / 1024;
+  constexpr int DS = D / 32;  // k-steps of S^T and dP^T
+  constexpr int MB = D / 16;  // 16-dim tiles of dq'^T
+  constexpr int NR = C::KBUF / 1024;
+  constexpr int kW = 8;
   __shared__ __attribute__((aligned(1024))) char Ks0[C::KBUF];
   __shared__ __attribute__((aligned(1024))) char Ks1[C::KBUF];
   __shared__ __attribute__((aligned(1024))) char Vs0[C::KBUF];
   __shared__ __attribute__((aligned(1024))) char Vs1[C::KBUF];
-  __shared__ __attribute__((aligned(1024))) char Ts0[C::TBYTES];
-  __shared__ __attribute__((aligned(1024))) char Ts1[C::TBYTES];
   __shared__ int s_range[6];
   __shared__ int s_kp[KT], s_kd[KT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r32 = lane & 31, half = lane >> 5;
+  const int l16 = lane & 15, q4 = lane >> 4;
   const int hs = blockIdx.x & 1, rest = blockIdx.x >> 1;
   const int g = rest % p.Hkv;
   const int chunk = *p.nchunks - 1 - rest / p.Hkv;  // longest prefixes first
@@ -557,7 +509,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
   const int k_lo = s_range[0], k_hi = s_range[1], full_lo = s_range[2], full_hi = s_range[3];
   const int dg_lo = s_range[4], dg_hi = s_range[5];
 
-  const int slot = hs * 128 + wave * 32 + r32;
+  const int slot = hs * 128 + wave * 16 + l16;
   const int rl = slot % p.QR, hl = slot / p.QR;
   const bool q_on = rl < jn;
   const int4 qi = p.qinfo[j0 + min(rl, jn - 1)];
@@ -566,50 +518,41 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
   const int q_d = qi.z;
   const int q_lo = min(max(qi.w, 0), q_p);
   const int q_head = g * p.G + hl;
-  bf16x8 qf[C::DK], df[C::DK];
+  bf16x8 qf[DS], df[DS];
   {
-    const size_t o = ((size_t)q_row * p.Hq + q_head) * D + half * 8;
+    const size_t o = ((size_t)q_row * p.Hq + q_head) * D + 8 * q4;
 #pragma unroll
-    for (int kk = 0; kk < C::DK; ++kk) {
-      qf[kk] = ld8(p.qr + o + kk * 16);
-      df[kk] = ld8(p.dob + o + kk * 16);
+    for (int kk = 0; kk < DS; ++kk) {
+      qf[kk] = ld8(p.qr + o + 32 * kk);
+      df[kk] = ld8(p.dob + o + 32 * kk);
     }
   }
   const size_t li = (size_t)q_head * T + q_row;
   const float lse2 = p.lse[li] * kLog2e, delta = p.dlt[li];
-  floatx16 acc[C::MT];
+  floatx4 acc[MB];
 #pragma unroll
-  for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // mode 0: no mask, 1: context range, 2: diagonal keys (meta in s_kp / s_kd)
-  auto compute = [&](const char* Ks, const char* Vs, const char* Ts, int mode, int key0) {
-    floatx16 s, dp;
+  auto compute = [&](const char* Ks, const char* Vs, int mode, int key0) {
+    floatx4 s[2], dp[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-    const char* kb = Ks + r32 * C::KROW + half * 16;
-    const char* vb = Vs + r32 * C::KROW + half * 16;
-    {
-      bf16x8 f[C::DK];
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dp[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const char* kr = Ks + (16 * kb + l16) * C::KROW + q4 * 16;
+      const char* vr = Vs + (16 * kb + l16) * C::KROW + q4 * 16;
 #pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) f[kk] = ld8(kb + kk * 32);
-#pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) s = mfma32(f[kk], qf[kk], s);
-      sched_reads_ahead<C::DK, PFQ, 1>();
+      for (int kk = 0; kk < DS; ++kk) {
+        s[kb] = mfma16(ld8(kr + kk * 64), qf[kk], s[kb]);
+        dp[kb] = mfma16(ld8(vr + kk * 64), df[kk], dp[kb]);
+      }
     }
-    {
-      bf16x8 f[C::DK];
+    bf16x8 sb;
 #pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) f[kk] = ld8(vb + kk * 32);
-#pragma unroll
-      for (int kk = 0; kk < C::DK; ++kk) dp = mfma32(f[kk], df[kk], dp);
-      sched_reads_ahead<C::DK, PFQ, 1>();
-    }
-    bf16x8 sb[2];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kl = 8 * (r >> 2) + 4 * half + (r & 3);
+    for (int e = 0; e < 8; ++e) {
+      const int kb = e >> 2, r = e & 3;
+      const int kl = 16 * kb + 4 * q4 + r;
       bool ok = true;
       if (mode == 1) {
         const int key = key0 + kl;
@@ -618,31 +561,27 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
         const int kp = s_kp[kl], kd = s_kd[kl];
         ok = kp == q_p && kd >= 1 && kd <= q_d;
       }
-      const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], p.c_log2, -lse2)) : 0.f;
-      sb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - delta));
+      const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c_log2, -lse2)) : 0.f;
+      sb[e] = (__bf16)(pr * (dp[kb][r] - delta));
     }
-    {
-      bf16x8 f[2 * C::MT];
+    // A operand: dims 16 mb + l16 of keys 4 q4 .. 4 q4 + 3 and 16 + 4 q4 .. (two transpose
+    // reads from the row-major K tile)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) f[ks * C::MT + mt] = ld8(Ts + t_off(mt * 32 + r32, ks * 2 + half));
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mt = 0; mt < C::MT; ++mt) acc[mt] = mfma32(f[ks * C::MT + mt], sb[ks], acc[mt]);
-      sched_reads_ahead<2 * C::MT, PFQ, 1>();
+    for (int mb = 0; mb < MB; ++mb) {
+      const char* a = Ks + (4 * q4 + (l16 >> 2)) * C::KROW + (16 * mb + 4 * (l16 & 3)) * 2;
+      const v4i16 lo = ld_tr16(a), hi = ld_tr16(a + 16 * C::KROW);
+      acc[mb] = mfma16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                       sb, acc[mb]);
     }
   };
 
   // ---- causal context: depth-0 key tiles ----
-  auto issue = [&](int t, char* Kd, char* Vd, char* Td) {
+  auto issue = [&](int t, char* Kd, char* Vd) {
     const char* bk = uniform_opaque(reinterpret_cast<const char*>(p.kr + ((size_t)t * KT * Hkv + g) * D));
     const char* bv = uniform_opaque(reinterpret_cast<const char*>(p.vpad + ((size_t)t * KT * Hkv + g) * D));
-    const char* bt = uniform_opaque(reinterpret_cast<const char*>(p.kt + ((size_t)g * p.ntiles + t) * (size_t)(D * KT)));
 #pragma unroll
-    for (int j = 0; j < (NR + 3) / 4; ++j) {
-      const int b = wave + 4 * j;
+    for (int j = 0; j < (NR + kW - 1) / kW; ++j) {
+      const int b = wave + kW * j;
       if (b < NR) {
         const int P = b * 1024 + lane * 16;
         const int x = P / C::KROW, off = P - x * C::KROW;
@@ -651,38 +590,25 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
         dma16(bv + lane_opaque(o), Vd + b * 1024);
       }
     }
-#pragma unroll
-    for (int j = 0; j < (NTB + 3) / 4; ++j) {
-      const int b = wave + 4 * j;
-      if (b < NTB) {
-        const int P = b * 1024 + lane * 16;
-        const int d = P >> 6, c = ((P >> 4) & 3) ^ ((d >> 2) & 3);
-        dma16(bt + lane_opaque((uint32_t)((d * KT + c * 8) * 2)), Td + b * 1024);
-      }
-    }
   };
-  // Two tiles per iteration, each buffer a distinct static array (so that LDS reads of one
-  // buffer do not wait on the DMA into the other), a single loop exit, and an odd last
-  // tile after the loop (an exit between the two halves made the register allocator
-  // shuttle the accumulators).
   const int t_first = k_lo / KT, t_last = k_hi / KT;
   auto full_tile = [&](int key0) { return key0 >= full_lo && key0 + KT - 1 <= full_hi; };
-  issue(t_first, Ks0, Vs0, Ts0);
+  issue(t_first, Ks0, Vs0);
   int t = t_first;
   for (; t + 1 <= t_last; t += 2) {
     wait_dma();
     __syncthreads();  // tile t landed in buffer 0; buffer 1 is free
-    issue(t + 1, Ks1, Vs1, Ts1);
-    compute(Ks0, Vs0, Ts0, full_tile(t * KT) ? 0 : 1, t * KT);
+    issue(t + 1, Ks1, Vs1);
+    compute(Ks0, Vs0, full_tile(t * KT) ? 0 : 1, t * KT);
     wait_dma();
     __syncthreads();  // tile t+1 landed in buffer 1; buffer 0 is free
-    if (t + 2 <= t_last) issue(t + 2, Ks0, Vs0, Ts0);
-    compute(Ks1, Vs1, Ts1, full_tile((t + 1) * KT) ? 0 : 1, (t + 1) * KT);
+    if (t + 2 <= t_last) issue(t + 2, Ks0, Vs0);
+    compute(Ks1, Vs1, full_tile((t + 1) * KT) ? 0 : 1, (t + 1) * KT);
   }
   if (t == t_last) {
     wait_dma();
     __syncthreads();
-    compute(Ks0, Vs0, Ts0, full_tile(t * KT) ? 0 : 1, t * KT);
+    compute(Ks0, Vs0, full_tile(t * KT) ? 0 : 1, t * KT);
   }
 
   // ---- diagonal extension: depth >= 1 rows of the chunk's anchors ----
@@ -699,7 +625,7 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
       s_kp[tid] = kp;
       s_kd[tid] = kd;
     }
-    for (int q = tid; q < KT * (D / 8); q += 256) {
+    for (int q = tid; q < KT * (D / 8); q += 64 * kW) {
       const int x = q / (D / 8), c = q % (D / 8), jk = jb + x;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (jk < dg_hi) {
@@ -709,27 +635,15 @@ __global__ __launch_bounds__(256, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
       }
       *reinterpret_cast<u32x4*>(Ks0 + x * C::KROW + c * 16) = kv;
       *reinterpret_cast<u32x4*>(Vs0 + x * C::KROW + c * 16) = vv;
-      const int tc = tchunk(x), te = telem(x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(Ts0 + t_off(c * 8 + e, tc) + te * 2) =
-            (uint16_t)((kv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     }
     __syncthreads();
-    compute(Ks0, Vs0, Ts0, 2, 0);
+    compute(Ks0, Vs0, 2, 0);
   }
 
   if (q_on) {
-    float* dst = p.dq + ((size_t)q_row * p.Hq + q_head) * D;
+    float* dst = p.dq + ((size_t)q_row * p.Hq + q_head) * D + 4 * q4;
 #pragma unroll
-    for (int mt = 0; mt < C::MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        floatx4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = acc[mt][4 * i + j] * p.scale;
-        *reinterpret_cast<floatx4*>(dst + mt * 32 + 8 * i + 4 * half) = w;
-      }
+    for (int mb = 0; mb < MB; ++mb) *reinterpret_cast<floatx4*>(dst + 16 * mb) = acc[mb] * p.scale;
   }
 }
 
@@ -774,14 +688,12 @@ hipError_t for_d(int D, F&& f) {
 AttnBwdLayout attn_bwd_layout(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D) {
   AttnBwdLayout L;
   const int64_t G = Hq / std::max(1, Hkv);
-  const size_t ntiles = (size_t)((n + KT - 1) / KT);
   L.ntq = (T * G + KT - 1) / KT;
   const size_t tile_bytes = (size_t)Hkv * L.ntq * KT * D * 2;
   size_t off = attn_layout(n, T, Hq, Hkv, D).total;
   L.fwd = 0;
   L.dob = off;   off += al256((size_t)T * Hq * D * 2);
   L.dlt = off;   off += al256((size_t)T * Hq * 4);
-  L.kt = off;    off += al256(ntiles * KT * Hkv * D * 2);
   L.vpad = off;  off += al256((size_t)(n + KT) * Hkv * D * 2);
   L.qtr = off;   off += al256(tile_bytes);
   L.dtr = off;   off += al256(tile_bytes);
@@ -811,7 +723,6 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
   p.kr = reinterpret_cast<const uint16_t*>(ws + F.krot);
   p.v = v;
   p.vpad = reinterpret_cast<const uint16_t*>(ws + L.vpad);
-  p.kt = reinterpret_cast<const uint16_t*>(ws + L.kt);
   p.dob = reinterpret_cast<const uint16_t*>(ws + L.dob);
   p.lse = lse;
   p.dlt = reinterpret_cast<const float*>(ws + L.dlt);
@@ -829,7 +740,6 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
   p.Hkv = a.Hkv;
   p.G = a.Hq / a.Hkv;
   p.QR = kAttnSlots / p.G;
-  p.ntiles = (a.n + KT - 1) / KT;
   p.ntq = L.ntq;
   p.nkb = (a.n + kBwdKeys - 1) / kBwdKeys;
   p.seg_len = L.seg_len;
@@ -846,8 +756,6 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
     const size_t items = (size_t)a.T * a.Hq * (D / 8);
     hipLaunchKernelGGL(bwd_dout_kernel<D>, dim3((unsigned)((items + 255) / 256)), dim3(256), 0,
                        stream, dout, out, dob, dlt, a.T, a.Hq);
-    hipLaunchKernelGGL(transpose_tiles_kernel<D>, dim3(p.ntiles, a.Hkv), dim3(256), 0, stream,
-                       p.kr, const_cast<uint16_t*>(p.kt), a.n, a.Hkv, p.ntiles);
     {
       const size_t work = (size_t)(a.n + KT) * a.Hkv * D / 8;
       const unsigned blocks = (unsigned)std::min<size_t>((work + 255) / 256, 65536);
@@ -871,7 +779,7 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
       hipLaunchKernelGGL(diag_kernel<D>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream,
                          p, idx, depth_off, a.K);
     }
-    hipLaunchKernelGGL(dq_kernel<D>, dim3(chunk_bound * a.Hkv * 2), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(dq_kernel<D>, dim3(chunk_bound * a.Hkv * 2), dim3(512), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t work = (size_t)a.T * (a.Hq + a.Hkv) * (D / 2);

@@ -20,7 +20,7 @@ constexpr int kBwdKeys = 128;
 
 // The backward's own workspace regions, after the forward's (offsets from the start).
 struct AttnBwdLayout {
-  size_t fwd, dob, dlt, kt, vpad, qtr, dtr, smeta, part, total;
+  size_t fwd, dob, dlt, vpad, qtr, dtr, smeta, part, total;
   int64_t ntq;   // query tiles per kv head
   int seg_len;   // query tiles per segment of the key-major pass
   int nseg;      // segments of the tile list
