@@ -46,7 +46,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct BCfg {
-  static constexpr int KROW = D * 2 + 16;                       // padded row of a row tile
+  // Rows padded by 32 bytes: a row starts 8 of the 64 LDS banks after the previous one, so
+  // the transpose reads (four consecutive rows, 32 bytes each, per 16 lanes) and the
+  // 16-byte row reads (16 rows per 16 lanes) are both free of bank conflicts; with 16 bytes
+  // the transpose reads of neighbouring rows overlapped by 4 banks.
+  static constexpr int KROW = D * 2 + 32;
   static constexpr int KBUF = (KT * KROW + 1023) / 1024 * 1024;  // whole DMA blocks
 };
 
