@@ -13,10 +13,11 @@
 //
 // Work decomposition:
 //   dq   query-major, like the forward: a workgroup takes half of one chunk's 256 query
-//        slots (4 waves of 32) and streams the chunk's depth-0 key tiles through LDS, then
-//        the chunk's diagonal keys. Per 32-key tile: S^T = K Q^T and dP^T = V dO^T (the
-//        lane holds one query column and 16 keys), P and dS in registers, then
-//        dq'^T += K^T dS^T with K^T tiles laid out like the forward's V^T tiles.
+//        slots (8 waves of 16) and streams the chunk's depth-0 key tiles through LDS, then
+//        the chunk's diagonal keys. Per 32-key tile, on 16x16x32 MFMAs: S^T = K Q^T and
+//        dP^T = V dO^T (the lane holds one query column and 8 keys), P and dS in
+//        registers, then dq'^T += K'^T dS^T with K'^T read from the row-major key tile by
+//        LDS transpose reads.
 //   dk, dv of depth-0 keys: key-major. A workgroup owns 128 consecutive keys (8 waves of
 //        16) of one kv head and streams every query tile that can see them: the query
 //        slots (anchor-major rows x G heads) of the anchors from the block's first key to
@@ -209,7 +210,7 @@ __device__ __forceinline__ void key_block_tiles(const BwdParams& p, int k0, int 
   b = (e1 * p.G + KT - 1) / KT;
 }
 
-// dk' (WK) and / or dv (WV) of the depth-0 keys [k0, k0 + 128) of kv head g, from the
+// dk' and dv of the depth-0 keys [k0, k0 + 128) of kv head g, from the
 // query tiles that see them inside one absolute segment of seg_len tiles of the list.
 // Workgroups are ordered segment-major, so those running at the same time stream the same
 // few segments and the tiles come from HBM about once per segment (later blocks hit the
@@ -226,11 +227,13 @@ __device__ __forceinline__ void key_block_tiles(const BwdParams& p, int k0, int 
 // 4 (l/16) .. + 3 and 16 + 4 (l/16) .. + 3. The A operands (dO^T, Q^T) are read from the
 // row-major tiles by LDS transpose reads, so a stage holds only the row tiles (35 KB at
 // D = 256 instead of 67 KB with transposed copies; 7% faster).
-template <int D, bool WK, bool WV>
+template <int D>
 __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
   using C = BCfg<D>;
   constexpr int DS = D / 32;  // k-steps of S and dP over D
   constexpr int MB = D / 16;  // 16-row blocks of dK^T and dV^T
+  constexpr int kPfS = 4;     // S / dP row reads in flight ahead of their MFMAs
+  constexpr int kPfT = 2;     // dV^T / dK^T MFMAs whose transpose reads are in flight
   // LDS regions of one stage, only those the pass reads
   // q' rows, dO rows (both row-major, padded rows), slot metadata; the transposed operands
   // of dV^T and dK^T are read from the row tiles by LDS transpose reads
@@ -265,27 +268,24 @@ __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
   const bool key_on = key <= k1;
   const int kc = min(key, k1);
   const int key_lo = p.qinfo[min(max(p.qstart[kc], 0), p.T - 1)].w;
-  bf16x8 kf[DS], vf[WK ? DS : 1];
+  bf16x8 kf[DS], vf[DS];
   {
     const uint16_t* krow = p.kr + ((size_t)kc * p.Hkv + g) * D + q4 * 8;
     const uint16_t* vrow = p.v + ((size_t)kc * p.Hkv + g) * D + q4 * 8;
 #pragma unroll
     for (int kk = 0; kk < DS; ++kk) {
       kf[kk] = ld8(krow + kk * 32);
-      if constexpr (WK) vf[kk] = ld8(vrow + kk * 32);
+      vf[kk] = ld8(vrow + kk * 32);
     }
   }
-  floatx4 dkt[WK ? MB : 1], dvt[WV ? MB : 1];
+  floatx4 dkt[MB], dvt[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    if constexpr (WK) dkt[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (WV) dvt[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int mb = 0; mb < MB; ++mb) dkt[mb] = dvt[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   auto issue = [&](int t, char* dst) {
     const size_t tb = (size_t)g * p.ntq + t;
-    const char* bq = uniform_opaque(reinterpret_cast<const char*>(p.qtr + tb * KT * D));
-    const char* bd = uniform_opaque(reinterpret_cast<const char*>(p.dtr + tb * KT * D));
+    const auto rq = dma_range(uniform_opaque(reinterpret_cast<const char*>(p.qtr + tb * KT * D)), KT * D * 2);
+    const auto rd = dma_range(uniform_opaque(reinterpret_cast<const char*>(p.dtr + tb * KT * D)), KT * D * 2);
 #pragma unroll
     for (int j = 0; j < (NR + kBwdWaves - 1) / kBwdWaves; ++j) {
       const int b = wave + kBwdWaves * j;
@@ -293,39 +293,46 @@ __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
         const int P = b * 1024 + lane * 16;
         const int x = P / C::KROW, off = P - x * C::KROW;
         const uint32_t o = (x < KT && off < D * 2) ? (uint32_t)(x * D * 2 + off) : 0u;
-        dma16(bq + lane_opaque(o), dst + RQ + b * 1024);
-        dma16(bd + lane_opaque(o), dst + RD + b * 1024);
+        dma16_buf(rq, o, dst + RQ + b * 1024);
+        dma16_buf(rd, o, dst + RD + b * 1024);
       }
     }
     if (wave == 0)
-      dma16(reinterpret_cast<const char*>(p.smeta + tb * KT) + (lane & 31) * 16, dst + RM);
+      dma16_buf(dma_range(uniform_opaque(reinterpret_cast<const char*>(p.smeta + tb * KT)), KT * 16),
+                (uint32_t)(lane & 31) * 16, dst + RM);
   };
 
   auto compute = [&](const char* B) {
+    // S = Q K^T and dP = dO V^T for the two 16-slot halves: four independent chains, one
+    // 16-byte row read per MFMA, interleaved so that no MFMA waits on its predecessor
     floatx4 s[2], dp[2];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      s[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      dp[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const char* qb = B + RQ + (16 * mi + l16) * C::KROW + q4 * 16;
+    for (int mi = 0; mi < 2; ++mi) s[mi] = dp[mi] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const char* qb = B + RQ + l16 * C::KROW + q4 * 16;
+    const char* db = B + RD + l16 * C::KROW + q4 * 16;
 #pragma unroll
-      for (int kk = 0; kk < DS; ++kk) s[mi] = mfma16(ld8(qb + kk * 64), kf[kk], s[mi]);
-      if constexpr (WK) {
-        const char* db = B + RD + (16 * mi + l16) * C::KROW + q4 * 16;
+    for (int kk = 0; kk < DS; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < DS; ++kk) dp[mi] = mfma16(ld8(db + kk * 64), vf[kk], dp[mi]);
+      for (int mi = 0; mi < 2; ++mi) {
+        s[mi] = mfma16(ld8(qb + 16 * mi * C::KROW + kk * 64), kf[kk], s[mi]);
+        dp[mi] = mfma16(ld8(db + 16 * mi * C::KROW + kk * 64), vf[kk], dp[mi]);
       }
     }
+    // One 16-byte metadata read per weight and a branch-free mask: a short-circuit test
+    // compiles to nested branches, each reading one field and waiting for it.
     const int4* meta = reinterpret_cast<const int4*>(B + RM);
+    int4 m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = meta[16 * (e >> 2) + 4 * q4 + (e & 3)];
     bf16x8 pb, sb;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int mi = e >> 2, r = e & 3;
-      const int4 m = meta[16 * mi + 4 * q4 + r];
-      const bool ok = key_on && m.y == key_lo && m.x >= key;
-      const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[mi][r], p.c_log2, -__int_as_float(m.z))) : 0.f;
+      const bool ok = key_on & (m[e].y == key_lo) & (m[e].x >= key);
+      const float ex = __builtin_amdgcn_exp2f(fmaf(s[mi][r], p.c_log2, -__int_as_float(m[e].z)));
+      const float pr = ok ? ex : 0.f;
       pb[e] = (__bf16)pr;
-      if constexpr (WK) sb[e] = (__bf16)(pr * (dp[mi][r] - __int_as_float(m.w)));
+      sb[e] = (__bf16)(pr * (dp[mi][r] - __int_as_float(m[e].w)));
     }
     // A operands of dV^T += dO^T P and dK^T += Q^T dS: dims 16 mb + l16 of slots
     // 4 q4 .. 4 q4 + 3 and 16 + 4 q4 .. (the order of the lane's weights), two transpose
@@ -337,9 +344,15 @@ __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
     };
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      if constexpr (WV) dvt[mb] = mfma16(tr_frag(B + RD, mb), pb, dvt[mb]);
-      if constexpr (WK) dkt[mb] = mfma16(tr_frag(B + RQ, mb), sb, dkt[mb]);
+      dvt[mb] = mfma16(tr_frag(B + RD, mb), pb, dvt[mb]);
+      dkt[mb] = mfma16(tr_frag(B + RQ, mb), sb, dkt[mb]);
     }
+    // LDS reads ahead of the MFMAs that take them: the S and dP row reads kPfS MFMAs
+    // ahead, the metadata behind the last of them, the transpose reads (two per MFMA)
+    // kPfT MFMAs ahead
+    sched_reads_ahead<4 * DS, kPfS, 1>();
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+    sched_reads_ahead<2 * MB, kPfT, 1, 2>();
   };
 
   // two tiles per iteration over two static buffers, one loop exit, odd last tile after
@@ -369,8 +382,8 @@ __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int d = 16 * mb + 4 * q4;
-      if constexpr (WK) *reinterpret_cast<floatx4*>(dkr + d) = dkt[mb];
-      if constexpr (WV) *reinterpret_cast<floatx4*>(dvr + d) = dvt[mb];
+      *reinterpret_cast<floatx4*>(dkr + d) = dkt[mb];
+      *reinterpret_cast<floatx4*>(dvr + d) = dvt[mb];
     }
   }
 }
@@ -581,8 +594,10 @@ __global__ __launch_bounds__(512, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
 
   // ---- causal context: depth-0 key tiles ----
   auto issue = [&](int t, char* Kd, char* Vd) {
-    const char* bk = uniform_opaque(reinterpret_cast<const char*>(p.kr + ((size_t)t * KT * Hkv + g) * D));
-    const char* bv = uniform_opaque(reinterpret_cast<const char*>(p.vpad + ((size_t)t * KT * Hkv + g) * D));
+    // a tile's rows of kv head g: KT rows Hkv * D apart
+    const uint32_t span = (uint32_t)(((KT - 1) * Hkv + 1) * D * 2);
+    const auto rk = dma_range(uniform_opaque(reinterpret_cast<const char*>(p.kr + ((size_t)t * KT * Hkv + g) * D)), span);
+    const auto rv = dma_range(uniform_opaque(reinterpret_cast<const char*>(p.vpad + ((size_t)t * KT * Hkv + g) * D)), span);
 #pragma unroll
     for (int j = 0; j < (NR + kW - 1) / kW; ++j) {
       const int b = wave + kW * j;
@@ -590,8 +605,8 @@ __global__ __launch_bounds__(512, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
         const int P = b * 1024 + lane * 16;
         const int x = P / C::KROW, off = P - x * C::KROW;
         const uint32_t o = (x < KT && off < D * 2) ? (uint32_t)(x * Hkv * D * 2 + off) : 0u;
-        dma16(bk + lane_opaque(o), Kd + b * 1024);
-        dma16(bv + lane_opaque(o), Vd + b * 1024);
+        dma16_buf(rk, o, Kd + b * 1024);
+        dma16_buf(rv, o, Vd + b * 1024);
       }
     }
   };
@@ -772,7 +787,7 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 kgrid((unsigned)((int64_t)nkb * a.Hkv * nseg));
-    hipLaunchKernelGGL((dkdv_kernel<D, true, true>), kgrid, dim3(kBwdThreads), 0, stream, p);
+    hipLaunchKernelGGL((dkdv_kernel<D>), kgrid, dim3(kBwdThreads), 0, stream, p);
     {
       const size_t count4 = (size_t)a.n * a.Hkv * D / 4;  // depth-0 rows of dk and dv
       const unsigned sb = (unsigned)std::min<size_t>((count4 + 255) / 256, 65536);

@@ -80,16 +80,33 @@ __device__ __forceinline__ void dma16(const void* src, char* lds_wave_base) {
                                    (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
 
-// Scheduling pattern for a run of N LDS reads each feeding M MFMAs: the first PF reads
-// go first, then one MFMA group and one read alternate, then the last PF MFMA groups.
+// The same LDS DMA in its buffer form (buffer_load_dwordx4 ... lds): lane l moves 16 bytes
+// from the range's byte voff to lds_wave_base + 16 l. The compiler's wait-count pass treats
+// the global form as a flat access that may touch LDS, and while one is outstanding it
+// makes every LDS read wait with lgkmcnt(0), draining the reads issued ahead of the MFMAs;
+// the buffer form it tracks on vmcnt alone. The range is a raw buffer resource (gfx9
+// descriptor, no stride) over [base, base + bytes): a lane offset at or past bytes loads
+// zeros instead of reading outside it. base is wave-uniform.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_range(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t range, uint32_t voff,
+                                          char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      range, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
+// Scheduling pattern for a run of N groups of R LDS reads, each group feeding M MFMAs: the
+// first PF groups of reads go first, then one MFMA group and one read group alternate,
+// then the last PF MFMA groups.
 constexpr int kSchedDsRead = 0x100, kSchedMfma = 0x008;
-template <int N, int PF, int M>
+template <int N, int PF, int M, int R = 1>
 __device__ __forceinline__ void sched_reads_ahead() {
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF, 0);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PF * R, 0);
 #pragma unroll
   for (int i = 0; i < N - PF; ++i) {
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, M, 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, R, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kSchedMfma, PF * M, 0);
 }
