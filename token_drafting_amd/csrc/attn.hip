@@ -216,6 +216,12 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
   int q_row[NT], q_head[NT], q_p[NT], q_d[NT], q_lo[NT];
   bool q_on[NT];
   bf16x8 qf[NT][C::DK];
+  // D = 256 on the main path: the last k-step's q fragment of each lane is kept in LDS (the
+  // k_lo buffer, which this path does not use) and read with the tile's K fragments. At the
+  // 256-register limit the compiler otherwise spills one to scratch and reloads it every
+  // tile behind the next tile's DMA, whose completion the reload's vmcnt wait then awaits.
+  constexpr bool kQInLds = !EXACT && D == 256;
+  char* const q_lds = Kl0 + tid * 16 * NT;
 
   floatx16 o[NT][C::MT];
   float m_run[NT], l_run[NT];
@@ -247,11 +253,28 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
 #pragma unroll
       for (int kk = 0; kk < C::DK; ++kk)
         kf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(kbase + kk * 32));
+      bf16x8 ql[NT];
+      if constexpr (kQInLds) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) ql[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(q_lds + nt * 16));
+      }
 #pragma unroll
       for (int kk = 0; kk < C::DK; ++kk)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[nt] = mfma32(kf[kk], qf[nt][kk], s[nt]);
-      sched_reads_ahead<C::DK, prefetch_k<D>(), NT>();
+        for (int nt = 0; nt < NT; ++nt)
+          s[nt] = mfma32(kf[kk], kQInLds && kk == C::DK - 1 ? ql[nt] : qf[nt][kk], s[nt]);
+      if constexpr (kQInLds) {
+        // the q read goes with the first read-ahead group
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, prefetch_k<D>() + NT, 0);
+#pragma unroll
+        for (int i = 0; i < C::DK - prefetch_k<D>(); ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, NT, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, prefetch_k<D>() * NT, 0);
+      } else {
+        sched_reads_ahead<C::DK, prefetch_k<D>(), NT>();
+      }
     } else {
 #pragma unroll
       for (int kk = 0; kk < C::DK; ++kk) {
@@ -380,19 +403,22 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
     voff[j] = (uint32_t)((d * KT + c * 8) * 2);
   }
   auto dma_k = [&](const uint16_t* src, int t, char* dst) {
-    const char* base = uniform_opaque(reinterpret_cast<const char*>(src + ((size_t)t * KT * Hkv + g) * D));
+    // the tile's KT rows of kv head g, Hkv * D apart
+    const auto range = dma_range(uniform_opaque(reinterpret_cast<const char*>(src + ((size_t)t * KT * Hkv + g) * D)),
+                                 (uint32_t)(((KT - 1) * Hkv + 1) * D * 2));
 #pragma unroll
     for (int j = 0; j < KI; ++j) {
       const int i = wave + j * C::WAVES;
-      if (i < C::KBUF / 1024) dma16(base + lane_opaque(koff[j]), dst + i * 1024);
+      if (i < C::KBUF / 1024) dma16_buf(range, koff[j], dst + i * 1024);
     }
   };
   auto dma_v = [&](int t, char* dst) {
-    const char* base = uniform_opaque(reinterpret_cast<const char*>(p.vt + ((size_t)g * p.ntiles + t) * (size_t)(D * KT)));
+    const auto range = dma_range(uniform_opaque(reinterpret_cast<const char*>(p.vt + ((size_t)g * p.ntiles + t) * (size_t)(D * KT))),
+                                 (uint32_t)(D * KT * 2));
 #pragma unroll
     for (int j = 0; j < VI; ++j) {
       const int i = wave + j * C::WAVES;
-      if (i < C::VBYTES / 1024) dma16(base + lane_opaque(voff[j]), dst + i * 1024);
+      if (i < C::VBYTES / 1024) dma16_buf(range, voff[j], dst + i * 1024);
     }
   };
   auto issue = [&](int t, char* Kd, char* Kld, char* Vd) {
@@ -468,6 +494,7 @@ __device__ __forceinline__ void attn_chunk(const AttnParams& p, AttnLds<D>& L, i
 #pragma unroll
     for (int kk = 0; kk < C::DK; ++kk)
       qf[nt][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kk * 16));
+    if constexpr (kQInLds) *reinterpret_cast<bf16x8*>(q_lds + nt * 16) = qf[nt][C::DK - 1];
   }
   for (int t = t_begin; t <= t_end; t += 2) {
     wait_dma();
