@@ -18,10 +18,12 @@
 // visited. The diagonal keys of the chunk's anchors are a short contiguous run of the
 // anchor-major list, processed as extra masked tiles.
 //
-// Staging. K and V^T tiles go global -> LDS with global_load_lds_dwordx4 (no register
-// round trip) into two LDS buffers: tile t+1 streams in while tile t is computed, one
-// barrier per tile. The loop is unrolled by two so each buffer is a distinct static
-// array and the compiler does not make LDS reads wait on the other buffer's loads.
+// Staging. K and V^T tiles go global -> LDS by LDS DMA in its buffer form
+// (buffer_load_dwordx4 ... lds, no register round trip) into two LDS buffers: tile t+1
+// streams in while tile t is computed, one barrier per tile. The loop is unrolled by two so
+// each buffer is a distinct static array and the compiler does not make LDS reads wait on
+// the other buffer's loads; the buffer form (not global_load_lds) lets the LDS reads issued
+// ahead of the MFMAs wait for themselves alone.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_bf16). Scores are computed transposed,
 // S^T = K * Q^T, so a lane holds one query column and 16 of the 32 keys of a tile: the

@@ -28,10 +28,10 @@
 //   dk, dv of depth >= 1 keys: a depth-e row is seen only by its own anchor's rows of
 //        depth >= e (at most K - e rows x G heads): one wave per key row and kv head on
 //        the vector units.
-// Tiles move global -> LDS by global_load_lds_dwordx4 into two buffers (tile t+1 streams
-// while tile t is computed). Operands are bf16 (q', k', v, dO, P, dS) with fp32
-// accumulation; P is exact up to rounding because lse is the forward's. Every path uses
-// the same bf16-rounded dO, Delta included.
+// Tiles move global -> LDS by LDS DMA in its buffer form (buffer_load_dwordx4 ... lds)
+// into two buffers (tile t+1 streams while tile t is computed). Operands are bf16 (q', k',
+// v, dO, P, dS) with fp32 accumulation; P is exact up to rounding because lse is the
+// forward's. Every path uses the same bf16-rounded dO, Delta included.
 #include <algorithm>
 
 #include "bwd.h"
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kBwdThreads) void dkdv_kernel(const BwdParams p) {
   constexpr int DS = D / 32;  // k-steps of S and dP over D
   constexpr int MB = D / 16;  // 16-row blocks of dK^T and dV^T
   constexpr int kPfS = 4;     // S / dP row reads in flight ahead of their MFMAs
-  constexpr int kPfT = 2;     // dV^T / dK^T MFMAs whose transpose reads are in flight
+  constexpr int kPfT = 3;     // dV^T / dK^T MFMAs whose transpose reads are in flight
   // LDS regions of one stage, only those the pass reads
   // q' rows, dO rows (both row-major, padded rows), slot metadata; the transposed operands
   // of dV^T and dK^T are read from the row tiles by LDS transpose reads
@@ -570,15 +570,17 @@ __global__ __launch_bounds__(512, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
     for (int e = 0; e < 8; ++e) {
       const int kb = e >> 2, r = e & 3;
       const int kl = 16 * kb + 4 * q4 + r;
+      // branch-free: the weight is computed for every key and masked by a select
       bool ok = true;
       if (mode == 1) {
         const int key = key0 + kl;
-        ok = key >= q_lo && key <= q_p;
+        ok = (key >= q_lo) & (key <= q_p);
       } else if (mode == 2) {
         const int kp = s_kp[kl], kd = s_kd[kl];
-        ok = kp == q_p && kd >= 1 && kd <= q_d;
+        ok = (kp == q_p) & (kd >= 1) & (kd <= q_d);
       }
-      const float pr = ok ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c_log2, -lse2)) : 0.f;
+      const float ex = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.c_log2, -lse2));
+      const float pr = ok ? ex : 0.f;
       sb[e] = (__bf16)(pr * (dp[kb][r] - delta));
     }
     // A operand: dims 16 mb + l16 of keys 4 q4 .. 4 q4 + 3 and 16 + 4 q4 .. (two transpose

@@ -50,7 +50,7 @@ __device__ __forceinline__ int lower_count(const int32_t* a, int len, int32_t x)
   return lo;
 }
 
-// ---- LDS DMA (global_load_lds_dwordx4) and scheduling helpers ----
+// ---- LDS DMA (global_load_lds_dwordx4, buffer_load_dwordx4 ... lds) and scheduling helpers ----
 
 // s_waitcnt vmcnt(N) with expcnt and lgkmcnt left at their maxima (N < 16): at most N of
 // this wave's vector-memory operations (here: LDS-DMA tile loads) are still outstanding.
