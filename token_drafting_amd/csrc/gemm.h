@@ -19,7 +19,8 @@
 // Workgroups go to the 8 XCDs round-robin by linear id, each XCD with its own L2; the
 // id is remapped so that XCD b % 8 runs a contiguous range of tile ids, and tile ids
 // enumerate the N tiles of one M block together: the N tiles that share an A block run
-// at the same time on one XCD and fetch that block from HBM once.
+// at the same time on one XCD and fetch that block from HBM once. The wide variant with
+// N tiles in multiples of 8 instead gives each XCD a fixed eighth of the N tiles (below).
 #pragma once
 
 #include <type_traits>
@@ -237,8 +238,21 @@ __global__ __launch_bounds__(kWideThreads) void dma_gemm_wide_kernel(const uint1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ntn = N / BNW;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BNW;
+  // With N tiles in multiples of the XCD count (wide outputs: the draft head, the gate/up
+  // projection, the 4096-wide fc), XCD x runs N tiles [x nx, (x + 1) nx) of every M block,
+  // so its slice of W stays in its L2 while the A blocks, re-read by the 8 XCDs, come from
+  // the last-level cache. Else an XCD runs all N tiles of a range of M blocks (W small).
+  int mblk, ntile;
+  if (ntn % kXcds == 0) {
+    const int nx = ntn / kXcds, i = blockIdx.x / kXcds;
+    mblk = i / nx;
+    ntile = (blockIdx.x % kXcds) * nx + i % nx;
+  } else {
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    mblk = tile / ntn;
+    ntile = tile % ntn;
+  }
+  const int m0 = mblk * BM, n0 = ntile * BNW;
   const int r32 = lane & 31, half = lane >> 5;
 
   uint32_t aoff[kADma], boff[kBDma];
