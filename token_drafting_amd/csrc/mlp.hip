@@ -223,14 +223,23 @@ struct StoreArgmaxKeys {
   static constexpr bool kWaveTile = true;
   uint64_t* keys;
   int nchunks;
+  // Per 64-column chunk a lane holds one key per row it covers (the larger of its two
+  // columns), V0 = 16 NI rows. The 32 lanes of a half-wave reduce them by a transposing
+  // butterfly: at the exchange with lane l ^ o, each lane keeps the half of its keys that
+  // bit o of its lane selects and takes the max with the partner's copy of that half, so
+  // the key count halves at every exchange (V0 - V0 / 32 exchanges per lane instead of
+  // 5 V0) and lane l ends with the rows V0 / 32 (l % 32) .. + V0 / 32 - 1.
   template <int NI, int NJ>
   __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
                                             int lane, int M, int N) const {
     static_assert(NJ % 2 == 0, "whole 64-column chunks");
+    constexpr int V0 = 16 * NI, VF = V0 / 32;
+    static_assert(V0 % 32 == 0, "whole rows per lane after the exchanges");
     const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int c = 0; c < NJ / 2; ++c) {
       const int cc = col0 + 64 * c;  // this chunk's first column
+      uint64_t k[V0];
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -239,22 +248,34 @@ struct StoreArgmaxKeys {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int col = cc + 32 * j + r32;
-            const uint64_t k = col < N ? ((uint64_t)order_key(acc[i][2 * c + j][r]) << 32) |
-                                             (uint64_t)(0xFFFFFFFFu - (uint32_t)col)
-                                       : 0;
-            best = k > best ? k : best;
+            const uint64_t key = col < N ? ((uint64_t)order_key(acc[i][2 * c + j][r]) << 32) |
+                                               (uint64_t)(0xFFFFFFFFu - (uint32_t)col)
+                                         : 0;
+            best = key > best ? key : best;
           }
-#pragma unroll
-          for (int o = 1; o < 32; o <<= 1) {
-            const uint32_t lo = __shfl_xor((uint32_t)best, o, 64);
-            const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o, 64);
-            const uint64_t other = ((uint64_t)hi << 32) | lo;
-            best = other > best ? other : best;
-          }
-          const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-          // a chunk whose 64 columns all lie past N (the last tile) has no key
-          if (r32 == 0 && row < M && cc < N) keys[(size_t)row * nchunks + (cc >> 6)] = best;
+          k[16 * i + r] = best;
         }
+#pragma unroll
+      for (int e = 0; e < 5; ++e) {
+        const int o = 16 >> e, v = V0 >> (e + 1);  // partner offset, keys kept
+        const bool up = (lane & o) != 0;
+#pragma unroll
+        for (int q = 0; q < v; ++q) {
+          const uint64_t send = up ? k[q] : k[q + v];
+          const uint64_t keep = up ? k[q + v] : k[q];
+          const uint32_t lo = __shfl_xor((uint32_t)send, o, 64);
+          const uint32_t hi = __shfl_xor((uint32_t)(send >> 32), o, 64);
+          const uint64_t got = ((uint64_t)hi << 32) | lo;
+          k[q] = got > keep ? got : keep;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < VF; ++q) {
+        const int x = VF * r32 + q, i = x >> 4, r = x & 15;
+        const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        // a chunk whose 64 columns all lie past N (the last tile) has no key
+        if (row < M && cc < N) keys[(size_t)row * nchunks + (cc >> 6)] = k[q];
+      }
     }
   }
 };
