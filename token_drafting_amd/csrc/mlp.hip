@@ -11,9 +11,9 @@
 //
 // Every product runs on the DMA-fed GEMM of gemm.h with its own epilogue:
 //   o_proj   A = o in bf16 (cast kernel), epilogue adds the residual, h1 in fp32;
-//   gate/up  B = W_gate and W_up interleaved by 16 rows (pack kernel), so in each 32-wide
-//            MFMA tile lanes l and l ^ 16 hold gate and up of the same intermediate
-//            column: the epilogue writes silu(gate) * up in bf16 and the pair never
+//   gate/up  B = W_gate and W_up interleaved by 32 rows (pack kernel), so a lane holds
+//            gate and up of the same intermediate column in two neighbouring 32-wide
+//            MFMA tiles: the epilogue writes silu(gate) * up in bf16 and the pair never
 //            exists in memory;
 //   down     epilogue adds h1, h2 in fp32;
 //   head     epilogue folds each wave's 64 columns into one order-preserving 64-bit key
@@ -92,8 +92,9 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
   }
 }
 
-// Rows of W_gate and W_up [I, H] interleaved by 16: packed row 32 j + t is gate row
-// 16 j + t for t < 16, up row 16 j + t - 16 otherwise. 16 bytes per thread step.
+// Rows of W_gate and W_up [I, H] interleaved by 32: packed row 64 j + t is gate row
+// 32 j + t for t < 32, up row 32 j + t - 32 otherwise (one 32-wide MFMA tile of gate
+// columns, then the up tile of the same outputs). 16 bytes per thread step.
 __global__ __launch_bounds__(256) void pack_gate_up_kernel(const uint16_t* __restrict__ gate,
                                                            const uint16_t* __restrict__ up,
                                                            uint16_t* __restrict__ out, int I,
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(256) void pack_gate_up_kernel(const uint16_t* __res
   for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
        t += (size_t)gridDim.x * blockDim.x) {
     const int prow = (int)(t / per_row), c = (int)(t % per_row);
-    const int j = prow >> 5, tt = prow & 31;
-    const uint16_t* src = tt < 16 ? gate + (size_t)(16 * j + tt) * H : up + (size_t)(16 * j + tt - 16) * H;
+    const int j = prow >> 6, tt = prow & 63;
+    const uint16_t* src = tt < 32 ? gate + (size_t)(32 * j + tt) * H : up + (size_t)(32 * j + tt - 32) * H;
     *reinterpret_cast<u32x4*>(out + (size_t)prow * H + c * 8) =
         *reinterpret_cast<const u32x4*>(src + c * 8);
   }
@@ -188,23 +189,26 @@ struct StoreSwiGLU {
   static constexpr bool kWaveTile = true;
   uint16_t* act;
   int I;
-  // acc[i][j]: the 32x32 MFMA tile at rows row0 + 32 i, columns col0 + 32 j
+  // acc[i][j]: the 32x32 MFMA tile at rows row0 + 32 i, columns col0 + 32 j. The packed
+  // columns come in blocks of 64 (32 gate, then 32 up for the same outputs) and a wave's
+  // columns start on a block, so tiles 2c and 2c + 1 give each lane the gate and up value
+  // of one output column: no lane exchange, and all 32 lanes of a row store.
   template <int NI, int NJ>
   __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
                                             int lane, int M, int N) const {
+    static_assert(NJ % 2 == 0, "gate and up tiles in pairs");
     const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int colb = col0 + 32 * j;  // packed columns colb .. colb + 31: 16 gate, 16 up
-        const int out_col = (colb >> 5) * 16 + r32;
+      for (int c = 0; c < NJ / 2; ++c) {
+        const int colb = col0 + 64 * c;  // first packed column of the block
+        const int out_col = (colb >> 6) * 32 + r32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float g = acc[i][j][r];
-          const float u = __shfl_xor(g, 16, 64);
+          const float g = acc[i][2 * c][r], u = acc[i][2 * c + 1][r];
           const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (r32 < 16 && colb < N && row < M)
+          if (colb < N && row < M)
             act[(size_t)row * I + out_col] = f32_to_bf16_bits(g / (1.f + __expf(-g)) * u);
         }
       }
