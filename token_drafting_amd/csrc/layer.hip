@@ -81,15 +81,39 @@ __global__ __launch_bounds__(256) void layer1_norm_kernel(const float* __restric
 // Column c of the projection goes to q (c < nq), k (next nk) or v (last nk), bf16.
 struct StoreQKV {
   static constexpr bool kWaveTile = false;
+  static constexpr bool kBlock = true;
   uint16_t* q;
   uint16_t* k;
   uint16_t* v;
   int nq, nk;
-  __device__ __forceinline__ void operator()(int row, int col, float val) const {
-    const uint16_t b = f32_to_bf16_bits(val);
-    if (col < nq) q[(size_t)row * nq + col] = b;
-    else if (col < nq + nk) k[(size_t)row * nk + (col - nq)] = b;
-    else v[(size_t)row * nk + (col - nq - nk)] = b;
+  // nq and nk are multiples of 64, so each 32-column MFMA tile of the wave lies inside one
+  // of q, k, v: the destination is chosen once per tile, not per element
+  template <int NI, int NJ>
+  __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
+                                            int lane, int M, int N) const {
+    const int r32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int cb = col0 + 32 * j;
+      if (cb >= N) continue;
+      uint16_t* dst;
+      int width, c0;
+      if (cb < nq) {
+        dst = q, width = nq, c0 = cb;
+      } else if (cb < nq + nk) {
+        dst = k, width = nk, c0 = cb - nq;
+      } else {
+        dst = v, width = nk, c0 = cb - nq - nk;
+      }
+      dst += c0 + r32;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < M) dst[(size_t)row * width] = f32_to_bf16_bits(acc[i][j][r]);
+        }
+    }
   }
 };
 
