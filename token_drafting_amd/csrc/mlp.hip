@@ -112,48 +112,80 @@ __global__ __launch_bounds__(256) void pack_gate_up_kernel(const uint16_t* __res
 }
 
 // out = acc + src (fp32, row stride N) over a wave's tile, with src scaled by inv[min(row,
-// n)] * w[col] when norm. Each MFMA tile loads all its src values before it stores any
-// result: with per-element read-then-write, every load would wait
-// behind the previous store (the compiler cannot move a load above a store it may alias;
-// the restrict-qualified pointers tell it they never do). Rows past M and columns past N
-// load clamped addresses and store nothing.
-template <int NI, int NJ>
+// n)] * w[col] when kNorm. Rows past M and columns past N load clamped addresses and store
+// nothing; the restrict-qualified pointers let the compiler move loads above stores.
+//   - Plain residual: the MFMA tiles are visited in turn and the src values of tile t + 1
+//     are loaded before tile t is stored, so a tile's loads are in flight while the
+//     previous tile stores (loaded and stored one tile at a time, every tile waited for its
+//     loads from memory in full).
+//   - kNorm: each MFMA tile loads all its src values (and its rows' scales, once per row
+//     block) before it stores; the pipelined form needs more registers than the tile has.
+template <int NI, int NJ, bool kNorm>
 __device__ __forceinline__ void add_tile(const floatx16 (&acc)[NI][NJ], float* __restrict__ out,
                                          const float* __restrict__ src,
                                          const float* __restrict__ inv,
-                                         const uint16_t* __restrict__ w, int N, int n, bool norm,
-                                         int row0, int col0, int lane, int M) {
+                                         const uint16_t* __restrict__ w, int N, int n, int row0,
+                                         int col0, int lane, int M) {
   const int r32 = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    float rs[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = min(row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3), M - 1);
-      rs[r] = norm ? inv[min(row, n)] : 1.f;
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = col0 + 32 * j + r32;
-      const int colc = min(col, N - 1);
-      const float wc = norm ? bf16_bits_to_f32(w[colc]) : 1.f;
-      float pre[16];
+  if constexpr (!kNorm) {
+    constexpr int NT = NI * NJ;
+    float buf[2][16];
+    auto load = [&](int t, float (&d)[16]) {
+      const int i = t / NJ, j = t % NJ;
+      const int colc = min(col0 + 32 * j + r32, N - 1);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = min(row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3), M - 1);
-        pre[r] = src[(size_t)row * N + colc] * rs[r] * wc;
+        d[r] = src[(size_t)row * N + colc];
       }
+    };
+    load(0, buf[0]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t + 1 < NT) load(t + 1, buf[(t + 1) & 1]);
+      const int i = t / NJ, j = t % NJ;
+      const int col = col0 + 32 * j + r32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < M && col < N) out[(size_t)row * N + col] = acc[i][j][r] + pre[r];
+        if (row < M && col < N) out[(size_t)row * N + col] = acc[i][j][r] + buf[t & 1][r];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one tile of loads ahead, no more
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float rs[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = min(row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3), M - 1);
+        rs[r] = inv[min(row, n)];
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int col = col0 + 32 * j + r32;
+        const int colc = min(col, N - 1);
+        const float wc = bf16_bits_to_f32(w[colc]);
+        float pre[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = min(row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3), M - 1);
+          pre[r] = src[(size_t)row * N + colc] * rs[r] * wc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < M && col < N) out[(size_t)row * N + col] = acc[i][j][r] + pre[r];
+        }
       }
     }
   }
 }
 
-// h1 = residual + acc: the residual is hidden (or rms(hidden) w_hidden, with the row's
-// 1/rms from inv; rows past n share row n's input).
+// h1 = residual + acc: the residual is hidden (or, kNorm, rms(hidden) w_hidden, with the
+// row's 1/rms from inv; rows past n share row n's input). The choice is a template
+// argument so that the plain residual carries no normalisation registers.
+template <bool kNorm>
 struct StoreResidual {
   static constexpr bool kWaveTile = false;
   static constexpr bool kBlock = true;
@@ -162,11 +194,10 @@ struct StoreResidual {
   const float* inv;
   const uint16_t* w;
   int N, n;
-  bool norm;
   template <int NI, int NJ>
   __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
                                             int lane, int M, int) const {
-    add_tile<NI, NJ>(acc, out, hidden, inv, w, N, n, norm, row0, col0, lane, M);
+    add_tile<NI, NJ, kNorm>(acc, out, hidden, inv, w, N, n, row0, col0, lane, M);
   }
 };
 
@@ -180,7 +211,7 @@ struct StoreAdd {
   template <int NI, int NJ>
   __device__ __forceinline__ void wave_tile(const floatx16 (&acc)[NI][NJ], int row0, int col0,
                                             int lane, int M, int) const {
-    add_tile<NI, NJ>(acc, out, add, nullptr, nullptr, N, 0, false, row0, col0, lane, M);
+    add_tile<NI, NJ, false>(acc, out, add, nullptr, nullptr, N, 0, row0, col0, lane, M);
   }
 };
 
@@ -354,9 +385,11 @@ hipError_t launch_layer1_post(const Layer1PostArgs& a, const float* attn, const 
                      0, stream, w_gate, w_up, wgu, a.I, a.H);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = gemm_launch(a_bf16, w_o, a.T, a.H, a.QW,
-                  StoreResidual{h1, hidden, inv, w_hid, a.H, a.n, a.norm_before_residual != 0},
-                  stream);
+  e = a.norm_before_residual
+          ? gemm_launch(a_bf16, w_o, a.T, a.H, a.QW,
+                        StoreResidual<true>{h1, hidden, inv, w_hid, a.H, a.n}, stream)
+          : gemm_launch(a_bf16, w_o, a.T, a.H, a.QW,
+                        StoreResidual<false>{h1, hidden, inv, w_hid, a.H, a.n}, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(rms_rows_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, h1, w_post, m,
                      a.T, a.H, a.eps);
