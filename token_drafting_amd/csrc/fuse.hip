@@ -142,12 +142,13 @@ __global__ __launch_bounds__(kThreads) void fc_gemm_kernel(
 }
 
 // The projected mask_hidden (one row): out[h] = sum_k x[k] W[h][k], one wave per output,
-// fp32 accumulation of the exact bf16 products.
-__global__ __launch_bounds__(256) void fc_row_kernel(const uint16_t* __restrict__ x,
-                                                    const uint16_t* __restrict__ W,
-                                                    float* __restrict__ out, int N, int K) {
+// fp32 accumulation of the exact bf16 products; block b of 256 threads takes outputs
+// 4 b .. 4 b + 3.
+__device__ __forceinline__ void fc_row_block(const uint16_t* __restrict__ x,
+                                             const uint16_t* __restrict__ W,
+                                             float* __restrict__ out, int N, int K, int b) {
   const int lane = threadIdx.x & 63;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int h = b * 4 + (threadIdx.x >> 6);
   if (h >= N) return;
   const uint16_t* w = W + (size_t)h * K;
   float acc = 0.f;
@@ -162,6 +163,12 @@ __global__ __launch_bounds__(256) void fc_row_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if (lane == 0) out[h] = acc;
+}
+
+__global__ __launch_bounds__(256) void fc_row_kernel(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ W,
+                                                    float* __restrict__ out, int N, int K) {
+  fc_row_block(x, W, out, N, K, blockIdx.x);
 }
 
 // Depth >= 1 rows: hidden = projected mask_hidden (row n), embedding of ptd_token_id.
@@ -190,13 +197,19 @@ __global__ __launch_bounds__(256) void fuse_fill_kernel(
   }
 }
 
-// The K-split fc GEMM's partials summed in a fixed order, in place: out = (out + p1) + p2
-// (p2 may be null), over `count` float4s.
-__global__ __launch_bounds__(256) void split_sum_kernel(float* __restrict__ out,
-                                                        const float* __restrict__ p1,
-                                                        const float* __restrict__ p2,
-                                                        size_t count) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+// The K-split fc GEMM's closing steps in one launch. Blocks [0, nsum) sum the partials in
+// a fixed order, in place: out = (out + p1) + p2 (p2 may be null), over `count` float4s.
+// Blocks past nsum project the mask row into row_out (hidden_out row n, which neither the
+// sum nor the partials touch), so that latency-bound product overlaps the sum.
+__global__ __launch_bounds__(256) void split_close_kernel(
+    float* __restrict__ out, const float* __restrict__ p1, const float* __restrict__ p2,
+    size_t count, int nsum, const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
+    float* __restrict__ row_out, int N, int K) {
+  if ((int)blockIdx.x >= nsum) {
+    fc_row_block(x, W, row_out, N, K, (int)blockIdx.x - nsum);
+    return;
+  }
+  const size_t stride = (size_t)nsum * blockDim.x;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < count; i += stride) {
     floatx4 o = reinterpret_cast<const floatx4*>(out)[i];
     const floatx4 b = reinterpret_cast<const floatx4*>(p1)[i];
@@ -292,11 +305,11 @@ hipError_t launch_fuse(const FuseArgs& a, const int32_t* idx, const uint16_t* au
                          grid, dim3(gemm::kThreads), 0, stream, aux, fc_weight, (int)a.n, a.H,
                          klen, parts, a.aux_dim);
     const size_t count = (size_t)a.n * a.H / 4;
-    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)std::min<size_t>((count + 255) / 256, 8192)),
-                       dim3(256), 0, stream, hidden_out, p1, p2, count);
-    if (a.T > a.n)
-      hipLaunchKernelGGL(fc_row_kernel, dim3((a.H + 3) / 4), dim3(256), 0, stream, mask_hidden,
-                         fc_weight, hidden_out + (size_t)a.n * a.H, a.H, a.aux_dim);
+    const int nsum = (int)std::min<size_t>((count + 255) / 256, 8192);
+    const int nrow = a.T > a.n ? (a.H + 3) / 4 : 0;
+    hipLaunchKernelGGL(split_close_kernel, dim3((unsigned)(nsum + nrow)), dim3(256), 0, stream,
+                       hidden_out, p1, p2, count, nsum, mask_hidden, fc_weight,
+                       hidden_out + (size_t)a.n * a.H, a.H, a.aux_dim);
   } else if (gemm::wide_width(a.n, a.H, a.aux_dim) != 0 ||
              a.aux_dim % (gemm::kStages * gemm::kDmaK) == 0) {
     // depth-0 rows on a DMA-fed kernel, the mask row (first depth-1 row) on its own
