@@ -668,27 +668,41 @@ __global__ __launch_bounds__(512, D <= 128 ? 2 : 1) void dq_kernel(const BwdPara
   }
 }
 
-// dq = R^T dq', dk = R^T dk' in place (R: the RoPE rotation at the row's position).
+// dq = R^T dq', dk = R^T dk' in place (R: the RoPE rotation at the row's position). A
+// thread takes 4 consecutive dims j .. j + 3 < D/2 of one (entry, head) and their partners
+// j + D/2 .. (16-byte accesses). Index is uint32_t when the item count, T (Hq + Hkv) D / 8,
+// fits 32 bits (cheap divisions), else uint64_t.
+template <int D, typename Index>
 __global__ __launch_bounds__(256) void unrotate_kernel(const int4* __restrict__ qinfo,
                                                        const float* __restrict__ cs,
                                                        const float* __restrict__ sn,
                                                        float* __restrict__ dq,
                                                        float* __restrict__ dk, int T, int Hq,
-                                                       int Hkv, int D, int max_pos) {
-  const int hd = D / 2, H = Hq + Hkv;
-  const size_t total = (size_t)T * H * hd;
-  for (size_t t = blockIdx.x * (size_t)blockDim.x + threadIdx.x; t < total;
-       t += (size_t)gridDim.x * blockDim.x) {
-    const size_t e = t / ((size_t)H * hd);
-    const int rem = (int)(t % ((size_t)H * hd)), h = rem / hd, j = rem % hd;
+                                                       int Hkv, int max_pos) {
+  constexpr int hd = D / 2, Q = hd / 4;  // float4 groups per half
+  const int H = Hq + Hkv;
+  const Index total = (Index)T * (Index)H * Q;
+  for (Index t = (Index)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (Index)gridDim.x * blockDim.x) {
+    const Index eh = t / Q;
+    const int j = (int)(t % Q) * 4;
+    const int e = (int)(eh / (Index)H), h = (int)(eh % (Index)H);
     const int4 qi = qinfo[e];
     const int row = min(max(qi.x, 0), T - 1);
     const int pos = min(max(qi.y - qi.w + qi.z, 0), max_pos);
-    const float c = cs[(size_t)pos * hd + j], s = sn[(size_t)pos * hd + j];
+    const floatx4 c = *reinterpret_cast<const floatx4*>(cs + (size_t)pos * hd + j);
+    const floatx4 s = *reinterpret_cast<const floatx4*>(sn + (size_t)pos * hd + j);
     float* x = h < Hq ? dq + ((size_t)row * Hq + h) * D : dk + ((size_t)row * Hkv + (h - Hq)) * D;
-    const float a = x[j], b = x[j + hd];
-    x[j] = a * c + b * s;
-    x[j + hd] = b * c - a * s;
+    const floatx4 a = *reinterpret_cast<const floatx4*>(x + j);
+    const floatx4 b = *reinterpret_cast<const floatx4*>(x + j + hd);
+    floatx4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = a[i] * c[i] + b[i] * s[i];
+      hi[i] = b[i] * c[i] - a[i] * s[i];
+    }
+    *reinterpret_cast<floatx4*>(x + j) = lo;
+    *reinterpret_cast<floatx4*>(x + j + hd) = hi;
   }
 }
 
@@ -803,10 +817,14 @@ hipError_t launch_attn_bwd(const AttnArgs& a, const int32_t* idx, const int32_t*
     hipLaunchKernelGGL(dq_kernel<D>, dim3(chunk_bound * a.Hkv * 2), dim3(512), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t work = (size_t)a.T * (a.Hq + a.Hkv) * (D / 2);
+    const size_t work = (size_t)a.T * (a.Hq + a.Hkv) * (D / 8);
     const unsigned blocks = (unsigned)std::min<size_t>((work + 255) / 256, 1 << 20);
-    hipLaunchKernelGGL(unrotate_kernel, dim3(blocks), dim3(256), 0, stream, p.qinfo, rope_cos,
-                       rope_sin, dq, dk, a.T, a.Hq, a.Hkv, D, a.max_pos);
+    if (work + (size_t)blocks * 256 < ((size_t)1 << 32))
+      hipLaunchKernelGGL((unrotate_kernel<D, uint32_t>), dim3(blocks), dim3(256), 0, stream,
+                         p.qinfo, rope_cos, rope_sin, dq, dk, a.T, a.Hq, a.Hkv, a.max_pos);
+    else
+      hipLaunchKernelGGL((unrotate_kernel<D, uint64_t>), dim3(blocks), dim3(256), 0, stream,
+                         p.qinfo, rope_cos, rope_sin, dq, dk, a.T, a.Hq, a.Hkv, a.max_pos);
     return hipGetLastError();
   });
 }
