@@ -189,7 +189,8 @@ size_t peagle_draft_attn_workspace_bytes(int64_t n, int64_t T, int32_t num_q_hea
  *   lse              fp32[Hq, T]      out, natural-log softmax denominators; may be NULL
  *   workspace        >= peagle_draft_attn_workspace_bytes(n, T, Hq, Hkv, D) bytes,
  *                    device memory, 256-byte aligned; its contents are scratch
- * head_dim in {64, 128, 256}; Hq % Hkv == 0 and 256 % (Hq/Hkv) == 0.
+ * head_dim in {64, 128, 256}; Hq % Hkv == 0 and 256 % (Hq/Hkv) == 0; Hkv * head_dim
+ * at most 2^25 (a 32-row key tile then stays below 2^31 bytes).
  * Equal to peagle_draft_attn_prepare followed by peagle_draft_attn_core.
  * Streams: every kernel goes on `stream` alone, ordered after earlier work on it and
  * before later work on it; the call creates no streams or events and takes no locks, so

@@ -126,6 +126,9 @@ def test_attention_argument_errors(lib):
     assert call(D=96) == peagle.ERR_UNSUPPORTED
     assert call(D=32) == peagle.ERR_UNSUPPORTED
     assert call(Hq=6, Hkv=2) == peagle.ERR_UNSUPPORTED   # group of 3 does not divide 256
+    assert call(Hq=1 << 19, Hkv=1 << 19) == peagle.ERR_WORKSPACE     # Hkv D = 2^25: shape taken
+    assert call(Hq=1 << 20, Hkv=1 << 20) == peagle.ERR_UNSUPPORTED   # 2^26: past the tile limit
+    assert call(Hq=1 << 19, Hkv=1 << 19, D=128) == peagle.ERR_UNSUPPORTED
     assert call(Hq=5, Hkv=2) == peagle.ERR_ARG
     assert call(max_pos=65) == peagle.ERR_ARG          # below n + K - 2
     assert call(ws=1024) == peagle.ERR_WORKSPACE

@@ -47,6 +47,8 @@ int attn_shape(int64_t n, int64_t T, int32_t Hq, int32_t Hkv, int32_t D) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PEAGLE_ERR_ARG;
   if (D != 64 && D != 128 && D != 256) return PEAGLE_ERR_UNSUPPORTED;
   if (kAttnSlots % (Hq / Hkv) != 0) return PEAGLE_ERR_UNSUPPORTED;
+  // the kernels address a 32-row tile of kv rows (Hkv D bf16 apart) with 32-bit offsets
+  if ((int64_t)Hkv * D > ((int64_t)1 << 25)) return PEAGLE_ERR_UNSUPPORTED;
   if ((double)(T + 32) * (double)Hq * (double)D > (double)((int64_t)1 << 44)) return PEAGLE_ERR_ARG;
   return PEAGLE_OK;
 }
