@@ -312,24 +312,35 @@ struct CacheTile {
 // Issue the loads of one cache tile: rows [0, rows) of kbase (row stride kstride elements;
 // rows past the end repeat the last one and are masked) and its V^T tile. Every cache byte
 // is read once per call, so the loads are nontemporal: they stream past the caches instead
-// of evicting lines that are still wanted (measured 8% faster).
+// of evicting lines that are still wanted (measured 8% faster). kbase and vtile are
+// wave-uniform: the loads go through raw buffer resources over the tile's bytes (scalar
+// registers) with 32-bit lane offsets (the row stride, Hkv D < 2^24 elements, keeps them
+// below 2^31). Per-lane 64-bit addresses had pushed the two-tile loop past its registers:
+// a spilled address reloaded from scratch once per tile, and its vmcnt wait drained the
+// next tile's loads.
+constexpr int kLoadNT = 2;  // cache policy of the buffer loads: nontemporal
 template <int D, bool kIssueAll>
 __device__ __forceinline__ void load_cache_tile(CacheTile<D>& t, const uint16_t* kbase,
                                                 size_t kstride, int rows,
                                                 const uint16_t* vtile, int l16, int grp) {
   constexpr int DK = D / 32, MT = D / 16;
+  const int rows_c = std::min(rows, kDecTile);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kbase), 0, (int)(((size_t)(rows_c - 1) * kstride + D) * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vtile), 0, D * kDecTile * 2, 0x00020000);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int row = std::min(16 * h + l16, rows - 1);
-    const uint16_t* kp = kbase + (size_t)row * kstride + 8 * grp;
+    const int row = std::min(16 * h + l16, rows_c - 1);
+    const uint32_t ko = (uint32_t)((size_t)row * kstride + 8 * grp) * 2;
 #pragma unroll
     for (int kk = 0; kk < DK; ++kk)
-      t.kf[h][kk] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * kk)));
+      t.kf[h][kk] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(kr, ko + 64 * kk, 0, kLoadNT));
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    t.vf[mt] = as_bf16x8(__builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(vtile + (16 * mt + l16) * kDecTile + 8 * grp)));
+    t.vf[mt] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(
+        vr, (uint32_t)((16 * mt + l16) * kDecTile + 8 * grp) * 2, 0, kLoadNT));
   // kIssueAll: every load of the tile is issued before the first wait on any of them, one
   // memory round trip per tile instead of one for K and then one for V (without this
   // barrier the compiler sinks the V loads below the scores under register pressure: 18%
@@ -352,7 +363,7 @@ __global__ __launch_bounds__(64 * kDecWaves, HEADS == 1 ? 1 : 2) void decode_att
   constexpr int kRedWaves = kMerge ? kDecWaves : 1;
   __shared__ float red_o[kRedWaves][kMerge ? PC : 1][kMerge ? D : 1];
   __shared__ float red_ml[kRedWaves][kMerge ? PC : 1][2];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
   const int K = p.K, Hkv = p.Hkv;
   const int ngg = Hkv / HEADS;
